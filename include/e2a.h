@@ -1,0 +1,182 @@
+/*
+ * e2a.h - C ABI of libe2a, an MI355X (gfx950) implementation of the
+ * on-the-fly equivariant attention layer of E2Former-V2 (arXiv 2601.16622,
+ * "E2Former-V2: On-the-Fly Equivariant Attention with Linear Activation
+ * Memory").
+ *
+ * The pages describe the layer's problem as atom positions, radius
+ * neighbourhoods j in N(i), node irrep features and attention heads
+ * (English technical summary, section 1 "Problem Statement" and section 2.2
+ * "On-the-Fly Equivariant Attention").  This header turns that into two calls:
+ *
+ *   e2a_build_neighbors  - cell-list radius graph, CSR sorted by destination;
+ *   e2a_attention_fwd    - the fused, node-centric layer.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named "device" are HIP device pointers owned by the caller.  The
+ *     library never frees them and keeps none of them after the call returns.
+ *     The library allocates no device memory: scratch comes in through a
+ *     caller-owned workspace whose size a *_workspace_bytes() query gives.
+ *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
+ *     All device work is enqueued on it, in order.
+ *   - Every function that can fail returns an e2a_status.  Argument checks run
+ *     on the host before anything is launched, so an invalid call touches
+ *     neither the device nor the outputs.  e2a_last_error_message() (per host
+ *     thread) says what failed.  No C++ exception crosses this boundary.
+ *   - Real spherical-harmonic components are stored at index l*l + l + m
+ *     (m = -l..l), orthonormal and without the Condon-Shortley phase, so the
+ *     l = 1 block is proportional to (y, z, x).
+ */
+#ifndef E2A_H_
+#define E2A_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define E2A_ABI_VERSION 1
+
+typedef int32_t e2a_status;
+enum {
+  E2A_OK = 0,
+  E2A_ERR_INVALID_ARG = 1,   /* null pointer, bad size, bad value, coordinates outside [0, box) */
+  E2A_ERR_CAPACITY = 2,      /* col_capacity too small; *n_edges holds the required count       */
+  E2A_ERR_BOX_TOO_SMALL = 3, /* a periodic box side is shorter than 2 * cutoff                 */
+  E2A_ERR_UNSUPPORTED = 4,   /* (L, C, H, dtype, variant) combination not built                 */
+  E2A_ERR_HIP = 5            /* a HIP runtime call failed; the message names it                 */
+};
+
+enum { E2A_DTYPE_F32 = 0, E2A_DTYPE_BF16 = 1 };
+
+/* Kernel choice for e2a_attention_fwd.  AUTO picks the MFMA kernel when it is
+ * built for (L, C, H, dtype) and the scalar reference kernel otherwise. */
+enum { E2A_VARIANT_AUTO = 0, E2A_VARIANT_REFERENCE = 1, E2A_VARIANT_MFMA = 2 };
+
+/* ABI version (E2A_ABI_VERSION of the built library). */
+int e2a_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* e2a_status_string(e2a_status s);
+
+/* Message of the last failing call on this host thread ("" if none). */
+const char* e2a_last_error_message(void);
+
+/* ------------------------------------------------------------------------ */
+/* Neighbour graph                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace e2a_build_neighbors needs for n_atoms atoms. */
+size_t e2a_neighbors_workspace_bytes(int64_t n_atoms);
+
+/*
+ * Radius graph N(i) = { j != i : batch_j == batch_i, d_ij < cutoff }
+ * (technical summary section 1: |E| ~ kN neighbour edges; section 2.2:
+ * the kernel iterates j in N(i)).
+ *
+ * The predicate is evaluated in fp32 with every operation correctly rounded
+ * and no fused multiply-add: dx = x_j - x_i per axis; in a periodic box
+ * dx -= box if dx > box/2, else dx += box if dx < -box/2; d2 = (dx*dx + dy*dy)
+ * + dz*dz; neighbour iff d2 < cutoff*cutoff (strict).  The result is exact
+ * and deterministic (independent of launch order).
+ *
+ *   pos          device f32 [n_atoms, 3].  Periodic: each coordinate must lie
+ *                in [0, box_d); otherwise E2A_ERR_INVALID_ARG.
+ *   batch        device i32 [n_atoms] graph ids, or NULL (one graph).
+ *   box          HOST f32 [3] periodic box sides, or NULL for open boundaries.
+ *   cutoff       > 0.  Every periodic side must be >= 2*cutoff
+ *                (E2A_ERR_BOX_TOO_SMALL).
+ *   row_ptr      device i64 [n_atoms + 1]: edges of i are col[row_ptr[i] ..
+ *                row_ptr[i+1]), ascending in j.
+ *   col          device i32 [col_capacity].
+ *   n_edges      HOST out: the number of edges.  If it exceeds col_capacity
+ *                the call returns E2A_ERR_CAPACITY with *n_edges set to the
+ *                required count and col untouched; retry with more space.
+ *   workspace    device scratch of e2a_neighbors_workspace_bytes(n_atoms).
+ *
+ * Blocks the calling host thread until the edge count is known (one device
+ * to host copy of 8 bytes, plus one more for open boundaries to read the
+ * bounding box).  Rows longer than 4096 neighbours give E2A_ERR_UNSUPPORTED.
+ */
+e2a_status e2a_build_neighbors(const float* pos, int64_t n_atoms, const int32_t* batch,
+                               const float* box, float cutoff, int64_t* row_ptr, int32_t* col,
+                               int64_t col_capacity, int64_t* n_edges, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Fused on-the-fly equivariant attention                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Number of SO(2) mixing weights for (L, C): ((L+1)C)^2 + 2 sum_{m=1..L} ((L+1-m)C)^2. */
+int64_t e2a_so2_param_count(int L, int C);
+
+typedef struct e2a_attn_args {
+  /* geometry and graph */
+  const float* pos;        /* device f32 [n_atoms, 3]                                 */
+  const float* box;        /* HOST f32 [3] or NULL (open); minimum image when set    */
+  int64_t n_atoms;
+  const int64_t* row_ptr;  /* device i64 [n_atoms + 1] (CSR by destination)          */
+  const int32_t* col;      /* device i32 [n_edges], neighbour j of each edge          */
+  int64_t n_edges;
+  float cutoff;            /* radius used by the radial basis envelope               */
+  /* shapes */
+  int L;                   /* 0..4: irrep degrees 0..L, (L+1)^2 components           */
+  int C;                   /* channels; multiple of H                                 */
+  int H;                   /* heads; head h owns channels [h C/H, (h+1) C/H)          */
+  int n_rbf;               /* must be 8                                                */
+  int dtype;               /* E2A_DTYPE_F32 or E2A_DTYPE_BF16: storage of the inputs  */
+  int variant;             /* E2A_VARIANT_*                                            */
+  /* inputs, all device, stored in `dtype` */
+  const void* feat;        /* [n_atoms, (L+1)^2, C] node irrep features h             */
+  const void* w_q;         /* [C, C]  q_i = h_{i,l=0} W_q                              */
+  const void* w_k;         /* [C, C]  k_j = h_{j,l=0} W_k                              */
+  const void* w_rad;       /* [n_rbf, L+1, C]  rho[l,c] = sum_k e_k(r) W_rad[k,l,c]     */
+  const void* w_so2;       /* [e2a_so2_param_count(L,C)] per-m blocks, see below      */
+  /* outputs, device */
+  float* out;              /* f32 [n_atoms, (L+1)^2, C], fully overwritten            */
+  float* out_lse;          /* f32 [n_atoms, H] log-sum-exp of the logits, or NULL     */
+  /* scratch */
+  void* workspace;         /* device, e2a_attention_workspace_bytes(...) bytes        */
+  size_t workspace_bytes;
+} e2a_attn_args;
+
+/* Bytes of device workspace e2a_attention_fwd needs. */
+size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype);
+
+/*
+ * o_i = sum_{j in N(i)} alpha_ij^{h(c)} v_ij for every destination atom i.
+ *
+ * Logits come from invariant scalars only (technical summary section 2.2,
+ * "Node-Centric Factorization", Eq. 6): q_i = h_{i,0} W_q, k_j = h_{j,0} W_k,
+ * s_ij^h = <q_i^h, k_j^h> / sqrt(C/H), alpha = softmax over j in N(i),
+ * computed with an online (streaming) softmax ("Online Softmax").
+ *
+ * Geometry enters only the value v_ij (section 2.1, "Equivariant Axis-Aligned
+ * Sparsification", and the abstract): r = x_j - x_i (minimum image), R_ij with
+ * R_ij r_hat = z, D^l = Wigner-D of R_ij; x^l = D^l h_j^l; per-m SO(2) mix
+ *   m = 0: y_{lo,0}  = sum_li x_{li,0} W0[li,lo]
+ *   m > 0: y_{lo,+m} = sum_li x_{li,+m} W1_m[li,lo] - x_{li,-m} W2_m[li,lo]
+ *          y_{lo,-m} = sum_li x_{li,+m} W2_m[li,lo] + x_{li,-m} W1_m[li,lo]
+ * then yhat_{l,m}[c] = rho[l,c] y_{l,m}[c] with the radial basis
+ * e_k(r) = exp(-g (r - mu_k)^2) (cos(pi r/cutoff) + 1)/2, mu_k = k cutoff/7,
+ * g = 1/(2 (cutoff/7)^2); and v^l = D^l^T yhat^l.  No per-edge tensor is
+ * written to device memory ("Elimination of Edge Materialization").
+ *
+ * w_so2 layout: for m = 0..L in order, a [(L+1-m)C] x [(L+1-m)C] row-major
+ * matrix with row (l_in - m)*C + c_in and column (l_out - m)*C + c_out; one
+ * such matrix (W0) for m = 0, two (W1 then W2) for each m >= 1.
+ *
+ * An atom with no neighbours gets o_i = 0 and lse = -inf.  Asynchronous: no
+ * host synchronisation.  Errors: E2A_ERR_INVALID_ARG (null pointer, C % H != 0,
+ * cutoff <= 0, n_rbf != 8, L outside 0..4, workspace too small),
+ * E2A_ERR_UNSUPPORTED (variant not built for the shape or dtype).
+ */
+e2a_status e2a_attention_fwd(const e2a_attn_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* E2A_H_ */

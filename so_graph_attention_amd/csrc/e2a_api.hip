@@ -1,0 +1,157 @@
+// C ABI of libe2a: argument checks (host only, before any launch), workspace
+// carving and dispatch.  See include/e2a.h for the contract of each call.
+#include <cmath>
+#include <cstring>
+
+#include "e2a_internal.hpp"
+
+namespace e2a {
+
+namespace {
+thread_local char g_msg[512] = "";
+}
+
+e2a_status fail(e2a_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_error() { g_msg[0] = '\0'; }
+
+namespace {
+
+struct AttnWs {
+  size_t q, k, w, total;
+};
+
+AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
+  AttnWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.q = take(sizeof(float) * (size_t)n * C);
+  w.k = take(sizeof(float) * (size_t)n * C);
+  w.w = take(mfma_supported(L, C, H, dtype) ? mfma_packed_weight_bytes(L, C) : 0);
+  w.total = off;
+  return w;
+}
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
+
+}  // namespace
+}  // namespace e2a
+
+using namespace e2a;
+
+extern "C" {
+
+int e2a_version(void) { return E2A_ABI_VERSION; }
+
+const char* e2a_status_string(e2a_status s) {
+  switch (s) {
+    case E2A_OK: return "E2A_OK";
+    case E2A_ERR_INVALID_ARG: return "E2A_ERR_INVALID_ARG";
+    case E2A_ERR_CAPACITY: return "E2A_ERR_CAPACITY";
+    case E2A_ERR_BOX_TOO_SMALL: return "E2A_ERR_BOX_TOO_SMALL";
+    case E2A_ERR_UNSUPPORTED: return "E2A_ERR_UNSUPPORTED";
+    case E2A_ERR_HIP: return "E2A_ERR_HIP";
+    default: return "E2A_ERR_UNKNOWN";
+  }
+}
+
+const char* e2a_last_error_message(void) { return g_msg; }
+
+size_t e2a_neighbors_workspace_bytes(int64_t n_atoms) {
+  return n_atoms < 0 ? 0 : neighbors_workspace_bytes(n_atoms);
+}
+
+e2a_status e2a_build_neighbors(const float* pos, int64_t n_atoms, const int32_t* batch, const float* box,
+                               float cutoff, int64_t* row_ptr, int32_t* col, int64_t col_capacity,
+                               int64_t* n_edges, void* workspace, size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (n_atoms < 0 || n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms=%lld out of range", (long long)n_atoms);
+  if (!n_edges) return fail(E2A_ERR_INVALID_ARG, "n_edges is NULL");
+  if (!row_ptr) return fail(E2A_ERR_INVALID_ARG, "row_ptr is NULL");
+  if (n_atoms > 0 && !pos) return fail(E2A_ERR_INVALID_ARG, "pos is NULL");
+  if (col_capacity < 0) return fail(E2A_ERR_INVALID_ARG, "col_capacity < 0");
+  if (col_capacity > 0 && !col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+  if (!finite_positive(cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
+  if (box) {
+    for (int d = 0; d < 3; ++d) {
+      if (!finite_positive(box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
+      if (box[d] < 2.0f * cutoff)
+        return fail(E2A_ERR_BOX_TOO_SMALL, "box[%d]=%g < 2*cutoff=%g", d, (double)box[d], 2.0 * cutoff);
+    }
+  }
+  const size_t need = neighbors_workspace_bytes(n_atoms);
+  if (n_atoms > 0 && (!workspace || workspace_bytes < need))
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  return build_neighbors_impl(pos, n_atoms, batch, box, cutoff, row_ptr, col, col_capacity, n_edges, workspace,
+                              workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int64_t e2a_so2_param_count(int L, int C) {
+  if (L < 0 || C <= 0) return 0;
+  int64_t n = 0;
+  for (int m = 0; m <= L; ++m) {
+    const int64_t k = (int64_t)(L + 1 - m) * C;
+    n += (m == 0 ? 1 : 2) * k * k;
+  }
+  return n;
+}
+
+size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype) {
+  if (n_atoms < 0 || L < 0 || L > 4 || C <= 0 || H <= 0) return 0;
+  return attn_ws_layout(n_atoms, L, C, H, dtype).total;
+}
+
+e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
+  if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
+  if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
+  if (a->L < 0 || a->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", a->L);
+  if (a->C <= 0 || a->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
+  if (a->C % a->H != 0) return fail(E2A_ERR_INVALID_ARG, "C=%d is not a multiple of H=%d", a->C, a->H);
+  if (a->n_rbf != 8) return fail(E2A_ERR_INVALID_ARG, "n_rbf=%d; only 8 is supported", a->n_rbf);
+  if (a->dtype != E2A_DTYPE_F32 && a->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", a->dtype);
+  if (a->variant < E2A_VARIANT_AUTO || a->variant > E2A_VARIANT_MFMA)
+    return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
+  if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
+  if (a->n_atoms > 0) {
+    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out};
+    const char* names[] = {"pos", "row_ptr", "feat", "w_q", "w_k", "w_rad", "w_so2", "out"};
+    for (int t = 0; t < 8; ++t)
+      if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
+    if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+  }
+  if (a->box)
+    for (int d = 0; d < 3; ++d)
+      if (!finite_positive(a->box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  if (a->variant == E2A_VARIANT_MFMA && !mfma_ok)
+    return fail(E2A_ERR_UNSUPPORTED, "MFMA kernel not built for L=%d C=%d H=%d dtype=%d", a->L, a->C, a->H, a->dtype);
+  const AttnWs ws = attn_ws_layout(a->n_atoms, a->L, a->C, a->H, a->dtype);
+  if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
+  if (a->n_atoms == 0) return E2A_OK;
+
+  AttnPlan pl{};
+  pl.a = a;
+  char* base = static_cast<char*>(a->workspace);
+  pl.q = reinterpret_cast<float*>(base + ws.q);
+  pl.k = reinterpret_cast<float*>(base + ws.k);
+  pl.w_packed = base + ws.w;
+  pl.periodic = a->box != nullptr;
+  for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  e2a_status st = launch_qk(pl, s);
+  if (st != E2A_OK) return st;
+  const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
+  return use_mfma ? launch_attention_mfma(pl, s) : launch_attention_reference(pl, s);
+}
+
+}  // extern "C"

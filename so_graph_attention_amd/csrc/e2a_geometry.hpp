@@ -1,0 +1,127 @@
+// Per-edge geometry of the on-the-fly equivariant attention layer
+// (arXiv 2601.16622, English technical summary section 2.1, "Equivariant
+// Axis-Aligned Sparsification"): the rotation that aligns an edge with z, the
+// real Wigner-D blocks of that rotation, and the radial basis.
+//
+// Everything here is plain fp32 arithmetic usable from device code and from a
+// host-only build, so the recursion can be checked on a CPU.
+#pragma once
+
+#include <math.h>
+
+#if defined(__HIPCC__)
+#define E2A_HD __host__ __device__ inline
+#else
+#define E2A_HD inline
+#endif
+
+namespace e2a {
+
+// Offset of block l inside a packed set of Wigner-D blocks D^0, D^1, ...:
+// sum_{k<l} (2k+1)^2 = l (4 l^2 - 1) / 3.
+E2A_HD constexpr int wig_off(int l) { return l * (4 * l * l - 1) / 3; }
+E2A_HD constexpr int wig_size(int L) { return wig_off(L + 1); }
+
+// Rotation R with R r_hat = z: R = R_y(-theta) R_z(-phi) for r_hat =
+// (sin t cos p, sin t sin p, cos t).  Rows: (ct cp, ct sp, -st), (-sp, cp, 0),
+// (st cp, st sp, ct).  At the poles phi = 0.
+E2A_HD void edge_rotation(const float u[3], float R[3][3]) {
+  const float st = sqrtf(u[0] * u[0] + u[1] * u[1]);
+  const float ct = u[2];
+  float cp = 1.0f, sp = 0.0f;
+  if (st > 0.0f) {
+    cp = u[0] / st;
+    sp = u[1] / st;
+  }
+  R[0][0] = ct * cp; R[0][1] = ct * sp; R[0][2] = -st;
+  R[1][0] = -sp;     R[1][1] = cp;      R[1][2] = 0.0f;
+  R[2][0] = st * cp; R[2][1] = st * sp; R[2][2] = ct;
+}
+
+// Real Wigner-D blocks D^0..D^L of rotation R, defined by Y^l(R v) = D^l Y^l(v)
+// for real harmonics without the Condon-Shortley phase stored at m = -l..l.
+// D^1 is R in (y, z, x) order; higher blocks follow the Ivanic-Ruedenberg
+// recursion (J. Phys. Chem. 100, 6342 (1996); erratum 102, 9099 (1998)),
+// which builds D^l from D^{l-1} and D^1.  Block l sits at D + wig_off(l),
+// row-major [(m + l)(2l + 1) + (n + l)].
+template <int L>
+E2A_HD void wigner_blocks(const float R[3][3], float* D) {
+  D[0] = 1.0f;
+  if (L < 1) return;
+  // (y, z, x) <- index m + 1
+  const int p[3] = {1, 2, 0};
+  float* D1 = D + wig_off(1);
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) D1[a * 3 + b] = R[p[a]][p[b]];
+#pragma unroll
+  for (int l = 2; l <= L; ++l) {
+    const float* Dp = D + wig_off(l - 1);
+    float* Dl = D + wig_off(l);
+    const int wp = 2 * l - 1;
+    auto r1 = [&](int i, int j) { return D1[(i + 1) * 3 + (j + 1)]; };
+    auto rp = [&](int a, int b) { return Dp[(a + l - 1) * wp + (b + l - 1)]; };
+    // P(i, a, b): a in [-(l-1), l-1], b in [-l, l]
+    auto P = [&](int i, int a, int b) {
+      if (b == l) return r1(i, 1) * rp(a, l - 1) - r1(i, -1) * rp(a, 1 - l);
+      if (b == -l) return r1(i, 1) * rp(a, 1 - l) + r1(i, -1) * rp(a, l - 1);
+      return r1(i, 0) * rp(a, b);
+    };
+#pragma unroll
+    for (int m = -l; m <= l; ++m) {
+      const int am = m < 0 ? -m : m;
+      const float d = (m == 0) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int n = -l; n <= l; ++n) {
+        const int an = n < 0 ? -n : n;
+        const float denom = (an == l) ? float((2 * l) * (2 * l - 1)) : float((l + n) * (l - n));
+        const float u = sqrtf(float((l + m) * (l - m)) / denom);
+        const float v = 0.5f * sqrtf((1.0f + d) * float((l + am - 1) * (l + am)) / denom) * (1.0f - 2.0f * d);
+        const float w = -0.5f * sqrtf(float((l - am - 1) * (l - am)) / denom) * (1.0f - d);
+        float acc = 0.0f;
+        if (am < l) acc += u * P(0, m, n);
+        if (m == 0) {
+          acc += v * (P(1, 1, n) + P(-1, -1, n));
+        } else if (m > 0) {
+          const float t1 = P(1, m - 1, n) * (m == 1 ? 1.41421356237f : 1.0f);
+          const float t2 = (m == 1) ? 0.0f : P(-1, 1 - m, n);
+          acc += v * (t1 - t2);
+          if (am < l - 1) acc += w * (P(1, m + 1, n) + P(-1, -m - 1, n));
+        } else {
+          const float t1 = (m == -1) ? 0.0f : P(1, m + 1, n);
+          const float t2 = P(-1, -m - 1, n) * (m == -1 ? 1.41421356237f : 1.0f);
+          acc += v * (t1 + t2);
+          if (am < l - 1) acc += w * (P(1, m - 1, n) - P(-1, -m + 1, n));
+        }
+        Dl[(m + l) * (2 * l + 1) + (n + l)] = acc;
+      }
+    }
+  }
+}
+
+// Runtime-L front end of wigner_blocks.
+E2A_HD void wigner_blocks_rt(int L, const float R[3][3], float* D) {
+  switch (L) {
+    case 0: wigner_blocks<0>(R, D); break;
+    case 1: wigner_blocks<1>(R, D); break;
+    case 2: wigner_blocks<2>(R, D); break;
+    case 3: wigner_blocks<3>(R, D); break;
+    default: wigner_blocks<4>(R, D); break;
+  }
+}
+
+// Radial basis: 8 Gaussians with centres mu_k = k rc/7, width = spacing, times
+// the cosine envelope (cos(pi r / rc) + 1) / 2.
+E2A_HD void radial_basis8(float r, float rc, float e[8]) {
+  const float delta = rc / 7.0f;
+  const float gamma = 0.5f / (delta * delta);
+  const float env = 0.5f * (cosf(3.14159265358979f * r / rc) + 1.0f);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float t = r - float(k) * delta;
+    e[k] = expf(-gamma * t * t) * env;
+  }
+}
+
+}  // namespace e2a

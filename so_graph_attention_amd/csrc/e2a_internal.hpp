@@ -1,0 +1,78 @@
+// Internal helpers shared by the libe2a translation units: status handling,
+// the per-thread error message, HIP error checks and bf16 conversion.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/e2a.h"
+
+namespace e2a {
+
+// Records a formatted message for e2a_last_error_message() and returns s.
+e2a_status fail(e2a_status s, const char* fmt, ...);
+void clear_error();
+
+#define E2A_HIP_CHECK(expr)                                                               \
+  do {                                                                                    \
+    hipError_t e2a_err_ = (expr);                                                         \
+    if (e2a_err_ != hipSuccess)                                                           \
+      return ::e2a::fail(E2A_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e2a_err_)); \
+  } while (0)
+
+#define E2A_LAUNCH_CHECK()                                                                 \
+  do {                                                                                     \
+    hipError_t e2a_err_ = hipGetLastError();                                               \
+    if (e2a_err_ != hipSuccess)                                                            \
+      return ::e2a::fail(E2A_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e2a_err_)); \
+  } while (0)
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// bf16 <-> fp32 (storage conversion only).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_as_f32(const T* p, size_t i);
+template <>
+__device__ __forceinline__ float load_as_f32<float>(const float* p, size_t i) {
+  return p[i];
+}
+template <>
+__device__ __forceinline__ float load_as_f32<uint16_t>(const uint16_t* p, size_t i) {
+  return bf16_to_f32(p[i]);
+}
+
+// Neighbour build (neighbors.hip).
+e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batch, const float* box,
+                                float cutoff, int64_t* row_ptr, int32_t* col, int64_t cap,
+                                int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t neighbors_workspace_bytes(int64_t n);
+
+// Attention (attention_*.hip).
+struct AttnPlan {
+  const e2a_attn_args* a;
+  float* q;           // workspace f32 [N, C]
+  float* k;           // workspace f32 [N, C]
+  void* w_packed;     // workspace, MFMA weight layout (MFMA path only)
+  float box[3];
+  int periodic;
+};
+e2a_status launch_qk(const AttnPlan& p, hipStream_t s);
+e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);
+bool mfma_supported(int L, int C, int H, int dtype);
+size_t mfma_packed_weight_bytes(int L, int C);
+e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
+
+}  // namespace e2a

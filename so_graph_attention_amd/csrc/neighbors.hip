@@ -1,0 +1,453 @@
+// Cell-list radius graph: CSR sorted by destination atom, rows ascending in j.
+//
+// The layer streams j in N(i) for every destination i (arXiv 2601.16622,
+// English technical summary section 2.2, "Streaming Reduction"; section 1
+// gives |E| ~ kN).  The pages do not say how N(i) is built; this is a
+// deterministic counting-sort cell list:
+//   1. bounding box (and coordinate check), read back once;
+//   2. bin atoms into cells of side >= 1.001 * cutoff (counting sort);
+//   3. count the neighbours of each atom over its <= 27 stencil cells;
+//   4. exclusive scan -> row_ptr; read the edge count back;
+//   5. one wavefront per atom gathers its neighbours with ballot compaction
+//      into LDS, bitonic-sorts them and writes the row.
+// The pair predicate is the fp32 rule documented in e2a.h, written with
+// explicitly rounded intrinsics so that no multiply-add is ever fused.
+#include <climits>
+
+#include "e2a_internal.hpp"
+
+namespace e2a {
+namespace {
+
+constexpr int kScanBlock = 1024;   // elements per scan block (256 threads x 4)
+constexpr int kMaxRow = 4096;      // longest row the LDS sort handles
+
+struct Grid {
+  int n[3];
+  float origin[3];
+  float inv_side[3];
+  int periodic;
+  float box[3];
+  float half[3];
+  float rc2;
+};
+
+__device__ __forceinline__ int cell_coord(float x, int d, const Grid& g) {
+  int c = static_cast<int>(floorf((x - g.origin[d]) * g.inv_side[d]));
+  return c < 0 ? 0 : (c >= g.n[d] ? g.n[d] - 1 : c);
+}
+
+// Up to three distinct stencil coordinates along one axis.
+__device__ __forceinline__ int stencil(int c, int d, const Grid& g, int out[3]) {
+  const int n = g.n[d];
+  if (g.periodic) {
+    if (n >= 3) {
+      out[0] = (c + n - 1) % n; out[1] = c; out[2] = (c + 1) % n;
+      return 3;
+    }
+    out[0] = 0; out[1] = 1;
+    return n;
+  }
+  int k = 0;
+  for (int o = -1; o <= 1; ++o) {
+    const int cc = c + o;
+    if (cc >= 0 && cc < n) out[k++] = cc;
+  }
+  return k;
+}
+
+__device__ __forceinline__ bool pair_ok(const float* pi, const float* pj, const Grid& g) {
+  float d2 = 0.0f;
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    float dx = __fsub_rn(pj[d], pi[d]);
+    if (g.periodic) {
+      if (dx > g.half[d]) dx = __fsub_rn(dx, g.box[d]);
+      else if (dx < -g.half[d]) dx = __fadd_rn(dx, g.box[d]);
+    }
+    const float sq = __fmul_rn(dx, dx);
+    d2 = (d == 0) ? sq : __fadd_rn(d2, sq);
+  }
+  return d2 < g.rc2;
+}
+
+// ---- bounding box ---------------------------------------------------------
+// out[0..2] = min, out[3..5] = max, out[6] = 1 if any coordinate is not finite.
+__global__ void k_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
+  __shared__ float smin[3][256], smax[3][256];
+  __shared__ int sbad[256];
+  float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+  int bad = 0;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const float x = pos[3 * i + d];
+      if (!isfinite(x)) bad = 1;
+      mn[d] = fminf(mn[d], x);
+      mx[d] = fmaxf(mx[d], x);
+    }
+  }
+  for (int d = 0; d < 3; ++d) { smin[d][threadIdx.x] = mn[d]; smax[d][threadIdx.x] = mx[d]; }
+  sbad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
+    if (threadIdx.x < s) {
+      for (int d = 0; d < 3; ++d) {
+        smin[d][threadIdx.x] = fminf(smin[d][threadIdx.x], smin[d][threadIdx.x + s]);
+        smax[d][threadIdx.x] = fmaxf(smax[d][threadIdx.x], smax[d][threadIdx.x + s]);
+      }
+      sbad[threadIdx.x] |= sbad[threadIdx.x + s];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    for (int d = 0; d < 3; ++d) { out[d] = smin[d][0]; out[3 + d] = smax[d][0]; }
+    out[6] = sbad[0] ? 1.0f : 0.0f;
+  }
+}
+
+// ---- counting sort into cells ----------------------------------------------
+__global__ void k_bin(const float* __restrict__ pos, int64_t n, Grid g, int32_t* __restrict__ cell_of,
+                      int32_t* __restrict__ cell_cnt) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int cx = cell_coord(pos[3 * i + 0], 0, g);
+  const int cy = cell_coord(pos[3 * i + 1], 1, g);
+  const int cz = cell_coord(pos[3 * i + 2], 2, g);
+  const int c = (cz * g.n[1] + cy) * g.n[0] + cx;
+  cell_of[i] = c;
+  atomicAdd(&cell_cnt[c], 1);
+}
+
+__global__ void k_scatter(int64_t n, const int32_t* __restrict__ cell_of, const int32_t* __restrict__ cell_start,
+                          int32_t* __restrict__ cursor, int32_t* __restrict__ cell_atoms) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int c = cell_of[i];
+  cell_atoms[cell_start[c] + atomicAdd(&cursor[c], 1)] = static_cast<int32_t>(i);
+}
+
+// ---- exclusive scan (int32 in, T out, total at out[n]) ---------------------
+__global__ void k_scan_reduce(const int32_t* __restrict__ in, int64_t n, int64_t* __restrict__ bsum) {
+  __shared__ int64_t s[256];
+  const int64_t base = blockIdx.x * (int64_t)kScanBlock;
+  int64_t acc = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = base + threadIdx.x * 4 + k;
+    if (t < n) acc += in[t];
+  }
+  s[threadIdx.x] = acc;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if (threadIdx.x < st) s[threadIdx.x] += s[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = s[0];
+}
+
+// One block: exclusive scan of nb block sums in place; total to bsum[nb].
+__global__ void k_scan_blocks(int64_t* __restrict__ bsum, int64_t nb) {
+  __shared__ int64_t s[256];
+  __shared__ int64_t carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < nb; base += 256) {
+    const int64_t t = base + threadIdx.x;
+    const int64_t v = t < nb ? bsum[t] : 0;
+    s[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int64_t add = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+      __syncthreads();
+      s[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (t < nb) bsum[t] = carry + s[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == 255) carry += s[255];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bsum[nb] = carry;
+}
+
+template <typename T>
+__global__ void k_scan_apply(const int32_t* __restrict__ in, int64_t n, const int64_t* __restrict__ boff,
+                             T* __restrict__ out) {
+  __shared__ int64_t s[256];
+  const int64_t base = blockIdx.x * (int64_t)kScanBlock;
+  int64_t v[4];
+  int64_t loc = 0;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = base + threadIdx.x * 4 + k;
+    v[k] = t < n ? in[t] : 0;
+    loc += v[k];
+  }
+  s[threadIdx.x] = loc;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int64_t add = threadIdx.x >= off ? s[threadIdx.x - off] : 0;
+    __syncthreads();
+    s[threadIdx.x] += add;
+    __syncthreads();
+  }
+  int64_t run = boff[blockIdx.x] + s[threadIdx.x] - loc;
+  for (int k = 0; k < 4; ++k) {
+    const int64_t t = base + threadIdx.x * 4 + k;
+    if (t < n) out[t] = static_cast<T>(run);
+    run += v[k];
+  }
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+    const int nb = gridDim.x;
+    out[n] = static_cast<T>(boff[nb]);
+  }
+}
+
+template <typename T>
+e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, hipStream_t s) {
+  const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
+  if (nb == 0) {
+    E2A_HIP_CHECK(hipMemsetAsync(out, 0, sizeof(T), s));
+    return E2A_OK;
+  }
+  k_scan_reduce<<<nb, 256, 0, s>>>(in, n, bsum);
+  k_scan_blocks<<<1, 256, 0, s>>>(bsum, nb);
+  k_scan_apply<T><<<nb, 256, 0, s>>>(in, n, bsum, out);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+// ---- neighbour count: one thread per destination atom ----------------------
+__global__ void k_count(const float* __restrict__ pos, int64_t n, const int32_t* __restrict__ batch, Grid g,
+                        const int32_t* __restrict__ cell_start, const int32_t* __restrict__ cell_atoms,
+                        int32_t* __restrict__ row_cnt, int32_t* __restrict__ max_row) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+  const int bi = batch ? batch[i] : 0;
+  int sx[3], sy[3], sz[3];
+  const int nx = stencil(cell_coord(pi[0], 0, g), 0, g, sx);
+  const int ny = stencil(cell_coord(pi[1], 1, g), 1, g, sy);
+  const int nz = stencil(cell_coord(pi[2], 2, g), 2, g, sz);
+  int cnt = 0;
+  for (int a = 0; a < nz; ++a)
+    for (int b = 0; b < ny; ++b)
+      for (int c = 0; c < nx; ++c) {
+        const int cell = (sz[a] * g.n[1] + sy[b]) * g.n[0] + sx[c];
+        for (int t = cell_start[cell]; t < cell_start[cell + 1]; ++t) {
+          const int j = cell_atoms[t];
+          if (j == i) continue;
+          if (batch && batch[j] != bi) continue;
+          const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+          cnt += pair_ok(pi, pj, g) ? 1 : 0;
+        }
+      }
+  row_cnt[i] = cnt;
+  atomicMax(max_row, cnt);
+}
+
+__global__ void k_readback(const int64_t* __restrict__ row_ptr, int64_t n, const int32_t* __restrict__ max_row,
+                           int64_t* __restrict__ out) {
+  out[0] = row_ptr[n];
+  out[1] = *max_row;
+}
+
+// ---- fill + sort: one wavefront (= one block) per destination atom ---------
+__global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int64_t n,
+                                             const int32_t* __restrict__ batch, Grid g,
+                                             const int32_t* __restrict__ cell_start,
+                                             const int32_t* __restrict__ cell_atoms,
+                                             const int64_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
+  __shared__ int32_t buf[kMaxRow];
+  const int64_t i = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+  const int bi = batch ? batch[i] : 0;
+  int sx[3], sy[3], sz[3];
+  const int nx = stencil(cell_coord(pi[0], 0, g), 0, g, sx);
+  const int ny = stencil(cell_coord(pi[1], 1, g), 1, g, sy);
+  const int nz = stencil(cell_coord(pi[2], 2, g), 2, g, sz);
+  int cnt = 0;
+  for (int a = 0; a < nz; ++a)
+    for (int b = 0; b < ny; ++b)
+      for (int c = 0; c < nx; ++c) {
+        const int cell = (sz[a] * g.n[1] + sy[b]) * g.n[0] + sx[c];
+        const int t0 = cell_start[cell], t1 = cell_start[cell + 1];
+        for (int base = t0; base < t1; base += 64) {
+          const int t = base + lane;
+          bool ok = false;
+          int j = 0;
+          if (t < t1) {
+            j = cell_atoms[t];
+            ok = (j != i) && (!batch || batch[j] == bi);
+            if (ok) {
+              const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+              ok = pair_ok(pi, pj, g);
+            }
+          }
+          const uint64_t mask = __ballot(ok);
+          if (ok) {
+            const int slot = cnt + __popcll(mask & ((1ull << lane) - 1ull));
+            if (slot < kMaxRow) buf[slot] = j;
+          }
+          cnt += __popcll(mask);
+        }
+      }
+  // The host has already checked cnt <= kMaxRow from the count pass.
+  int P = 1;
+  while (P < cnt) P <<= 1;
+  for (int t = cnt + lane; t < P; t += 64) buf[t] = INT_MAX;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int t = lane; t < P; t += 64) {
+        const int u = t ^ jj;
+        if (u > t) {
+          const int x = buf[t], y = buf[u];
+          const bool up = (t & k) == 0;
+          if ((x > y) == up) { buf[t] = y; buf[u] = x; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int64_t o = row_ptr[i];
+  for (int t = lane; t < cnt; t += 64) col[o + t] = buf[t];
+}
+
+struct WsLayout {
+  size_t cell_of, cell_cnt, cursor, cell_atoms, row_cnt, bsum, small, total;
+  int64_t cap_cells;
+};
+
+WsLayout ws_layout(int64_t n) {
+  WsLayout w{};
+  const int64_t cap = 4 * n + 4096;
+  const int64_t nb = (std::max<int64_t>(n, cap + 1) + kScanBlock - 1) / kScanBlock + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.cell_of = take(sizeof(int32_t) * n);
+  w.cell_cnt = take(sizeof(int32_t) * (cap + 1));
+  w.cursor = take(sizeof(int32_t) * cap);
+  w.cell_atoms = take(sizeof(int32_t) * n);
+  w.row_cnt = take(sizeof(int32_t) * n);
+  w.bsum = take(sizeof(int64_t) * nb);
+  w.small = take(256);
+  w.total = off;
+  w.cap_cells = cap;
+  return w;
+}
+
+}  // namespace
+
+size_t neighbors_workspace_bytes(int64_t n) { return ws_layout(n).total; }
+
+e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batch, const float* box,
+                                float cutoff, int64_t* row_ptr, int32_t* col, int64_t cap_edges,
+                                int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t s) {
+  const WsLayout L = ws_layout(n);
+  if (ws_bytes < L.total) return fail(E2A_ERR_INVALID_ARG, "workspace_bytes %zu < required %zu", ws_bytes, L.total);
+  char* base = static_cast<char*>(ws);
+  int32_t* cell_of = reinterpret_cast<int32_t*>(base + L.cell_of);
+  int32_t* cell_cnt = reinterpret_cast<int32_t*>(base + L.cell_cnt);
+  int32_t* cursor = reinterpret_cast<int32_t*>(base + L.cursor);
+  int32_t* cell_atoms = reinterpret_cast<int32_t*>(base + L.cell_atoms);
+  int32_t* row_cnt = reinterpret_cast<int32_t*>(base + L.row_cnt);
+  int64_t* bsum = reinterpret_cast<int64_t*>(base + L.bsum);
+  float* bbox = reinterpret_cast<float*>(base + L.small);
+  int32_t* max_row = reinterpret_cast<int32_t*>(base + L.small + 64);
+  int64_t* rb = reinterpret_cast<int64_t*>(base + L.small + 128);
+
+  if (n == 0) {
+    E2A_HIP_CHECK(hipMemsetAsync(row_ptr, 0, sizeof(int64_t), s));
+    *n_edges = 0;
+    return E2A_OK;
+  }
+
+  // 1. bounding box and coordinate check
+  k_bbox<<<1, 256, 0, s>>>(pos, n, bbox);
+  E2A_LAUNCH_CHECK();
+  float hb[8];
+  E2A_HIP_CHECK(hipMemcpyAsync(hb, bbox, 7 * sizeof(float), hipMemcpyDeviceToHost, s));
+  E2A_HIP_CHECK(hipStreamSynchronize(s));
+  if (hb[6] != 0.0f) return fail(E2A_ERR_INVALID_ARG, "positions contain a non-finite value");
+
+  Grid g{};
+  g.periodic = box != nullptr;
+  g.rc2 = cutoff * cutoff;
+  const float side_min = cutoff * 1.001f;
+  int64_t ncell = 1;
+  for (int d = 0; d < 3; ++d) {
+    if (g.periodic) {
+      if (hb[d] < 0.0f || hb[3 + d] >= box[d])
+        return fail(E2A_ERR_INVALID_ARG, "periodic coordinate on axis %d outside [0, %g): range [%g, %g]", d,
+                    (double)box[d], (double)hb[d], (double)hb[3 + d]);
+      g.n[d] = std::max(1, static_cast<int>(floorf(box[d] / side_min)));
+      g.origin[d] = 0.0f;
+      g.box[d] = box[d];
+      g.half[d] = 0.5f * box[d];
+    } else {
+      g.n[d] = static_cast<int>(floorf((hb[3 + d] - hb[d]) / side_min)) + 1;
+      g.origin[d] = hb[d];
+    }
+  }
+  // keep the cell count within the workspace by coarsening the largest axis
+  for (;;) {
+    ncell = (int64_t)g.n[0] * g.n[1] * g.n[2];
+    if (ncell <= L.cap_cells) break;
+    int d = 0;
+    if (g.n[1] > g.n[d]) d = 1;
+    if (g.n[2] > g.n[d]) d = 2;
+    g.n[d] = std::max(1, g.n[d] / 2);
+  }
+  for (int d = 0; d < 3; ++d) {
+    float side;
+    if (g.periodic) side = box[d] / g.n[d];
+    else side = std::max(side_min, (hb[3 + d] - hb[d]) / g.n[d] * 1.0001f);
+    g.inv_side[d] = 1.0f / side;
+  }
+
+  const int tpb = 256;
+  const int64_t nblk = (n + tpb - 1) / tpb;
+  // 2. counting sort into cells
+  E2A_HIP_CHECK(hipMemsetAsync(cell_cnt, 0, sizeof(int32_t) * (ncell + 1), s));
+  E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
+  E2A_HIP_CHECK(hipMemsetAsync(max_row, 0, sizeof(int32_t), s));
+  k_bin<<<nblk, tpb, 0, s>>>(pos, n, g, cell_of, cell_cnt);
+  E2A_LAUNCH_CHECK();
+  // cell_cnt -> exclusive starts in place is not allowed (in/out alias): use cursor area? no:
+  // scan into row_cnt scratch would be too small, so scan to cell_cnt via a copy in cursor.
+  E2A_HIP_CHECK(hipMemcpyAsync(cursor, cell_cnt, sizeof(int32_t) * ncell, hipMemcpyDeviceToDevice, s));
+  {
+    e2a_status st = exclusive_scan<int32_t>(cursor, ncell, cell_cnt, bsum, s);
+    if (st != E2A_OK) return st;
+  }
+  E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
+  k_scatter<<<nblk, tpb, 0, s>>>(n, cell_of, cell_cnt, cursor, cell_atoms);
+  E2A_LAUNCH_CHECK();
+
+  // 3-4. count, scan, read back
+  k_count<<<nblk, tpb, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_cnt, max_row);
+  E2A_LAUNCH_CHECK();
+  {
+    e2a_status st = exclusive_scan<int64_t>(row_cnt, n, row_ptr, bsum, s);
+    if (st != E2A_OK) return st;
+  }
+  k_readback<<<1, 1, 0, s>>>(row_ptr, n, max_row, rb);
+  E2A_LAUNCH_CHECK();
+  int64_t hr[2];
+  E2A_HIP_CHECK(hipMemcpyAsync(hr, rb, sizeof(hr), hipMemcpyDeviceToHost, s));
+  E2A_HIP_CHECK(hipStreamSynchronize(s));
+  *n_edges = hr[0];
+  if (hr[1] > kMaxRow)
+    return fail(E2A_ERR_UNSUPPORTED, "an atom has %lld neighbours; rows longer than %d are not supported",
+                (long long)hr[1], kMaxRow);
+  if (hr[0] > cap_edges)
+    return fail(E2A_ERR_CAPACITY, "need %lld edges, col_capacity is %lld", (long long)hr[0], (long long)cap_edges);
+
+  // 5. fill and sort rows
+  k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+}  // namespace e2a

@@ -1,0 +1,213 @@
+"""Thin ctypes binding of libe2a (include/e2a.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library.
+PyTorch supplies device buffers and the current stream.  The library must be
+built in-tree first (``python -m so_graph_attention_amd.build``); importing
+this module without it raises, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libe2a.so")
+
+E2A_OK = 0
+E2A_ERR_INVALID_ARG = 1
+E2A_ERR_CAPACITY = 2
+E2A_ERR_BOX_TOO_SMALL = 3
+E2A_ERR_UNSUPPORTED = 4
+E2A_ERR_HIP = 5
+E2A_DTYPE_F32 = 0
+E2A_DTYPE_BF16 = 1
+VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
+
+# Every symbol include/e2a.h declares.
+EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
+            "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd"]
+
+
+class E2AError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+class AttnArgs(ctypes.Structure):
+    _fields_ = [
+        ("pos", ctypes.c_void_p), ("box", ctypes.c_void_p), ("n_atoms", ctypes.c_int64),
+        ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("n_edges", ctypes.c_int64),
+        ("cutoff", ctypes.c_float), ("L", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int),
+        ("n_rbf", ctypes.c_int), ("dtype", ctypes.c_int), ("variant", ctypes.c_int),
+        ("feat", ctypes.c_void_p), ("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p),
+        ("w_rad", ctypes.c_void_p), ("w_so2", ctypes.c_void_p), ("out", ctypes.c_void_p),
+        ("out_lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libe2a.so not built at {_LIB_PATH}; run `python -m so_graph_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.e2a_version.restype = ctypes.c_int
+    lib.e2a_status_string.restype = ctypes.c_char_p
+    lib.e2a_status_string.argtypes = [ctypes.c_int32]
+    lib.e2a_last_error_message.restype = ctypes.c_char_p
+    lib.e2a_neighbors_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_neighbors_workspace_bytes.argtypes = [ctypes.c_int64]
+    lib.e2a_build_neighbors.restype = ctypes.c_int32
+    lib.e2a_build_neighbors.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+    lib.e2a_so2_param_count.restype = ctypes.c_int64
+    lib.e2a_so2_param_count.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.e2a_attention_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_attention_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                  ctypes.c_int]
+    lib.e2a_attention_fwd.restype = ctypes.c_int32
+    lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    return _lib
+
+
+def e2a_version() -> int:
+    return _lib.e2a_version()
+
+
+def status_string(s: int) -> str:
+    return _lib.e2a_status_string(int(s)).decode()
+
+
+def last_error_message() -> str:
+    return _lib.e2a_last_error_message().decode()
+
+
+def e2a_so2_param_count(L: int, C: int) -> int:
+    return int(_lib.e2a_so2_param_count(L, C))
+
+
+def e2a_neighbors_workspace_bytes(n_atoms: int) -> int:
+    return int(_lib.e2a_neighbors_workspace_bytes(n_atoms))
+
+
+def e2a_attention_workspace_bytes(n_atoms: int, L: int, C: int, H: int, dtype: int) -> int:
+    return int(_lib.e2a_attention_workspace_bytes(n_atoms, L, C, H, dtype))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream if torch.cuda.is_available() else None
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int):
+    if status != E2A_OK:
+        raise E2AError(status, last_error_message())
+
+
+def _box_arg(box):
+    if box is None:
+        return None, None
+    arr = (ctypes.c_float * 3)(*[float(b) for b in box])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def e2a_build_neighbors(pos: torch.Tensor, cutoff: float, box=None, batch: Optional[torch.Tensor] = None,
+                        capacity: Optional[int] = None, stream=None):
+    """CSR radius graph (row_ptr int64 [N+1], col int32 [E]) on pos.device."""
+    _need(pos, "pos", torch.float32)
+    n = pos.shape[0]
+    dev = pos.device
+    if batch is not None:
+        _need(batch, "batch", torch.int32, dev)
+    row_ptr = torch.empty(n + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(1, e2a_neighbors_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    cap = int(capacity) if capacity is not None else max(64, 64 * n)
+    box_arr, box_p = _box_arg(box)
+    while True:
+        col = torch.empty(max(1, cap), dtype=torch.int32, device=dev)
+        ne = ctypes.c_int64(0)
+        st = _lib.e2a_build_neighbors(_ptr(pos), n, _ptr(batch), box_p, ctypes.c_float(cutoff), _ptr(row_ptr),
+                                      _ptr(col), cap, ctypes.byref(ne), _ptr(ws), ws.numel(), _stream(stream))
+        if st == E2A_ERR_CAPACITY and capacity is None:
+            cap = int(ne.value)
+            continue
+        _check(st)
+        return row_ptr, col[: ne.value]
+
+
+def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
+                      cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
+                      workspace=None, stream=None, with_lse: bool = False):
+    """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
+
+    Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
+    dev = pos.device
+    n = pos.shape[0]
+    if feat.dtype == torch.bfloat16:
+        dtype = E2A_DTYPE_BF16
+    elif feat.dtype == torch.float32:
+        dtype = E2A_DTYPE_F32
+    else:
+        raise TypeError("feat must be float32 or bfloat16")
+    _need(pos, "pos", torch.float32, dev)
+    _need(row_ptr, "row_ptr", torch.int64, dev)
+    _need(col, "col", torch.int32, dev)
+    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
+        _need(t, name, feat.dtype, dev)
+    K = (L + 1) ** 2
+    if out is None:
+        out = torch.empty((n, K, C), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    if with_lse and out_lse is None:
+        out_lse = torch.empty((n, H), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_attention_workspace_bytes(n, L, C, H, dtype)), dtype=torch.uint8,
+                                device=dev)
+    box_arr, box_p = _box_arg(box)
+    a = AttnArgs()
+    a.pos = _ptr(pos)
+    a.box = box_p
+    a.n_atoms = n
+    a.row_ptr = _ptr(row_ptr)
+    a.col = _ptr(col)
+    a.n_edges = col.numel()
+    a.cutoff = float(cutoff)
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
+    a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    _check(_lib.e2a_attention_fwd(ctypes.byref(a), _stream(stream)))
+    del box_arr
+    return (out, out_lse) if with_lse else out

@@ -1,0 +1,181 @@
+"""CPU-side checks of the C ABI: the library loads, exports what include/e2a.h
+declares, and rejects invalid calls on the host before touching a device.
+Also checks the host build of the per-edge geometry routines (edge rotation,
+Ivanic-Ruedenberg Wigner-D recursion, radial basis) against the oracle."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+import so_graph_attention_amd.e2a as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "e2a.h")
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(e2a_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declarations_are_exported():
+    names = declared_functions()
+    assert set(names) == set(B.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT\s+(e2a_\w+)", out))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(B.lib(), n)
+
+
+def test_version_and_status_strings():
+    assert B.e2a_version() == 1
+    assert B.status_string(0) == "E2A_OK"
+    assert B.status_string(2) == "E2A_ERR_CAPACITY"
+    assert B.status_string(99) == "E2A_ERR_UNKNOWN"
+
+
+def test_param_count_and_workspace_queries():
+    assert B.e2a_so2_param_count(4, 128) == 1392640
+    assert B.e2a_so2_param_count(3, 128) == 720896
+    assert B.e2a_so2_param_count(1, 16) == 1536
+    assert B.e2a_neighbors_workspace_bytes(100000) > 100000 * 12
+    assert B.e2a_attention_workspace_bytes(1000, 4, 128, 8, B.E2A_DTYPE_BF16) >= 2 * 1000 * 128 * 4
+    assert B.e2a_attention_workspace_bytes(10, 5, 128, 8, 1) == 0
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails host validation first
+
+
+def nb_call(**kw):
+    args = dict(pos=FAKE, n=10, batch=None, box=None, cutoff=5.0, row_ptr=FAKE, col=FAKE, cap=100,
+                ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    ne = ctypes.c_int64(-1)
+    box = args["box"]
+    box_p = None if box is None else ctypes.cast((ctypes.c_float * 3)(*box), ctypes.c_void_p)
+    st = B.lib().e2a_build_neighbors(args["pos"], args["n"], args["batch"], box_p, ctypes.c_float(args["cutoff"]),
+                                     args["row_ptr"], args["col"], args["cap"], ctypes.byref(ne), args["ws"],
+                                     args["ws_bytes"], None)
+    return st, B.last_error_message()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(pos=None), B.E2A_ERR_INVALID_ARG),
+    (dict(row_ptr=None), B.E2A_ERR_INVALID_ARG),
+    (dict(col=None), B.E2A_ERR_INVALID_ARG),
+    (dict(cutoff=0.0), B.E2A_ERR_INVALID_ARG),
+    (dict(cutoff=float("nan")), B.E2A_ERR_INVALID_ARG),
+    (dict(n=-1), B.E2A_ERR_INVALID_ARG),
+    (dict(cap=-5), B.E2A_ERR_INVALID_ARG),
+    (dict(ws=None), B.E2A_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), B.E2A_ERR_INVALID_ARG),
+    (dict(box=(9.0, 20.0, 20.0)), B.E2A_ERR_BOX_TOO_SMALL),
+    (dict(box=(20.0, -1.0, 20.0)), B.E2A_ERR_INVALID_ARG),
+])
+def test_build_neighbors_rejects_on_host(kw, status):
+    st, msg = nb_call(**kw)
+    assert st == status, (st, msg)
+    assert msg
+
+
+def attn_args(**kw):
+    a = B.AttnArgs()
+    a.pos = a.row_ptr = a.col = a.feat = a.w_q = a.w_k = a.w_rad = a.w_so2 = a.out = a.workspace = FAKE
+    a.n_atoms, a.n_edges, a.cutoff = 10, 20, 5.0
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = 1, 16, 1, 8, 0, 0
+    a.workspace_bytes = 1 << 30
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=16, H=3), B.E2A_ERR_INVALID_ARG),
+    (dict(L=5), B.E2A_ERR_INVALID_ARG),
+    (dict(L=-1), B.E2A_ERR_INVALID_ARG),
+    (dict(n_rbf=6), B.E2A_ERR_INVALID_ARG),
+    (dict(dtype=7), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=9), B.E2A_ERR_INVALID_ARG),
+    (dict(cutoff=-1.0), B.E2A_ERR_INVALID_ARG),
+    (dict(feat=None), B.E2A_ERR_INVALID_ARG),
+    (dict(w_so2=None), B.E2A_ERR_INVALID_ARG),
+    (dict(out=None), B.E2A_ERR_INVALID_ARG),
+    (dict(col=None), B.E2A_ERR_INVALID_ARG),
+    (dict(n_edges=-1), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=2), B.E2A_ERR_UNSUPPORTED),          # no MFMA build for L=1, C=16, fp32
+    (dict(workspace_bytes=8), B.E2A_ERR_INVALID_ARG),
+    (dict(workspace=None), B.E2A_ERR_INVALID_ARG),
+])
+def test_attention_rejects_on_host(kw, status):
+    a = attn_args(**kw)
+    st = B.lib().e2a_attention_fwd(ctypes.byref(a), None)
+    assert st == status, (st, B.last_error_message())
+    assert B.last_error_message()
+
+
+def test_attention_null_args():
+    assert B.lib().e2a_attention_fwd(None, None) == B.E2A_ERR_INVALID_ARG
+
+
+def test_binding_refuses_missing_library(tmp_path, monkeypatch):
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("e2a_copy", B.__file__)
+    mod = importlib.util.module_from_spec(spec)
+    monkeypatch.setattr(os.path, "exists", lambda p: False)
+    with pytest.raises(ImportError):
+        spec.loader.exec_module(mod)
+
+
+# ------------------------------------------------------ host geometry -------
+HOSTGEOM = os.path.join(os.path.dirname(B.library_path()), "libe2a_hostgeom.so")
+
+
+@pytest.fixture(scope="module")
+def hg():
+    return ctypes.CDLL(HOSTGEOM)
+
+
+def _cp(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def test_host_edge_rotation_matches_oracle(hg):
+    rng = np.random.default_rng(0)
+    u = rng.standard_normal((300, 3))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u[:4] = [[0, 0, 1], [0, 0, -1], [1, 0, 0], [0, -1, 0]]
+    u32 = np.ascontiguousarray(u, dtype=np.float32)
+    R = np.zeros((300, 9), dtype=np.float32)
+    hg.e2a_host_edge_rotation(_cp(u32), 300, _cp(R))
+    assert np.max(np.abs(R.reshape(-1, 3, 3) - O.edge_rotation(u32.astype(np.float64)))) < 2e-6
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_host_wigner_recursion_matches_oracle(hg, L):
+    rng = np.random.default_rng(L)
+    u = rng.standard_normal((200, 3))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u[:2] = [[0, 0, 1], [0, 0, -1]]
+    R = np.ascontiguousarray(O.edge_rotation(u), dtype=np.float32)
+    nw = sum((2 * l + 1) ** 2 for l in range(L + 1))
+    D = np.zeros((200, nw), dtype=np.float32)
+    hg.e2a_host_wigner(L, _cp(R), 200, _cp(D))
+    off = 0
+    for l in range(L + 1):
+        k = 2 * l + 1
+        want = O.wigner_d(l, R.astype(np.float64))
+        assert np.max(np.abs(D[:, off:off + k * k].reshape(-1, k, k) - want)) < 1e-6, l
+        off += k * k
+
+
+def test_host_radial_basis_matches_oracle(hg):
+    r = np.ascontiguousarray(np.linspace(0.5, 5.0, 97), dtype=np.float32)
+    e = np.zeros((97, 8), dtype=np.float32)
+    hg.e2a_host_radial_basis8(_cp(r), 97, ctypes.c_float(5.0), _cp(e))
+    assert np.max(np.abs(e - O.radial_basis(r.astype(np.float64), 5.0))) < 2e-6

@@ -1,0 +1,91 @@
+"""GPU neighbour build vs the oracle's fp32 radius graph: bit-exact CSR."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import make_config
+from workloads.generators import isolated_atom_variant
+
+from gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def B():
+    import so_graph_attention_amd.e2a as mod
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return mod
+
+
+def gpu_csr(B, w, **kw):
+    pos = torch.from_numpy(np.ascontiguousarray(w.pos)).cuda()
+    batch = None if w.batch is None else torch.from_numpy(w.batch.astype(np.int32)).cuda()
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff, box=None if w.box is None else w.box.tolist(), batch=batch, **kw)
+    torch.cuda.synchronize()
+    return rp.cpu().numpy(), col.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", ["tiny", "drug", "drug_origin", "water", "protein", "large"])
+def test_neighbors_bit_exact(B, name):
+    log(f"[neighbors] {name}")
+    w = make_config(name, C=4, H=1, L=0)
+    rp_o, col_o = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    rp_g, col_g = gpu_csr(B, w)
+    log(f"[neighbors] {name}: E oracle {col_o.size} gpu {col_g.size}")
+    assert np.array_equal(rp_g, rp_o)
+    assert np.array_equal(col_g, col_o)
+
+
+def test_neighbors_capacity_retry(B):
+    log("[neighbors] capacity")
+    w = make_config("tiny", C=4, H=1, L=0)
+    rp_o, col_o = O.neighbor_list(w.pos, w.cutoff)
+    pos = torch.from_numpy(w.pos).cuda()
+    with pytest.raises(B.E2AError) as ei:
+        B.e2a_build_neighbors(pos, w.cutoff, capacity=10)
+    assert ei.value.status == B.E2A_ERR_CAPACITY
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff)   # binding retries with the reported count
+    assert np.array_equal(col.cpu().numpy(), col_o)
+
+
+def test_neighbors_edge_cases(B):
+    log("[neighbors] edge cases")
+    # empty system
+    rp, col = B.e2a_build_neighbors(torch.zeros((0, 3), device="cuda"), 5.0)
+    assert rp.cpu().tolist() == [0] and col.numel() == 0
+    # one atom, and an isolated atom
+    rp, col = B.e2a_build_neighbors(torch.zeros((1, 3), device="cuda"), 5.0)
+    assert rp.cpu().tolist() == [0, 0]
+    w = isolated_atom_variant(make_config("tiny", C=4, H=1, L=0))
+    rp_o, col_o = O.neighbor_list(w.pos, w.cutoff)
+    rp_g, col_g = gpu_csr(B, w)
+    assert np.array_equal(rp_g, rp_o) and np.array_equal(col_g, col_o) and rp_g[-1] == rp_g[-2]
+    # periodic coordinate outside [0, box)
+    pos = torch.tensor([[1.0, 1.0, 1.0], [25.0, 1.0, 1.0]], device="cuda")
+    with pytest.raises(B.E2AError) as ei:
+        B.e2a_build_neighbors(pos, 5.0, box=[20.0, 20.0, 20.0])
+    assert ei.value.status == B.E2A_ERR_INVALID_ARG
+    with pytest.raises(B.E2AError) as ei:
+        B.e2a_build_neighbors(pos, 5.0, box=[9.0, 40.0, 40.0])
+    assert ei.value.status == B.E2A_ERR_BOX_TOO_SMALL
+    # non-finite coordinate
+    pos = torch.tensor([[1.0, float("nan"), 1.0], [2.0, 1.0, 1.0]], device="cuda")
+    with pytest.raises(B.E2AError):
+        B.e2a_build_neighbors(pos, 5.0)
+
+
+@pytest.mark.parametrize("side", [10.5, 14.0, 16.0])
+def test_neighbors_small_periodic_boxes(B, side):
+    """Boxes of 2-3 cutoffs give 1 or 2 cells per axis: the stencil must not
+    visit a cell twice."""
+    log(f"[neighbors] small box {side}")
+    rng = np.random.default_rng(int(side * 10))
+    n = int(0.1 * side ** 3)
+    pos = rng.uniform(0, side, (n, 3)).astype(np.float32)
+    pos[pos >= np.float32(side)] = 0
+    box = np.full(3, side, dtype=np.float32)
+    rp_o, col_o = O.neighbor_list_bruteforce(pos, 5.0, box)
+    rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0, box=box.tolist())
+    assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
