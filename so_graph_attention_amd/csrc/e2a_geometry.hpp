@@ -38,65 +38,71 @@ E2A_HD void edge_rotation(const float u[3], float R[3][3]) {
   R[2][0] = st * cp; R[2][1] = st * sp; R[2][2] = ct;
 }
 
+// One entry D^l[m][n] (l >= 2) of the Ivanic-Ruedenberg recursion (J. Phys.
+// Chem. 100, 6342 (1996); erratum 102, 9099 (1998)), which builds D^l from
+// D^{l-1} and D^1.  r1(i, j) returns D^1[i][j] and rp(a, b) returns
+// D^{l-1}[a][b], both with signed indices.
+template <typename R1, typename RP>
+E2A_HD float ir_entry(int l, int m, int n, const R1& r1, const RP& rp) {
+  // P(i, a, b): a in [-(l-1), l-1], b in [-l, l]
+  auto P = [&](int i, int a, int b) {
+    if (b == l) return r1(i, 1) * rp(a, l - 1) - r1(i, -1) * rp(a, 1 - l);
+    if (b == -l) return r1(i, 1) * rp(a, 1 - l) + r1(i, -1) * rp(a, l - 1);
+    return r1(i, 0) * rp(a, b);
+  };
+  const int am = m < 0 ? -m : m;
+  const int an = n < 0 ? -n : n;
+  const float d = (m == 0) ? 1.0f : 0.0f;
+  const float denom = (an == l) ? float((2 * l) * (2 * l - 1)) : float((l + n) * (l - n));
+  const float u = sqrtf(float((l + m) * (l - m)) / denom);
+  const float v = 0.5f * sqrtf((1.0f + d) * float((l + am - 1) * (l + am)) / denom) * (1.0f - 2.0f * d);
+  const float w = -0.5f * sqrtf(float((l - am - 1) * (l - am)) / denom) * (1.0f - d);
+  float acc = 0.0f;
+  if (am < l) acc += u * P(0, m, n);
+  if (m == 0) {
+    acc += v * (P(1, 1, n) + P(-1, -1, n));
+  } else if (m > 0) {
+    const float t1 = P(1, m - 1, n) * (m == 1 ? 1.41421356237f : 1.0f);
+    const float t2 = (m == 1) ? 0.0f : P(-1, 1 - m, n);
+    acc += v * (t1 - t2);
+    if (am < l - 1) acc += w * (P(1, m + 1, n) + P(-1, -m - 1, n));
+  } else {
+    const float t1 = (m == -1) ? 0.0f : P(1, m + 1, n);
+    const float t2 = P(-1, -m - 1, n) * (m == -1 ? 1.41421356237f : 1.0f);
+    acc += v * (t1 + t2);
+    if (am < l - 1) acc += w * (P(1, m - 1, n) - P(-1, -m + 1, n));
+  }
+  return acc;
+}
+
+// D^1 in the harmonic order (y, z, x) <- index m + 1, written with row stride ld.
+E2A_HD void wigner_l1(const float R[3][3], float* D1, int ld) {
+  const int p[3] = {1, 2, 0};
+  for (int a = 0; a < 3; ++a)
+    for (int b = 0; b < 3; ++b) D1[a * ld + b] = R[p[a]][p[b]];
+}
+
 // Real Wigner-D blocks D^0..D^L of rotation R, defined by Y^l(R v) = D^l Y^l(v)
 // for real harmonics without the Condon-Shortley phase stored at m = -l..l.
-// D^1 is R in (y, z, x) order; higher blocks follow the Ivanic-Ruedenberg
-// recursion (J. Phys. Chem. 100, 6342 (1996); erratum 102, 9099 (1998)),
-// which builds D^l from D^{l-1} and D^1.  Block l sits at D + wig_off(l),
-// row-major [(m + l)(2l + 1) + (n + l)].
+// D^1 is R in (y, z, x) order; higher blocks follow ir_entry.  Block l sits at
+// D + wig_off(l), row-major [(m + l)(2l + 1) + (n + l)].
 template <int L>
 E2A_HD void wigner_blocks(const float R[3][3], float* D) {
   D[0] = 1.0f;
   if (L < 1) return;
-  // (y, z, x) <- index m + 1
-  const int p[3] = {1, 2, 0};
   float* D1 = D + wig_off(1);
-#pragma unroll
-  for (int a = 0; a < 3; ++a)
-#pragma unroll
-    for (int b = 0; b < 3; ++b) D1[a * 3 + b] = R[p[a]][p[b]];
+  wigner_l1(R, D1, 3);
+  auto r1 = [&](int i, int j) { return D1[(i + 1) * 3 + (j + 1)]; };
 #pragma unroll
   for (int l = 2; l <= L; ++l) {
     const float* Dp = D + wig_off(l - 1);
     float* Dl = D + wig_off(l);
     const int wp = 2 * l - 1;
-    auto r1 = [&](int i, int j) { return D1[(i + 1) * 3 + (j + 1)]; };
     auto rp = [&](int a, int b) { return Dp[(a + l - 1) * wp + (b + l - 1)]; };
-    // P(i, a, b): a in [-(l-1), l-1], b in [-l, l]
-    auto P = [&](int i, int a, int b) {
-      if (b == l) return r1(i, 1) * rp(a, l - 1) - r1(i, -1) * rp(a, 1 - l);
-      if (b == -l) return r1(i, 1) * rp(a, 1 - l) + r1(i, -1) * rp(a, l - 1);
-      return r1(i, 0) * rp(a, b);
-    };
 #pragma unroll
-    for (int m = -l; m <= l; ++m) {
-      const int am = m < 0 ? -m : m;
-      const float d = (m == 0) ? 1.0f : 0.0f;
+    for (int m = -l; m <= l; ++m)
 #pragma unroll
-      for (int n = -l; n <= l; ++n) {
-        const int an = n < 0 ? -n : n;
-        const float denom = (an == l) ? float((2 * l) * (2 * l - 1)) : float((l + n) * (l - n));
-        const float u = sqrtf(float((l + m) * (l - m)) / denom);
-        const float v = 0.5f * sqrtf((1.0f + d) * float((l + am - 1) * (l + am)) / denom) * (1.0f - 2.0f * d);
-        const float w = -0.5f * sqrtf(float((l - am - 1) * (l - am)) / denom) * (1.0f - d);
-        float acc = 0.0f;
-        if (am < l) acc += u * P(0, m, n);
-        if (m == 0) {
-          acc += v * (P(1, 1, n) + P(-1, -1, n));
-        } else if (m > 0) {
-          const float t1 = P(1, m - 1, n) * (m == 1 ? 1.41421356237f : 1.0f);
-          const float t2 = (m == 1) ? 0.0f : P(-1, 1 - m, n);
-          acc += v * (t1 - t2);
-          if (am < l - 1) acc += w * (P(1, m + 1, n) + P(-1, -m - 1, n));
-        } else {
-          const float t1 = (m == -1) ? 0.0f : P(1, m + 1, n);
-          const float t2 = P(-1, -m - 1, n) * (m == -1 ? 1.41421356237f : 1.0f);
-          acc += v * (t1 + t2);
-          if (am < l - 1) acc += w * (P(1, m - 1, n) - P(-1, -m + 1, n));
-        }
-        Dl[(m + l) * (2 * l + 1) + (n + l)] = acc;
-      }
-    }
+      for (int n = -l; n <= l; ++n) Dl[(m + l) * (2 * l + 1) + (n + l)] = ir_entry(l, m, n, r1, rp);
   }
 }
 

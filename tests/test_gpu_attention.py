@@ -100,3 +100,32 @@ def test_reference_kernel_bf16_configs_sampled(B, name):
     err = rel_l2(out[dest], want)
     log(f"[attn] reference {name} rel-L2 {err:.3e} on {dest.size} atoms")
     assert err <= TOL_F32
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_mfma_kernel_tiny_geometry_full_output(B, L):
+    """C = 128, H = 8, bf16: every output of a 64-atom system (rows of 11-36
+    neighbours: one or two 32-edge chunks with ragged tails)."""
+    log(f"[attn] mfma tiny-geometry L={L}")
+    w, rp, col, d = setup(B, "tiny", L=L, C=128, H=8, dtype="bf16")
+    out, lse = run_gpu(B, w, d, "mfma")
+    want, want_lse = oracle_out(w, rp, col, None)
+    err = rel_l2(out, want)
+    log(f"[attn] mfma L={L} rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL_BF16
+    assert np.max(np.abs(lse - want_lse)) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["drug", "drug_origin", "water", "protein", "large"])
+def test_mfma_kernel_full_configs_sampled(B, name):
+    log(f"[attn] mfma {name}")
+    w, rp, col, d = setup(B, name)
+    out, lse = run_gpu(B, w, d, "auto")
+    assert np.all(np.isfinite(out))
+    dest = sample_dest(rp, 64, seed=11)
+    want, want_lse = oracle_out(w, rp, col, dest)
+    err = rel_l2(out[dest], want)
+    log(f"[attn] mfma {name} rel-L2 {err:.3e} on {dest.size} atoms")
+    assert err <= TOL_BF16
+    assert np.max(np.abs(lse[dest] - want_lse)) <= 1e-4
