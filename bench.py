@@ -1,0 +1,204 @@
+#!/usr/bin/env python
+"""Benchmark of the on-the-fly equivariant attention layer on one MI355X.
+
+One step is one pass of the whole hot path over the 100k-atom system: the
+cell-list neighbour build (e2a_build_neighbors) and the fused layer
+(e2a_attention_fwd: q/k prologue, weight packing, fused MFMA kernel).  Inputs
+are resident in device memory before timing starts.  The headline value is
+neighbour edges per second of the whole step; the fused kernel's own time,
+measured with HIP events on the stream it runs on, gives the roofline block.
+The fp64 oracle is timed on the host's cores on a bounded sample of
+destination atoms as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "neighbour edges/sec per attention layer (1 MI355X); achieved TFLOPS % of roofline"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_large_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "so_graph_attention_amd", "csrc", "attention_mfma.hip")
+
+
+def progress(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def flops_per_edge(L, C):
+    """Algorithmic work per edge: SO(2) mix 2[(L+1)^2 + 4 sum_{m>=1} (L+1-m)^2] C^2,
+    rotations in and out 4 sum_l (2l+1)^2 C, radial 2*8*(L+1) C, accumulate
+    2 (L+1)^2 C, logits 2 C."""
+    so2 = 2 * ((L + 1) ** 2 + 4 * sum((L + 1 - m) ** 2 for m in range(1, L + 1))) * C * C
+    rot = 4 * sum((2 * l + 1) ** 2 for l in range(L + 1)) * C
+    rad = 2 * 8 * (L + 1) * C
+    accum = 2 * (L + 1) ** 2 * C
+    return so2 + rot + rad + accum + 2 * C
+
+
+def traffic_per_launch():
+    """Measured HBM bytes per launch of the fused kernel from the committed
+    rocprofv3 counter summary, or None when the kernel source changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        m = re.match(r"^\s*([a-z_]+)\s*:\s*(\S+)", line)
+        if m:
+            kv[m.group(1)] = m.group(2)
+    import hashlib
+    sha = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    if kv.get("kernel_source_sha") != sha or "hbm_bytes_per_launch" not in kv:
+        return None
+    return float(kv["hbm_bytes_per_launch"])
+
+
+def cpu_baseline(w, rp, col, seconds):
+    """The oracle as it stands on a seeded sample of destination atoms, grown in
+    batches of 32 until about `seconds` of CPU time have been spent."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    feat = w.as_f32("feat")
+    args = (rp, col, feat, w.as_f32("w_q"), w.as_f32("w_k"), w.as_f32("w_rad"), w.as_f32("w_so2"),
+            w.L, w.C, w.H, w.cutoff)
+    order = np.random.default_rng(2024).permutation(w.n_atoms)
+    done = 0
+    edges = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and done < w.n_atoms:
+        dest = np.sort(order[done:done + 32])
+        O.attention(w.pos, *args, box=w.box, dest=dest)
+        edges += int((rp[dest + 1] - rp[dest]).sum())
+        done += dest.size
+    dt = time.perf_counter() - t0
+    return {"value": edges / dt, "unit": "edges/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} seeded destination atoms ({edges} edges) of the same 100k-atom workload, "
+                      f"{dt:.1f} s of fp64 NumPy on {threads} BLAS threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="large")
+    ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "reference"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import so_graph_attention_amd.e2a as B
+    from workloads import make_config
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    progress(f"generating workload {args.config}")
+    w = make_config(args.config)
+    box = None if w.box is None else w.box.tolist()
+
+    def stored(name):
+        a = getattr(w, name)
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    pos = torch.from_numpy(w.pos).to(dev)
+    batch = None if w.batch is None else torch.from_numpy(w.batch.astype(np.int32)).to(dev)
+    feat, w_q, w_k, w_rad, w_so2 = (stored(n) for n in ("feat", "w_q", "w_k", "w_rad", "w_so2"))
+    n = w.n_atoms
+    K = (w.L + 1) ** 2
+    dtype_code = B.E2A_DTYPE_BF16 if w.dtype == "bf16" else B.E2A_DTYPE_F32
+    out = torch.empty((n, K, w.C), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.e2a_attention_workspace_bytes(n, w.L, w.C, w.H, dtype_code), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch)
+    n_edges = int(col.numel())
+    progress(f"{n} atoms, {n_edges} edges; warmup {args.warmup}")
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        r, c = B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch, capacity=n_edges)
+        if ev is not None:
+            ev[1].record(stream)
+        B.e2a_attention_fwd(pos, r, c, feat, w_q, w_k, w_rad, w_so2, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff,
+                            box=box, variant=args.variant, out=out, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    progress(f"timing {args.steps} steps")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    nb_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    progress(f"step {ms_step:.3f} ms (neighbours {nb_ms:.3f} ms, attention {attn_ms:.3f} ms)")
+
+    f_edge = flops_per_edge(w.L, w.C)
+    achieved = f_edge * n_edges / (attn_ms * 1e-3) / 1e12
+    traffic = traffic_per_launch()
+    result = {
+        "metric": METRIC,
+        "value": n_edges / (ms_step * 1e-3),
+        "unit": "edges/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{args.config}: {n} atoms, "
+                               + ("periodic box %.3g A" % w.box[0] if w.box is not None else "open boundaries")
+                               + f", cutoff {w.cutoff:g} A, L={w.L}, C={w.C}, H={w.H}, {w.dtype} storage",
+                   "n_atoms": n, "n_edges": n_edges, "L": w.L, "C": w.C, "H": w.H,
+                   "variant": args.variant},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "kernel": "e2a_attention_fwd (fused MFMA kernel + q/k prologue + weight pack)",
+                     "flop_per_edge": f_edge},
+        "breakdown": {"neighbors_ms": nb_ms, "attention_ms": attn_ms,
+                      "attention_edges_per_s": n_edges / (attn_ms * 1e-3)},
+    }
+    if not args.no_cpu_baseline:
+        progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
+        rp_h = rp.cpu().numpy()
+        col_h = col.cpu().numpy()
+        result["cpu_baseline"] = cpu_baseline(w, rp_h, col_h, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

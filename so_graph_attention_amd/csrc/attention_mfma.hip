@@ -34,6 +34,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kC = 128;      // channels
@@ -121,6 +122,30 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, cons
 __device__ __forceinline__ f32x16 mfma_f16(const f16x8 a, const f16x8 b, const f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16_f16(const f16x8 a, const f16x8 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+// Node accumulator of one degree lo for this wave's 32 channels: two 16x16
+// MFMA tiles (rows n = 0..15 >= 2 lo + 1, columns = channels 0-15 and 16-31
+// of the wave).  Lane l holds rows 4 (l / 16) + r, column l % 16.
+struct NodeAcc {
+  f32x4 a;   // channels 32 w + 0..15
+  f32x4 b;   // channels 32 w + 16..31
+};
+
+// Rotate-out contraction step: acc[n][c] += sum_k G[n][k] U[k][c] over the 16
+// (edge, sign) slots this k-step carries.  The 32x32 GEMM result gives lane l
+// the values of channel l % 32 for 8 edges (lanes 0-31 and 32-63 hold
+// different edges).  In the 16x16x32 MFMA, k-slot group g = l / 16 comes from
+// lanes 16 g .. 16 g + 15: groups 0 and 2 carry channels 0-15, groups 1 and 3
+// channels 16-31, so each of the two MFMAs keeps its own groups and zeroes
+// the others.  G (the D rows) is the same register for both.
+__device__ __forceinline__ void rotate_out_step(NodeAcc& acc, const f16x8 g, const f16x8 u, bool grp_odd) {
+  const f16x8 zero = {};
+  acc.a = mfma16_f16(g, grp_odd ? zero : u, acc.a);
+  acc.b = mfma16_f16(g, grp_odd ? u : zero, acc.b);
+}
 
 // Row of a 32x32 MFMA result held by accumulator register r of a lane in
 // half h (lanes 0-31: h = 0, lanes 32-63: h = 1); the column is lane % 32.
@@ -135,6 +160,9 @@ struct MfmaParams {
   const uint16_t* feat;
   const bf16x8* wpk;
   const f16x8* radpk;
+  const int32_t* order;   // destination atoms in spatial (Morton) order
+  int64_t n_atoms;
+  int64_t per_xcd;        // ceil(n_atoms / 8)
   float* out;
   float* out_lse;
   float box[3];
@@ -156,39 +184,43 @@ struct Smem {
 };
 
 // Rotate the chunk's neighbour features into the edge frames and write the
-// GEMM operand of block M (bf16, padded rows) to LDS.
-template <int L, int M>
-__device__ __forceinline__ void build_a(const MfmaParams& p, const Smem& s, int tid) {
+// GEMM operand of block M (bf16, padded rows) to LDS: for each degree l >= M,
+// x_{l,+-M}[c] = sum_n D^l[l +- M][n] h_j[l*l + n][c].  Thread t owns channel
+// group t % 16 (8 channels) of edges t / 16 and t / 16 + 16; the 2l+1
+// feature loads of an edge are in flight before the first multiply.
+template <int L, int M, int l>
+__device__ __forceinline__ void build_a_l(const MfmaParams& p, const Smem& s, int tid) {
   using S = Shape<L>;
-  constexpr int NL = L + 1 - M;
+  constexpr int W = 2 * l + 1;
   constexpr int stride = S::astride(M);
-  tid = opaque(tid);
+  const int g = tid & 15;
 #pragma unroll 1
-  for (int t = tid; t < kET * NL * 16; t += kThreads) {
-    const int g = t & 15;
-    const int el = t >> 4;
-    const int e = el / NL;
-    const int l = M + el % NL;
+  for (int h = 0; h < 2; ++h) {
+    const int e = (tid >> 4) + 16 * h;
     const uint16_t* hp = p.feat + ((int64_t)s.j[e] * S::K + l * l) * kC + 8 * g;
+    uint4 raw[W];
+#pragma unroll
+    for (int n = 0; n < W; ++n) raw[n] = *reinterpret_cast<const uint4*>(hp + n * kC);
     const float* De = s.D + e * S::DSZ + doff(l);
     const float* Dp = De + (l + M) * dpad(l);
     const float* Dm = De + (l - M) * dpad(l);
     float xp[8], xm[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) { xp[q] = 0.0f; xm[q] = 0.0f; }
-    for (int n = 0; n < 2 * l + 1; ++n) {
+#pragma unroll
+    for (int n = 0; n < W; ++n) {
       float hv[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(hp + n * kC), hv);
+      unpack_bf16x8(raw[n], hv);
       const float dp = Dp[n];
 #pragma unroll
       for (int q = 0; q < 8; ++q) xp[q] += dp * hv[q];
-      if (M > 0) {
+      if constexpr (M > 0) {
         const float dm = Dm[n];
 #pragma unroll
         for (int q = 0; q < 8; ++q) xm[q] += dm * hv[q];
       }
     }
-    if (M == 0) {
+    if constexpr (M == 0) {
       *reinterpret_cast<bf16x8*>(s.A + e * stride + l * kC + 8 * g) = to_vec8<bf16x8>(xp);
     } else {
       const int row = 32 * (e >> 4) + (e & 15);
@@ -197,6 +229,13 @@ __device__ __forceinline__ void build_a(const MfmaParams& p, const Smem& s, int 
       *reinterpret_cast<bf16x8*>(s.A + (row + 16) * stride + colk) = to_vec8<bf16x8>(xm);
     }
   }
+  if constexpr (l < L) build_a_l<L, M, l + 1>(p, s, tid);
+}
+
+template <int L, int M>
+__device__ __forceinline__ void build_a(const MfmaParams& p, const Smem& s, int tid) {
+  static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
+  build_a_l<L, M, M>(p, s, opaque(tid));
 }
 
 // A operand of the rotate-out contraction: row n of D^l rows `mrow`, for the
@@ -211,68 +250,153 @@ __device__ __forceinline__ f16x8 dt_frag(const _Float16* row_base, int eg, int h
   return v;
 }
 
+// 16-byte load of a B fragment through a buffer resource: the per-lane offset
+// stays in one VGPR and the k-step advances a scalar offset.
+__device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // GEMM of block M for this wave's 32 output channels, then the epilogue:
 // y_{+-m} from the W1/W2 products, u = alpha * rho * y (rho from one MFMA
 // against the radial basis), and the partial rotate-out
 // acc_lo[n][c] += sum_{edges, +-} D^lo[lo +- M][n] u_{+-}[c], itself an MFMA
 // contraction over the chunk's edges.
+//
+// The K loops are software-pipelined by hand: weight fragments are loaded
+// kPre k-steps before use and A fragments one step before, and a scheduling
+// barrier after every k-step keeps the compiler from sinking the loads back
+// next to their MFMAs (which would expose the full L2 latency each step).
 template <int L, int M>
-__device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, int lane, int wave,
-                                          const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                          f32x16 (&nacc)[L + 1]) {
+__device__ __forceinline__ void epilogue_m0(const Smem& s, int lo, const f32x16& c0, const f16x8& arbf0,
+                                            const f16x8& brad, const float (&alpha)[16], int half, int n,
+                                            bool grp_odd, NodeAcc& acc) {
+  const f32x16 rho = mfma_f16(arbf0, brad, f32x16{});
+  float u[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) u[r] = alpha[r] * rho[r] * c0[r];
+  const bool nvalid = n < 2 * lo + 1;
+  const _Float16* drow = s.DT + wig_off(lo) * kET + (lo * (2 * lo + 1) + n) * kET;
+  rotate_out_step(acc, dt_frag(drow, 0, half, nvalid), to_vec8<f16x8>(u), grp_odd);
+  rotate_out_step(acc, dt_frag(drow, 16, half, nvalid), to_vec8<f16x8>(u + 8), grp_odd);
+}
+
+// |m| = 0: output blocks lo0 and lo0 + 1 (when present) share each A fragment.
+template <int L, int LO0>
+__device__ __forceinline__ void gemm_m0(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int lane,
+                                        int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
+                                        NodeAcc (&nacc)[L + 1]) {
   using S = Shape<L>;
+  constexpr int M = 0;
   constexpr int KS = S::km(M) / 16;
   constexpr int stride = S::astride(M);
-  const f16x8 zero8 = {};
+  constexpr bool two = LO0 + 1 <= L;
+  constexpr int kPre = two ? 8 : 12;
+  const int half = lane >> 5;
+  const int c_own = 32 * wave + (lane & 31);
+  const int voff = lane * 16;
+  const uint16_t* ap = s.A + (lane & 31) * stride + 8 * half;
+  const int sb0 = static_cast<int>((S::woff(M) + (int64_t)((LO0 - M) * 4 + wave) * S::wblock(M)) * 16);
+  const int sb1 = static_cast<int>((S::woff(M) + (int64_t)((LO0 + 1 - M) * 4 + wave) * S::wblock(M)) * 16);
+  f32x16 c0 = {}, c1 = {};
+  bf16x8 r0[kPre], r1[kPre];
 #pragma unroll
-  for (int lo = M; lo <= L; ++lo) {
-    lane = opaque(lane);
+  for (int q = 0; q < kPre; ++q) {
+    r0[q] = load_b(wrsrc, voff, sb0 + q * 1024);
+    if constexpr (two) r1[q] = load_b(wrsrc, voff, sb1 + q * 1024);
+  }
+  bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
+#pragma unroll
+  for (int st = 0; st < KS; ++st) {
+    const int q = st % kPre;
+    const bf16x8 b0 = r0[q];
+    bf16x8 b1 = {};
+    if constexpr (two) b1 = r1[q];
+    if (st + kPre < KS) {
+      r0[q] = load_b(wrsrc, voff, sb0 + (st + kPre) * 1024);
+      if constexpr (two) r1[q] = load_b(wrsrc, voff, sb1 + (st + kPre) * 1024);
+    }
+    bf16x8 an = a;
+    if (st + 1 < KS) an = *reinterpret_cast<const bf16x8*>(ap + (st + 1) * 16);
+    c0 = mfma_bf16(a, b0, c0);
+    if constexpr (two) c1 = mfma_bf16(a, b1, c1);
+    a = an;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int n = lane & 15;
+  const bool grp_odd = (lane >> 4) & 1;
+  const f16x8 zero8 = {};
+  {
+    const f16x8 brad = half == 0 ? p.radpk[LO0 * kC + c_own] : zero8;
+    epilogue_m0<L, M>(s, LO0, c0, arbf[0], brad, alpha, half, n, grp_odd, nacc[LO0]);
+  }
+  if constexpr (two) {
+    const f16x8 brad = half == 0 ? p.radpk[(LO0 + 1) * kC + c_own] : zero8;
+    epilogue_m0<L, M>(s, LO0 + 1, c1, arbf[0], brad, alpha, half, n, grp_odd, nacc[LO0 + 1]);
+  }
+  if constexpr (LO0 + 2 <= L) gemm_m0<L, LO0 + 2>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
+}
+
+template <int L, int M>
+__device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc,
+                                          int lane, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
+                                          NodeAcc (&nacc)[L + 1]) {
+  using S = Shape<L>;
+  lane = opaque(lane);
+  if constexpr (M == 0) {
+    gemm_m0<L, 0>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
+  } else {
+    constexpr int KS = S::km(M) / 16;
+    constexpr int stride = S::astride(M);
+    constexpr int kPre = 6;
     const int half = lane >> 5;
     const int c_own = 32 * wave + (lane & 31);
-    const int row = lane & 31;
-    const int kof = 8 * half;
-    const bf16x8* bp = p.wpk + S::woff(M) + (int64_t)((lo - M) * 4 + wave) * S::wblock(M) + lane;
-    const f16x8 brad = half == 0 ? p.radpk[lo * kC + c_own] : zero8;
-    const int n = row;
-    const bool nvalid = n < 2 * lo + 1;
-    const _Float16* dt_lo = s.DT + wig_off(lo) * kET;
-    if (M == 0) {
-      f32x16 c0 = {};
-      const uint16_t* ap = s.A + row * stride + kof;
-#pragma unroll 2
-      for (int st = 0; st < KS; ++st) {
-        const bf16x8 b = bp[st * 64];
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ap + st * 16);
-        c0 = mfma_bf16(a, b, c0);
-      }
-      const f32x16 rho = mfma_f16(arbf[0], brad, f32x16{});
-      float u[16];
+    const int n = lane & 15;                 // D row of the rotate-out A operand
+    const bool grp_odd = (lane >> 4) & 1;    // lane group 1 or 3: channels 16-31
+    const int voff = lane * 16;
+    const f16x8 zero8 = {};
+    const uint16_t* ap0 = s.A + (lane & 31) * stride + 8 * half;
+    const uint16_t* ap1 = ap0 + 32 * stride;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) u[r] = alpha[r] * rho[r] * c0[r];
-      const _Float16* drow = dt_lo + (lo * (2 * lo + 1) + n) * kET;
-      nacc[lo] = mfma_f16(dt_frag(drow, 0, half, nvalid), to_vec8<f16x8>(u), nacc[lo]);
-      nacc[lo] = mfma_f16(dt_frag(drow, 16, half, nvalid), to_vec8<f16x8>(u + 8), nacc[lo]);
-    } else {
+    for (int lo = M; lo <= L; ++lo) {
+      const int sblk = static_cast<int>((S::woff(M) + (int64_t)((lo - M) * 4 + wave) * S::wblock(M)) * 16);
       f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
-      const uint16_t* ap0 = s.A + row * stride + kof;
-      const uint16_t* ap1 = ap0 + 32 * stride;
-#pragma unroll 2
+      bf16x8 b1r[kPre], b2r[kPre];
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) {
+        b1r[q] = load_b(wrsrc, voff, sblk + q * 2048);
+        b2r[q] = load_b(wrsrc, voff, sblk + q * 2048 + 1024);
+      }
+      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0);
+      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap1);
+#pragma unroll
       for (int st = 0; st < KS; ++st) {
-        const bf16x8 b1 = bp[(2 * st) * 64];
-        const bf16x8 b2 = bp[(2 * st + 1) * 64];
-        const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0 + st * 16);
-        const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap1 + st * 16);
+        const int q = st % kPre;
+        const bf16x8 b1 = b1r[q], b2 = b2r[q];
+        if (st + kPre < KS) {
+          b1r[q] = load_b(wrsrc, voff, sblk + (st + kPre) * 2048);
+          b2r[q] = load_b(wrsrc, voff, sblk + (st + kPre) * 2048 + 1024);
+        }
+        bf16x8 a0n = a0, a1n = a1;
+        if (st + 1 < KS) {
+          a0n = *reinterpret_cast<const bf16x8*>(ap0 + (st + 1) * 16);
+          a1n = *reinterpret_cast<const bf16x8*>(ap1 + (st + 1) * 16);
+        }
         c00 = mfma_bf16(a0, b1, c00);
         c01 = mfma_bf16(a0, b2, c01);
         c10 = mfma_bf16(a1, b1, c10);
         c11 = mfma_bf16(a1, b2, c11);
+        a0 = a0n;
+        a1 = a1n;
+        __builtin_amdgcn_sched_barrier(0);
       }
+      const f16x8 brad = half == 0 ? p.radpk[lo * kC + c_own] : zero8;
+      const bool nvalid = n < 2 * lo + 1;
+      const _Float16* dt_lo = s.DT + wig_off(lo) * kET;
       const _Float16* drow_p = dt_lo + ((lo + M) * (2 * lo + 1) + n) * kET;
       const _Float16* drow_m = dt_lo + ((lo - M) * (2 * lo + 1) + n) * kET;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const f32x16 C1 = t == 0 ? c00 : c10;
-        const f32x16 C2 = t == 0 ? c01 : c11;
+      auto tile = [&](int t, const f32x16& C1, const f32x16& C2) {
         const f32x16 rho = mfma_f16(arbf[1 + t], brad, f32x16{});
         float up[8], um[8];
 #pragma unroll
@@ -281,22 +405,52 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, in
           up[r] = sc * (C1[r] - C2[r + 8]);
           um[r] = sc * (C2[r] + C1[r + 8]);
         }
-        nacc[lo] = mfma_f16(dt_frag(drow_p, 16 * t, half, nvalid), to_vec8<f16x8>(up), nacc[lo]);
-        nacc[lo] = mfma_f16(dt_frag(drow_m, 16 * t, half, nvalid), to_vec8<f16x8>(um), nacc[lo]);
-      }
+        rotate_out_step(nacc[lo], dt_frag(drow_p, 16 * t, half, nvalid), to_vec8<f16x8>(up), grp_odd);
+        rotate_out_step(nacc[lo], dt_frag(drow_m, 16 * t, half, nvalid), to_vec8<f16x8>(um), grp_odd);
+      };
+      tile(0, c00, c01);
+      tile(1, c10, c11);
     }
   }
 }
 
+// D^l for l = 2..L of all chunk edges, one (edge, row) per thread and level.
+template <int L, int l>
+__device__ __forceinline__ void wig_level(const Smem& s, int tid) {
+  using S = Shape<L>;
+  constexpr int w = 2 * l + 1;
+#pragma unroll 1
+  for (int t = opaque(tid); t < kET * w; t += kThreads) {
+    const int e = t / w, mi = t % w;
+    float* De = s.D + e * S::DSZ;
+    float r1[3][3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a)
+#pragma unroll
+      for (int b = 0; b < 3; ++b) r1[a][b] = De[doff(1) + a * dpad(1) + b];
+    const float* Dp = De + doff(l - 1);
+    auto rp = [&](int a) { return Dp + (a + l - 1) * dpad(l - 1); };
+    float out[w];
+    ir_row<l>(mi - l, r1, rp, out);
+#pragma unroll
+    for (int n = 0; n < w; ++n) {
+      De[doff(l) + mi * dpad(l) + n] = out[n];
+      s.DT[(wig_off(l) + mi * w + n) * kET + e] = static_cast<_Float16>(out[n]);
+    }
+  }
+  __syncthreads();
+  if constexpr (l < L) wig_level<L, l + 1>(s, tid);
+}
+
 template <int L, int M>
-__device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, int tid, int lane, int wave,
-                                         const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                         f32x16 (&nacc)[L + 1]) {
+__device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid,
+                                         int lane, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
+                                         NodeAcc (&nacc)[L + 1]) {
   build_a<L, M>(p, s, tid);
   __syncthreads();
-  mma_block<L, M>(p, s, lane, wave, arbf, alpha, nacc);
+  mma_block<L, M>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
   __syncthreads();
-  if constexpr (M < L) do_block<L, M + 1>(p, s, tid, lane, wave, arbf, alpha, nacc);
+  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, lane, wave, arbf, alpha, nacc);
 }
 
 template <int L>
@@ -316,14 +470,22 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
   s.l_run = s.m_run + kH;
   s.scale = s.l_run + kH;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16x8*>(p.wpk), (short)0, static_cast<int>(S::wtotal() * 16), 0x00020000);
+  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD one
+  // contiguous stretch of the spatial order so that neighbouring destinations
+  // (which share most neighbours) run on the same L2.
+  const int64_t slot = (int64_t)(blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  if (slot >= p.n_atoms) return;
+  const int64_t i = p.order[slot];
 
   if (tid < kC) s.q[tid] = p.q[i * kC + tid];
   if (tid < kH) { s.m_run[tid] = -INFINITY; s.l_run[tid] = 0.0f; }
-  f32x16 nacc[L + 1];
+  NodeAcc nacc[L + 1];
 #pragma unroll
-  for (int l = 0; l <= L; ++l) nacc[l] = f32x16{};
+  for (int l = 0; l <= L; ++l) nacc[l] = NodeAcc{f32x4{}, f32x4{}};
   const float xi[3] = {p.pos[3 * i], p.pos[3 * i + 1], p.pos[3 * i + 2]};
   const int64_t e_beg = p.row_ptr[i], e_end = p.row_ptr[i + 1];
 
@@ -405,25 +567,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
       s.m_run[h] = mx;
       s.scale[h] = sc;
     }
-#pragma unroll
-    for (int l = 2; l <= L; ++l) {
-      const int w = 2 * l + 1;
-#pragma unroll 1
-      for (int t = opaque(tid); t < kET * w * w; t += kThreads) {
-        const int e = t / (w * w), idx = t % (w * w);
-        const int mi = idx / w, ni = idx % w;
-        float* De = s.D + e * S::DSZ;
-        const float* D1 = De + doff(1);
-        const float* Dp = De + doff(l - 1);
-        const int pp = dpad(l - 1);
-        auto r1 = [&](int a, int b) { return D1[(a + 1) * dpad(1) + (b + 1)]; };
-        auto rp = [&](int a, int b) { return Dp[(a + l - 1) * pp + (b + l - 1)]; };
-        const float v = ir_entry(l, mi - l, ni - l, r1, rp);
-        De[doff(l) + mi * dpad(l) + ni] = v;
-        s.DT[(wig_off(l) + idx) * kET + e] = static_cast<_Float16>(v);
-      }
-      __syncthreads();
-    }
+    if constexpr (L >= 2) wig_level<L, 2>(s, tid);
     __syncthreads();
     // per-lane constants of this chunk: attention weights of the 16 edges
     // whose rows this lane holds, the radial-basis A operands, and the
@@ -436,29 +580,36 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
       const int h_own = (32 * wave + (ln & 31)) / kDH;
 #pragma unroll
       for (int r = 0; r < 16; ++r) alpha[r] = s.alpha[crow(r, half) * kH + h_own];
-      const float sc = s.scale[h_own];
+      // the wave's 32 channels are heads 2w and 2w+1
+      const float sa = s.scale[2 * wave], sb = s.scale[2 * wave + 1];
 #pragma unroll
-      for (int l = 0; l <= L; ++l) nacc[l] *= sc;
+      for (int l = 0; l <= L; ++l) {
+        nacc[l].a *= sa;
+        nacc[l].b *= sb;
+      }
       float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       const int r = ln & 31;
       arbf[0] = to_vec8<f16x8>(half == 0 ? s.rbf + r * 8 : z);
       arbf[1] = to_vec8<f16x8>(half == 0 ? s.rbf + (r & 15) * 8 : z);
       arbf[2] = to_vec8<f16x8>(half == 0 ? s.rbf + (16 + (r & 15)) * 8 : z);
     }
-    do_block<L, 0>(p, s, tid, lane, wave, arbf, alpha, nacc);
+    do_block<L, 0>(p, s, wrsrc, tid, lane, wave, arbf, alpha, nacc);
   }
   __syncthreads();
   {
-    const int half = lane >> 5;
-    const int c_own = 32 * wave + (lane & 31);
-    const float l = s.l_run[c_own / kDH];
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    const int c0 = 32 * wave + (lane & 15);
+    const float la = s.l_run[2 * wave], lb = s.l_run[2 * wave + 1];
+    const float ia = la > 0.0f ? 1.0f / la : 0.0f, ib = lb > 0.0f ? 1.0f / lb : 0.0f;
 #pragma unroll
     for (int lo = 0; lo <= L; ++lo)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = crow(r, half);
-        if (n < 2 * lo + 1) p.out[(i * K + lo * lo + n) * kC + c_own] = nacc[lo][r] * inv;
+      for (int r = 0; r < 4; ++r) {
+        const int n = 4 * (lane >> 4) + r;
+        if (n < 2 * lo + 1) {
+          float* o = p.out + (i * K + lo * lo + n) * kC + c0;
+          o[0] = nacc[lo].a[r] * ia;
+          o[16] = nacc[lo].b[r] * ib;
+        }
       }
   }
   if (p.out_lse && tid < kH)
@@ -508,17 +659,118 @@ __global__ void k_pack_rad(const uint16_t* __restrict__ w, f16x8* __restrict__ o
   out[v] = to_vec8<f16x8>(vals);
 }
 
-template <int L>
-size_t packed_bytes() {
-  return align_up(Shape<L>::wtotal() * 16, 256) + align_up((L + 1) * kC * 16, 256);
+constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
+constexpr int kOrderBins = 1 << (3 * kOrderBits);
+
+__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
+  __shared__ float smin[3][256], smax[3][256];
+  float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      mn[d] = fminf(mn[d], pos[3 * i + d]);
+      mx[d] = fmaxf(mx[d], pos[3 * i + d]);
+    }
+  for (int d = 0; d < 3; ++d) { smin[d][threadIdx.x] = mn[d]; smax[d][threadIdx.x] = mx[d]; }
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st)
+      for (int d = 0; d < 3; ++d) {
+        smin[d][threadIdx.x] = fminf(smin[d][threadIdx.x], smin[d][threadIdx.x + st]);
+        smax[d][threadIdx.x] = fmaxf(smax[d][threadIdx.x], smax[d][threadIdx.x + st]);
+      }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0)
+    for (int d = 0; d < 3; ++d) { out[d] = smin[d][0]; out[3 + d] = smax[d][0]; }
 }
+
+__device__ __forceinline__ uint32_t spread3(uint32_t v) {
+  uint32_t r = 0;
+#pragma unroll
+  for (int b = 0; b < kOrderBits; ++b) r |= ((v >> b) & 1u) << (3 * b);
+  return r;
+}
+
+__global__ void k_ord_keys(const float* __restrict__ pos, int64_t n, const float* __restrict__ bbox,
+                           int32_t* __restrict__ key, int32_t* __restrict__ bins) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  uint32_t c[3];
+#pragma unroll
+  for (int d = 0; d < 3; ++d) {
+    const float ext = fmaxf(bbox[3 + d] - bbox[d], 1e-6f);
+    float f = (pos[3 * i + d] - bbox[d]) / ext * float(1 << kOrderBits);
+    f = fminf(fmaxf(f, 0.0f), float((1 << kOrderBits) - 1));
+    c[d] = static_cast<uint32_t>(f);
+  }
+  const int32_t k = static_cast<int32_t>(spread3(c[0]) | (spread3(c[1]) << 1) | (spread3(c[2]) << 2));
+  key[i] = k;
+  atomicAdd(&bins[k], 1);
+}
+
+__global__ void k_ord_scatter(int64_t n, const int32_t* __restrict__ key, const int32_t* __restrict__ start,
+                              int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int k = key[i];
+  order[start[k] + atomicAdd(&cursor[k], 1)] = static_cast<int32_t>(i);
+}
+
+struct MfmaWs {
+  size_t w, rad, order, key, bins, cursor, bsum, bbox, total;
+};
+
+template <int L>
+MfmaWs mfma_ws_layout(int64_t n) {
+  using S = Shape<L>;
+  MfmaWs m{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  m.w = take(S::wtotal() * 16);
+  m.rad = take((L + 1) * kC * 16);
+  m.order = take(sizeof(int32_t) * n);
+  m.key = take(sizeof(int32_t) * n);
+  m.bins = take(sizeof(int32_t) * (kOrderBins + 1));
+  m.cursor = take(sizeof(int32_t) * kOrderBins);
+  m.bsum = take(sizeof(int64_t) * scan_bsum_count(kOrderBins));
+  m.bbox = take(8 * sizeof(float));
+  m.total = off;
+  return m;
+}
+
 
 template <int L>
 e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   using S = Shape<L>;
   const e2a_attn_args* a = pl.a;
-  bf16x8* wpk = static_cast<bf16x8*>(pl.w_packed);
-  f16x8* radpk = reinterpret_cast<f16x8*>(static_cast<char*>(pl.w_packed) + align_up(S::wtotal() * 16, 256));
+  const MfmaWs W = mfma_ws_layout<L>(a->n_atoms);
+  char* wb = static_cast<char*>(pl.mfma_ws);
+  bf16x8* wpk = reinterpret_cast<bf16x8*>(wb + W.w);
+  f16x8* radpk = reinterpret_cast<f16x8*>(wb + W.rad);
+  int32_t* order = reinterpret_cast<int32_t*>(wb + W.order);
+  int32_t* key = reinterpret_cast<int32_t*>(wb + W.key);
+  int32_t* bins = reinterpret_cast<int32_t*>(wb + W.bins);
+  int32_t* cursor = reinterpret_cast<int32_t*>(wb + W.cursor);
+  int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
+  float* bbox = reinterpret_cast<float*>(wb + W.bbox);
+  const int64_t n = a->n_atoms;
+  {
+    // spatial order of the destination atoms: Morton code of a 64^3 grid over
+    // the bounding box, counting-sorted (order only affects locality)
+    const int64_t nb = (n + 255) / 256;
+    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox);
+    E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
+    E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * kOrderBins, st));
+    k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, bins);
+    E2A_LAUNCH_CHECK();
+    e2a_status ss = exclusive_scan_i32(bins, kOrderBins, cursor, bsum, st);
+    if (ss != E2A_OK) return ss;
+    // cursor now holds the bin starts; reuse bins as the running cursor
+    E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
+    k_ord_scatter<<<nb, 256, 0, st>>>(n, key, cursor, bins, order);
+    E2A_LAUNCH_CHECK();
+  }
   {
     const int64_t nv = S::wtotal();
     k_pack_so2<L><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2), wpk);
@@ -534,6 +786,9 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   p.feat = static_cast<const uint16_t*>(a->feat);
   p.wpk = wpk;
   p.radpk = radpk;
+  p.order = order;
+  p.n_atoms = n;
+  p.per_xcd = (n + 7) / 8;
   p.out = a->out;
   p.out_lse = a->out_lse;
   for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
@@ -541,7 +796,7 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   p.cutoff = a->cutoff;
   E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<L>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::total));
-  hipLaunchKernelGGL(k_attn_mfma<L>, dim3(a->n_atoms), dim3(kThreads), S::total, st, p);
+  hipLaunchKernelGGL(k_attn_mfma<L>, dim3(8 * p.per_xcd), dim3(kThreads), S::total, st, p);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
@@ -552,13 +807,13 @@ bool mfma_supported(int L, int C, int H, int dtype) {
   return L >= 1 && L <= 4 && C == kC && H == kH && dtype == E2A_DTYPE_BF16;
 }
 
-size_t mfma_packed_weight_bytes(int L, int C) {
+size_t mfma_workspace_bytes(int64_t n, int L, int C) {
   if (C != kC) return 0;
   switch (L) {
-    case 1: return packed_bytes<1>();
-    case 2: return packed_bytes<2>();
-    case 3: return packed_bytes<3>();
-    case 4: return packed_bytes<4>();
+    case 1: return mfma_ws_layout<1>(n).total;
+    case 2: return mfma_ws_layout<2>(n).total;
+    case 3: return mfma_ws_layout<3>(n).total;
+    case 4: return mfma_ws_layout<4>(n).total;
     default: return 0;
   }
 }

@@ -33,7 +33,7 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   w.q = take(sizeof(float) * (size_t)n * C);
   w.k = take(sizeof(float) * (size_t)n * C);
-  w.w = take(mfma_supported(L, C, H, dtype) ? mfma_packed_weight_bytes(L, C) : 0);
+  w.w = take(mfma_supported(L, C, H, dtype) ? mfma_workspace_bytes(n, L, C) : 0);
   w.total = off;
   return w;
 }
@@ -143,7 +143,7 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
   char* base = static_cast<char*>(a->workspace);
   pl.q = reinterpret_cast<float*>(base + ws.q);
   pl.k = reinterpret_cast<float*>(base + ws.k);
-  pl.w_packed = base + ws.w;
+  pl.mfma_ws = base + ws.w;
   pl.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
   hipStream_t s = static_cast<hipStream_t>(stream);

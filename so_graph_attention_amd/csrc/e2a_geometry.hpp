@@ -75,6 +75,67 @@ E2A_HD float ir_entry(int l, int m, int n, const R1& r1, const RP& rp) {
   return acc;
 }
 
+// Row m of D^l (compile-time l >= 2) by the same recursion as ir_entry,
+// grouped per row: the U, V and W terms use at most five (i, a) pairs whose
+// coefficients depend on m alone, and every column n carries the factor
+// 1/sqrt(denominator(n)).  r1[i+1][j+1] = D^1[i][j]; rp(a) points at row a of
+// D^{l-1} (column b at index b + l - 1).  Writes out[n + l], n = -l..l.
+template <int l, typename RP>
+E2A_HD void ir_row(int m, const float r1[3][3], const RP& rp, float* out) {
+  const int am = m < 0 ? -m : m;
+  const float d = (m == 0) ? 1.0f : 0.0f;
+  const float cu = (am < l) ? sqrtf(float((l + m) * (l - m))) : 0.0f;
+  const float cv = 0.5f * sqrtf((1.0f + d) * float((l + am - 1) * (l + am))) * (1.0f - 2.0f * d);
+  const float cw = (am < l - 1) ? -0.5f * sqrtf(float((l - am - 1) * (l - am))) : 0.0f;
+  const float s2 = 1.41421356237f;
+  int ii[5], aa[5];
+  float cc[5];
+  ii[0] = 0; aa[0] = (am < l) ? m : 0; cc[0] = cu;
+  if (m == 0) {
+    ii[1] = 1;  aa[1] = 1;  cc[1] = cv;
+    ii[2] = -1; aa[2] = -1; cc[2] = cv;
+    ii[3] = 1;  aa[3] = 0;  cc[3] = 0.0f;
+    ii[4] = -1; aa[4] = 0;  cc[4] = 0.0f;
+  } else if (m > 0) {
+    ii[1] = 1;  aa[1] = m - 1;                   cc[1] = cv * (m == 1 ? s2 : 1.0f);
+    ii[2] = -1; aa[2] = (m == 1) ? 0 : 1 - m;    cc[2] = (m == 1) ? 0.0f : -cv;
+    ii[3] = 1;  aa[3] = (am < l - 1) ? m + 1 : 0;  cc[3] = cw;
+    ii[4] = -1; aa[4] = (am < l - 1) ? -m - 1 : 0; cc[4] = cw;
+  } else {
+    ii[1] = 1;  aa[1] = (m == -1) ? 0 : m + 1;   cc[1] = (m == -1) ? 0.0f : cv;
+    ii[2] = -1; aa[2] = -m - 1;                  cc[2] = cv * (m == -1 ? s2 : 1.0f);
+    ii[3] = 1;  aa[3] = (am < l - 1) ? m - 1 : 0;  cc[3] = cw;
+    ii[4] = -1; aa[4] = (am < l - 1) ? -m + 1 : 0; cc[4] = -cw;
+  }
+  float g0[5], gp[5], gm[5];   // r1(i_k, 0), r1(i_k, +1), r1(i_k, -1)
+  float row[5][2 * l - 1];
+#pragma unroll
+  for (int k = 0; k < 5; ++k) {
+    const int i = ii[k] + 1;
+    g0[k] = i == 0 ? r1[0][1] : (i == 1 ? r1[1][1] : r1[2][1]);
+    gp[k] = i == 0 ? r1[0][2] : (i == 1 ? r1[1][2] : r1[2][2]);
+    gm[k] = i == 0 ? r1[0][0] : (i == 1 ? r1[1][0] : r1[2][0]);
+    const float* rk = rp(aa[k]);
+#pragma unroll
+    for (int b = 0; b < 2 * l - 1; ++b) row[k][b] = rk[b];
+  }
+#pragma unroll
+  for (int n = -l; n <= l; ++n) {
+    const int an = n < 0 ? -n : n;
+    const float inv = 1.0f / sqrtf(an == l ? float((2 * l) * (2 * l - 1)) : float((l + n) * (l - n)));
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      float pk;
+      if (n == l) pk = gp[k] * row[k][2 * l - 2] - gm[k] * row[k][0];
+      else if (n == -l) pk = gp[k] * row[k][0] + gm[k] * row[k][2 * l - 2];
+      else pk = g0[k] * row[k][n + l - 1];
+      acc += cc[k] * pk;
+    }
+    out[n + l] = acc * inv;
+  }
+}
+
 // D^1 in the harmonic order (y, z, x) <- index m + 1, written with row stride ld.
 E2A_HD void wigner_l1(const float R[3][3], float* D1, int ld) {
   const int p[3] = {1, 2, 0};

@@ -59,20 +59,24 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
                                 float cutoff, int64_t* row_ptr, int32_t* col, int64_t cap,
                                 int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t neighbors_workspace_bytes(int64_t n);
+// Exclusive scan of n int32 values into out[0..n] (total at out[n]); bsum needs
+// scan_bsum_count(n) int64 entries of scratch.
+e2a_status exclusive_scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, hipStream_t s);
+int64_t scan_bsum_count(int64_t n);
 
 // Attention (attention_*.hip).
 struct AttnPlan {
   const e2a_attn_args* a;
   float* q;           // workspace f32 [N, C]
   float* k;           // workspace f32 [N, C]
-  void* w_packed;     // workspace, MFMA weight layout (MFMA path only)
+  void* mfma_ws;      // workspace of the MFMA path (packed weights, atom order)
   float box[3];
   int periodic;
 };
 e2a_status launch_qk(const AttnPlan& p, hipStream_t s);
 e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);
 bool mfma_supported(int L, int C, int H, int dtype);
-size_t mfma_packed_weight_bytes(int L, int C);
+size_t mfma_workspace_bytes(int64_t n, int L, int C);
 e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
 
 }  // namespace e2a

@@ -23,6 +23,36 @@ void e2a_host_wigner(int L, const float* R_in, int n, float* D_out) {
   }
 }
 
+// Same blocks built row by row with ir_row (the form the matrix-core kernel uses).
+void e2a_host_wigner_rows(int L, const float* R_in, int n, float* D_out) {
+  const int sz = e2a::wig_size(L);
+  for (int e = 0; e < n; ++e) {
+    float R[3][3];
+    for (int a = 0; a < 3; ++a)
+      for (int b = 0; b < 3; ++b) R[a][b] = R_in[9 * e + 3 * a + b];
+    float* D = D_out + (size_t)sz * e;
+    D[0] = 1.0f;
+    if (L < 1) continue;
+    float r1[3][3];
+    e2a::wigner_l1(R, &r1[0][0], 3);
+    for (int a = 0; a < 3; ++a)
+      for (int b = 0; b < 3; ++b) D[1 + 3 * a + b] = r1[a][b];
+    for (int l = 2; l <= L; ++l) {
+      const float* Dp = D + e2a::wig_off(l - 1);
+      float* Dl = D + e2a::wig_off(l);
+      for (int m = -l; m <= l; ++m) {
+        auto rp = [&](int a) { return Dp + (a + l - 1) * (2 * l - 1); };
+        float* out = Dl + (m + l) * (2 * l + 1);
+        switch (l) {
+          case 2: e2a::ir_row<2>(m, r1, rp, out); break;
+          case 3: e2a::ir_row<3>(m, r1, rp, out); break;
+          default: e2a::ir_row<4>(m, r1, rp, out); break;
+        }
+      }
+    }
+  }
+}
+
 void e2a_host_radial_basis8(const float* r, int n, float rc, float* out) {
   for (int e = 0; e < n; ++e) e2a::radial_basis8(r[e], rc, out + 8 * e);
 }

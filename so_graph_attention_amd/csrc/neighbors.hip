@@ -341,6 +341,12 @@ WsLayout ws_layout(int64_t n) {
 
 size_t neighbors_workspace_bytes(int64_t n) { return ws_layout(n).total; }
 
+e2a_status exclusive_scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, hipStream_t s) {
+  return exclusive_scan<int32_t>(in, n, out, bsum, s);
+}
+
+int64_t scan_bsum_count(int64_t n) { return (n + kScanBlock - 1) / kScanBlock + 1; }
+
 e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batch, const float* box,
                                 float cutoff, int64_t* row_ptr, int32_t* col, int64_t cap_edges,
                                 int64_t* n_edges, void* ws, size_t ws_bytes, hipStream_t s) {
