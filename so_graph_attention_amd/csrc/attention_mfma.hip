@@ -24,6 +24,8 @@
 //     of an edge land in the same lane), scales by alpha and by the radial
 //     weights (one extra MFMA against the radial basis), and folds the partial
 //     rotate-out D^T of this |m| into per-lane accumulators for all (l, m').
+#include <utility>
+
 #include "e2a_geometry.hpp"
 #include "e2a_internal.hpp"
 
@@ -80,8 +82,48 @@ struct Shape {
     for (int k = 0; k < m; ++k) o += (int64_t)fps(k) * km(k) * km(k);
     return o;
   }
+  // weight stream of one chunk: block m has nb(m) output blocks (pairs for
+  // m = 0) of ks(m) k-steps; sbase(m) is its first step in the chunk
+  static constexpr int ks(int m) { return km(m) / 16; }
+  static constexpr int nb(int m) { return m == 0 ? (L + 2) / 2 : L + 1 - m; }
+  static constexpr int tot(int m) { return nb(m) * ks(m); }
+  static constexpr int sbase(int m) {
+    int o = 0;
+    for (int k = 0; k < m; ++k) o += tot(k);
+    return o;
+  }
+  static constexpr int stot() { return sbase(L + 1); }
+  static constexpr int blk_lo(int m, int b, int f) { return m == 0 ? 2 * b + f : m + b; }
+  static constexpr bool has1(int m, int b) { return m > 0 || 2 * b + 1 <= L; }
+  // block m of the chunk stream holding chunk step G (0 <= G < stot())
+  static constexpr int stream_m(int G) {
+    int m = 0;
+    while (m < L && G >= sbase(m + 1)) ++m;
+    return m;
+  }
+  // byte offset of fragment f of chunk step G, without the wave's column term
+  static constexpr int stream_off(int G, int f) {
+    const int m = stream_m(G);
+    const int g = G - sbase(m);
+    const int b = g / ks(m), st = g % ks(m);
+    return m == 0 ? static_cast<int>((woff(0) + (int64_t)(blk_lo(0, b, f) * 4) * wblock(0)) * 16) + st * 1024
+                  : static_cast<int>((woff(m) + (int64_t)((blk_lo(m, b, 0) - m) * 4) * wblock(m)) * 16) +
+                        st * 2048 + f * 1024;
+  }
+  static constexpr bool stream_has1(int G) {
+    const int m = stream_m(G);
+    return has1(m, (G - sbase(m)) / ks(m));
+  }
+  static constexpr int64_t wave_bytes(int m) { return wblock(m) * 16; }
+  // two A regions: even m in A0, odd m in A1 (block m+1 is built while m runs)
+  static constexpr int amax_par(int par) {
+    int b = 0;
+    for (int m = par; m <= L; m += 2) b = abytes(m) > b ? abytes(m) : b;
+    return b;
+  }
+  static constexpr int off_A1 = (amax_par(0) + 255) / 256 * 256;
   // LDS layout (bytes)
-  static constexpr int off_D = amax();
+  static constexpr int off_D = off_A1 + (amax_par(1) + 255) / 256 * 256;
   static constexpr int off_DT = off_D + kET * DSZ * 4;
   static constexpr int off_rbf = off_DT + DT * 2;
   static constexpr int off_alpha = off_rbf + kET * 8 * 4;
@@ -106,6 +148,18 @@ __device__ __forceinline__ void unpack_bf16x8(const uint4 raw, float* h) {
     h[2 * t] = __uint_as_float(w[t] << 16);
     h[2 * t + 1] = __uint_as_float(w[t] & 0xFFFF0000u);
   }
+}
+
+// Calls f(std::integral_constant<int, i>) for i = 0..N-1: every index is a
+// compile-time constant, so register arrays indexed by it never spill and
+// pipeline decisions resolve statically.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Hides a value's origin from the optimiser so that lane-dependent addresses
@@ -171,7 +225,8 @@ struct MfmaParams {
 };
 
 struct Smem {
-  uint16_t* A;
+  uint16_t* A0;    // GEMM operand of even |m| blocks
+  uint16_t* A1;    // GEMM operand of odd |m| blocks
   float* D;
   _Float16* DT;
   float* rbf;
@@ -183,59 +238,69 @@ struct Smem {
   float* scale;
 };
 
-// Rotate the chunk's neighbour features into the edge frames and write the
-// GEMM operand of block M (bf16, padded rows) to LDS: for each degree l >= M,
-// x_{l,+-M}[c] = sum_n D^l[l +- M][n] h_j[l*l + n][c].  Thread t owns channel
-// group t % 16 (8 channels) of edges t / 16 and t / 16 + 16; the 2l+1
-// feature loads of an edge are in flight before the first multiply.
-template <int L, int M, int l>
-__device__ __forceinline__ void build_a_l(const MfmaParams& p, const Smem& s, int tid) {
+// Rotate-in task tau of block MN for this thread: degree l = MN + tau / 2,
+// edge (tid / 16) + 16 (tau % 2), channels 8 (tid % 16) .. +8:
+// x_{l,+-MN}[c] = sum_n D^l[l +- MN][n] h_j[l*l + n][c], written as bf16 to
+// the block's GEMM operand (rows: edge, and for MN > 0 the +MN row of edge e
+// at 32 (e / 16) + e % 16 with its -MN row 16 below; columns (l - MN) C + c).
+// The loads and the arithmetic are separate calls so that the loads can be
+// issued well before their use.
+template <int L, int MN, int TAU>
+__device__ __forceinline__ void task_load(const MfmaParams& p, const Smem& s, int tid, uint4 (&raw)[2 * L + 1]) {
   using S = Shape<L>;
-  constexpr int W = 2 * l + 1;
-  constexpr int stride = S::astride(M);
-  const int g = tid & 15;
-#pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
-    const int e = (tid >> 4) + 16 * h;
-    const uint16_t* hp = p.feat + ((int64_t)s.j[e] * S::K + l * l) * kC + 8 * g;
-    uint4 raw[W];
+  constexpr int l = MN + (TAU >> 1);
+  const int e = (tid >> 4) + 16 * (TAU & 1);
+  const uint16_t* hp = p.feat + ((int64_t)s.j[e] * S::K + l * l) * kC + 8 * (tid & 15);
 #pragma unroll
-    for (int n = 0; n < W; ++n) raw[n] = *reinterpret_cast<const uint4*>(hp + n * kC);
-    const float* De = s.D + e * S::DSZ + doff(l);
-    const float* Dp = De + (l + M) * dpad(l);
-    const float* Dm = De + (l - M) * dpad(l);
-    float xp[8], xm[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) { xp[q] = 0.0f; xm[q] = 0.0f; }
-#pragma unroll
-    for (int n = 0; n < W; ++n) {
-      float hv[8];
-      unpack_bf16x8(raw[n], hv);
-      const float dp = Dp[n];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xp[q] += dp * hv[q];
-      if constexpr (M > 0) {
-        const float dm = Dm[n];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) xm[q] += dm * hv[q];
-      }
-    }
-    if constexpr (M == 0) {
-      *reinterpret_cast<bf16x8*>(s.A + e * stride + l * kC + 8 * g) = to_vec8<bf16x8>(xp);
-    } else {
-      const int row = 32 * (e >> 4) + (e & 15);
-      const int colk = (l - M) * kC + 8 * g;
-      *reinterpret_cast<bf16x8*>(s.A + row * stride + colk) = to_vec8<bf16x8>(xp);
-      *reinterpret_cast<bf16x8*>(s.A + (row + 16) * stride + colk) = to_vec8<bf16x8>(xm);
-    }
-  }
-  if constexpr (l < L) build_a_l<L, M, l + 1>(p, s, tid);
+  for (int n = 0; n < 2 * l + 1; ++n) raw[n] = *reinterpret_cast<const uint4*>(hp + n * kC);
 }
 
-template <int L, int M>
-__device__ __forceinline__ void build_a(const MfmaParams& p, const Smem& s, int tid) {
+template <int L, int MN, int TAU>
+__device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid, const uint4 (&raw)[2 * L + 1]) {
+  using S = Shape<L>;
+  constexpr int stride = S::astride(MN);
+  constexpr int l = MN + (TAU >> 1);
+  const int e = (tid >> 4) + 16 * (TAU & 1);
+  const int g = tid & 15;
+  const float* De = s.D + e * S::DSZ + doff(l);
+  const float* Dp = De + (l + MN) * dpad(l);
+  const float* Dm = De + (l - MN) * dpad(l);
+  float xp[8], xm[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) { xp[q] = 0.0f; xm[q] = 0.0f; }
+#pragma unroll
+  for (int n = 0; n < 2 * l + 1; ++n) {
+    float hv[8];
+    unpack_bf16x8(raw[n], hv);
+    const float dp = Dp[n];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xp[q] += dp * hv[q];
+    if constexpr (MN > 0) {
+      const float dm = Dm[n];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) xm[q] += dm * hv[q];
+    }
+  }
+  if constexpr (MN == 0) {
+    *reinterpret_cast<bf16x8*>(A + e * stride + l * kC + 8 * g) = to_vec8<bf16x8>(xp);
+  } else {
+    const int row = 32 * (e >> 4) + (e & 15);
+    const int colk = (l - MN) * kC + 8 * g;
+    *reinterpret_cast<bf16x8*>(A + row * stride + colk) = to_vec8<bf16x8>(xp);
+    *reinterpret_cast<bf16x8*>(A + (row + 16) * stride + colk) = to_vec8<bf16x8>(xm);
+  }
+}
+
+// Stand-alone rotate-in of block 0 (the start of a chunk), one task at a time.
+template <int L>
+__device__ __forceinline__ void build_a0(const MfmaParams& p, const Smem& s, int tid) {
   static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
-  build_a_l<L, M, M>(p, s, opaque(tid));
+  tid = opaque(tid);
+  uint4 raw[2 * L + 1];
+  static_for<2 * (L + 1)>([&](auto tau) {
+    task_load<L, 0, decltype(tau)::value>(p, s, tid, raw);
+    task_compute<L, 0, decltype(tau)::value>(s, s.A0, tid, raw);
+  });
 }
 
 // A operand of the rotate-out contraction: row n of D^l rows `mrow`, for the
@@ -258,140 +323,119 @@ __device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// GEMM of block M for this wave's 32 output channels, then the epilogue:
-// y_{+-m} from the W1/W2 products, u = alpha * rho * y (rho from one MFMA
-// against the radial basis), and the partial rotate-out
+constexpr int kRing = 8;   // weight k-steps in flight per wave
+struct WRing {
+  bf16x8 r[kRing][2];
+};
+
+// Loads chunk step G of the weight stream into its ring slot G % kRing.
+template <int L, int G>
+__device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t wrsrc, int voff, int wave) {
+  using S = Shape<L>;
+  constexpr int m = S::stream_m(G);
+  constexpr int off0 = S::stream_off(G, 0);
+  constexpr int off1 = S::stream_off(G, 1);
+  const int wo = static_cast<int>(wave * S::wave_bytes(m));
+  ring.r[G % kRing][0] = load_b(wrsrc, voff, wo + off0);
+  if constexpr (S::stream_has1(G)) ring.r[G % kRing][1] = load_b(wrsrc, voff, wo + off1);
+}
+
+// GEMM of block M for this wave's 32 output channels, then the epilogue of
+// each output block: y_{+-m} from the W1/W2 products, u = alpha * rho * y
+// (rho from one MFMA against the radial basis), and the partial rotate-out
 // acc_lo[n][c] += sum_{edges, +-} D^lo[lo +- M][n] u_{+-}[c], itself an MFMA
 // contraction over the chunk's edges.
 //
-// The K loops are software-pipelined by hand: weight fragments are loaded
-// kPre k-steps before use and A fragments one step before, and a scheduling
-// barrier after every k-step keeps the compiler from sinking the loads back
-// next to their MFMAs (which would expose the full L2 latency each step).
-template <int L, int M>
-__device__ __forceinline__ void epilogue_m0(const Smem& s, int lo, const f32x16& c0, const f16x8& arbf0,
-                                            const f16x8& brad, const float (&alpha)[16], int half, int n,
-                                            bool grp_odd, NodeAcc& acc) {
-  const f32x16 rho = mfma_f16(arbf0, brad, f32x16{});
-  float u[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) u[r] = alpha[r] * rho[r] * c0[r];
-  const bool nvalid = n < 2 * lo + 1;
-  const _Float16* drow = s.DT + wig_off(lo) * kET + (lo * (2 * lo + 1) + n) * kET;
-  rotate_out_step(acc, dt_frag(drow, 0, half, nvalid), to_vec8<f16x8>(u), grp_odd);
-  rotate_out_step(acc, dt_frag(drow, 16, half, nvalid), to_vec8<f16x8>(u + 8), grp_odd);
-}
-
-// |m| = 0: output blocks lo0 and lo0 + 1 (when present) share each A fragment.
-template <int L, int LO0>
-__device__ __forceinline__ void gemm_m0(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int lane,
-                                        int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                        NodeAcc (&nacc)[L + 1]) {
-  using S = Shape<L>;
-  constexpr int M = 0;
-  constexpr int KS = S::km(M) / 16;
-  constexpr int stride = S::astride(M);
-  constexpr bool two = LO0 + 1 <= L;
-  constexpr int kPre = two ? 8 : 12;
-  const int half = lane >> 5;
-  const int c_own = 32 * wave + (lane & 31);
-  const int voff = lane * 16;
-  const uint16_t* ap = s.A + (lane & 31) * stride + 8 * half;
-  const int sb0 = static_cast<int>((S::woff(M) + (int64_t)((LO0 - M) * 4 + wave) * S::wblock(M)) * 16);
-  const int sb1 = static_cast<int>((S::woff(M) + (int64_t)((LO0 + 1 - M) * 4 + wave) * S::wblock(M)) * 16);
-  f32x16 c0 = {}, c1 = {};
-  bf16x8 r0[kPre], r1[kPre];
-#pragma unroll
-  for (int q = 0; q < kPre; ++q) {
-    r0[q] = load_b(wrsrc, voff, sb0 + q * 1024);
-    if constexpr (two) r1[q] = load_b(wrsrc, voff, sb1 + q * 1024);
-  }
-  bf16x8 a = *reinterpret_cast<const bf16x8*>(ap);
-#pragma unroll
-  for (int st = 0; st < KS; ++st) {
-    const int q = st % kPre;
-    const bf16x8 b0 = r0[q];
-    bf16x8 b1 = {};
-    if constexpr (two) b1 = r1[q];
-    if (st + kPre < KS) {
-      r0[q] = load_b(wrsrc, voff, sb0 + (st + kPre) * 1024);
-      if constexpr (two) r1[q] = load_b(wrsrc, voff, sb1 + (st + kPre) * 1024);
-    }
-    bf16x8 an = a;
-    if (st + 1 < KS) an = *reinterpret_cast<const bf16x8*>(ap + (st + 1) * 16);
-    c0 = mfma_bf16(a, b0, c0);
-    if constexpr (two) c1 = mfma_bf16(a, b1, c1);
-    a = an;
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  const int n = lane & 15;
-  const bool grp_odd = (lane >> 4) & 1;
-  const f16x8 zero8 = {};
-  {
-    const f16x8 brad = half == 0 ? p.radpk[LO0 * kC + c_own] : zero8;
-    epilogue_m0<L, M>(s, LO0, c0, arbf[0], brad, alpha, half, n, grp_odd, nacc[LO0]);
-  }
-  if constexpr (two) {
-    const f16x8 brad = half == 0 ? p.radpk[(LO0 + 1) * kC + c_own] : zero8;
-    epilogue_m0<L, M>(s, LO0 + 1, c1, arbf[0], brad, alpha, half, n, grp_odd, nacc[LO0 + 1]);
-  }
-  if constexpr (LO0 + 2 <= L) gemm_m0<L, LO0 + 2>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
-}
-
+// Software pipeline, all fixed at compile time: the weight stream runs kRing
+// k-steps ahead (continuing into the next block and the next chunk, whose
+// weights are the same), A fragments one step ahead, and the rotate-in of
+// block M+1 is spread over the k-steps (task loads every P steps, arithmetic
+// P-1 steps later) so that its VALU work and feature loads overlap the MFMAs.
+// A scheduling barrier after every k-step keeps the compiler from undoing
+// this order.
 template <int L, int M>
 __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc,
-                                          int lane, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                          NodeAcc (&nacc)[L + 1]) {
+                                          int tid, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
+                                          NodeAcc (&nacc)[L + 1], WRing& ring) {
   using S = Shape<L>;
-  lane = opaque(lane);
-  if constexpr (M == 0) {
-    gemm_m0<L, 0>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
-  } else {
-    constexpr int KS = S::km(M) / 16;
-    constexpr int stride = S::astride(M);
-    constexpr int kPre = 6;
-    const int half = lane >> 5;
-    const int c_own = 32 * wave + (lane & 31);
-    const int n = lane & 15;                 // D row of the rotate-out A operand
-    const bool grp_odd = (lane >> 4) & 1;    // lane group 1 or 3: channels 16-31
-    const int voff = lane * 16;
-    const f16x8 zero8 = {};
-    const uint16_t* ap0 = s.A + (lane & 31) * stride + 8 * half;
-    const uint16_t* ap1 = ap0 + 32 * stride;
-#pragma unroll
-    for (int lo = M; lo <= L; ++lo) {
-      const int sblk = static_cast<int>((S::woff(M) + (int64_t)((lo - M) * 4 + wave) * S::wblock(M)) * 16);
-      f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
-      bf16x8 b1r[kPre], b2r[kPre];
-#pragma unroll
-      for (int q = 0; q < kPre; ++q) {
-        b1r[q] = load_b(wrsrc, voff, sblk + q * 2048);
-        b2r[q] = load_b(wrsrc, voff, sblk + q * 2048 + 1024);
+  constexpr int KS = S::ks(M);
+  constexpr int stride = S::astride(M);
+  constexpr int NT = M < L ? 2 * (L - M) : 0;       // rotate-in tasks of block M+1 per thread
+  constexpr int P = NT ? S::tot(M) / NT : 1;
+  static_assert(NT == 0 || P >= 2, "too few k-steps to hide the next rotate-in");
+  uint16_t* const Acur = (M % 2 == 0) ? s.A0 : s.A1;
+  uint16_t* const Anext = (M % 2 == 0) ? s.A1 : s.A0;
+  tid = opaque(tid);
+  const int lane = tid & 63;
+  const int half = lane >> 5;
+  const int c_own = 32 * wave + (lane & 31);
+  const int n = lane & 15;                 // D row of the rotate-out A operand
+  const bool grp_odd = (lane >> 4) & 1;    // lane group 1 or 3: channels 16-31
+  const int voff = lane * 16;
+  const f16x8 zero8 = {};
+  const uint16_t* ap0 = Acur + (lane & 31) * stride + 8 * half;
+  const uint16_t* ap1 = ap0 + 32 * stride;   // second row tile (m > 0 only)
+  bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0);
+  bf16x8 a1 = {};
+  if constexpr (M > 0) a1 = *reinterpret_cast<const bf16x8*>(ap1);
+  uint4 raw[2 * L + 1];
+  static_for<S::nb(M)>([&](auto bc) {
+    constexpr int b = decltype(bc)::value;
+    f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
+    // radial-weight fragments of this block's output degrees, fetched now so
+    // that they have landed by the epilogue
+    f16x8 brad0 = zero8, brad1 = zero8;
+    if (half == 0) {
+      brad0 = p.radpk[S::blk_lo(M, b, 0) * kC + c_own];
+      if constexpr (M == 0 && S::has1(M, b)) brad1 = p.radpk[S::blk_lo(M, b, 1) * kC + c_own];
+    }
+    static_for<KS>([&](auto stc) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int g = b * KS + st;
+      constexpr int G = S::sbase(M) + g;
+      const bf16x8 b0 = ring.r[G % kRing][0];
+      const bf16x8 b1 = ring.r[G % kRing][1];
+      wring_load<L, (G + kRing) % S::stot()>(ring, wrsrc, voff, wave);
+      constexpr int sn = (st + 1) % KS;
+      const bf16x8 a0n = *reinterpret_cast<const bf16x8*>(ap0 + sn * 16);
+      bf16x8 a1n = {};
+      if constexpr (M > 0) a1n = *reinterpret_cast<const bf16x8*>(ap1 + sn * 16);
+      c00 = mfma_bf16(a0, b0, c00);
+      if constexpr (M == 0) {
+        if constexpr (S::has1(M, b)) c01 = mfma_bf16(a0, b1, c01);
+      } else {
+        c01 = mfma_bf16(a0, b1, c01);
+        c10 = mfma_bf16(a1, b0, c10);
+        c11 = mfma_bf16(a1, b1, c11);
       }
-      bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0);
-      bf16x8 a1 = *reinterpret_cast<const bf16x8*>(ap1);
+      a0 = a0n;
+      a1 = a1n;
+      if constexpr (NT > 0 && g % P == 0 && g / P < NT)
+        task_load<L, (M < L ? M + 1 : L), (g / P) % (NT > 0 ? NT : 1)>(p, s, tid, raw);
+      if constexpr (NT > 0 && g % P == P - 1 && g / P < NT)
+        task_compute<L, (M < L ? M + 1 : L), (g / P) % (NT > 0 ? NT : 1)>(s, Anext, tid, raw);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (M == 0) {
+      static_for<2>([&](auto fc) {
+        constexpr int f = decltype(fc)::value;
+        if constexpr (f == 0 || S::has1(M, b)) {
+          constexpr int lo = S::blk_lo(M, b, f);
+          const f32x16& c0 = f == 0 ? c00 : c01;
+          const f16x8 brad = f == 0 ? brad0 : brad1;
+          const f32x16 rho = mfma_f16(arbf[0], brad, f32x16{});
+          float u[16];
 #pragma unroll
-      for (int st = 0; st < KS; ++st) {
-        const int q = st % kPre;
-        const bf16x8 b1 = b1r[q], b2 = b2r[q];
-        if (st + kPre < KS) {
-          b1r[q] = load_b(wrsrc, voff, sblk + (st + kPre) * 2048);
-          b2r[q] = load_b(wrsrc, voff, sblk + (st + kPre) * 2048 + 1024);
+          for (int r = 0; r < 16; ++r) u[r] = alpha[r] * rho[r] * c0[r];
+          const bool nvalid = n < 2 * lo + 1;
+          const _Float16* drow = s.DT + wig_off(lo) * kET + (lo * (2 * lo + 1) + n) * kET;
+          rotate_out_step(nacc[lo], dt_frag(drow, 0, half, nvalid), to_vec8<f16x8>(u), grp_odd);
+          rotate_out_step(nacc[lo], dt_frag(drow, 16, half, nvalid), to_vec8<f16x8>(u + 8), grp_odd);
         }
-        bf16x8 a0n = a0, a1n = a1;
-        if (st + 1 < KS) {
-          a0n = *reinterpret_cast<const bf16x8*>(ap0 + (st + 1) * 16);
-          a1n = *reinterpret_cast<const bf16x8*>(ap1 + (st + 1) * 16);
-        }
-        c00 = mfma_bf16(a0, b1, c00);
-        c01 = mfma_bf16(a0, b2, c01);
-        c10 = mfma_bf16(a1, b1, c10);
-        c11 = mfma_bf16(a1, b2, c11);
-        a0 = a0n;
-        a1 = a1n;
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      const f16x8 brad = half == 0 ? p.radpk[lo * kC + c_own] : zero8;
+      });
+    } else {
+      constexpr int lo = S::blk_lo(M, b, 0);
+      const f16x8 brad = brad0;
       const bool nvalid = n < 2 * lo + 1;
       const _Float16* dt_lo = s.DT + wig_off(lo) * kET;
       const _Float16* drow_p = dt_lo + ((lo + M) * (2 * lo + 1) + n) * kET;
@@ -411,7 +455,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
       tile(0, c00, c01);
       tile(1, c10, c11);
     }
-  }
+  });
 }
 
 // D^l for l = 2..L of all chunk edges, one (edge, row) per thread and level.
@@ -442,15 +486,15 @@ __device__ __forceinline__ void wig_level(const Smem& s, int tid) {
   if constexpr (l < L) wig_level<L, l + 1>(s, tid);
 }
 
+// Blocks M = 0..L of one chunk: GEMM of M (while block M+1 is rotated in),
+// then a barrier so that the next block's operand is complete.
 template <int L, int M>
 __device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid,
-                                         int lane, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                         NodeAcc (&nacc)[L + 1]) {
-  build_a<L, M>(p, s, tid);
+                                         int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
+                                         NodeAcc (&nacc)[L + 1], WRing& ring) {
+  mma_block<L, M>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
   __syncthreads();
-  mma_block<L, M>(p, s, wrsrc, lane, wave, arbf, alpha, nacc);
-  __syncthreads();
-  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, lane, wave, arbf, alpha, nacc);
+  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
 }
 
 template <int L>
@@ -459,7 +503,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
   constexpr int K = S::K;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Smem s;
-  s.A = reinterpret_cast<uint16_t*>(smem);
+  s.A0 = reinterpret_cast<uint16_t*>(smem);
+  s.A1 = reinterpret_cast<uint16_t*>(smem + S::off_A1);
   s.D = reinterpret_cast<float*>(smem + S::off_D);
   s.DT = reinterpret_cast<_Float16*>(smem + S::off_DT);
   s.rbf = reinterpret_cast<float*>(smem + S::off_rbf);
@@ -488,6 +533,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
   for (int l = 0; l <= L; ++l) nacc[l] = NodeAcc{f32x4{}, f32x4{}};
   const float xi[3] = {p.pos[3 * i], p.pos[3 * i + 1], p.pos[3 * i + 2]};
   const int64_t e_beg = p.row_ptr[i], e_end = p.row_ptr[i + 1];
+  // the weight stream is the same for every chunk: prime it once
+  WRing ring;
+  {
+    const int voff = opaque(lane) * 16;
+    static_for<kRing>([&](auto Gc) { wring_load<L, decltype(Gc)::value>(ring, wrsrc, voff, wave); });
+  }
 
   for (int64_t e0 = e_beg; e0 < e_end; e0 += kET) {
     const int ne = (e_end - e0) < kET ? static_cast<int>(e_end - e0) : kET;
@@ -593,7 +644,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
       arbf[1] = to_vec8<f16x8>(half == 0 ? s.rbf + (r & 15) * 8 : z);
       arbf[2] = to_vec8<f16x8>(half == 0 ? s.rbf + (16 + (r & 15)) * 8 : z);
     }
-    do_block<L, 0>(p, s, wrsrc, tid, lane, wave, arbf, alpha, nacc);
+    build_a0<L>(p, s, tid);
+    __syncthreads();
+    do_block<L, 0>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
   }
   __syncthreads();
   {
