@@ -255,32 +255,34 @@ __device__ __forceinline__ void task_load(const MfmaParams& p, const Smem& s, in
   for (int n = 0; n < 2 * l + 1; ++n) raw[n] = *reinterpret_cast<const uint4*>(hp + n * kC);
 }
 
+// Term n of rotate-in task TAU: xp += D^l[l+MN][n] h[n], xm += D^l[l-MN][n] h[n].
+template <int L, int MN, int TAU, int N>
+__device__ __forceinline__ void task_term(const Smem& s, int tid, const uint4 (&raw)[2 * L + 1], float (&xp)[8],
+                                          float (&xm)[8]) {
+  using S = Shape<L>;
+  constexpr int l = MN + (TAU >> 1);
+  const int e = (tid >> 4) + 16 * (TAU & 1);
+  const float* De = s.D + e * S::DSZ + doff(l);
+  float hv[8];
+  unpack_bf16x8(raw[N], hv);
+  const float dp = De[(l + MN) * dpad(l) + N];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) xp[q] = (N == 0 ? 0.0f : xp[q]) + dp * hv[q];
+  if constexpr (MN > 0) {
+    const float dm = De[(l - MN) * dpad(l) + N];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) xm[q] = (N == 0 ? 0.0f : xm[q]) + dm * hv[q];
+  }
+}
+
+// Rounds task TAU's result to bf16 and writes it to block MN's GEMM operand.
 template <int L, int MN, int TAU>
-__device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid, const uint4 (&raw)[2 * L + 1]) {
+__device__ __forceinline__ void task_store(uint16_t* A, int tid, const float (&xp)[8], const float (&xm)[8]) {
   using S = Shape<L>;
   constexpr int stride = S::astride(MN);
   constexpr int l = MN + (TAU >> 1);
   const int e = (tid >> 4) + 16 * (TAU & 1);
   const int g = tid & 15;
-  const float* De = s.D + e * S::DSZ + doff(l);
-  const float* Dp = De + (l + MN) * dpad(l);
-  const float* Dm = De + (l - MN) * dpad(l);
-  float xp[8], xm[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) { xp[q] = 0.0f; xm[q] = 0.0f; }
-#pragma unroll
-  for (int n = 0; n < 2 * l + 1; ++n) {
-    float hv[8];
-    unpack_bf16x8(raw[n], hv);
-    const float dp = Dp[n];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) xp[q] += dp * hv[q];
-    if constexpr (MN > 0) {
-      const float dm = Dm[n];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) xm[q] += dm * hv[q];
-    }
-  }
   if constexpr (MN == 0) {
     *reinterpret_cast<bf16x8*>(A + e * stride + l * kC + 8 * g) = to_vec8<bf16x8>(xp);
   } else {
@@ -291,17 +293,66 @@ __device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid
   }
 }
 
-// Stand-alone rotate-in of block 0 (the start of a chunk), one task at a time.
+template <int L, int MN, int TAU>
+__device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid, const uint4 (&raw)[2 * L + 1]) {
+  constexpr int W = 2 * (MN + (TAU >> 1)) + 1;
+  float xp[8], xm[8];
+  static_for<W>([&](auto nc) { task_term<L, MN, TAU, decltype(nc)::value>(s, tid, raw, xp, xm); });
+  task_store<L, MN, TAU>(A, tid, xp, xm);
+}
+
+// Stand-alone rotate-in of block 0 (the start of a chunk): the loads of task
+// tau+1 are issued before task tau's arithmetic.
 template <int L>
 __device__ __forceinline__ void build_a0(const MfmaParams& p, const Smem& s, int tid) {
   static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
   tid = opaque(tid);
-  uint4 raw[2 * L + 1];
-  static_for<2 * (L + 1)>([&](auto tau) {
-    task_load<L, 0, decltype(tau)::value>(p, s, tid, raw);
-    task_compute<L, 0, decltype(tau)::value>(s, s.A0, tid, raw);
+  uint4 raw[2][2 * L + 1];
+  task_load<L, 0, 0>(p, s, tid, raw[0]);
+  static_for<2 * (L + 1)>([&](auto tc) {
+    constexpr int tau = decltype(tc)::value;
+    if constexpr (tau + 1 < 2 * (L + 1)) task_load<L, 0, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
+    task_compute<L, 0, tau>(s, s.A0, tid, raw[tau & 1]);
   });
 }
+
+// Compile-time schedule of block M+1's rotate-in inside block M's k-steps:
+// tasks run one after another; task tau issues its loads at start(tau),
+// accumulates term n at start(tau) + delta + n, and stores one step later.
+template <int L, int M>
+struct TaskSched {
+  using S = Shape<L>;
+  static constexpr int NT = M < L ? 2 * (L - M) : 0;
+  static constexpr int W(int tau) { return 2 * (M + 1 + tau / 2) + 1; }
+  static constexpr int work() {
+    int w = 0;
+    for (int t = 0; t < NT; ++t) w += W(t) + 1;
+    return w;
+  }
+  static constexpr int delta() {
+    if (NT == 0) return 0;
+    const int d = (S::tot(M) - work()) / NT;
+    return d > 6 ? 6 : d;
+  }
+  static constexpr int start(int tau) {
+    int o = 0;
+    for (int t = 0; t < tau; ++t) o += delta() + W(t) + 1;
+    return o;
+  }
+  // task whose loads are issued at step g (or -1)
+  static constexpr int load_at(int g) {
+    for (int t = 0; t < NT; ++t)
+      if (g == start(t)) return t;
+    return -1;
+  }
+  // task and term accumulated at step g (term == W: store), or task -1
+  static constexpr int term_task(int g) {
+    for (int t = 0; t < NT; ++t)
+      if (g >= start(t) + delta() && g <= start(t) + delta() + W(t)) return t;
+    return -1;
+  }
+  static constexpr int term_n(int g) { return term_task(g) < 0 ? 0 : g - start(term_task(g)) - delta(); }
+};
 
 // A operand of the rotate-out contraction: row n of D^l rows `mrow`, for the
 // 8 edges eg + crow(q, h), q = 0..7, as fp16.  Rows n >= 2l+1 are zero.
@@ -349,8 +400,8 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
 // Software pipeline, all fixed at compile time: the weight stream runs kRing
 // k-steps ahead (continuing into the next block and the next chunk, whose
 // weights are the same), A fragments one step ahead, and the rotate-in of
-// block M+1 is spread over the k-steps (task loads every P steps, arithmetic
-// P-1 steps later) so that its VALU work and feature loads overlap the MFMAs.
+// block M+1 is spread over the k-steps (TaskSched: one term per step) so that
+// its VALU work and feature loads overlap the MFMAs.
 // A scheduling barrier after every k-step keeps the compiler from undoing
 // this order.
 template <int L, int M>
@@ -360,9 +411,9 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
   using S = Shape<L>;
   constexpr int KS = S::ks(M);
   constexpr int stride = S::astride(M);
-  constexpr int NT = M < L ? 2 * (L - M) : 0;       // rotate-in tasks of block M+1 per thread
-  constexpr int P = NT ? S::tot(M) / NT : 1;
-  static_assert(NT == 0 || P >= 2, "too few k-steps to hide the next rotate-in");
+  using TS = TaskSched<L, M>;
+  constexpr int NT = TS::NT;                          // rotate-in tasks of block M+1 per thread
+  static_assert(NT == 0 || TS::delta() >= 2, "too few k-steps to hide the next rotate-in");
   uint16_t* const Acur = (M % 2 == 0) ? s.A0 : s.A1;
   uint16_t* const Anext = (M % 2 == 0) ? s.A1 : s.A0;
   tid = opaque(tid);
@@ -379,6 +430,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
   bf16x8 a1 = {};
   if constexpr (M > 0) a1 = *reinterpret_cast<const bf16x8*>(ap1);
   uint4 raw[2 * L + 1];
+  float txp[8], txm[8];
   static_for<S::nb(M)>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
     f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
@@ -410,10 +462,17 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
       }
       a0 = a0n;
       a1 = a1n;
-      if constexpr (NT > 0 && g % P == 0 && g / P < NT)
-        task_load<L, (M < L ? M + 1 : L), (g / P) % (NT > 0 ? NT : 1)>(p, s, tid, raw);
-      if constexpr (NT > 0 && g % P == P - 1 && g / P < NT)
-        task_compute<L, (M < L ? M + 1 : L), (g / P) % (NT > 0 ? NT : 1)>(s, Anext, tid, raw);
+      if constexpr (NT > 0) {
+        constexpr int MN = M < L ? M + 1 : L;
+        constexpr int tl = TS::load_at(g);
+        if constexpr (tl >= 0) task_load<L, MN, tl>(p, s, tid, raw);
+        constexpr int tt = TS::term_task(g);
+        if constexpr (tt >= 0) {
+          constexpr int tn = TS::term_n(g);
+          if constexpr (tn < TS::W(tt)) task_term<L, MN, tt, tn>(s, tid, raw, txp, txm);
+          else task_store<L, MN, tt>(Anext, tid, txp, txm);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (M == 0) {
