@@ -11,9 +11,15 @@
 // result is rotated back.
 //
 // Mapping onto CDNA4 (C = 128, H = 8, bf16 storage, fp32 accumulation):
+//   * two workgroups of 256 threads share a CU (each under 80 KB of LDS and
+//     256 registers per lane), so that one workgroup's latency-bound phases
+//     (edge geometry, Wigner-D, softmax, rotate-in) run while the other
+//     keeps the matrix cores busy;
 //   * per chunk, 32 lanes build the edge frames, D^1 and the radial basis;
 //     all 256 threads then extend D^2..D^L level by level (one matrix entry
-//     per thread per step) and compute the 32 x 8 logits;
+//     per thread per step, fp32, in the GEMM operand's LDS space, which is
+//     free at that point) and compute the 32 x 8 logits; an fp16 copy of D
+//     feeds both rotations;
 //   * per |m| block the 256 threads rotate h_j into the aligned frame and
 //     write the GEMM operand A (rows = edges, and for m > 0 the +m rows of 16
 //     edges followed by their -m rows) to LDS as bf16;
@@ -38,12 +44,15 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 128;      // channels
 constexpr int kH = 8;        // heads
 constexpr int kDH = 16;      // channels per head
 constexpr int kET = 32;      // edges per chunk
 constexpr int kThreads = 256;
+constexpr int kMinStretch = 4;     // destinations per work grab: at least
+constexpr int kMaxStretch = 128;   // and at most
 
 // Wigner-D rows in LDS are padded to a multiple of 4 floats (16-byte reads).
 __host__ __device__ constexpr int dpad(int l) { return ((2 * l + 1) + 3) / 4 * 4; }
@@ -56,7 +65,7 @@ __host__ __device__ constexpr int doff(int l) {
 template <int L>
 struct Shape {
   static constexpr int K = (L + 1) * (L + 1);
-  static constexpr int DSZ = doff(L + 1);                       // fp32 D floats per edge
+  static constexpr int DSZ = doff(L + 1);                       // fp32 D floats per edge (set-up only)
   static constexpr int DT = wig_size(L) * kET;                  // fp16 transposed D, [entry][edge]
   static constexpr int km(int m) { return (L + 1 - m) * kC; }   // GEMM K (= N) of block m
   static constexpr int astride(int m) { return km(m) + 8; }     // bf16 per A row (padded)
@@ -115,22 +124,17 @@ struct Shape {
     return has1(m, (G - sbase(m)) / ks(m));
   }
   static constexpr int64_t wave_bytes(int m) { return wblock(m) * 16; }
-  // two A regions: even m in A0, odd m in A1 (block m+1 is built while m runs)
-  static constexpr int amax_par(int par) {
-    int b = 0;
-    for (int m = par; m <= L; m += 2) b = abytes(m) > b ? abytes(m) : b;
-    return b;
-  }
-  static constexpr int off_A1 = (amax_par(0) + 255) / 256 * 256;
-  // LDS layout (bytes)
-  static constexpr int off_D = off_A1 + (amax_par(1) + 255) / 256 * 256;
-  static constexpr int off_DT = off_D + kET * DSZ * 4;
+  // LDS layout (bytes): one GEMM operand region, which also holds the fp32
+  // D of the chunk while the recursion runs
+  static constexpr int off_DT = (amax() > kET * DSZ * 4 ? amax() : kET * DSZ * 4 + 255) / 256 * 256;
   static constexpr int off_rbf = off_DT + DT * 2;
   static constexpr int off_alpha = off_rbf + kET * 8 * 4;
   static constexpr int off_q = off_alpha + kET * kH * 4;
-  static constexpr int off_j = off_q + kC * 4;
+  static constexpr int off_j = off_q + 2 * kC * 4;
   static constexpr int off_stat = off_j + kET * 4;
-  static constexpr int total = off_stat + 3 * kH * 4;
+  static constexpr int off_work = off_stat + 5 * kH * 4;
+  static constexpr int total = off_work + 2 * 4;
+  static_assert(total <= 80 * 1024, "two workgroups per CU");
 };
 
 template <typename V>
@@ -181,12 +185,25 @@ __device__ __forceinline__ f32x4 mfma16_f16(const f16x8 a, const f16x8 b, const 
 }
 
 // Node accumulator of one degree lo for this wave's 32 channels: two 16x16
-// MFMA tiles (rows n = 0..15 >= 2 lo + 1, columns = channels 0-15 and 16-31
-// of the wave).  Lane l holds rows 4 (l / 16) + r, column l % 16.
+// MFMA tiles (columns = channels 0-15 and 16-31 of the wave).  Lane l holds
+// rows 4 (l / 16) + r, column l % 16.
 struct NodeAcc {
   f32x4 a;   // channels 32 w + 0..15
   f32x4 b;   // channels 32 w + 16..31
 };
+
+// A chunk carries the edges of at most two destination atoms: A (the first
+// nA edge slots) and B (the next nB, starting B's list).  For lo <= 3 both
+// share acc[lo]: rows 0-7 hold A's 2 lo + 1 output rows (lanes 0-31) and
+// rows 8-15 B's (lanes 32-63).  Degree 4 needs 9 rows, so B's part of it
+// goes to `hi`.  B's rows are zero whenever a chunk starts.
+template <int L>
+struct NodeState {
+  NodeAcc acc[L + 1];
+  NodeAcc hi;
+};
+template <int LO>
+__host__ __device__ constexpr bool packed_lo() { return 2 * LO + 1 <= 8; }
 
 // Rotate-out contraction step: acc[n][c] += sum_k G[n][k] U[k][c] over the 16
 // (edge, sign) slots this k-step carries.  The 32x32 GEMM result gives lane l
@@ -216,7 +233,8 @@ struct MfmaParams {
   const f16x8* radpk;
   const int32_t* order;   // destination atoms in spatial (Morton) order
   int64_t n_atoms;
-  int64_t per_xcd;        // ceil(n_atoms / 8)
+  int32_t* queue;         // per-XCD count of destinations handed out (zero at launch)
+  int wg_per_xcd;
   float* out;
   float* out_lse;
   float box[3];
@@ -225,17 +243,25 @@ struct MfmaParams {
 };
 
 struct Smem {
-  uint16_t* A0;    // GEMM operand of even |m| blocks
-  uint16_t* A1;    // GEMM operand of odd |m| blocks
-  float* D;
-  _Float16* DT;
+  uint16_t* A;     // GEMM operand of the current |m| block
+  float* D;        // fp32 D^0..D^L of the chunk (aliases A; set-up only)
+  _Float16* DT;    // fp16 D, [entry][edge]
   float* rbf;
-  float* alpha;
-  float* q;
+  float* alpha;    // [edge][head]: logits, then softmax weights
+  float* q;        // [2][C]: queries of destinations A and B
   int* j;
-  float* m_run;
-  float* l_run;
-  float* scale;
+  float* m_run;    // [2][H] running max of A and B
+  float* l_run;    // [2][H] running normaliser of A and B
+  float* scale;    // [H] rescale of A's accumulators in this chunk
+  int* work;       // [2] the stretch handed to this workgroup
+};
+
+// Per-lane constants of one chunk.
+struct Lane {
+  float alpha[16];   // softmax weights of the 16 edges whose GEMM rows the lane holds (its head)
+  f16x8 arbf[3];     // radial-basis A operands (all 32 edges; edges 0-15; edges 16-31)
+  u32x4 mk[2];       // per fp16 pair of the rotate-out operand: keep A's edges (edge groups 0, 16)
+  uint32_t flip;     // ~0 on lanes whose packed rows (n >= 8) belong to B
 };
 
 // Rotate-in task tau of block MN for this thread: degree l = MN + tau / 2,
@@ -259,17 +285,16 @@ __device__ __forceinline__ void task_load(const MfmaParams& p, const Smem& s, in
 template <int L, int MN, int TAU, int N>
 __device__ __forceinline__ void task_term(const Smem& s, int tid, const uint4 (&raw)[2 * L + 1], float (&xp)[8],
                                           float (&xm)[8]) {
-  using S = Shape<L>;
   constexpr int l = MN + (TAU >> 1);
   const int e = (tid >> 4) + 16 * (TAU & 1);
-  const float* De = s.D + e * S::DSZ + doff(l);
+  const _Float16* dl = s.DT + wig_off(l) * kET + e;
   float hv[8];
   unpack_bf16x8(raw[N], hv);
-  const float dp = De[(l + MN) * dpad(l) + N];
+  const float dp = static_cast<float>(dl[((l + MN) * (2 * l + 1) + N) * kET]);
 #pragma unroll
   for (int q = 0; q < 8; ++q) xp[q] = (N == 0 ? 0.0f : xp[q]) + dp * hv[q];
   if constexpr (MN > 0) {
-    const float dm = De[(l - MN) * dpad(l) + N];
+    const float dm = static_cast<float>(dl[((l - MN) * (2 * l + 1) + N) * kET]);
 #pragma unroll
     for (int q = 0; q < 8; ++q) xm[q] = (N == 0 ? 0.0f : xm[q]) + dm * hv[q];
   }
@@ -301,58 +326,21 @@ __device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid
   task_store<L, MN, TAU>(A, tid, xp, xm);
 }
 
-// Stand-alone rotate-in of block 0 (the start of a chunk): the loads of task
-// tau+1 are issued before task tau's arithmetic.
-template <int L>
-__device__ __forceinline__ void build_a0(const MfmaParams& p, const Smem& s, int tid) {
+// Rotate-in of block MN: all its tasks, the loads of task tau+1 issued before
+// task tau's arithmetic.
+template <int L, int MN>
+__device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, int tid) {
   static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
+  constexpr int NT = 2 * (L + 1 - MN);
   tid = opaque(tid);
   uint4 raw[2][2 * L + 1];
-  task_load<L, 0, 0>(p, s, tid, raw[0]);
-  static_for<2 * (L + 1)>([&](auto tc) {
+  task_load<L, MN, 0>(p, s, tid, raw[0]);
+  static_for<NT>([&](auto tc) {
     constexpr int tau = decltype(tc)::value;
-    if constexpr (tau + 1 < 2 * (L + 1)) task_load<L, 0, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
-    task_compute<L, 0, tau>(s, s.A0, tid, raw[tau & 1]);
+    if constexpr (tau + 1 < NT) task_load<L, MN, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
+    task_compute<L, MN, tau>(s, s.A, tid, raw[tau & 1]);
   });
 }
-
-// Compile-time schedule of block M+1's rotate-in inside block M's k-steps:
-// tasks run one after another; task tau issues its loads at start(tau),
-// accumulates term n at start(tau) + delta + n, and stores one step later.
-template <int L, int M>
-struct TaskSched {
-  using S = Shape<L>;
-  static constexpr int NT = M < L ? 2 * (L - M) : 0;
-  static constexpr int W(int tau) { return 2 * (M + 1 + tau / 2) + 1; }
-  static constexpr int work() {
-    int w = 0;
-    for (int t = 0; t < NT; ++t) w += W(t) + 1;
-    return w;
-  }
-  static constexpr int delta() {
-    if (NT == 0) return 0;
-    const int d = (S::tot(M) - work()) / NT;
-    return d > 6 ? 6 : d;
-  }
-  static constexpr int start(int tau) {
-    int o = 0;
-    for (int t = 0; t < tau; ++t) o += delta() + W(t) + 1;
-    return o;
-  }
-  // task whose loads are issued at step g (or -1)
-  static constexpr int load_at(int g) {
-    for (int t = 0; t < NT; ++t)
-      if (g == start(t)) return t;
-    return -1;
-  }
-  // task and term accumulated at step g (term == W: store), or task -1
-  static constexpr int term_task(int g) {
-    for (int t = 0; t < NT; ++t)
-      if (g >= start(t) + delta() && g <= start(t) + delta() + W(t)) return t;
-    return -1;
-  }
-  static constexpr int term_n(int g) { return term_task(g) < 0 ? 0 : g - start(term_task(g)) - delta(); }
-};
 
 // A operand of the rotate-out contraction: row n of D^l rows `mrow`, for the
 // 8 edges eg + crow(q, h), q = 0..7, as fp16.  Rows n >= 2l+1 are zero.
@@ -366,6 +354,29 @@ __device__ __forceinline__ f16x8 dt_frag(const _Float16* row_base, int eg, int h
   return v;
 }
 
+// Rotate-out of one fragment: D^LO row `row`, the 8 edges of group eg that
+// this lane's k-slots carry, contracted with u into the node accumulators.
+// Packed degrees: the lane's D column is n mod 8 and the G entries of the
+// other destination's edges are zero.  Degree 4: A's edges go to acc[4] and,
+// when the chunk has a B, B's edges to hi.
+template <int L, int LO, int ROW, int EG>
+__device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const Lane& ln, int lane, const f16x8 u,
+                                        bool has_b) {
+  constexpr int W = 2 * LO + 1;
+  const int n = lane & 15;
+  const int ncol = packed_lo<LO>() ? (n & 7) : n;
+  const bool grp_odd = (lane >> 4) & 1;    // lane group 1 or 3: channels 16-31
+  const _Float16* drow = s.DT + (wig_off(LO) + ROW * W + ncol) * kET;
+  const u32x4 g = __builtin_bit_cast(u32x4, dt_frag(drow, EG, lane >> 5, ncol < W));
+  const u32x4 mA = ln.mk[EG / 16];
+  if constexpr (packed_lo<LO>()) {
+    rotate_out_step(ns.acc[LO], __builtin_bit_cast(f16x8, g & (mA ^ ln.flip)), u, grp_odd);
+  } else {
+    rotate_out_step(ns.acc[LO], __builtin_bit_cast(f16x8, g & mA), u, grp_odd);
+    if (has_b) rotate_out_step(ns.hi, __builtin_bit_cast(f16x8, g & ~mA), u, grp_odd);
+  }
+}
+
 // 16-byte load of a B fragment through a buffer resource: the per-lane offset
 // stays in one VGPR and the k-step advances a scalar offset.
 __device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -374,7 +385,7 @@ __device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-constexpr int kRing = 8;   // weight k-steps in flight per wave
+constexpr int kRing = 4;   // weight k-steps in flight per wave
 struct WRing {
   bf16x8 r[kRing][2];
 };
@@ -386,9 +397,11 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
   constexpr int m = S::stream_m(G);
   constexpr int off0 = S::stream_off(G, 0);
   constexpr int off1 = S::stream_off(G, 1);
-  const int wo = static_cast<int>(wave * S::wave_bytes(m));
-  ring.r[G % kRing][0] = load_b(wrsrc, voff, wo + off0);
-  if constexpr (S::stream_has1(G)) ring.r[G % kRing][1] = load_b(wrsrc, voff, wo + off1);
+  // the wave's column term goes into the per-lane offset, so that the scalar
+  // offsets are constants (rematerialised, never kept live in SGPRs)
+  const int vo = voff + wave * static_cast<int>(S::wave_bytes(m));
+  ring.r[G % kRing][0] = load_b(wrsrc, vo, off0);
+  if constexpr (S::stream_has1(G)) ring.r[G % kRing][1] = load_b(wrsrc, vo, off1);
 }
 
 // GEMM of block M for this wave's 32 output channels, then the epilogue of
@@ -399,38 +412,26 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
 //
 // Software pipeline, all fixed at compile time: the weight stream runs kRing
 // k-steps ahead (continuing into the next block and the next chunk, whose
-// weights are the same), A fragments one step ahead, and the rotate-in of
-// block M+1 is spread over the k-steps (TaskSched: one term per step) so that
-// its VALU work and feature loads overlap the MFMAs.
-// A scheduling barrier after every k-step keeps the compiler from undoing
-// this order.
+// weights are the same) and A fragments one step ahead.  A scheduling
+// barrier after every k-step keeps the compiler from undoing this order.
 template <int L, int M>
 __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc,
-                                          int tid, int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                          NodeAcc (&nacc)[L + 1], WRing& ring) {
+                                          int tid, int wave, const Lane& ln, bool has_b, NodeState<L>& ns,
+                                          WRing& ring) {
   using S = Shape<L>;
   constexpr int KS = S::ks(M);
   constexpr int stride = S::astride(M);
-  using TS = TaskSched<L, M>;
-  constexpr int NT = TS::NT;                          // rotate-in tasks of block M+1 per thread
-  static_assert(NT == 0 || TS::delta() >= 2, "too few k-steps to hide the next rotate-in");
-  uint16_t* const Acur = (M % 2 == 0) ? s.A0 : s.A1;
-  uint16_t* const Anext = (M % 2 == 0) ? s.A1 : s.A0;
   tid = opaque(tid);
   const int lane = tid & 63;
   const int half = lane >> 5;
   const int c_own = 32 * wave + (lane & 31);
-  const int n = lane & 15;                 // D row of the rotate-out A operand
-  const bool grp_odd = (lane >> 4) & 1;    // lane group 1 or 3: channels 16-31
   const int voff = lane * 16;
   const f16x8 zero8 = {};
-  const uint16_t* ap0 = Acur + (lane & 31) * stride + 8 * half;
+  const uint16_t* ap0 = s.A + (lane & 31) * stride + 8 * half;
   const uint16_t* ap1 = ap0 + 32 * stride;   // second row tile (m > 0 only)
   bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0);
   bf16x8 a1 = {};
   if constexpr (M > 0) a1 = *reinterpret_cast<const bf16x8*>(ap1);
-  uint4 raw[2 * L + 1];
-  float txp[8], txm[8];
   static_for<S::nb(M)>([&](auto bc) {
     constexpr int b = decltype(bc)::value;
     f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
@@ -462,17 +463,6 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
       }
       a0 = a0n;
       a1 = a1n;
-      if constexpr (NT > 0) {
-        constexpr int MN = M < L ? M + 1 : L;
-        constexpr int tl = TS::load_at(g);
-        if constexpr (tl >= 0) task_load<L, MN, tl>(p, s, tid, raw);
-        constexpr int tt = TS::term_task(g);
-        if constexpr (tt >= 0) {
-          constexpr int tn = TS::term_n(g);
-          if constexpr (tn < TS::W(tt)) task_term<L, MN, tt, tn>(s, tid, raw, txp, txm);
-          else task_store<L, MN, tt>(Anext, tid, txp, txm);
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (M == 0) {
@@ -482,37 +472,32 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
           constexpr int lo = S::blk_lo(M, b, f);
           const f32x16& c0 = f == 0 ? c00 : c01;
           const f16x8 brad = f == 0 ? brad0 : brad1;
-          const f32x16 rho = mfma_f16(arbf[0], brad, f32x16{});
+          const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
           float u[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) u[r] = alpha[r] * rho[r] * c0[r];
-          const bool nvalid = n < 2 * lo + 1;
-          const _Float16* drow = s.DT + wig_off(lo) * kET + (lo * (2 * lo + 1) + n) * kET;
-          rotate_out_step(nacc[lo], dt_frag(drow, 0, half, nvalid), to_vec8<f16x8>(u), grp_odd);
-          rotate_out_step(nacc[lo], dt_frag(drow, 16, half, nvalid), to_vec8<f16x8>(u + 8), grp_odd);
+          for (int r = 0; r < 16; ++r) u[r] = ln.alpha[r] * rho[r] * c0[r];
+          rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
+          rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
         }
       });
     } else {
       constexpr int lo = S::blk_lo(M, b, 0);
       const f16x8 brad = brad0;
-      const bool nvalid = n < 2 * lo + 1;
-      const _Float16* dt_lo = s.DT + wig_off(lo) * kET;
-      const _Float16* drow_p = dt_lo + ((lo + M) * (2 * lo + 1) + n) * kET;
-      const _Float16* drow_m = dt_lo + ((lo - M) * (2 * lo + 1) + n) * kET;
-      auto tile = [&](int t, const f32x16& C1, const f32x16& C2) {
-        const f32x16 rho = mfma_f16(arbf[1 + t], brad, f32x16{});
+      static_for<2>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        const f32x16& C1 = t == 0 ? c00 : c10;
+        const f32x16& C2 = t == 0 ? c01 : c11;
+        const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
         float up[8], um[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          const float sc = alpha[r + 8 * t] * rho[r];
+          const float sc = ln.alpha[r + 8 * t] * rho[r];
           up[r] = sc * (C1[r] - C2[r + 8]);
           um[r] = sc * (C2[r] + C1[r + 8]);
         }
-        rotate_out_step(nacc[lo], dt_frag(drow_p, 16 * t, half, nvalid), to_vec8<f16x8>(up), grp_odd);
-        rotate_out_step(nacc[lo], dt_frag(drow_m, 16 * t, half, nvalid), to_vec8<f16x8>(um), grp_odd);
-      };
-      tile(0, c00, c01);
-      tile(1, c10, c11);
+        rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
+        rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+      });
     }
   });
 }
@@ -545,87 +530,218 @@ __device__ __forceinline__ void wig_level(const Smem& s, int tid) {
   if constexpr (l < L) wig_level<L, l + 1>(s, tid);
 }
 
-// Blocks M = 0..L of one chunk: GEMM of M (while block M+1 is rotated in),
-// then a barrier so that the next block's operand is complete.
+// Blocks M = 0..L of one chunk: rotate-in of M into the operand region, a
+// barrier, the GEMM of M, and a barrier before the region is rewritten.
 template <int L, int M>
 __device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid,
-                                         int wave, const f16x8 (&arbf)[3], const float (&alpha)[16],
-                                         NodeAcc (&nacc)[L + 1], WRing& ring) {
-  mma_block<L, M>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
+                                         int wave, const Lane& ln, bool has_b, NodeState<L>& ns, WRing& ring) {
+  rotate_in<L, M>(p, s, tid);
   __syncthreads();
-  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
+  mma_block<L, M>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+  __syncthreads();
+  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
 }
 
+// Writes destination A's output (the normalised node accumulator, lanes of
+// rows 0-7 for packed degrees) and its log-normaliser, then moves B's partial
+// state into A's place and clears B's.
 template <int L>
-__global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
+__device__ __forceinline__ void finish_a(const MfmaParams& p, const Smem& s, NodeState<L>& ns, int64_t i, int tid,
+                                         int wave) {
+  constexpr int K = Shape<L>::K;
+  tid = opaque(tid);
+  const int lane = tid & 63;
+  __syncthreads();
+  {
+    const int c0 = 32 * wave + (lane & 15);
+    const float la = s.l_run[2 * wave], lb = s.l_run[2 * wave + 1];
+    const float ia = la > 0.0f ? 1.0f / la : 0.0f, ib = lb > 0.0f ? 1.0f / lb : 0.0f;
+    static_for<L + 1>([&](auto lc) {
+      constexpr int lo = decltype(lc)::value;
+      if (packed_lo<lo>() ? lane < 32 : true) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int n = 4 * (lane >> 4) + r;
+          if (n < 2 * lo + 1) {
+            float* o = p.out + (i * K + lo * lo + n) * kC + c0;
+            o[0] = ns.acc[lo].a[r] * ia;
+            o[16] = ns.acc[lo].b[r] * ib;
+          }
+        }
+      }
+    });
+  }
+  if (p.out_lse && tid < kH)
+    p.out_lse[i * kH + tid] = s.l_run[tid] > 0.0f ? s.m_run[tid] + logf(s.l_run[tid]) : -INFINITY;
+  __syncthreads();
+  if (tid < kH) {
+    s.m_run[tid] = s.m_run[kH + tid];
+    s.l_run[tid] = s.l_run[kH + tid];
+    s.m_run[kH + tid] = -INFINITY;
+    s.l_run[kH + tid] = 0.0f;
+  }
+  static_for<L + 1>([&](auto lc) {
+    constexpr int lo = decltype(lc)::value;
+    if constexpr (packed_lo<lo>()) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float va = __shfl_down(ns.acc[lo].a[r], 32);
+        const float vb = __shfl_down(ns.acc[lo].b[r], 32);
+        ns.acc[lo].a[r] = lane < 32 ? va : 0.0f;
+        ns.acc[lo].b[r] = lane < 32 ? vb : 0.0f;
+      }
+    } else {
+      ns.acc[lo] = ns.hi;
+      ns.hi = NodeAcc{f32x4{}, f32x4{}};
+    }
+  });
+}
+
+// One stretch [s_lo, s_hi) of the spatial order: the destinations'
+// concatenated neighbour lists in chunks of 32 edge slots; a chunk holds the
+// rest of the current atom A and, when A ends inside it, the start of the
+// next atom B.  Only the stretch's last chunk is padded.
+template <int L>
+__device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
+                                        int wave, int64_t s_lo, int64_t s_hi, NodeState<L>& ns, WRing& ring);
+
+// A persistent workgroup takes stretches of destinations until its XCD's
+// range is exhausted.
+template <int L>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn_mfma(MfmaParams p) {
   using S = Shape<L>;
-  constexpr int K = S::K;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Smem s;
-  s.A0 = reinterpret_cast<uint16_t*>(smem);
-  s.A1 = reinterpret_cast<uint16_t*>(smem + S::off_A1);
-  s.D = reinterpret_cast<float*>(smem + S::off_D);
+  s.A = reinterpret_cast<uint16_t*>(smem);
+  s.D = reinterpret_cast<float*>(smem);
   s.DT = reinterpret_cast<_Float16*>(smem + S::off_DT);
   s.rbf = reinterpret_cast<float*>(smem + S::off_rbf);
   s.alpha = reinterpret_cast<float*>(smem + S::off_alpha);
   s.q = reinterpret_cast<float*>(smem + S::off_q);
   s.j = reinterpret_cast<int*>(smem + S::off_j);
   s.m_run = reinterpret_cast<float*>(smem + S::off_stat);
-  s.l_run = s.m_run + kH;
-  s.scale = s.l_run + kH;
+  s.l_run = s.m_run + 2 * kH;
+  s.scale = s.l_run + 2 * kH;
+  s.work = reinterpret_cast<int*>(smem + S::off_work);
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid0 = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
   const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<bf16x8*>(p.wpk), (short)0, static_cast<int>(S::wtotal() * 16), 0x00020000);
-  // Workgroups are dealt to the 8 XCDs round-robin; give each XCD one
-  // contiguous stretch of the spatial order so that neighbouring destinations
-  // (which share most neighbours) run on the same L2.
-  const int64_t slot = (int64_t)(blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
-  if (slot >= p.n_atoms) return;
-  const int64_t i = p.order[slot];
-
-  if (tid < kC) s.q[tid] = p.q[i * kC + tid];
-  if (tid < kH) { s.m_run[tid] = -INFINITY; s.l_run[tid] = 0.0f; }
-  NodeAcc nacc[L + 1];
+  if (tid0 < 2 * kH) { s.m_run[tid0] = -INFINITY; s.l_run[tid0] = 0.0f; }
+  NodeState<L> ns;
 #pragma unroll
-  for (int l = 0; l <= L; ++l) nacc[l] = NodeAcc{f32x4{}, f32x4{}};
-  const float xi[3] = {p.pos[3 * i], p.pos[3 * i + 1], p.pos[3 * i + 2]};
-  const int64_t e_beg = p.row_ptr[i], e_end = p.row_ptr[i + 1];
+  for (int l = 0; l <= L; ++l) ns.acc[l] = NodeAcc{f32x4{}, f32x4{}};
+  ns.hi = NodeAcc{f32x4{}, f32x4{}};
   // the weight stream is the same for every chunk: prime it once
   WRing ring;
   {
-    const int voff = opaque(lane) * 16;
+    const int voff = opaque(tid0 & 63) * 16;
     static_for<kRing>([&](auto Gc) { wring_load<L, decltype(Gc)::value>(ring, wrsrc, voff, wave); });
   }
 
-  for (int64_t e0 = e_beg; e0 < e_end; e0 += kET) {
-    const int ne = (e_end - e0) < kET ? static_cast<int>(e_end - e0) : kET;
+  // Workgroups are dealt to the 8 XCDs round-robin.  Each XCD owns one
+  // eighth of the spatial order (neighbouring destinations share most
+  // neighbours, so they should meet in the same L2) and hands it out in
+  // stretches whose size shrinks as the range drains (guided scheduling).
+  const int xcd = blockIdx.x & 7;
+  const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
+  const int64_t span = x_hi - x_lo;
+  for (;;) {
+    if (tid0 == 0) {
+      const int done = __hip_atomic_load(p.queue + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      int64_t take = (span - done) / (2 * p.wg_per_xcd);
+      take = take < kMinStretch ? kMinStretch : (take > kMaxStretch ? kMaxStretch : take);
+      s.work[0] = atomicAdd(p.queue + xcd, static_cast<int>(take));
+      s.work[1] = static_cast<int>(take);
+    }
+    __syncthreads();
+    const int64_t first = s.work[0], take = s.work[1];
+    __syncthreads();
+    if (first >= span) break;
+    const int64_t s_lo = x_lo + first, s_hi = x_lo + (first + take < span ? first + take : span);
+    stretch<L>(p, s, wrsrc, tid0, wave, s_lo, s_hi, ns, ring);
+  }
+}
+
+template <int L>
+__device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
+                                        int wave, int64_t s_lo, int64_t s_hi, NodeState<L>& ns, WRing& ring) {
+  using S = Shape<L>;
+  constexpr int K = S::K;
+  auto degree = [&](int64_t sl) {
+    const int64_t i = p.order[sl];
+    return p.row_ptr[i + 1] - p.row_ptr[i];
+  };
+  // atoms without neighbours: zero output, log-normaliser -inf
+  for (int64_t sl = s_lo + tid0; sl < s_hi; sl += kThreads) {
+    if (degree(sl) == 0) {
+      const int64_t i = p.order[sl];
+      for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
+      if (p.out_lse)
+        for (int h = 0; h < kH; ++h) p.out_lse[i * kH + h] = -INFINITY;
+    }
+  }
+  auto next_nz = [&](int64_t sl) {
+    while (sl < s_hi && degree(sl) == 0) ++sl;
+    return sl;
+  };
+  int64_t sa = next_nz(s_lo), a0 = 0;
+  while (sa < s_hi) {
+    // lane-dependent values are derived afresh in every chunk rather than
+    // hoisted out of the loop and kept live (or spilled) across it
+    const int tid = opaque(tid0);
+    const int lane = tid & 63;
+    // chunk plan (uniform): nA edges of A from offset a0, then nB of B
+    const int64_t ia = p.order[sa];
+    const int64_t deg_a = p.row_ptr[ia + 1] - p.row_ptr[ia];
+    const int nA = static_cast<int>(deg_a - a0 < kET ? deg_a - a0 : kET);
+    const bool a_done = a0 + nA == deg_a;
+    int64_t sb = s_hi, ib = ia;
+    int nB = 0;
+    bool b_done = false;
+    if (a_done && nA < kET) {
+      sb = next_nz(sa + 1);
+      if (sb < s_hi) {
+        ib = p.order[sb];
+        const int64_t deg_b = p.row_ptr[ib + 1] - p.row_ptr[ib];
+        nB = static_cast<int>(deg_b < kET - nA ? deg_b : kET - nA);
+        b_done = nB == deg_b;
+      }
+    }
+    const int ne = nA + nB;
+    const bool has_b = nB > 0;
+    const int64_t ea = p.row_ptr[ia] + a0, eb = p.row_ptr[ib];
+
+    if (tid < kC) s.q[tid] = p.q[ia * kC + tid];
+    else if (has_b) s.q[tid] = p.q[ib * kC + (tid - kC)];
     __syncthreads();
     // edge frames, D^0, D^1 and the radial basis: one lane per edge
     if (tid < kET) {
+      const bool in_b = tid >= nA;
+      const int64_t id = in_b ? ib : ia;
       float* De = s.D + tid * S::DSZ;
       float R[3][3] = {{0, 0, 0}, {0, 0, 0}, {0, 0, 0}};
       float d0 = 0.0f;
       float e8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      int j = static_cast<int>(i);
+      int j = static_cast<int>(id);
       if (tid < ne) {
-        j = p.col[e0 + tid];
+        j = p.col[in_b ? eb + (tid - nA) : ea + tid];
         float r3[3];
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
-          float dx = p.pos[3 * (int64_t)j + d] - xi[d];
+          float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * id + d];
           if (p.periodic) {
             if (dx > 0.5f * p.box[d]) dx -= p.box[d];
             else if (dx < -0.5f * p.box[d]) dx += p.box[d];
           }
           r3[d] = dx;
         }
-        const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-        const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+        const float rr = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
+        const float u[3] = {r3[0] / rr, r3[1] / rr, r3[2] / rr};
         edge_rotation(u, R);
         d0 = 1.0f;
-        radial_basis8(r, p.cutoff, e8);
+        radial_basis8(rr, p.cutoff, e8);
       }
       s.j[tid] = j;
       De[0] = d0;
@@ -647,85 +763,95 @@ __global__ void __launch_bounds__(kThreads, 1) k_attn_mfma(MfmaParams p) {
       const int e = tid >> 3, h = tid & 7;
       float sv = -INFINITY;
       if (e < ne) {
-        const int j = p.col[e0 + e];
+        const int j = p.col[e >= nA ? eb + (e - nA) : ea + e];
         const float4* kp = reinterpret_cast<const float4*>(p.k + (int64_t)j * kC + h * kDH);
+        const float* qv = s.q + (e >= nA ? kC : 0) + h * kDH;
         float d = 0.0f;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float4 kv = kp[t];
-          const float* qv = s.q + h * kDH + 4 * t;
-          d += kv.x * qv[0] + kv.y * qv[1] + kv.z * qv[2] + kv.w * qv[3];
+          d += kv.x * qv[4 * t] + kv.y * qv[4 * t + 1] + kv.z * qv[4 * t + 2] + kv.w * qv[4 * t + 3];
         }
         sv = d * 0.25f;
       }
       s.alpha[e * kH + h] = sv;
     }
     __syncthreads();
-    // online softmax update (one thread per head) while the others extend D
-    if (tid < kH) {
-      const int h = tid;
-      float mx = s.m_run[h];
-      for (int e = 0; e < ne; ++e) mx = fmaxf(mx, s.alpha[e * kH + h]);
-      const float sc = expf(s.m_run[h] - mx);
-      float sum = 0.0f;
-      for (int e = 0; e < kET; ++e) {
-        const float a = e < ne ? expf(s.alpha[e * kH + h] - mx) : 0.0f;
-        s.alpha[e * kH + h] = a;
-        sum += a;
+    // online softmax update, one thread per (destination, head), while the
+    // others extend D; padding slots get weight 0
+    if (tid < 2 * kH) {
+      const int d = tid / kH, h = tid % kH;
+      const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
+      if (b1 > b0) {
+        float mx = s.m_run[d * kH + h];
+        for (int e = b0; e < b1; ++e) mx = fmaxf(mx, s.alpha[e * kH + h]);
+        const float sc = expf(s.m_run[d * kH + h] - mx);
+        float sum = 0.0f;
+        for (int e = b0; e < b1; ++e) {
+          const float a = expf(s.alpha[e * kH + h] - mx);
+          s.alpha[e * kH + h] = a;
+          sum += a;
+        }
+        s.l_run[d * kH + h] = s.l_run[d * kH + h] * sc + sum;
+        s.m_run[d * kH + h] = mx;
+        if (d == 0) s.scale[h] = sc;
       }
-      s.l_run[h] = s.l_run[h] * sc + sum;
-      s.m_run[h] = mx;
-      s.scale[h] = sc;
+      if (d == 1)
+        for (int e = ne; e < kET; ++e) s.alpha[e * kH + h] = 0.0f;
     }
     if constexpr (L >= 2) wig_level<L, 2>(s, tid);
     __syncthreads();
-    // per-lane constants of this chunk: attention weights of the 16 edges
-    // whose rows this lane holds, the radial-basis A operands, and the
-    // rescale of the running accumulators
-    float alpha[16];
-    f16x8 arbf[3];
+    // per-lane constants of this chunk, and the rescale of A's running
+    // accumulators (B's rows are zero)
+    Lane ln;
     {
-      const int ln = opaque(lane);
-      const int half = ln >> 5;
-      const int h_own = (32 * wave + (ln & 31)) / kDH;
+      const int lnr = opaque(lane);
+      const int half = lnr >> 5;
+      const int h_own = (32 * wave + (lnr & 31)) / kDH;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) alpha[r] = s.alpha[crow(r, half) * kH + h_own];
+      for (int q = 0; q < 16; ++q) ln.alpha[q] = s.alpha[crow(q, half) * kH + h_own];
       // the wave's 32 channels are heads 2w and 2w+1
-      const float sa = s.scale[2 * wave], sb = s.scale[2 * wave + 1];
+      const float sa_ = s.scale[2 * wave], sb_ = s.scale[2 * wave + 1];
 #pragma unroll
       for (int l = 0; l <= L; ++l) {
-        nacc[l].a *= sa;
-        nacc[l].b *= sb;
+        ns.acc[l].a *= sa_;
+        ns.acc[l].b *= sb_;
       }
       float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      const int r = ln & 31;
-      arbf[0] = to_vec8<f16x8>(half == 0 ? s.rbf + r * 8 : z);
-      arbf[1] = to_vec8<f16x8>(half == 0 ? s.rbf + (r & 15) * 8 : z);
-      arbf[2] = to_vec8<f16x8>(half == 0 ? s.rbf + (16 + (r & 15)) * 8 : z);
-    }
-    build_a0<L>(p, s, tid);
-    __syncthreads();
-    do_block<L, 0>(p, s, wrsrc, tid, wave, arbf, alpha, nacc, ring);
-  }
-  __syncthreads();
-  {
-    const int c0 = 32 * wave + (lane & 15);
-    const float la = s.l_run[2 * wave], lb = s.l_run[2 * wave + 1];
-    const float ia = la > 0.0f ? 1.0f / la : 0.0f, ib = lb > 0.0f ? 1.0f / lb : 0.0f;
+      const int rr = lnr & 31;
+      ln.arbf[0] = to_vec8<f16x8>(half == 0 ? s.rbf + rr * 8 : z);
+      ln.arbf[1] = to_vec8<f16x8>(half == 0 ? s.rbf + (rr & 15) * 8 : z);
+      ln.arbf[2] = to_vec8<f16x8>(half == 0 ? s.rbf + (16 + (rr & 15)) * 8 : z);
 #pragma unroll
-    for (int lo = 0; lo <= L; ++lo)
+      for (int g = 0; g < 2; ++g)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = 4 * (lane >> 4) + r;
-        if (n < 2 * lo + 1) {
-          float* o = p.out + (i * K + lo * lo + n) * kC + c0;
-          o[0] = nacc[lo].a[r] * ia;
-          o[16] = nacc[lo].b[r] * ib;
+        for (int q = 0; q < 4; ++q) {
+          const int t0 = 16 * g + 8 * (q >> 1) + 4 * half + 2 * (q & 1);
+          ln.mk[g][q] = (t0 < nA ? 0x0000FFFFu : 0u) | (t0 + 1 < nA ? 0xFFFF0000u : 0u);
         }
+      ln.flip = (lnr & 8) ? ~0u : 0u;
+    }
+    do_block<L, 0>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+    // advance: finish A (and B if it also ended), B becomes A
+    if (a_done) {
+      finish_a<L>(p, s, ns, ia, tid, wave);
+      if (has_b) {
+        if (b_done) {
+          finish_a<L>(p, s, ns, ib, tid, wave);
+          sa = next_nz(sb + 1);
+          a0 = 0;
+        } else {
+          sa = sb;
+          a0 = nB;
+        }
+      } else {
+        sa = next_nz(sa + 1);
+        a0 = 0;
       }
+    } else {
+      a0 += nA;
+    }
   }
-  if (p.out_lse && tid < kH)
-    p.out_lse[i * kH + tid] = s.l_run[tid] > 0.0f ? s.m_run[tid] + logf(s.l_run[tid]) : -INFINITY;
 }
 
 // Logical SO(2) weights -> B-fragment image: vector v holds, for lane
@@ -774,7 +900,11 @@ __global__ void k_pack_rad(const uint16_t* __restrict__ w, f16x8* __restrict__ o
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
 constexpr int kOrderBins = 1 << (3 * kOrderBits);
 
-__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
+// Bounding box of the positions; also clears the per-XCD work counters of the
+// layer kernel that follows.
+__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out,
+                           int32_t* __restrict__ queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
   __shared__ float smin[3][256], smax[3][256];
   float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
@@ -830,7 +960,7 @@ __global__ void k_ord_scatter(int64_t n, const int32_t* __restrict__ key, const 
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, bins, cursor, bsum, bbox, total;
+  size_t w, rad, order, key, bins, cursor, bsum, bbox, queue, total;
 };
 
 template <int L>
@@ -847,6 +977,7 @@ MfmaWs mfma_ws_layout(int64_t n) {
   m.cursor = take(sizeof(int32_t) * kOrderBins);
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kOrderBins));
   m.bbox = take(8 * sizeof(float));
+  m.queue = take(8 * sizeof(int32_t));
   m.total = off;
   return m;
 }
@@ -866,12 +997,13 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   int32_t* cursor = reinterpret_cast<int32_t*>(wb + W.cursor);
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
+  int32_t* queue = reinterpret_cast<int32_t*>(wb + W.queue);
   const int64_t n = a->n_atoms;
   {
     // spatial order of the destination atoms: Morton code of a 64^3 grid over
     // the bounding box, counting-sorted (order only affects locality)
     const int64_t nb = (n + 255) / 256;
-    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox);
+    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox, queue);
     E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
     E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * kOrderBins, st));
     k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, bins);
@@ -900,7 +1032,18 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   p.radpk = radpk;
   p.order = order;
   p.n_atoms = n;
-  p.per_xcd = (n + 7) / 8;
+  // persistent grid: two workgroups per CU (the LDS and register budget),
+  // fewer when the system is small
+  int dev = 0, n_cu = 0;
+  E2A_HIP_CHECK(hipGetDevice(&dev));
+  E2A_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
+  const int64_t per_xcd_atoms = (n + 7) / 8;
+  int64_t wpx = (2 * (int64_t)n_cu + 7) / 8;
+  const int64_t by_size = (per_xcd_atoms + kMinStretch - 1) / kMinStretch;
+  if (wpx > by_size) wpx = by_size;
+  if (wpx < 1) wpx = 1;
+  p.queue = queue;
+  p.wg_per_xcd = static_cast<int>(wpx);
   p.out = a->out;
   p.out_lse = a->out_lse;
   for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
@@ -908,7 +1051,7 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   p.cutoff = a->cutoff;
   E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<L>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::total));
-  hipLaunchKernelGGL(k_attn_mfma<L>, dim3(8 * p.per_xcd), dim3(kThreads), S::total, st, p);
+  hipLaunchKernelGGL(k_attn_mfma<L>, dim3(8 * p.wg_per_xcd), dim3(kThreads), S::total, st, p);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }

@@ -129,3 +129,46 @@ def test_mfma_kernel_full_configs_sampled(B, name):
     log(f"[attn] mfma {name} rel-L2 {err:.3e} on {dest.size} atoms")
     assert err <= TOL_BF16
     assert np.max(np.abs(lse[dest] - want_lse)) <= 1e-4
+
+
+def cluster_geometry(sizes, cutoff, seed):
+    """Separated tight clusters: every atom of a cluster of size g has exactly
+    g - 1 neighbours (all pairs closer than the cutoff, clusters 3 cutoffs
+    apart), so the degrees of the system are chosen directly."""
+    rng = np.random.default_rng(seed)
+    pos = []
+    for c, g in enumerate(sizes):
+        centre = np.array([3.0 * cutoff * c, 0.5 * cutoff * (c % 3), 0.0])
+        v = rng.normal(size=(g, 3))
+        v *= (cutoff / 3.2) * rng.random((g, 1)) ** (1 / 3) / np.linalg.norm(v, axis=1, keepdims=True)
+        pos.append(centre + v)
+    pos = np.concatenate(pos).astype(np.float32)
+    return pos, None, None, {"clusters": list(sizes)}
+
+
+@pytest.mark.parametrize("L", [1, 4])
+def test_mfma_kernel_chunk_packing_degrees(B, L):
+    """Degrees 0 (several isolated atoms in a row), 1, 2, 4, 8, 16, 31, 32,
+    33 and 64: chunks that end inside an atom, hold two atoms, finish both,
+    or are filled exactly; every output compared."""
+    sizes = [1, 1, 1, 2, 3, 5, 9, 17, 1, 32, 33, 34, 2, 65, 1]
+    cutoff = float(np.float32(5.0))
+    geom = cluster_geometry(sizes, cutoff, seed=21)
+    w = make_config("tiny", L=L, C=128, H=8, dtype="bf16", geometry=geom)
+    w.cutoff = cutoff
+    log(f"[attn] mfma chunk packing L={L}: {w.n_atoms} atoms")
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    deg = np.diff(rp)
+    assert sorted(set(deg.tolist())) == sorted({g - 1 for g in sizes})
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    out, lse = run_gpu(B, w, d, "mfma")
+    want, want_lse = oracle_out(w, rp, col, None)
+    assert np.all(np.isfinite(out))
+    iso = deg == 0
+    assert np.all(out[iso] == 0) and np.all(np.isneginf(lse[iso]))
+    err = rel_l2(out, want)
+    log(f"[attn] mfma chunk packing L={L} rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
+    assert np.max(np.abs(lse[~iso] - want_lse[~iso])) <= 1e-4
