@@ -51,8 +51,7 @@ constexpr int kH = 8;        // heads
 constexpr int kDH = 16;      // channels per head
 constexpr int kET = 32;      // edges per chunk
 constexpr int kThreads = 256;
-constexpr int kMinStretch = 4;     // destinations per work grab: at least
-constexpr int kMaxStretch = 128;   // and at most
+constexpr int kMinPerWg = 4;       // destinations per workgroup, at least
 
 // Wigner-D rows in LDS are padded to a multiple of 4 floats (16-byte reads).
 __host__ __device__ constexpr int dpad(int l) { return ((2 * l + 1) + 3) / 4 * 4; }
@@ -132,8 +131,7 @@ struct Shape {
   static constexpr int off_q = off_alpha + kET * kH * 4;
   static constexpr int off_j = off_q + 2 * kC * 4;
   static constexpr int off_stat = off_j + kET * 4;
-  static constexpr int off_work = off_stat + 5 * kH * 4;
-  static constexpr int total = off_work + 2 * 4;
+  static constexpr int total = off_stat + 5 * kH * 4;
   static_assert(total <= 80 * 1024, "two workgroups per CU");
 };
 
@@ -233,7 +231,6 @@ struct MfmaParams {
   const f16x8* radpk;
   const int32_t* order;   // destination atoms in spatial (Morton) order
   int64_t n_atoms;
-  int32_t* queue;         // per-XCD count of destinations handed out (zero at launch)
   int wg_per_xcd;
   float* out;
   float* out_lse;
@@ -253,7 +250,6 @@ struct Smem {
   float* m_run;    // [2][H] running max of A and B
   float* l_run;    // [2][H] running normaliser of A and B
   float* scale;    // [H] rescale of A's accumulators in this chunk
-  int* work;       // [2] the stretch handed to this workgroup
 };
 
 // Per-lane constants of one chunk.
@@ -597,16 +593,17 @@ __device__ __forceinline__ void finish_a(const MfmaParams& p, const Smem& s, Nod
   });
 }
 
-// One stretch [s_lo, s_hi) of the spatial order: the destinations'
-// concatenated neighbour lists in chunks of 32 edge slots; a chunk holds the
-// rest of the current atom A and, when A ends inside it, the start of the
-// next atom B.  Only the stretch's last chunk is padded.
+// The destinations s_lo, s_lo + step, ... (< s_hi) of the spatial order:
+// their concatenated neighbour lists in chunks of 32 edge slots; a chunk
+// holds the rest of the current atom A and, when A ends inside it, the start
+// of the next atom B.  Only the last chunk is padded.
 template <int L>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
-                                        int wave, int64_t s_lo, int64_t s_hi, NodeState<L>& ns, WRing& ring);
+                                        int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
+                                        WRing& ring);
 
-// A persistent workgroup takes stretches of destinations until its XCD's
-// range is exhausted.
+// A persistent workgroup processes every wg_per_xcd-th destination of its
+// XCD's range.
 template <int L>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn_mfma(MfmaParams p) {
   using S = Shape<L>;
@@ -622,7 +619,6 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   s.m_run = reinterpret_cast<float*>(smem + S::off_stat);
   s.l_run = s.m_run + 2 * kH;
   s.scale = s.l_run + 2 * kH;
-  s.work = reinterpret_cast<int*>(smem + S::off_work);
 
   const int tid0 = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid0 >> 6);
@@ -641,32 +637,18 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
 
   // Workgroups are dealt to the 8 XCDs round-robin.  Each XCD owns one
-  // eighth of the spatial order (neighbouring destinations share most
-  // neighbours, so they should meet in the same L2) and hands it out in
-  // stretches whose size shrinks as the range drains (guided scheduling).
+  // eighth of the spatial order, dealt cyclically to its workgroups: at any
+  // time they work on neighbouring destinations, which share most of their
+  // neighbours' features in the XCD's L2.
   const int xcd = blockIdx.x & 7;
   const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
-  const int64_t span = x_hi - x_lo;
-  for (;;) {
-    if (tid0 == 0) {
-      const int done = __hip_atomic_load(p.queue + xcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      int64_t take = (span - done) / (2 * p.wg_per_xcd);
-      take = take < kMinStretch ? kMinStretch : (take > kMaxStretch ? kMaxStretch : take);
-      s.work[0] = atomicAdd(p.queue + xcd, static_cast<int>(take));
-      s.work[1] = static_cast<int>(take);
-    }
-    __syncthreads();
-    const int64_t first = s.work[0], take = s.work[1];
-    __syncthreads();
-    if (first >= span) break;
-    const int64_t s_lo = x_lo + first, s_hi = x_lo + (first + take < span ? first + take : span);
-    stretch<L>(p, s, wrsrc, tid0, wave, s_lo, s_hi, ns, ring);
-  }
+  stretch<L>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
 }
 
 template <int L>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
-                                        int wave, int64_t s_lo, int64_t s_hi, NodeState<L>& ns, WRing& ring) {
+                                        int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
+                                        WRing& ring) {
   using S = Shape<L>;
   constexpr int K = S::K;
   auto degree = [&](int64_t sl) {
@@ -674,7 +656,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     return p.row_ptr[i + 1] - p.row_ptr[i];
   };
   // atoms without neighbours: zero output, log-normaliser -inf
-  for (int64_t sl = s_lo + tid0; sl < s_hi; sl += kThreads) {
+  for (int64_t sl = s_lo + tid0 * step; sl < s_hi; sl += kThreads * step) {
     if (degree(sl) == 0) {
       const int64_t i = p.order[sl];
       for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
@@ -683,7 +665,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     }
   }
   auto next_nz = [&](int64_t sl) {
-    while (sl < s_hi && degree(sl) == 0) ++sl;
+    while (sl < s_hi && degree(sl) == 0) sl += step;
     return sl;
   };
   int64_t sa = next_nz(s_lo), a0 = 0;
@@ -701,7 +683,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     int nB = 0;
     bool b_done = false;
     if (a_done && nA < kET) {
-      sb = next_nz(sa + 1);
+      sb = next_nz(sa + step);
       if (sb < s_hi) {
         ib = p.order[sb];
         const int64_t deg_b = p.row_ptr[ib + 1] - p.row_ptr[ib];
@@ -838,14 +820,14 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       if (has_b) {
         if (b_done) {
           finish_a<L>(p, s, ns, ib, tid, wave);
-          sa = next_nz(sb + 1);
+          sa = next_nz(sb + step);
           a0 = 0;
         } else {
           sa = sb;
           a0 = nB;
         }
       } else {
-        sa = next_nz(sa + 1);
+        sa = next_nz(sa + step);
         a0 = 0;
       }
     } else {
@@ -900,11 +882,7 @@ __global__ void k_pack_rad(const uint16_t* __restrict__ w, f16x8* __restrict__ o
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
 constexpr int kOrderBins = 1 << (3 * kOrderBits);
 
-// Bounding box of the positions; also clears the per-XCD work counters of the
-// layer kernel that follows.
-__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out,
-                           int32_t* __restrict__ queue) {
-  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
+__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
   __shared__ float smin[3][256], smax[3][256];
   float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
@@ -960,7 +938,7 @@ __global__ void k_ord_scatter(int64_t n, const int32_t* __restrict__ key, const 
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, bins, cursor, bsum, bbox, queue, total;
+  size_t w, rad, order, key, bins, cursor, bsum, bbox, total;
 };
 
 template <int L>
@@ -977,7 +955,6 @@ MfmaWs mfma_ws_layout(int64_t n) {
   m.cursor = take(sizeof(int32_t) * kOrderBins);
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kOrderBins));
   m.bbox = take(8 * sizeof(float));
-  m.queue = take(8 * sizeof(int32_t));
   m.total = off;
   return m;
 }
@@ -997,13 +974,12 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   int32_t* cursor = reinterpret_cast<int32_t*>(wb + W.cursor);
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
-  int32_t* queue = reinterpret_cast<int32_t*>(wb + W.queue);
   const int64_t n = a->n_atoms;
   {
     // spatial order of the destination atoms: Morton code of a 64^3 grid over
     // the bounding box, counting-sorted (order only affects locality)
     const int64_t nb = (n + 255) / 256;
-    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox, queue);
+    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox);
     E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
     E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * kOrderBins, st));
     k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, bins);
@@ -1039,10 +1015,9 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   E2A_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
   const int64_t per_xcd_atoms = (n + 7) / 8;
   int64_t wpx = (2 * (int64_t)n_cu + 7) / 8;
-  const int64_t by_size = (per_xcd_atoms + kMinStretch - 1) / kMinStretch;
+  const int64_t by_size = (per_xcd_atoms + kMinPerWg - 1) / kMinPerWg;
   if (wpx > by_size) wpx = by_size;
   if (wpx < 1) wpx = 1;
-  p.queue = queue;
   p.wg_per_xcd = static_cast<int>(wpx);
   p.out = a->out;
   p.out_lse = a->out_lse;
