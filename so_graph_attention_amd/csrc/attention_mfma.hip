@@ -880,7 +880,9 @@ __global__ void k_pack_rad(const uint16_t* __restrict__ w, f16x8* __restrict__ o
 }
 
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
-constexpr int kOrderBins = 1 << (3 * kOrderBits);
+constexpr int kRadixBits = 9;                        // two radix passes over 18-bit keys
+constexpr int kRadix = 1 << kRadixBits;
+constexpr int kSortBlock = 1024;                     // elements per sort block (4 rounds of 256)
 
 __global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
   __shared__ float smin[3][256], smax[3][256];
@@ -913,7 +915,7 @@ __device__ __forceinline__ uint32_t spread3(uint32_t v) {
 }
 
 __global__ void k_ord_keys(const float* __restrict__ pos, int64_t n, const float* __restrict__ bbox,
-                           int32_t* __restrict__ key, int32_t* __restrict__ bins) {
+                           int32_t* __restrict__ key, int32_t* __restrict__ val) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
   uint32_t c[3];
@@ -924,22 +926,76 @@ __global__ void k_ord_keys(const float* __restrict__ pos, int64_t n, const float
     f = fminf(fmaxf(f, 0.0f), float((1 << kOrderBits) - 1));
     c[d] = static_cast<uint32_t>(f);
   }
-  const int32_t k = static_cast<int32_t>(spread3(c[0]) | (spread3(c[1]) << 1) | (spread3(c[2]) << 2));
-  key[i] = k;
-  atomicAdd(&bins[k], 1);
+  key[i] = static_cast<int32_t>(spread3(c[0]) | (spread3(c[1]) << 1) | (spread3(c[2]) << 2));
+  val[i] = static_cast<int32_t>(i);
 }
 
-__global__ void k_ord_scatter(int64_t n, const int32_t* __restrict__ key, const int32_t* __restrict__ start,
-                              int32_t* __restrict__ cursor, int32_t* __restrict__ order) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int k = key[i];
-  order[start[k] + atomicAdd(&cursor[k], 1)] = static_cast<int32_t>(i);
+// LSD radix sort of (Morton key, atom index) pairs, one kRadixBits digit per
+// pass.  The sort is stable, so the order (and with it the way atoms share
+// edge chunks in the layer kernel) is the same on every launch.
+//
+// Per-block digit counts, digit-major: hist[d * nblk + b].
+__global__ void k_radix_hist(const int32_t* __restrict__ key, int64_t n, int shift, int32_t* __restrict__ hist,
+                             int64_t nblk) {
+  __shared__ int32_t h[kRadix];
+  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) h[d] = 0;
+  __syncthreads();
+  const int64_t base = blockIdx.x * (int64_t)kSortBlock;
+  for (int t = threadIdx.x; t < kSortBlock; t += blockDim.x) {
+    const int64_t i = base + t;
+    if (i < n) atomicAdd(&h[(key[i] >> shift) & (kRadix - 1)], 1);
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
+}
+
+// Stable scatter: element i of block b (digit d) goes to off[d * nblk + b]
+// plus the number of earlier elements of the block with digit d.  The block's
+// 1024 elements go in 4 rounds of 256 in index order; within a round the waves
+// take turns, and inside a wave the lanes holding the same digit are found with
+// one ballot per digit bit.
+__global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict__ key_in,
+                                                       const int32_t* __restrict__ val_in, int64_t n, int shift,
+                                                       const int32_t* __restrict__ off, int64_t nblk,
+                                                       int32_t* __restrict__ key_out, int32_t* __restrict__ val_out) {
+  __shared__ int32_t next[kRadix];
+  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) next[d] = off[(int64_t)d * nblk + blockIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int64_t base = blockIdx.x * (int64_t)kSortBlock;
+  for (int round = 0; round < kSortBlock / 256; ++round) {
+    const int64_t i = base + round * 256 + threadIdx.x;
+    const bool valid = i < n;
+    const int32_t k = valid ? key_in[i] : 0;
+    const int32_t v = valid ? val_in[i] : 0;
+    const int d = (k >> shift) & (kRadix - 1);
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < kRadixBits; ++bit) {
+      const uint64_t b = __ballot((d >> bit) & 1);
+      same &= ((d >> bit) & 1) ? b : ~b;
+    }
+    const int rank = __popcll(same & below);
+    const int count = __popcll(same);
+    for (int w = 0; w < 4; ++w) {
+      if (wave == w && valid) {
+        const int32_t at = next[d] + rank;
+        key_out[at] = k;
+        val_out[at] = v;
+      }
+      __syncthreads();
+      if (wave == w && valid && rank == 0) next[d] += count;
+      __syncthreads();
+    }
+  }
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, bins, cursor, bsum, bbox, total;
+  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, total;
 };
+
+inline int64_t sort_blocks(int64_t n) { return (n + kSortBlock - 1) / kSortBlock; }
 
 template <int L>
 MfmaWs mfma_ws_layout(int64_t n) {
@@ -951,9 +1007,11 @@ MfmaWs mfma_ws_layout(int64_t n) {
   m.rad = take((L + 1) * kC * 16);
   m.order = take(sizeof(int32_t) * n);
   m.key = take(sizeof(int32_t) * n);
-  m.bins = take(sizeof(int32_t) * (kOrderBins + 1));
-  m.cursor = take(sizeof(int32_t) * kOrderBins);
-  m.bsum = take(sizeof(int64_t) * scan_bsum_count(kOrderBins));
+  m.key2 = take(sizeof(int32_t) * n);
+  m.val2 = take(sizeof(int32_t) * n);
+  m.hist = take(sizeof(int32_t) * kRadix * sort_blocks(n));
+  m.off = take(sizeof(int32_t) * (kRadix * sort_blocks(n) + 1));   // the scan also writes the total
+  m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
   m.bbox = take(8 * sizeof(float));
   m.total = off;
   return m;
@@ -970,26 +1028,34 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   f16x8* radpk = reinterpret_cast<f16x8*>(wb + W.rad);
   int32_t* order = reinterpret_cast<int32_t*>(wb + W.order);
   int32_t* key = reinterpret_cast<int32_t*>(wb + W.key);
-  int32_t* bins = reinterpret_cast<int32_t*>(wb + W.bins);
-  int32_t* cursor = reinterpret_cast<int32_t*>(wb + W.cursor);
+  int32_t* key2 = reinterpret_cast<int32_t*>(wb + W.key2);
+  int32_t* val2 = reinterpret_cast<int32_t*>(wb + W.val2);
+  int32_t* hist = reinterpret_cast<int32_t*>(wb + W.hist);
+  int32_t* off = reinterpret_cast<int32_t*>(wb + W.off);
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
   const int64_t n = a->n_atoms;
   {
     // spatial order of the destination atoms: Morton code of a 64^3 grid over
-    // the bounding box, counting-sorted (order only affects locality)
+    // the bounding box, stably sorted with the atom index as the tie-break
     const int64_t nb = (n + 255) / 256;
+    const int64_t nblk = sort_blocks(n);
     k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox);
-    E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
-    E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * kOrderBins, st));
-    k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, bins);
+    k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, order);
     E2A_LAUNCH_CHECK();
-    e2a_status ss = exclusive_scan_i32(bins, kOrderBins, cursor, bsum, st);
-    if (ss != E2A_OK) return ss;
-    // cursor now holds the bin starts; reuse bins as the running cursor
-    E2A_HIP_CHECK(hipMemsetAsync(bins, 0, sizeof(int32_t) * (kOrderBins + 1), st));
-    k_ord_scatter<<<nb, 256, 0, st>>>(n, key, cursor, bins, order);
-    E2A_LAUNCH_CHECK();
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass * kRadixBits;
+      const int32_t* kin = pass == 0 ? key : key2;
+      const int32_t* vin = pass == 0 ? order : val2;
+      int32_t* kout = pass == 0 ? key2 : key;
+      int32_t* vout = pass == 0 ? val2 : order;
+      k_radix_hist<<<nblk, 256, 0, st>>>(kin, n, shift, hist, nblk);
+      E2A_LAUNCH_CHECK();
+      e2a_status ss = exclusive_scan_i32(hist, kRadix * nblk, off, bsum, st);
+      if (ss != E2A_OK) return ss;
+      k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout);
+      E2A_LAUNCH_CHECK();
+    }
   }
   {
     const int64_t nv = S::wtotal();

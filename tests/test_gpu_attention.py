@@ -172,3 +172,16 @@ def test_mfma_kernel_chunk_packing_degrees(B, L):
     log(f"[attn] mfma chunk packing L={L} rel-L2 {err:.3e}")
     assert err <= TOL_BF16
     assert np.max(np.abs(lse[~iso] - want_lse[~iso])) <= 1e-4
+
+
+@pytest.mark.parametrize("name", ["drug", "protein"])
+def test_mfma_kernel_is_deterministic(B, name):
+    """Two launches on the same inputs give bit-identical outputs: the spatial
+    order of destinations (which decides how atoms share edge chunks, and so
+    the fp32 summation order) must not depend on timing."""
+    log(f"[attn] mfma determinism {name}")
+    w, rp, col, d = setup(B, name)
+    out0, lse0 = run_gpu(B, w, d, "auto")
+    out1, lse1 = run_gpu(B, w, d, "auto")
+    assert np.array_equal(out0, out1)
+    assert np.array_equal(lse0, lse1)
