@@ -449,7 +449,14 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
       const bf16x8 a0n = *reinterpret_cast<const bf16x8*>(ap0 + sn * 16);
       bf16x8 a1n = {};
       if constexpr (M > 0) a1n = *reinterpret_cast<const bf16x8*>(ap1 + sn * 16);
-      c00 = mfma_bf16(a0, b0, c00);
+      if constexpr (M == 0 && !S::has1(M, b)) {
+        // a single output degree: alternate two accumulators so that
+        // consecutive MFMAs do not wait on each other's result
+        if constexpr (st % 2 == 0) c00 = mfma_bf16(a0, b0, c00);
+        else c01 = mfma_bf16(a0, b0, c01);
+      } else {
+        c00 = mfma_bf16(a0, b0, c00);
+      }
       if constexpr (M == 0) {
         if constexpr (S::has1(M, b)) c01 = mfma_bf16(a0, b1, c01);
       } else {
@@ -466,7 +473,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
         constexpr int f = decltype(fc)::value;
         if constexpr (f == 0 || S::has1(M, b)) {
           constexpr int lo = S::blk_lo(M, b, f);
-          const f32x16& c0 = f == 0 ? c00 : c01;
+          const f32x16 c0 = f == 0 ? (S::has1(M, b) ? c00 : c00 + c01) : c01;
           const f16x8 brad = f == 0 ? brad0 : brad1;
           const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
           float u[16];
@@ -593,6 +600,17 @@ __device__ __forceinline__ void finish_a(const MfmaParams& p, const Smem& s, Nod
   });
 }
 
+// Uniform description of one chunk: nA edge slots of destination A (its
+// edges a0 .. a0 + nA - 1), then nB slots of destination B (its first nB).
+struct ChunkPlan {
+  int64_t sa, a0;     // A's slot in the spatial order, and its first edge in the chunk
+  int64_t ia, ib;     // atom ids of A and B (ib = ia without B)
+  int64_t ea, eb;     // first neighbour-list entry of A's and B's part
+  int64_t sb;         // B's slot
+  int nA, nB;
+  bool a_done, b_done;
+};
+
 // The destinations s_lo, s_lo + step, ... (< s_hi) of the spatial order:
 // their concatenated neighbour lists in chunks of 32 edge slots; a chunk
 // holds the rest of the current atom A and, when A ends inside it, the start
@@ -668,33 +686,60 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     while (sl < s_hi && degree(sl) == 0) sl += step;
     return sl;
   };
-  int64_t sa = next_nz(s_lo), a0 = 0;
-  while (sa < s_hi) {
+  auto make_plan = [&](int64_t sa, int64_t a0) {
+    ChunkPlan c{};
+    c.sa = sa;
+    c.a0 = a0;
+    c.sb = s_hi;
+    if (sa >= s_hi) return c;
+    c.ia = p.order[sa];
+    const int64_t deg_a = p.row_ptr[c.ia + 1] - p.row_ptr[c.ia];
+    c.nA = static_cast<int>(deg_a - a0 < kET ? deg_a - a0 : kET);
+    c.a_done = a0 + c.nA == deg_a;
+    c.ib = c.ia;
+    if (c.a_done && c.nA < kET) {
+      c.sb = next_nz(sa + step);
+      if (c.sb < s_hi) {
+        c.ib = p.order[c.sb];
+        const int64_t deg_b = p.row_ptr[c.ib + 1] - p.row_ptr[c.ib];
+        c.nB = static_cast<int>(deg_b < kET - c.nA ? deg_b : kET - c.nA);
+        c.b_done = c.nB == deg_b;
+      }
+    }
+    c.ea = p.row_ptr[c.ia] + a0;
+    c.eb = p.row_ptr[c.ib];
+    return c;
+  };
+  // the chunk after c: finish A (and B if it also ended), B becomes A
+  auto next_plan = [&](const ChunkPlan& c) {
+    if (!c.a_done) return make_plan(c.sa, c.a0 + c.nA);
+    if (c.nB == 0) return make_plan(next_nz(c.sa + step), 0);
+    if (c.b_done) return make_plan(next_nz(c.sb + step), 0);
+    return make_plan(c.sb, c.nB);
+  };
+  // neighbour index of edge slot t of chunk c (the atom itself for padding)
+  auto slot_col = [&](const ChunkPlan& c, int t) {
+    if (c.sa >= s_hi || t >= c.nA + c.nB) return static_cast<int>(t >= c.nA ? c.ib : c.ia);
+    return p.col[t < c.nA ? c.ea + t : c.eb + (t - c.nA)];
+  };
+  ChunkPlan cur = make_plan(next_nz(s_lo), 0);
+  int jcur = slot_col(cur, static_cast<int>(tid0 & (kET - 1)));
+  while (cur.sa < s_hi) {
     // lane-dependent values are derived afresh in every chunk rather than
     // hoisted out of the loop and kept live (or spilled) across it
     const int tid = opaque(tid0);
     const int lane = tid & 63;
-    // chunk plan (uniform): nA edges of A from offset a0, then nB of B
-    const int64_t ia = p.order[sa];
-    const int64_t deg_a = p.row_ptr[ia + 1] - p.row_ptr[ia];
-    const int nA = static_cast<int>(deg_a - a0 < kET ? deg_a - a0 : kET);
-    const bool a_done = a0 + nA == deg_a;
-    int64_t sb = s_hi, ib = ia;
-    int nB = 0;
-    bool b_done = false;
-    if (a_done && nA < kET) {
-      sb = next_nz(sa + step);
-      if (sb < s_hi) {
-        ib = p.order[sb];
-        const int64_t deg_b = p.row_ptr[ib + 1] - p.row_ptr[ib];
-        nB = static_cast<int>(deg_b < kET - nA ? deg_b : kET - nA);
-        b_done = nB == deg_b;
-      }
-    }
+    const int64_t ia = cur.ia, ib = cur.ib, ea = cur.ea, eb = cur.eb;
+    const int nA = cur.nA, nB = cur.nB;
+    const bool a_done = cur.a_done, b_done = cur.b_done;
     const int ne = nA + nB;
     const bool has_b = nB > 0;
-    const int64_t ea = p.row_ptr[ia] + a0, eb = p.row_ptr[ib];
+    // the next chunk's plan and neighbour indices are fetched now, so that
+    // their load latency overlaps this chunk's work
+    const ChunkPlan nxt = next_plan(cur);
+    const int jnext = slot_col(nxt, tid & (kET - 1));
 
+    if (tid < kET) s.j[tid] = jcur;
     if (tid < kC) s.q[tid] = p.q[ia * kC + tid];
     else if (has_b) s.q[tid] = p.q[ib * kC + (tid - kC)];
     __syncthreads();
@@ -706,9 +751,8 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       float R[3][3] = {{0, 0, 0}, {0, 0, 0}, {0, 0, 0}};
       float d0 = 0.0f;
       float e8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      int j = static_cast<int>(id);
+      const int j = jcur;
       if (tid < ne) {
-        j = p.col[in_b ? eb + (tid - nA) : ea + tid];
         float r3[3];
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
@@ -725,7 +769,6 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
         d0 = 1.0f;
         radial_basis8(rr, p.cutoff, e8);
       }
-      s.j[tid] = j;
       De[0] = d0;
       s.DT[tid] = static_cast<_Float16>(d0);
       float D1[9];
@@ -745,7 +788,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       const int e = tid >> 3, h = tid & 7;
       float sv = -INFINITY;
       if (e < ne) {
-        const int j = p.col[e >= nA ? eb + (e - nA) : ea + e];
+        const int j = s.j[e];
         const float4* kp = reinterpret_cast<const float4*>(p.k + (int64_t)j * kC + h * kDH);
         const float* qv = s.q + (e >= nA ? kC : 0) + h * kDH;
         float d = 0.0f;
@@ -814,25 +857,13 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       ln.flip = (lnr & 8) ? ~0u : 0u;
     }
     do_block<L, 0>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
-    // advance: finish A (and B if it also ended), B becomes A
+    // finish A (and B if it also ended); B's partial state becomes A's
     if (a_done) {
       finish_a<L>(p, s, ns, ia, tid, wave);
-      if (has_b) {
-        if (b_done) {
-          finish_a<L>(p, s, ns, ib, tid, wave);
-          sa = next_nz(sb + step);
-          a0 = 0;
-        } else {
-          sa = sb;
-          a0 = nB;
-        }
-      } else {
-        sa = next_nz(sa + step);
-        a0 = 0;
-      }
-    } else {
-      a0 += nA;
+      if (b_done) finish_a<L>(p, s, ns, ib, tid, wave);
     }
+    cur = nxt;
+    jcur = jnext;
   }
 }
 
