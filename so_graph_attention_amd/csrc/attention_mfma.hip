@@ -381,7 +381,7 @@ __device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-constexpr int kRing = 4;   // weight k-steps in flight per wave
+constexpr int kRing = 2;   // weight k-steps in flight per wave
 struct WRing {
   bf16x8 r[kRing][2];
 };
@@ -390,6 +390,9 @@ struct WRing {
 template <int L, int G>
 __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t wrsrc, int voff, int wave) {
   using S = Shape<L>;
+  // the ring runs on from one chunk into the next, so the step after the
+  // last of a chunk (step 0 again) must land in the slot that step frees
+  static_assert(S::stot() % kRing == 0, "chunk step count must be a multiple of the ring depth");
   constexpr int m = S::stream_m(G);
   constexpr int off0 = S::stream_off(G, 0);
   constexpr int off1 = S::stream_off(G, 1);
