@@ -918,29 +918,6 @@ constexpr int kRadixBits = 9;                        // two radix passes over 18
 constexpr int kRadix = 1 << kRadixBits;
 constexpr int kSortBlock = 1024;                     // elements per sort block (4 rounds of 256)
 
-__global__ void k_ord_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
-  __shared__ float smin[3][256], smax[3][256];
-  float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x)
-#pragma unroll
-    for (int d = 0; d < 3; ++d) {
-      mn[d] = fminf(mn[d], pos[3 * i + d]);
-      mx[d] = fmaxf(mx[d], pos[3 * i + d]);
-    }
-  for (int d = 0; d < 3; ++d) { smin[d][threadIdx.x] = mn[d]; smax[d][threadIdx.x] = mx[d]; }
-  __syncthreads();
-  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
-    if (threadIdx.x < st)
-      for (int d = 0; d < 3; ++d) {
-        smin[d][threadIdx.x] = fminf(smin[d][threadIdx.x], smin[d][threadIdx.x + st]);
-        smax[d][threadIdx.x] = fmaxf(smax[d][threadIdx.x], smax[d][threadIdx.x + st]);
-      }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0)
-    for (int d = 0; d < 3; ++d) { out[d] = smin[d][0]; out[3 + d] = smax[d][0]; }
-}
-
 __device__ __forceinline__ uint32_t spread3(uint32_t v) {
   uint32_t r = 0;
 #pragma unroll
@@ -1026,7 +1003,7 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, total;
+  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part, total;
 };
 
 inline int64_t sort_blocks(int64_t n) { return (n + kSortBlock - 1) / kSortBlock; }
@@ -1047,6 +1024,7 @@ MfmaWs mfma_ws_layout(int64_t n) {
   m.off = take(sizeof(int32_t) * (kRadix * sort_blocks(n) + 1));   // the scan also writes the total
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
   m.bbox = take(8 * sizeof(float));
+  m.bbox_part = take(sizeof(float) * kBboxPartialFloats);
   m.total = off;
   return m;
 }
@@ -1068,13 +1046,17 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   int32_t* off = reinterpret_cast<int32_t*>(wb + W.off);
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
+  float* bbox_part = reinterpret_cast<float*>(wb + W.bbox_part);
   const int64_t n = a->n_atoms;
   {
     // spatial order of the destination atoms: Morton code of a 64^3 grid over
     // the bounding box, stably sorted with the atom index as the tie-break
     const int64_t nb = (n + 255) / 256;
     const int64_t nblk = sort_blocks(n);
-    k_ord_bbox<<<1, 256, 0, st>>>(a->pos, n, bbox);
+    {
+      const e2a_status sb = launch_bbox(a->pos, n, bbox_part, bbox, st);
+      if (sb != E2A_OK) return sb;
+    }
     k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, order);
     E2A_LAUNCH_CHECK();
     for (int pass = 0; pass < 2; ++pass) {

@@ -63,6 +63,10 @@ size_t neighbors_workspace_bytes(int64_t n);
 // scan_bsum_count(n) int64 entries of scratch.
 e2a_status exclusive_scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, hipStream_t s);
 int64_t scan_bsum_count(int64_t n);
+// Bounding box of n positions into out[0..6] (min xyz, max xyz, 1 if any
+// coordinate is not finite); partial needs kBboxPartialFloats floats.
+constexpr int kBboxPartialFloats = 8 * 256;
+e2a_status launch_bbox(const float* pos, int64_t n, float* partial, float* out, hipStream_t s);
 
 // Attention (attention_*.hip).
 struct AttnPlan {

@@ -6,10 +6,12 @@
 // deterministic counting-sort cell list:
 //   1. bounding box (and coordinate check), read back once;
 //   2. bin atoms into cells of side >= 1.001 * cutoff (counting sort);
-//   3. count the neighbours of each atom over its <= 27 stencil cells;
-//   4. exclusive scan -> row_ptr; read the edge count back;
+//   3. count the neighbours of each atom over its <= 27 stencil cells (one
+//      wavefront per atom, the cells' candidates flattened across lanes);
+//   4. exclusive scan -> row_ptr; read the edge count and longest row back;
 //   5. one wavefront per atom gathers its neighbours with ballot compaction
-//      into LDS, bitonic-sorts them and writes the row.
+//      into LDS and writes the row sorted (rank of each entry for rows of up
+//      to 256, an LDS bitonic sort for longer ones).
 // The pair predicate is the fp32 rule documented in e2a.h, written with
 // explicitly rounded intrinsics so that no multiply-add is ever fused.
 #include <climits>
@@ -21,6 +23,8 @@ namespace {
 
 constexpr int kScanBlock = 1024;   // elements per scan block (256 threads x 4)
 constexpr int kMaxRow = 4096;      // longest row the LDS sort handles
+constexpr int kRowFast = 256;      // rows up to this length take the wave-per-atom fill
+constexpr int kBboxBlocks = kBboxPartialFloats / 8;   // first-stage blocks of the bounding box
 
 struct Grid {
   int n[3];
@@ -73,12 +77,32 @@ __device__ __forceinline__ bool pair_ok(const float* pi, const float* pj, const 
 
 // ---- bounding box ---------------------------------------------------------
 // out[0..2] = min, out[3..5] = max, out[6] = 1 if any coordinate is not finite.
-__global__ void k_bbox(const float* __restrict__ pos, int64_t n, float* __restrict__ out) {
+__device__ __forceinline__ void bbox_reduce(float (&mn)[3], float (&mx)[3], int& bad, float (*smin)[256],
+                                            float (*smax)[256], int* sbad) {
+  for (int d = 0; d < 3; ++d) { smin[d][threadIdx.x] = mn[d]; smax[d][threadIdx.x] = mx[d]; }
+  sbad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) {
+      for (int d = 0; d < 3; ++d) {
+        smin[d][threadIdx.x] = fminf(smin[d][threadIdx.x], smin[d][threadIdx.x + st]);
+        smax[d][threadIdx.x] = fmaxf(smax[d][threadIdx.x], smax[d][threadIdx.x + st]);
+      }
+      sbad[threadIdx.x] |= sbad[threadIdx.x + st];
+    }
+    __syncthreads();
+  }
+}
+
+// Stage 1: block b reduces atoms b, b + gridDim.x, ... (grid-stride by block
+// and thread) into partial[b][0..6].
+__global__ void __launch_bounds__(256) k_bbox_partial(const float* __restrict__ pos, int64_t n,
+                                                      float* __restrict__ partial) {
   __shared__ float smin[3][256], smax[3][256];
   __shared__ int sbad[256];
   float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
   int bad = 0;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
 #pragma unroll
     for (int d = 0; d < 3; ++d) {
       const float x = pos[3 * i + d];
@@ -87,26 +111,34 @@ __global__ void k_bbox(const float* __restrict__ pos, int64_t n, float* __restri
       mx[d] = fmaxf(mx[d], x);
     }
   }
-  for (int d = 0; d < 3; ++d) { smin[d][threadIdx.x] = mn[d]; smax[d][threadIdx.x] = mx[d]; }
-  sbad[threadIdx.x] = bad;
-  __syncthreads();
-  for (int s = blockDim.x / 2; s > 0; s >>= 1) {
-    if (threadIdx.x < s) {
-      for (int d = 0; d < 3; ++d) {
-        smin[d][threadIdx.x] = fminf(smin[d][threadIdx.x], smin[d][threadIdx.x + s]);
-        smax[d][threadIdx.x] = fmaxf(smax[d][threadIdx.x], smax[d][threadIdx.x + s]);
-      }
-      sbad[threadIdx.x] |= sbad[threadIdx.x + s];
-    }
-    __syncthreads();
+  bbox_reduce(mn, mx, bad, smin, smax, sbad);
+  if (threadIdx.x == 0) {
+    float* o = partial + 8 * blockIdx.x;
+    for (int d = 0; d < 3; ++d) { o[d] = smin[d][0]; o[3 + d] = smax[d][0]; }
+    o[6] = sbad[0] ? 1.0f : 0.0f;
   }
+}
+
+// Stage 2: out[0..2] = min, out[3..5] = max, out[6] = 1 if any coordinate is
+// not finite.
+__global__ void __launch_bounds__(256) k_bbox_final(const float* __restrict__ partial, int nparts,
+                                                    float* __restrict__ out) {
+  __shared__ float smin[3][256], smax[3][256];
+  __shared__ int sbad[256];
+  float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+  int bad = 0;
+  for (int b = threadIdx.x; b < nparts; b += blockDim.x) {
+    const float* o = partial + 8 * b;
+    for (int d = 0; d < 3; ++d) { mn[d] = fminf(mn[d], o[d]); mx[d] = fmaxf(mx[d], o[3 + d]); }
+    bad |= o[6] != 0.0f;
+  }
+  bbox_reduce(mn, mx, bad, smin, smax, sbad);
   if (threadIdx.x == 0) {
     for (int d = 0; d < 3; ++d) { out[d] = smin[d][0]; out[3 + d] = smax[d][0]; }
     out[6] = sbad[0] ? 1.0f : 0.0f;
   }
 }
 
-// ---- counting sort into cells ----------------------------------------------
 __global__ void k_bin(const float* __restrict__ pos, int64_t n, Grid g, int32_t* __restrict__ cell_of,
                       int32_t* __restrict__ cell_cnt) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -216,42 +248,159 @@ e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, h
   return E2A_OK;
 }
 
-// ---- neighbour count: one thread per destination atom ----------------------
-__global__ void k_count(const float* __restrict__ pos, int64_t n, const int32_t* __restrict__ batch, Grid g,
-                        const int32_t* __restrict__ cell_start, const int32_t* __restrict__ cell_atoms,
-                        int32_t* __restrict__ row_cnt, int32_t* __restrict__ max_row) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
-  const int bi = batch ? batch[i] : 0;
+// ---- candidates of one destination atom, one wavefront ---------------------
+// The <= 27 stencil cells' atom ranges are flattened: lane l handles
+// candidates l, l + 64, ... of the concatenation (cells in stencil order,
+// atoms in cell order), so that every pass keeps all 64 lanes busy.
+// sh: 64 ints of LDS for this wavefront.  f(valid, j) is called once per
+// pass by every lane.
+template <typename F>
+__device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid& g,
+                                               const int32_t* __restrict__ cell_start,
+                                               const int32_t* __restrict__ cell_atoms, int lane, int* sh, F&& f) {
   int sx[3], sy[3], sz[3];
   const int nx = stencil(cell_coord(pi[0], 0, g), 0, g, sx);
   const int ny = stencil(cell_coord(pi[1], 1, g), 1, g, sy);
   const int nz = stencil(cell_coord(pi[2], 2, g), 2, g, sz);
-  int cnt = 0;
-  for (int a = 0; a < nz; ++a)
-    for (int b = 0; b < ny; ++b)
-      for (int c = 0; c < nx; ++c) {
-        const int cell = (sz[a] * g.n[1] + sy[b]) * g.n[0] + sx[c];
-        for (int t = cell_start[cell]; t < cell_start[cell + 1]; ++t) {
-          const int j = cell_atoms[t];
-          if (j == i) continue;
-          if (batch && batch[j] != bi) continue;
-          const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
-          cnt += pair_ok(pi, pj, g) ? 1 : 0;
-        }
+  const int ncells = nx * ny * nz;
+  int cstart = 0, ccnt = 0;
+  if (lane < ncells) {
+    const int a = lane / (ny * nx), b = (lane / nx) % ny, c = lane % nx;
+    const int cell = (sz[a] * g.n[1] + sy[b]) * g.n[0] + sx[c];
+    cstart = cell_start[cell];
+    ccnt = cell_start[cell + 1] - cstart;
+  }
+  int incl = ccnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  const int total = __shfl(incl, 63);
+  if (lane < 32) {
+    sh[lane] = incl - ccnt;   // first flattened index of the lane's cell
+    sh[32 + lane] = cstart;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  for (int base = 0; base < total; base += 64) {
+    const int t = base + lane;
+    bool valid = t < total;
+    int j = 0;
+    if (valid) {
+      // last cell whose first index is <= t (empty cells never win: the next
+      // non-empty cell starts after t)
+      int lo = 0, hi = ncells;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (sh[mid] <= t) lo = mid;
+        else hi = mid;
       }
-  row_cnt[i] = cnt;
-  atomicMax(max_row, cnt);
+      j = cell_atoms[sh[32 + lo] + (t - sh[lo])];
+    }
+    f(valid, j);
+  }
 }
 
-__global__ void k_readback(const int64_t* __restrict__ row_ptr, int64_t n, const int32_t* __restrict__ max_row,
-                           int64_t* __restrict__ out) {
-  out[0] = row_ptr[n];
-  out[1] = *max_row;
+// ---- neighbour count: one wavefront per destination atom, 4 per block ------
+__global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, int64_t n,
+                                               const int32_t* __restrict__ batch, Grid g,
+                                               const int32_t* __restrict__ cell_start,
+                                               const int32_t* __restrict__ cell_atoms, int32_t* __restrict__ row_cnt) {
+  __shared__ int sh[4][64];
+  const int w = threadIdx.x >> 6;
+  const int64_t i = blockIdx.x * 4 + w;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+  const int bi = batch ? batch[i] : 0;
+  int cnt = 0;
+  for_candidates(pi, g, cell_start, cell_atoms, lane, sh[w], [&](bool valid, int j) {
+    bool ok = valid && (j != i) && (!batch || batch[j] == bi);
+    if (ok) {
+      const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+      ok = pair_ok(pi, pj, g);
+    }
+    cnt += __popcll(__ballot(ok));
+  });
+  if (lane == 0) row_cnt[i] = cnt;
 }
 
-// ---- fill + sort: one wavefront (= one block) per destination atom ---------
+// out[0] = number of edges, out[1] = longest row (one block of 1024 threads,
+// four independent loads in flight per thread).
+__global__ void __launch_bounds__(1024) k_readback(const int64_t* __restrict__ row_ptr, int64_t n,
+                                                   const int32_t* __restrict__ row_cnt, int64_t* __restrict__ out) {
+  __shared__ int32_t sm[1024];
+  int32_t m = 0;
+  for (int64_t i = threadIdx.x; i < n; i += 4 * (int64_t)blockDim.x) {
+    int32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t k = i + u * (int64_t)blockDim.x;
+      v[u] = k < n ? row_cnt[k] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = max(m, v[u]);
+  }
+  sm[threadIdx.x] = m;
+  __syncthreads();
+  for (int st = blockDim.x / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) sm[threadIdx.x] = max(sm[threadIdx.x], sm[threadIdx.x + st]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    out[0] = row_ptr[n];
+    out[1] = sm[0];
+  }
+}
+
+// ---- fill + sort, rows of at most kRowFast entries: one wavefront per atom,
+// 4 per block.  Candidates are compacted into the wave's LDS row with a
+// ballot; each entry's position in the sorted row is the number of smaller
+// entries (the atom ids of a row are distinct), so the row is written sorted
+// straight from registers.
+__global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos, int64_t n,
+                                                   const int32_t* __restrict__ batch, Grid g,
+                                                   const int32_t* __restrict__ cell_start,
+                                                   const int32_t* __restrict__ cell_atoms,
+                                                   const int64_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
+  __shared__ int32_t rows[4][kRowFast];
+  __shared__ int sh[4][64];
+  const int w = threadIdx.x >> 6;
+  const int64_t i = blockIdx.x * 4 + w;
+  const int lane = threadIdx.x & 63;
+  if (i >= n) return;
+  int32_t* buf = rows[w];
+  const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
+  const int bi = batch ? batch[i] : 0;
+  int cnt = 0;
+  for_candidates(pi, g, cell_start, cell_atoms, lane, sh[w], [&](bool valid, int j) {
+    bool ok = valid && (j != i) && (!batch || batch[j] == bi);
+    if (ok) {
+      const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+      ok = pair_ok(pi, pj, g);
+    }
+    const uint64_t mask = __ballot(ok);
+    if (ok) {
+      const int slot = cnt + __popcll(mask & ((1ull << lane) - 1ull));
+      if (slot < kRowFast) buf[slot] = j;
+    }
+    cnt += __popcll(mask);
+  });
+  // The host launches this kernel only when every row fits (count pass).
+  // the row was written by other lanes of this wavefront
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int64_t o = row_ptr[i];
+  for (int t = lane; t < cnt; t += 64) {
+    const int32_t v = buf[t];
+    int rank = 0;
+    for (int u = 0; u < cnt; ++u) rank += buf[u] < v ? 1 : 0;
+    col[o + rank] = v;
+  }
+}
+
+// ---- fill + sort, any row up to kMaxRow: one wavefront (= one block) per atom
 __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int64_t n,
                                              const int32_t* __restrict__ batch, Grid g,
                                              const int32_t* __restrict__ cell_start,
@@ -315,7 +464,7 @@ __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int6
 }
 
 struct WsLayout {
-  size_t cell_of, cell_cnt, cursor, cell_atoms, row_cnt, bsum, small, total;
+  size_t cell_of, cell_cnt, cursor, cell_atoms, row_cnt, bsum, small, bbox_part, total;
   int64_t cap_cells;
 };
 
@@ -332,6 +481,7 @@ WsLayout ws_layout(int64_t n) {
   w.row_cnt = take(sizeof(int32_t) * n);
   w.bsum = take(sizeof(int64_t) * nb);
   w.small = take(256);
+  w.bbox_part = take(sizeof(float) * kBboxPartialFloats);
   w.total = off;
   w.cap_cells = cap;
   return w;
@@ -340,6 +490,14 @@ WsLayout ws_layout(int64_t n) {
 }  // namespace
 
 size_t neighbors_workspace_bytes(int64_t n) { return ws_layout(n).total; }
+
+e2a_status launch_bbox(const float* pos, int64_t n, float* partial, float* out, hipStream_t s) {
+  const int nparts = static_cast<int>(std::min<int64_t>(kBboxBlocks, (n + 255) / 256));
+  k_bbox_partial<<<nparts, 256, 0, s>>>(pos, n, partial);
+  k_bbox_final<<<1, 256, 0, s>>>(partial, nparts, out);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
 
 e2a_status exclusive_scan_i32(const int32_t* in, int64_t n, int32_t* out, int64_t* bsum, hipStream_t s) {
   return exclusive_scan<int32_t>(in, n, out, bsum, s);
@@ -360,7 +518,7 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   int32_t* row_cnt = reinterpret_cast<int32_t*>(base + L.row_cnt);
   int64_t* bsum = reinterpret_cast<int64_t*>(base + L.bsum);
   float* bbox = reinterpret_cast<float*>(base + L.small);
-  int32_t* max_row = reinterpret_cast<int32_t*>(base + L.small + 64);
+  float* bbox_part = reinterpret_cast<float*>(base + L.bbox_part);
   int64_t* rb = reinterpret_cast<int64_t*>(base + L.small + 128);
 
   if (n == 0) {
@@ -370,8 +528,10 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   }
 
   // 1. bounding box and coordinate check
-  k_bbox<<<1, 256, 0, s>>>(pos, n, bbox);
-  E2A_LAUNCH_CHECK();
+  {
+    const e2a_status st = launch_bbox(pos, n, bbox_part, bbox, s);
+    if (st != E2A_OK) return st;
+  }
   float hb[8];
   E2A_HIP_CHECK(hipMemcpyAsync(hb, bbox, 7 * sizeof(float), hipMemcpyDeviceToHost, s));
   E2A_HIP_CHECK(hipStreamSynchronize(s));
@@ -417,7 +577,6 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   // 2. counting sort into cells
   E2A_HIP_CHECK(hipMemsetAsync(cell_cnt, 0, sizeof(int32_t) * (ncell + 1), s));
   E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
-  E2A_HIP_CHECK(hipMemsetAsync(max_row, 0, sizeof(int32_t), s));
   k_bin<<<nblk, tpb, 0, s>>>(pos, n, g, cell_of, cell_cnt);
   E2A_LAUNCH_CHECK();
   // cell_cnt -> exclusive starts in place is not allowed (in/out alias): use cursor area? no:
@@ -432,13 +591,14 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   E2A_LAUNCH_CHECK();
 
   // 3-4. count, scan, read back
-  k_count<<<nblk, tpb, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_cnt, max_row);
+  const int64_t nwblk = (n + 3) / 4;   // wave-per-atom kernels: 4 atoms per block
+  k_count<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_cnt);
   E2A_LAUNCH_CHECK();
   {
     e2a_status st = exclusive_scan<int64_t>(row_cnt, n, row_ptr, bsum, s);
     if (st != E2A_OK) return st;
   }
-  k_readback<<<1, 1, 0, s>>>(row_ptr, n, max_row, rb);
+  k_readback<<<1, 1024, 0, s>>>(row_ptr, n, row_cnt, rb);
   E2A_LAUNCH_CHECK();
   int64_t hr[2];
   E2A_HIP_CHECK(hipMemcpyAsync(hr, rb, sizeof(hr), hipMemcpyDeviceToHost, s));
@@ -451,7 +611,10 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
     return fail(E2A_ERR_CAPACITY, "need %lld edges, col_capacity is %lld", (long long)hr[0], (long long)cap_edges);
 
   // 5. fill and sort rows
-  k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
+  if (hr[1] <= kRowFast)
+    k_fill_fast<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
+  else
+    k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
