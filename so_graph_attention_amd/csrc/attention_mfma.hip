@@ -123,9 +123,20 @@ struct Shape {
     return has1(m, (G - sbase(m)) / ks(m));
   }
   static constexpr int64_t wave_bytes(int m) { return wblock(m) * 16; }
-  // LDS layout (bytes): one GEMM operand region, which also holds the fp32
+  // The last two blocks (m = L-1 and L) are rotated in by one pass over the
+  // degree-L feature rows; their operands sit side by side, block L's at
+  // a_off(L).
+  static constexpr int rup(int x) { return (x + 255) / 256 * 256; }
+  static constexpr int a_off(int m) { return m == L && L >= 1 ? rup(abytes(L - 1)) : 0; }
+  static constexpr int aregion() {
+    int b = amax();
+    if (a_off(L) + abytes(L) > b) b = a_off(L) + abytes(L);
+    if (kET * DSZ * 4 > b) b = kET * DSZ * 4;
+    return rup(b);
+  }
+  // LDS layout (bytes): the GEMM operand region, which also holds the fp32
   // D of the chunk while the recursion runs
-  static constexpr int off_DT = (amax() > kET * DSZ * 4 ? amax() : kET * DSZ * 4 + 255) / 256 * 256;
+  static constexpr int off_DT = aregion();
   static constexpr int off_rbf = off_DT + DT * 2;
   static constexpr int off_alpha = off_rbf + kET * 8 * 4;
   static constexpr int off_q = off_alpha + kET * kH * 4;
@@ -326,15 +337,20 @@ __device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid
 // task tau's arithmetic.
 template <int L, int MN>
 __device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, int tid) {
+  using S = Shape<L>;
   static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
   constexpr int NT = 2 * (L + 1 - MN);
+  // for MN = L-1 the last two tasks (degree L) also produce block L
+  constexpr bool pair = MN == L - 1;
   tid = opaque(tid);
   uint4 raw[2][2 * L + 1];
   task_load<L, MN, 0>(p, s, tid, raw[0]);
   static_for<NT>([&](auto tc) {
     constexpr int tau = decltype(tc)::value;
     if constexpr (tau + 1 < NT) task_load<L, MN, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
-    task_compute<L, MN, tau>(s, s.A, tid, raw[tau & 1]);
+    task_compute<L, MN, tau>(s, s.A + S::a_off(MN) / 2, tid, raw[tau & 1]);
+    if constexpr (pair && tau >= NT - 2)
+      task_compute<L, L, tau - (NT - 2)>(s, s.A + S::a_off(L) / 2, tid, raw[tau & 1]);
   });
 }
 
@@ -426,7 +442,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
   const int c_own = 32 * wave + (lane & 31);
   const int voff = lane * 16;
   const f16x8 zero8 = {};
-  const uint16_t* ap0 = s.A + (lane & 31) * stride + 8 * half;
+  const uint16_t* ap0 = s.A + S::a_off(M) / 2 + (lane & 31) * stride + 8 * half;
   const uint16_t* ap1 = ap0 + 32 * stride;   // second row tile (m > 0 only)
   bf16x8 a0 = *reinterpret_cast<const bf16x8*>(ap0);
   bf16x8 a1 = {};
@@ -537,15 +553,22 @@ __device__ __forceinline__ void wig_level(const Smem& s, int tid) {
 }
 
 // Blocks M = 0..L of one chunk: rotate-in of M into the operand region, a
-// barrier, the GEMM of M, and a barrier before the region is rewritten.
+// barrier, the GEMM of M, and a barrier before the region is rewritten;
+// blocks L-1 and L share one rotate-in pass and run their GEMMs back to back.
 template <int L, int M>
 __device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid,
                                          int wave, const Lane& ln, bool has_b, NodeState<L>& ns, WRing& ring) {
   rotate_in<L, M>(p, s, tid);
   __syncthreads();
   mma_block<L, M>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
-  __syncthreads();
-  if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+  if constexpr (M == L - 1) {
+    // block L was rotated in with block L-1 and has its own operand space
+    mma_block<L, L>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+    __syncthreads();
+  } else {
+    __syncthreads();
+    if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+  }
 }
 
 // Writes destination A's output (the normalised node accumulator, lanes of
