@@ -90,6 +90,31 @@ def cpu_baseline(w, rp, col, seconds):
                       f"{dt:.1f} s of fp64 NumPy on {threads} BLAS threads"}
 
 
+def cpu_single_thread(name, seconds):
+    """The oracle with one BLAS thread on a small workload (all of it, or a
+    seeded sample of destinations grown in batches of 32 until about
+    `seconds` have been spent)."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+    from workloads import make_config
+    w = make_config(name)
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    args = (rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"), w.as_f32("w_rad"), w.as_f32("w_so2"),
+            w.L, w.C, w.H, w.cutoff)
+    order = np.random.default_rng(2024).permutation(w.n_atoms)
+    done = edges = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while done < w.n_atoms and (done == 0 or time.perf_counter() - t0 < seconds):
+            dest = np.sort(order[done:done + 32])
+            O.attention(w.pos, *args, box=w.box, dest=dest)
+            edges += int((rp[dest + 1] - rp[dest]).sum())
+            done += dest.size
+        dt = time.perf_counter() - t0
+    return {"workload": name, "value": edges / dt, "unit": "edges/s", "cores": 1,
+            "sample": f"{done} of {w.n_atoms} destination atoms ({edges} edges), {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -197,6 +222,9 @@ def main():
         rp_h = rp.cpu().numpy()
         col_h = col.cpu().numpy()
         result["cpu_baseline"] = cpu_baseline(w, rp_h, col_h, args.cpu_seconds)
+        progress("oracle single-thread runs (tiny, drug)")
+        result["cpu_baseline"]["single_thread"] = [cpu_single_thread("tiny", 2.0),
+                                                   cpu_single_thread("drug", 5.0)]
     print(json.dumps(result), flush=True)
 
 

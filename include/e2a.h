@@ -169,7 +169,9 @@ size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int d
  * such matrix (W0) for m = 0, two (W1 then W2) for each m >= 1.
  *
  * An atom with no neighbours gets o_i = 0 and lse = -inf.  Asynchronous: no
- * host synchronisation.  Errors: E2A_ERR_INVALID_ARG (null pointer, C % H != 0,
+ * host synchronisation, no device-memory set or copy commands, only kernel
+ * launches on the stream (so a caller may record the call into a HIP graph).
+ * Deterministic: the same inputs give bit-identical outputs.  Errors: E2A_ERR_INVALID_ARG (null pointer, C % H != 0,
  * cutoff <= 0, n_rbf != 8, L outside 0..4, workspace too small),
  * E2A_ERR_UNSUPPORTED (variant not built for the shape or dtype).
  */

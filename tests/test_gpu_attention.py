@@ -185,3 +185,38 @@ def test_mfma_kernel_is_deterministic(B, name):
     out1, lse1 = run_gpu(B, w, d, "auto")
     assert np.array_equal(out0, out1)
     assert np.array_equal(lse0, lse1)
+
+
+def test_mfma_kernel_graph_capture_replays(B):
+    """The layer enqueues only kernels (no memset/copy nodes, no host sync),
+    so it can be recorded into a HIP graph.  Three replays, with eager work
+    and synchronisation between them, each match the eager result bitwise."""
+    log("[attn] mfma graph capture, drug")
+    w, rp, col, d = setup(B, "drug")
+    n, K = w.n_atoms, (w.L + 1) ** 2
+    args = (d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"], d["w_so2"])
+    kw = dict(L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=None if w.box is None else w.box.tolist())
+    eager, eager_lse = B.e2a_attention_fwd(*args, **kw, with_lse=True)
+    torch.cuda.synchronize()
+    eager, eager_lse = eager.cpu().numpy(), eager_lse.cpu().numpy()
+    out = torch.empty((n, K, w.C), dtype=torch.float32, device="cuda")
+    lse = torch.empty((n, w.H), dtype=torch.float32, device="cuda")
+    ws = torch.empty(B.e2a_attention_workspace_bytes(n, w.L, w.C, w.H, B.E2A_DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        B.e2a_attention_fwd(*args, **kw, out=out, out_lse=lse, workspace=ws, with_lse=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.e2a_attention_fwd(*args, **kw, out=out, out_lse=lse, workspace=ws, with_lse=True)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep}"
+        assert np.array_equal(lse.cpu().numpy(), eager_lse), f"replay {rep}"
