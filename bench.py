@@ -126,7 +126,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).",
+        print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).",
               file=sys.stderr)
         sys.exit(2)
 

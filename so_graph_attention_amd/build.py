@@ -1,6 +1,6 @@
 """Build libe2a.so (HIP, gfx950) and the host-only geometry check library in-tree.
 
-Usage:  python -m so_graph_attention_amd.build   (or __graft_entry__.build())
+Usage:  python -m so_graph_attention_amd.build
 """
 from __future__ import annotations
 
