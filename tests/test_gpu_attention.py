@@ -220,3 +220,27 @@ def test_mfma_kernel_graph_capture_replays(B):
         torch.cuda.synchronize()
         assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep}"
         assert np.array_equal(lse.cpu().numpy(), eager_lse), f"replay {rep}"
+
+
+def test_mfma_kernel_long_rows(B):
+    """Destinations with 300 neighbours (about ten 32-edge chunks each),
+    L = 1, sampled destinations against the oracle."""
+    from test_gpu_neighbors import dense_cluster
+    log("[attn] mfma long rows")
+    geom = (dense_cluster(300, seed=5), None, None, {"cluster": 300})
+    w = make_config("tiny", L=1, C=128, H=8, dtype="bf16", geometry=geom)
+    w.cutoff = float(np.float32(5.0))
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    out, lse = run_gpu(B, w, d, "mfma")
+    dest = np.array([0, 1, 77, 150, 299, 300, 301, 320, 340])
+    want, want_lse = oracle_out(w, rp, col, dest)
+    err = rel_l2(out[dest], want)
+    log(f"[attn] mfma long rows rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL_BF16
+    iso = np.diff(rp)[dest] == 0
+    assert np.all(np.isneginf(lse[dest][iso])) and np.all(np.isneginf(want_lse[iso]))
+    assert np.max(np.abs(lse[dest][~iso] - want_lse[~iso])) <= 1e-4

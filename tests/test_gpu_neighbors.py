@@ -89,3 +89,25 @@ def test_neighbors_small_periodic_boxes(B, side):
     rp_o, col_o = O.neighbor_list_bruteforce(pos, 5.0, box)
     rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0, box=box.tolist())
     assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
+
+
+def dense_cluster(deg, seed):
+    """deg + 1 atoms within a ball of radius 2.4 A (every pair closer than a
+    5 A cutoff: each has exactly deg neighbours) plus 40 atoms far away."""
+    rng = np.random.default_rng(seed)
+    v = rng.normal(size=(deg + 1, 3))
+    v *= 2.4 * rng.random((deg + 1, 1)) ** (1 / 3) / np.linalg.norm(v, axis=1, keepdims=True)
+    far = rng.uniform(0, 60, (40, 3)) + np.array([30.0, 0.0, 0.0])
+    return np.concatenate([v + 10.0, far]).astype(np.float32)
+
+
+@pytest.mark.parametrize("deg", [256, 300])
+def test_neighbors_long_rows(B, deg):
+    """Rows of exactly 256 fill the per-wave row buffer of the fast fill;
+    longer rows take the LDS bitonic path."""
+    log(f"[neighbors] long rows {deg}")
+    pos = dense_cluster(deg, seed=deg)
+    rp_o, col_o = O.neighbor_list(pos, 5.0)
+    assert np.diff(rp_o).max() == deg
+    rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0)
+    assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
