@@ -7,6 +7,7 @@ calls it, and it shares no code, table or constant with the HIP sources.
 from .e2a_oracle import (  # noqa: F401
     attention,
     attention_online,
+    convolution,
     edge_messages,
     edge_rotation,
     min_image,

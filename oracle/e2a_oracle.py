@@ -16,7 +16,8 @@ Parity status: every function here is pinned by the CPU test suite (Lemma 4.1
 sparsity, spherical-harmonic closed forms and SciPy, Wigner-D group laws, gauge
 invariance, rotation equivariance, permutation invariance, an L=1 closed form,
 softmax limits, online == two-pass, brute-force neighbours, and equality with a
-dense Clebsch-Gordan tensor product).  The conventions those invariants leave
+dense Clebsch-Gordan tensor product; the convolution against the attention
+layer with uniform weights).  The conventions those invariants leave
 free (edge direction, W2 sign, radial basis widths, 1/sqrt(d_h), head split, no
 self loop) are readings, not facts the pages fix.
 """
@@ -407,6 +408,45 @@ def attention(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, 
             lse[nz] = seg_lse
         t = u
     return out, lse
+
+
+def convolution(pos, row_ptr, col, feat, w_rad, w_so2, L, C, cutoff, box=None, dest=None, chunk_edges=4096):
+    """The EAAS convolution stage (technical summary section 2.1, "Equivariant
+    Axis-Aligned Sparsification", whose result is stated for the convolution
+    stage): the same per-edge messages v_ij as the attention layer (from
+    ``edge_messages``), summed over the neighbourhood with no attention
+    weights, o_i = sum_{j in N(i)} v_ij.  Readings: a plain sum (no division
+    by the degree), no residual or output projection; an empty N(i) gives
+    o_i = 0.  Returns out [len(dest),(L+1)^2,C] fp64."""
+    pos = np.asarray(pos, dtype=np.float64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    n = pos.shape[0]
+    dest = np.arange(n) if dest is None else np.asarray(dest, dtype=np.int64)
+    K = (L + 1) ** 2
+    blocks = so2_blocks(w_so2, L, C)
+    out = np.zeros((dest.size, K, C))
+    deg = row_ptr[dest + 1] - row_ptr[dest]
+    t = 0
+    while t < dest.size:
+        u = t
+        tot = 0
+        while u < dest.size and (u == t or tot + deg[u] <= chunk_edges):
+            tot += deg[u]
+            u += 1
+        sel = np.arange(t, u)
+        nz = sel[deg[sel] > 0]
+        if nz.size:
+            e_idx = np.concatenate([np.arange(row_ptr[dest[a]], row_ptr[dest[a] + 1]) for a in nz])
+            lens = deg[nz]
+            starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+            src = col[e_idx]
+            rvec = min_image(pos[src] - pos[dest[np.repeat(nz, lens)]], box)
+            v = edge_messages(rvec, np.asarray(feat[src], dtype=np.float64), w_rad, w_so2, L, C, cutoff,
+                              blocks=blocks)
+            out[nz] = np.add.reduceat(v, starts, axis=0)
+        t = u
+    return out
 
 
 def attention_online(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box=None,

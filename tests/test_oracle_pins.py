@@ -6,7 +6,8 @@ frame, closed forms and SciPy for the spherical harmonics, group laws of the
 Wigner-D blocks, gauge freedom about the edge axis, rotation/translation
 equivariance and permutation invariance of the layer, an L = 1 closed form in
 vector notation, softmax algebra, online == two-pass, brute-force neighbours,
-the empty-row case, and equality with a dense Clebsch-Gordan tensor product.
+the empty-row case, equality with a dense Clebsch-Gordan tensor product, and
+the convolution against uniform-weight attention.
 """
 import math
 
@@ -448,6 +449,48 @@ def test_p12_empty_row_is_zero():
     o, lse = run(w, rp, col)
     assert np.all(o[-1] == 0) and np.all(np.isneginf(lse[-1]))
     assert np.all(np.abs(o[:-1]).sum(axis=(1, 2)) > 0)
+
+
+# ---------------------------------------------------------------- P13 -------
+def conv(w, rp, col, pos=None, feat=None, **kw):
+    pos = w.pos if pos is None else pos
+    feat = w.as_f32("feat") if feat is None else feat
+    return O.convolution(pos, rp, col, feat, w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.cutoff,
+                         box=w.box, **kw)
+
+
+@pytest.mark.parametrize("name", ["tiny", "drug"])
+def test_p13_convolution_is_degree_times_uniform_attention(name):
+    """With W_q = 0 every logit is 0, so softmax gives each of the deg_i
+    neighbours weight exactly 1/deg_i and the attention output is the
+    neighbour mean of v_ij; the convolution (the plain sum) must be deg_i
+    times it.  Checks the convolution against the pinned attention oracle on
+    rows of every degree, including the empty ones."""
+    w = make_config(name) if name == "tiny" else make_config(name, C=8, H=2, L=2)
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    dest = np.arange(min(w.n_atoms, 400))
+    oc = conv(w, rp, col, dest=dest)
+    oa, _ = run(w, rp, col, dest=dest, w_q_zero=True)
+    deg = (rp[dest + 1] - rp[dest]).astype(np.float64)
+    assert rel(oc, deg[:, None, None] * oa) <= 1e-13
+    assert np.all(oc[deg == 0] == 0)
+
+
+def test_p13_convolution_equivariance_and_linearity(tiny):
+    """Positions R x + t and features D(R) h give D(R) o; and the sum of
+    messages is linear in the features (the logits, the only nonlinear part of
+    attention, are absent)."""
+    w, rp, col = tiny
+    rng = np.random.default_rng(13)
+    R = random_rotation(rng)
+    t = rng.standard_normal(3) * 10
+    f = w.as_f32("feat").astype(np.float64)
+    o0 = conv(w, rp, col, pos=w.pos.astype(np.float64), feat=f)
+    o1 = conv(w, rp, col, pos=w.pos.astype(np.float64) @ R.T + t, feat=_block_rotate(f, R, w.L))
+    assert rel(o1, _block_rotate(o0, R, w.L)) <= 1e-12
+    g = rng.standard_normal(f.shape)
+    a, b = 0.7, -1.9
+    assert rel(conv(w, rp, col, feat=a * f + b * g), a * o0 + b * conv(w, rp, col, feat=g)) <= 1e-12
 
 
 # ------------------------------------------------------------ radial basis --
