@@ -8,7 +8,9 @@ are resident in device memory before timing starts.  The headline value is
 neighbour edges per second of the whole step; the fused kernel's own time,
 measured with HIP events on the stream it runs on, gives the roofline block.
 The fp64 oracle is timed on the host's cores on a bounded sample of
-destination atoms as the CPU baseline.
+destination atoms as the CPU baseline.  The convolution stage (e2a_conv_fwd,
+the same messages summed without attention) is timed separately and reported
+in the breakdown.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -189,6 +191,23 @@ def main():
     attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
     progress(f"step {ms_step:.3f} ms (neighbours {nb_ms:.3f} ms, attention {attn_ms:.3f} ms)")
 
+    # the convolution stage (same messages, no attention weights), timed on
+    # its own after the steps; it is not part of the headline step
+    def conv():
+        B.e2a_conv_fwd(pos, rp, col, feat, w_rad, w_so2, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box,
+                       variant=args.variant, out=out, workspace=ws)
+
+    for _ in range(2):
+        conv()
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    cev[0].record(stream)
+    for _ in range(args.steps):
+        conv()
+    cev[1].record(stream)
+    torch.cuda.synchronize()
+    conv_ms = cev[0].elapsed_time(cev[1]) / args.steps
+    progress(f"convolution {conv_ms:.3f} ms")
+
     f_edge = flops_per_edge(w.L, w.C)
     achieved = f_edge * n_edges / (attn_ms * 1e-3) / 1e12
     traffic = traffic_per_launch()
@@ -215,7 +234,9 @@ def main():
                      "kernel": "e2a_attention_fwd (fused MFMA kernel + q/k prologue + weight pack)",
                      "flop_per_edge": f_edge},
         "breakdown": {"neighbors_ms": nb_ms, "attention_ms": attn_ms,
-                      "attention_edges_per_s": n_edges / (attn_ms * 1e-3)},
+                      "attention_edges_per_s": n_edges / (attn_ms * 1e-3),
+                      "conv_ms": conv_ms, "conv_edges_per_s": n_edges / (conv_ms * 1e-3),
+                      "conv_tflops": (f_edge - 2 * w.C) * n_edges / (conv_ms * 1e-3) / 1e12},
     }
     if not args.no_cpu_baseline:
         progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")

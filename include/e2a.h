@@ -7,10 +7,12 @@
  * The pages describe the layer's problem as atom positions, radius
  * neighbourhoods j in N(i), node irrep features and attention heads
  * (English technical summary, section 1 "Problem Statement" and section 2.2
- * "On-the-Fly Equivariant Attention").  This header turns that into two calls:
+ * "On-the-Fly Equivariant Attention").  This header turns that into these calls:
  *
  *   e2a_build_neighbors  - cell-list radius graph, CSR sorted by destination;
- *   e2a_attention_fwd    - the fused, node-centric layer.
+ *   e2a_attention_fwd    - the fused, node-centric layer;
+ *   e2a_conv_fwd         - the same messages summed without attention (the
+ *                          EAAS convolution stage).
  *
  * Conventions shared by every entry point:
  *   - Pointers named "device" are HIP device pointers owned by the caller.  The
@@ -176,6 +178,22 @@ size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int d
  * E2A_ERR_UNSUPPORTED (variant not built for the shape or dtype).
  */
 e2a_status e2a_attention_fwd(const e2a_attn_args* args, void* stream);
+
+/*
+ * The EAAS convolution stage: o_i = sum_{j in N(i)} v_ij, the same per-edge
+ * messages v_ij as e2a_attention_fwd (rotate in, per-m SO(2) mix, radial
+ * scale, rotate out) summed over the neighbourhood with no attention weights
+ * (technical summary section 2.1, "Equivariant Axis-Aligned Sparsification",
+ * whose result is stated for the convolution stage).  A plain sum: no
+ * division by the degree.
+ *
+ * Takes the same e2a_attn_args: w_q and w_k are not read (may be NULL), H
+ * only selects the build (the MFMA kernel is built for H = 8), and out_lse is
+ * ignored (nothing is written there).  An atom with no neighbours gets
+ * o_i = 0.  Same workspace (e2a_attention_workspace_bytes), same asynchrony,
+ * determinism and errors as e2a_attention_fwd.
+ */
+e2a_status e2a_conv_fwd(const e2a_attn_args* args, void* stream);
 
 #ifdef __cplusplus
 }

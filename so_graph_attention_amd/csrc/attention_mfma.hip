@@ -30,6 +30,9 @@
 //     of an edge land in the same lane), scales by alpha and by the radial
 //     weights (one extra MFMA against the radial basis), and folds the partial
 //     rotate-out D^T of this |m| into per-lane accumulators for all (l, m').
+//
+// The same kernel computes the EAAS convolution stage (section 2.1) when
+// p.conv is set: every edge weight is 1 and the messages are summed.
 #include <utility>
 
 #include "e2a_geometry.hpp"
@@ -248,6 +251,7 @@ struct MfmaParams {
   float box[3];
   int periodic;
   float cutoff;
+  int conv;   // convolution: every edge weight 1, no normaliser
 };
 
 struct Smem {
@@ -766,8 +770,10 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     const int jnext = slot_col(nxt, tid & (kET - 1));
 
     if (tid < kET) s.j[tid] = jcur;
-    if (tid < kC) s.q[tid] = p.q[ia * kC + tid];
-    else if (has_b) s.q[tid] = p.q[ib * kC + (tid - kC)];
+    if (!p.conv) {
+      if (tid < kC) s.q[tid] = p.q[ia * kC + tid];
+      else if (has_b) s.q[tid] = p.q[ib * kC + (tid - kC)];
+    }
     __syncthreads();
     // edge frames, D^0, D^1 and the radial basis: one lane per edge
     if (tid < kET) {
@@ -813,7 +819,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     {
       const int e = tid >> 3, h = tid & 7;
       float sv = -INFINITY;
-      if (e < ne) {
+      if (e < ne && !p.conv) {
         const int j = s.j[e];
         const float4* kp = reinterpret_cast<const float4*>(p.k + (int64_t)j * kC + h * kDH);
         const float* qv = s.q + (e >= nA ? kC : 0) + h * kDH;
@@ -833,7 +839,15 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     if (tid < 2 * kH) {
       const int d = tid / kH, h = tid % kH;
       const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
-      if (b1 > b0) {
+      if (p.conv) {
+        // convolution: weight 1 for every edge, normaliser 1, no rescale
+        for (int e = b0; e < b1; ++e) s.alpha[e * kH + h] = 1.0f;
+        if (b1 > b0) {
+          s.l_run[d * kH + h] = 1.0f;
+          s.m_run[d * kH + h] = 0.0f;
+        }
+        if (d == 0) s.scale[h] = 1.0f;
+      } else if (b1 > b0) {
         float mx = s.m_run[d * kH + h];
         for (int e = b0; e < b1; ++e) mx = fmaxf(mx, s.alpha[e * kH + h]);
         const float sc = expf(s.m_run[d * kH + h] - mx);
@@ -1125,7 +1139,8 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   if (wpx < 1) wpx = 1;
   p.wg_per_xcd = static_cast<int>(wpx);
   p.out = a->out;
-  p.out_lse = a->out_lse;
+  p.out_lse = pl.conv ? nullptr : a->out_lse;
+  p.conv = pl.conv ? 1 : 0;
   for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
   p.periodic = pl.periodic;
   p.cutoff = a->cutoff;

@@ -10,7 +10,9 @@
 // SO(2) mix of section 2.1, scales by the radial weights, rotates back and
 // folds the result into an online softmax.  Only the running max, the
 // normaliser and the value accumulator live across neighbours, all in LDS; no
-// per-edge tensor is written to device memory.
+// per-edge tensor is written to device memory.  With the convolution flag
+// (section 2.1: the EAAS convolution stage) every edge weight is 1 and the
+// messages are simply summed.
 //
 // This kernel keeps every product in fp32 on the vector ALUs.  It serves the
 // fp32 configurations (where bf16 matrix cores would miss a 1e-5 tolerance)
@@ -66,6 +68,7 @@ struct RefParams {
   int periodic;
   float cutoff;
   int C, H;
+  int conv;   // convolution: every edge weight 1, no normaliser
 };
 
 template <int L, typename T>
@@ -94,7 +97,8 @@ __global__ void __launch_bounds__(256) k_attention_reference(RefParams p, const 
   const float inv_sqrt_dh = 1.0f / sqrtf(static_cast<float>(dh));
 
   for (int t = tid; t < K * C; t += blockDim.x) acc[t] = 0.0f;
-  for (int t = tid; t < C; t += blockDim.x) qi[t] = p.q[i * C + t];
+  if (!p.conv)
+    for (int t = tid; t < C; t += blockDim.x) qi[t] = p.q[i * C + t];
   for (int t = tid; t < H; t += blockDim.x) { sm[t] = -INFINITY; sl[t] = 0.0f; }
   const float xi[3] = {p.pos[3 * i], p.pos[3 * i + 1], p.pos[3 * i + 2]};
   __syncthreads();
@@ -133,7 +137,14 @@ __global__ void __launch_bounds__(256) k_attention_reference(RefParams p, const 
       wigner_blocks<L>(R, D);
       radial_basis8(r, p.cutoff, rbf);
     }
-    if (tid >= 64 && tid < 64 + H) {
+    if (p.conv && tid >= 64 && tid < 64 + H) {
+      // convolution: weight 1 for every edge, nothing to rescale
+      const int h = tid - 64;
+      sl[h] = 1.0f;
+      sm[h] = 0.0f;
+      st[h] = 1.0f;
+      sp[h] = 1.0f;
+    } else if (tid >= 64 && tid < 64 + H) {
       const int h = tid - 64;
       const int j = p.col[e];
       float s = 0.0f;
@@ -237,7 +248,8 @@ e2a_status launch_ref_typed(const AttnPlan& pl, hipStream_t s) {
   p.q = pl.q;
   p.k = pl.k;
   p.out = a->out;
-  p.out_lse = a->out_lse;
+  p.out_lse = pl.conv ? nullptr : a->out_lse;
+  p.conv = pl.conv ? 1 : 0;
   for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
   p.periodic = pl.periodic;
   p.cutoff = a->cutoff;

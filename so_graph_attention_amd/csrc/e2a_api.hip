@@ -107,8 +107,14 @@ size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int d
   return attn_ws_layout(n_atoms, L, C, H, dtype).total;
 }
 
-e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
-  clear_error();
+}  // extern "C"
+
+namespace {
+
+// Shared body of the attention and convolution entry points: host-side
+// argument checks, then the launches.  The convolution needs no W_q / W_k and
+// writes no log-normaliser.
+e2a_status run_layer(const e2a_attn_args* a, void* stream, bool conv) {
   if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
   if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
   if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
@@ -121,9 +127,10 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
     return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
   if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
   if (a->n_atoms > 0) {
-    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out};
-    const char* names[] = {"pos", "row_ptr", "feat", "w_q", "w_k", "w_rad", "w_so2", "out"};
-    for (int t = 0; t < 8; ++t)
+    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_rad, a->w_so2, a->out, a->w_q, a->w_k};
+    const char* names[] = {"pos", "row_ptr", "feat", "w_rad", "w_so2", "out", "w_q", "w_k"};
+    const int need = conv ? 6 : 8;
+    for (int t = 0; t < need; ++t)
       if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
     if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
   }
@@ -145,13 +152,30 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
   pl.k = reinterpret_cast<float*>(base + ws.k);
   pl.mfma_ws = base + ws.w;
   pl.periodic = a->box != nullptr;
+  pl.conv = conv;
   for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
   hipStream_t s = static_cast<hipStream_t>(stream);
 
-  e2a_status st = launch_qk(pl, s);
-  if (st != E2A_OK) return st;
+  if (!conv) {
+    e2a_status st = launch_qk(pl, s);
+    if (st != E2A_OK) return st;
+  }
   const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
   return use_mfma ? launch_attention_mfma(pl, s) : launch_attention_reference(pl, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
+  clear_error();
+  return run_layer(a, stream, false);
+}
+
+e2a_status e2a_conv_fwd(const e2a_attn_args* a, void* stream) {
+  clear_error();
+  return run_layer(a, stream, true);
 }
 
 }  // extern "C"

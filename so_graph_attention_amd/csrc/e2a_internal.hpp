@@ -76,6 +76,7 @@ struct AttnPlan {
   void* mfma_ws;      // workspace of the MFMA path (packed weights, atom order)
   float box[3];
   int periodic;
+  bool conv;          // sum of the messages (no attention weights, no log-normaliser)
 };
 e2a_status launch_qk(const AttnPlan& p, hipStream_t s);
 e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);

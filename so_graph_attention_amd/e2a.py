@@ -27,7 +27,8 @@ VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
 
 # Every symbol include/e2a.h declares.
 EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
-            "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd"]
+            "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
+            "e2a_conv_fwd"]
 
 
 class E2AError(RuntimeError):
@@ -70,6 +71,8 @@ def _load():
                                                   ctypes.c_int]
     lib.e2a_attention_fwd.restype = ctypes.c_int32
     lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.e2a_conv_fwd.restype = ctypes.c_int32
+    lib.e2a_conv_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     return lib
 
 
@@ -165,12 +168,8 @@ def e2a_build_neighbors(pos: torch.Tensor, cutoff: float, box=None, batch: Optio
         return row_ptr, col[: ne.value]
 
 
-def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
-                      cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
-                      workspace=None, stream=None, with_lse: bool = False):
-    """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
-
-    Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
+def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box, variant, out, out_lse,
+           workspace, stream):
     dev = pos.device
     n = pos.shape[0]
     if feat.dtype == torch.bfloat16:
@@ -183,13 +182,12 @@ def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int
     _need(row_ptr, "row_ptr", torch.int64, dev)
     _need(col, "col", torch.int32, dev)
     for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
-        _need(t, name, feat.dtype, dev)
+        if t is not None:
+            _need(t, name, feat.dtype, dev)
     K = (L + 1) ** 2
     if out is None:
         out = torch.empty((n, K, C), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
-    if with_lse and out_lse is None:
-        out_lse = torch.empty((n, H), dtype=torch.float32, device=dev)
     if workspace is None:
         workspace = torch.empty(max(1, e2a_attention_workspace_bytes(n, L, C, H, dtype)), dtype=torch.uint8,
                                 device=dev)
@@ -208,6 +206,28 @@ def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int
     a.out_lse = _ptr(out_lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = workspace.numel()
-    _check(_lib.e2a_attention_fwd(ctypes.byref(a), _stream(stream)))
+    _check(fn(ctypes.byref(a), _stream(stream)))
     del box_arr
+    return out
+
+
+def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
+                      cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
+                      workspace=None, stream=None, with_lse: bool = False):
+    """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
+
+    Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
+    if with_lse and out_lse is None:
+        out_lse = torch.empty((pos.shape[0], H), dtype=torch.float32, device=pos.device)
+    out = _layer(_lib.e2a_attention_fwd, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box,
+                 variant, out, out_lse, workspace, stream)
     return (out, out_lse) if with_lse else out
+
+
+def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: int = 8, cutoff: float, box=None,
+                 variant: str = "auto", out=None, workspace=None, stream=None):
+    """Sum of the same per-edge messages without attention weights (the EAAS
+    convolution stage); returns out [N,(L+1)^2,C] fp32.  H only selects the
+    build (the MFMA kernel is built for H = 8)."""
+    return _layer(_lib.e2a_conv_fwd, pos, row_ptr, col, feat, None, None, w_rad, w_so2, L, C, H, cutoff, box,
+                  variant, out, None, workspace, stream)

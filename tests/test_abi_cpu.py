@@ -123,6 +123,37 @@ def test_attention_null_args():
     assert B.lib().e2a_attention_fwd(None, None) == B.E2A_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=16, H=3), B.E2A_ERR_INVALID_ARG),
+    (dict(L=5), B.E2A_ERR_INVALID_ARG),
+    (dict(n_rbf=6), B.E2A_ERR_INVALID_ARG),
+    (dict(cutoff=-1.0), B.E2A_ERR_INVALID_ARG),
+    (dict(feat=None), B.E2A_ERR_INVALID_ARG),
+    (dict(w_rad=None), B.E2A_ERR_INVALID_ARG),
+    (dict(w_so2=None), B.E2A_ERR_INVALID_ARG),
+    (dict(out=None), B.E2A_ERR_INVALID_ARG),
+    (dict(col=None), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=2), B.E2A_ERR_UNSUPPORTED),
+    (dict(workspace=None), B.E2A_ERR_INVALID_ARG),
+])
+def test_conv_rejects_on_host(kw, status):
+    a = attn_args(**kw)
+    st = B.lib().e2a_conv_fwd(ctypes.byref(a), None)
+    assert st == status, (st, B.last_error_message())
+    assert B.last_error_message()
+
+
+def test_conv_does_not_need_qk_weights():
+    """W_q and W_k may be NULL for the convolution: with them NULL and the
+    workspace missing, the call fails on the workspace, not on W_q."""
+    a = attn_args(w_q=None, w_k=None, workspace=None)
+    assert B.lib().e2a_attention_fwd(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "w_q" in B.last_error_message()
+    assert B.lib().e2a_conv_fwd(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "workspace" in B.last_error_message()
+    assert B.lib().e2a_conv_fwd(None, None) == B.E2A_ERR_INVALID_ARG
+
+
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     import importlib.util
     spec = importlib.util.spec_from_file_location("e2a_copy", B.__file__)
