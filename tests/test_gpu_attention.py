@@ -244,3 +244,36 @@ def test_mfma_kernel_long_rows(B):
     iso = np.diff(rp)[dest] == 0
     assert np.all(np.isneginf(lse[dest][iso])) and np.all(np.isneginf(want_lse[iso]))
     assert np.max(np.abs(lse[dest][~iso] - want_lse[~iso])) <= 1e-4
+
+
+def test_mfma_kernel_rows_at_the_limit(B):
+    """Destinations with 4096 neighbours (the neighbour build's maximum row,
+    128 full 32-edge chunks each), L = 1; sampled destinations against the
+    oracle, attention and convolution."""
+    from test_gpu_neighbors import dense_cluster
+    log("[attn] mfma rows of 4096")
+    geom = (dense_cluster(4096, seed=43), None, None, {"cluster": 4096})
+    w = make_config("tiny", L=1, C=128, H=8, dtype="bf16", geometry=geom)
+    w.cutoff = float(np.float32(5.0))
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    assert np.diff(rp).max() == 4096
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    out, lse = run_gpu(B, w, d, "mfma")
+    dest = np.array([0, 2048, 4096, 4097, 4120])
+    want, want_lse = oracle_out(w, rp, col, dest)
+    err = rel_l2(out[dest], want)
+    log(f"[attn] mfma 4096-row rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL_BF16
+    iso = np.diff(rp)[dest] == 0
+    assert np.max(np.abs(lse[dest][~iso] - want_lse[~iso])) <= 1e-4
+    conv = B.e2a_conv_fwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_rad"], d["w_so2"], L=w.L, C=w.C,
+                          H=w.H, cutoff=w.cutoff, variant="mfma")
+    torch.cuda.synchronize()
+    cwant = O.convolution(w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C,
+                          w.cutoff, dest=dest)
+    cerr = rel_l2(conv.cpu().numpy()[dest], cwant)
+    log(f"[conv] mfma 4096-row rel-L2 {cerr:.3e}")
+    assert cerr <= TOL_BF16

@@ -111,3 +111,19 @@ def test_neighbors_long_rows(B, deg):
     assert np.diff(rp_o).max() == deg
     rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0)
     assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
+
+
+def test_neighbors_row_limit(B):
+    """4096 neighbours, the documented maximum, fill the general path's LDS
+    sort buffer exactly and come out bit-exact; 4097 are refused with
+    E2A_ERR_UNSUPPORTED (from the count pass, before any row is filled)."""
+    log("[neighbors] row limit 4096 / 4097")
+    pos = dense_cluster(4096, seed=41)
+    rp_o, col_o = O.neighbor_list(pos, 5.0)
+    assert np.diff(rp_o).max() == 4096
+    rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0)
+    assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
+    pos = dense_cluster(4097, seed=42)
+    with pytest.raises(B.E2AError) as ei:
+        B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0)
+    assert ei.value.status == B.E2A_ERR_UNSUPPORTED
