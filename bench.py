@@ -65,6 +65,16 @@ def traffic_per_launch():
     return float(kv["hbm_bytes_per_launch"])
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, rp, col, seconds):
     """The oracle as it stands on a seeded sample of destination atoms, grown in
     batches of 32 until about `seconds` of CPU time have been spent."""
@@ -89,7 +99,8 @@ def cpu_baseline(w, rp, col, seconds):
     dt = time.perf_counter() - t0
     return {"value": edges / dt, "unit": "edges/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} seeded destination atoms ({edges} edges) of the same 100k-atom workload, "
-                      f"{dt:.1f} s of fp64 NumPy on {threads} BLAS threads"}
+                      f"{dt:.1f} s of fp64 NumPy on {threads} BLAS threads",
+            "host": {"cpu_model": cpu_model(), "os_cpu_count": os.cpu_count()}}
 
 
 def cpu_single_thread(name, seconds):
@@ -120,7 +131,7 @@ def cpu_single_thread(name, seconds):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="large")
     ap.add_argument("--variant", default="auto", choices=["auto", "mfma", "reference"])
@@ -188,7 +199,9 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     nb_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    attn_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in events]))
+    attn_all = [e[1].elapsed_time(e[2]) for e in events]
+    attn_ms = float(np.mean(attn_all))
+    attn_med = float(np.median(attn_all))
     progress(f"step {ms_step:.3f} ms (neighbours {nb_ms:.3f} ms, attention {attn_ms:.3f} ms)")
 
     # the convolution stage (same messages, no attention weights), timed on
@@ -233,7 +246,7 @@ def main():
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                      "kernel": "e2a_attention_fwd (fused MFMA kernel + q/k prologue + weight pack)",
                      "flop_per_edge": f_edge},
-        "breakdown": {"neighbors_ms": nb_ms, "attention_ms": attn_ms,
+        "breakdown": {"neighbors_ms": nb_ms, "attention_ms": attn_ms, "attention_ms_median": attn_med,
                       "attention_edges_per_s": n_edges / (attn_ms * 1e-3),
                       "conv_ms": conv_ms, "conv_edges_per_s": n_edges / (conv_ms * 1e-3),
                       "conv_tflops": (f_edge - 2 * w.C) * n_edges / (conv_ms * 1e-3) / 1e12},
