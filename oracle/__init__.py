@@ -6,9 +6,11 @@ calls it, and it shares no code, table or constant with the HIP sources.
 """
 from .e2a_oracle import (  # noqa: F401
     attention,
+    attention_backward,
     attention_online,
     convolution,
     edge_messages,
+    edge_messages_vjp,
     edge_rotation,
     min_image,
     neighbor_list,

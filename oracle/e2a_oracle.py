@@ -17,7 +17,8 @@ sparsity, spherical-harmonic closed forms and SciPy, Wigner-D group laws, gauge
 invariance, rotation equivariance, permutation invariance, an L=1 closed form,
 softmax limits, online == two-pass, brute-force neighbours, and equality with a
 dense Clebsch-Gordan tensor product; the convolution against the attention
-layer with uniform weights).  The conventions those invariants leave
+layer with uniform weights; the message adjoint by the exact adjoint identity
+and the feature gradient by central finite differences of the layer).  The conventions those invariants leave
 free (edge direction, W2 sign, radial basis widths, 1/sqrt(d_h), head split, no
 self loop) are readings, not facts the pages fix.
 """
@@ -327,6 +328,47 @@ def edge_messages(rvec, h_src, w_rad, w_so2, L, C, cutoff, gauge=None, rho=None,
     return v
 
 
+def edge_messages_vjp(rvec, g, w_rad, w_so2, L, C, cutoff, blocks=None):
+    """Adjoint of ``edge_messages`` with respect to h_src: for cotangents g
+    [E,(L+1)^2,C] of the messages returns dh [E,(L+1)^2,C].  Every step of the
+    message is linear in h_src, so this is the transpose of each step taken in
+    reverse order: dyhat^l = D^l g^l (transpose of the rotate-out), dy = rho *
+    dyhat (the radial scale is diagonal), the transposed per-m blocks
+      m = 0: dx_0 = dy_0 W0^T
+      m > 0: dx_+ = dy_+ W1^T + dy_- W2^T,  dx_- = -dy_+ W2^T + dy_- W1^T
+    and dh^l = D^l^T dx^l (transpose of the rotate-in)."""
+    rvec = np.asarray(rvec, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    E = rvec.shape[0]
+    r = np.linalg.norm(rvec, axis=1)
+    R = edge_rotation(rvec / r[:, None])
+    if blocks is None:
+        blocks = so2_blocks(w_so2, L, C)
+    D = [wigner_d(l, R) for l in range(L + 1)]
+    e = radial_basis(r, cutoff, np.asarray(w_rad).shape[0])
+    rho = np.einsum("ek,klc->elc", e, np.asarray(w_rad, dtype=np.float64))
+    dy = [rho[:, l, None, :] * np.einsum("enm,emc->enc", D[l], g[:, l * l:(l + 1) ** 2, :]) for l in range(L + 1)]
+    dx = [np.zeros_like(dy[l]) for l in range(L + 1)]
+    dY0 = np.concatenate([dy[l][:, l, :] for l in range(L + 1)], axis=1)
+    dX0 = dY0 @ blocks[0].T
+    for l in range(L + 1):
+        dx[l][:, l, :] = dX0[:, l * C:(l + 1) * C]
+    for m in range(1, L + 1):
+        W1, W2 = blocks[m]
+        dYp = np.concatenate([dy[l][:, l + m, :] for l in range(m, L + 1)], axis=1)
+        dYm = np.concatenate([dy[l][:, l - m, :] for l in range(m, L + 1)], axis=1)
+        dXp = dYp @ W1.T + dYm @ W2.T
+        dXm = -dYp @ W2.T + dYm @ W1.T
+        for l in range(m, L + 1):
+            s = (l - m) * C
+            dx[l][:, l + m, :] = dXp[:, s:s + C]
+            dx[l][:, l - m, :] = dXm[:, s:s + C]
+    dh = np.empty((E, (L + 1) ** 2, C))
+    for l in range(L + 1):
+        dh[:, l * l:(l + 1) ** 2, :] = np.einsum("emn,emc->enc", D[l], dx[l])
+    return dh
+
+
 # ---------------------------------------------------------------------------
 # Attention
 # ---------------------------------------------------------------------------
@@ -447,6 +489,81 @@ def convolution(pos, row_ptr, col, feat, w_rad, w_so2, L, C, cutoff, box=None, d
             out[nz] = np.add.reduceat(v, starts, axis=0)
         t = u
     return out
+
+
+def attention_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, grad_out, box=None,
+                       dest=None, chunk_edges=4096):
+    """Gradient of the layer with respect to the node features, dL/dh, for a
+    cotangent grad_out = dL/do [N,(L+1)^2,C] (the backward the technical
+    summary section 2.2 implies for training: per-edge quantities are
+    recomputed from the saved per-destination softmax statistics instead of
+    being stored).  Chain rule through ``attention``:
+
+      dv_ij     = alpha_ij^{h(c)} G_i                       (value path)
+      dalpha_ij = sum_{k, c in h} G_i v_ij,  delta_i = sum_{k, c in h} G_i o_i
+      ds_ij     = alpha_ij (dalpha_ij - delta_i)            (softmax)
+      dq_i = sum_j ds_ij k_j / sqrt(C/H),  dk_j = sum_i ds_ij q_i / sqrt(C/H)
+      dh_j = sum_{i: j in N(i)} edge_messages_vjp(r_ij, dv_ij)
+             + [l = 0 block] dq_j W_q^T + dk_j W_k^T.
+
+    Returns dh for the atoms ``dest`` (default all) [len(dest),(L+1)^2,C]
+    fp64; only the destinations whose edges reach ``dest`` are evaluated."""
+    pos = np.asarray(pos, dtype=np.float64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    n = pos.shape[0]
+    dest = np.arange(n) if dest is None else np.asarray(dest, dtype=np.int64)
+    K = (L + 1) ** 2
+    dh_ = C // H
+    blocks = so2_blocks(w_so2, L, C)
+    G = np.asarray(grad_out, dtype=np.float64)
+    q, k = qk_projection(np.asarray(feat, dtype=np.float64), w_q, w_k)
+    head_of_c = np.arange(C) // dh_
+    want = np.zeros(n, dtype=bool)
+    want[dest] = True
+    # centres i whose edges reach a wanted atom (as neighbour) or that are wanted themselves
+    src_rows = np.repeat(np.arange(n), np.diff(row_ptr))
+    centres = np.zeros(n, dtype=bool)
+    centres[src_rows[want[col]]] = True
+    centres |= want
+    cen = np.nonzero(centres & (np.diff(row_ptr) > 0))[0]
+    dfeat = np.zeros((n, K, C))
+    dq = np.zeros((n, C))
+    dk = np.zeros((n, C))
+    deg = row_ptr[cen + 1] - row_ptr[cen]
+    t = 0
+    while t < cen.size:
+        u = t
+        tot = 0
+        while u < cen.size and (u == t or tot + deg[u] <= chunk_edges):
+            tot += deg[u]
+            u += 1
+        ci = cen[t:u]
+        lens = deg[t:u]
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        e_idx = np.concatenate([np.arange(row_ptr[i], row_ptr[i + 1]) for i in ci])
+        i_of_e = np.repeat(ci, lens)
+        j_of_e = col[e_idx]
+        rvec = min_image(pos[j_of_e] - pos[i_of_e], box)
+        v = edge_messages(rvec, np.asarray(feat[j_of_e], dtype=np.float64), w_rad, w_so2, L, C, cutoff,
+                          blocks=blocks)
+        s = (q[i_of_e] * k[j_of_e]).reshape(-1, H, dh_).sum(axis=2) / math.sqrt(dh_)
+        alpha, _ = segment_softmax(s, starts, lens)
+        o = np.add.reduceat(alpha[:, head_of_c][:, None, :] * v, starts, axis=0)
+        Gi = G[i_of_e]
+        dalpha = (Gi * v).reshape(-1, K, H, dh_).sum(axis=(1, 3))
+        delta = (G[ci] * o).reshape(-1, K, H, dh_).sum(axis=(1, 3))
+        ds = alpha * (dalpha - np.repeat(delta, lens, axis=0))
+        dq[ci] += np.add.reduceat(np.repeat(ds, dh_, axis=1) * k[j_of_e], starts, axis=0) / math.sqrt(dh_)
+        np.add.at(dk, j_of_e, np.repeat(ds, dh_, axis=1) * q[i_of_e] / math.sqrt(dh_))
+        sel = want[j_of_e]
+        if sel.any():
+            dv = alpha[sel][:, head_of_c][:, None, :] * Gi[sel]
+            dh = edge_messages_vjp(rvec[sel], dv, w_rad, w_so2, L, C, cutoff, blocks=blocks)
+            np.add.at(dfeat, j_of_e[sel], dh)
+        t = u
+    dfeat[:, 0, :] += dq @ np.asarray(w_q, dtype=np.float64).T + dk @ np.asarray(w_k, dtype=np.float64).T
+    return dfeat[dest]
 
 
 def attention_online(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box=None,

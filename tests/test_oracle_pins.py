@@ -6,8 +6,9 @@ frame, closed forms and SciPy for the spherical harmonics, group laws of the
 Wigner-D blocks, gauge freedom about the edge axis, rotation/translation
 equivariance and permutation invariance of the layer, an L = 1 closed form in
 vector notation, softmax algebra, online == two-pass, brute-force neighbours,
-the empty-row case, equality with a dense Clebsch-Gordan tensor product, and
-the convolution against uniform-weight attention.
+the empty-row case, equality with a dense Clebsch-Gordan tensor product, the
+convolution against uniform-weight attention, and the feature gradient (the
+message adjoint identity and central finite differences of the layer).
 """
 import math
 
@@ -491,6 +492,89 @@ def test_p13_convolution_equivariance_and_linearity(tiny):
     g = rng.standard_normal(f.shape)
     a, b = 0.7, -1.9
     assert rel(conv(w, rp, col, feat=a * f + b * g), a * o0 + b * conv(w, rp, col, feat=g)) <= 1e-12
+
+
+# ---------------------------------------------------------------- P14 -------
+def _so2_count(L, C):
+    return sum((1 if m == 0 else 2) * ((L + 1 - m) * C) ** 2 for m in range(L + 1))
+
+
+@pytest.mark.parametrize("L,C", [(1, 4), (3, 5), (4, 3)])
+def test_p14_message_adjoint_identity(L, C):
+    """The message is linear in the neighbour's features, so its adjoint must
+    satisfy <edge_messages(h), g> = <h, edge_messages_vjp(g)> exactly (up to
+    rounding) for any edges, features, cotangents and weights."""
+    rng = np.random.default_rng(140 + L)
+    E = 9
+    rvec = rng.standard_normal((E, 3)) * 2.0
+    h = rng.standard_normal((E, (L + 1) ** 2, C))
+    g = rng.standard_normal((E, (L + 1) ** 2, C))
+    w_rad = rng.standard_normal((8, L + 1, C))
+    w_so2 = rng.standard_normal(_so2_count(L, C))
+    a = np.sum(O.edge_messages(rvec, h, w_rad, w_so2, L, C, 5.0) * g)
+    b = np.sum(h * O.edge_messages_vjp(rvec, g, w_rad, w_so2, L, C, 5.0))
+    assert abs(a - b) <= 1e-12 * max(abs(a), 1.0)
+
+
+def _small_periodic(L, C, H):
+    rng = np.random.default_rng(1414)
+    box = np.full(3, 11.0)
+    pos = _to_f32_periodic(_rsa_periodic(rng, 120, 11.0, 0.9), box)
+    return make_config("tiny", L=L, C=C, H=H, geometry=(pos, box.astype(np.float32), None, {}))
+
+
+@pytest.mark.parametrize("case", ["tiny_L1_H2", "tiny_L3_H2", "periodic_L2_H2"])
+def test_p14_feature_gradient_finite_differences(case):
+    """dL/dh from attention_backward against central differences of
+    L(h) = <G, attention(h)> along two random directions: one that moves only
+    the l = 0 block (the path through the logits, q and k, and the values) and
+    one that moves only l >= 1 (the values alone).  fp64, fourth-order
+    central differences with eps = 2e-4 (the error falls as eps^4 and is
+    about 1e-10 relative here)."""
+    if case == "tiny_L1_H2":
+        w = make_config("tiny", C=16, H=2)
+    elif case == "tiny_L3_H2":
+        w = make_config("tiny", L=3, C=8, H=2)
+    else:
+        w = _small_periodic(2, 8, 2)
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    rng = np.random.default_rng(1415)
+    f = w.as_f32("feat").astype(np.float64)
+    # scale the weights up so that the logits vary and the softmax is not flat
+    wq, wk = 3.0 * w.as_f32("w_q").astype(np.float64), 3.0 * w.as_f32("w_k").astype(np.float64)
+    G = rng.standard_normal(f.shape)
+
+    def loss(ff):
+        o, _ = O.attention(w.pos, rp, col, ff, wq, wk, w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H,
+                           w.cutoff, box=w.box)
+        return float(np.sum(G * o))
+
+    grad = O.attention_backward(w.pos, rp, col, f, wq, wk, w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H,
+                                w.cutoff, G, box=w.box)
+    eps = 2e-4
+    for part in ("l0", "rest"):
+        u = rng.standard_normal(f.shape)
+        if part == "l0":
+            u[:, 1:, :] = 0
+        else:
+            u[:, 0, :] = 0
+        # fourth-order central difference (error O(eps^4))
+        fd = (-loss(f + 2 * eps * u) + 8 * loss(f + eps * u) - 8 * loss(f - eps * u) + loss(f - 2 * eps * u)) \
+            / (12 * eps)
+        an = float(np.sum(grad * u))
+        assert abs(fd - an) <= 1e-8 * max(abs(an), 1e-3), (part, fd, an)
+
+
+def test_p14_feature_gradient_subset_equals_full(tiny):
+    """Asking for the gradient of some atoms only gives the same rows as the
+    full gradient."""
+    w, rp, col = tiny
+    G = np.random.default_rng(1416).standard_normal((w.n_atoms, (w.L + 1) ** 2, w.C))
+    args = (w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"), w.as_f32("w_rad"),
+            w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G)
+    full = O.attention_backward(*args)
+    dest = np.array([0, 5, 17, 63])
+    assert rel(O.attention_backward(*args, dest=dest), full[dest]) <= 1e-13
 
 
 # ------------------------------------------------------------ radial basis --
