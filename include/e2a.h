@@ -12,7 +12,9 @@
  *   e2a_build_neighbors  - cell-list radius graph, CSR sorted by destination;
  *   e2a_attention_fwd    - the fused, node-centric layer;
  *   e2a_conv_fwd         - the same messages summed without attention (the
- *                          EAAS convolution stage).
+ *                          EAAS convolution stage);
+ *   e2a_attention_bwd    - the layer's gradient with respect to the node
+ *                          features.
  *
  * Conventions shared by every entry point:
  *   - Pointers named "device" are HIP device pointers owned by the caller.  The
@@ -194,6 +196,43 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* args, void* stream);
  * determinism and errors as e2a_attention_fwd.
  */
 e2a_status e2a_conv_fwd(const e2a_attn_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Feature gradient                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of device workspace e2a_attention_bwd needs. */
+size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H);
+
+/*
+ * dL/dh of e2a_attention_fwd for a cotangent grad_out = dL/do: the backward
+ * that training the layer needs (technical summary section 2.2: per-edge
+ * quantities are recomputed from the per-destination softmax statistics
+ * rather than stored).  With G = grad_out, alpha_ij = exp(s_ij - lse_i):
+ *   ds_ij = alpha_ij (sum_{k, c in h} G_i v_ij - sum_{k, c in h} G_i o_i),
+ *   dh_j  = sum_{i: j in N(i)} D_ij^T SO2^T(rho_ij * D_ij (alpha_ij G_i))
+ *           + [l = 0] (sum_j' ds_jj' k_j' W_q^T + sum_i ds_ij q_i W_k^T) / sqrt(C/H),
+ * where SO2^T is the transposed per-m mix and D_ij, rho_ij belong to the
+ * edge from centre i to neighbour j.  Gradients of the weights and positions
+ * are not computed.
+ *
+ *   args       the forward's arguments, with out = the forward's output o
+ *              (f32 [n_atoms, (L+1)^2, C]) and out_lse = its log-normaliser
+ *              (f32 [n_atoms, H]), both INPUTS here and both required;
+ *              workspace / workspace_bytes as e2a_attention_bwd_workspace_bytes
+ *              gives for (n_atoms, n_edges).  The neighbour graph must be
+ *              symmetric (j in N(i) iff i in N(j)), as e2a_build_neighbors
+ *              builds it, with rows ascending in j.
+ *   grad_out   device f32 [n_atoms, (L+1)^2, C].
+ *   grad_feat  device f32 [n_atoms, (L+1)^2, C], fully overwritten.
+ *
+ * Runs scalar fp32 kernels (variant AUTO or REFERENCE; MFMA gives
+ * E2A_ERR_UNSUPPORTED).  The workspace keeps one float per edge and head
+ * (the softmax gradient ds).  Asynchronous and deterministic, like the
+ * forward.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG for a NULL
+ * out, out_lse, grad_out or grad_feat.
+ */
+e2a_status e2a_attention_bwd(const e2a_attn_args* args, const float* grad_out, float* grad_feat, void* stream);
 
 #ifdef __cplusplus
 }

@@ -7,6 +7,8 @@ names below, so that the build step can run before the library exists."""
 
 _EXPORTS = (
     "E2AError",
+    "e2a_attention_bwd",
+    "e2a_attention_bwd_workspace_bytes",
     "e2a_attention_fwd",
     "e2a_attention_workspace_bytes",
     "e2a_build_neighbors",

@@ -38,6 +38,22 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   return w;
 }
 
+struct BwdWs {
+  size_t q, k, dq, ds, total;
+};
+
+BwdWs bwd_ws_layout(int64_t n, int64_t e, int C, int H) {
+  BwdWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.q = take(sizeof(float) * (size_t)n * C);
+  w.k = take(sizeof(float) * (size_t)n * C);
+  w.dq = take(sizeof(float) * (size_t)n * C);
+  w.ds = take(sizeof(float) * (size_t)e * H);
+  w.total = off;
+  return w;
+}
+
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
 }  // namespace
@@ -176,6 +192,64 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
 e2a_status e2a_conv_fwd(const e2a_attn_args* a, void* stream) {
   clear_error();
   return run_layer(a, stream, true);
+}
+
+size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H) {
+  if (n_atoms < 0 || n_edges < 0 || L < 0 || L > 4 || C <= 0 || H <= 0) return 0;
+  return bwd_ws_layout(n_atoms, n_edges, C, H).total;
+}
+
+e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, float* grad_feat, void* stream) {
+  clear_error();
+  if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
+  if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
+  if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
+  if (a->L < 0 || a->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", a->L);
+  if (a->C <= 0 || a->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
+  if (a->C % a->H != 0) return fail(E2A_ERR_INVALID_ARG, "C=%d is not a multiple of H=%d", a->C, a->H);
+  if (a->H > 192) return fail(E2A_ERR_UNSUPPORTED, "H=%d; the backward kernels take at most 192 heads", a->H);
+  if (a->n_rbf != 8) return fail(E2A_ERR_INVALID_ARG, "n_rbf=%d; only 8 is supported", a->n_rbf);
+  if (a->dtype != E2A_DTYPE_F32 && a->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", a->dtype);
+  if (a->variant < E2A_VARIANT_AUTO || a->variant > E2A_VARIANT_MFMA)
+    return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
+  if (a->variant == E2A_VARIANT_MFMA) return fail(E2A_ERR_UNSUPPORTED, "the backward has no MFMA kernel");
+  if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
+  if (a->n_atoms > 0) {
+    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out, a->out_lse,
+                          grad_out, grad_feat};
+    const char* names[] = {"pos", "row_ptr", "feat", "w_q", "w_k", "w_rad", "w_so2", "out", "out_lse",
+                           "grad_out", "grad_feat"};
+    for (int t = 0; t < 11; ++t)
+      if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
+    if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+  }
+  if (a->box)
+    for (int d = 0; d < 3; ++d)
+      if (!finite_positive(a->box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
+  const BwdWs ws = bwd_ws_layout(a->n_atoms, a->n_edges, a->C, a->H);
+  if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
+  if (a->n_atoms == 0) return E2A_OK;
+
+  char* base = static_cast<char*>(a->workspace);
+  AttnPlan qk{};
+  qk.a = a;
+  qk.q = reinterpret_cast<float*>(base + ws.q);
+  qk.k = reinterpret_cast<float*>(base + ws.k);
+  BwdPlan pl{};
+  pl.a = a;
+  pl.grad_out = grad_out;
+  pl.grad_feat = grad_feat;
+  pl.q = qk.q;
+  pl.k = qk.k;
+  pl.dq = reinterpret_cast<float*>(base + ws.dq);
+  pl.ds = reinterpret_cast<float*>(base + ws.ds);
+  pl.periodic = a->box != nullptr;
+  for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  e2a_status st = launch_qk(qk, s);
+  if (st != E2A_OK) return st;
+  return launch_attention_backward(pl, s);
 }
 
 }  // extern "C"

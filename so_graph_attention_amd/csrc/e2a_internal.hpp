@@ -83,5 +83,18 @@ e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);
 bool mfma_supported(int L, int C, int H, int dtype);
 size_t mfma_workspace_bytes(int64_t n, int L, int C);
 e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
+// Feature gradient (attention_backward.hip).
+struct BwdPlan {
+  const e2a_attn_args* a;
+  const float* grad_out;   // dL/do [N, K, C]
+  float* grad_feat;        // dL/dh [N, K, C]
+  float* q;                // workspace f32 [N, C]
+  float* k;                // workspace f32 [N, C]
+  float* dq;               // workspace f32 [N, C]
+  float* ds;               // workspace f32 [E, H]
+  float box[3];
+  int periodic;
+};
+e2a_status launch_attention_backward(const BwdPlan& p, hipStream_t s);
 
 }  // namespace e2a

@@ -28,7 +28,7 @@ VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
 # Every symbol include/e2a.h declares.
 EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
             "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
-            "e2a_conv_fwd"]
+            "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd"]
 
 
 class E2AError(RuntimeError):
@@ -73,6 +73,11 @@ def _load():
     lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_conv_fwd.restype = ctypes.c_int32
     lib.e2a_conv_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.e2a_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_attention_bwd_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                                      ctypes.c_int]
+    lib.e2a_attention_bwd.restype = ctypes.c_int32
+    lib.e2a_attention_bwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -231,3 +236,53 @@ def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: in
     build (the MFMA kernel is built for H = 8)."""
     return _layer(_lib.e2a_conv_fwd, pos, row_ptr, col, feat, None, None, w_rad, w_so2, L, C, H, cutoff, box,
                   variant, out, None, workspace, stream)
+
+
+def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
+    return int(_lib.e2a_attention_bwd_workspace_bytes(n_atoms, n_edges, L, C, H))
+
+
+def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, *, L: int, C: int,
+                      H: int, cutoff: float, box=None, grad_feat=None, workspace=None, stream=None):
+    """dL/dh of the layer for grad_out = dL/do, from the forward's output and
+    log-normaliser; returns grad_feat [N,(L+1)^2,C] fp32."""
+    dev = pos.device
+    n = pos.shape[0]
+    if feat.dtype == torch.bfloat16:
+        dtype = E2A_DTYPE_BF16
+    elif feat.dtype == torch.float32:
+        dtype = E2A_DTYPE_F32
+    else:
+        raise TypeError("feat must be float32 or bfloat16")
+    _need(pos, "pos", torch.float32, dev)
+    _need(row_ptr, "row_ptr", torch.int64, dev)
+    _need(col, "col", torch.int32, dev)
+    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
+        _need(t, name, feat.dtype, dev)
+    for name, t in (("out", out), ("out_lse", out_lse), ("grad_out", grad_out)):
+        _need(t, name, torch.float32, dev)
+    K = (L + 1) ** 2
+    if grad_feat is None:
+        grad_feat = torch.empty((n, K, C), dtype=torch.float32, device=dev)
+    _need(grad_feat, "grad_feat", torch.float32, dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_attention_bwd_workspace_bytes(n, col.numel(), L, C, H)),
+                                dtype=torch.uint8, device=dev)
+    box_arr, box_p = _box_arg(box)
+    a = AttnArgs()
+    a.pos = _ptr(pos)
+    a.box = box_p
+    a.n_atoms = n
+    a.row_ptr = _ptr(row_ptr)
+    a.col = _ptr(col)
+    a.n_edges = col.numel()
+    a.cutoff = float(cutoff)
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS["auto"]
+    a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    _check(_lib.e2a_attention_bwd(ctypes.byref(a), _ptr(grad_out), _ptr(grad_feat), _stream(stream)))
+    del box_arr
+    return grad_feat

@@ -154,6 +154,31 @@ def test_conv_does_not_need_qk_weights():
     assert B.lib().e2a_conv_fwd(None, None) == B.E2A_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw,grads,status", [
+    (dict(), (None, FAKE), B.E2A_ERR_INVALID_ARG),                  # grad_out
+    (dict(), (FAKE, None), B.E2A_ERR_INVALID_ARG),                  # grad_feat
+    (dict(out=None), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),          # the forward's output is an input here
+    (dict(out_lse=None), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=2), (FAKE, FAKE), B.E2A_ERR_UNSUPPORTED),         # no MFMA backward
+    (dict(C=16, H=3), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(workspace_bytes=8), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),
+])
+def test_backward_rejects_on_host(kw, grads, status):
+    kw = dict(out_lse=FAKE, **kw) if "out_lse" not in kw else kw
+    a = attn_args(**kw)
+    st = B.lib().e2a_attention_bwd(ctypes.byref(a), grads[0], grads[1], None)
+    assert st == status, (st, B.last_error_message())
+    assert B.last_error_message()
+    assert B.lib().e2a_attention_bwd(None, FAKE, FAKE, None) == B.E2A_ERR_INVALID_ARG
+
+
+def test_backward_workspace_query():
+    n, e = 1000, 30000
+    got = B.e2a_attention_bwd_workspace_bytes(n, e, 3, 128, 8)
+    assert got >= 4 * (3 * n * 128 + e * 8)
+    assert B.e2a_attention_bwd_workspace_bytes(-1, e, 3, 128, 8) == 0
+
+
 def test_binding_refuses_missing_library(tmp_path, monkeypatch):
     import importlib.util
     spec = importlib.util.spec_from_file_location("e2a_copy", B.__file__)

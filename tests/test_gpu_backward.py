@@ -1,0 +1,128 @@
+"""GPU feature gradient (e2a_attention_bwd) vs the fp64 oracle's
+``attention_backward`` on the same seeded inputs and the same seeded
+cotangent.
+
+The backward reads the forward's output o and log-normaliser.  Most tests take
+them from the fp32 scalar forward, so that the comparison measures the
+backward kernels (fp32 throughout): relative L2 <= 1e-5, the forward's fp32
+bound (ds = alpha (dalpha - delta) subtracts two sums of the same size, but
+the measured error stays below 1e-6).  One test takes o and lse from the bf16
+MFMA forward (whose outputs are within 2e-2 of the oracle's) and holds the
+gradient to 2e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import make_config
+
+from gpu_util import log, rel_l2, sample_dest, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+@pytest.fixture(scope="module")
+def B():
+    import so_graph_attention_amd.e2a as mod
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return mod
+
+
+def setup(w, seed=99):
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    G = np.random.default_rng(seed).standard_normal((w.n_atoms, (w.L + 1) ** 2, w.C)).astype(np.float32)
+    d["G"] = torch.from_numpy(G).cuda()
+    return rp, col, d, G
+
+
+def gpu_grad(B, w, d, fwd_variant="reference"):
+    box = None if w.box is None else w.box.tolist()
+    out, lse = B.e2a_attention_fwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                                   d["w_so2"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, variant=fwd_variant,
+                                   with_lse=True)
+    g = B.e2a_attention_bwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                            d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box)
+    torch.cuda.synchronize()
+    return g.cpu().numpy()
+
+
+def oracle_grad(w, rp, col, G, dest=None):
+    return O.attention_backward(w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"),
+                                w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G, box=w.box,
+                                dest=dest)
+
+
+@pytest.mark.parametrize("L,C,H,dtype", [(1, 16, 1, "f32"), (1, 16, 2, "f32"), (0, 8, 2, "f32"),
+                                         (2, 24, 3, "bf16"), (3, 32, 4, "f32"), (4, 32, 8, "bf16")])
+def test_bwd_tiny_geometry_full(B, L, C, H, dtype):
+    log(f"[bwd] tiny geometry L={L} C={C} H={H} {dtype}")
+    w = make_config("tiny", L=L, C=C, H=H, dtype=dtype)
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d)
+    err = rel_l2(got, oracle_grad(w, rp, col, G))
+    log(f"[bwd] rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL_F32
+
+
+def test_bwd_small_periodic_box(B):
+    """120 atoms in an 11 A periodic box (about 47 neighbours each; minimum
+    image on every edge frame)."""
+    from workloads.generators import _rsa_periodic, _to_f32_periodic
+    log("[bwd] periodic")
+    rng = np.random.default_rng(1414)
+    box = np.full(3, 11.0)
+    pos = _to_f32_periodic(_rsa_periodic(rng, 120, 11.0, 0.9), box)
+    w = make_config("tiny", L=2, C=16, H=2, geometry=(pos, box.astype(np.float32), None, {}))
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d)
+    err = rel_l2(got, oracle_grad(w, rp, col, G))
+    log(f"[bwd] periodic rel-L2 {err:.3e}")
+    assert err <= TOL_F32
+
+
+def test_bwd_drug_sampled(B):
+    """The drug-like batch (L = 3, C = 128, H = 8, bf16 storage): seeded sample
+    of atoms, backward on the fp32 forward's outputs."""
+    log("[bwd] drug sampled")
+    w = make_config("drug")
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d)
+    dest = sample_dest(rp, 40, seed=21)
+    err = rel_l2(got[dest], oracle_grad(w, rp, col, G, dest))
+    log(f"[bwd] drug rel-L2 {err:.3e} on {dest.size} atoms")
+    assert err <= TOL_F32
+
+
+def test_bwd_after_mfma_forward(B):
+    """The same, with o and lse from the bf16 MFMA forward."""
+    log("[bwd] drug after the MFMA forward")
+    w = make_config("drug")
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d, fwd_variant="mfma")
+    dest = sample_dest(rp, 40, seed=22)
+    err = rel_l2(got[dest], oracle_grad(w, rp, col, G, dest))
+    log(f"[bwd] drug (MFMA forward) rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
+
+
+def test_bwd_isolated_atom_and_determinism(B):
+    """An atom with no neighbours gets the gradient of its l = 0 block only
+    through nothing (it is no one's neighbour and has no edges): zero.  Two
+    launches give bit-identical gradients."""
+    from workloads.generators import isolated_atom_variant
+    log("[bwd] isolated atom, determinism")
+    w = isolated_atom_variant(make_config("tiny", L=2, C=16, H=2))
+    rp, col, d, G = setup(w)
+    assert rp[-1] == rp[-2]
+    g1 = gpu_grad(B, w, d)
+    g2 = gpu_grad(B, w, d)
+    assert np.array_equal(g1, g2)
+    assert np.all(g1[-1] == 0)
+    assert rel_l2(g1, oracle_grad(w, rp, col, G)) <= TOL_F32
