@@ -362,10 +362,65 @@ __global__ void __launch_bounds__(256) k_bwd_value(BwdParams p, const T* __restr
   }
 }
 
-template <int L, typename T>
-e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t s) {
+// delta_i^h = sum_{k, c in h} G_i o_i, one thread per (atom, head).
+__global__ void k_bwd_delta(const float* __restrict__ grad, const float* __restrict__ out, int64_t n, int K, int C,
+                            int H, float* __restrict__ delta) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= n * H) return;
+  const int64_t i = t / H;
+  const int h = static_cast<int>(t % H), dh = C / H;
+  float s = 0.0f;
+  for (int kk = 0; kk < K; ++kk) {
+    const float* g = grad + (i * K + kk) * C + h * dh;
+    const float* o = out + (i * K + kk) * C + h * dh;
+    for (int c = 0; c < dh; ++c) s += g[c] * o[c];
+  }
+  delta[t] = s;
+}
+
+// The l = 0 terms of the gradient after the matrix-core passes, one
+// workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj' k_j' / sqrt(C/H),
+// dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found in the ascending
+// row of i), and grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T.
+template <typename T>
+__global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict__ w_q, const T* __restrict__ w_k,
+                                                 int K) {
+  const int C = p.C, H = p.H, dh = C / H;
+  extern __shared__ float smem[];
+  float* dq = smem;
+  float* dk = smem + C;
+  const int64_t j = blockIdx.x;
+  const float inv = 1.0f / sqrtf(static_cast<float>(dh));
+  const int64_t t0 = p.row_ptr[j], t1 = p.row_ptr[j + 1];
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    const int h = c / dh;
+    float aq = 0.0f, ak = 0.0f;
+    for (int64_t t = t0; t < t1; ++t) {
+      const int i = p.col[t];
+      aq += p.ds[t * H + h] * p.k[(int64_t)i * C + c];
+      const int64_t end = p.row_ptr[i + 1];
+      int64_t lo = p.row_ptr[i], hi = end;
+      while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (p.col[mid] < j) lo = mid + 1;
+        else hi = mid;
+      }
+      if (lo < end && p.col[lo] == j) ak += p.ds[lo * H + h] * p.q[(int64_t)i * C + c];
+    }
+    dq[c] = aq * inv;
+    dk[c] = ak * inv;
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    float v = 0.0f;
+    for (int cp = 0; cp < C; ++cp)
+      v += dq[cp] * load_as_f32(w_q, (size_t)c * C + cp) + dk[cp] * load_as_f32(w_k, (size_t)c * C + cp);
+    p.grad_feat[j * K * C + c] += v;
+  }
+}
+
+BwdParams bwd_params(const BwdPlan& pl) {
   const e2a_attn_args* a = pl.a;
-  constexpr int K = (L + 1) * (L + 1);
   BwdParams p{};
   p.pos = a->pos;
   p.row_ptr = a->row_ptr;
@@ -383,6 +438,14 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t s) {
   p.cutoff = a->cutoff;
   p.C = a->C;
   p.H = a->H;
+  return p;
+}
+
+template <int L, typename T>
+e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t s) {
+  const e2a_attn_args* a = pl.a;
+  constexpr int K = (L + 1) * (L + 1);
+  const BwdParams p = bwd_params(pl);
   const size_t smem = sizeof(float) * (3 * K * a->C + (L + 1) * a->C + 3 * a->C + wig_size(L) + 3 * a->H);
   if (smem > 160 * 1024) return fail(E2A_ERR_UNSUPPORTED, "backward kernels: C=%d too large for LDS", a->C);
   hipLaunchKernelGGL((k_bwd_query<L, T>), dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const T*>(a->feat),
@@ -408,6 +471,30 @@ e2a_status launch_bwd_dtype(const BwdPlan& pl, hipStream_t s) {
 }
 
 }  // namespace
+
+e2a_status launch_bwd_delta(const BwdPlan& pl, float* delta, hipStream_t s) {
+  const e2a_attn_args* a = pl.a;
+  const int K = (a->L + 1) * (a->L + 1);
+  const int64_t nt = a->n_atoms * a->H;
+  k_bwd_delta<<<(nt + 255) / 256, 256, 0, s>>>(pl.grad_out, a->out, a->n_atoms, K, a->C, a->H, delta);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+e2a_status launch_bwd_qk(const BwdPlan& pl, hipStream_t s) {
+  const e2a_attn_args* a = pl.a;
+  const int K = (a->L + 1) * (a->L + 1);
+  const BwdParams p = bwd_params(pl);
+  const size_t smem = sizeof(float) * 2 * a->C;
+  if (a->dtype == E2A_DTYPE_BF16)
+    hipLaunchKernelGGL(k_bwd_qk<uint16_t>, dim3(a->n_atoms), dim3(256), smem, s, p,
+                       static_cast<const uint16_t*>(a->w_q), static_cast<const uint16_t*>(a->w_k), K);
+  else
+    hipLaunchKernelGGL(k_bwd_qk<float>, dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const float*>(a->w_q),
+                       static_cast<const float*>(a->w_k), K);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
 
 e2a_status launch_attention_backward(const BwdPlan& pl, hipStream_t s) {
   if (pl.a->n_atoms == 0) return E2A_OK;

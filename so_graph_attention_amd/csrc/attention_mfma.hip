@@ -31,8 +31,9 @@
 //     weights (one extra MFMA against the radial basis), and folds the partial
 //     rotate-out D^T of this |m| into per-lane accumulators for all (l, m').
 //
-// The same kernel computes the EAAS convolution stage (section 2.1) when
-// p.conv is set: every edge weight is 1 and the messages are summed.
+// The same kernel, instantiated in other modes, computes the EAAS
+// convolution stage (section 2.1: every edge weight 1, the messages summed)
+// and the two passes of the layer's feature gradient.
 #include <utility>
 
 #include "e2a_geometry.hpp"
@@ -55,6 +56,15 @@ constexpr int kDH = 16;      // channels per head
 constexpr int kET = 32;      // edges per chunk
 constexpr int kThreads = 256;
 constexpr int kMinPerWg = 4;       // destinations per workgroup, at least
+
+// Kernel modes: the forward layer, and the two passes of its feature
+// gradient.  The query pass recomputes each edge's message and reduces it
+// against the destination's cotangent (the softmax gradient ds); the value
+// pass carries the cotangents back along the reversed edges through the
+// transposed mix.
+constexpr int kFwd = 0, kBwdQ = 1, kBwdV = 2;
+// The convolution stage: the forward with every edge weight 1.
+constexpr int kConv = 3;
 
 // Wigner-D rows in LDS are padded to a multiple of 4 floats (16-byte reads).
 __host__ __device__ constexpr int dpad(int l) { return ((2 * l + 1) + 3) / 4 * 4; }
@@ -251,7 +261,12 @@ struct MfmaParams {
   float box[3];
   int periodic;
   float cutoff;
-  int conv;   // convolution: every edge weight 1, no normaliser
+  // feature gradient
+  const float* lse;        // the forward's log-normaliser [N, H]
+  const float* grad;       // query pass: the cotangent G [N, K, C]
+  const float* delta;      // query pass: sum_{k, c in h} G_i o_i [N, H]
+  const uint16_t* wrad;    // value pass: W_rad [8][L+1][C]
+  float* ds;               // query pass: softmax gradient [E, H]
 };
 
 struct Smem {
@@ -273,6 +288,8 @@ struct Lane {
   f16x8 arbf[3];     // radial-basis A operands (all 32 edges; edges 0-15; edges 16-31)
   u32x4 mk[2];       // per fp16 pair of the rotate-out operand: keep A's edges (edge groups 0, 16)
   uint32_t flip;     // ~0 on lanes whose packed rows (n >= 8) belong to B
+  int nA;            // query pass: edges 0 .. nA-1 belong to A
+  int64_t ia, ib;    // query pass: atom ids of A and B
 };
 
 // Rotate-in task tau of block MN for this thread: degree l = MN + tau / 2,
@@ -329,17 +346,40 @@ __device__ __forceinline__ void task_store(uint16_t* A, int tid, const float (&x
   }
 }
 
-template <int L, int MN, int TAU>
-__device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid, const uint4 (&raw)[2 * L + 1]) {
-  constexpr int W = 2 * (MN + (TAU >> 1)) + 1;
+template <int L, int MN, int TAU, int MD>
+__device__ __forceinline__ void task_compute(const MfmaParams& p, const Smem& s, uint16_t* A, int tid,
+                                             const uint4 (&raw)[2 * L + 1]) {
+  constexpr int l = MN + (TAU >> 1);
+  constexpr int W = 2 * l + 1;
   float xp[8], xm[8];
   static_for<W>([&](auto nc) { task_term<L, MN, TAU, decltype(nc)::value>(s, tid, raw, xp, xm); });
+  if constexpr (MD == kBwdV) {
+    // value pass: the rotated cotangent is scaled by the edge's weight
+    // alpha (its head) and by the radial weights rho[l][c] of this degree
+    const int e = (tid >> 4) + 16 * (TAU & 1);
+    const int c0 = 8 * (tid & 15);
+    const float a = s.alpha[e * kH + c0 / kDH];
+    float rho[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) {
+      float w[8];
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.wrad + (k * (L + 1) + l) * kC + c0), w);
+      const float rb = s.rbf[e * 8 + k];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rho[q] += rb * w[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      xp[q] *= a * rho[q];
+      xm[q] *= a * rho[q];
+    }
+  }
   task_store<L, MN, TAU>(A, tid, xp, xm);
 }
 
 // Rotate-in of block MN: all its tasks, the loads of task tau+1 issued before
 // task tau's arithmetic.
-template <int L, int MN>
+template <int L, int MN, int MD>
 __device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, int tid) {
   using S = Shape<L>;
   static_assert(kThreads == 16 * kET / 2, "two edges x 16 channel groups per thread");
@@ -352,9 +392,9 @@ __device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, in
   static_for<NT>([&](auto tc) {
     constexpr int tau = decltype(tc)::value;
     if constexpr (tau + 1 < NT) task_load<L, MN, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
-    task_compute<L, MN, tau>(s, s.A + S::a_off(MN) / 2, tid, raw[tau & 1]);
+    task_compute<L, MN, tau, MD>(p, s, s.A + S::a_off(MN) / 2, tid, raw[tau & 1]);
     if constexpr (pair && tau >= NT - 2)
-      task_compute<L, L, tau - (NT - 2)>(s, s.A + S::a_off(L) / 2, tid, raw[tau & 1]);
+      task_compute<L, L, tau - (NT - 2), MD>(p, s, s.A + S::a_off(L) / 2, tid, raw[tau & 1]);
   });
 }
 
@@ -423,6 +463,56 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
   if constexpr (S::stream_has1(G)) ring.r[G % kRing][1] = load_b(wrsrc, vo, off1);
 }
 
+// Query pass: adds sum_{c in head} rho y (D G_dest)[lo, m][c] over the
+// lane's 16 (edge, row) values to dal[edge][head].  Register r of the lane
+// holds edge ebase + crow(r, half) (r < 8 for a +-m tile: its row r and row
+// r + 8 are the +m and -m rows of one edge).  rows[s] are the D^lo rows of
+// the values yv[s][r]; the cotangent of each edge's destination is rotated
+// into the edge's frame here, from fp16 D reads of four edges at a time.
+template <int L, int LO, int NR, int NS>
+__device__ __forceinline__ void dalpha_acc(const MfmaParams& p, const Smem& s, const Lane& ln, int lane, int wave,
+                                           int ebase, const int (&rows)[NS], const float (&yv)[NS][16]) {
+  constexpr int K = Shape<L>::K;
+  constexpr int W = 2 * LO + 1;
+  const int half = lane >> 5;
+  const int c = 32 * wave + (lane & 31);
+  float gA[W], gB[W];
+#pragma unroll
+  for (int n = 0; n < W; ++n) {
+    gA[n] = p.grad[(ln.ia * K + LO * LO + n) * kC + c];
+    gB[n] = p.grad[(ln.ib * K + LO * LO + n) * kC + c];
+  }
+  float prod[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) prod[r] = 0.0f;
+#pragma unroll
+  for (int si = 0; si < NS; ++si) {
+#pragma unroll
+    for (int a = 0; a < NR / 4; ++a) {
+      const int e0 = ebase + 8 * a + 4 * half;
+      float gr[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int n = 0; n < W; ++n) {
+        const f16x4 d4 = *reinterpret_cast<const f16x4*>(s.DT + (wig_off(LO) + rows[si] * W + n) * kET + e0);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gr[q] += static_cast<float>(d4[q]) * (e0 + q < ln.nA ? gA[n] : gB[n]);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) prod[4 * a + q] += yv[si][4 * a + q] * gr[q];
+    }
+  }
+  const int head = c / kDH;
+#pragma unroll
+  for (int r = 0; r < NR; ++r) {
+    float v = prod[r];
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    if ((lane & 15) == 0) s.q[(ebase + crow(r, half)) * kH + head] += v;
+  }
+}
+
 // GEMM of block M for this wave's 32 output channels, then the epilogue of
 // each output block: y_{+-m} from the W1/W2 products, u = alpha * rho * y
 // (rho from one MFMA against the radial basis), and the partial rotate-out
@@ -433,7 +523,7 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
 // k-steps ahead (continuing into the next block and the next chunk, whose
 // weights are the same) and A fragments one step ahead.  A scheduling
 // barrier after every k-step keeps the compiler from undoing this order.
-template <int L, int M>
+template <int L, int M, int MD>
 __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc,
                                           int tid, int wave, const Lane& ln, bool has_b, NodeState<L>& ns,
                                           WRing& ring) {
@@ -457,7 +547,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
     // radial-weight fragments of this block's output degrees, fetched now so
     // that they have landed by the epilogue
     f16x8 brad0 = zero8, brad1 = zero8;
-    if (half == 0) {
+    if (MD != kBwdV && half == 0) {
       brad0 = p.radpk[S::blk_lo(M, b, 0) * kC + c_own];
       if constexpr (M == 0 && S::has1(M, b)) brad1 = p.radpk[S::blk_lo(M, b, 1) * kC + c_own];
     }
@@ -497,13 +587,30 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
         if constexpr (f == 0 || S::has1(M, b)) {
           constexpr int lo = S::blk_lo(M, b, f);
           const f32x16 c0 = f == 0 ? (S::has1(M, b) ? c00 : c00 + c01) : c01;
-          const f16x8 brad = f == 0 ? brad0 : brad1;
-          const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
-          float u[16];
+          if constexpr (MD == kBwdV) {
+            // value pass: alpha and rho were applied to the rotated input
+            float u[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) u[r] = ln.alpha[r] * rho[r] * c0[r];
-          rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
-          rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+            for (int r = 0; r < 16; ++r) u[r] = c0[r];
+            rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
+            rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+          } else {
+            const f16x8 brad = f == 0 ? brad0 : brad1;
+            const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
+            if constexpr (MD == kBwdQ) {
+              float yv[1][16];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) yv[0][r] = rho[r] * c0[r];
+              const int rows[1] = {lo};
+              dalpha_acc<L, lo, 16, 1>(p, s, ln, lane, wave, 0, rows, yv);
+            } else {
+              float u[16];
+#pragma unroll
+              for (int r = 0; r < 16; ++r) u[r] = ln.alpha[r] * rho[r] * c0[r];
+              rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
+              rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+            }
+          }
         }
       });
     } else {
@@ -513,16 +620,38 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
         constexpr int t = decltype(tc)::value;
         const f32x16& C1 = t == 0 ? c00 : c10;
         const f32x16& C2 = t == 0 ? c01 : c11;
-        const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
-        float up[8], um[8];
+        if constexpr (MD == kBwdV) {
+          float up[8], um[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const float sc = ln.alpha[r + 8 * t] * rho[r];
-          up[r] = sc * (C1[r] - C2[r + 8]);
-          um[r] = sc * (C2[r] + C1[r + 8]);
+          for (int r = 0; r < 8; ++r) {
+            up[r] = C1[r] - C2[r + 8];
+            um[r] = C2[r] + C1[r + 8];
+          }
+          rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
+          rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+        } else {
+          const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
+          if constexpr (MD == kBwdQ) {
+            float yv[2][16];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              yv[0][r] = rho[r] * (C1[r] - C2[r + 8]);
+              yv[1][r] = rho[r] * (C2[r] + C1[r + 8]);
+            }
+            const int rows[2] = {lo + M, lo - M};
+            dalpha_acc<L, lo, 8, 2>(p, s, ln, lane, wave, 16 * t, rows, yv);
+          } else {
+            float up[8], um[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+              const float sc = ln.alpha[r + 8 * t] * rho[r];
+              up[r] = sc * (C1[r] - C2[r + 8]);
+              um[r] = sc * (C2[r] + C1[r + 8]);
+            }
+            rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
+            rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+          }
         }
-        rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
-        rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
       });
     }
   });
@@ -559,19 +688,19 @@ __device__ __forceinline__ void wig_level(const Smem& s, int tid) {
 // Blocks M = 0..L of one chunk: rotate-in of M into the operand region, a
 // barrier, the GEMM of M, and a barrier before the region is rewritten;
 // blocks L-1 and L share one rotate-in pass and run their GEMMs back to back.
-template <int L, int M>
+template <int L, int M, int MD>
 __device__ __forceinline__ void do_block(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid,
                                          int wave, const Lane& ln, bool has_b, NodeState<L>& ns, WRing& ring) {
-  rotate_in<L, M>(p, s, tid);
+  rotate_in<L, M, MD>(p, s, tid);
   __syncthreads();
-  mma_block<L, M>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+  mma_block<L, M, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
   if constexpr (M == L - 1) {
     // block L was rotated in with block L-1 and has its own operand space
-    mma_block<L, L>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+    mma_block<L, L, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
     __syncthreads();
   } else {
     __syncthreads();
-    if constexpr (M < L) do_block<L, M + 1>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+    if constexpr (M < L) do_block<L, M + 1, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
   }
 }
 
@@ -645,14 +774,14 @@ struct ChunkPlan {
 // their concatenated neighbour lists in chunks of 32 edge slots; a chunk
 // holds the rest of the current atom A and, when A ends inside it, the start
 // of the next atom B.  Only the last chunk is padded.
-template <int L>
+template <int L, int MD>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
                                         int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
                                         WRing& ring);
 
 // A persistent workgroup processes every wg_per_xcd-th destination of its
 // XCD's range.
-template <int L>
+template <int L, int MD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn_mfma(MfmaParams p) {
   using S = Shape<L>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -690,10 +819,10 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   // neighbours' features in the XCD's L2.
   const int xcd = blockIdx.x & 7;
   const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
-  stretch<L>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
+  stretch<L, MD>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
 }
 
-template <int L>
+template <int L, int MD>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
                                         int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
                                         WRing& ring) {
@@ -703,8 +832,9 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     const int64_t i = p.order[sl];
     return p.row_ptr[i + 1] - p.row_ptr[i];
   };
-  // atoms without neighbours: zero output, log-normaliser -inf
-  for (int64_t sl = s_lo + tid0 * step; sl < s_hi; sl += kThreads * step) {
+  // atoms without neighbours: zero output, log-normaliser -inf (the query
+  // pass writes no output)
+  for (int64_t sl = s_lo + tid0 * step; MD != kBwdQ && sl < s_hi; sl += kThreads * step) {
     if (degree(sl) == 0) {
       const int64_t i = p.order[sl];
       for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
@@ -769,10 +899,14 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     const ChunkPlan nxt = next_plan(cur);
     const int jnext = slot_col(nxt, tid & (kET - 1));
 
+    // logits s = <q_i, k_j>: the value pass runs over the reversed edges, so
+    // its centre supplies the key and its neighbour the query
+    const float* qsrc = MD == kBwdV ? p.k : p.q;
+    const float* ksrc = MD == kBwdV ? p.q : p.k;
     if (tid < kET) s.j[tid] = jcur;
-    if (!p.conv) {
-      if (tid < kC) s.q[tid] = p.q[ia * kC + tid];
-      else if (has_b) s.q[tid] = p.q[ib * kC + (tid - kC)];
+    if constexpr (MD != kConv) {
+      if (tid < kC) s.q[tid] = qsrc[ia * kC + tid];
+      else if (has_b) s.q[tid] = qsrc[ib * kC + (tid - kC)];
     }
     __syncthreads();
     // edge frames, D^0, D^1 and the radial basis: one lane per edge
@@ -788,7 +922,10 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
         float r3[3];
 #pragma unroll
         for (int d = 0; d < 3; ++d) {
-          float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * id + d];
+          // the value pass takes the frame of the edge from its neighbour to
+          // its centre: the same fp32 difference the forward computed
+          float dx = MD == kBwdV ? p.pos[3 * id + d] - p.pos[3 * (int64_t)j + d]
+                                 : p.pos[3 * (int64_t)j + d] - p.pos[3 * id + d];
           if (p.periodic) {
             if (dx > 0.5f * p.box[d]) dx -= p.box[d];
             else if (dx < -0.5f * p.box[d]) dx += p.box[d];
@@ -819,9 +956,9 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     {
       const int e = tid >> 3, h = tid & 7;
       float sv = -INFINITY;
-      if (e < ne && !p.conv) {
+      if (e < ne && MD != kConv) {
         const int j = s.j[e];
-        const float4* kp = reinterpret_cast<const float4*>(p.k + (int64_t)j * kC + h * kDH);
+        const float4* kp = reinterpret_cast<const float4*>(ksrc + (int64_t)j * kC + h * kDH);
         const float* qv = s.q + (e >= nA ? kC : 0) + h * kDH;
         float d = 0.0f;
 #pragma unroll
@@ -839,7 +976,19 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     if (tid < 2 * kH) {
       const int d = tid / kH, h = tid % kH;
       const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
-      if (p.conv) {
+      if constexpr (MD == kBwdQ || MD == kBwdV) {
+        // feature gradient: alpha from the forward's log-normaliser of the
+        // destination of the forward edge (the neighbour, in the value pass)
+        for (int e = b0; e < b1; ++e) {
+          const int64_t src = MD == kBwdQ ? (d == 0 ? ia : ib) : (int64_t)s.j[e];
+          s.alpha[e * kH + h] = expf(s.alpha[e * kH + h] - p.lse[src * kH + h]);
+        }
+        if (b1 > b0) {
+          s.l_run[d * kH + h] = 1.0f;
+          s.m_run[d * kH + h] = 0.0f;
+        }
+        if (d == 0) s.scale[h] = 1.0f;
+      } else if (MD == kConv) {
         // convolution: weight 1 for every edge, normaliser 1, no rescale
         for (int e = b0; e < b1; ++e) s.alpha[e * kH + h] = 1.0f;
         if (b1 > b0) {
@@ -895,10 +1044,28 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           ln.mk[g][q] = (t0 < nA ? 0x0000FFFFu : 0u) | (t0 + 1 < nA ? 0xFFFF0000u : 0u);
         }
       ln.flip = (lnr & 8) ? ~0u : 0u;
+      if constexpr (MD == kBwdQ) {
+        ln.nA = nA;
+        ln.ia = ia;
+        ln.ib = ib;
+        // s.q (free after the logits) collects dalpha[edge][head]
+        s.q[tid] = 0.0f;
+      }
     }
-    do_block<L, 0>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
-    // finish A (and B if it also ended); B's partial state becomes A's
-    if (a_done) {
+    do_block<L, 0, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
+    if constexpr (MD == kBwdQ) {
+      // ds = alpha (dalpha - delta) for the chunk's edges, one (edge, head)
+      // per thread, at the edge's place in the neighbour list
+      const int e = tid >> 3, h = tid & 7;
+      if (e < ne) {
+        const bool in_b = e >= nA;
+        const int64_t id = in_b ? ib : ia;
+        const int64_t g = in_b ? eb + (e - nA) : ea + e;
+        p.ds[g * kH + h] = s.alpha[e * kH + h] * (s.q[e * kH + h] - p.delta[id * kH + h]);
+      }
+      __syncthreads();
+    } else if (a_done) {
+      // finish A (and B if it also ended); B's partial state becomes A's
       finish_a<L>(p, s, ns, ia, tid, wave);
       if (b_done) finish_a<L>(p, s, ns, ib, tid, wave);
     }
@@ -909,8 +1076,11 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
 
 // Logical SO(2) weights -> B-fragment image: vector v holds, for lane
 // v % 64 of one k-step, the 8 values W[k0 .. k0+7][n] with k0 = 16 s + 8 (lane/32)
-// and n = (l_out - m) C + 32 wave + lane % 32.
-template <int L>
+// and n = (l_out - m) C + 32 wave + lane % 32.  With TR set, the image of the
+// transposed mix the value pass needs: W0^T for m = 0, and W1^T, -W2^T for
+// m > 0 (so that the kernel's complex product gives dx_+ = dy_+ W1^T + dy_- W2^T
+// and dx_- = -dy_+ W2^T + dy_- W1^T).
+template <int L, bool TR>
 __global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ out) {
   using S = Shape<L>;
   const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
@@ -930,7 +1100,10 @@ __global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ 
   const int64_t n = (int64_t)lo_rel * kC + 32 * wv + lane % 32;
   uint16_t vals[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) vals[q] = base[(k0 + q) * km + n];
+  for (int q = 0; q < 8; ++q) {
+    if constexpr (TR) vals[q] = base[n * km + k0 + q] ^ (wsel == 1 ? 0x8000 : 0);
+    else vals[q] = base[(k0 + q) * km + n];
+  }
   uint4 o;
   o.x = vals[0] | (uint32_t(vals[1]) << 16);
   o.y = vals[2] | (uint32_t(vals[3]) << 16);
@@ -1040,13 +1213,15 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part, total;
+  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
+  size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta
+  size_t total;
 };
 
 inline int64_t sort_blocks(int64_t n) { return (n + kSortBlock - 1) / kSortBlock; }
 
 template <int L>
-MfmaWs mfma_ws_layout(int64_t n) {
+MfmaWs mfma_ws_layout(int64_t n, bool backward) {
   using S = Shape<L>;
   MfmaWs m{};
   size_t off = 0;
@@ -1062,19 +1237,26 @@ MfmaWs mfma_ws_layout(int64_t n) {
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
   m.bbox = take(8 * sizeof(float));
   m.bbox_part = take(sizeof(float) * kBboxPartialFloats);
+  if (backward) {
+    m.wt = take(S::wtotal() * 16);
+    m.gbf = take(sizeof(uint16_t) * n * S::K * kC);
+    m.delta = take(sizeof(float) * n * kH);
+  }
   m.total = off;
   return m;
 }
 
+__global__ void k_to_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f32_to_bf16_rne(in[i]);
+}
 
+// Spatial order of the destinations (Morton code of a 64^3 grid over the
+// bounding box, stably sorted with the atom index as the tie-break) and the
+// packed forward weights.
 template <int L>
-e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
+e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_t st) {
   using S = Shape<L>;
-  const e2a_attn_args* a = pl.a;
-  const MfmaWs W = mfma_ws_layout<L>(a->n_atoms);
-  char* wb = static_cast<char*>(pl.mfma_ws);
-  bf16x8* wpk = reinterpret_cast<bf16x8*>(wb + W.w);
-  f16x8* radpk = reinterpret_cast<f16x8*>(wb + W.rad);
   int32_t* order = reinterpret_cast<int32_t*>(wb + W.order);
   int32_t* key = reinterpret_cast<int32_t*>(wb + W.key);
   int32_t* key2 = reinterpret_cast<int32_t*>(wb + W.key2);
@@ -1085,70 +1267,133 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
   float* bbox_part = reinterpret_cast<float*>(wb + W.bbox_part);
   const int64_t n = a->n_atoms;
+  const int64_t nb = (n + 255) / 256;
+  const int64_t nblk = sort_blocks(n);
   {
-    // spatial order of the destination atoms: Morton code of a 64^3 grid over
-    // the bounding box, stably sorted with the atom index as the tie-break
-    const int64_t nb = (n + 255) / 256;
-    const int64_t nblk = sort_blocks(n);
-    {
-      const e2a_status sb = launch_bbox(a->pos, n, bbox_part, bbox, st);
-      if (sb != E2A_OK) return sb;
-    }
-    k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, order);
-    E2A_LAUNCH_CHECK();
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass * kRadixBits;
-      const int32_t* kin = pass == 0 ? key : key2;
-      const int32_t* vin = pass == 0 ? order : val2;
-      int32_t* kout = pass == 0 ? key2 : key;
-      int32_t* vout = pass == 0 ? val2 : order;
-      k_radix_hist<<<nblk, 256, 0, st>>>(kin, n, shift, hist, nblk);
-      E2A_LAUNCH_CHECK();
-      e2a_status ss = exclusive_scan_i32(hist, kRadix * nblk, off, bsum, st);
-      if (ss != E2A_OK) return ss;
-      k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout);
-      E2A_LAUNCH_CHECK();
-    }
+    const e2a_status sb = launch_bbox(a->pos, n, bbox_part, bbox, st);
+    if (sb != E2A_OK) return sb;
   }
-  {
-    const int64_t nv = S::wtotal();
-    k_pack_so2<L><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2), wpk);
-    k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_rad), radpk);
+  k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, order);
+  E2A_LAUNCH_CHECK();
+  for (int pass = 0; pass < 2; ++pass) {
+    const int shift = pass * kRadixBits;
+    const int32_t* kin = pass == 0 ? key : key2;
+    const int32_t* vin = pass == 0 ? order : val2;
+    int32_t* kout = pass == 0 ? key2 : key;
+    int32_t* vout = pass == 0 ? val2 : order;
+    k_radix_hist<<<nblk, 256, 0, st>>>(kin, n, shift, hist, nblk);
+    E2A_LAUNCH_CHECK();
+    e2a_status ss = exclusive_scan_i32(hist, kRadix * nblk, off, bsum, st);
+    if (ss != E2A_OK) return ss;
+    k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout);
     E2A_LAUNCH_CHECK();
   }
-  MfmaParams p{};
+  const int64_t nv = S::wtotal();
+  k_pack_so2<L, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
+                                                          reinterpret_cast<bf16x8*>(wb + W.w));
+  k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_rad),
+                                                            reinterpret_cast<f16x8*>(wb + W.rad));
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+// Parameters shared by every mode; the persistent grid has two workgroups
+// per CU (the LDS and register budget), fewer when the system is small.
+template <int L>
+e2a_status base_params(const e2a_attn_args* a, const MfmaWs& W, char* wb, const float* box, int periodic,
+                       MfmaParams& p) {
+  p = MfmaParams{};
   p.pos = a->pos;
   p.row_ptr = a->row_ptr;
   p.col = a->col;
-  p.q = pl.q;
-  p.k = pl.k;
   p.feat = static_cast<const uint16_t*>(a->feat);
-  p.wpk = wpk;
-  p.radpk = radpk;
-  p.order = order;
-  p.n_atoms = n;
-  // persistent grid: two workgroups per CU (the LDS and register budget),
-  // fewer when the system is small
+  p.wpk = reinterpret_cast<const bf16x8*>(wb + W.w);
+  p.radpk = reinterpret_cast<const f16x8*>(wb + W.rad);
+  p.order = reinterpret_cast<const int32_t*>(wb + W.order);
+  p.n_atoms = a->n_atoms;
   int dev = 0, n_cu = 0;
   E2A_HIP_CHECK(hipGetDevice(&dev));
   E2A_HIP_CHECK(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev));
-  const int64_t per_xcd_atoms = (n + 7) / 8;
+  const int64_t per_xcd_atoms = (a->n_atoms + 7) / 8;
   int64_t wpx = (2 * (int64_t)n_cu + 7) / 8;
   const int64_t by_size = (per_xcd_atoms + kMinPerWg - 1) / kMinPerWg;
   if (wpx > by_size) wpx = by_size;
   if (wpx < 1) wpx = 1;
   p.wg_per_xcd = static_cast<int>(wpx);
-  p.out = a->out;
-  p.out_lse = pl.conv ? nullptr : a->out_lse;
-  p.conv = pl.conv ? 1 : 0;
-  for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
-  p.periodic = pl.periodic;
+  for (int d = 0; d < 3; ++d) p.box[d] = box[d];
+  p.periodic = periodic;
   p.cutoff = a->cutoff;
-  E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<L>),
+  return E2A_OK;
+}
+
+template <int L, int MD>
+e2a_status launch_mode(const MfmaParams& p, hipStream_t st) {
+  using S = Shape<L>;
+  E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<L, MD>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::total));
-  hipLaunchKernelGGL(k_attn_mfma<L>, dim3(8 * p.wg_per_xcd), dim3(kThreads), S::total, st, p);
+  hipLaunchKernelGGL((k_attn_mfma<L, MD>), dim3(8 * p.wg_per_xcd), dim3(kThreads), S::total, st, p);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
+}
+
+template <int L>
+e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
+  const e2a_attn_args* a = pl.a;
+  const MfmaWs W = mfma_ws_layout<L>(a->n_atoms, false);
+  char* wb = static_cast<char*>(pl.mfma_ws);
+  e2a_status e = prepare<L>(a, W, wb, st);
+  if (e != E2A_OK) return e;
+  MfmaParams p;
+  e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
+  if (e != E2A_OK) return e;
+  p.q = pl.q;
+  p.k = pl.k;
+  p.out = a->out;
+  p.out_lse = pl.conv ? nullptr : a->out_lse;
+  return pl.conv ? launch_mode<L, kConv>(p, st) : launch_mode<L, kFwd>(p, st);
+}
+
+// Feature gradient on the matrix cores: delta, the query pass (ds), the
+// value pass (the transposed messages into grad_feat) and the l = 0 terms.
+template <int L>
+e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
+  using S = Shape<L>;
+  const e2a_attn_args* a = pl.a;
+  const MfmaWs W = mfma_ws_layout<L>(a->n_atoms, true);
+  char* wb = static_cast<char*>(pl.mfma_ws);
+  e2a_status e = prepare<L>(a, W, wb, st);
+  if (e != E2A_OK) return e;
+  {
+    const int64_t nv = S::wtotal();
+    k_pack_so2<L, true><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
+                                                           reinterpret_cast<bf16x8*>(wb + W.wt));
+    const int64_t ng = a->n_atoms * S::K * kC;
+    k_to_bf16<<<(ng + 255) / 256, 256, 0, st>>>(pl.grad_out, reinterpret_cast<uint16_t*>(wb + W.gbf), ng);
+    E2A_LAUNCH_CHECK();
+  }
+  float* delta = reinterpret_cast<float*>(wb + W.delta);
+  e = launch_bwd_delta(pl, delta, st);
+  if (e != E2A_OK) return e;
+  MfmaParams p;
+  e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
+  if (e != E2A_OK) return e;
+  p.q = pl.q;
+  p.k = pl.k;
+  p.lse = a->out_lse;
+  // query pass
+  p.grad = pl.grad_out;
+  p.delta = delta;
+  p.ds = pl.ds;
+  e = launch_mode<L, kBwdQ>(p, st);
+  if (e != E2A_OK) return e;
+  // value pass: the cotangent in bf16 takes the features' place
+  p.feat = reinterpret_cast<const uint16_t*>(wb + W.gbf);
+  p.wpk = reinterpret_cast<const bf16x8*>(wb + W.wt);
+  p.wrad = static_cast<const uint16_t*>(a->w_rad);
+  p.out = pl.grad_feat;
+  e = launch_mode<L, kBwdV>(p, st);
+  if (e != E2A_OK) return e;
+  return launch_bwd_qk(pl, st);
 }
 
 }  // namespace
@@ -1157,14 +1402,24 @@ bool mfma_supported(int L, int C, int H, int dtype) {
   return L >= 1 && L <= 4 && C == kC && H == kH && dtype == E2A_DTYPE_BF16;
 }
 
-size_t mfma_workspace_bytes(int64_t n, int L, int C) {
+size_t mfma_workspace_bytes(int64_t n, int L, int C, bool backward) {
   if (C != kC) return 0;
   switch (L) {
-    case 1: return mfma_ws_layout<1>(n).total;
-    case 2: return mfma_ws_layout<2>(n).total;
-    case 3: return mfma_ws_layout<3>(n).total;
-    case 4: return mfma_ws_layout<4>(n).total;
+    case 1: return mfma_ws_layout<1>(n, backward).total;
+    case 2: return mfma_ws_layout<2>(n, backward).total;
+    case 3: return mfma_ws_layout<3>(n, backward).total;
+    case 4: return mfma_ws_layout<4>(n, backward).total;
     default: return 0;
+  }
+}
+
+e2a_status launch_backward_mfma(const BwdPlan& pl, hipStream_t s) {
+  switch (pl.a->L) {
+    case 1: return launch_bwd_typed<1>(pl, s);
+    case 2: return launch_bwd_typed<2>(pl, s);
+    case 3: return launch_bwd_typed<3>(pl, s);
+    case 4: return launch_bwd_typed<4>(pl, s);
+    default: return fail(E2A_ERR_UNSUPPORTED, "MFMA backward: L=%d", pl.a->L);
   }
 }
 

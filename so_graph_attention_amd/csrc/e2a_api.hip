@@ -33,16 +33,18 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   w.q = take(sizeof(float) * (size_t)n * C);
   w.k = take(sizeof(float) * (size_t)n * C);
-  w.w = take(mfma_supported(L, C, H, dtype) ? mfma_workspace_bytes(n, L, C) : 0);
+  w.w = take(mfma_supported(L, C, H, dtype) ? mfma_workspace_bytes(n, L, C, false) : 0);
   w.total = off;
   return w;
 }
 
 struct BwdWs {
-  size_t q, k, dq, ds, total;
+  size_t q, k, dq, ds, mfma, total;
 };
 
-BwdWs bwd_ws_layout(int64_t n, int64_t e, int C, int H) {
+// The matrix-core region is sized whenever (L, C, H) has a bf16 build, so
+// that the size does not depend on the storage type.
+BwdWs bwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   BwdWs w{};
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
@@ -50,6 +52,7 @@ BwdWs bwd_ws_layout(int64_t n, int64_t e, int C, int H) {
   w.k = take(sizeof(float) * (size_t)n * C);
   w.dq = take(sizeof(float) * (size_t)n * C);
   w.ds = take(sizeof(float) * (size_t)e * H);
+  w.mfma = take(mfma_supported(L, C, H, E2A_DTYPE_BF16) ? mfma_workspace_bytes(n, L, C, true) : 0);
   w.total = off;
   return w;
 }
@@ -196,7 +199,7 @@ e2a_status e2a_conv_fwd(const e2a_attn_args* a, void* stream) {
 
 size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H) {
   if (n_atoms < 0 || n_edges < 0 || L < 0 || L > 4 || C <= 0 || H <= 0) return 0;
-  return bwd_ws_layout(n_atoms, n_edges, C, H).total;
+  return bwd_ws_layout(n_atoms, n_edges, L, C, H).total;
 }
 
 e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, float* grad_feat, void* stream) {
@@ -212,7 +215,9 @@ e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, floa
   if (a->dtype != E2A_DTYPE_F32 && a->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", a->dtype);
   if (a->variant < E2A_VARIANT_AUTO || a->variant > E2A_VARIANT_MFMA)
     return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
-  if (a->variant == E2A_VARIANT_MFMA) return fail(E2A_ERR_UNSUPPORTED, "the backward has no MFMA kernel");
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  if (a->variant == E2A_VARIANT_MFMA && !mfma_ok)
+    return fail(E2A_ERR_UNSUPPORTED, "MFMA kernel not built for L=%d C=%d H=%d dtype=%d", a->L, a->C, a->H, a->dtype);
   if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
   if (a->n_atoms > 0) {
     const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out, a->out_lse,
@@ -226,7 +231,7 @@ e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, floa
   if (a->box)
     for (int d = 0; d < 3; ++d)
       if (!finite_positive(a->box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
-  const BwdWs ws = bwd_ws_layout(a->n_atoms, a->n_edges, a->C, a->H);
+  const BwdWs ws = bwd_ws_layout(a->n_atoms, a->n_edges, a->L, a->C, a->H);
   if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
     return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
   if (a->n_atoms == 0) return E2A_OK;
@@ -244,12 +249,14 @@ e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, floa
   pl.k = qk.k;
   pl.dq = reinterpret_cast<float*>(base + ws.dq);
   pl.ds = reinterpret_cast<float*>(base + ws.ds);
+  pl.mfma_ws = base + ws.mfma;
   pl.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
   hipStream_t s = static_cast<hipStream_t>(stream);
   e2a_status st = launch_qk(qk, s);
   if (st != E2A_OK) return st;
-  return launch_attention_backward(pl, s);
+  const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
+  return use_mfma ? launch_backward_mfma(pl, s) : launch_attention_backward(pl, s);
 }
 
 }  // extern "C"

@@ -81,7 +81,7 @@ struct AttnPlan {
 e2a_status launch_qk(const AttnPlan& p, hipStream_t s);
 e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);
 bool mfma_supported(int L, int C, int H, int dtype);
-size_t mfma_workspace_bytes(int64_t n, int L, int C);
+size_t mfma_workspace_bytes(int64_t n, int L, int C, bool backward);
 e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
 // Feature gradient (attention_backward.hip).
 struct BwdPlan {
@@ -92,9 +92,14 @@ struct BwdPlan {
   float* k;                // workspace f32 [N, C]
   float* dq;               // workspace f32 [N, C]
   float* ds;               // workspace f32 [E, H]
+  void* mfma_ws;           // workspace of the matrix-core path
   float box[3];
   int periodic;
 };
+// Scalar passes (any shape), and the matrix-core passes with their helpers.
 e2a_status launch_attention_backward(const BwdPlan& p, hipStream_t s);
+e2a_status launch_backward_mfma(const BwdPlan& p, hipStream_t s);
+e2a_status launch_bwd_delta(const BwdPlan& p, float* delta, hipStream_t s);
+e2a_status launch_bwd_qk(const BwdPlan& p, hipStream_t s);
 
 }  // namespace e2a

@@ -243,7 +243,8 @@ def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int
 
 
 def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, *, L: int, C: int,
-                      H: int, cutoff: float, box=None, grad_feat=None, workspace=None, stream=None):
+                      H: int, cutoff: float, box=None, variant: str = "auto", grad_feat=None, workspace=None,
+                      stream=None):
     """dL/dh of the layer for grad_out = dL/do, from the forward's output and
     log-normaliser; returns grad_feat [N,(L+1)^2,C] fp32."""
     dev = pos.device
@@ -277,7 +278,7 @@ def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_
     a.col = _ptr(col)
     a.n_edges = col.numel()
     a.cutoff = float(cutoff)
-    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS["auto"]
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
     a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
     a.out = _ptr(out)
     a.out_lse = _ptr(out_lse)

@@ -8,7 +8,9 @@ backward kernels (fp32 throughout): relative L2 <= 1e-5, the forward's fp32
 bound (ds = alpha (dalpha - delta) subtracts two sums of the same size, but
 the measured error stays below 1e-6).  One test takes o and lse from the bf16
 MFMA forward (whose outputs are within 2e-2 of the oracle's) and holds the
-gradient to 2e-2."""
+gradient to 2e-2.  The matrix-core backward (bf16 operands, fp32 accumulation)
+is held to 2e-2 against the oracle, on full outputs of 64-atom systems and on
+samples of the drug-like and 100k-atom workloads."""
 import numpy as np
 import pytest
 import torch
@@ -41,13 +43,14 @@ def setup(w, seed=99):
     return rp, col, d, G
 
 
-def gpu_grad(B, w, d, fwd_variant="reference"):
+def gpu_grad(B, w, d, fwd_variant="reference", bwd_variant="reference"):
     box = None if w.box is None else w.box.tolist()
     out, lse = B.e2a_attention_fwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
                                    d["w_so2"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, variant=fwd_variant,
                                    with_lse=True)
     g = B.e2a_attention_bwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
-                            d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box)
+                            d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box,
+                            variant=bwd_variant)
     torch.cuda.synchronize()
     return g.cpu().numpy()
 
@@ -105,7 +108,7 @@ def test_bwd_after_mfma_forward(B):
     log("[bwd] drug after the MFMA forward")
     w = make_config("drug")
     rp, col, d, G = setup(w)
-    got = gpu_grad(B, w, d, fwd_variant="mfma")
+    got = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="reference")
     dest = sample_dest(rp, 40, seed=22)
     err = rel_l2(got[dest], oracle_grad(w, rp, col, G, dest))
     log(f"[bwd] drug (MFMA forward) rel-L2 {err:.3e}")
@@ -126,3 +129,41 @@ def test_bwd_isolated_atom_and_determinism(B):
     assert np.array_equal(g1, g2)
     assert np.all(g1[-1] == 0)
     assert rel_l2(g1, oracle_grad(w, rp, col, G)) <= TOL_F32
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_bwd_mfma_tiny_geometry_full(B, L):
+    """Matrix-core passes, C = 128, H = 8, bf16: every row of the gradient of
+    a 64-atom system, against the oracle and against the scalar kernels."""
+    log(f"[bwd] mfma tiny geometry L={L}")
+    w = make_config("tiny", L=L, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    ref = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="reference")
+    err = rel_l2(got, oracle_grad(w, rp, col, G))
+    log(f"[bwd] mfma L={L} rel-L2 {err:.3e}, vs scalar {rel_l2(got, ref):.3e}")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL_BF16
+    assert rel_l2(got, ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("name", ["drug", "large"])
+def test_bwd_mfma_configs_sampled(B, name):
+    log(f"[bwd] mfma {name}")
+    w = make_config(name)
+    rp, col, d, G = setup(w)
+    got = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    assert np.all(np.isfinite(got))
+    dest = sample_dest(rp, 24, seed=23)
+    err = rel_l2(got[dest], oracle_grad(w, rp, col, G, dest))
+    log(f"[bwd] mfma {name} rel-L2 {err:.3e} on {dest.size} atoms")
+    assert err <= TOL_BF16
+
+
+def test_bwd_mfma_deterministic(B):
+    log("[bwd] mfma determinism")
+    w = make_config("drug")
+    rp, col, d, G = setup(w)
+    g1 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    g2 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    assert np.array_equal(g1, g2)
