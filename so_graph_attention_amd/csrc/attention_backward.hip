@@ -362,26 +362,31 @@ __global__ void __launch_bounds__(256) k_bwd_value(BwdParams p, const T* __restr
   }
 }
 
-// delta_i^h = sum_{k, c in h} G_i o_i, one thread per (atom, head).
-__global__ void k_bwd_delta(const float* __restrict__ grad, const float* __restrict__ out, int64_t n, int K, int C,
-                            int H, float* __restrict__ delta) {
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= n * H) return;
-  const int64_t i = t / H;
-  const int h = static_cast<int>(t % H), dh = C / H;
-  float s = 0.0f;
-  for (int kk = 0; kk < K; ++kk) {
-    const float* g = grad + (i * K + kk) * C + h * dh;
-    const float* o = out + (i * K + kk) * C + h * dh;
-    for (int c = 0; c < dh; ++c) s += g[c] * o[c];
+// delta_i^h = sum_{k, c in h} G_i o_i: one workgroup per atom, one thread
+// per channel (coalesced rows), then a sum over each head's channels.
+__global__ void k_bwd_delta(const float* __restrict__ grad, const float* __restrict__ out, int K, int C, int H,
+                            float* __restrict__ delta) {
+  extern __shared__ float sc[];
+  const int64_t i = blockIdx.x;
+  const int dh = C / H;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    float v = 0.0f;
+    for (int kk = 0; kk < K; ++kk) v += grad[(i * K + kk) * C + c] * out[(i * K + kk) * C + c];
+    sc[c] = v;
   }
-  delta[t] = s;
+  __syncthreads();
+  for (int h = threadIdx.x; h < H; h += blockDim.x) {
+    float v = 0.0f;
+    for (int c = h * dh; c < (h + 1) * dh; ++c) v += sc[c];
+    delta[i * H + h] = v;
+  }
 }
 
 // The l = 0 terms of the gradient after the matrix-core passes, one
 // workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj' k_j' / sqrt(C/H),
 // dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found in the ascending
-// row of i), and grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T.
+// row of i, once per edge, in tiles of blockDim edges), and
+// grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T.
 template <typename T>
 __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict__ w_q, const T* __restrict__ w_k,
                                                  int K) {
@@ -389,15 +394,15 @@ __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict
   extern __shared__ float smem[];
   float* dq = smem;
   float* dk = smem + C;
+  int64_t* rev = reinterpret_cast<int64_t*>(smem + 2 * C);   // [blockDim]: place of j in row i, or -1
   const int64_t j = blockIdx.x;
   const float inv = 1.0f / sqrtf(static_cast<float>(dh));
   const int64_t t0 = p.row_ptr[j], t1 = p.row_ptr[j + 1];
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    const int h = c / dh;
-    float aq = 0.0f, ak = 0.0f;
-    for (int64_t t = t0; t < t1; ++t) {
+  for (int c = threadIdx.x; c < C; c += blockDim.x) dq[c] = dk[c] = 0.0f;
+  for (int64_t base = t0; base < t1; base += blockDim.x) {
+    const int64_t t = base + threadIdx.x;
+    if (t < t1) {
       const int i = p.col[t];
-      aq += p.ds[t * H + h] * p.k[(int64_t)i * C + c];
       const int64_t end = p.row_ptr[i + 1];
       int64_t lo = p.row_ptr[i], hi = end;
       while (lo < hi) {
@@ -405,16 +410,29 @@ __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict
         if (p.col[mid] < j) lo = mid + 1;
         else hi = mid;
       }
-      if (lo < end && p.col[lo] == j) ak += p.ds[lo * H + h] * p.q[(int64_t)i * C + c];
+      rev[threadIdx.x] = (lo < end && p.col[lo] == j) ? lo : -1;
     }
-    dq[c] = aq * inv;
-    dk[c] = ak * inv;
+    __syncthreads();
+    const int64_t nt = t1 - base < (int64_t)blockDim.x ? t1 - base : (int64_t)blockDim.x;
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+      const int h = c / dh;
+      float aq = 0.0f, ak = 0.0f;
+      for (int u = 0; u < nt; ++u) {
+        const int i = p.col[base + u];
+        aq += p.ds[(base + u) * H + h] * p.k[(int64_t)i * C + c];
+        const int64_t e = rev[u];
+        if (e >= 0) ak += p.ds[e * H + h] * p.q[(int64_t)i * C + c];
+      }
+      dq[c] += aq;
+      dk[c] += ak;
+    }
+    __syncthreads();
   }
   __syncthreads();
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     float v = 0.0f;
     for (int cp = 0; cp < C; ++cp)
-      v += dq[cp] * load_as_f32(w_q, (size_t)c * C + cp) + dk[cp] * load_as_f32(w_k, (size_t)c * C + cp);
+      v += dq[cp] * inv * load_as_f32(w_q, (size_t)c * C + cp) + dk[cp] * inv * load_as_f32(w_k, (size_t)c * C + cp);
     p.grad_feat[j * K * C + c] += v;
   }
 }
@@ -475,8 +493,7 @@ e2a_status launch_bwd_dtype(const BwdPlan& pl, hipStream_t s) {
 e2a_status launch_bwd_delta(const BwdPlan& pl, float* delta, hipStream_t s) {
   const e2a_attn_args* a = pl.a;
   const int K = (a->L + 1) * (a->L + 1);
-  const int64_t nt = a->n_atoms * a->H;
-  k_bwd_delta<<<(nt + 255) / 256, 256, 0, s>>>(pl.grad_out, a->out, a->n_atoms, K, a->C, a->H, delta);
+  k_bwd_delta<<<a->n_atoms, 128, sizeof(float) * a->C, s>>>(pl.grad_out, a->out, K, a->C, a->H, delta);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
@@ -485,7 +502,7 @@ e2a_status launch_bwd_qk(const BwdPlan& pl, hipStream_t s) {
   const e2a_attn_args* a = pl.a;
   const int K = (a->L + 1) * (a->L + 1);
   const BwdParams p = bwd_params(pl);
-  const size_t smem = sizeof(float) * 2 * a->C;
+  const size_t smem = sizeof(float) * 2 * a->C + sizeof(int64_t) * 256;
   if (a->dtype == E2A_DTYPE_BF16)
     hipLaunchKernelGGL(k_bwd_qk<uint16_t>, dim3(a->n_atoms), dim3(256), smem, s, p,
                        static_cast<const uint16_t*>(a->w_q), static_cast<const uint16_t*>(a->w_k), K);
