@@ -346,9 +346,30 @@ __device__ __forceinline__ void task_store(uint16_t* A, int tid, const float (&x
   }
 }
 
+// Value pass: rho[l][c] for the thread's 8 channels and its two edges
+// (tid / 16 and tid / 16 + 16), from one read of W_rad[.][l][c0 .. c0+7].
+template <int L>
+__device__ __forceinline__ void rho_pair(const MfmaParams& p, const Smem& s, int tid, int l, float (&rho)[2][8]) {
+  const int e = tid >> 4;
+  const int c0 = 8 * (tid & 15);
+#pragma unroll
+  for (int q = 0; q < 8; ++q) rho[0][q] = rho[1][q] = 0.0f;
+#pragma unroll 1
+  for (int k = 0; k < 8; ++k) {
+    float w[8];
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.wrad + (k * (L + 1) + l) * kC + c0), w);
+    const float r0 = s.rbf[e * 8 + k], r1 = s.rbf[(e + 16) * 8 + k];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      rho[0][q] += r0 * w[q];
+      rho[1][q] += r1 * w[q];
+    }
+  }
+}
+
 template <int L, int MN, int TAU, int MD>
-__device__ __forceinline__ void task_compute(const MfmaParams& p, const Smem& s, uint16_t* A, int tid,
-                                             const uint4 (&raw)[2 * L + 1]) {
+__device__ __forceinline__ void task_compute(const Smem& s, uint16_t* A, int tid, const uint4 (&raw)[2 * L + 1],
+                                             const float (&rho)[8]) {
   constexpr int l = MN + (TAU >> 1);
   constexpr int W = 2 * l + 1;
   float xp[8], xm[8];
@@ -357,17 +378,7 @@ __device__ __forceinline__ void task_compute(const MfmaParams& p, const Smem& s,
     // value pass: the rotated cotangent is scaled by the edge's weight
     // alpha (its head) and by the radial weights rho[l][c] of this degree
     const int e = (tid >> 4) + 16 * (TAU & 1);
-    const int c0 = 8 * (tid & 15);
-    const float a = s.alpha[e * kH + c0 / kDH];
-    float rho[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll 1
-    for (int k = 0; k < 8; ++k) {
-      float w[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.wrad + (k * (L + 1) + l) * kC + c0), w);
-      const float rb = s.rbf[e * 8 + k];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) rho[q] += rb * w[q];
-    }
+    const float a = s.alpha[e * kH + 8 * (tid & 15) / kDH];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       xp[q] *= a * rho[q];
@@ -388,13 +399,16 @@ __device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, in
   constexpr bool pair = MN == L - 1;
   tid = opaque(tid);
   uint4 raw[2][2 * L + 1];
+  float rho[2][8];   // value pass: rho of the current degree for the thread's two edges
   task_load<L, MN, 0>(p, s, tid, raw[0]);
   static_for<NT>([&](auto tc) {
     constexpr int tau = decltype(tc)::value;
     if constexpr (tau + 1 < NT) task_load<L, MN, tau + 1>(p, s, tid, raw[(tau + 1) & 1]);
-    task_compute<L, MN, tau, MD>(p, s, s.A + S::a_off(MN) / 2, tid, raw[tau & 1]);
+    // tasks 2d and 2d+1 share degree MN + d (one edge each)
+    if constexpr (MD == kBwdV && tau % 2 == 0) rho_pair<L>(p, s, tid, MN + tau / 2, rho);
+    task_compute<L, MN, tau, MD>(s, s.A + S::a_off(MN) / 2, tid, raw[tau & 1], rho[tau & 1]);
     if constexpr (pair && tau >= NT - 2)
-      task_compute<L, L, tau - (NT - 2), MD>(p, s, s.A + S::a_off(L) / 2, tid, raw[tau & 1]);
+      task_compute<L, L, tau - (NT - 2), MD>(s, s.A + S::a_off(L) / 2, tid, raw[tau & 1], rho[tau & 1]);
   });
 }
 
