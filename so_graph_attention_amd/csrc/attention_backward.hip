@@ -382,14 +382,22 @@ __global__ void k_bwd_delta(const float* __restrict__ grad, const float* __restr
   }
 }
 
+// W_q^T and W_k^T in fp32, so that the l = 0 terms read them by rows.
+template <typename T>
+__global__ void k_wqk_transpose(const T* __restrict__ w_q, const T* __restrict__ w_k, int C, float* __restrict__ wt) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)C * C) return;
+  const int64_t c = t / C, cp = t % C;
+  wt[cp * C + c] = load_as_f32(w_q, t);
+  wt[(int64_t)C * C + cp * C + c] = load_as_f32(w_k, t);
+}
+
 // The l = 0 terms of the gradient after the matrix-core passes, one
 // workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj' k_j' / sqrt(C/H),
 // dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found in the ascending
 // row of i, once per edge, in tiles of blockDim edges), and
-// grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T.
-template <typename T>
-__global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict__ w_q, const T* __restrict__ w_k,
-                                                 int K) {
+// grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T (wt = W_q^T, W_k^T).
+__global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const float* __restrict__ wt, int K) {
   const int C = p.C, H = p.H, dh = C / H;
   extern __shared__ float smem[];
   float* dq = smem;
@@ -429,11 +437,12 @@ __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const T* __restrict
     __syncthreads();
   }
   __syncthreads();
+  const float* wqt = wt;
+  const float* wkt = wt + (size_t)C * C;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     float v = 0.0f;
-    for (int cp = 0; cp < C; ++cp)
-      v += dq[cp] * inv * load_as_f32(w_q, (size_t)c * C + cp) + dk[cp] * inv * load_as_f32(w_k, (size_t)c * C + cp);
-    p.grad_feat[j * K * C + c] += v;
+    for (int cp = 0; cp < C; ++cp) v += dq[cp] * wqt[(size_t)cp * C + c] + dk[cp] * wkt[(size_t)cp * C + c];
+    p.grad_feat[j * K * C + c] += v * inv;
   }
 }
 
@@ -502,13 +511,16 @@ e2a_status launch_bwd_qk(const BwdPlan& pl, hipStream_t s) {
   const e2a_attn_args* a = pl.a;
   const int K = (a->L + 1) * (a->L + 1);
   const BwdParams p = bwd_params(pl);
-  const size_t smem = sizeof(float) * 2 * a->C + sizeof(int64_t) * 256;
+  const int64_t cc = (int64_t)a->C * a->C;
   if (a->dtype == E2A_DTYPE_BF16)
-    hipLaunchKernelGGL(k_bwd_qk<uint16_t>, dim3(a->n_atoms), dim3(256), smem, s, p,
-                       static_cast<const uint16_t*>(a->w_q), static_cast<const uint16_t*>(a->w_k), K);
+    hipLaunchKernelGGL(k_wqk_transpose<uint16_t>, dim3((cc + 255) / 256), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a->w_q), static_cast<const uint16_t*>(a->w_k), a->C, pl.wqkt);
   else
-    hipLaunchKernelGGL(k_bwd_qk<float>, dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const float*>(a->w_q),
-                       static_cast<const float*>(a->w_k), K);
+    hipLaunchKernelGGL(k_wqk_transpose<float>, dim3((cc + 255) / 256), dim3(256), 0, s,
+                       static_cast<const float*>(a->w_q), static_cast<const float*>(a->w_k), a->C, pl.wqkt);
+  E2A_LAUNCH_CHECK();
+  const size_t smem = sizeof(float) * 2 * a->C + sizeof(int64_t) * 256;
+  hipLaunchKernelGGL(k_bwd_qk, dim3(a->n_atoms), dim3(256), smem, s, p, pl.wqkt, K);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }

@@ -39,7 +39,7 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
 }
 
 struct BwdWs {
-  size_t q, k, dq, ds, mfma, total;
+  size_t q, k, dq, ds, wqkt, mfma, total;
 };
 
 // The matrix-core region is sized whenever (L, C, H) has a bf16 build, so
@@ -52,6 +52,7 @@ BwdWs bwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   w.k = take(sizeof(float) * (size_t)n * C);
   w.dq = take(sizeof(float) * (size_t)n * C);
   w.ds = take(sizeof(float) * (size_t)e * H);
+  w.wqkt = take(sizeof(float) * 2 * (size_t)C * C);
   w.mfma = take(mfma_supported(L, C, H, E2A_DTYPE_BF16) ? mfma_workspace_bytes(n, L, C, true) : 0);
   w.total = off;
   return w;
@@ -249,6 +250,7 @@ e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, floa
   pl.k = qk.k;
   pl.dq = reinterpret_cast<float*>(base + ws.dq);
   pl.ds = reinterpret_cast<float*>(base + ws.ds);
+  pl.wqkt = reinterpret_cast<float*>(base + ws.wqkt);
   pl.mfma_ws = base + ws.mfma;
   pl.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;

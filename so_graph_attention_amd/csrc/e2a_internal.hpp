@@ -92,6 +92,7 @@ struct BwdPlan {
   float* k;                // workspace f32 [N, C]
   float* dq;               // workspace f32 [N, C]
   float* ds;               // workspace f32 [E, H]
+  float* wqkt;             // workspace f32 [2][C][C]: W_q^T, W_k^T
   void* mfma_ws;           // workspace of the matrix-core path
   float box[3];
   int periodic;
