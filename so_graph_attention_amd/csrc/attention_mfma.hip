@@ -80,6 +80,9 @@ struct Shape {
   static constexpr int DSZ = doff(L + 1);                       // fp32 D floats per edge (set-up only)
   static constexpr int DT = wig_size(L) * kET;                  // fp16 transposed D, [entry][edge]
   static constexpr int km(int m) { return (L + 1 - m) * kC; }   // GEMM K (= N) of block m
+  // query pass: 8-entry slots per (atom, channel) of the fp16 cotangent, one
+  // per degree (2 lo + 1 <= 7 entries, zero-padded) and a second for degree 4
+  static constexpr int gslots = L >= 4 ? L + 2 : L + 1;
   static constexpr int astride(int m) { return km(m) + 8; }     // bf16 per A row (padded)
   static constexpr int arows(int m) { return m == 0 ? kET : 2 * kET; }
   static constexpr int abytes(int m) { return arows(m) * astride(m) * 2; }
@@ -196,6 +199,11 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
+// Materialises a running sum where it stands: without it the whole chain of
+// additions is sunk to the sum's last use, with every term held live (or
+// spilled) until then.
+__device__ __forceinline__ void pin(float& x) { asm volatile("" : "+v"(x)); }
+
 __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, const f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -223,6 +231,7 @@ template <int L>
 struct NodeState {
   NodeAcc acc[L + 1];
   NodeAcc hi;
+  float dal[16];   // query pass: dalpha partials of the lane's 16 edges crow(r, half), its channel
 };
 template <int LO>
 __host__ __device__ constexpr bool packed_lo() { return 2 * LO + 1 <= 8; }
@@ -263,8 +272,9 @@ struct MfmaParams {
   float cutoff;
   // feature gradient
   const float* lse;        // the forward's log-normaliser [N, H]
-  const float* grad;       // query pass: the cotangent G [N, K, C]
   const float* delta;      // query pass: sum_{k, c in h} G_i o_i [N, H]
+  const f16x8* gpk;        // query pass: scaled fp16 cotangent, [N][gslots][C] vectors of 8
+  const float* gsc;        // query pass: per-atom inverse scale of gpk
   const uint16_t* wrad;    // value pass: W_rad [8][L+1][C]
   float* ds;               // query pass: softmax gradient [E, H]
 };
@@ -290,6 +300,7 @@ struct Lane {
   uint32_t flip;     // ~0 on lanes whose packed rows (n >= 8) belong to B
   int nA;            // query pass: edges 0 .. nA-1 belong to A
   int64_t ia, ib;    // query pass: atom ids of A and B
+  float gsA, gsB;    // query pass: inverse cotangent scales of A and B
 };
 
 // Rotate-in task tau of block MN for this thread: degree l = MN + tau / 2,
@@ -477,54 +488,92 @@ __device__ __forceinline__ void wring_load(WRing& ring, __amdgpu_buffer_rsrc_t w
   if constexpr (S::stream_has1(G)) ring.r[G % kRing][1] = load_b(wrsrc, vo, off1);
 }
 
-// Query pass: adds sum_{c in head} rho y (D G_dest)[lo, m][c] over the
-// lane's 16 (edge, row) values to dal[edge][head].  Register r of the lane
-// holds edge ebase + crow(r, half) (r < 8 for a +-m tile: its row r and row
-// r + 8 are the +m and -m rows of one edge).  rows[s] are the D^lo rows of
-// the values yv[s][r]; the cotangent of each edge's destination is rotated
-// into the edge's frame here, from fp16 D reads of four edges at a time.
-template <int L, int LO, int NR, int NS>
-__device__ __forceinline__ void dalpha_acc(const MfmaParams& p, const Smem& s, const Lane& ln, int lane, int wave,
-                                           int ebase, const int (&rows)[NS], const float (&yv)[NS][16]) {
-  constexpr int K = Shape<L>::K;
-  constexpr int W = 2 * LO + 1;
+// Query pass: B operands of degree LO's rotated cotangent, this lane's
+// channel 32 wave + lane % 32.  Degrees up to 3 carry A's G in k = 0-7 (lanes
+// 0-31) and B's in k = 8-15 (lanes 32-63); degree 4 has one operand per
+// destination, k = n (slot 4 holds n = 0-7, slot 5 n = 8).
+template <int L, int LO>
+__device__ __forceinline__ void grad_frags(const MfmaParams& p, const Lane& ln, int lane, int wave, f16x8& g0,
+                                           f16x8& g1) {
+  constexpr int NSL = Shape<L>::gslots;
   const int half = lane >> 5;
   const int c = 32 * wave + (lane & 31);
-  float gA[W], gB[W];
-#pragma unroll
-  for (int n = 0; n < W; ++n) {
-    gA[n] = p.grad[(ln.ia * K + LO * LO + n) * kC + c];
-    gB[n] = p.grad[(ln.ib * K + LO * LO + n) * kC + c];
+  if constexpr (LO < 4) {
+    // arithmetic, not a select: a select here becomes a load through a
+    // selected pointer into a private copy of the lane constants
+    const int64_t id = ln.ia + half * (ln.ib - ln.ia);
+    g0 = p.gpk[(id * NSL + LO) * kC + c];
+  } else {
+    g0 = p.gpk[(ln.ia * NSL + 4 + half) * kC + c];
+    g1 = p.gpk[(ln.ib * NSL + 4 + half) * kC + c];
   }
-  float prod[NR];
+}
+
+// Query pass: the cotangent of each row's destination in the edge's frame,
+// (D^LO G_dest)[row][c] = sum_n D^LO[row][n] G_dest[LO^2 + n][c], for the 32
+// rows of one output tile of block M: for M = 0 edge r (0-31) and D row LO;
+// for M > 0 edge 16 T + r % 16, D row LO + M (r < 16) or LO - M.  One matrix
+// product over k = n per destination, with the D entries (fp16, from LDS) as
+// A, the row r = lane % 32 and entries 8 (lane / 32) .. +7; a row keeps only
+// the half of k, or the product, that carries its own destination's G.  The
+// result is in G's scale (the destination's gsc undoes it).
+template <int L, int LO, int M, int T>
+__device__ __forceinline__ f32x16 rot_grad(const Smem& s, const Lane& ln, int lane, const f16x8 g0,
+                                           const f16x8 g1) {
+  constexpr int W = 2 * LO + 1;
+  // nothing here depends on the GEMM: a fresh lane index keeps these reads
+  // and products after it, instead of hoisted above it with their results
+  // held (or spilled) across the k-loop
+  lane = opaque(lane);
+  const int half = lane >> 5;
+  const int r = lane & 31;
+  const int e = M == 0 ? r : 16 * T + (r & 15);
+  const int mrow = M == 0 ? LO : (r < 16 ? LO + M : LO - M);
+  const _Float16* dr = s.DT + (wig_off(LO) + mrow * W) * kET + e;
+  const bool in_a = e < ln.nA;
+  f16x8 a = {};
+  if constexpr (LO < 4) {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) prod[r] = 0.0f;
+    for (int q = 0; q < W; ++q) a[q] = dr[q * kET];
+    const u32x4 keep = (in_a == (half == 0)) ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
+    return mfma_f16(__builtin_bit_cast(f16x8, __builtin_bit_cast(u32x4, a) & keep), g0, f32x16{});
+  } else {
+    // k = 8-15 carry n = 8 in their first entry; the others meet zeros in B
+    a[0] = dr[8 * half * kET];
 #pragma unroll
-  for (int si = 0; si < NS; ++si) {
-#pragma unroll
-    for (int a = 0; a < NR / 4; ++a) {
-      const int e0 = ebase + 8 * a + 4 * half;
-      float gr[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int n = 0; n < W; ++n) {
-        const f16x4 d4 = *reinterpret_cast<const f16x4*>(s.DT + (wig_off(LO) + rows[si] * W + n) * kET + e0);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) gr[q] += static_cast<float>(d4[q]) * (e0 + q < ln.nA ? gA[n] : gB[n]);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) prod[4 * a + q] += yv[si][4 * a + q] * gr[q];
-    }
+    for (int q = 1; q < 8; ++q) a[q] = dr[q * kET];
+    const u32x4 av = __builtin_bit_cast(u32x4, a);
+    const u32x4 ma = in_a ? u32x4{~0u, ~0u, ~0u, ~0u} : u32x4{0u, 0u, 0u, 0u};
+    const f32x16 g = mfma_f16(__builtin_bit_cast(f16x8, av & ma), g0, f32x16{});
+    return mfma_f16(__builtin_bit_cast(f16x8, av & ~ma), g1, g);
   }
-  const int head = c / kDH;
+}
+
+// One exchange step of a reduce-scatter over a row of 16 lanes: the partner
+// (through DPP control CTRL) differs from this lane in bit B of the lane
+// index; of the 2N values the lane keeps the half that bit selects and adds
+// the partner's copy of it.
+template <int CTRL, int B, int N>
+__device__ __forceinline__ void rs_step(float (&v)[16], int lane) {
+  const bool up = (lane & B) != 0;
 #pragma unroll
-  for (int r = 0; r < NR; ++r) {
-    float v = prod[r];
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
-    if ((lane & 15) == 0) s.q[(ebase + crow(r, half)) * kH + head] += v;
+  for (int k = 0; k < N; ++k) {
+    const float send = up ? v[k] : v[k + N];
+    const float keep = up ? v[k + N] : v[k];
+    const int got = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, send), CTRL, 0xF, 0xF, false);
+    v[k] = keep + __builtin_bit_cast(float, got);
   }
+}
+
+// Sum of v[r] over the 16 lanes of this lane's row, returned in lane r of the
+// row (r = lane % 16).  Partners: 15 - i (row mirror), 7 - i (half mirror),
+// i ^ 2 and i ^ 1 (quad permutations); they flip bits 3, 2, 1, 0 in turn.
+__device__ __forceinline__ float row_reduce_scatter16(float (&v)[16], int lane) {
+  rs_step<0x140, 8, 8>(v, lane);
+  rs_step<0x141, 4, 4>(v, lane);
+  rs_step<0x4E, 2, 2>(v, lane);
+  rs_step<0xB1, 1, 1>(v, lane);
+  return v[0];
 }
 
 // GEMM of block M for this wave's 32 output channels, then the epilogue of
@@ -564,6 +613,17 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
     if (MD != kBwdV && half == 0) {
       brad0 = p.radpk[S::blk_lo(M, b, 0) * kC + c_own];
       if constexpr (M == 0 && S::has1(M, b)) brad1 = p.radpk[S::blk_lo(M, b, 1) * kC + c_own];
+    }
+    // query pass: the destinations' cotangent of the block's output degrees
+    // (a pair of degrees below 4, or degree 4 alone: two operands at most)
+    f16x8 gq0 = zero8, gq1 = zero8;
+    if constexpr (MD == kBwdQ) {
+      if constexpr (M == 0 && S::has1(M, b)) {
+        grad_frags<L, S::blk_lo(M, b, 0)>(p, ln, lane, wave, gq0, gq1);
+        grad_frags<L, S::blk_lo(M, b, 1)>(p, ln, lane, wave, gq1, gq1);
+      } else {
+        grad_frags<L, S::blk_lo(M, b, 0)>(p, ln, lane, wave, gq0, gq1);
+      }
     }
     static_for<KS>([&](auto stc) {
       constexpr int st = decltype(stc)::value;
@@ -612,11 +672,13 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
             const f16x8 brad = f == 0 ? brad0 : brad1;
             const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
             if constexpr (MD == kBwdQ) {
-              float yv[1][16];
+              // the two operands are (lo0, lo1) for a pair, (A, B) for degree 4
+              const f32x16 gt = rot_grad<L, lo, 0, 0>(s, ln, lane, f == 0 ? gq0 : gq1, gq1);
 #pragma unroll
-              for (int r = 0; r < 16; ++r) yv[0][r] = rho[r] * c0[r];
-              const int rows[1] = {lo};
-              dalpha_acc<L, lo, 16, 1>(p, s, ln, lane, wave, 0, rows, yv);
+              for (int r = 0; r < 16; ++r) {
+                ns.dal[r] += rho[r] * c0[r] * gt[r];
+                pin(ns.dal[r]);
+              }
             } else {
               float u[16];
 #pragma unroll
@@ -646,14 +708,13 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
         } else {
           const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
           if constexpr (MD == kBwdQ) {
-            float yv[2][16];
+            // tile rows r and r + 16 are the +M and -M rows of one edge
+            const f32x16 gt = rot_grad<L, lo, M, t>(s, ln, lane, gq0, gq1);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-              yv[0][r] = rho[r] * (C1[r] - C2[r + 8]);
-              yv[1][r] = rho[r] * (C2[r] + C1[r + 8]);
+              ns.dal[8 * t + r] += rho[r] * ((C1[r] - C2[r + 8]) * gt[r] + (C2[r] + C1[r + 8]) * gt[r + 8]);
+              pin(ns.dal[8 * t + r]);
             }
-            const int rows[2] = {lo + M, lo - M};
-            dalpha_acc<L, lo, 8, 2>(p, s, ln, lane, wave, 16 * t, rows, yv);
           } else {
             float up[8], um[8];
 #pragma unroll
@@ -1062,12 +1123,25 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
         ln.nA = nA;
         ln.ia = ia;
         ln.ib = ib;
-        // s.q (free after the logits) collects dalpha[edge][head]
-        s.q[tid] = 0.0f;
+        ln.gsA = p.gsc[ia];
+        ln.gsB = p.gsc[ib];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ns.dal[r] = 0.0f;
       }
     }
     do_block<L, 0, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
     if constexpr (MD == kBwdQ) {
+      // dalpha[edge][head]: the lane's partials summed over the head's 16
+      // channels (a row of 16 lanes), lane r of the row ending with edge
+      // crow(r, half); s.q is free since the logits
+      {
+        const int lane = tid & 63;
+        const float v = row_reduce_scatter16(ns.dal, lane);
+        const int e = crow(lane & 15, lane >> 5);
+        const int head = 2 * wave + ((lane >> 4) & 1);
+        s.q[e * kH + head] = v * (e < nA ? ln.gsA : ln.gsB);
+      }
+      __syncthreads();
       // ds = alpha (dalpha - delta) for the chunk's edges, one (edge, head)
       // per thread, at the edge's place in the neighbour list
       const int e = tid >> 3, h = tid & 7;
@@ -1228,7 +1302,8 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 
 struct MfmaWs {
   size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
-  size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta
+  size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
+  size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales
   size_t total;
 };
 
@@ -1255,14 +1330,55 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
     m.wt = take(S::wtotal() * 16);
     m.gbf = take(sizeof(uint16_t) * n * S::K * kC);
     m.delta = take(sizeof(float) * n * kH);
+    m.gpk = take(16 * n * S::gslots * kC);
+    m.gsc = take(sizeof(float) * n);
   }
   m.total = off;
   return m;
 }
 
-__global__ void k_to_bf16(const float* __restrict__ in, uint16_t* __restrict__ out, int64_t n) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i < n) out[i] = f32_to_bf16_rne(in[i]);
+// The cotangent G in the two forms the feature gradient reads, one atom per
+// workgroup: bf16 (the value pass's features) and, for the query pass, fp16
+// times a power of two s_i that puts max |G_i| in [2^14, 2^15), so that small
+// cotangents keep fp16's precision and none overflows; gsc[i] = 1 / s_i.
+// The fp16 form is in 8-entry vectors per (slot, channel): slot lo holds
+// G[lo^2 + n], n < 2 lo + 1, zero-padded; degree 4 also fills slot 5 with
+// n = 8 (then zeros).
+template <int L>
+__global__ void __launch_bounds__(256) k_prep_grad(const float* __restrict__ g, uint16_t* __restrict__ gbf,
+                                                   f16x8* __restrict__ gpk, float* __restrict__ gsc) {
+  using S = Shape<L>;
+  constexpr int NSL = S::gslots;
+  __shared__ float red[4];
+  const int64_t i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* gi = g + i * S::K * kC;
+  uint16_t* bi = gbf + i * S::K * kC;
+  float mx = 0.0f;
+  for (int t = tid; t < S::K * kC; t += 256) {
+    const float v = gi[t];
+    bi[t] = f32_to_bf16_rne(v);
+    mx = fmaxf(mx, fabsf(v));
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  // max |G_i| < 2^(E - 126) for its biased exponent E: s_i = 2^(141 - E)
+  const int E = static_cast<int>((__float_as_uint(mx) >> 23) & 0xffu);
+  const int sh = min(100, max(-100, 141 - E));
+  const float sc = __uint_as_float(static_cast<uint32_t>(127 + sh) << 23);
+  if (tid == 0) gsc[i] = __uint_as_float(static_cast<uint32_t>(127 - sh) << 23);
+  for (int t = tid; t < NSL * kC; t += 256) {
+    const int slot = t / kC, c = t % kC;
+    const int lo = slot <= L ? slot : L;
+    const int nb = slot <= L ? 0 : 8;
+    f16x8 v = {};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (nb + q < 2 * lo + 1) v[q] = static_cast<_Float16>(gi[(lo * lo + nb + q) * kC + c] * sc);
+    gpk[(i * NSL + slot) * kC + c] = v;
+  }
 }
 
 // Spatial order of the destinations (Morton code of a 64^3 grid over the
@@ -1381,8 +1497,9 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
     const int64_t nv = S::wtotal();
     k_pack_so2<L, true><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
                                                            reinterpret_cast<bf16x8*>(wb + W.wt));
-    const int64_t ng = a->n_atoms * S::K * kC;
-    k_to_bf16<<<(ng + 255) / 256, 256, 0, st>>>(pl.grad_out, reinterpret_cast<uint16_t*>(wb + W.gbf), ng);
+    k_prep_grad<L><<<a->n_atoms, 256, 0, st>>>(pl.grad_out, reinterpret_cast<uint16_t*>(wb + W.gbf),
+                                               reinterpret_cast<f16x8*>(wb + W.gpk),
+                                               reinterpret_cast<float*>(wb + W.gsc));
     E2A_LAUNCH_CHECK();
   }
   float* delta = reinterpret_cast<float*>(wb + W.delta);
@@ -1395,7 +1512,8 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.k = pl.k;
   p.lse = a->out_lse;
   // query pass
-  p.grad = pl.grad_out;
+  p.gpk = reinterpret_cast<const f16x8*>(wb + W.gpk);
+  p.gsc = reinterpret_cast<const float*>(wb + W.gsc);
   p.delta = delta;
   p.ds = pl.ds;
   e = launch_mode<L, kBwdQ>(p, st);
