@@ -357,24 +357,37 @@ __device__ __forceinline__ void task_store(uint16_t* A, int tid, const float (&x
   }
 }
 
-// Value pass: rho[l][c] for the thread's 8 channels and its two edges
-// (tid / 16 and tid / 16 + 16), from one read of W_rad[.][l][c0 .. c0+7].
+// Value pass: rho[l][c] = sum_k rbf[e][k] W_rad[k][l][c] for the thread's 8
+// channels 8 g .. 8 g + 7 (g = lane % 16) and its two edges (tid / 16 and
+// tid / 16 + 16), as 16x16x32 fp16 products whose result lands in exactly
+// that layout: row 4 i + r, column g of product h is rho[e_i][8 g + 4 h + r]
+// for the wave's edge i = lane / 16.  The k index 8 r' + kb pairs basis
+// function kb with channel offset r': A's row 4 i + r holds edge i's basis
+// values in group r' = r only, B's column g holds the 8 basis weights of
+// channel 8 g + r' + 4 h (one packed vector).  Operands and precision are
+// those of the forward's radial product.
 template <int L>
 __device__ __forceinline__ void rho_pair(const MfmaParams& p, const Smem& s, int tid, int l, float (&rho)[2][8]) {
-  const int e = tid >> 4;
-  const int c0 = 8 * (tid & 15);
+  // rebuilt in every call (a fresh lane index) rather than kept live across the chunk
+  const int lane = opaque(tid) & 63, wave = tid >> 6;
+  const int e = 4 * wave + ((lane & 15) >> 2);   // the edge of A's row lane % 16
+  const bool diag = (lane & 3) == (lane >> 4);
+  f16x8 a0 = {}, a1 = {};
+  if (diag) {
+    a0 = to_vec8<f16x8>(s.rbf + e * 8);
+    a1 = to_vec8<f16x8>(s.rbf + (e + 16) * 8);
+  }
+  const f16x8* wl = p.radpk + l * kC + 8 * (lane & 15) + (lane >> 4);
+  const f16x8 b0 = wl[0], b1 = wl[4];
+  const f32x4 z = {};
+  const f32x4 r00 = mfma16_f16(a0, b0, z), r01 = mfma16_f16(a0, b1, z);
+  const f32x4 r10 = mfma16_f16(a1, b0, z), r11 = mfma16_f16(a1, b1, z);
 #pragma unroll
-  for (int q = 0; q < 8; ++q) rho[0][q] = rho[1][q] = 0.0f;
-#pragma unroll 1
-  for (int k = 0; k < 8; ++k) {
-    float w[8];
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.wrad + (k * (L + 1) + l) * kC + c0), w);
-    const float r0 = s.rbf[e * 8 + k], r1 = s.rbf[(e + 16) * 8 + k];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      rho[0][q] += r0 * w[q];
-      rho[1][q] += r1 * w[q];
-    }
+  for (int r = 0; r < 4; ++r) {
+    rho[0][r] = r00[r];
+    rho[0][4 + r] = r01[r];
+    rho[1][r] = r10[r];
+    rho[1][4 + r] = r11[r];
   }
 }
 
