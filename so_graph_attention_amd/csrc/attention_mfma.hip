@@ -275,7 +275,6 @@ struct MfmaParams {
   const float* delta;      // query pass: sum_{k, c in h} G_i o_i [N, H]
   const f16x8* gpk;        // query pass: scaled fp16 cotangent, [N][gslots][C] vectors of 8
   const float* gsc;        // query pass: per-atom inverse scale of gpk
-  const uint16_t* wrad;    // value pass: W_rad [8][L+1][C]
   float* ds;               // query pass: softmax gradient [E, H]
 };
 
@@ -1534,7 +1533,6 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   // value pass: the cotangent in bf16 takes the features' place
   p.feat = reinterpret_cast<const uint16_t*>(wb + W.gbf);
   p.wpk = reinterpret_cast<const bf16x8*>(wb + W.wt);
-  p.wrad = static_cast<const uint16_t*>(a->w_rad);
   p.out = pl.grad_feat;
   e = launch_mode<L, kBwdV>(p, st);
   if (e != E2A_OK) return e;
