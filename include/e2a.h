@@ -226,11 +226,18 @@ size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L
  *   grad_out   device f32 [n_atoms, (L+1)^2, C].
  *   grad_feat  device f32 [n_atoms, (L+1)^2, C], fully overwritten.
  *
- * Runs scalar fp32 kernels (variant AUTO or REFERENCE; MFMA gives
- * E2A_ERR_UNSUPPORTED).  The workspace keeps one float per edge and head
- * (the softmax gradient ds).  Asynchronous and deterministic, like the
- * forward.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG for a NULL
- * out, out_lse, grad_out or grad_feat.
+ * Variant REFERENCE runs scalar fp32 kernels (any shape, fp32 or bf16
+ * storage).  MFMA runs the matrix-core passes (bf16 storage, C = 128, H = 8,
+ * 1 <= L <= 4; other shapes give E2A_ERR_UNSUPPORTED): a query pass and a
+ * value pass of the forward's fused kernel with bf16 operands and fp32
+ * accumulation, relative L2 error a few 1e-3 against an exact gradient.
+ * AUTO takes MFMA where it is built, else REFERENCE.  The matrix-core passes
+ * normalise the cotangent by powers of two (per atom, and by its largest
+ * entry), so its magnitude does not matter within fp32's normal range.
+ * The workspace keeps one float per edge and head (the softmax gradient ds)
+ * and, for MFMA, the cotangent's copies.  Asynchronous and deterministic,
+ * like the forward.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG
+ * for a NULL out, out_lse, grad_out or grad_feat.
  */
 e2a_status e2a_attention_bwd(const e2a_attn_args* args, const float* grad_out, float* grad_feat, void* stream);
 

@@ -275,6 +275,7 @@ struct MfmaParams {
   const float* delta;      // query pass: sum_{k, c in h} G_i o_i [N, H]
   const f16x8* gpk;        // query pass: scaled fp16 cotangent, [N][gslots][C] vectors of 8
   const float* gsc;        // query pass: per-atom inverse scale of gpk
+  const float* gnorm;      // value pass: power of two that brings max |G| into [1, 2)
   float* ds;               // query pass: softmax gradient [E, H]
 };
 
@@ -1070,8 +1071,14 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           const int64_t src = MD == kBwdQ ? (d == 0 ? ia : ib) : (int64_t)s.j[e];
           s.alpha[e * kH + h] = expf(s.alpha[e * kH + h] - p.lse[src * kH + h]);
         }
+        // the value pass carries the cotangent times gnorm (alpha scaled by
+        // it), so that its rotate-out coefficients sit in fp16's range
+        // whatever the cotangent's magnitude; the normaliser divides it out
+        const float gs = MD == kBwdV ? *p.gnorm : 1.0f;
+        if constexpr (MD == kBwdV)
+          for (int e = b0; e < b1; ++e) s.alpha[e * kH + h] *= gs;
         if (b1 > b0) {
-          s.l_run[d * kH + h] = 1.0f;
+          s.l_run[d * kH + h] = gs;
           s.m_run[d * kH + h] = 0.0f;
         }
         if (d == 0) s.scale[h] = 1.0f;
@@ -1315,7 +1322,8 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 struct MfmaWs {
   size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
   size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
-  size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales
+  size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales,
+  size_t gnorm;            // and the value pass's cotangent scale
   size_t total;
 };
 
@@ -1344,6 +1352,7 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
     m.delta = take(sizeof(float) * n * kH);
     m.gpk = take(16 * n * S::gslots * kC);
     m.gsc = take(sizeof(float) * n);
+    m.gnorm = take(sizeof(float));
   }
   m.total = off;
   return m;
@@ -1390,6 +1399,24 @@ __global__ void __launch_bounds__(256) k_prep_grad(const float* __restrict__ g, 
     for (int q = 0; q < 8; ++q)
       if (nb + q < 2 * lo + 1) v[q] = static_cast<_Float16>(gi[(lo * lo + nb + q) * kC + c] * sc);
     gpk[(i * NSL + slot) * kC + c] = v;
+  }
+}
+
+// The value pass's cotangent scale from the per-atom ones: gsc[i] = 2^(E_i - 141)
+// for the biased exponent E_i of max |G_i|, so the largest gsc marks the
+// largest max |G_i| = 1.f 2^(E - 127), and 2^-14 / max gsc = 2^(127 - E)
+// brings it into [1, 2).  One workgroup; every value involved is a power of
+// two, so the result is exact.
+__global__ void __launch_bounds__(1024) k_grad_norm(const float* __restrict__ gsc, int64_t n, float* __restrict__ gnorm) {
+  __shared__ float red[16];
+  float mx = 0.0f;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) mx = fmaxf(mx, gsc[i]);
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < 16; ++w) mx = fmaxf(mx, red[w]);
+    *gnorm = 0x1p-14f / mx;
   }
 }
 
@@ -1513,6 +1540,9 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
                                                reinterpret_cast<f16x8*>(wb + W.gpk),
                                                reinterpret_cast<float*>(wb + W.gsc));
     E2A_LAUNCH_CHECK();
+    k_grad_norm<<<1, 1024, 0, st>>>(reinterpret_cast<const float*>(wb + W.gsc), a->n_atoms,
+                                    reinterpret_cast<float*>(wb + W.gnorm));
+    E2A_LAUNCH_CHECK();
   }
   float* delta = reinterpret_cast<float*>(wb + W.delta);
   e = launch_bwd_delta(pl, delta, st);
@@ -1526,6 +1556,7 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   // query pass
   p.gpk = reinterpret_cast<const f16x8*>(wb + W.gpk);
   p.gsc = reinterpret_cast<const float*>(wb + W.gsc);
+  p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
   p.delta = delta;
   p.ds = pl.ds;
   e = launch_mode<L, kBwdQ>(p, st);

@@ -170,3 +170,33 @@ def test_bwd_mfma_deterministic(B):
     g1 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
     g2 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
     assert np.array_equal(g1, g2)
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 20])
+def test_bwd_mfma_cotangent_power_of_two(B, scale):
+    """The matrix-core passes normalise the cotangent by powers of two (per
+    atom for the query pass's fp16 copy, by its global maximum in the value
+    pass), so every rounding sees the same significands and a cotangent
+    scaled by 2^-20 or 2^20 gives exactly the scaled gradient."""
+    log(f"[bwd] mfma cotangent x {scale:g}")
+    w = make_config("tiny", L=4, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w)
+    g1 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    d["G"] = d["G"] * scale
+    g2 = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    assert np.array_equal(g2, g1 * np.float32(scale))
+
+
+@pytest.mark.parametrize("scale", [1e-7, 1e6])
+def test_bwd_mfma_cotangent_magnitude(B, scale):
+    """Cotangents whose fp16 images would be subnormal (1e-7) or overflow
+    (1e6) without the normalisation keep the bf16 bound against the oracle."""
+    log(f"[bwd] mfma cotangent magnitude {scale:g}")
+    w = make_config("tiny", L=3, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w)
+    Gs = (G.astype(np.float64) * scale).astype(np.float32)
+    d["G"] = torch.from_numpy(Gs).cuda()
+    got = gpu_grad(B, w, d, fwd_variant="mfma", bwd_variant="mfma")
+    err = rel_l2(got, oracle_grad(w, rp, col, Gs))
+    log(f"[bwd] mfma cotangent x {scale:g}: rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL_BF16
