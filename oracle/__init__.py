@@ -8,9 +8,11 @@ from .e2a_oracle import (  # noqa: F401
     attention,
     attention_backward,
     attention_online,
+    attention_weight_backward,
     convolution,
     edge_messages,
     edge_messages_vjp,
+    edge_messages_weight_vjp,
     edge_rotation,
     min_image,
     neighbor_list,

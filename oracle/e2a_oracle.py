@@ -566,6 +566,130 @@ def attention_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H,
     return dfeat[dest]
 
 
+def edge_messages_weight_vjp(rvec, h_src, g, w_rad, w_so2, L, C, cutoff, blocks=None):
+    """Gradients of sum_e <edge_messages(r_e, h_e), g_e> with respect to the
+    radial weights and the per-m SO(2) blocks, summed over the edges.  With
+    the message v = D^T (rho * y), y = SO2(x), x = D h, rho = e(r) W_rad
+    (the steps of ``edge_messages``), the chain rule taken step by step:
+
+      dyhat^l = D^l g^l                          (edge-frame cotangent of rho*y)
+      drho[l, c] = sum_m y^l[m][c] dyhat^l[m][c],   dW_rad[k, l, c] = sum_e e_k drho
+      dy = rho * dyhat
+      m = 0: dW0 = X0^T dY0
+      m > 0: dW1 = Xp^T dYp + Xm^T dYm,   dW2 = -Xm^T dYp + Xp^T dYm
+
+    (from y_+ = x_+ W1 - x_- W2 and y_- = x_+ W2 + x_- W1).  Returns
+    (dw_rad [n_rbf, L+1, C], dw_so2 flat in the layout of w_so2), fp64."""
+    rvec = np.asarray(rvec, dtype=np.float64)
+    h = np.asarray(h_src, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    r = np.linalg.norm(rvec, axis=1)
+    R = edge_rotation(rvec / r[:, None])
+    if blocks is None:
+        blocks = so2_blocks(w_so2, L, C)
+    D = [wigner_d(l, R) for l in range(L + 1)]
+    x = [np.einsum("emn,enc->emc", D[l], h[:, l * l:(l + 1) ** 2, :]) for l in range(L + 1)]
+    e = radial_basis(r, cutoff, np.asarray(w_rad).shape[0])
+    rho = np.einsum("ek,klc->elc", e, np.asarray(w_rad, dtype=np.float64))
+    dyhat = [np.einsum("enm,emc->enc", D[l], g[:, l * l:(l + 1) ** 2, :]) for l in range(L + 1)]
+    # y = SO2(x), as in edge_messages
+    y = [np.zeros_like(x[l]) for l in range(L + 1)]
+    X0 = np.concatenate([x[l][:, l, :] for l in range(L + 1)], axis=1)
+    Y0 = X0 @ blocks[0]
+    for l in range(L + 1):
+        y[l][:, l, :] = Y0[:, l * C:(l + 1) * C]
+    Xp_, Xm_ = {}, {}
+    for m in range(1, L + 1):
+        W1, W2 = blocks[m]
+        Xp = np.concatenate([x[l][:, l + m, :] for l in range(m, L + 1)], axis=1)
+        Xm = np.concatenate([x[l][:, l - m, :] for l in range(m, L + 1)], axis=1)
+        Xp_[m], Xm_[m] = Xp, Xm
+        Yp = Xp @ W1 - Xm @ W2
+        Ym = Xp @ W2 + Xm @ W1
+        for l in range(m, L + 1):
+            s = (l - m) * C
+            y[l][:, l + m, :] = Yp[:, s:s + C]
+            y[l][:, l - m, :] = Ym[:, s:s + C]
+    # radial weights
+    drho = np.stack([np.sum(y[l] * dyhat[l], axis=1) for l in range(L + 1)], axis=1)   # [E, L+1, C]
+    dw_rad = np.einsum("ek,elc->klc", e, drho)
+    # SO(2) blocks
+    dy = [rho[:, l, None, :] * dyhat[l] for l in range(L + 1)]
+    parts = []
+    dY0 = np.concatenate([dy[l][:, l, :] for l in range(L + 1)], axis=1)
+    parts.append((X0.T @ dY0).ravel())
+    for m in range(1, L + 1):
+        dYp = np.concatenate([dy[l][:, l + m, :] for l in range(m, L + 1)], axis=1)
+        dYm = np.concatenate([dy[l][:, l - m, :] for l in range(m, L + 1)], axis=1)
+        Xp, Xm = Xp_[m], Xm_[m]
+        parts.append((Xp.T @ dYp + Xm.T @ dYm).ravel())
+        parts.append((-Xm.T @ dYp + Xp.T @ dYm).ravel())
+    return dw_rad, np.concatenate(parts)
+
+
+def attention_weight_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, grad_out,
+                              box=None, chunk_edges=4096):
+    """Gradients of the layer with respect to its weights for a cotangent
+    grad_out = dL/do (what training the layer needs besides dL/dh; technical
+    summary section 2.2 recomputes per-edge quantities from the per-destination
+    softmax statistics in the backward).  Chain rule through ``attention``,
+    with ds, dq and dk as in ``attention_backward``:
+
+      dW_q = sum_i h_{i,0}^T dq_i,   dW_k = sum_j h_{j,0}^T dk_j   (q = h_0 W_q, k = h_0 W_k)
+      dW_rad, dW_so2 = sum over edges (i, j) of edge_messages_weight_vjp(r_ij, h_j, alpha_ij G_i).
+
+    Returns a dict with w_q [C, C], w_k [C, C], w_rad [n_rbf, L+1, C] and
+    w_so2 (flat, the layout of w_so2), fp64."""
+    pos = np.asarray(pos, dtype=np.float64)
+    row_ptr = np.asarray(row_ptr, dtype=np.int64)
+    col = np.asarray(col, dtype=np.int64)
+    n = pos.shape[0]
+    K = (L + 1) ** 2
+    dh_ = C // H
+    blocks = so2_blocks(w_so2, L, C)
+    feat = np.asarray(feat, dtype=np.float64)
+    G = np.asarray(grad_out, dtype=np.float64)
+    q, k = qk_projection(feat, w_q, w_k)
+    head_of_c = np.arange(C) // dh_
+    cen = np.nonzero(np.diff(row_ptr) > 0)[0]
+    dq = np.zeros((n, C))
+    dk = np.zeros((n, C))
+    dw_rad = np.zeros(np.asarray(w_rad).shape)
+    dw_so2 = np.zeros(np.asarray(w_so2).size)
+    deg = row_ptr[cen + 1] - row_ptr[cen]
+    t = 0
+    while t < cen.size:
+        u = t
+        tot = 0
+        while u < cen.size and (u == t or tot + deg[u] <= chunk_edges):
+            tot += deg[u]
+            u += 1
+        ci = cen[t:u]
+        lens = deg[t:u]
+        starts = np.concatenate([[0], np.cumsum(lens)[:-1]])
+        e_idx = np.concatenate([np.arange(row_ptr[i], row_ptr[i + 1]) for i in ci])
+        i_of_e = np.repeat(ci, lens)
+        j_of_e = col[e_idx]
+        rvec = min_image(pos[j_of_e] - pos[i_of_e], box)
+        v = edge_messages(rvec, feat[j_of_e], w_rad, w_so2, L, C, cutoff, blocks=blocks)
+        s = (q[i_of_e] * k[j_of_e]).reshape(-1, H, dh_).sum(axis=2) / math.sqrt(dh_)
+        alpha, _ = segment_softmax(s, starts, lens)
+        o = np.add.reduceat(alpha[:, head_of_c][:, None, :] * v, starts, axis=0)
+        Gi = G[i_of_e]
+        dalpha = (Gi * v).reshape(-1, K, H, dh_).sum(axis=(1, 3))
+        delta = (G[ci] * o).reshape(-1, K, H, dh_).sum(axis=(1, 3))
+        ds = alpha * (dalpha - np.repeat(delta, lens, axis=0))
+        dq[ci] += np.add.reduceat(np.repeat(ds, dh_, axis=1) * k[j_of_e], starts, axis=0) / math.sqrt(dh_)
+        np.add.at(dk, j_of_e, np.repeat(ds, dh_, axis=1) * q[i_of_e] / math.sqrt(dh_))
+        dv = alpha[:, head_of_c][:, None, :] * Gi
+        gr, gs = edge_messages_weight_vjp(rvec, feat[j_of_e], dv, w_rad, w_so2, L, C, cutoff, blocks=blocks)
+        dw_rad += gr
+        dw_so2 += gs
+        t = u
+    h0 = feat[:, 0, :]
+    return {"w_q": h0.T @ dq, "w_k": h0.T @ dk, "w_rad": dw_rad, "w_so2": dw_so2}
+
+
 def attention_online(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box=None,
                      dest=None, block=5):
     """Same layer with the streaming reduction of technical summary section 2.2

@@ -577,6 +577,81 @@ def test_p14_feature_gradient_subset_equals_full(tiny):
     assert rel(O.attention_backward(*args, dest=dest), full[dest]) <= 1e-13
 
 
+# ---------------------------------------------------------------- P15 -------
+@pytest.mark.parametrize("L,C", [(1, 4), (3, 5), (4, 3)])
+def test_p15_weight_vjp_adjoint_identities(L, C):
+    """The message is linear in W_so2 for fixed W_rad and linear in W_rad for
+    fixed W_so2, so for any direction U the weight adjoints must satisfy
+    <edge_messages(W_rad, U), g> = <dW_so2, U> and
+    <edge_messages(U, W_so2), g> = <dW_rad, U> exactly (up to rounding)."""
+    rng = np.random.default_rng(150 + L)
+    E = 9
+    rvec = rng.standard_normal((E, 3)) * 2.0
+    h = rng.standard_normal((E, (L + 1) ** 2, C))
+    g = rng.standard_normal((E, (L + 1) ** 2, C))
+    w_rad = rng.standard_normal((8, L + 1, C))
+    w_so2 = rng.standard_normal(_so2_count(L, C))
+    dw_rad, dw_so2 = O.edge_messages_weight_vjp(rvec, h, g, w_rad, w_so2, L, C, 5.0)
+    assert dw_rad.shape == w_rad.shape and dw_so2.shape == w_so2.shape
+    u_so2 = rng.standard_normal(w_so2.shape)
+    a = np.sum(O.edge_messages(rvec, h, w_rad, u_so2, L, C, 5.0) * g)
+    assert abs(a - np.sum(dw_so2 * u_so2)) <= 1e-12 * max(abs(a), 1.0)
+    u_rad = rng.standard_normal(w_rad.shape)
+    b = np.sum(O.edge_messages(rvec, h, u_rad, w_so2, L, C, 5.0) * g)
+    assert abs(b - np.sum(dw_rad * u_rad)) <= 1e-12 * max(abs(b), 1.0)
+
+
+@pytest.mark.parametrize("case", ["tiny_L1_H2", "periodic_L2_H2"])
+def test_p15_weight_gradient_finite_differences(case):
+    """dL/dW for W_q, W_k, W_rad and W_so2 from attention_weight_backward
+    against fourth-order central differences of L(W) = <G, attention(W)>
+    along a random direction per weight (fp64, eps = 2e-4; W_q and W_k reach
+    the loss through the softmax, W_rad and W_so2 linearly)."""
+    if case == "tiny_L1_H2":
+        w = make_config("tiny", C=16, H=2)
+    else:
+        w = _small_periodic(2, 8, 2)
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    rng = np.random.default_rng(1515)
+    f = w.as_f32("feat").astype(np.float64)
+    W = {"w_q": 3.0 * w.as_f32("w_q").astype(np.float64), "w_k": 3.0 * w.as_f32("w_k").astype(np.float64),
+         "w_rad": w.as_f32("w_rad").astype(np.float64), "w_so2": w.as_f32("w_so2").astype(np.float64)}
+    G = rng.standard_normal(f.shape)
+
+    def loss(WW):
+        o, _ = O.attention(w.pos, rp, col, f, WW["w_q"], WW["w_k"], WW["w_rad"], WW["w_so2"], w.L, w.C, w.H,
+                           w.cutoff, box=w.box)
+        return float(np.sum(G * o))
+
+    grads = O.attention_weight_backward(w.pos, rp, col, f, W["w_q"], W["w_k"], W["w_rad"], W["w_so2"], w.L, w.C,
+                                        w.H, w.cutoff, G, box=w.box)
+    eps = 2e-4
+    for name in ("w_q", "w_k", "w_rad", "w_so2"):
+        assert grads[name].shape == W[name].shape
+        u = rng.standard_normal(W[name].shape)
+
+        def at(t):
+            WW = dict(W)
+            WW[name] = W[name] + t * u
+            return loss(WW)
+
+        fd = (-at(2 * eps) + 8 * at(eps) - 8 * at(-eps) + at(-2 * eps)) / (12 * eps)
+        an = float(np.sum(grads[name] * u))
+        assert abs(fd - an) <= 1e-8 * max(abs(an), 1e-3), (name, fd, an)
+
+
+def test_p15_weight_gradient_chunking_invariant(tiny):
+    """The weight gradients do not depend on how the edges are grouped."""
+    w, rp, col = tiny
+    G = np.random.default_rng(1516).standard_normal((w.n_atoms, (w.L + 1) ** 2, w.C))
+    args = (w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"), w.as_f32("w_rad"),
+            w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G)
+    a = O.attention_weight_backward(*args)
+    b = O.attention_weight_backward(*args, chunk_edges=7)
+    for name in a:
+        assert rel(a[name], b[name]) <= 1e-13, name
+
+
 # ------------------------------------------------------------ radial basis --
 def test_radial_basis_definition_points():
     rc = 5.0
