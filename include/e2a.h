@@ -241,6 +241,49 @@ size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L
  */
 e2a_status e2a_attention_bwd(const e2a_attn_args* args, const float* grad_out, float* grad_feat, void* stream);
 
+/* Workspace bytes e2a_attention_bwd_weights needs for these sizes (the same
+ * for fp32 and bf16 storage); 0 for invalid sizes. */
+size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H);
+
+/*
+ * Gradients of e2a_attention_fwd with respect to its weights, and optionally
+ * its node features, for a cotangent grad_out = dL/do: what training the
+ * layer needs (technical summary section 2.2; the message steps of section
+ * 2.1).  With ds_ij, dq_i, dk_j as in e2a_attention_bwd, the edge cotangent
+ * alpha_ij G_i, x_ij = D_ij h_j, y = SO2(x), dyhat = D_ij (alpha_ij G_i),
+ * rho_ij[l][c] = sum_k e_k(r_ij) W_rad[k][l][c] and dy = rho_ij dyhat:
+ *   dW_q = sum_i h_{i,0}^T dq_i,   dW_k = sum_j h_{j,0}^T dk_j,
+ *   dW_rad[k][l][c] = sum_ij e_k(r_ij) sum_m y[l,m][c] dyhat[l,m][c],
+ *   per m: dW0 = sum X0^T dY0,  dW1 = sum Xp^T dYp + Xm^T dYm,
+ *          dW2 = sum Xp^T dYm - Xm^T dYp
+ * (X0, Xp, Xm the rows m = 0, +m, -m of x laid out as in w_so2's blocks).
+ * Gradients with respect to positions are not computed.
+ *
+ *   args        as for e2a_attention_bwd (out and out_lse of the forward are
+ *               required); workspace / workspace_bytes as
+ *               e2a_attention_bwd_weights_workspace_bytes gives.
+ *   grad_out    device f32 [n_atoms, (L+1)^2, C].
+ *   grad_feat   NULL, or device f32 [n_atoms, (L+1)^2, C]: dL/dh as
+ *               e2a_attention_bwd computes it.
+ *   grad_w_q, grad_w_k   NULL or device f32 [C, C] (layout of w_q, w_k).
+ *   grad_w_rad  NULL or device f32 [8, L+1, C].
+ *   grad_w_so2  NULL or device f32 [e2a_so2_param_count(L, C)] (layout of w_so2).
+ * Every output that is set is overwritten; at least one must be set.
+ *
+ * dL/dh and ds come from the same kernels as e2a_attention_bwd (variant as
+ * there); the query pass runs only when grad_feat, grad_w_q or grad_w_k is
+ * set.  W_rad and W_so2 sum over all edges into matrices too large for a
+ * workgroup, so the workspace holds per-edge tensors for one batch of at
+ * most 65536 edges at a time: rotated features and cotangents (storage
+ * precision), SO2(x) in fp32.  The GEMMs run on the matrix cores for bf16
+ * storage (bf16 operands, fp32 sums) and in fp32 otherwise; all sums run in
+ * a fixed order, so results are bit-reproducible.  Asynchronous.  Errors as
+ * e2a_attention_bwd, plus E2A_ERR_INVALID_ARG when no output is set.
+ */
+e2a_status e2a_attention_bwd_weights(const e2a_attn_args* args, const float* grad_out, float* grad_feat,
+                                     float* grad_w_q, float* grad_w_k, float* grad_w_rad, float* grad_w_so2,
+                                     void* stream);
+
 #ifdef __cplusplus
 }
 #endif

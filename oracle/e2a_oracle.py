@@ -628,7 +628,7 @@ def edge_messages_weight_vjp(rvec, h_src, g, w_rad, w_so2, L, C, cutoff, blocks=
 
 
 def attention_weight_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, grad_out,
-                              box=None, chunk_edges=4096):
+                              box=None, chunk_edges=4096, centres=None):
     """Gradients of the layer with respect to its weights for a cotangent
     grad_out = dL/do (what training the layer needs besides dL/dh; technical
     summary section 2.2 recomputes per-edge quantities from the per-destination
@@ -637,6 +637,11 @@ def attention_weight_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L
 
       dW_q = sum_i h_{i,0}^T dq_i,   dW_k = sum_j h_{j,0}^T dk_j   (q = h_0 W_q, k = h_0 W_k)
       dW_rad, dW_so2 = sum over edges (i, j) of edge_messages_weight_vjp(r_ij, h_j, alpha_ij G_i).
+
+    ``centres`` (default all) limits the sums to the edges of those
+    destinations: every term of an edge (i, j) carries G_i (through
+    alpha_ij G_i or ds_ij), so when G vanishes outside ``centres`` the result
+    is the full gradient.
 
     Returns a dict with w_q [C, C], w_k [C, C], w_rad [n_rbf, L+1, C] and
     w_so2 (flat, the layout of w_so2), fp64."""
@@ -652,6 +657,8 @@ def attention_weight_backward(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L
     q, k = qk_projection(feat, w_q, w_k)
     head_of_c = np.arange(C) // dh_
     cen = np.nonzero(np.diff(row_ptr) > 0)[0]
+    if centres is not None:
+        cen = np.intersect1d(cen, np.asarray(centres, dtype=np.int64))
     dq = np.zeros((n, C))
     dk = np.zeros((n, C))
     dw_rad = np.zeros(np.asarray(w_rad).shape)

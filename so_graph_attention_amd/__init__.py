@@ -9,6 +9,8 @@ _EXPORTS = (
     "E2AError",
     "e2a_attention_bwd",
     "e2a_attention_bwd_workspace_bytes",
+    "e2a_attention_bwd_weights",
+    "e2a_attention_bwd_weights_workspace_bytes",
     "e2a_attention_fwd",
     "e2a_attention_workspace_bytes",
     "e2a_build_neighbors",

@@ -40,6 +40,8 @@ struct BwdParams {
   float* ds;            // [E, H]
   float* dq;            // [N, C]
   float* grad_feat;     // [N, K, C]
+  float* wdq;           // optional outputs of k_bwd_qk: dq, dk [N, C]
+  float* wdk;
   float box[3];
   int periodic;
   float cutoff;
@@ -395,8 +397,10 @@ __global__ void k_wqk_transpose(const T* __restrict__ w_q, const T* __restrict__
 // The l = 0 terms of the gradient after the matrix-core passes, one
 // workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj' k_j' / sqrt(C/H),
 // dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found in the ascending
-// row of i, once per edge, in tiles of blockDim edges), and
-// grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T (wt = W_q^T, W_k^T).
+// row of i, once per edge, in tiles of blockDim edges), and, when grad_feat
+// is set, grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T (wt = W_q^T, W_k^T);
+// dq_j and dk_j themselves go to wdq, wdk when those are set (the weight
+// gradients' inputs).
 __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const float* __restrict__ wt, int K) {
   const int C = p.C, H = p.H, dh = C / H;
   extern __shared__ float smem[];
@@ -437,6 +441,12 @@ __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const float* __rest
     __syncthreads();
   }
   __syncthreads();
+  if (p.wdq)
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+      p.wdq[j * C + c] = dq[c] * inv;
+      p.wdk[j * C + c] = dk[c] * inv;
+    }
+  if (!p.grad_feat) return;
   const float* wqt = wt;
   const float* wkt = wt + (size_t)C * C;
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
@@ -460,6 +470,8 @@ BwdParams bwd_params(const BwdPlan& pl) {
   p.ds = pl.ds;
   p.dq = pl.dq;
   p.grad_feat = pl.grad_feat;
+  p.wdq = pl.wdq;
+  p.wdk = pl.wdk;
   for (int d = 0; d < 3; ++d) p.box[d] = pl.box[d];
   p.periodic = pl.periodic;
   p.cutoff = a->cutoff;
@@ -478,10 +490,18 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_query<L, T>), dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const T*>(a->feat),
                      static_cast<const T*>(a->w_rad), static_cast<const T*>(a->w_so2));
   E2A_LAUNCH_CHECK();
-  hipLaunchKernelGGL((k_bwd_value<L, T>), dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const T*>(a->w_q),
-                     static_cast<const T*>(a->w_k), static_cast<const T*>(a->w_rad),
-                     static_cast<const T*>(a->w_so2));
-  E2A_LAUNCH_CHECK();
+  if (pl.grad_feat) {
+    hipLaunchKernelGGL((k_bwd_value<L, T>), dim3(a->n_atoms), dim3(256), smem, s, p, static_cast<const T*>(a->w_q),
+                       static_cast<const T*>(a->w_k), static_cast<const T*>(a->w_rad),
+                       static_cast<const T*>(a->w_so2));
+    E2A_LAUNCH_CHECK();
+  }
+  if (pl.wdq) {
+    // dq, dk for the weight gradients (the value pass adds its own l = 0 terms)
+    BwdPlan qk = pl;
+    qk.grad_feat = nullptr;
+    return launch_bwd_qk(qk, s);
+  }
   return E2A_OK;
 }
 

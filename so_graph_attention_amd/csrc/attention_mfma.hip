@@ -1561,6 +1561,7 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.ds = pl.ds;
   e = launch_mode<L, kBwdQ>(p, st);
   if (e != E2A_OK) return e;
+  if (!pl.grad_feat) return pl.wdq ? launch_bwd_qk(pl, st) : E2A_OK;
   // value pass: the cotangent in bf16 takes the features' place
   p.feat = reinterpret_cast<const uint16_t*>(wb + W.gbf);
   p.wpk = reinterpret_cast<const bf16x8*>(wb + W.wt);

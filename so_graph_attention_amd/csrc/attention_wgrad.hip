@@ -1,0 +1,833 @@
+// Weight gradients of the fused layer: dL/dW_q, dL/dW_k, dL/dW_rad and the
+// per-m SO(2) blocks dL/dW_so2, for a cotangent G = dL/do.
+//
+// arXiv 2601.16622, technical summary section 2.1 (the EAAS message: rotate
+// in, per-m SO(2) mix, radial scale, rotate out) and section 2.2 (attention
+// weights from invariant logits; the backward recomputes per-edge quantities
+// from the per-destination softmax statistics).  With the edge cotangent
+// alpha_ij G_i of the message v_ij = D^T (rho * SO2(D h_j)):
+//   dyhat = D (alpha G_i)                          edge-frame cotangent of rho * y
+//   drho[l][c] = sum_m y[l,m][c] dyhat[l,m][c]     y = SO2(x), x = D h_j
+//   dW_rad[k][l][c] = sum over edges of e_k(r) drho[l][c]
+//   dy = rho * dyhat
+//   dW0 = X0^T dY0,  dW1 = Xp^T dYp + Xm^T dYm,  dW2 = Xp^T dYm - Xm^T dYp
+//   dW_q = sum_i h_{i,0}^T dq_i,  dW_k = sum_j h_{j,0}^T dk_j.
+// Each of these is a sum over all edges (or atoms) into a matrix far larger
+// than a workgroup can hold, so unlike the forward this path keeps per-edge
+// tensors: for a batch of edges it writes x and dyhat in the row layout of
+// the per-m GEMMs (block 0: one row per edge, [B][(L+1)C]; block m > 0: the
+// +m rows [B][(L+1-m)C], then the -m rows), forms Y = SO2(X) and the weight
+// gradients as GEMMs, and moves on to the next batch.  The GEMMs sum in a
+// fixed order (split-K partials reduced in order), so results are
+// bit-reproducible.
+#include <type_traits>
+
+#include "e2a_geometry.hpp"
+#include "e2a_internal.hpp"
+
+namespace e2a {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int64_t kWgBatch = 65536;   // edges per batch
+constexpr int kEB = 16;               // edges per gather workgroup
+constexpr int64_t kRhoPer = 32;       // edges per k_wg_rho range
+
+template <typename T>
+__device__ __forceinline__ void store_as(T* p, int64_t i, float v);
+template <>
+__device__ __forceinline__ void store_as<float>(float* p, int64_t i, float v) {
+  p[i] = v;
+}
+template <>
+__device__ __forceinline__ void store_as<uint16_t>(uint16_t* p, int64_t i, float v) {
+  p[i] = f32_to_bf16_rne(v);
+}
+
+__device__ __forceinline__ int degree_of(int comp) {
+  int l = 0;
+  while ((l + 1) * (l + 1) <= comp) ++l;
+  return l;
+}
+
+// Element offsets of the per-m matrices in one batch tensor.
+struct BatchLayout {
+  int64_t B;         // rows per matrix (edges per batch)
+  int64_t moff[5];   // block m: m = 0 one [B][K_0]; m > 0 [B][K_m] (+m rows) then [B][K_m] (-m rows)
+  int64_t total;
+};
+
+BatchLayout batch_layout(int64_t B, int L, int C) {
+  BatchLayout b{};
+  b.B = B;
+  int64_t o = 0;
+  for (int m = 0; m <= L; ++m) {
+    b.moff[m] = o;
+    o += (m == 0 ? 1 : 2) * B * (int64_t)(L + 1 - m) * C;
+  }
+  b.total = o;
+  return b;
+}
+
+// Place of row (l, m) channel c of batch edge b in a batch tensor.
+__device__ __forceinline__ int64_t batch_index(const BatchLayout& bl, int L, int C, int64_t b, int l, int m, int c) {
+  const int am = m < 0 ? -m : m;
+  const int64_t km = (int64_t)(L + 1 - am) * C;
+  return bl.moff[am] + (m < 0 ? bl.B * km : 0) + b * km + (int64_t)(l - am) * C + c;
+}
+
+__global__ void k_edge_rows(const int64_t* __restrict__ row_ptr, int64_t n, int32_t* __restrict__ src) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) src[e] = static_cast<int32_t>(i);
+}
+
+// Wt[n][k] = W[k][n] for one km x km block (the Y products read both
+// operands along k).
+template <typename T>
+__global__ void k_transpose_block(const T* __restrict__ w, int64_t km, T* __restrict__ wt) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= km * km) return;
+  const int64_t k = t / km, n = t - k * km;
+  wt[n * km + k] = w[t];
+}
+
+__global__ void k_zero(float* __restrict__ p, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+struct GatherParams {
+  const float* pos;
+  const int32_t* col;
+  const int32_t* src;
+  const float* q;
+  const float* k;
+  const float* lse;
+  const float* grad;
+  float box[3];
+  int periodic;
+  float cutoff;
+  int C, H;
+  int64_t e0, nb;   // the batch: edges e0 .. e0 + nb - 1 of the neighbour list
+  BatchLayout bl;
+  float* rbf;       // [B][8]
+};
+
+// Degree l of the gather: one (edge, channel) per work item reads the
+// degree's 2l + 1 feature and cotangent entries once and writes all 2l + 1
+// rows of x and dyhat.
+template <int L, int l, typename T>
+__device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __restrict__ feat, T* __restrict__ X,
+                                              T* __restrict__ GT, const float* D, const float* al, const int* ii,
+                                              const int* jj, int64_t b0, int tid) {
+  constexpr int K = (L + 1) * (L + 1);
+  constexpr int WS = wig_size(L);
+  constexpr int w = 2 * l + 1;
+  const int C = p.C, H = p.H, dh = C / H;
+  for (int t = tid; t < kEB * C; t += blockDim.x) {
+    const int s = t / C, c = t - s * C;
+    if (ii[s] < 0) continue;
+    const T* hj = feat + ((int64_t)jj[s] * K + l * l) * C + c;
+    const float* gi = p.grad + ((int64_t)ii[s] * K + l * l) * C + c;
+    float hv[w], gv[w];
+#pragma unroll
+    for (int n = 0; n < w; ++n) {
+      hv[n] = load_as_f32(hj, (size_t)n * C);
+      gv[n] = gi[(int64_t)n * C];
+    }
+    const float a = al[s * H + c / dh];
+    const float* Dl = D + s * WS + wig_off(l);
+#pragma unroll
+    for (int mi = 0; mi < w; ++mi) {
+      float x = 0.0f, g = 0.0f;
+#pragma unroll
+      for (int n = 0; n < w; ++n) {
+        x += Dl[mi * w + n] * hv[n];
+        g += Dl[mi * w + n] * gv[n];
+      }
+      const int64_t idx = batch_index(p.bl, L, C, b0 + s, l, mi - l, c);
+      store_as(X, idx, x);
+      store_as(GT, idx, g * a);
+    }
+  }
+  if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, ii, jj, b0, tid);
+}
+
+// x = D h_j and dyhat = D (alpha G_i) for kEB edges of the batch: the edges'
+// frames, Wigner blocks, radial bases and attention weights first (one
+// thread per edge), then the degrees one after another.
+template <int L, typename T>
+__global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __restrict__ feat, T* __restrict__ X,
+                                                   T* __restrict__ GT) {
+  constexpr int K = (L + 1) * (L + 1);
+  constexpr int WS = wig_size(L);
+  extern __shared__ float sm[];
+  float* D = sm;                       // [kEB][WS]
+  float* al = D + kEB * WS;            // [kEB][H]
+  __shared__ int ii[kEB], jj[kEB];
+  const int C = p.C, H = p.H, dh = C / H;
+  const int64_t b0 = (int64_t)blockIdx.x * kEB;
+  const int tid = threadIdx.x;
+  if (tid < kEB) {
+    const int64_t b = b0 + tid;
+    ii[tid] = -1;
+    if (b < p.nb) {
+      const int64_t e = p.e0 + b;
+      const int i = p.src[e], j = p.col[e];
+      ii[tid] = i;
+      jj[tid] = j;
+      float r3[3];
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * (int64_t)i + d];
+        if (p.periodic) {
+          if (dx > 0.5f * p.box[d]) dx -= p.box[d];
+          else if (dx < -0.5f * p.box[d]) dx += p.box[d];
+        }
+        r3[d] = dx;
+      }
+      const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
+      const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+      float R[3][3];
+      edge_rotation(u, R);
+      wigner_blocks<L>(R, D + tid * WS);
+      float e8[8];
+      radial_basis8(r, p.cutoff, e8);
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) p.rbf[b * 8 + kk] = e8[kk];
+      const float inv = 1.0f / sqrtf(static_cast<float>(dh));
+      for (int h = 0; h < H; ++h) {
+        float sv = 0.0f;
+        for (int d = 0; d < dh; ++d) sv += p.q[(int64_t)i * C + h * dh + d] * p.k[(int64_t)j * C + h * dh + d];
+        al[tid * H + h] = expf(sv * inv - p.lse[(int64_t)i * H + h]);
+      }
+    }
+  }
+  __syncthreads();
+  gather_degree<L, 0, T>(p, feat, X, GT, D, al, ii, jj, b0, tid);
+}
+
+// dy = rho dyhat in place and, when Y is set, drho[b][l][c] = sum_m
+// y[l,m][c] dyhat[l,m][c] summed into this range's part of dW_rad:
+// part[z][k][(l, c)] (+)= sum over the range's edges b of rbf[b][k] drho[b][l][c]
+// (added to what the slot holds from earlier batches when acc_parts is set).
+// One thread per (degree, channel) and range of edges (consecutive threads
+// take consecutive channels, so the row reads coalesce).
+template <int L, typename T>
+__global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
+                         const T* __restrict__ w_rad, const float* __restrict__ Y, T* __restrict__ GT,
+                         float* __restrict__ part, bool acc_parts) {
+  const int lc = blockIdx.x * blockDim.x + threadIdx.x;
+  const int z = blockIdx.y;
+  if (lc >= (L + 1) * C) return;
+  const int l = lc / C, c = lc - l * C;
+  float wr[8], acc[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    wr[kk] = load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
+    acc[kk] = 0.0f;
+  }
+  const int64_t b1 = (z + 1) * per < nb ? (z + 1) * per : nb;
+  for (int64_t b = z * per; b < b1; ++b) {
+    float rho = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rho += rbf[b * 8 + kk] * wr[kk];
+    float dr = 0.0f;
+    for (int m = -l; m <= l; ++m) {
+      const int64_t idx = batch_index(bl, L, C, b, l, m, c);
+      const float g = load_as_f32(GT, (size_t)idx);
+      if (Y) dr += Y[idx] * g;
+      store_as(GT, idx, rho * g);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) acc[kk] += rbf[b * 8 + kk] * dr;
+  }
+  if (Y)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      float* pp = part + ((int64_t)z * 8 + kk) * (L + 1) * C + lc;
+      *pp = acc_parts ? *pp + acc[kk] : acc[kk];
+    }
+}
+
+// ---------------------------------------------------------------- GEMMs ----
+// C[m * ldc + n] += alpha * sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak],
+// B(k, n) = B[k sbk + n sbn].  One workgroup per output tile and k-range;
+// with several k-ranges each writes alpha times its partial tile (or adds it
+// to what its slot holds, so that several products and several edge batches
+// can share one set of partials) and a second kernel adds the partials in
+// order.
+struct Gemm {
+  const void* A;
+  int64_t sam, sak;
+  const void* B;
+  int64_t sbk, sbn;
+  int64_t M, N, K;
+  float alpha;
+  float* C;
+  int64_t ldc;
+  float* part;     // [S][M][N] when S > 1
+  int S;
+  int64_t kper;    // k per split, a multiple of 32
+  bool overwrite;  // C = alpha AB instead of C += alpha AB
+  bool part_acc;   // S > 1: add alpha AB to the partials instead of storing it
+};
+
+// bf16 x bf16 on the matrix cores: a 128 x 128 output tile per workgroup,
+// four waves of 64 x 64 (2 x 2 tiles of v_mfma_f32_32x32x16_bf16), 32-deep k
+// slices double-buffered in LDS with k contiguous (the layout the fragments
+// read).  An operand whose contiguous dimension is k is copied in 16-byte
+// vectors; one contiguous along m (or n) is read in 16-byte vectors along m
+// and transposed on its way into LDS; anything else (or a ragged edge) goes
+// element by element.
+constexpr int kTM = 128, kBK = 32, kPad = 8;
+struct GemmSmem {
+  uint16_t a[2][kTM][kBK + kPad];
+  uint16_t b[2][kTM][kBK + kPad];
+};
+
+// One 128 x 32 slice of an operand X(r, k) = X[r sr + k sk] (rows r0 ..
+// r0+127 of m or n, k0 .. k0+31), fetched into registers first and written
+// to LDS ([r - r0][k - k0]) after the current slice's products, so that the
+// global loads' latency overlaps them.  vk / vr: 16-byte vectors along k or
+// along r are allowed; otherwise (and on ragged edges) element by element.
+struct Slice {
+  uint32_t v[2][4];
+};
+
+__device__ __forceinline__ void fetch_slice(const uint16_t* __restrict__ X, int64_t sr, int64_t sk, int64_t r0,
+                                            int64_t R, int64_t k0, int64_t ke, bool vk, bool vr, int tid,
+                                            Slice& f) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int idx = tid + 256 * v;
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (vk || !vr) {
+      // rows idx / 4, k offset 8 (idx % 4)
+      const int r = idx >> 2, kq = (idx & 3) * 8;
+      const int64_t m = r0 + r, k = k0 + kq;
+      if (vk && m < R && k + 8 <= ke) {
+        w = *reinterpret_cast<const u32x4*>(X + m * sr + k);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t e = (m < R && k + q < ke) ? X[m * sr + (k + q) * sk] : 0u;
+          w[q >> 1] |= e << (16 * (q & 1));
+        }
+      }
+    } else {
+      // rows 8 (tid / 16) .. +7 at k = 2 (tid % 16) + v: each thread holds a
+      // pair of neighbouring k for 8 rows, written to LDS as 32-bit words
+      const int kq = 2 * (tid & 15) + v, rq = (tid >> 4) * 8;
+      const int64_t m = r0 + rq, k = k0 + kq;
+      if (k < ke && m + 8 <= R) {
+        w = *reinterpret_cast<const u32x4*>(X + m + k * sk);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t e = (k < ke && m + q < R) ? X[(m + q) + k * sk] : 0u;
+          w[q >> 1] |= e << (16 * (q & 1));
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f.v[v][q] = w[q];
+  }
+}
+
+__device__ __forceinline__ void commit_slice(const Slice& f, bool vr_layout, uint16_t (*dst)[kBK + kPad], int tid) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int v = 0; v < 2; ++v) {
+    const int idx = tid + 256 * v;
+    if (!vr_layout) {
+      const int r = idx >> 2, kq = (idx & 3) * 8;
+      *reinterpret_cast<u32x4*>(&dst[r][kq]) = u32x4{f.v[v][0], f.v[v][1], f.v[v][2], f.v[v][3]};
+    } else if (v == 1) {
+      // v = 0 and 1 hold k = 2 (tid % 16) and that + 1 for rows 8 (tid / 16) ..
+      const int kp = tid & 15, rq = (tid >> 4) * 8;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const uint32_t lo = (f.v[0][q >> 1] >> (16 * (q & 1))) & 0xffffu;
+        const uint32_t hi = (f.v[1][q >> 1] >> (16 * (q & 1))) & 0xffffu;
+        *reinterpret_cast<uint32_t*>(&dst[rq + q][2 * kp]) = lo | (hi << 16);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ bool aligned16(const void* p, int64_t stride) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && stride % 8 == 0;
+}
+
+__global__ void __launch_bounds__(256) k_gemm_mfma(Gemm g) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  const uint16_t* A = static_cast<const uint16_t*>(g.A);
+  const uint16_t* B = static_cast<const uint16_t*>(g.B);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int64_t m0 = (int64_t)blockIdx.y * kTM, n0 = (int64_t)blockIdx.x * kTM;
+  const int64_t kb = (int64_t)blockIdx.z * g.kper;
+  const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
+  // A(m, k) = A[m sam + k sak]; B(k, n) = B[n sbn + k sbk]
+  const bool avk = g.sak == 1 && aligned16(A, g.sam), avr = !avk && g.sam == 1 && aligned16(A, g.sak);
+  const bool bvk = g.sbk == 1 && aligned16(B, g.sbn), bvr = !bvk && g.sbn == 1 && aligned16(B, g.sbk);
+  f32x16 acc[2][2] = {};
+  Slice fa, fb;
+  int buf = 0;
+  if (kb < ke) {
+    fetch_slice(A, g.sam, g.sak, m0, g.M, kb, ke, avk, avr, tid, fa);
+    fetch_slice(B, g.sbn, g.sbk, n0, g.N, kb, ke, bvk, bvr, tid, fb);
+    commit_slice(fa, avr, sm.a[0], tid);
+    commit_slice(fb, bvr, sm.b[0], tid);
+  }
+  __syncthreads();
+  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    const bool more = k0 + kBK < ke;
+    if (more) {
+      fetch_slice(A, g.sam, g.sak, m0, g.M, k0 + kBK, ke, avk, avr, tid, fa);
+      fetch_slice(B, g.sbn, g.sbk, n0, g.N, k0 + kBK, ke, bvk, bvr, tid, fb);
+    }
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 16) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = *reinterpret_cast<const bf16x8*>(&sm.a[buf][wm * 64 + t * 32 + (lane & 31)][ks + 8 * (lane >> 5)]);
+        bfr[t] = *reinterpret_cast<const bf16x8*>(&sm.b[buf][wn * 64 + t * 32 + (lane & 31)][ks + 8 * (lane >> 5)]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      commit_slice(fa, avr, sm.a[buf ^ 1], tid);
+      commit_slice(fb, bvr, sm.b[buf ^ 1], tid);
+    }
+    __syncthreads();
+    buf ^= 1;
+  }
+  // register r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (m < g.M && n < g.N) {
+          const float v = acc[i][j][r];
+          if (g.S > 1) {
+            float* pp = g.part + ((int64_t)blockIdx.z * g.M + m) * g.N + n;
+            *pp = g.part_acc ? *pp + g.alpha * v : g.alpha * v;
+          } else if (g.overwrite) {
+            g.C[m * g.ldc + n] = g.alpha * v;
+          } else {
+            g.C[m * g.ldc + n] += g.alpha * v;
+          }
+        }
+      }
+}
+
+// Any operand types, fp32 on the vector ALUs: 64 x 64 tiles, a 4 x 4 block of
+// outputs per thread, 16-deep k slices in LDS.
+template <typename TA, typename TB>
+__global__ void __launch_bounds__(256) k_gemm_valu(Gemm g) {
+  constexpr int BK = 16;
+  __shared__ float As[BK][64];
+  __shared__ float Bs[BK][64];
+  const TA* A = static_cast<const TA*>(g.A);
+  const TB* B = static_cast<const TB*>(g.B);
+  const int tid = threadIdx.x;
+  const int tm = tid >> 4, tn = tid & 15;
+  const int64_t m0 = (int64_t)blockIdx.y * 64, n0 = (int64_t)blockIdx.x * 64;
+  const int64_t kb = (int64_t)blockIdx.z * g.kper;
+  const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
+  float acc[4][4] = {};
+  for (int64_t k0 = kb; k0 < ke; k0 += BK) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;   // 0 .. 1023 over (k, row)
+      // the contiguous dimension runs across neighbouring threads
+      int kk, r;
+      if (g.sak == 1) { kk = idx & 15; r = idx >> 4; } else { r = idx & 63; kk = idx >> 6; }
+      const int64_t m = m0 + r, k = k0 + kk;
+      As[kk][r] = (m < g.M && k < ke) ? load_as_f32(A, (size_t)(m * g.sam + k * g.sak)) : 0.0f;
+      int kb2, c;
+      if (g.sbk == 1) { kb2 = idx & 15; c = idx >> 4; } else { c = idx & 63; kb2 = idx >> 6; }
+      const int64_t n = n0 + c, k2 = k0 + kb2;
+      Bs[kb2][c] = (n < g.N && k2 < ke) ? load_as_f32(B, (size_t)(k2 * g.sbk + n * g.sbn)) : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = As[kk][tm * 4 + u];
+        b[u] = Bs[kk][tn * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] += a[u] * b[v];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t m = m0 + tm * 4 + u, n = n0 + tn * 4 + v;
+      if (m < g.M && n < g.N) {
+        if (g.S > 1) {
+          float* pp = g.part + ((int64_t)blockIdx.z * g.M + m) * g.N + n;
+          *pp = g.part_acc ? *pp + g.alpha * acc[u][v] : g.alpha * acc[u][v];
+        } else if (g.overwrite) g.C[m * g.ldc + n] = g.alpha * acc[u][v];
+        else g.C[m * g.ldc + n] += g.alpha * acc[u][v];
+      }
+    }
+}
+
+__global__ void k_gemm_reduce(Gemm g) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= g.M * g.N) return;
+  float s = 0.0f;
+  for (int z = 0; z < g.S; ++z) s += g.part[z * g.M * g.N + t];
+  const int64_t m = t / g.N, n = t - m * g.N;
+  if (g.overwrite) g.C[m * g.ldc + n] = s;
+  else g.C[m * g.ldc + n] += s;
+}
+
+constexpr int64_t kTargetGroups = 1024;   // workgroups a GEMM launch aims for
+
+template <typename TA, typename TB>
+constexpr int64_t tile_of() {
+  return std::is_same<TA, uint16_t>::value && std::is_same<TB, uint16_t>::value ? kTM : 64;
+}
+
+// Launches the product kernel for g with g.S k-ranges of g.kper (set by the caller).
+template <typename TA, typename TB>
+e2a_status launch_gemm(const Gemm& g, hipStream_t st) {
+  constexpr int64_t tm = tile_of<TA, TB>();
+  const dim3 grid(static_cast<unsigned>((g.N + tm - 1) / tm), static_cast<unsigned>((g.M + tm - 1) / tm),
+                  static_cast<unsigned>(g.S));
+  if constexpr (tm == kTM)
+    k_gemm_mfma<<<grid, 256, 0, st>>>(g);
+  else
+    k_gemm_valu<TA, TB><<<grid, 256, 0, st>>>(g);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+e2a_status reduce_parts(const Gemm& g, hipStream_t st) {
+  k_gemm_reduce<<<static_cast<unsigned>((g.M * g.N + 255) / 256), 256, 0, st>>>(g);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+// k-ranges for a product with `tiles` output tiles: about kTargetGroups
+// workgroups, at least 256 k per range, at most `smax`.
+int64_t pick_splits(int64_t tiles, int64_t K, int64_t smax) {
+  int64_t S = (kTargetGroups + tiles - 1) / tiles;
+  if (S > (K + 255) / 256) S = (K + 255) / 256;
+  if (S > smax) S = smax;
+  return S < 1 ? 1 : S;
+}
+
+// One product into C, its partials (if any) in part.
+template <typename TA, typename TB>
+e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
+  if (g.M <= 0 || g.N <= 0 || g.K <= 0) return E2A_OK;
+  constexpr int64_t tm = tile_of<TA, TB>();
+  const int64_t tiles = ((g.M + tm - 1) / tm) * ((g.N + tm - 1) / tm);
+  const int64_t S = pick_splits(tiles, g.K, part_floats / (g.M * g.N));
+  g.S = static_cast<int>(S);
+  g.kper = ((g.K + S - 1) / S + 31) / 32 * 32;
+  g.part_acc = false;
+  e2a_status e = launch_gemm<TA, TB>(g, st);
+  if (e != E2A_OK || S == 1) return e;
+  return reduce_parts(g, st);
+}
+
+// The SO(2) weight gradients sum over every batch: each of the 2L + 1
+// matrices keeps kDwSplits(m) partials for the whole call, which every batch's
+// products add to, and one reduction at the end.
+int64_t dw_splits(int L, int C, int m) {
+  const int64_t km = (int64_t)(L + 1 - m) * C;
+  const int64_t t = (km + kTM - 1) / kTM;
+  int64_t S = (512 + t * t - 1) / (t * t);
+  return S > 64 ? 64 : S;
+}
+
+int64_t dw_part_floats(int L, int C) {
+  int64_t f = 0;
+  for (int m = 0; m <= L; ++m) {
+    const int64_t km = (int64_t)(L + 1 - m) * C;
+    f += (m == 0 ? 1 : 2) * dw_splits(L, C, m) * km * km;
+  }
+  return f;
+}
+
+Gemm make_gemm(const void* A, int64_t sam, int64_t sak, const void* B, int64_t sbk, int64_t sbn, int64_t M,
+               int64_t N, int64_t K, float alpha, float* C, int64_t ldc, float* part, bool overwrite = false) {
+  Gemm g{};
+  g.overwrite = overwrite;
+  g.A = A;
+  g.sam = sam;
+  g.sak = sak;
+  g.B = B;
+  g.sbk = sbk;
+  g.sbn = sbn;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.alpha = alpha;
+  g.C = C;
+  g.ldc = ldc;
+  g.part = part;
+  return g;
+}
+
+struct WgWs {
+  size_t src, X, GT, Y, rbf, part, dwpart, rhopart, wt, total;
+  int64_t B, part_floats;
+};
+
+WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C) {
+  WgWs w{};
+  const int64_t B = e < kWgBatch ? (e > 0 ? e : 1) : kWgBatch;
+  const int64_t per = B * (int64_t)(L + 1) * (L + 1) * C;   // elements of one batch tensor
+  const int64_t K0 = (int64_t)(L + 1) * C;
+  int64_t pf = 16 * K0 * K0;
+  if (256 * (int64_t)C * C > pf) pf = 256 * (int64_t)C * C;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.src = take(sizeof(int32_t) * (size_t)(e > 0 ? e : 1));
+  w.X = take(sizeof(float) * (size_t)per);     // sized for fp32 storage
+  w.GT = take(sizeof(float) * (size_t)per);
+  w.Y = take(sizeof(float) * (size_t)per);
+  w.rbf = take(sizeof(float) * 8 * (size_t)B);
+  w.part = take(sizeof(float) * (size_t)pf);
+  w.dwpart = take(sizeof(float) * (size_t)dw_part_floats(L, C));
+  w.rhopart = take(sizeof(float) * (size_t)((B + kRhoPer - 1) / kRhoPer) * 8 * K0);
+  int64_t so2 = 0;
+  for (int m = 0; m <= L; ++m) so2 += (m == 0 ? 1 : 2) * ((int64_t)(L + 1 - m) * C) * ((int64_t)(L + 1 - m) * C);
+  w.wt = take(sizeof(float) * (size_t)so2);   // sized for fp32 storage
+  w.total = off;
+  w.B = B;
+  w.part_floats = pf;
+  (void)n;
+  return w;
+}
+
+template <int L, typename T>
+e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
+  const e2a_attn_args* a = pl.a;
+  constexpr int K = (L + 1) * (L + 1);
+  const int C = a->C, H = a->H;
+  const int64_t n = a->n_atoms, E = a->n_edges;
+  const int64_t K0 = (int64_t)(L + 1) * C;
+  const WgWs W = wg_ws_layout(n, E, L, C);
+  char* wb = static_cast<char*>(pl.ws);
+  float* part = reinterpret_cast<float*>(wb + W.part);
+  auto zero = [&](float* p, int64_t cnt) {
+    if (!p || cnt <= 0) return;
+    k_zero<<<static_cast<unsigned>((cnt + 255) / 256), 256, 0, st>>>(p, cnt);
+  };
+  int64_t so2_count = 0;
+  for (int m = 0; m <= L; ++m) so2_count += (m == 0 ? 1 : 2) * ((int64_t)(L + 1 - m) * C) * ((int64_t)(L + 1 - m) * C);
+  zero(pl.w_q, (int64_t)C * C);
+  zero(pl.w_k, (int64_t)C * C);
+  zero(pl.w_rad, 8 * K0);
+  zero(pl.w_so2, so2_count);
+  E2A_LAUNCH_CHECK();
+  const T* feat = static_cast<const T*>(a->feat);
+  // dW_q = sum_i h_{i,0}^T dq_i, dW_k likewise (A(m, k) = h_k[0][m])
+  if (pl.w_q) {
+    const e2a_status e = gemm<T, float>(make_gemm(feat, 1, (int64_t)K * C, pl.dq, C, 1, C, C, n, 1.0f, pl.w_q, C,
+                                                  part), W.part_floats, st);
+    if (e != E2A_OK) return e;
+  }
+  if (pl.w_k) {
+    const e2a_status e = gemm<T, float>(make_gemm(feat, 1, (int64_t)K * C, pl.dk, C, 1, C, C, n, 1.0f, pl.w_k, C,
+                                                  part), W.part_floats, st);
+    if (e != E2A_OK) return e;
+  }
+  if ((!pl.w_rad && !pl.w_so2) || E == 0) return E2A_OK;
+
+  int32_t* src = reinterpret_cast<int32_t*>(wb + W.src);
+  k_edge_rows<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(a->row_ptr, n, src);
+  E2A_LAUNCH_CHECK();
+  T* X = reinterpret_cast<T*>(wb + W.X);
+  T* GT = reinterpret_cast<T*>(wb + W.GT);
+  float* Y = reinterpret_cast<float*>(wb + W.Y);
+  float* rbf = reinterpret_cast<float*>(wb + W.rbf);
+  const BatchLayout bl = batch_layout(W.B, L, C);
+  const T* wso2 = static_cast<const T*>(a->w_so2);
+  int64_t woff[L + 1];
+  {
+    int64_t o = 0;
+    for (int m = 0; m <= L; ++m) {
+      woff[m] = o;
+      const int64_t km = (int64_t)(L + 1 - m) * C;
+      o += (m == 0 ? 1 : 2) * km * km;
+    }
+  }
+  // W^T per block, for the Y products (only dW_rad needs Y)
+  T* wt = reinterpret_cast<T*>(wb + W.wt);
+  if (pl.w_rad)
+    for (int m = 0; m <= L; ++m) {
+      const int64_t km = (int64_t)(L + 1 - m) * C;
+      for (int w2 = 0; w2 < (m == 0 ? 1 : 2); ++w2) {
+        k_transpose_block<T><<<static_cast<unsigned>((km * km + 255) / 256), 256, 0, st>>>(
+            wso2 + woff[m] + w2 * km * km, km, wt + woff[m] + w2 * km * km);
+        E2A_LAUNCH_CHECK();
+      }
+    }
+  float* rhopart = reinterpret_cast<float*>(wb + W.rhopart);
+  for (int64_t e0 = 0; e0 < E; e0 += W.B) {
+    const int64_t nb = E - e0 < W.B ? E - e0 : W.B;
+    GatherParams gp{};
+    gp.pos = a->pos;
+    gp.col = a->col;
+    gp.src = src;
+    gp.q = pl.q;
+    gp.k = pl.k;
+    gp.lse = a->out_lse;
+    gp.grad = pl.grad_out;
+    for (int d = 0; d < 3; ++d) gp.box[d] = pl.box[d];
+    gp.periodic = pl.periodic;
+    gp.cutoff = a->cutoff;
+    gp.C = C;
+    gp.H = H;
+    gp.e0 = e0;
+    gp.nb = nb;
+    gp.bl = bl;
+    gp.rbf = rbf;
+    const size_t smem = sizeof(float) * kEB * (wig_size(L) + H);
+    k_wg_gather<L, T><<<static_cast<unsigned>((nb + kEB - 1) / kEB), 256, smem, st>>>(gp, feat, X, GT);
+    E2A_LAUNCH_CHECK();
+    // Y = SO2(X): Y0 = X0 W0; Yp = Xp W1 - Xm W2; Ym = Xp W2 + Xm W1 (only
+    // drho needs it)
+    for (int m = 0; pl.w_rad && m <= L; ++m) {
+      const int64_t km = (int64_t)(L + 1 - m) * C;
+      const T* Xp = X + bl.moff[m];
+      float* Yp = Y + bl.moff[m];
+      const T* W1 = wt + woff[m];   // W1^T (W0^T for m = 0), [n][k]
+      e2a_status e;
+      if (m == 0) {
+        e = gemm<T, T>(make_gemm(Xp, km, 1, W1, 1, km, nb, km, km, 1.0f, Yp, km, part, true), W.part_floats, st);
+        if (e != E2A_OK) return e;
+        continue;
+      }
+      const T* Xm = Xp + bl.B * km;
+      float* Ym = Yp + bl.B * km;
+      const T* W2 = W1 + km * km;
+      const struct { const T* x; const T* w; float* y; float s; bool first; } terms[4] = {
+          {Xp, W1, Yp, 1.0f, true}, {Xm, W2, Yp, -1.0f, false}, {Xp, W2, Ym, 1.0f, true}, {Xm, W1, Ym, 1.0f, false}};
+      for (const auto& t : terms) {
+        e = gemm<T, T>(make_gemm(t.x, km, 1, t.w, 1, km, nb, km, km, t.s, t.y, km, part, t.first), W.part_floats,
+                       st);
+        if (e != E2A_OK) return e;
+      }
+    }
+    // dy = rho dyhat, and dW_rad[k][(l, c)] += sum_b rbf[b][k] drho[b][(l, c)]
+    // through per-range partials added in order
+    {
+      const int64_t per = kRhoPer;
+      const int64_t nz = (nb + per - 1) / per;
+      const dim3 grid(static_cast<unsigned>((K0 + 255) / 256), static_cast<unsigned>(nz));
+      k_wg_rho<L, T><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, static_cast<const T*>(a->w_rad),
+                                           pl.w_rad ? Y : nullptr, GT, rhopart, e0 > 0);
+      E2A_LAUNCH_CHECK();
+    }
+    if (pl.w_so2) {
+      float* dwp = reinterpret_cast<float*>(wb + W.dwpart);
+      for (int m = 0; m <= L; ++m) {
+        const int64_t km = (int64_t)(L + 1 - m) * C;
+        const int64_t S = dw_splits(L, C, m);
+        const T* Xp = X + bl.moff[m];
+        const T* DYp = GT + bl.moff[m];
+        float* p1 = dwp;
+        float* p2 = dwp + S * km * km;
+        dwp += (m == 0 ? 1 : 2) * S * km * km;
+        // A(m', k) = X[k][m'] (transposed rows), B(k, n) = dY[k][n]
+        const T* Xm = Xp + bl.B * km;
+        const T* DYm = DYp + bl.B * km;
+        const struct { const T* x; const T* dy; float* part; float s; bool first; } terms[4] = {
+            {Xp, DYp, p1, 1.0f, true}, {Xm, DYm, p1, 1.0f, false}, {Xp, DYm, p2, 1.0f, true},
+            {Xm, DYp, p2, -1.0f, false}};
+        for (int t = 0; t < (m == 0 ? 1 : 4); ++t) {
+          Gemm g = make_gemm(terms[t].x, 1, km, terms[t].dy, km, 1, km, km, nb, terms[t].s, nullptr, km,
+                             terms[t].part);
+          g.S = static_cast<int>(S);
+          g.kper = ((nb + S - 1) / S + 31) / 32 * 32;
+          g.part_acc = !(e0 == 0 && terms[t].first);
+          const e2a_status e = launch_gemm<T, T>(g, st);
+          if (e != E2A_OK) return e;
+        }
+      }
+    }
+  }
+  if (pl.w_rad) {
+    // the edge ranges' partials of dW_rad, added in order (the first batch
+    // is the largest, so it set every slot)
+    Gemm r = make_gemm(nullptr, 0, 0, nullptr, 0, 0, 8, K0, 0, 1.0f, pl.w_rad, K0, rhopart);
+    r.S = static_cast<int>((W.B + kRhoPer - 1) / kRhoPer);
+    r.overwrite = true;
+    const e2a_status e = reduce_parts(r, st);
+    if (e != E2A_OK) return e;
+  }
+  if (pl.w_so2) {
+    // the partials of every matrix, added in order into its block of dW_so2
+    const float* dwp = reinterpret_cast<const float*>(wb + W.dwpart);
+    for (int m = 0; m <= L; ++m) {
+      const int64_t km = (int64_t)(L + 1 - m) * C;
+      const int64_t S = dw_splits(L, C, m);
+      for (int w = 0; w < (m == 0 ? 1 : 2); ++w) {
+        Gemm r = make_gemm(nullptr, 0, 0, nullptr, 0, 0, km, km, 0, 1.0f, pl.w_so2 + woff[m] + w * km * km, km,
+                           const_cast<float*>(dwp));
+        r.S = static_cast<int>(S);
+        r.overwrite = true;
+        const e2a_status e = reduce_parts(r, st);
+        if (e != E2A_OK) return e;
+        dwp += S * km * km;
+      }
+    }
+  }
+  return E2A_OK;
+}
+
+template <typename T>
+e2a_status run_wgrad_dtype(const WgradPlan& pl, hipStream_t st) {
+  switch (pl.a->L) {
+    case 0: return run_wgrad<0, T>(pl, st);
+    case 1: return run_wgrad<1, T>(pl, st);
+    case 2: return run_wgrad<2, T>(pl, st);
+    case 3: return run_wgrad<3, T>(pl, st);
+    case 4: return run_wgrad<4, T>(pl, st);
+    default: return fail(E2A_ERR_UNSUPPORTED, "L=%d", pl.a->L);
+  }
+}
+
+}  // namespace
+
+size_t wgrad_workspace_bytes(int64_t n, int64_t e, int L, int C, int H, int dtype) {
+  (void)H;
+  (void)dtype;
+  return wg_ws_layout(n, e, L, C).total;
+}
+
+e2a_status launch_weight_grads(const WgradPlan& pl, hipStream_t s) {
+  if (pl.a->n_atoms == 0) return E2A_OK;
+  return pl.a->dtype == E2A_DTYPE_BF16 ? run_wgrad_dtype<uint16_t>(pl, s) : run_wgrad_dtype<float>(pl, s);
+}
+
+}  // namespace e2a

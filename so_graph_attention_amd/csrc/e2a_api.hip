@@ -60,6 +60,86 @@ BwdWs bwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
+// The weight-gradient call: the feature-gradient workspace, dq and dk, and
+// the batches of the weight GEMMs.
+struct WBwdWs {
+  BwdWs b;
+  size_t dq, dk, wg, total;
+};
+
+WBwdWs wbwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
+  WBwdWs w{};
+  w.b = bwd_ws_layout(n, e, L, C, H);
+  size_t off = w.b.total;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
+  w.dq = take(sizeof(float) * (size_t)n * C);
+  w.dk = take(sizeof(float) * (size_t)n * C);
+  w.wg = take(wgrad_workspace_bytes(n, e, L, C, H, E2A_DTYPE_F32));
+  w.total = off;
+  return w;
+}
+
+// Checks shared by the backward calls (all inputs; the outputs are checked
+// by each call).
+e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
+  if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
+  if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
+  if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
+  if (a->L < 0 || a->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", a->L);
+  if (a->C <= 0 || a->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
+  if (a->C % a->H != 0) return fail(E2A_ERR_INVALID_ARG, "C=%d is not a multiple of H=%d", a->C, a->H);
+  if (a->H > 192) return fail(E2A_ERR_UNSUPPORTED, "H=%d; the backward kernels take at most 192 heads", a->H);
+  if (a->n_rbf != 8) return fail(E2A_ERR_INVALID_ARG, "n_rbf=%d; only 8 is supported", a->n_rbf);
+  if (a->dtype != E2A_DTYPE_F32 && a->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", a->dtype);
+  if (a->variant < E2A_VARIANT_AUTO || a->variant > E2A_VARIANT_MFMA)
+    return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
+  if (a->variant == E2A_VARIANT_MFMA && !mfma_supported(a->L, a->C, a->H, a->dtype))
+    return fail(E2A_ERR_UNSUPPORTED, "MFMA kernel not built for L=%d C=%d H=%d dtype=%d", a->L, a->C, a->H, a->dtype);
+  if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
+  if (a->n_atoms > 0) {
+    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out, a->out_lse,
+                          grad_out};
+    const char* names[] = {"pos", "row_ptr", "feat", "w_q", "w_k", "w_rad", "w_so2", "out", "out_lse",
+                           "grad_out"};
+    for (int t = 0; t < 10; ++t)
+      if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
+    if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+  }
+  if (a->box)
+    for (int d = 0; d < 3; ++d)
+      if (!finite_positive(a->box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
+  return E2A_OK;
+}
+
+// q, k, then the query pass (ds) and, with grad_feat, the value pass and the
+// l = 0 terms; dq and dk to wdq, wdk when those are set.
+e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* grad_feat, float* wdq, float* wdk,
+                        char* base, const BwdWs& ws, hipStream_t s) {
+  AttnPlan qk{};
+  qk.a = a;
+  qk.q = reinterpret_cast<float*>(base + ws.q);
+  qk.k = reinterpret_cast<float*>(base + ws.k);
+  BwdPlan pl{};
+  pl.a = a;
+  pl.grad_out = grad_out;
+  pl.grad_feat = grad_feat;
+  pl.q = qk.q;
+  pl.k = qk.k;
+  pl.dq = reinterpret_cast<float*>(base + ws.dq);
+  pl.ds = reinterpret_cast<float*>(base + ws.ds);
+  pl.wqkt = reinterpret_cast<float*>(base + ws.wqkt);
+  pl.mfma_ws = base + ws.mfma;
+  pl.wdq = wdq;
+  pl.wdk = wdk;
+  pl.periodic = a->box != nullptr;
+  for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
+  e2a_status st = launch_qk(qk, s);
+  if (st != E2A_OK) return st;
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
+  return use_mfma ? launch_backward_mfma(pl, s) : launch_attention_backward(pl, s);
+}
+
 }  // namespace
 }  // namespace e2a
 
@@ -205,60 +285,66 @@ size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L
 
 e2a_status e2a_attention_bwd(const e2a_attn_args* a, const float* grad_out, float* grad_feat, void* stream) {
   clear_error();
-  if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
-  if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
-  if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
-  if (a->L < 0 || a->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", a->L);
-  if (a->C <= 0 || a->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
-  if (a->C % a->H != 0) return fail(E2A_ERR_INVALID_ARG, "C=%d is not a multiple of H=%d", a->C, a->H);
-  if (a->H > 192) return fail(E2A_ERR_UNSUPPORTED, "H=%d; the backward kernels take at most 192 heads", a->H);
-  if (a->n_rbf != 8) return fail(E2A_ERR_INVALID_ARG, "n_rbf=%d; only 8 is supported", a->n_rbf);
-  if (a->dtype != E2A_DTYPE_F32 && a->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", a->dtype);
-  if (a->variant < E2A_VARIANT_AUTO || a->variant > E2A_VARIANT_MFMA)
-    return fail(E2A_ERR_INVALID_ARG, "variant=%d", a->variant);
-  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
-  if (a->variant == E2A_VARIANT_MFMA && !mfma_ok)
-    return fail(E2A_ERR_UNSUPPORTED, "MFMA kernel not built for L=%d C=%d H=%d dtype=%d", a->L, a->C, a->H, a->dtype);
-  if (!finite_positive(a->cutoff)) return fail(E2A_ERR_INVALID_ARG, "cutoff must be finite and > 0");
-  if (a->n_atoms > 0) {
-    const void* ptrs[] = {a->pos, a->row_ptr, a->feat, a->w_q, a->w_k, a->w_rad, a->w_so2, a->out, a->out_lse,
-                          grad_out, grad_feat};
-    const char* names[] = {"pos", "row_ptr", "feat", "w_q", "w_k", "w_rad", "w_so2", "out", "out_lse",
-                           "grad_out", "grad_feat"};
-    for (int t = 0; t < 11; ++t)
-      if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
-    if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
-  }
-  if (a->box)
-    for (int d = 0; d < 3; ++d)
-      if (!finite_positive(a->box[d])) return fail(E2A_ERR_INVALID_ARG, "box[%d] must be finite and > 0", d);
+  e2a_status st = check_bwd_args(a, grad_out);
+  if (st != E2A_OK) return st;
+  if (a->n_atoms > 0 && !grad_feat) return fail(E2A_ERR_INVALID_ARG, "grad_feat is NULL");
   const BwdWs ws = bwd_ws_layout(a->n_atoms, a->n_edges, a->L, a->C, a->H);
   if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
     return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
   if (a->n_atoms == 0) return E2A_OK;
+  return run_backward(a, grad_out, grad_feat, nullptr, nullptr, static_cast<char*>(a->workspace), ws,
+                      static_cast<hipStream_t>(stream));
+}
 
-  char* base = static_cast<char*>(a->workspace);
-  AttnPlan qk{};
-  qk.a = a;
-  qk.q = reinterpret_cast<float*>(base + ws.q);
-  qk.k = reinterpret_cast<float*>(base + ws.k);
-  BwdPlan pl{};
-  pl.a = a;
-  pl.grad_out = grad_out;
-  pl.grad_feat = grad_feat;
-  pl.q = qk.q;
-  pl.k = qk.k;
-  pl.dq = reinterpret_cast<float*>(base + ws.dq);
-  pl.ds = reinterpret_cast<float*>(base + ws.ds);
-  pl.wqkt = reinterpret_cast<float*>(base + ws.wqkt);
-  pl.mfma_ws = base + ws.mfma;
-  pl.periodic = a->box != nullptr;
-  for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  e2a_status st = launch_qk(qk, s);
+size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H) {
+  if (n_atoms < 0 || n_edges < 0 || L < 0 || L > 4 || C <= 0 || H <= 0) return 0;
+  return wbwd_ws_layout(n_atoms, n_edges, L, C, H).total;
+}
+
+e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_out, float* grad_feat,
+                                     float* grad_w_q, float* grad_w_k, float* grad_w_rad, float* grad_w_so2,
+                                     void* stream) {
+  clear_error();
+  e2a_status st = check_bwd_args(a, grad_out);
   if (st != E2A_OK) return st;
-  const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
-  return use_mfma ? launch_backward_mfma(pl, s) : launch_attention_backward(pl, s);
+  if (!grad_feat && !grad_w_q && !grad_w_k && !grad_w_rad && !grad_w_so2)
+    return fail(E2A_ERR_INVALID_ARG, "no output requested");
+  const WBwdWs ws = wbwd_ws_layout(a->n_atoms, a->n_edges, a->L, a->C, a->H);
+  if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
+  if (a->n_atoms == 0) return E2A_OK;
+  char* base = static_cast<char*>(a->workspace);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* dq = reinterpret_cast<float*>(base + ws.dq);
+  float* dk = reinterpret_cast<float*>(base + ws.dk);
+  const bool want_qk = grad_w_q || grad_w_k;
+  if (grad_feat || want_qk) {
+    // the softmax gradient ds (and dL/dh when asked for); dq, dk from it
+    st = run_backward(a, grad_out, grad_feat, want_qk ? dq : nullptr, want_qk ? dk : nullptr, base, ws.b, s);
+  } else {
+    // dW_rad and dW_so2 need only q and k (for the attention weights)
+    AttnPlan qk{};
+    qk.a = a;
+    qk.q = reinterpret_cast<float*>(base + ws.b.q);
+    qk.k = reinterpret_cast<float*>(base + ws.b.k);
+    st = launch_qk(qk, s);
+  }
+  if (st != E2A_OK) return st;
+  WgradPlan wp{};
+  wp.a = a;
+  wp.grad_out = grad_out;
+  wp.q = reinterpret_cast<const float*>(base + ws.b.q);
+  wp.k = reinterpret_cast<const float*>(base + ws.b.k);
+  wp.dq = dq;
+  wp.dk = dk;
+  wp.w_q = grad_w_q;
+  wp.w_k = grad_w_k;
+  wp.w_rad = grad_w_rad;
+  wp.w_so2 = grad_w_so2;
+  wp.ws = base + ws.wg;
+  wp.periodic = a->box != nullptr;
+  for (int d = 0; d < 3; ++d) wp.box[d] = a->box ? a->box[d] : 0.0f;
+  return launch_weight_grads(wp, s);
 }
 
 }  // extern "C"

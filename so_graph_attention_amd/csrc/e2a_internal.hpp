@@ -94,13 +94,35 @@ struct BwdPlan {
   float* ds;               // workspace f32 [E, H]
   float* wqkt;             // workspace f32 [2][C][C]: W_q^T, W_k^T
   void* mfma_ws;           // workspace of the matrix-core path
+  float* wdq;              // if set: dq_j = sum_j' ds_jj' k_j' / sqrt(C/H), f32 [N, C]
+  float* wdk;              // if set: dk_j = sum_i ds_ij q_i / sqrt(C/H), f32 [N, C]
   float box[3];
   int periodic;
 };
 // Scalar passes (any shape), and the matrix-core passes with their helpers.
+// grad_feat may be null: then only ds (and wdq, wdk if set) are formed.
 e2a_status launch_attention_backward(const BwdPlan& p, hipStream_t s);
 e2a_status launch_backward_mfma(const BwdPlan& p, hipStream_t s);
 e2a_status launch_bwd_delta(const BwdPlan& p, float* delta, hipStream_t s);
 e2a_status launch_bwd_qk(const BwdPlan& p, hipStream_t s);
+
+// Weight gradients (attention_wgrad.hip), after ds and dq, dk are formed.
+struct WgradPlan {
+  const e2a_attn_args* a;
+  const float* grad_out;   // G [N, K, C]
+  const float* q;          // f32 [N, C]
+  const float* k;          // f32 [N, C]
+  const float* dq;         // f32 [N, C] (needed for w_q)
+  const float* dk;         // f32 [N, C] (needed for w_k)
+  float* w_q;              // outputs, each optional
+  float* w_k;
+  float* w_rad;
+  float* w_so2;
+  void* ws;                // wgrad_workspace_bytes(...)
+  float box[3];
+  int periodic;
+};
+size_t wgrad_workspace_bytes(int64_t n, int64_t e, int L, int C, int H, int dtype);
+e2a_status launch_weight_grads(const WgradPlan& p, hipStream_t s);
 
 }  // namespace e2a

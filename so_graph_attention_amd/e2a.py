@@ -28,7 +28,8 @@ VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
 # Every symbol include/e2a.h declares.
 EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
             "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
-            "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd"]
+            "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd",
+            "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights"]
 
 
 class E2AError(RuntimeError):
@@ -78,6 +79,13 @@ def _load():
                                                       ctypes.c_int]
     lib.e2a_attention_bwd.restype = ctypes.c_int32
     lib.e2a_attention_bwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.e2a_attention_bwd_weights_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_attention_bwd_weights_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                              ctypes.c_int, ctypes.c_int]
+    lib.e2a_attention_bwd_weights.restype = ctypes.c_int32
+    lib.e2a_attention_bwd_weights.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]
     return lib
 
 
@@ -240,6 +248,75 @@ def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: in
 
 def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
     return int(_lib.e2a_attention_bwd_workspace_bytes(n_atoms, n_edges, L, C, H))
+
+
+def _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff, box,
+              variant, workspace):
+    """Checks the backward calls' inputs and fills their argument struct;
+    returns (args, box array to keep alive)."""
+    dev = pos.device
+    n = pos.shape[0]
+    if feat.dtype == torch.bfloat16:
+        dtype = E2A_DTYPE_BF16
+    elif feat.dtype == torch.float32:
+        dtype = E2A_DTYPE_F32
+    else:
+        raise TypeError("feat must be float32 or bfloat16")
+    _need(pos, "pos", torch.float32, dev)
+    _need(row_ptr, "row_ptr", torch.int64, dev)
+    _need(col, "col", torch.int32, dev)
+    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
+        _need(t, name, feat.dtype, dev)
+    for name, t in (("out", out), ("out_lse", out_lse), ("grad_out", grad_out)):
+        _need(t, name, torch.float32, dev)
+    box_arr, box_p = _box_arg(box)
+    a = AttnArgs()
+    a.pos = _ptr(pos)
+    a.box = box_p
+    a.n_atoms = n
+    a.row_ptr = _ptr(row_ptr)
+    a.col = _ptr(col)
+    a.n_edges = col.numel()
+    a.cutoff = float(cutoff)
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
+    a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
+    a.out = _ptr(out)
+    a.out_lse = _ptr(out_lse)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel()
+    return a, box_arr
+
+
+def e2a_attention_bwd_weights_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
+    return int(_lib.e2a_attention_bwd_weights_workspace_bytes(n_atoms, n_edges, L, C, H))
+
+
+def e2a_attention_bwd_weights(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, *, L: int,
+                              C: int, H: int, cutoff: float, box=None, variant: str = "auto", feat_grad: bool = True,
+                              weights=("w_q", "w_k", "w_rad", "w_so2"), workspace=None, stream=None):
+    """Gradients of the layer with respect to its weights (those named in
+    ``weights``) and, with feat_grad, its node features, for grad_out = dL/do.
+    Returns a dict of fp32 tensors: "feat" [N,(L+1)^2,C], "w_q", "w_k" [C,C],
+    "w_rad" [8,L+1,C], "w_so2" (flat, the layout of w_so2)."""
+    dev = pos.device
+    n = pos.shape[0]
+    K = (L + 1) ** 2
+    shapes = {"feat": (n, K, C), "w_q": (C, C), "w_k": (C, C), "w_rad": (8, L + 1, C),
+              "w_so2": (e2a_so2_param_count(L, C),)}
+    want = (["feat"] if feat_grad else []) + list(weights)
+    for name in want:
+        if name not in shapes:
+            raise ValueError(f"unknown gradient {name!r}")
+    res = {name: torch.empty(shapes[name], dtype=torch.float32, device=dev) for name in want}
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_attention_bwd_weights_workspace_bytes(n, col.numel(), L, C, H)),
+                                dtype=torch.uint8, device=dev)
+    a, box_arr = _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff,
+                           box, variant, workspace)
+    outs = [_ptr(res[name]) if name in res else None for name in ("feat", "w_q", "w_k", "w_rad", "w_so2")]
+    _check(_lib.e2a_attention_bwd_weights(ctypes.byref(a), _ptr(grad_out), *outs, _stream(stream)))
+    del box_arr
+    return res
 
 
 def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, *, L: int, C: int,

@@ -172,6 +172,37 @@ def test_backward_rejects_on_host(kw, grads, status):
     assert B.lib().e2a_attention_bwd(None, FAKE, FAKE, None) == B.E2A_ERR_INVALID_ARG
 
 
+@pytest.mark.parametrize("kw,grads,status", [
+    (dict(), (None, FAKE, FAKE), B.E2A_ERR_INVALID_ARG),             # grad_out
+    (dict(), (FAKE, None, None), B.E2A_ERR_INVALID_ARG),             # no output requested
+    (dict(out_lse=None), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),  # alpha needs the log-normaliser
+    (dict(w_rad=None), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=2), (FAKE, None, FAKE), B.E2A_ERR_UNSUPPORTED),
+    (dict(C=16, H=3), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(workspace_bytes=8), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
+])
+def test_weight_backward_rejects_on_host(kw, grads, status):
+    """e2a_attention_bwd_weights (grad_out, grad_feat, grad_w_so2 here; the
+    other outputs NULL) checks its arguments before any launch."""
+    kw = dict(out_lse=FAKE, **kw) if "out_lse" not in kw else kw
+    a = attn_args(**kw)
+    st = B.lib().e2a_attention_bwd_weights(ctypes.byref(a), grads[0], grads[1], None, None, None, grads[2], None)
+    assert st == status, (st, B.last_error_message())
+    assert B.last_error_message()
+    assert B.lib().e2a_attention_bwd_weights(None, FAKE, FAKE, None, None, None, None, None) == B.E2A_ERR_INVALID_ARG
+
+
+def test_weight_backward_workspace_query():
+    """The weight-gradient workspace holds the feature-gradient one, dq, dk,
+    and one batch of per-edge tensors (x, dyhat, SO2(x): 3 x (L+1)^2 C floats
+    per edge, at most 65536 edges)."""
+    n, e, L, C = 1000, 30000, 3, 128
+    got = B.e2a_attention_bwd_weights_workspace_bytes(n, e, L, C, 8)
+    assert got >= B.e2a_attention_bwd_workspace_bytes(n, e, L, C, 8) + 4 * (2 * n * C + 3 * e * (L + 1) ** 2 * C)
+    assert B.e2a_attention_bwd_weights_workspace_bytes(n, 100, L, C, 8) < got   # the batch shrinks with E
+    assert B.e2a_attention_bwd_weights_workspace_bytes(n, -1, L, C, 8) == 0
+
+
 def test_backward_workspace_query():
     n, e = 1000, 30000
     got = B.e2a_attention_bwd_workspace_bytes(n, e, 3, 128, 8)

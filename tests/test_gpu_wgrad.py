@@ -1,0 +1,154 @@
+"""GPU weight gradients (e2a_attention_bwd_weights) vs the fp64 oracle's
+attention_weight_backward on the same seeded inputs and cotangent.
+
+The backward reads the forward's log-normaliser; these tests take it from
+the fp32 scalar forward (except where named), so that the comparison
+measures the weight-gradient kernels.  fp32 storage: relative L2 <= 1e-5 per
+weight (fp32 GEMMs).  bf16 storage: <= 2e-2 (bf16 operands on the matrix
+cores, fp32 sums).  The weight gradients are sums over every edge, so the
+full-size workloads cannot be sampled by rows as dL/dh is; there the
+cotangent is nonzero on a seeded sample of destinations only, which makes
+every other edge's terms vanish, while the GPU still runs all edges (and all
+batches of 65536)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from workloads import make_config
+
+from gpu_util import log, rel_l2, sample_dest, to_device
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+NAMES = ("w_q", "w_k", "w_rad", "w_so2")
+
+
+@pytest.fixture(scope="module")
+def B():
+    import so_graph_attention_amd.e2a as mod
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return mod
+
+
+def setup(w, seed=77, keep=None):
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    G = np.random.default_rng(seed).standard_normal((w.n_atoms, (w.L + 1) ** 2, w.C)).astype(np.float32)
+    if keep is not None:
+        G[np.setdiff1d(np.arange(w.n_atoms), keep)] = 0.0
+    d["G"] = torch.from_numpy(G).cuda()
+    return rp, col, d, G
+
+
+def forward(B, w, d, variant="reference"):
+    box = None if w.box is None else w.box.tolist()
+    return B.e2a_attention_fwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                               d["w_so2"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, variant=variant,
+                               with_lse=True)
+
+
+def gpu_wgrad(B, w, d, out, lse, variant="auto", **kw):
+    box = None if w.box is None else w.box.tolist()
+    res = B.e2a_attention_bwd_weights(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                                      d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box,
+                                      variant=variant, **kw)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def oracle_wgrad(w, rp, col, G, centres=None):
+    return O.attention_weight_backward(w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"),
+                                       w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G, box=w.box,
+                                       centres=centres)
+
+
+def check(got, want, tol, tag):
+    for name in NAMES:
+        err = rel_l2(got[name].reshape(want[name].shape), want[name])
+        log(f"[wgrad] {tag} {name}: rel-L2 {err:.3e}")
+        assert np.all(np.isfinite(got[name])), name
+        assert err <= tol, (name, err)
+
+
+@pytest.mark.parametrize("L,C,H", [(0, 8, 2), (1, 16, 2), (2, 16, 2), (3, 8, 1), (4, 8, 2)])
+def test_wgrad_f32_tiny_full(B, L, C, H):
+    """fp32 storage, every weight of a 64-atom system; dL/dh from the same
+    call equals e2a_attention_bwd's."""
+    log(f"[wgrad] f32 tiny L={L} C={C} H={H}")
+    w = make_config("tiny", L=L, C=C, H=H)
+    rp, col, d, G = setup(w)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference")
+    check(got, oracle_wgrad(w, rp, col, G), TOL_F32, f"f32 L={L}")
+    feat = B.e2a_attention_bwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                               d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff,
+                               variant="reference")
+    torch.cuda.synchronize()
+    assert np.array_equal(got["feat"], feat.cpu().numpy())
+
+
+def test_wgrad_f32_periodic_box(B):
+    log("[wgrad] f32 periodic box")
+    rng = np.random.default_rng(1516)
+    box = np.full(3, 9.0, dtype=np.float32)
+    pts = []
+    while len(pts) < 90:   # random points at least 0.9 apart (minimum image)
+        p = rng.random(3) * 9.0
+        if all(np.linalg.norm((p - q + 4.5) % 9.0 - 4.5) >= 0.9 for q in pts):
+            pts.append(p)
+    pos = np.array(pts, dtype=np.float32)
+    w = make_config("tiny", L=2, C=8, H=2, geometry=(pos, box, None, {}))
+    rp, col, d, G = setup(w)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference", feat_grad=False)
+    check(got, oracle_wgrad(w, rp, col, G), TOL_F32, "f32 periodic")
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_wgrad_bf16_tiny_full(B, L):
+    """bf16 storage, C = 128, H = 8: the matrix-core GEMMs (and the
+    matrix-core query pass for ds), every weight of a 64-atom system."""
+    log(f"[wgrad] bf16 tiny L={L}")
+    w = make_config("tiny", L=L, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse)
+    check(got, oracle_wgrad(w, rp, col, G), TOL_BF16, f"bf16 L={L}")
+
+
+def test_wgrad_bf16_drug_sparse_cotangent(B):
+    """The drug-like workload (347k edges: 6 batches), with the MFMA forward's
+    log-normaliser; G nonzero on 24 sampled destinations."""
+    log("[wgrad] bf16 drug, sparse cotangent")
+    w = make_config("drug")
+    rp0, _ = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    keep = sample_dest(rp0, 24, seed=31)
+    rp, col, d, G = setup(w, keep=keep)
+    out, lse = forward(B, w, d, variant="mfma")
+    got = gpu_wgrad(B, w, d, out, lse, feat_grad=False)
+    check(got, oracle_wgrad(w, rp, col, G, centres=keep), TOL_BF16, "bf16 drug")
+
+
+def test_wgrad_deterministic_and_partial_requests(B):
+    """Two calls are bit-identical, and asking for some outputs only (which
+    skips the query pass when neither dL/dh nor W_q, W_k is wanted) gives the
+    same values as the full call."""
+    log("[wgrad] determinism and partial requests")
+    w = make_config("tiny", L=3, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w)
+    out, lse = forward(B, w, d)
+    full = gpu_wgrad(B, w, d, out, lse)
+    again = gpu_wgrad(B, w, d, out, lse)
+    for name in full:
+        assert np.array_equal(full[name], again[name]), name
+    part = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_rad", "w_so2"))
+    assert set(part) == {"w_rad", "w_so2"}
+    for name in part:
+        assert np.array_equal(part[name], full[name]), name
+    qk = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_k",))
+    assert np.array_equal(qk["w_k"], full["w_k"])

@@ -640,6 +640,21 @@ def test_p15_weight_gradient_finite_differences(case):
         assert abs(fd - an) <= 1e-8 * max(abs(an), 1e-3), (name, fd, an)
 
 
+def test_p15_weight_gradient_centres_with_sparse_cotangent(tiny):
+    """With G zero outside a set of destinations, summing over those
+    destinations' edges only gives the full weight gradients."""
+    w, rp, col = tiny
+    G = np.random.default_rng(1517).standard_normal((w.n_atoms, (w.L + 1) ** 2, w.C))
+    keep = np.array([3, 10, 11, 40])
+    G[np.setdiff1d(np.arange(w.n_atoms), keep)] = 0.0
+    args = (w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"), w.as_f32("w_rad"),
+            w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G)
+    a = O.attention_weight_backward(*args)
+    b = O.attention_weight_backward(*args, centres=keep)
+    for name in a:
+        assert rel(a[name], b[name]) <= 1e-13, name
+
+
 def test_p15_weight_gradient_chunking_invariant(tiny):
     """The weight gradients do not depend on how the edges are grouped."""
     w, rp, col = tiny
