@@ -164,6 +164,49 @@ def backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, b
                                 "l = 0 terms"}
 
 
+def so2_flops_per_edge(L, C):
+    """The SO(2) mix alone: 2[(L+1)^2 + 4 sum_{m>=1} (L+1-m)^2] C^2 per edge."""
+    return 2 * ((L + 1) ** 2 + 4 * sum((L + 1 - m) ** 2 for m in range(1, L + 1))) * C * C
+
+
+def training_backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box):
+    """Everything training the layer needs from one cotangent
+    (e2a_attention_bwd_weights: dL/dh and the gradients of W_q, W_k, W_rad,
+    W_so2); one warm-up and two timed calls.  Algorithmic work: the feature
+    gradient's two passes plus, for the weights, the SO(2) mix of the rotated
+    features (for dW_rad) and the weight products, each the size of the
+    forward's mix."""
+    e = int(col.numel())
+    out, lse = B.e2a_attention_fwd(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, L=w.L, C=w.C, H=w.H,
+                                   cutoff=w.cutoff, box=box, with_lse=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(8)
+    G = torch.randn(tuple(out.shape), generator=gen, device=dev, dtype=torch.float32)
+    ws = torch.empty(B.e2a_attention_bwd_weights_workspace_bytes(w.n_atoms, e, w.L, w.C, w.H), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        return B.e2a_attention_bwd_weights(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, out, lse, G, L=w.L, C=w.C,
+                                           H=w.H, cutoff=w.cutoff, box=box, workspace=ws)
+
+    run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(2):
+        res = run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 2
+    finite = all(bool(torch.isfinite(v).all()) for v in res.values())
+    flops = (2 * flops_per_edge(w.L, w.C) + 2 * so2_flops_per_edge(w.L, w.C)) * e
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"train_backward_ms": ms, "train_backward_tflops": tflops,
+            "train_backward_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS, "train_backward_finite": finite,
+            "train_backward_kernels": "e2a_attention_bwd_weights: dL/dh and dW_q, dW_k, dW_rad, dW_so2 "
+                                      "(per-edge batches of 65536, GEMMs on the matrix cores)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -265,6 +308,9 @@ def main():
         progress("timing the feature gradient")
         bwd = backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box)
         progress(f"feature gradient {bwd['backward_ms']:.1f} ms")
+        progress("timing the training backward (feature and weight gradients)")
+        bwd.update(training_backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box))
+        progress(f"training backward {bwd['train_backward_ms']:.1f} ms")
 
     achieved = f_edge * n_edges / (attn_ms * 1e-3) / 1e12
     traffic = traffic_per_launch()
