@@ -8,6 +8,7 @@ from .e2a_oracle import (  # noqa: F401
     attention,
     attention_backward,
     attention_online,
+    attention_position_backward,
     attention_weight_backward,
     convolution,
     edge_messages,

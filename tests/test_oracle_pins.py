@@ -667,6 +667,106 @@ def test_p15_weight_gradient_chunking_invariant(tiny):
         assert rel(a[name], b[name]) <= 1e-13, name
 
 
+# ---------------------------------------------------------------- P16 -------
+def _pos_case(L, C, H, seed=1600):
+    w = make_config("tiny", L=L, C=C, H=H)
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    G = np.random.default_rng(seed).standard_normal((w.n_atoms, (L + 1) ** 2, C))
+    f = w.as_f32("feat").astype(np.float64)
+    W = [w.as_f32(n).astype(np.float64) for n in ("w_q", "w_k", "w_rad", "w_so2")]
+    return w, rp, col, G, f, W
+
+
+def _pos_grad(w, pos, rp, col, f, W, G, **kw):
+    return O.attention_position_backward(pos, rp, col, f, *W, w.L, w.C, w.H, w.cutoff, G, box=w.box, **kw)
+
+
+def test_p16_position_gradient_translation_invariance():
+    """The layer depends on positions only through edge vectors, so the
+    gradients of all atoms sum to zero."""
+    w, rp, col, G, f, W = _pos_case(2, 8, 2)
+    g = _pos_grad(w, w.pos.astype(np.float64), rp, col, f, W, G)
+    assert np.abs(g.sum(axis=0)).max() <= 1e-8 * np.abs(g).max()
+
+
+def test_p16_position_gradient_rotation_equivariance():
+    """Rotating the positions by Q and every degree-l block of the features
+    and of the cotangent by D^l(Q) leaves L = <G, o> unchanged (o rotates with
+    them), so the position gradients rotate: g(Q x) = Q g(x)."""
+    w, rp, col, G, f, W = _pos_case(2, 8, 2, seed=1601)
+    rng = np.random.default_rng(1602)
+    Q, _ = np.linalg.qr(rng.standard_normal((3, 3)))
+    if np.linalg.det(Q) < 0:
+        Q[:, 0] = -Q[:, 0]
+    pos = w.pos.astype(np.float64)
+    c = pos.mean(axis=0)
+    pos_r = (pos - c) @ Q.T + c
+    f_r, G_r = f.copy(), G.copy()
+    for l in range(w.L + 1):
+        D = O.wigner_d(l, Q)
+        sl = slice(l * l, (l + 1) ** 2)
+        f_r[:, sl, :] = np.einsum("mn,anc->amc", D, f[:, sl, :])
+        G_r[:, sl, :] = np.einsum("mn,anc->amc", D, G[:, sl, :])
+    atoms = np.array([0, 7, 21, 40, 63])
+    g = _pos_grad(w, pos, rp, col, f, W, G, atoms=atoms)
+    g_r = _pos_grad(w, pos_r, rp, col, f_r, W, G_r, atoms=atoms)
+    assert rel(g_r, g @ Q.T) <= 1e-8
+
+
+def test_p16_position_gradient_zero_torque_for_scalars():
+    """With only l = 0 features (L = 0) the loss is rotation invariant, so the
+    total torque sum_a x_a x g_a vanishes."""
+    w, rp, col, G, f, W = _pos_case(0, 8, 2, seed=1603)
+    pos = w.pos.astype(np.float64)
+    g = _pos_grad(w, pos, rp, col, f, W, G)
+    torque = np.cross(pos - pos.mean(axis=0), g).sum(axis=0)
+    assert np.abs(torque).max() <= 1e-8 * np.abs(np.cross(pos, g)).max()
+
+
+def test_p16_position_gradient_two_atoms_closed_form():
+    """Two atoms within the cutoff, L = 0, one head: each has one neighbour
+    (softmax weight 1), so o_i[c] = rho(r)[c] (h_j W0)[c] with
+    rho[c] = sum_k e_k(r) W_rad[k][0][c], and L = sum_i <G_i, o_i> depends on
+    the positions through r = |x_1 - x_0| alone:
+    dL/dx_1 = -dL/dx_0 = r_hat sum_i sum_c G_i[c] (h_j W0)[c] sum_k W_rad[k][0][c] e_k'(r),
+    with e_k(r) = exp(-gamma (r - mu_k)^2) (cos(pi r / r_c) + 1) / 2 differentiated by hand."""
+    rc = 5.0
+    pos = np.array([[1.0, 2.0, 3.0], [2.3, 1.1, 4.2]], dtype=np.float32)
+    w = make_config("tiny", L=0, C=4, H=1, geometry=(pos, None, None, {}))
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    assert col.size == 2 and abs(w.cutoff - rc) < 1e-6
+    rng = np.random.default_rng(1605)
+    G = rng.standard_normal((2, 1, 4))
+    f = w.as_f32("feat").astype(np.float64)
+    W = [w.as_f32(n).astype(np.float64) for n in ("w_q", "w_k", "w_rad", "w_so2")]
+    g = _pos_grad(w, pos.astype(np.float64), rp, col, f, W, G)
+    d = pos[1].astype(np.float64) - pos[0].astype(np.float64)
+    r = np.linalg.norm(d)
+    delta = rc / 7
+    gamma = 1.0 / (2 * delta * delta)
+    mu = np.arange(8) * delta
+    gauss = np.exp(-gamma * (r - mu) ** 2)
+    env = 0.5 * (np.cos(np.pi * r / rc) + 1)
+    denv = -0.5 * np.pi / rc * np.sin(np.pi * r / rc)
+    de = gauss * (-2 * gamma * (r - mu)) * env + gauss * denv          # e_k'(r)
+    drho = np.einsum("k,kc->c", de, W[2][:, 0, :])                      # d rho[c] / dr
+    W0 = W[3].reshape(4, 4)
+    dldr = sum(float(np.sum(G[i, 0] * (f[1 - i, 0] @ W0) * drho)) for i in range(2))
+    want = dldr * d / r
+    assert rel(g[1], want) <= 1e-8 and rel(g[0], -want) <= 1e-8
+
+
+def test_p16_position_gradient_step_size():
+    """Halving the difference step changes the result by far less than the
+    bounds it is held to (the truncation error falls as eps^4)."""
+    w, rp, col, G, f, W = _pos_case(1, 8, 2, seed=1604)
+    pos = w.pos.astype(np.float64)
+    atoms = np.array([3, 30])
+    a = _pos_grad(w, pos, rp, col, f, W, G, atoms=atoms, eps=1e-4)
+    b = _pos_grad(w, pos, rp, col, f, W, G, atoms=atoms, eps=5e-5)
+    assert rel(a, b) <= 1e-9
+
+
 # ------------------------------------------------------------ radial basis --
 def test_radial_basis_definition_points():
     rc = 5.0
