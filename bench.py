@@ -169,6 +169,38 @@ def so2_flops_per_edge(L, C):
     return 2 * ((L + 1) ** 2 + 4 * sum((L + 1 - m) ** 2 for m in range(1, L + 1))) * C * C
 
 
+def forces_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box):
+    """What forces from an energy built on the layer need from one cotangent:
+    dL/dh (for the layers below) and dL/dx (e2a_attention_bwd_weights with
+    the position output); one warm-up and two timed calls."""
+    e = int(col.numel())
+    out, lse = B.e2a_attention_fwd(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, L=w.L, C=w.C, H=w.H,
+                                   cutoff=w.cutoff, box=box, with_lse=True)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(9)
+    G = torch.randn(tuple(out.shape), generator=gen, device=dev, dtype=torch.float32)
+    ws = torch.empty(B.e2a_attention_bwd_weights_workspace_bytes(w.n_atoms, e, w.L, w.C, w.H), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        return B.e2a_attention_bwd_weights(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, out, lse, G, L=w.L, C=w.C,
+                                           H=w.H, cutoff=w.cutoff, box=box, weights=(), pos_grad=True, workspace=ws)
+
+    run()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(2):
+        res = run()
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 2
+    return {"forces_ms": ms, "forces_edges_per_s": e / (ms * 1e-3),
+            "forces_finite": all(bool(torch.isfinite(v).all()) for v in res.values()),
+            "forces_kernels": "e2a_attention_bwd_weights: dL/dh and dL/dx (per-edge batches: SO2(x) and "
+                              "SO2^T(dy) on the matrix cores, Wigner tangents per edge)"}
+
+
 def training_backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box):
     """Everything training the layer needs from one cotangent
     (e2a_attention_bwd_weights: dL/dh and the gradients of W_q, W_k, W_rad,
@@ -311,6 +343,9 @@ def main():
         progress("timing the training backward (feature and weight gradients)")
         bwd.update(training_backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box))
         progress(f"training backward {bwd['train_backward_ms']:.1f} ms")
+        progress("timing the forces (feature and position gradients)")
+        bwd.update(forces_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, box))
+        progress(f"forces {bwd['forces_ms']:.1f} ms")
 
     achieved = f_edge * n_edges / (attn_ms * 1e-3) / 1e12
     traffic = traffic_per_launch()

@@ -247,9 +247,9 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
 
 /*
  * Gradients of e2a_attention_fwd with respect to its weights, and optionally
- * its node features, for a cotangent grad_out = dL/do: what training the
- * layer needs (technical summary section 2.2; the message steps of section
- * 2.1).  With ds_ij, dq_i, dk_j as in e2a_attention_bwd, the edge cotangent
+ * its node features and the atom positions, for a cotangent grad_out =
+ * dL/do: what training the layer needs, and the forces of an energy built on
+ * it (technical summary section 2.2; the message steps of section 2.1).  With ds_ij, dq_i, dk_j as in e2a_attention_bwd, the edge cotangent
  * alpha_ij G_i, x_ij = D_ij h_j, y = SO2(x), dyhat = D_ij (alpha_ij G_i),
  * rho_ij[l][c] = sum_k e_k(r_ij) W_rad[k][l][c] and dy = rho_ij dyhat:
  *   dW_q = sum_i h_{i,0}^T dq_i,   dW_k = sum_j h_{j,0}^T dk_j,
@@ -257,7 +257,12 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
  *   per m: dW0 = sum X0^T dY0,  dW1 = sum Xp^T dYp + Xm^T dYm,
  *          dW2 = sum Xp^T dYm - Xm^T dYp
  * (X0, Xp, Xm the rows m = 0, +m, -m of x laid out as in w_so2's blocks).
- * Gradients with respect to positions are not computed.
+ * Positions (neighbour graph held fixed): each edge vector r_ij = x_j - x_i
+ * enters through its length (the radial basis) and its direction (the
+ * Wigner blocks); with T_a the derivative along a rotation of r_hat about
+ * axis a (the frame turned with it, dD^l = D^l(R(1 - [e_a]x)) - D^l) and
+ * s = sum_{l,c} dL/drho[l][c] drho[l][c]/dr,
+ *   dL/dr_ij = s r_hat + (T x r_hat) / |r|,   dL/dx_j += dL/dr_ij, dL/dx_i -= dL/dr_ij.
  *
  *   args        as for e2a_attention_bwd (out and out_lse of the forward are
  *               required); workspace / workspace_bytes as
@@ -268,6 +273,7 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
  *   grad_w_q, grad_w_k   NULL or device f32 [C, C] (layout of w_q, w_k).
  *   grad_w_rad  NULL or device f32 [8, L+1, C].
  *   grad_w_so2  NULL or device f32 [e2a_so2_param_count(L, C)] (layout of w_so2).
+ *   grad_pos    NULL or device f32 [n_atoms, 3] (layout of pos).
  * Every output that is set is overwritten; at least one must be set.
  *
  * dL/dh and ds come from the same kernels as e2a_attention_bwd (variant as
@@ -282,7 +288,7 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
  */
 e2a_status e2a_attention_bwd_weights(const e2a_attn_args* args, const float* grad_out, float* grad_feat,
                                      float* grad_w_q, float* grad_w_k, float* grad_w_rad, float* grad_w_so2,
-                                     void* stream);
+                                     float* grad_pos, void* stream);
 
 #ifdef __cplusplus
 }

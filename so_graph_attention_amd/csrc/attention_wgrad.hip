@@ -114,6 +114,8 @@ struct GatherParams {
   int64_t e0, nb;   // the batch: edges e0 .. e0 + nb - 1 of the neighbour list
   BatchLayout bl;
   float* rbf;       // [B][8]
+  float* rbfd;      // if set: d e_k / d r, [B][8]
+  float* alpha;     // if set: the edges' attention weights, [B][H]
 };
 
 // Degree l of the gather: one (edge, channel) per work item reads the
@@ -198,11 +200,17 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
       radial_basis8(r, p.cutoff, e8);
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) p.rbf[b * 8 + kk] = e8[kk];
+      if (p.rbfd) {
+        radial_basis8_deriv(r, p.cutoff, e8);
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) p.rbfd[b * 8 + kk] = e8[kk];
+      }
       const float inv = 1.0f / sqrtf(static_cast<float>(dh));
       for (int h = 0; h < H; ++h) {
         float sv = 0.0f;
         for (int d = 0; d < dh; ++d) sv += p.q[(int64_t)i * C + h * dh + d] * p.k[(int64_t)j * C + h * dh + d];
         al[tid * H + h] = expf(sv * inv - p.lse[(int64_t)i * H + h]);
+        if (p.alpha) p.alpha[b * H + h] = al[tid * H + h];
       }
     }
   }
@@ -211,15 +219,17 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
 }
 
 // dy = rho dyhat in place and, when Y is set, drho[b][l][c] = sum_m
-// y[l,m][c] dyhat[l,m][c] summed into this range's part of dW_rad:
-// part[z][k][(l, c)] (+)= sum over the range's edges b of rbf[b][k] drho[b][l][c]
-// (added to what the slot holds from earlier batches when acc_parts is set).
+// y[l,m][c] dyhat[l,m][c]: when part is set, summed into this range's part of
+// dW_rad, part[z][k][(l, c)] (+)= sum over the range's edges b of
+// rbf[b][k] drho[b][l][c] (added to what the slot holds from earlier batches
+// when acc_parts is set); when drp is set, drp[b][(l, c)] = drho[b][l][c]
+// d rho[l][c] / d r, the edge length's share (rbfd = d e_k / d r).
 // One thread per (degree, channel) and range of edges (consecutive threads
 // take consecutive channels, so the row reads coalesce).
 template <int L, typename T>
 __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
-                         const T* __restrict__ w_rad, const float* __restrict__ Y, T* __restrict__ GT,
-                         float* __restrict__ part, bool acc_parts) {
+                         const float* __restrict__ rbfd, const T* __restrict__ w_rad, const float* __restrict__ Y,
+                         T* __restrict__ GT, float* __restrict__ part, bool acc_parts, float* __restrict__ drp) {
   const int lc = blockIdx.x * blockDim.x + threadIdx.x;
   const int z = blockIdx.y;
   if (lc >= (L + 1) * C) return;
@@ -244,13 +254,222 @@ __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const f
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) acc[kk] += rbf[b * 8 + kk] * dr;
+    if (drp) {
+      float dro = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) dro += rbfd[b * 8 + kk] * wr[kk];
+      drp[b * (L + 1) * C + lc] = dr * dro;
+    }
   }
-  if (Y)
+  if (part)
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       float* pp = part + ((int64_t)z * 8 + kk) * (L + 1) * C + lc;
       *pp = acc_parts ? *pp + acc[kk] : acc[kk];
     }
+}
+
+// ------------------------------------------------------------ positions ----
+// The layer depends on an edge vector r = x_j - x_i through its length (the
+// radial basis) and its direction (the Wigner blocks of the frame R).  The
+// frame is any rotation taking r_hat to z (the SO(2) mix commutes with
+// rotations about z), so turning r_hat by a small rotation w, r_hat ->
+// r_hat + w x r_hat, may be followed by R -> R (1 - [w]x), D^l -> D^l(R) +
+// dD^l with dR = -R [w]x: smooth everywhere, unlike the angles of R.  Then
+//   dL/dw_a = sum_l <dL/dD^l, dD^l/dw_a>,
+//   dL/dD^l[m][n] = sum_c dx[l,m][c] h_j[l,n][c] + yhat[l,m][c] alpha G_i[l,n][c]
+// (x = D h_j enters the mix, v = D^T yhat leaves it, yhat = rho y, dx =
+// SO2^T(rho dyhat)), and dL/dr = s r_hat + (T x r_hat) / |r| with
+// T_a = dL/dw_a and s = sum_{l,c} drho[l][c] d rho[l][c] / d r.
+struct ForceParams {
+  const float* pos;
+  const int32_t* col;
+  const int32_t* src;
+  const float* grad;    // G [N, K, C]
+  const float* alpha;   // [B][H]
+  const float* rbf;     // [B][8]
+  const float* Y;       // batch tensor: y = SO2(x), fp32
+  const float* dX;      // batch tensor: dx = SO2^T(dy), fp32
+  const float* drp;     // [B][(L+1) C]
+  float* gedge;         // [E][3]: dL/dr of every edge
+  float box[3];
+  int periodic;
+  int C, H;
+  int64_t e0;
+  BatchLayout bl;
+};
+
+// Degree l's share of dL/dD: the lane sums the products over its channels,
+// the wave sums the lanes, and lane 0 writes its wave's part.
+template <int L, int l, typename T>
+__device__ __forceinline__ void force_degree(const ForceParams& p, const T* __restrict__ feat,
+                                             const T* __restrict__ w_rad, int64_t b, int i, int j, float* part,
+                                             int tid) {
+  constexpr int K = (L + 1) * (L + 1);
+  constexpr int w = 2 * l + 1;
+  const int C = p.C, H = p.H, dh = C / H;
+  float P[w * w];
+#pragma unroll
+  for (int t = 0; t < w * w; ++t) P[t] = 0.0f;
+  for (int c = tid; c < C; c += blockDim.x) {
+    float rho = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) rho += p.rbf[b * 8 + kk] * load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
+    const float a = p.alpha[b * H + c / dh];
+    float dx[w], yh[w], hv[w], ag[w];
+#pragma unroll
+    for (int q = 0; q < w; ++q) {
+      const int64_t idx = batch_index(p.bl, L, C, b, l, q - l, c);
+      dx[q] = p.dX[idx];
+      yh[q] = rho * p.Y[idx];
+      hv[q] = load_as_f32(feat, (size_t)(((int64_t)j * K + l * l + q) * C + c));
+      ag[q] = a * p.grad[((int64_t)i * K + l * l + q) * C + c];
+    }
+#pragma unroll
+    for (int m = 0; m < w; ++m)
+#pragma unroll
+      for (int n = 0; n < w; ++n) P[m * w + n] += dx[m] * hv[n] + yh[m] * ag[n];
+  }
+#pragma unroll
+  for (int t = 0; t < w * w; ++t) {
+    float v = P[t];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    if ((tid & 63) == 0) part[(tid >> 6) * wig_size(L) + wig_off(l) + t] = v;
+  }
+  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, part, tid);
+}
+
+// One edge per workgroup of 128 threads (two waves).
+template <int L, typename T>
+__global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __restrict__ feat,
+                                                  const T* __restrict__ w_rad) {
+  constexpr int WS = wig_size(L);
+  __shared__ float D[4][WS];          // D and its three tangents dD/dw_a
+  __shared__ float part[2][WS];       // the two waves' shares of dL/dD
+  __shared__ float rad[2];
+  __shared__ float fr[4];             // r_hat, |r|
+  __shared__ int ij[2];
+  const int64_t b = blockIdx.x;
+  const int64_t e = p.e0 + b;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const int i = p.src[e], j = p.col[e];
+    ij[0] = i;
+    ij[1] = j;
+    float r3[3];
+    for (int d = 0; d < 3; ++d) {
+      float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * (int64_t)i + d];
+      if (p.periodic) {
+        if (dx > 0.5f * p.box[d]) dx -= p.box[d];
+        else if (dx < -0.5f * p.box[d]) dx += p.box[d];
+      }
+      r3[d] = dx;
+    }
+    const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
+    const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+    fr[0] = u[0];
+    fr[1] = u[1];
+    fr[2] = u[2];
+    fr[3] = r;
+    float R[3][3];
+    edge_rotation(u, R);
+    D[0][0] = 1.0f;
+    D[1][0] = D[2][0] = D[3][0] = 0.0f;
+    if constexpr (L >= 1) {
+      wigner_l1(R, &D[0][wig_off(1)], 3);
+      for (int a = 0; a < 3; ++a) {
+        // dR = -R [e_a]x, [e_a]x v = e_a x v
+        float dR[3][3];
+        for (int r0 = 0; r0 < 3; ++r0)
+          for (int c0 = 0; c0 < 3; ++c0) {
+            // ([e_a]x)[k][c0] = eps(k, a, c0)... column c0 of [e_a]x is e_a x e_c0
+            float v = 0.0f;
+            for (int k = 0; k < 3; ++k) {
+              const float ex = (k == (a + 1) % 3 && c0 == (a + 2) % 3) ? -1.0f
+                               : (k == (a + 2) % 3 && c0 == (a + 1) % 3) ? 1.0f : 0.0f;
+              v += R[r0][k] * ex;
+            }
+            dR[r0][c0] = -v;
+          }
+        wigner_l1(dR, &D[1 + a][wig_off(1)], 3);
+      }
+    }
+  }
+  __syncthreads();
+  // degrees 2 .. L: the recursion is bilinear in D^1 and D^{l-1}, so each
+  // tangent is ir(dD^1, D^{l-1}) + ir(D^1, dD^{l-1})
+  for (int l = 2; l <= L; ++l) {
+    const int w = 2 * l + 1, wp = 2 * l - 1;
+    for (int t = tid; t < 4 * w * w; t += blockDim.x) {
+      const int comp = t / (w * w), mn = t - comp * w * w;
+      const int m = mn / w - l, n = mn % w - l;
+      auto r1v = [&](int a, int c) { return D[0][wig_off(1) + (a + 1) * 3 + (c + 1)]; };
+      auto rpv = [&](int a, int c) { return D[0][wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
+      float v;
+      if (comp == 0) {
+        v = ir_entry(l, m, n, r1v, rpv);
+      } else {
+        const float* dt = D[comp];
+        auto r1d = [&](int a, int c) { return dt[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
+        auto rpd = [&](int a, int c) { return dt[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
+        v = ir_entry(l, m, n, r1d, rpv) + ir_entry(l, m, n, r1v, rpd);
+      }
+      D[comp][wig_off(l) + mn] = v;
+    }
+    __syncthreads();
+  }
+  force_degree<L, 0, T>(p, feat, w_rad, b, ij[0], ij[1], &part[0][0], tid);
+  // the edge length's share
+  {
+    float sv = 0.0f;
+    for (int c = tid; c < p.C; c += blockDim.x)
+      for (int l = 0; l <= L; ++l) sv += p.drp[b * (L + 1) * p.C + l * p.C + c];
+    for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
+    if ((tid & 63) == 0) rad[tid >> 6] = sv;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float T3[3] = {0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < WS; ++t) {
+      const float g = part[0][t] + part[1][t];
+      T3[0] += g * D[1][t];
+      T3[1] += g * D[2][t];
+      T3[2] += g * D[3][t];
+    }
+    const float s = rad[0] + rad[1];
+    const float* u = fr;
+    const float ir = 1.0f / fr[3];
+    // (T x u) / |r| + s u
+    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + s * u[0];
+    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + s * u[1];
+    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
+  }
+}
+
+// dL/dx_a = sum over edges (i, a) of dL/dr minus sum over edges (a, j): the
+// edges (i, a) are found in the ascending rows of a's neighbours (the graph
+// is symmetric), one atom per thread, in a fixed order.
+__global__ void k_pos_assemble(const int64_t* __restrict__ row_ptr, const int32_t* __restrict__ col, int64_t n,
+                               const float* __restrict__ gedge, float* __restrict__ grad_pos) {
+  const int64_t a = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (a >= n) return;
+  float g[3] = {0.0f, 0.0f, 0.0f};
+  for (int64_t e = row_ptr[a]; e < row_ptr[a + 1]; ++e) {
+    const int i = col[e];
+    int64_t lo = row_ptr[i], hi = row_ptr[i + 1];
+    const int64_t end = hi;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (col[mid] < a) lo = mid + 1;
+      else hi = mid;
+    }
+    for (int d = 0; d < 3; ++d) {
+      g[d] -= gedge[e * 3 + d];
+      if (lo < end && col[lo] == a) g[d] += gedge[lo * 3 + d];
+    }
+  }
+  for (int d = 0; d < 3; ++d) grad_pos[a * 3 + d] = g[d];
 }
 
 // ---------------------------------------------------------------- GEMMs ----
@@ -596,11 +815,13 @@ Gemm make_gemm(const void* A, int64_t sam, int64_t sak, const void* B, int64_t s
 }
 
 struct WgWs {
-  size_t src, X, GT, Y, rbf, part, dwpart, rhopart, wt, total;
+  size_t src, X, GT, Y, rbf, part, dwpart, rhopart, wt;
+  size_t rbfd, alpha, drp, dX, gedge;   // position gradient only
+  size_t total;
   int64_t B, part_floats;
 };
 
-WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C) {
+WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   WgWs w{};
   const int64_t B = e < kWgBatch ? (e > 0 ? e : 1) : kWgBatch;
   const int64_t per = B * (int64_t)(L + 1) * (L + 1) * C;   // elements of one batch tensor
@@ -620,6 +841,11 @@ WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C) {
   int64_t so2 = 0;
   for (int m = 0; m <= L; ++m) so2 += (m == 0 ? 1 : 2) * ((int64_t)(L + 1 - m) * C) * ((int64_t)(L + 1 - m) * C);
   w.wt = take(sizeof(float) * (size_t)so2);   // sized for fp32 storage
+  w.rbfd = take(sizeof(float) * 8 * (size_t)B);
+  w.alpha = take(sizeof(float) * (size_t)B * H);
+  w.drp = take(sizeof(float) * (size_t)B * K0);
+  w.dX = take(sizeof(float) * (size_t)per);
+  w.gedge = take(sizeof(float) * 3 * (size_t)(e > 0 ? e : 1));
   w.total = off;
   w.B = B;
   w.part_floats = pf;
@@ -634,7 +860,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
   const int C = a->C, H = a->H;
   const int64_t n = a->n_atoms, E = a->n_edges;
   const int64_t K0 = (int64_t)(L + 1) * C;
-  const WgWs W = wg_ws_layout(n, E, L, C);
+  const WgWs W = wg_ws_layout(n, E, L, C, H);
   char* wb = static_cast<char*>(pl.ws);
   float* part = reinterpret_cast<float*>(wb + W.part);
   auto zero = [&](float* p, int64_t cnt) {
@@ -647,6 +873,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
   zero(pl.w_k, (int64_t)C * C);
   zero(pl.w_rad, 8 * K0);
   zero(pl.w_so2, so2_count);
+  zero(pl.pos, 3 * n);
   E2A_LAUNCH_CHECK();
   const T* feat = static_cast<const T*>(a->feat);
   // dW_q = sum_i h_{i,0}^T dq_i, dW_k likewise (A(m, k) = h_k[0][m])
@@ -660,7 +887,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
                                                   part), W.part_floats, st);
     if (e != E2A_OK) return e;
   }
-  if ((!pl.w_rad && !pl.w_so2) || E == 0) return E2A_OK;
+  if ((!pl.w_rad && !pl.w_so2 && !pl.pos) || E == 0) return E2A_OK;
+  const bool need_y = pl.w_rad || pl.pos;   // drho needs SO2(x)
 
   int32_t* src = reinterpret_cast<int32_t*>(wb + W.src);
   k_edge_rows<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(a->row_ptr, n, src);
@@ -680,9 +908,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       o += (m == 0 ? 1 : 2) * km * km;
     }
   }
-  // W^T per block, for the Y products (only dW_rad needs Y)
+  // W^T per block, for the Y products
   T* wt = reinterpret_cast<T*>(wb + W.wt);
-  if (pl.w_rad)
+  if (need_y)
     for (int m = 0; m <= L; ++m) {
       const int64_t km = (int64_t)(L + 1 - m) * C;
       for (int w2 = 0; w2 < (m == 0 ? 1 : 2); ++w2) {
@@ -711,12 +939,14 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     gp.nb = nb;
     gp.bl = bl;
     gp.rbf = rbf;
+    gp.rbfd = pl.pos ? reinterpret_cast<float*>(wb + W.rbfd) : nullptr;
+    gp.alpha = pl.pos ? reinterpret_cast<float*>(wb + W.alpha) : nullptr;
     const size_t smem = sizeof(float) * kEB * (wig_size(L) + H);
     k_wg_gather<L, T><<<static_cast<unsigned>((nb + kEB - 1) / kEB), 256, smem, st>>>(gp, feat, X, GT);
     E2A_LAUNCH_CHECK();
-    // Y = SO2(X): Y0 = X0 W0; Yp = Xp W1 - Xm W2; Ym = Xp W2 + Xm W1 (only
-    // drho needs it)
-    for (int m = 0; pl.w_rad && m <= L; ++m) {
+    // Y = SO2(X): Y0 = X0 W0; Yp = Xp W1 - Xm W2; Ym = Xp W2 + Xm W1 (for
+    // drho and the rotate-out's share of the position gradient)
+    for (int m = 0; need_y && m <= L; ++m) {
       const int64_t km = (int64_t)(L + 1 - m) * C;
       const T* Xp = X + bl.moff[m];
       float* Yp = Y + bl.moff[m];
@@ -744,8 +974,10 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       const int64_t per = kRhoPer;
       const int64_t nz = (nb + per - 1) / per;
       const dim3 grid(static_cast<unsigned>((K0 + 255) / 256), static_cast<unsigned>(nz));
-      k_wg_rho<L, T><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, static_cast<const T*>(a->w_rad),
-                                           pl.w_rad ? Y : nullptr, GT, rhopart, e0 > 0);
+      k_wg_rho<L, T><<<grid, 256, 0, st>>>(
+          bl, nb, C, per, rbf, reinterpret_cast<const float*>(wb + W.rbfd), static_cast<const T*>(a->w_rad),
+          need_y ? Y : nullptr, GT, pl.w_rad ? rhopart : nullptr, e0 > 0,
+          pl.pos ? reinterpret_cast<float*>(wb + W.drp) : nullptr);
       E2A_LAUNCH_CHECK();
     }
     if (pl.w_so2) {
@@ -775,6 +1007,58 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         }
       }
     }
+    if (pl.pos) {
+      // dx = SO2^T(dy): dX0 = dY0 W0^T; dXp = dYp W1^T + dYm W2^T;
+      // dXm = -dYp W2^T + dYm W1^T (W read as [n][k]: contiguous along k)
+      float* dX = reinterpret_cast<float*>(wb + W.dX);
+      for (int m = 0; m <= L; ++m) {
+        const int64_t km = (int64_t)(L + 1 - m) * C;
+        const T* DYp = GT + bl.moff[m];
+        const T* W1 = wso2 + woff[m];
+        float* dXp = dX + bl.moff[m];
+        e2a_status e;
+        if (m == 0) {
+          e = gemm<T, T>(make_gemm(DYp, km, 1, W1, 1, km, nb, km, km, 1.0f, dXp, km, part, true), W.part_floats, st);
+          if (e != E2A_OK) return e;
+          continue;
+        }
+        const T* DYm = DYp + bl.B * km;
+        const T* W2 = W1 + km * km;
+        float* dXm = dXp + bl.B * km;
+        const struct { const T* dy; const T* w; float* x; float s; bool first; } terms[4] = {
+            {DYp, W1, dXp, 1.0f, true}, {DYm, W2, dXp, 1.0f, false}, {DYp, W2, dXm, -1.0f, true},
+            {DYm, W1, dXm, 1.0f, false}};
+        for (const auto& t : terms) {
+          e = gemm<T, T>(make_gemm(t.dy, km, 1, t.w, 1, km, nb, km, km, t.s, t.x, km, part, t.first),
+                         W.part_floats, st);
+          if (e != E2A_OK) return e;
+        }
+      }
+      ForceParams fp{};
+      fp.pos = a->pos;
+      fp.col = a->col;
+      fp.src = src;
+      fp.grad = pl.grad_out;
+      fp.alpha = reinterpret_cast<const float*>(wb + W.alpha);
+      fp.rbf = rbf;
+      fp.Y = Y;
+      fp.dX = dX;
+      fp.drp = reinterpret_cast<const float*>(wb + W.drp);
+      fp.gedge = reinterpret_cast<float*>(wb + W.gedge);
+      for (int d = 0; d < 3; ++d) fp.box[d] = pl.box[d];
+      fp.periodic = pl.periodic;
+      fp.C = C;
+      fp.H = H;
+      fp.e0 = e0;
+      fp.bl = bl;
+      k_wg_force<L, T><<<static_cast<unsigned>(nb), 128, 0, st>>>(fp, feat, static_cast<const T*>(a->w_rad));
+      E2A_LAUNCH_CHECK();
+    }
+  }
+  if (pl.pos) {
+    k_pos_assemble<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(
+        a->row_ptr, a->col, n, reinterpret_cast<const float*>(wb + W.gedge), pl.pos);
+    E2A_LAUNCH_CHECK();
   }
   if (pl.w_rad) {
     // the edge ranges' partials of dW_rad, added in order (the first batch
@@ -820,9 +1104,8 @@ e2a_status run_wgrad_dtype(const WgradPlan& pl, hipStream_t st) {
 }  // namespace
 
 size_t wgrad_workspace_bytes(int64_t n, int64_t e, int L, int C, int H, int dtype) {
-  (void)H;
   (void)dtype;
-  return wg_ws_layout(n, e, L, C).total;
+  return wg_ws_layout(n, e, L, C, H).total;
 }
 
 e2a_status launch_weight_grads(const WgradPlan& pl, hipStream_t s) {

@@ -303,11 +303,11 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
 
 e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_out, float* grad_feat,
                                      float* grad_w_q, float* grad_w_k, float* grad_w_rad, float* grad_w_so2,
-                                     void* stream) {
+                                     float* grad_pos, void* stream) {
   clear_error();
   e2a_status st = check_bwd_args(a, grad_out);
   if (st != E2A_OK) return st;
-  if (!grad_feat && !grad_w_q && !grad_w_k && !grad_w_rad && !grad_w_so2)
+  if (!grad_feat && !grad_w_q && !grad_w_k && !grad_w_rad && !grad_w_so2 && !grad_pos)
     return fail(E2A_ERR_INVALID_ARG, "no output requested");
   const WBwdWs ws = wbwd_ws_layout(a->n_atoms, a->n_edges, a->L, a->C, a->H);
   if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
@@ -322,7 +322,8 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
     // the softmax gradient ds (and dL/dh when asked for); dq, dk from it
     st = run_backward(a, grad_out, grad_feat, want_qk ? dq : nullptr, want_qk ? dk : nullptr, base, ws.b, s);
   } else {
-    // dW_rad and dW_so2 need only q and k (for the attention weights)
+    // dW_rad, dW_so2 and the positions need only q and k (for the
+    // attention weights)
     AttnPlan qk{};
     qk.a = a;
     qk.q = reinterpret_cast<float*>(base + ws.b.q);
@@ -341,6 +342,7 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   wp.w_k = grad_w_k;
   wp.w_rad = grad_w_rad;
   wp.w_so2 = grad_w_so2;
+  wp.pos = grad_pos;
   wp.ws = base + ws.wg;
   wp.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) wp.box[d] = a->box ? a->box[d] : 0.0f;

@@ -191,4 +191,20 @@ E2A_HD void radial_basis8(float r, float rc, float e[8]) {
   }
 }
 
+// d e_k / d r of radial_basis8: the Gaussian's slope times the envelope plus
+// the Gaussian times the envelope's slope, -(pi / 2 rc) sin(pi r / rc).
+E2A_HD void radial_basis8_deriv(float r, float rc, float de[8]) {
+  const float delta = rc / 7.0f;
+  const float gamma = 0.5f / (delta * delta);
+  const float a = 3.14159265358979f / rc;
+  const float env = 0.5f * (cosf(a * r) + 1.0f);
+  const float denv = -0.5f * a * sinf(a * r);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float t = r - float(k) * delta;
+    const float g = expf(-gamma * t * t);
+    de[k] = g * (-2.0f * gamma * t * env + denv);
+  }
+}
+
 }  // namespace e2a

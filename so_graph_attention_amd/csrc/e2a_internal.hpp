@@ -118,6 +118,7 @@ struct WgradPlan {
   float* w_k;
   float* w_rad;
   float* w_so2;
+  float* pos;              // dL/dx [N, 3] (optional)
   void* ws;                // wgrad_workspace_bytes(...)
   float box[3];
   int periodic;

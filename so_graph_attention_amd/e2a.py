@@ -85,7 +85,7 @@ def _load():
     lib.e2a_attention_bwd_weights.restype = ctypes.c_int32
     lib.e2a_attention_bwd_weights.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p, ctypes.c_void_p,
                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
-                                              ctypes.c_void_p]
+                                              ctypes.c_void_p, ctypes.c_void_p]
     return lib
 
 
@@ -293,17 +293,19 @@ def e2a_attention_bwd_weights_workspace_bytes(n_atoms: int, n_edges: int, L: int
 
 def e2a_attention_bwd_weights(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, *, L: int,
                               C: int, H: int, cutoff: float, box=None, variant: str = "auto", feat_grad: bool = True,
-                              weights=("w_q", "w_k", "w_rad", "w_so2"), workspace=None, stream=None):
+                              weights=("w_q", "w_k", "w_rad", "w_so2"), pos_grad: bool = False, workspace=None,
+                              stream=None):
     """Gradients of the layer with respect to its weights (those named in
-    ``weights``) and, with feat_grad, its node features, for grad_out = dL/do.
-    Returns a dict of fp32 tensors: "feat" [N,(L+1)^2,C], "w_q", "w_k" [C,C],
-    "w_rad" [8,L+1,C], "w_so2" (flat, the layout of w_so2)."""
+    ``weights``), with feat_grad its node features and with pos_grad the atom
+    positions, for grad_out = dL/do.  Returns a dict of fp32 tensors: "feat"
+    [N,(L+1)^2,C], "w_q", "w_k" [C,C], "w_rad" [8,L+1,C], "w_so2" (flat, the
+    layout of w_so2), "pos" [N,3]."""
     dev = pos.device
     n = pos.shape[0]
     K = (L + 1) ** 2
     shapes = {"feat": (n, K, C), "w_q": (C, C), "w_k": (C, C), "w_rad": (8, L + 1, C),
-              "w_so2": (e2a_so2_param_count(L, C),)}
-    want = (["feat"] if feat_grad else []) + list(weights)
+              "w_so2": (e2a_so2_param_count(L, C),), "pos": (n, 3)}
+    want = (["feat"] if feat_grad else []) + list(weights) + (["pos"] if pos_grad else [])
     for name in want:
         if name not in shapes:
             raise ValueError(f"unknown gradient {name!r}")
@@ -313,7 +315,7 @@ def e2a_attention_bwd_weights(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, o
                                 dtype=torch.uint8, device=dev)
     a, box_arr = _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff,
                            box, variant, workspace)
-    outs = [_ptr(res[name]) if name in res else None for name in ("feat", "w_q", "w_k", "w_rad", "w_so2")]
+    outs = [_ptr(res[name]) if name in res else None for name in ("feat", "w_q", "w_k", "w_rad", "w_so2", "pos")]
     _check(_lib.e2a_attention_bwd_weights(ctypes.byref(a), _ptr(grad_out), *outs, _stream(stream)))
     del box_arr
     return res

@@ -186,10 +186,12 @@ def test_weight_backward_rejects_on_host(kw, grads, status):
     other outputs NULL) checks its arguments before any launch."""
     kw = dict(out_lse=FAKE, **kw) if "out_lse" not in kw else kw
     a = attn_args(**kw)
-    st = B.lib().e2a_attention_bwd_weights(ctypes.byref(a), grads[0], grads[1], None, None, None, grads[2], None)
+    st = B.lib().e2a_attention_bwd_weights(ctypes.byref(a), grads[0], grads[1], None, None, None, grads[2], None,
+                                           None)
     assert st == status, (st, B.last_error_message())
     assert B.last_error_message()
-    assert B.lib().e2a_attention_bwd_weights(None, FAKE, FAKE, None, None, None, None, None) == B.E2A_ERR_INVALID_ARG
+    assert B.lib().e2a_attention_bwd_weights(None, FAKE, FAKE, None, None, None, None, None, None) == \
+        B.E2A_ERR_INVALID_ARG
 
 
 def test_weight_backward_workspace_query():

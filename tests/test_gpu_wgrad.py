@@ -1,5 +1,6 @@
-"""GPU weight gradients (e2a_attention_bwd_weights) vs the fp64 oracle's
-attention_weight_backward on the same seeded inputs and cotangent.
+"""GPU weight and position gradients (e2a_attention_bwd_weights) vs the fp64
+oracle's attention_weight_backward and attention_position_backward on the
+same seeded inputs and cotangent.
 
 The backward reads the forward's log-normaliser; these tests take it from
 the fp32 scalar forward (except where named), so that the comparison
@@ -152,3 +153,84 @@ def test_wgrad_deterministic_and_partial_requests(B):
         assert np.array_equal(part[name], full[name]), name
     qk = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_k",))
     assert np.array_equal(qk["w_k"], full["w_k"])
+
+
+def oracle_pos(w, rp, col, G, atoms=None):
+    return O.attention_position_backward(w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"),
+                                         w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G,
+                                         box=w.box, atoms=atoms)
+
+
+def check_pos(got, want, tol, tag):
+    err = rel_l2(got, want)
+    log(f"[wgrad] {tag} positions: rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= tol, err
+
+
+@pytest.mark.parametrize("L,C,H", [(0, 8, 2), (1, 8, 2), (2, 8, 2), (4, 8, 1)])
+def test_pos_f32_tiny_full(B, L, C, H):
+    """fp32 storage: every atom's position gradient of a 64-atom system
+    against the oracle's central differences (graph held fixed)."""
+    log(f"[wgrad] positions f32 tiny L={L}")
+    w = make_config("tiny", L=L, C=C, H=H)
+    rp, col, d, G = setup(w, seed=78)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference", feat_grad=False, weights=(), pos_grad=True)
+    check_pos(got["pos"], oracle_pos(w, rp, col, G), TOL_F32, f"f32 L={L}")
+
+
+def test_pos_f32_periodic_box(B):
+    log("[wgrad] positions f32 periodic box")
+    rng = np.random.default_rng(1517)
+    box = np.full(3, 9.0, dtype=np.float32)
+    pts = []
+    while len(pts) < 90:
+        p = rng.random(3) * 9.0
+        if all(np.linalg.norm((p - q + 4.5) % 9.0 - 4.5) >= 0.9 for q in pts):
+            pts.append(p)
+    w = make_config("tiny", L=2, C=8, H=2, geometry=(np.array(pts, dtype=np.float32), box, None, {}))
+    rp, col, d, G = setup(w, seed=79)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference", feat_grad=False, weights=(), pos_grad=True)
+    atoms = np.arange(0, 90, 6)
+    check_pos(got["pos"][atoms], oracle_pos(w, rp, col, G, atoms), TOL_F32, "f32 periodic")
+
+
+@pytest.mark.parametrize("L", [2, 4])
+def test_pos_bf16_tiny_sampled(B, L):
+    """bf16 storage, C = 128, H = 8 (matrix-core GEMMs), on 16 atoms."""
+    log(f"[wgrad] positions bf16 tiny L={L}")
+    w = make_config("tiny", L=L, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w, seed=80)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=(), pos_grad=True)
+    atoms = np.arange(0, 64, 4)
+    check_pos(got["pos"][atoms], oracle_pos(w, rp, col, G, atoms), TOL_BF16, f"bf16 L={L}")
+
+
+def test_pos_bf16_drug_sparse_cotangent(B):
+    """The drug-like workload (all its edges and batches on the GPU) with the
+    cotangent on 8 sampled destinations; the oracle's differences at those
+    atoms and at one neighbour of each."""
+    log("[wgrad] positions bf16 drug, sparse cotangent")
+    w = make_config("drug")
+    rp0, col0 = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    keep = sample_dest(rp0, 8, seed=32)
+    rp, col, d, G = setup(w, keep=keep)
+    out, lse = forward(B, w, d, variant="mfma")
+    got = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_so2",), pos_grad=True)
+    nbr = np.array([col[rp[i]] for i in keep if rp[i + 1] > rp[i]], dtype=np.int64)
+    atoms = np.unique(np.concatenate([keep, nbr]))
+    check_pos(got["pos"][atoms], oracle_pos(w, rp, col, G, atoms), TOL_BF16, "bf16 drug")
+
+
+def test_pos_deterministic_and_with_weights(B):
+    """Position gradients are bit-identical across calls and do not change
+    when the weight gradients are asked for in the same call."""
+    log("[wgrad] positions determinism")
+    w = make_config("tiny", L=3, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w, seed=81)
+    out, lse = forward(B, w, d)
+    a = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=(), pos_grad=True)
+    b = gpu_wgrad(B, w, d, out, lse, pos_grad=True)
+    assert np.array_equal(a["pos"], b["pos"])
