@@ -299,19 +299,20 @@ struct ForceParams {
   BatchLayout bl;
 };
 
-// Degree l's share of dL/dD: the lane sums the products over its channels,
-// the wave sums the lanes, and lane 0 writes its wave's part.
+// Degree l's share of dL/dD for the wave's edge: the lane sums the products
+// over its channels (every 64th), the wave sums the lanes, and lane 0 writes
+// dL/dD[l][m][n] to part.
 template <int L, int l, typename T>
 __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __restrict__ feat,
                                              const T* __restrict__ w_rad, int64_t b, int i, int j, float* part,
-                                             int tid) {
+                                             int lane) {
   constexpr int K = (L + 1) * (L + 1);
   constexpr int w = 2 * l + 1;
   const int C = p.C, H = p.H, dh = C / H;
   float P[w * w];
 #pragma unroll
   for (int t = 0; t < w * w; ++t) P[t] = 0.0f;
-  for (int c = tid; c < C; c += blockDim.x) {
+  for (int c = lane; c < C; c += 64) {
     float rho = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) rho += p.rbf[b * 8 + kk] * load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
@@ -335,28 +336,32 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
     float v = P[t];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if ((tid & 63) == 0) part[(tid >> 6) * wig_size(L) + wig_off(l) + t] = v;
+    if (lane == 0) part[wig_off(l) + t] = v;
   }
-  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, part, tid);
+  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, part, lane);
 }
 
-// One edge per workgroup of 128 threads (two waves).
+// One edge per wave, four per workgroup.  Lane 0 sets up the frame, D^1 and
+// its tangents; the degrees 2 .. L follow with the wave's lanes sharing the
+// entries; then the products, summed over the channels within the wave.
+constexpr int kForceEdges = 4;
 template <int L, typename T>
-__global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __restrict__ feat,
-                                                  const T* __restrict__ w_rad) {
+__global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, int64_t nb, const T* __restrict__ feat,
+                                                               const T* __restrict__ w_rad) {
   constexpr int WS = wig_size(L);
-  __shared__ float D[4][WS];          // D and its three tangents dD/dw_a
-  __shared__ float part[2][WS];       // the two waves' shares of dL/dD
-  __shared__ float rad[2];
-  __shared__ float fr[4];             // r_hat, |r|
-  __shared__ int ij[2];
-  const int64_t b = blockIdx.x;
+  __shared__ float Ds[kForceEdges][4][WS];   // D and its three tangents dD/dw_a
+  __shared__ float parts[kForceEdges][WS];   // dL/dD
+  __shared__ float fr[kForceEdges][4];       // r_hat, |r|
+  __shared__ int ijs[kForceEdges][2];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t b = (int64_t)blockIdx.x * kForceEdges + wv;
+  const bool live = b < nb;                  // every wave still takes part in the barriers
   const int64_t e = p.e0 + b;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
+  float (*D)[WS] = Ds[wv];
+  if (lane == 0 && live) {
     const int i = p.src[e], j = p.col[e];
-    ij[0] = i;
-    ij[1] = j;
+    ijs[wv][0] = i;
+    ijs[wv][1] = j;
     float r3[3];
     for (int d = 0; d < 3; ++d) {
       float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * (int64_t)i + d];
@@ -368,10 +373,10 @@ __global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __rest
     }
     const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
     const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
-    fr[0] = u[0];
-    fr[1] = u[1];
-    fr[2] = u[2];
-    fr[3] = r;
+    fr[wv][0] = u[0];
+    fr[wv][1] = u[1];
+    fr[wv][2] = u[2];
+    fr[wv][3] = r;
     float R[3][3];
     edge_rotation(u, R);
     D[0][0] = 1.0f;
@@ -379,11 +384,10 @@ __global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __rest
     if constexpr (L >= 1) {
       wigner_l1(R, &D[0][wig_off(1)], 3);
       for (int a = 0; a < 3; ++a) {
-        // dR = -R [e_a]x, [e_a]x v = e_a x v
+        // dR = -R [e_a]x, ([e_a]x)[k][c] = eps(k, a, c)
         float dR[3][3];
         for (int r0 = 0; r0 < 3; ++r0)
           for (int c0 = 0; c0 < 3; ++c0) {
-            // ([e_a]x)[k][c0] = eps(k, a, c0)... column c0 of [e_a]x is e_a x e_c0
             float v = 0.0f;
             for (int k = 0; k < 3; ++k) {
               const float ex = (k == (a + 1) % 3 && c0 == (a + 2) % 3) ? -1.0f
@@ -401,7 +405,7 @@ __global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __rest
   // tangent is ir(dD^1, D^{l-1}) + ir(D^1, dD^{l-1})
   for (int l = 2; l <= L; ++l) {
     const int w = 2 * l + 1, wp = 2 * l - 1;
-    for (int t = tid; t < 4 * w * w; t += blockDim.x) {
+    for (int t = lane; live && t < 4 * w * w; t += 64) {
       const int comp = t / (w * w), mn = t - comp * w * w;
       const int m = mn / w - l, n = mn % w - l;
       auto r1v = [&](int a, int c) { return D[0][wig_off(1) + (a + 1) * 3 + (c + 1)]; };
@@ -419,31 +423,30 @@ __global__ void __launch_bounds__(128) k_wg_force(ForceParams p, const T* __rest
     }
     __syncthreads();
   }
-  force_degree<L, 0, T>(p, feat, w_rad, b, ij[0], ij[1], &part[0][0], tid);
+  if (!live) return;
+  force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], parts[wv], lane);
   // the edge length's share
-  {
-    float sv = 0.0f;
-    for (int c = tid; c < p.C; c += blockDim.x)
-      for (int l = 0; l <= L; ++l) sv += p.drp[b * (L + 1) * p.C + l * p.C + c];
-    for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
-    if ((tid & 63) == 0) rad[tid >> 6] = sv;
+  float sv = 0.0f;
+  for (int c = lane; c < p.C; c += 64)
+    for (int l = 0; l <= L; ++l) sv += p.drp[b * (L + 1) * p.C + l * p.C + c];
+  for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
+  // T_a = <dL/dD, dD/dw_a>: the lanes share the entries, then the wave sums
+  float T3[3] = {0.0f, 0.0f, 0.0f};
+  for (int t = lane; t < WS; t += 64) {
+    const float g = parts[wv][t];
+    T3[0] += g * D[1][t];
+    T3[1] += g * D[2][t];
+    T3[2] += g * D[3][t];
   }
-  __syncthreads();
-  if (tid == 0) {
-    float T3[3] = {0.0f, 0.0f, 0.0f};
-    for (int t = 0; t < WS; ++t) {
-      const float g = part[0][t] + part[1][t];
-      T3[0] += g * D[1][t];
-      T3[1] += g * D[2][t];
-      T3[2] += g * D[3][t];
-    }
-    const float s = rad[0] + rad[1];
-    const float* u = fr;
-    const float ir = 1.0f / fr[3];
+  for (int a = 0; a < 3; ++a)
+    for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
+  if (lane == 0) {
+    const float* u = fr[wv];
+    const float ir = 1.0f / u[3];
     // (T x u) / |r| + s u
-    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + s * u[0];
-    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + s * u[1];
-    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
+    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + sv * u[0];
+    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + sv * u[1];
+    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + sv * u[2];
   }
 }
 
@@ -1051,7 +1054,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       fp.H = H;
       fp.e0 = e0;
       fp.bl = bl;
-      k_wg_force<L, T><<<static_cast<unsigned>(nb), 128, 0, st>>>(fp, feat, static_cast<const T*>(a->w_rad));
+      k_wg_force<L, T><<<static_cast<unsigned>((nb + kForceEdges - 1) / kForceEdges), 64 * kForceEdges, 0, st>>>(
+          fp, nb, feat, static_cast<const T*>(a->w_rad));
       E2A_LAUNCH_CHECK();
     }
   }
