@@ -384,18 +384,8 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
     if constexpr (L >= 1) {
       wigner_l1(R, &D[0][wig_off(1)], 3);
       for (int a = 0; a < 3; ++a) {
-        // dR = -R [e_a]x, ([e_a]x)[k][c] = eps(k, a, c)
         float dR[3][3];
-        for (int r0 = 0; r0 < 3; ++r0)
-          for (int c0 = 0; c0 < 3; ++c0) {
-            float v = 0.0f;
-            for (int k = 0; k < 3; ++k) {
-              const float ex = (k == (a + 1) % 3 && c0 == (a + 2) % 3) ? -1.0f
-                               : (k == (a + 2) % 3 && c0 == (a + 1) % 3) ? 1.0f : 0.0f;
-              v += R[r0][k] * ex;
-            }
-            dR[r0][c0] = -v;
-          }
+        frame_tangent(R, a, dR);
         wigner_l1(dR, &D[1 + a][wig_off(1)], 3);
       }
     }
@@ -408,16 +398,13 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
     for (int t = lane; live && t < 4 * w * w; t += 64) {
       const int comp = t / (w * w), mn = t - comp * w * w;
       const int m = mn / w - l, n = mn % w - l;
-      auto r1v = [&](int a, int c) { return D[0][wig_off(1) + (a + 1) * 3 + (c + 1)]; };
-      auto rpv = [&](int a, int c) { return D[0][wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
       float v;
       if (comp == 0) {
+        auto r1v = [&](int a, int c) { return D[0][wig_off(1) + (a + 1) * 3 + (c + 1)]; };
+        auto rpv = [&](int a, int c) { return D[0][wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
         v = ir_entry(l, m, n, r1v, rpv);
       } else {
-        const float* dt = D[comp];
-        auto r1d = [&](int a, int c) { return dt[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
-        auto rpd = [&](int a, int c) { return dt[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
-        v = ir_entry(l, m, n, r1d, rpv) + ir_entry(l, m, n, r1v, rpd);
+        v = wigner_tangent_entry(l, m, n, D[0], D[comp]);
       }
       D[comp][wig_off(l) + mn] = v;
     }

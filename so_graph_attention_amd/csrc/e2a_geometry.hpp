@@ -167,6 +167,31 @@ E2A_HD void wigner_blocks(const float R[3][3], float* D) {
   }
 }
 
+// The frame's change when r_hat turns about axis a and the frame turns with
+// it: R -> R (1 - t [e_a]x), so dR/dt = -R [e_a]x with ([e_a]x)[k][c] = eps(k, a, c).
+E2A_HD void frame_tangent(const float R[3][3], int a, float dR[3][3]) {
+  const int a1 = (a + 1) % 3, a2 = (a + 2) % 3;
+  for (int r = 0; r < 3; ++r) {
+    // (R [e_a]x)[r][c] = sum_k R[r][k] eps(k, a, c): +R[r][a2] at c = a1, -R[r][a1] at c = a2
+    dR[r][a] = 0.0f;
+    dR[r][a1] = -R[r][a2];
+    dR[r][a2] = R[r][a1];
+  }
+}
+
+// Entry (m, n) of block l >= 2 of a tangent of the Wigner blocks.  The
+// recursion is bilinear in D^1 and D^{l-1}, so the tangent is
+// ir(dD^1, D^{l-1}) + ir(D^1, dD^{l-1}); D and dD hold blocks 0 .. l-1 at
+// wig_off.
+E2A_HD float wigner_tangent_entry(int l, int m, int n, const float* D, const float* dD) {
+  const int wp = 2 * l - 1;
+  auto r1v = [&](int a, int c) { return D[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
+  auto rpv = [&](int a, int c) { return D[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
+  auto r1d = [&](int a, int c) { return dD[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
+  auto rpd = [&](int a, int c) { return dD[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
+  return ir_entry(l, m, n, r1d, rpv) + ir_entry(l, m, n, r1v, rpd);
+}
+
 // Runtime-L front end of wigner_blocks.
 E2A_HD void wigner_blocks_rt(int L, const float R[3][3], float* D) {
   switch (L) {

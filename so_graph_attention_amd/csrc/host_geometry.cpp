@@ -57,4 +57,33 @@ void e2a_host_radial_basis8(const float* r, int n, float rc, float* out) {
   for (int e = 0; e < n; ++e) e2a::radial_basis8(r[e], rc, out + 8 * e);
 }
 
+void e2a_host_radial_basis8_deriv(const float* r, int n, float rc, float* out) {
+  for (int e = 0; e < n; ++e) e2a::radial_basis8_deriv(r[e], rc, out + 8 * e);
+}
+
+// The three tangents of the Wigner blocks for the frame turned about x, y, z
+// (the position gradient's form): dD_out[(e * 3 + a) * wig_size(L) + ...].
+void e2a_host_wigner_tangents(int L, const float* R_in, int n, float* dD_out) {
+  const int sz = e2a::wig_size(L);
+  float D[e2a::wig_size(4)];
+  for (int e = 0; e < n; ++e) {
+    float R[3][3];
+    for (int a = 0; a < 3; ++a)
+      for (int b = 0; b < 3; ++b) R[a][b] = R_in[9 * e + 3 * a + b];
+    e2a::wigner_blocks_rt(L, R, D);
+    for (int a = 0; a < 3; ++a) {
+      float* dD = dD_out + (size_t)(e * 3 + a) * sz;
+      dD[0] = 0.0f;
+      if (L < 1) continue;
+      float dR[3][3];
+      e2a::frame_tangent(R, a, dR);
+      e2a::wigner_l1(dR, dD + e2a::wig_off(1), 3);
+      for (int l = 2; l <= L; ++l)
+        for (int m = -l; m <= l; ++m)
+          for (int k = -l; k <= l; ++k)
+            dD[e2a::wig_off(l) + (m + l) * (2 * l + 1) + (k + l)] = e2a::wigner_tangent_entry(l, m, k, D, dD);
+    }
+  }
+}
+
 }

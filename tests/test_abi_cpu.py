@@ -268,3 +268,49 @@ def test_host_radial_basis_matches_oracle(hg):
     e = np.zeros((97, 8), dtype=np.float32)
     hg.e2a_host_radial_basis8(_cp(r), 97, ctypes.c_float(5.0), _cp(e))
     assert np.max(np.abs(e - O.radial_basis(r.astype(np.float64), 5.0))) < 2e-6
+
+
+def test_host_radial_basis_derivative_matches_oracle(hg):
+    """radial_basis8_deriv (the position gradient's edge-length factor) against
+    fourth-order central differences of the oracle's basis in fp64."""
+    r = np.ascontiguousarray(np.linspace(0.5, 4.99, 97), dtype=np.float32)
+    de = np.zeros((97, 8), dtype=np.float32)
+    hg.e2a_host_radial_basis8_deriv(_cp(r), 97, ctypes.c_float(5.0), _cp(de))
+    r64, h = r.astype(np.float64), 1e-4
+    f = lambda x: O.radial_basis(x, 5.0)
+    want = (-f(r64 + 2 * h) + 8 * f(r64 + h) - 8 * f(r64 - h) + f(r64 - 2 * h)) / (12 * h)
+    assert np.max(np.abs(de - want)) <= 2e-5 * np.max(np.abs(want))
+
+
+def test_host_wigner_tangents_match_oracle(hg):
+    """The three tangents of D^0..D^4 for the frame turned about x, y, z
+    (R -> R exp(-t [e_a]x)), as the position gradient forms them, against
+    central differences of the oracle's fp64 Wigner blocks; the edges include
+    both poles, where the frame's angles are singular."""
+    L = 4
+    rng = np.random.default_rng(44)
+    u = rng.standard_normal((60, 3))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u[:2] = [[0, 0, 1], [0, 0, -1]]
+    R = O.edge_rotation(u)
+    R32 = np.ascontiguousarray(R, dtype=np.float32)
+    nw = sum((2 * l + 1) ** 2 for l in range(L + 1))
+    dD = np.zeros((60, 3, nw), dtype=np.float32)
+    hg.e2a_host_wigner_tangents(L, _cp(R32), 60, _cp(dD))
+
+    def turn(a, t):
+        K = np.zeros((3, 3))
+        K[(a + 2) % 3, (a + 1) % 3], K[(a + 1) % 3, (a + 2) % 3] = 1.0, -1.0   # [e_a]x
+        return np.eye(3) + np.sin(t) * K + (1 - np.cos(t)) * (K @ K)          # exp(t [e_a]x)
+
+    h = 1e-4
+    R64 = R32.astype(np.float64)
+    for a in range(3):
+        off = 0
+        for l in range(L + 1):
+            k = 2 * l + 1
+            f = lambda t: O.wigner_d(l, R64 @ turn(a, -t))
+            want = (-f(2 * h) + 8 * f(h) - 8 * f(-h) + f(-2 * h)) / (12 * h)
+            got = dD[:, a, off:off + k * k].reshape(-1, k, k)
+            assert np.max(np.abs(got - want)) <= 2e-5 * max(1.0, np.max(np.abs(want))), (a, l)
+            off += k * k
