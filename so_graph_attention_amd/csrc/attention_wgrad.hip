@@ -1,5 +1,7 @@
-// Weight gradients of the fused layer: dL/dW_q, dL/dW_k, dL/dW_rad and the
-// per-m SO(2) blocks dL/dW_so2, for a cotangent G = dL/do.
+// Weight and position gradients of the fused layer: dL/dW_q, dL/dW_k,
+// dL/dW_rad, the per-m SO(2) blocks dL/dW_so2 and dL/dx, for a cotangent
+// G = dL/do (the position gradient's own steps are described with its
+// kernels below).
 //
 // arXiv 2601.16622, technical summary section 2.1 (the EAAS message: rotate
 // in, per-m SO(2) mix, radial scale, rotate out) and section 2.2 (attention
@@ -44,12 +46,6 @@ __device__ __forceinline__ void store_as<float>(float* p, int64_t i, float v) {
 template <>
 __device__ __forceinline__ void store_as<uint16_t>(uint16_t* p, int64_t i, float v) {
   p[i] = f32_to_bf16_rne(v);
-}
-
-__device__ __forceinline__ int degree_of(int comp) {
-  int l = 0;
-  while ((l + 1) * (l + 1) <= comp) ++l;
-  return l;
 }
 
 // Element offsets of the per-m matrices in one batch tensor.
@@ -164,7 +160,6 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
 template <int L, typename T>
 __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __restrict__ feat, T* __restrict__ X,
                                                    T* __restrict__ GT) {
-  constexpr int K = (L + 1) * (L + 1);
   constexpr int WS = wig_size(L);
   extern __shared__ float sm[];
   float* D = sm;                       // [kEB][WS]
