@@ -35,7 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int64_t kWgBatch = 65536;   // edges per batch
 constexpr int kEB = 16;               // edges per gather workgroup
-constexpr int64_t kRhoPer = 32;       // edges per k_wg_rho range
+constexpr int64_t kRhoPer = 8;        // edges per k_wg_rho range
 
 template <typename T>
 __device__ __forceinline__ void store_as(T* p, int64_t i, float v);
