@@ -234,3 +234,29 @@ def test_pos_deterministic_and_with_weights(B):
     a = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=(), pos_grad=True)
     b = gpu_wgrad(B, w, d, out, lse, pos_grad=True)
     assert np.array_equal(a["pos"], b["pos"])
+
+
+def test_wgrad_no_edges_and_isolated_atom(B):
+    """Atoms farther apart than the cutoff: no edges, so every weight and
+    position gradient is zero.  Then one atom set apart from a small cluster:
+    its position gradient is exactly zero and the rest match the oracle."""
+    log("[wgrad] no edges, isolated atom")
+    far = np.array([[1.0, 1.0, 1.0], [20.0, 1.0, 1.0], [1.0, 20.0, 1.0]], dtype=np.float32)
+    w = make_config("tiny", L=2, C=8, H=2, geometry=(far, None, None, {}))
+    rp, col, d, G = setup(w, seed=82)
+    assert col.size == 0
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference", pos_grad=True)
+    for name, v in got.items():
+        assert np.all(v == 0), name
+    rng = np.random.default_rng(83)
+    cluster = (rng.random((12, 3)) * 4.0).astype(np.float32)
+    pos = np.concatenate([cluster, np.array([[40.0, 40.0, 40.0]], dtype=np.float32)])
+    w = make_config("tiny", L=2, C=8, H=2, geometry=(pos, None, None, {}))
+    rp, col, d, G = setup(w, seed=84)
+    assert rp[-1] == rp[-2]   # the last atom has no neighbours
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, variant="reference", feat_grad=False, pos_grad=True)
+    assert np.all(got["pos"][-1] == 0)
+    check_pos(got["pos"], oracle_pos(w, rp, col, G), TOL_F32, "f32 cluster + isolated atom")
+    check(got, oracle_wgrad(w, rp, col, G), TOL_F32, "f32 cluster + isolated atom")
