@@ -63,6 +63,11 @@ constexpr int kMinPerWg = 4;       // destinations per workgroup, at least
 // pass carries the cotangents back along the reversed edges through the
 // transposed mix.
 constexpr int kFwd = 0, kBwdQ = 1, kBwdV = 2;
+// Radial pass of the weight gradient: the query pass's recomputation, with
+// dW_rad[k][l][c] = sum_edges e_k(r) alpha sum_m y[l,m][c] (D G_i)[l,m][c]
+// accumulated per workgroup instead of dalpha.
+constexpr int kBwdR = 4;
+constexpr int kMaxRadWg = 2048;   // radial pass: at most this many workgroups (partial slots)
 // The convolution stage: the forward with every edge weight 1.
 constexpr int kConv = 3;
 
@@ -232,6 +237,7 @@ struct NodeState {
   NodeAcc acc[L + 1];
   NodeAcc hi;
   float dal[16];   // query pass: dalpha partials of the lane's 16 edges crow(r, half), its channel
+  NodeAcc rad[3];  // radial pass: dW_rad of degree pairs (0, 1), (2, 3), (4): rows 0-7 even, 8-15 odd degree
 };
 template <int LO>
 __host__ __device__ constexpr bool packed_lo() { return 2 * LO + 1 <= 8; }
@@ -276,6 +282,7 @@ struct MfmaParams {
   const f16x8* gpk;        // query pass: scaled fp16 cotangent, [N][gslots][C] vectors of 8
   const float* gsc;        // query pass: per-atom inverse scale of gpk
   const float* gnorm;      // value pass: power of two that brings max |G| into [1, 2)
+  float* rad_part;         // radial pass: per-workgroup dW_rad partials [WG][8][(L+1) C], times gnorm
   float* ds;               // query pass: softmax gradient [E, H]
 };
 
@@ -471,6 +478,25 @@ __device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const L
   }
 }
 
+// Radial pass: degree LO's share of the chunk's dW_rad,
+// acc[k][c] += sum over the 8 edges EG + crow(q, h) of rbf[edge][k] t[edge][c],
+// with the rotate-out's k-slot layout (t in the GEMM result's registers as
+// the B operand, the basis values in place of the D rows as A).  Degrees
+// share accumulator tiles in pairs: an even degree uses rows 0-7 (k), an odd
+// one rows 8-15.
+template <int L, int LO, int EG>
+__device__ __forceinline__ void rad_acc(NodeState<L>& ns, const Smem& s, int lane, const f16x8 t) {
+  const int row = lane & 15;
+  const bool valid = (LO & 1) ? row >= 8 : row < 8;
+  const int k = row & 7, h = lane >> 5;
+  f16x8 a = {};
+  if (valid) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a[q] = static_cast<_Float16>(s.rbf[(EG + crow(q, h)) * 8 + k]);
+  }
+  rotate_out_step(ns.rad[LO / 2], a, t, (lane >> 4) & 1);
+}
+
 // 16-byte load of a B fragment through a buffer resource: the per-lane offset
 // stays in one VGPR and the k-step advances a scalar offset.
 __device__ __forceinline__ bf16x8 load_b(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
@@ -623,14 +649,14 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
     // radial-weight fragments of this block's output degrees, fetched now so
     // that they have landed by the epilogue
     f16x8 brad0 = zero8, brad1 = zero8;
-    if (MD != kBwdV && half == 0) {
+    if (MD != kBwdV && MD != kBwdR && half == 0) {
       brad0 = p.radpk[S::blk_lo(M, b, 0) * kC + c_own];
       if constexpr (M == 0 && S::has1(M, b)) brad1 = p.radpk[S::blk_lo(M, b, 1) * kC + c_own];
     }
     // query pass: the destinations' cotangent of the block's output degrees
     // (a pair of degrees below 4, or degree 4 alone: two operands at most)
     f16x8 gq0 = zero8, gq1 = zero8;
-    if constexpr (MD == kBwdQ) {
+    if constexpr (MD == kBwdQ || MD == kBwdR) {
       if constexpr (M == 0 && S::has1(M, b)) {
         grad_frags<L, S::blk_lo(M, b, 0)>(p, ln, lane, wave, gq0, gq1);
         grad_frags<L, S::blk_lo(M, b, 1)>(p, ln, lane, wave, gq1, gq1);
@@ -681,6 +707,14 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
             for (int r = 0; r < 16; ++r) u[r] = c0[r];
             rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
             rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+          } else if constexpr (MD == kBwdR) {
+            // t = alpha y (D G) per (edge, channel), alpha carrying the edge's scales
+            const f32x16 gt = rot_grad<L, lo, 0, 0>(s, ln, lane, f == 0 ? gq0 : gq1, gq1);
+            float t[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) t[r] = ln.alpha[r] * c0[r] * gt[r];
+            rad_acc<L, lo, 0>(ns, s, lane, to_vec8<f16x8>(t));
+            rad_acc<L, lo, 16>(ns, s, lane, to_vec8<f16x8>(t + 8));
           } else {
             const f16x8 brad = f == 0 ? brad0 : brad1;
             const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
@@ -718,6 +752,14 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
           }
           rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
           rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+        } else if constexpr (MD == kBwdR) {
+          // the edge's +M and -M rows summed: drho takes sum over m
+          const f32x16 gt = rot_grad<L, lo, M, t>(s, ln, lane, gq0, gq1);
+          float ts[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            ts[r] = ln.alpha[8 * t + r] * ((C1[r] - C2[r + 8]) * gt[r] + (C2[r] + C1[r + 8]) * gt[r + 8]);
+          rad_acc<L, lo, 16 * t>(ns, s, lane, to_vec8<f16x8>(ts));
         } else {
           const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
           if constexpr (MD == kBwdQ) {
@@ -894,6 +936,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 #pragma unroll
   for (int l = 0; l <= L; ++l) ns.acc[l] = NodeAcc{f32x4{}, f32x4{}};
   ns.hi = NodeAcc{f32x4{}, f32x4{}};
+#pragma unroll
+  for (int t = 0; t < 3; ++t) ns.rad[t] = NodeAcc{f32x4{}, f32x4{}};
   // the weight stream is the same for every chunk: prime it once
   WRing ring;
   {
@@ -908,6 +952,24 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int xcd = blockIdx.x & 7;
   const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
   stretch<L, MD>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
+  if constexpr (MD == kBwdR) {
+    // lane l holds rows 4 (l / 16) + i (basis k of an even or odd degree),
+    // channel 32 wave + l % 16 (a) and + 16 (b)
+    const int lane = tid0 & 63;
+#pragma unroll
+    for (int t = 0; t < (L + 2) / 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 4 * (lane >> 4) + i;
+        const int lo = 2 * t + (row >= 8 ? 1 : 0);
+        if (lo <= L) {
+          float* dst = p.rad_part + ((int64_t)blockIdx.x * 8 + (row & 7)) * (L + 1) * kC + lo * kC + 32 * wave +
+                       (lane & 15);
+          dst[0] = ns.rad[t].a[i];
+          dst[16] = ns.rad[t].b[i];
+        }
+      }
+  }
 }
 
 template <int L, int MD>
@@ -922,7 +984,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
   };
   // atoms without neighbours: zero output, log-normaliser -inf (the query
   // pass writes no output)
-  for (int64_t sl = s_lo + tid0 * step; MD != kBwdQ && sl < s_hi; sl += kThreads * step) {
+  for (int64_t sl = s_lo + tid0 * step; MD != kBwdQ && MD != kBwdR && sl < s_hi; sl += kThreads * step) {
     if (degree(sl) == 0) {
       const int64_t i = p.order[sl];
       for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
@@ -1064,11 +1126,11 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     if (tid < 2 * kH) {
       const int d = tid / kH, h = tid % kH;
       const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
-      if constexpr (MD == kBwdQ || MD == kBwdV) {
+      if constexpr (MD == kBwdQ || MD == kBwdV || MD == kBwdR) {
         // feature gradient: alpha from the forward's log-normaliser of the
         // destination of the forward edge (the neighbour, in the value pass)
         for (int e = b0; e < b1; ++e) {
-          const int64_t src = MD == kBwdQ ? (d == 0 ? ia : ib) : (int64_t)s.j[e];
+          const int64_t src = MD != kBwdV ? (d == 0 ? ia : ib) : (int64_t)s.j[e];
           s.alpha[e * kH + h] = expf(s.alpha[e * kH + h] - p.lse[src * kH + h]);
         }
         // the value pass carries the cotangent times gnorm (alpha scaled by
@@ -1138,14 +1200,24 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           ln.mk[g][q] = (t0 < nA ? 0x0000FFFFu : 0u) | (t0 + 1 < nA ? 0xFFFF0000u : 0u);
         }
       ln.flip = (lnr & 8) ? ~0u : 0u;
-      if constexpr (MD == kBwdQ) {
+      if constexpr (MD == kBwdQ || MD == kBwdR) {
         ln.nA = nA;
         ln.ia = ia;
         ln.ib = ib;
         ln.gsA = p.gsc[ia];
         ln.gsB = p.gsc[ib];
+      }
+      if constexpr (MD == kBwdQ) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) ns.dal[r] = 0.0f;
+      }
+      if constexpr (MD == kBwdR) {
+        // the rotated cotangent is in its atom's fp16 scale: undo it per
+        // edge, then apply the global power of two that keeps alpha y (D G)
+        // in fp16's range (divided out when the partials are added)
+        const float gn = *p.gnorm;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) ln.alpha[q] *= (crow(q, half) < nA ? ln.gsA : ln.gsB) * gn;
       }
     }
     do_block<L, 0, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
@@ -1171,6 +1243,8 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
         p.ds[g * kH + h] = s.alpha[e * kH + h] * (s.q[e * kH + h] - p.delta[id * kH + h]);
       }
       __syncthreads();
+    } else if constexpr (MD == kBwdR) {
+      // the radial pass only accumulates; the workgroup writes at the end
     } else if (a_done) {
       // finish A (and B if it also ended); B's partial state becomes A's
       finish_a<L>(p, s, ns, ia, tid, wave);
@@ -1323,7 +1397,8 @@ struct MfmaWs {
   size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
   size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
   size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales,
-  size_t gnorm;            // and the value pass's cotangent scale
+  size_t gnorm;            // and the value pass's cotangent scale,
+  size_t radpart;          // and the radial pass's per-workgroup dW_rad partials
   size_t total;
 };
 
@@ -1353,6 +1428,7 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
     m.gpk = take(16 * n * S::gslots * kC);
     m.gsc = take(sizeof(float) * n);
     m.gnorm = take(sizeof(float));
+    m.radpart = take(sizeof(float) * kMaxRadWg * 8 * (L + 1) * kC);
   }
   m.total = off;
   return m;
@@ -1571,7 +1647,64 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   return launch_bwd_qk(pl, st);
 }
 
+// dW_rad[k][l][c] = (sum over workgroups, in order, of their partials) / gnorm.
+template <int L>
+__global__ void k_rad_reduce(const float* __restrict__ part, int n_wg, const float* __restrict__ gnorm,
+                             float* __restrict__ w_rad) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int N = 8 * (L + 1) * kC;
+  if (t >= N) return;
+  float v = 0.0f;
+  for (int g = 0; g < n_wg; ++g) v += part[(int64_t)g * N + t];
+  w_rad[t] = v / *gnorm;
+}
+
+// dW_rad on the matrix cores: the cotangent's copies, then the radial pass
+// and the reduction of its partials.
+template <int L>
+e2a_status launch_radial_typed(const BwdPlan& pl, float* w_rad, hipStream_t st) {
+  const e2a_attn_args* a = pl.a;
+  const MfmaWs W = mfma_ws_layout<L>(a->n_atoms, true);
+  char* wb = static_cast<char*>(pl.mfma_ws);
+  e2a_status e = prepare<L>(a, W, wb, st);
+  if (e != E2A_OK) return e;
+  k_prep_grad<L><<<a->n_atoms, 256, 0, st>>>(pl.grad_out, reinterpret_cast<uint16_t*>(wb + W.gbf),
+                                             reinterpret_cast<f16x8*>(wb + W.gpk),
+                                             reinterpret_cast<float*>(wb + W.gsc));
+  E2A_LAUNCH_CHECK();
+  k_grad_norm<<<1, 1024, 0, st>>>(reinterpret_cast<const float*>(wb + W.gsc), a->n_atoms,
+                                  reinterpret_cast<float*>(wb + W.gnorm));
+  E2A_LAUNCH_CHECK();
+  MfmaParams p;
+  e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
+  if (e != E2A_OK) return e;
+  if (8 * p.wg_per_xcd > kMaxRadWg) p.wg_per_xcd = kMaxRadWg / 8;
+  p.q = pl.q;
+  p.k = pl.k;
+  p.lse = a->out_lse;
+  p.gpk = reinterpret_cast<const f16x8*>(wb + W.gpk);
+  p.gsc = reinterpret_cast<const float*>(wb + W.gsc);
+  p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
+  p.rad_part = reinterpret_cast<float*>(wb + W.radpart);
+  e = launch_mode<L, kBwdR>(p, st);
+  if (e != E2A_OK) return e;
+  constexpr int N = 8 * (L + 1) * kC;
+  k_rad_reduce<L><<<(N + 255) / 256, 256, 0, st>>>(p.rad_part, 8 * p.wg_per_xcd, p.gnorm, w_rad);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
 }  // namespace
+
+e2a_status launch_radial_mfma(const BwdPlan& pl, float* w_rad, hipStream_t s) {
+  switch (pl.a->L) {
+    case 1: return launch_radial_typed<1>(pl, w_rad, s);
+    case 2: return launch_radial_typed<2>(pl, w_rad, s);
+    case 3: return launch_radial_typed<3>(pl, w_rad, s);
+    case 4: return launch_radial_typed<4>(pl, w_rad, s);
+    default: return fail(E2A_ERR_UNSUPPORTED, "MFMA radial pass: L=%d", pl.a->L);
+  }
+}
 
 bool mfma_supported(int L, int C, int H, int dtype) {
   return L >= 1 && L <= 4 && C == kC && H == kH && dtype == E2A_DTYPE_BF16;

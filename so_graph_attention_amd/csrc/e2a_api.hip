@@ -331,6 +331,24 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
     st = launch_qk(qk, s);
   }
   if (st != E2A_OK) return st;
+  // dW_rad by the fused kernel's radial pass where the MFMA build covers the
+  // shape, so that the batches need no SO2(x); with the positions asked for
+  // they form SO2(x) anyway and take dW_rad along
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  const bool rad_mfma = grad_w_rad && !grad_pos &&
+                        (a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok));
+  if (rad_mfma) {
+    BwdPlan rp{};
+    rp.a = a;
+    rp.grad_out = grad_out;
+    rp.q = reinterpret_cast<float*>(base + ws.b.q);
+    rp.k = reinterpret_cast<float*>(base + ws.b.k);
+    rp.mfma_ws = base + ws.b.mfma;
+    rp.periodic = a->box != nullptr;
+    for (int d = 0; d < 3; ++d) rp.box[d] = a->box ? a->box[d] : 0.0f;
+    st = launch_radial_mfma(rp, grad_w_rad, s);
+    if (st != E2A_OK) return st;
+  }
   WgradPlan wp{};
   wp.a = a;
   wp.grad_out = grad_out;
@@ -340,7 +358,7 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   wp.dk = dk;
   wp.w_q = grad_w_q;
   wp.w_k = grad_w_k;
-  wp.w_rad = grad_w_rad;
+  wp.w_rad = rad_mfma ? nullptr : grad_w_rad;
   wp.w_so2 = grad_w_so2;
   wp.pos = grad_pos;
   wp.ws = base + ws.wg;

@@ -105,6 +105,8 @@ e2a_status launch_attention_backward(const BwdPlan& p, hipStream_t s);
 e2a_status launch_backward_mfma(const BwdPlan& p, hipStream_t s);
 e2a_status launch_bwd_delta(const BwdPlan& p, float* delta, hipStream_t s);
 e2a_status launch_bwd_qk(const BwdPlan& p, hipStream_t s);
+// dW_rad by the matrix-core radial pass (the MFMA build's shapes), into w_rad.
+e2a_status launch_radial_mfma(const BwdPlan& p, float* w_rad, hipStream_t s);
 
 // Weight gradients (attention_wgrad.hip), after ds and dq, dk are formed.
 struct WgradPlan {

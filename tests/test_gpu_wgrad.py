@@ -138,7 +138,8 @@ def test_wgrad_bf16_drug_sparse_cotangent(B):
 def test_wgrad_deterministic_and_partial_requests(B):
     """Two calls are bit-identical, and asking for some outputs only (which
     skips the query pass when neither dL/dh nor W_q, W_k is wanted) gives the
-    same values as the full call."""
+    same values as the full call; dW_rad from the edge batches (with the
+    positions) agrees with the fused kernel's radial pass."""
     log("[wgrad] determinism and partial requests")
     w = make_config("tiny", L=3, C=128, H=8, dtype="bf16")
     rp, col, d, G = setup(w)
@@ -153,6 +154,12 @@ def test_wgrad_deterministic_and_partial_requests(B):
         assert np.array_equal(part[name], full[name]), name
     qk = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_k",))
     assert np.array_equal(qk["w_k"], full["w_k"])
+    # with the positions asked for, dW_rad comes from the edge batches instead
+    # of the fused kernel's radial pass: the same gradient to the bf16 bound
+    withpos = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=("w_rad",), pos_grad=True)
+    err = rel_l2(withpos["w_rad"], full["w_rad"])
+    log(f"[wgrad] w_rad batches vs radial pass: rel-L2 {err:.3e}")
+    assert err <= TOL_BF16
 
 
 def oracle_pos(w, rp, col, G, atoms=None):
