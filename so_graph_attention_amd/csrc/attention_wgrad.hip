@@ -112,15 +112,16 @@ struct GatherParams {
   float* rbf;       // [B][8]
   float* rbfd;      // if set: d e_k / d r, [B][8]
   float* alpha;     // if set: the edges' attention weights, [B][H]
+  const void* w_rad;   // if set: the cotangent rows are written as dy = rho dyhat
 };
 
 // Degree l of the gather: one (edge, channel) per work item reads the
 // degree's 2l + 1 feature and cotangent entries once and writes all 2l + 1
-// rows of x and dyhat.
+// rows of x and dyhat (or dy = rho dyhat).
 template <int L, int l, typename T>
 __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __restrict__ feat, T* __restrict__ X,
-                                              T* __restrict__ GT, const float* D, const float* al, const int* ii,
-                                              const int* jj, int64_t b0, int tid) {
+                                              T* __restrict__ GT, const float* D, const float* al, const float* rb,
+                                              const int* ii, const int* jj, int64_t b0, int tid) {
   constexpr int K = (L + 1) * (L + 1);
   constexpr int WS = wig_size(L);
   constexpr int w = 2 * l + 1;
@@ -136,7 +137,14 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
       hv[n] = load_as_f32(hj, (size_t)n * C);
       gv[n] = gi[(int64_t)n * C];
     }
-    const float a = al[s * H + c / dh];
+    float a = al[s * H + c / dh];
+    if (p.w_rad) {
+      const T* wr = static_cast<const T*>(p.w_rad);
+      float rho = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) rho += rb[s * 8 + kk] * load_as_f32(wr, (size_t)(kk * (L + 1) + l) * C + c);
+      a *= rho;
+    }
     const float* Dl = D + s * WS + wig_off(l);
 #pragma unroll
     for (int mi = 0; mi < w; ++mi) {
@@ -151,12 +159,12 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
       store_as(GT, idx, g * a);
     }
   }
-  if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, ii, jj, b0, tid);
+  if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
-// x = D h_j and dyhat = D (alpha G_i) for kEB edges of the batch: the edges'
-// frames, Wigner blocks, radial bases and attention weights first (one
-// thread per edge), then the degrees one after another.
+// x = D h_j and dyhat = D (alpha G_i) (or rho dyhat) for kEB edges of the
+// batch: the edges' frames, Wigner blocks, radial bases and attention weights
+// first (one thread per edge), then the degrees one after another.
 template <int L, typename T>
 __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __restrict__ feat, T* __restrict__ X,
                                                    T* __restrict__ GT) {
@@ -164,6 +172,7 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
   extern __shared__ float sm[];
   float* D = sm;                       // [kEB][WS]
   float* al = D + kEB * WS;            // [kEB][H]
+  __shared__ float rb[kEB * 8];
   __shared__ int ii[kEB], jj[kEB];
   const int C = p.C, H = p.H, dh = C / H;
   const int64_t b0 = (int64_t)blockIdx.x * kEB;
@@ -194,7 +203,10 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
       float e8[8];
       radial_basis8(r, p.cutoff, e8);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) p.rbf[b * 8 + kk] = e8[kk];
+      for (int kk = 0; kk < 8; ++kk) {
+        p.rbf[b * 8 + kk] = e8[kk];
+        rb[tid * 8 + kk] = e8[kk];
+      }
       if (p.rbfd) {
         radial_basis8_deriv(r, p.cutoff, e8);
 #pragma unroll
@@ -210,7 +222,7 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
     }
   }
   __syncthreads();
-  gather_degree<L, 0, T>(p, feat, X, GT, D, al, ii, jj, b0, tid);
+  gather_degree<L, 0, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
 // dy = rho dyhat in place and, when Y is set, drho[b][l][c] = sum_m
@@ -761,13 +773,17 @@ e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
 }
 
 // The SO(2) weight gradients sum over every batch: each of the 2L + 1
-// matrices keeps kDwSplits(m) partials for the whole call, which every batch's
-// products add to, and one reduction at the end.
+// matrices keeps dw_splits(m) partials for the whole call, which every batch's
+// products add to, and one reduction at the end.  The product kernel holds
+// two workgroups per CU (192 VGPRs a lane), 512 on the 256 CUs, and a launch
+// with a few workgroups more than that takes a second round: the split count
+// fills the 512 slots without passing them (tiles x S <= 512).
+constexpr int64_t kGemmSlots = 512;
 int64_t dw_splits(int L, int C, int m) {
   const int64_t km = (int64_t)(L + 1 - m) * C;
   const int64_t t = (km + kTM - 1) / kTM;
-  int64_t S = (512 + t * t - 1) / (t * t);
-  return S > 64 ? 64 : S;
+  const int64_t S = kGemmSlots / (t * t);
+  return S < 1 ? 1 : S;
 }
 
 int64_t dw_part_floats(int L, int C) {
@@ -926,6 +942,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     gp.rbf = rbf;
     gp.rbfd = pl.pos ? reinterpret_cast<float*>(wb + W.rbfd) : nullptr;
     gp.alpha = pl.pos ? reinterpret_cast<float*>(wb + W.alpha) : nullptr;
+    // without drho in the batches dyhat serves only as dy: scale it here
+    gp.w_rad = need_y ? nullptr : a->w_rad;
     const size_t smem = sizeof(float) * kEB * (wig_size(L) + H);
     k_wg_gather<L, T><<<static_cast<unsigned>((nb + kEB - 1) / kEB), 256, smem, st>>>(gp, feat, X, GT);
     E2A_LAUNCH_CHECK();
@@ -955,7 +973,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     }
     // dy = rho dyhat, and dW_rad[k][(l, c)] += sum_b rbf[b][k] drho[b][(l, c)]
     // through per-range partials added in order
-    {
+    if (need_y) {
       const int64_t per = kRhoPer;
       const int64_t nz = (nb + per - 1) / per;
       const dim3 grid(static_cast<unsigned>((K0 + 255) / 256), static_cast<unsigned>(nz));
