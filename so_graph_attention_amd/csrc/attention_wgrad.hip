@@ -232,15 +232,16 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
 // when acc_parts is set); when drp is set, drp[b][(l, c)] = drho[b][l][c]
 // d rho[l][c] / d r, the edge length's share (rbfd = d e_k / d r).
 // One thread per (degree, channel) and range of edges (consecutive threads
-// take consecutive channels, so the row reads coalesce).
-template <int L, typename T>
-__global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
-                         const float* __restrict__ rbfd, const T* __restrict__ w_rad, const float* __restrict__ Y,
-                         T* __restrict__ GT, float* __restrict__ part, bool acc_parts, float* __restrict__ drp) {
-  const int lc = blockIdx.x * blockDim.x + threadIdx.x;
-  const int z = blockIdx.y;
-  if (lc >= (L + 1) * C) return;
-  const int l = lc / C, c = lc - l * C;
+// take consecutive channels, so the row reads coalesce); each edge's 2l + 1
+// rows are loaded together before any is written back.
+template <int L, int l, typename T>
+__device__ __forceinline__ void rho_degree(const BatchLayout& bl, int64_t nb, int C, int64_t per, int z, int c,
+                                           const float* __restrict__ rbf, const float* __restrict__ rbfd,
+                                           const T* __restrict__ w_rad, const float* __restrict__ Y,
+                                           T* __restrict__ GT, float* __restrict__ part, bool acc_parts,
+                                           float* __restrict__ drp) {
+  constexpr int w = 2 * l + 1;
+  const int lc = l * C + c;
   float wr[8], acc[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
@@ -249,15 +250,22 @@ __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const f
   }
   const int64_t b1 = (z + 1) * per < nb ? (z + 1) * per : nb;
   for (int64_t b = z * per; b < b1; ++b) {
+    float g[w], y[w];
+    int64_t idx[w];
+#pragma unroll
+    for (int q = 0; q < w; ++q) {
+      idx[q] = batch_index(bl, L, C, b, l, q - l, c);
+      g[q] = load_as_f32(GT, (size_t)idx[q]);
+      y[q] = Y ? Y[idx[q]] : 0.0f;
+    }
     float rho = 0.0f;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) rho += rbf[b * 8 + kk] * wr[kk];
     float dr = 0.0f;
-    for (int m = -l; m <= l; ++m) {
-      const int64_t idx = batch_index(bl, L, C, b, l, m, c);
-      const float g = load_as_f32(GT, (size_t)idx);
-      if (Y) dr += Y[idx] * g;
-      store_as(GT, idx, rho * g);
+#pragma unroll
+    for (int q = 0; q < w; ++q) {
+      dr += y[q] * g[q];
+      store_as(GT, idx[q], rho * g[q]);
     }
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) acc[kk] += rbf[b * 8 + kk] * dr;
@@ -274,6 +282,33 @@ __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const f
       float* pp = part + ((int64_t)z * 8 + kk) * (L + 1) * C + lc;
       *pp = acc_parts ? *pp + acc[kk] : acc[kk];
     }
+}
+
+// The thread's degree ld as a compile-time constant (uniform over a wave when
+// C is a multiple of 64).
+template <int L, int l, typename T>
+__device__ __forceinline__ void rho_dispatch(int ld, const BatchLayout& bl, int64_t nb, int C, int64_t per, int z,
+                                             int c, const float* __restrict__ rbf, const float* __restrict__ rbfd,
+                                             const T* __restrict__ w_rad, const float* __restrict__ Y,
+                                             T* __restrict__ GT, float* __restrict__ part, bool acc_parts,
+                                             float* __restrict__ drp) {
+  if (ld == l) {
+    rho_degree<L, l, T>(bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
+    return;
+  }
+  if constexpr (l < L)
+    rho_dispatch<L, l + 1, T>(ld, bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
+}
+
+template <int L, typename T>
+__global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
+                         const float* __restrict__ rbfd, const T* __restrict__ w_rad, const float* __restrict__ Y,
+                         T* __restrict__ GT, float* __restrict__ part, bool acc_parts, float* __restrict__ drp) {
+  const int lc = blockIdx.x * blockDim.x + threadIdx.x;
+  const int z = blockIdx.y;
+  if (lc >= (L + 1) * C) return;
+  const int l = lc / C, c = lc - l * C;
+  rho_dispatch<L, 0, T>(l, bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
 }
 
 // ------------------------------------------------------------ positions ----
