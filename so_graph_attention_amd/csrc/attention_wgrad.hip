@@ -383,9 +383,29 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
   if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, part, lane);
 }
 
+// Block l >= 2 of D (component 0) and of its three tangents dD/dw_a
+// (components 1 .. 3), one row per lane (4 (2l + 1) <= 36 lanes), every wave
+// of the workgroup reaching the barrier.  Component 0 takes the tangent rule
+// with D in place of dD, which gives twice the row of D^l (halved exactly),
+// so that the lanes of a wave run one path.
+template <int L, int l>
+__device__ __forceinline__ void force_wigner(float (*D)[wig_size(L)], bool live, int lane) {
+  constexpr int w = 2 * l + 1;
+  if (live && lane < 4 * w) {
+    const int comp = lane / w, m = lane - comp * w - l;
+    float o[w];
+    wigner_tangent_row<l>(m, D[0], D[comp], o);
+    const float h = comp == 0 ? 0.5f : 1.0f;
+#pragma unroll
+    for (int n = 0; n < w; ++n) D[comp][wig_off(l) + (m + l) * w + n] = o[n] * h;
+  }
+  __syncthreads();
+  if constexpr (l < L) force_wigner<L, l + 1>(D, live, lane);
+}
+
 // One edge per wave, four per workgroup.  Lane 0 sets up the frame, D^1 and
-// its tangents; the degrees 2 .. L follow with the wave's lanes sharing the
-// entries; then the products, summed over the channels within the wave.
+// its tangents; the degrees 2 .. L follow one row per lane; then the
+// products, summed over the channels within the wave.
 constexpr int kForceEdges = 4;
 template <int L, typename T>
 __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, int64_t nb, const T* __restrict__ feat,
@@ -433,25 +453,7 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
     }
   }
   __syncthreads();
-  // degrees 2 .. L: the recursion is bilinear in D^1 and D^{l-1}, so each
-  // tangent is ir(dD^1, D^{l-1}) + ir(D^1, dD^{l-1})
-  for (int l = 2; l <= L; ++l) {
-    const int w = 2 * l + 1, wp = 2 * l - 1;
-    for (int t = lane; live && t < 4 * w * w; t += 64) {
-      const int comp = t / (w * w), mn = t - comp * w * w;
-      const int m = mn / w - l, n = mn % w - l;
-      float v;
-      if (comp == 0) {
-        auto r1v = [&](int a, int c) { return D[0][wig_off(1) + (a + 1) * 3 + (c + 1)]; };
-        auto rpv = [&](int a, int c) { return D[0][wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
-        v = ir_entry(l, m, n, r1v, rpv);
-      } else {
-        v = wigner_tangent_entry(l, m, n, D[0], D[comp]);
-      }
-      D[comp][wig_off(l) + mn] = v;
-    }
-    __syncthreads();
-  }
+  if constexpr (L >= 2) force_wigner<L, 2>(D, live, lane);
   if (!live) return;
   force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], parts[wv], lane);
   // the edge length's share

@@ -179,17 +179,27 @@ E2A_HD void frame_tangent(const float R[3][3], int a, float dR[3][3]) {
   }
 }
 
-// Entry (m, n) of block l >= 2 of a tangent of the Wigner blocks.  The
-// recursion is bilinear in D^1 and D^{l-1}, so the tangent is
-// ir(dD^1, D^{l-1}) + ir(D^1, dD^{l-1}); D and dD hold blocks 0 .. l-1 at
-// wig_off.
-E2A_HD float wigner_tangent_entry(int l, int m, int n, const float* D, const float* dD) {
-  const int wp = 2 * l - 1;
-  auto r1v = [&](int a, int c) { return D[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
-  auto rpv = [&](int a, int c) { return D[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
-  auto r1d = [&](int a, int c) { return dD[wig_off(1) + (a + 1) * 3 + (c + 1)]; };
-  auto rpd = [&](int a, int c) { return dD[wig_off(l - 1) + (a + l - 1) * wp + (c + l - 1)]; };
-  return ir_entry(l, m, n, r1d, rpv) + ir_entry(l, m, n, r1v, rpd);
+// Row m of block l >= 2 of a tangent of the Wigner blocks.  The recursion is
+// bilinear in D^1 and D^{l-1}, so the tangent row is ir(dD^1, D^{l-1}) +
+// ir(D^1, dD^{l-1}); D and dD hold blocks 0 .. l-1 at wig_off.  Writes
+// out[n + l], n = -l..l.
+template <int l>
+E2A_HD void wigner_tangent_row(int m, const float* D, const float* dD, float* out) {
+  constexpr int w = 2 * l + 1, wp = 2 * l - 1;
+  float r1[3][3], d1[3][3];
+  for (int a = 0; a < 3; ++a)
+    for (int b = 0; b < 3; ++b) {
+      r1[a][b] = D[wig_off(1) + a * 3 + b];
+      d1[a][b] = dD[wig_off(1) + a * 3 + b];
+    }
+  const float* pv = D + wig_off(l - 1);
+  const float* pd = dD + wig_off(l - 1);
+  auto rpv = [&](int a) { return pv + (a + l - 1) * wp; };
+  auto rpd = [&](int a) { return pd + (a + l - 1) * wp; };
+  float o1[w], o2[w];
+  ir_row<l>(m, d1, rpv, o1);
+  ir_row<l>(m, r1, rpd, o2);
+  for (int n = 0; n < w; ++n) out[n] = o1[n] + o2[n];
 }
 
 // Runtime-L front end of wigner_blocks.

@@ -2,6 +2,19 @@
 // recursion, the edge rotation and the radial basis can be checked on a CPU.
 #include "e2a_geometry.hpp"
 
+namespace {
+
+// Blocks l .. L of one tangent, row by row, from its blocks below l.
+template <int l>
+void tangent_blocks(int L, const float* D, float* dD) {
+  for (int m = -l; m <= l; ++m) e2a::wigner_tangent_row<l>(m, D, dD, dD + e2a::wig_off(l) + (m + l) * (2 * l + 1));
+  if constexpr (l < 4) {
+    if (l < L) tangent_blocks<l + 1>(L, D, dD);
+  }
+}
+
+}  // namespace
+
 extern "C" {
 
 void e2a_host_edge_rotation(const float* rhat, int n, float* R_out) {
@@ -78,10 +91,7 @@ void e2a_host_wigner_tangents(int L, const float* R_in, int n, float* dD_out) {
       float dR[3][3];
       e2a::frame_tangent(R, a, dR);
       e2a::wigner_l1(dR, dD + e2a::wig_off(1), 3);
-      for (int l = 2; l <= L; ++l)
-        for (int m = -l; m <= l; ++m)
-          for (int k = -l; k <= l; ++k)
-            dD[e2a::wig_off(l) + (m + l) * (2 * l + 1) + (k + l)] = e2a::wigner_tangent_entry(l, m, k, D, dD);
+      if (L >= 2) tangent_blocks<2>(L, D, dD);
     }
   }
 }
