@@ -508,7 +508,10 @@ __global__ void k_pos_assemble(const int64_t* __restrict__ row_ptr, const int32_
 
 // ---------------------------------------------------------------- GEMMs ----
 // C[m * ldc + n] += alpha * sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak],
-// B(k, n) = B[k sbk + n sbn].  One workgroup per output tile and k-range;
+// B(k, n) = B[k sbk + n sbn].  With A2 set the k range is two segments: k <
+// K1 reads A and B, k >= K1 reads A2 and B2 (same strides) at k - K1, the
+// second product negated when neg2 is set, so that a sum of two products
+// is one launch and one write.  One workgroup per output tile and k-range;
 // with several k-ranges each writes alpha times its partial tile (or adds it
 // to what its slot holds, so that several products and several edge batches
 // can share one set of partials) and a second kernel adds the partials in
@@ -523,6 +526,10 @@ struct Gemm {
   float* C;
   int64_t ldc;
   float* part;     // [S][M][N] when S > 1
+  const void* A2;  // if set: second segment (the matrix-core kernel only)
+  const void* B2;
+  int64_t K1;      // first segment's length, a multiple of 32
+  bool neg2;
   int S;
   int64_t kper;    // k per split, a multiple of 32
   bool overwrite;  // C = alpha AB instead of C += alpha AB
@@ -617,34 +624,51 @@ __device__ __forceinline__ bool aligned16(const void* p, int64_t stride) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && stride % 8 == 0;
 }
 
-__global__ void __launch_bounds__(256) k_gemm_mfma(Gemm g) {
+__global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   __shared__ __attribute__((aligned(16))) GemmSmem sm;
   const uint16_t* A = static_cast<const uint16_t*>(g.A);
   const uint16_t* B = static_cast<const uint16_t*>(g.B);
+  const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
+  const uint16_t* B2 = static_cast<const uint16_t*>(g.B2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
   const int64_t m0 = (int64_t)blockIdx.y * kTM, n0 = (int64_t)blockIdx.x * kTM;
   const int64_t kb = (int64_t)blockIdx.z * g.kper;
   const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
+  const int64_t k1 = A2 ? g.K1 : g.K;   // end of the first segment
   // A(m, k) = A[m sam + k sak]; B(k, n) = B[n sbn + k sbk]
-  const bool avk = g.sak == 1 && aligned16(A, g.sam), avr = !avk && g.sam == 1 && aligned16(A, g.sak);
-  const bool bvk = g.sbk == 1 && aligned16(B, g.sbn), bvr = !bvk && g.sbn == 1 && aligned16(B, g.sbk);
+  const bool avk = g.sak == 1 && aligned16(A, g.sam) && (!A2 || aligned16(A2, g.sam));
+  const bool avr = !avk && g.sam == 1 && aligned16(A, g.sak) && (!A2 || aligned16(A2, g.sak));
+  const bool bvk = g.sbk == 1 && aligned16(B, g.sbn) && (!B2 || aligned16(B2, g.sbn));
+  const bool bvr = !bvk && g.sbn == 1 && aligned16(B, g.sbk) && (!B2 || aligned16(B2, g.sbk));
+  // the slice at k0 (a multiple of 32 from kb, never across K1)
+  auto fetch = [&](int64_t k0, Slice& fa, Slice& fb) {
+    if (k0 < k1) {
+      const int64_t e1 = ke < k1 ? ke : k1;
+      fetch_slice(A, g.sam, g.sak, m0, g.M, k0, e1, avk, avr, tid, fa);
+      fetch_slice(B, g.sbn, g.sbk, n0, g.N, k0, e1, bvk, bvr, tid, fb);
+    } else {
+      fetch_slice(A2, g.sam, g.sak, m0, g.M, k0 - k1, ke - k1, avk, avr, tid, fa);
+      fetch_slice(B2, g.sbn, g.sbk, n0, g.N, k0 - k1, ke - k1, bvk, bvr, tid, fb);
+      if (g.neg2)
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) fb.v[v][q] ^= 0x80008000u;   // bf16 sign bits
+    }
+  };
   f32x16 acc[2][2] = {};
   Slice fa, fb;
   int buf = 0;
   if (kb < ke) {
-    fetch_slice(A, g.sam, g.sak, m0, g.M, kb, ke, avk, avr, tid, fa);
-    fetch_slice(B, g.sbn, g.sbk, n0, g.N, kb, ke, bvk, bvr, tid, fb);
+    fetch(kb, fa, fb);
     commit_slice(fa, avr, sm.a[0], tid);
     commit_slice(fb, bvr, sm.b[0], tid);
   }
   __syncthreads();
   for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
     const bool more = k0 + kBK < ke;
-    if (more) {
-      fetch_slice(A, g.sam, g.sak, m0, g.M, k0 + kBK, ke, avk, avr, tid, fa);
-      fetch_slice(B, g.sbn, g.sbk, n0, g.N, k0 + kBK, ke, bvk, bvr, tid, fb);
-    }
+    if (more) fetch(k0 + kBK, fa, fb);
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 16) {
       bf16x8 af[2], bfr[2];
@@ -812,10 +836,11 @@ e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
 // The SO(2) weight gradients sum over every batch: each of the 2L + 1
 // matrices keeps dw_splits(m) partials for the whole call, which every batch's
 // products add to, and one reduction at the end.  The product kernel holds
-// two workgroups per CU (192 VGPRs a lane), 512 on the 256 CUs, and a launch
-// with a few workgroups more than that takes a second round: the split count
-// fills the 512 slots without passing them (tiles x S <= 512).
-constexpr int64_t kGemmSlots = 512;
+// three workgroups per CU (at most 168 VGPRs a lane, 40 KB of LDS each), 768
+// on the 256 CUs, and a launch with a few workgroups more than that takes a
+// second round: the split count fills the 768 slots without passing them
+// (tiles x S <= 768).
+constexpr int64_t kGemmSlots = 768;
 int64_t dw_splits(int L, int C, int m) {
   const int64_t km = (int64_t)(L + 1 - m) * C;
   const int64_t t = (km + kTM - 1) / kTM;
@@ -891,8 +916,18 @@ WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   return w;
 }
 
+// Second k segment of a product (matrix-core kernel): A2, B2 at k - K1.
+void pair_segments(Gemm& g, const void* A2, const void* B2, int64_t K1, bool neg2) {
+  g.A2 = A2;
+  g.B2 = B2;
+  g.K1 = K1;
+  g.neg2 = neg2;
+}
+
 template <int L, typename T>
 e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
+  // bf16 products run on the matrix-core kernel, which takes two k segments
+  constexpr bool kPairs = std::is_same<T, uint16_t>::value;
   const e2a_attn_args* a = pl.a;
   constexpr int K = (L + 1) * (L + 1);
   const int C = a->C, H = a->H;
@@ -1000,6 +1035,17 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       const T* Xm = Xp + bl.B * km;
       float* Ym = Yp + bl.B * km;
       const T* W2 = W1 + km * km;
+      if (kPairs && km % kBK == 0) {
+        // one launch per output: Yp = [Xp | Xm] [W1; -W2], Ym = [Xp | Xm] [W2; W1]
+        for (int t = 0; t < 2; ++t) {
+          Gemm g = make_gemm(Xp, km, 1, t == 0 ? W1 : W2, 1, km, nb, km, 2 * km, 1.0f, t == 0 ? Yp : Ym, km, part,
+                             true);
+          pair_segments(g, Xm, t == 0 ? W2 : W1, km, t == 0);
+          e = gemm<T, T>(g, W.part_floats, st);
+          if (e != E2A_OK) return e;
+        }
+        continue;
+      }
       const struct { const T* x; const T* w; float* y; float s; bool first; } terms[4] = {
           {Xp, W1, Yp, 1.0f, true}, {Xm, W2, Yp, -1.0f, false}, {Xp, W2, Ym, 1.0f, true}, {Xm, W1, Ym, 1.0f, false}};
       for (const auto& t : terms) {
@@ -1033,6 +1079,20 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         // A(m', k) = X[k][m'] (transposed rows), B(k, n) = dY[k][n]
         const T* Xm = Xp + bl.B * km;
         const T* DYm = DYp + bl.B * km;
+        if (kPairs && nb % kBK == 0) {
+          // one launch per matrix: p1 (+)= [Xp; Xm]^T [dYp; dYm], p2 (+)= [Xp; Xm]^T [dYm; -dYp]
+          for (int t = 0; t < (m == 0 ? 1 : 2); ++t) {
+            Gemm g = make_gemm(Xp, 1, km, t == 0 ? DYp : DYm, km, 1, km, km, m == 0 ? nb : 2 * nb, 1.0f, nullptr,
+                               km, t == 0 ? p1 : p2);
+            if (m > 0) pair_segments(g, Xm, t == 0 ? DYm : DYp, nb, t == 1);
+            g.S = static_cast<int>(S);
+            g.kper = ((g.K + S - 1) / S + 31) / 32 * 32;
+            g.part_acc = e0 > 0;
+            const e2a_status e = launch_gemm<T, T>(g, st);
+            if (e != E2A_OK) return e;
+          }
+          continue;
+        }
         const struct { const T* x; const T* dy; float* part; float s; bool first; } terms[4] = {
             {Xp, DYp, p1, 1.0f, true}, {Xm, DYm, p1, 1.0f, false}, {Xp, DYm, p2, 1.0f, true},
             {Xm, DYp, p2, -1.0f, false}};
@@ -1065,6 +1125,17 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         const T* DYm = DYp + bl.B * km;
         const T* W2 = W1 + km * km;
         float* dXm = dXp + bl.B * km;
+        if (kPairs && km % kBK == 0) {
+          // one launch per output: dXp = [dYp | dYm] [W1^T; W2^T], dXm = [dYm | dYp] [W1^T; -W2^T]
+          for (int t = 0; t < 2; ++t) {
+            Gemm g = make_gemm(t == 0 ? DYp : DYm, km, 1, W1, 1, km, nb, km, 2 * km, 1.0f, t == 0 ? dXp : dXm, km,
+                               part, true);
+            pair_segments(g, t == 0 ? DYm : DYp, W2, km, t == 1);
+            e = gemm<T, T>(g, W.part_floats, st);
+            if (e != E2A_OK) return e;
+          }
+          continue;
+        }
         const struct { const T* dy; const T* w; float* x; float s; bool first; } terms[4] = {
             {DYp, W1, dXp, 1.0f, true}, {DYm, W2, dXp, 1.0f, false}, {DYp, W2, dXm, -1.0f, true},
             {DYm, W1, dXm, 1.0f, false}};
