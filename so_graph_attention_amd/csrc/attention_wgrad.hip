@@ -632,8 +632,17 @@ __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   const uint16_t* B2 = static_cast<const uint16_t*>(g.B2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kTM, n0 = (int64_t)blockIdx.x * kTM;
-  const int64_t kb = (int64_t)blockIdx.z * g.kper;
+  // Workgroups are dealt to the 8 XCDs in turn (id mod 8).  Work item w runs
+  // on XCD w / (share), so that each XCD takes a contiguous run of items (n
+  // tile fastest, then m tile, then k range): the tiles that read the same
+  // rows of an operand run side by side under one L2.
+  const uint32_t nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+  const uint32_t id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const uint32_t q = total / 8, r = total % 8, xcd = id % 8, local = id / 8;
+  const uint32_t wi = (xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q) + local;
+  const uint32_t bx = wi % nx, by = (wi / nx) % ny, bz = wi / (nx * ny);
+  const int64_t m0 = (int64_t)by * kTM, n0 = (int64_t)bx * kTM;
+  const int64_t kb = (int64_t)bz * g.kper;
   const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
   const int64_t k1 = A2 ? g.K1 : g.K;   // end of the first segment
   // A(m, k) = A[m sam + k sak]; B(k, n) = B[n sbn + k sbk]
@@ -701,7 +710,7 @@ __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
         if (m < g.M && n < g.N) {
           const float v = acc[i][j][r];
           if (g.S > 1) {
-            float* pp = g.part + ((int64_t)blockIdx.z * g.M + m) * g.N + n;
+            float* pp = g.part + ((int64_t)bz * g.M + m) * g.N + n;
             *pp = g.part_acc ? *pp + g.alpha * v : g.alpha * v;
           } else if (g.overwrite) {
             g.C[m * g.ldc + n] = g.alpha * v;
