@@ -620,12 +620,22 @@ __device__ __forceinline__ void commit_slice(const Slice& f, bool vr_layout, uin
   }
 }
 
-__device__ __forceinline__ bool aligned16(const void* p, int64_t stride) {
+__host__ __device__ __forceinline__ bool aligned16(const void* p, int64_t stride) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0 && stride % 8 == 0;
 }
 
-__global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
-  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+// Operand layouts: 16-byte vectors along k, along m (or n), or element by
+// element.  kAny: decided per launch from the strides and alignments.
+constexpr int kVecK = 1, kVecR = 2, kElem = 0, kAny = -1;
+
+__host__ __device__ __forceinline__ int operand_layout(const void* X, const void* X2, int64_t sr, int64_t sk) {
+  if (sk == 1 && aligned16(X, sr) && (!X2 || aligned16(X2, sr))) return kVecK;
+  if (sr == 1 && aligned16(X, sk) && (!X2 || aligned16(X2, sk))) return kVecR;
+  return kElem;
+}
+
+template <int AV, int BV>
+__device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
   const uint16_t* A = static_cast<const uint16_t*>(g.A);
   const uint16_t* B = static_cast<const uint16_t*>(g.B);
   const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
@@ -646,10 +656,9 @@ __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
   const int64_t k1 = A2 ? g.K1 : g.K;   // end of the first segment
   // A(m, k) = A[m sam + k sak]; B(k, n) = B[n sbn + k sbk]
-  const bool avk = g.sak == 1 && aligned16(A, g.sam) && (!A2 || aligned16(A2, g.sam));
-  const bool avr = !avk && g.sam == 1 && aligned16(A, g.sak) && (!A2 || aligned16(A2, g.sak));
-  const bool bvk = g.sbk == 1 && aligned16(B, g.sbn) && (!B2 || aligned16(B2, g.sbn));
-  const bool bvr = !bvk && g.sbn == 1 && aligned16(B, g.sbk) && (!B2 || aligned16(B2, g.sbk));
+  const int av = AV == kAny ? operand_layout(A, A2, g.sam, g.sak) : AV;
+  const int bv = BV == kAny ? operand_layout(B, B2, g.sbn, g.sbk) : BV;
+  const bool avk = av == kVecK, avr = av == kVecR, bvk = bv == kVecK, bvr = bv == kVecR;
   // the slice at k0 (a multiple of 32 from kb, never across K1)
   auto fetch = [&](int64_t k0, Slice& fa, Slice& fb) {
     if (k0 < k1) {
@@ -719,6 +728,21 @@ __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
           }
         }
       }
+}
+
+// Any layouts, three workgroups per CU (168 VGPRs).
+__global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  gemm_body<kAny, kAny>(g, sm);
+}
+
+// Both operands contiguous along m and n (the weight products Xᵀ dY, which
+// contract over edges): with the layout fixed the kernel fits 128 VGPRs, so
+// four workgroups share a CU (the LDS holds exactly four) and a third more
+// slices are in flight; the loop is bound by the slices' load latency.
+__global__ void __launch_bounds__(256, 4) k_gemm_mfma_tt(Gemm g) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  gemm_body<kVecR, kVecR>(g, sm);
 }
 
 // Any operand types, fp32 on the vector ALUs: 64 x 64 tiles, a 4 x 4 block of
@@ -804,9 +828,12 @@ e2a_status launch_gemm(const Gemm& g, hipStream_t st) {
   constexpr int64_t tm = tile_of<TA, TB>();
   const dim3 grid(static_cast<unsigned>((g.N + tm - 1) / tm), static_cast<unsigned>((g.M + tm - 1) / tm),
                   static_cast<unsigned>(g.S));
-  if constexpr (tm == kTM)
-    k_gemm_mfma<<<grid, 256, 0, st>>>(g);
-  else
+  if constexpr (tm == kTM) {
+    if (operand_layout(g.A, g.A2, g.sam, g.sak) == kVecR && operand_layout(g.B, g.B2, g.sbn, g.sbk) == kVecR)
+      k_gemm_mfma_tt<<<grid, 256, 0, st>>>(g);
+    else
+      k_gemm_mfma<<<grid, 256, 0, st>>>(g);
+  } else
     k_gemm_valu<TA, TB><<<grid, 256, 0, st>>>(g);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
@@ -844,12 +871,12 @@ e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
 
 // The SO(2) weight gradients sum over every batch: each of the 2L + 1
 // matrices keeps dw_splits(m) partials for the whole call, which every batch's
-// products add to, and one reduction at the end.  The product kernel holds
-// three workgroups per CU (at most 168 VGPRs a lane, 40 KB of LDS each), 768
-// on the 256 CUs, and a launch with a few workgroups more than that takes a
-// second round: the split count fills the 768 slots without passing them
-// (tiles x S <= 768).
-constexpr int64_t kGemmSlots = 768;
+// products add to, and one reduction at the end.  These products run on
+// k_gemm_mfma_tt, four workgroups per CU (128 VGPRs a lane, 40 KB of LDS
+// each), 1024 on the 256 CUs, and a launch with a few workgroups more than
+// that takes a second round: the split count fills the 1024 slots without
+// passing them (tiles x S <= 1024).
+constexpr int64_t kGemmSlots = 1024;
 int64_t dw_splits(int L, int C, int m) {
   const int64_t km = (int64_t)(L + 1 - m) * C;
   const int64_t t = (km + kTM - 1) / kTM;
