@@ -162,9 +162,38 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
   if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
+// D^l (l = 2..L) of the workgroup's edges from D^1 and D^{l-1}, one (edge,
+// row) per thread and level (the row recursion of the fused kernel).
+template <int L, int l>
+__device__ __forceinline__ void gather_wigner(float* D, const int* ii, int tid) {
+  if constexpr (l <= L) {
+    constexpr int WS = wig_size(L), w = 2 * l + 1, wp = 2 * l - 1;
+    for (int t = tid; t < kEB * w; t += blockDim.x) {
+      const int s = t / w, mi = t - s * w;
+      if (ii[s] < 0) continue;
+      float* De = D + s * WS;
+      float r1[3][3];
+#pragma unroll
+      for (int a = 0; a < 3; ++a)
+#pragma unroll
+        for (int b = 0; b < 3; ++b) r1[a][b] = De[wig_off(1) + a * 3 + b];
+      const float* Dp = De + wig_off(l - 1);
+      auto rp = [&](int a) { return Dp + (a + l - 1) * wp; };
+      float out[w];
+      ir_row<l>(mi - l, r1, rp, out);
+#pragma unroll
+      for (int n = 0; n < w; ++n) De[wig_off(l) + mi * w + n] = out[n];
+    }
+    __syncthreads();
+    gather_wigner<L, l + 1>(D, ii, tid);
+  }
+}
+
 // x = D h_j and dyhat = D (alpha G_i) (or rho dyhat) for kEB edges of the
-// batch: the edges' frames, Wigner blocks, radial bases and attention weights
-// first (one thread per edge), then the degrees one after another.
+// batch: the edges' frames, D^0, D^1 and radial bases (one lane of the first
+// wave per edge) while the other waves compute the attention weights (one
+// (edge, head) per thread), then D^2 .. D^L row by row, then the degrees one
+// after another.
 template <int L, typename T>
 __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __restrict__ feat, T* __restrict__ X,
                                                    T* __restrict__ GT) {
@@ -177,6 +206,7 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
   const int C = p.C, H = p.H, dh = C / H;
   const int64_t b0 = (int64_t)blockIdx.x * kEB;
   const int tid = threadIdx.x;
+  static_assert(kEB <= 64, "one lane of the first wave per edge");
   if (tid < kEB) {
     const int64_t b = b0 + tid;
     ii[tid] = -1;
@@ -199,7 +229,9 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
       const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
       float R[3][3];
       edge_rotation(u, R);
-      wigner_blocks<L>(R, D + tid * WS);
+      float* De = D + tid * WS;
+      De[0] = 1.0f;
+      if constexpr (L >= 1) wigner_l1(R, De + wig_off(1), 3);
       float e8[8];
       radial_basis8(r, p.cutoff, e8);
 #pragma unroll
@@ -212,16 +244,26 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) p.rbfd[b * 8 + kk] = e8[kk];
       }
-      const float inv = 1.0f / sqrtf(static_cast<float>(dh));
-      for (int h = 0; h < H; ++h) {
-        float sv = 0.0f;
-        for (int d = 0; d < dh; ++d) sv += p.q[(int64_t)i * C + h * dh + d] * p.k[(int64_t)j * C + h * dh + d];
-        al[tid * H + h] = expf(sv * inv - p.lse[(int64_t)i * H + h]);
-        if (p.alpha) p.alpha[b * H + h] = al[tid * H + h];
-      }
+    }
+  } else if (tid >= 64) {
+    const float inv = 1.0f / sqrtf(static_cast<float>(dh));
+    for (int t = tid - 64; t < kEB * H; t += blockDim.x - 64) {
+      const int s = t / H, h = t - s * H;
+      const int64_t b = b0 + s;
+      if (b >= p.nb) continue;
+      const int64_t e = p.e0 + b;
+      const int64_t i = p.src[e], j = p.col[e];
+      const float* qi = p.q + i * C + h * dh;
+      const float* kj = p.k + j * C + h * dh;
+      float sv = 0.0f;
+      for (int d = 0; d < dh; ++d) sv += qi[d] * kj[d];
+      const float a = expf(sv * inv - p.lse[i * H + h]);
+      al[s * H + h] = a;
+      if (p.alpha) p.alpha[b * H + h] = a;
     }
   }
   __syncthreads();
+  gather_wigner<L, 2>(D, ii, tid);
   gather_degree<L, 0, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
