@@ -596,10 +596,14 @@ struct GemmSmem {
 // to LDS ([r - r0][k - k0]) after the current slice's products, so that the
 // global loads' latency overlaps them.  vk / vr: 16-byte vectors along k or
 // along r are allowed; otherwise (and on ragged edges) element by element.
+// EXACT: the caller guarantees that k ranges and the extent along the vector
+// are multiples of 8, so a ragged tile edge is a whole vector past the end and
+// reads as zeros, with no element-by-element path.
 struct Slice {
   uint32_t v[2][4];
 };
 
+template <bool EXACT>
 __device__ __forceinline__ void fetch_slice(const uint16_t* __restrict__ X, int64_t sr, int64_t sk, int64_t r0,
                                             int64_t R, int64_t k0, int64_t ke, bool vk, bool vr, int tid,
                                             Slice& f) {
@@ -612,7 +616,10 @@ __device__ __forceinline__ void fetch_slice(const uint16_t* __restrict__ X, int6
       // rows idx / 4, k offset 8 (idx % 4)
       const int r = idx >> 2, kq = (idx & 3) * 8;
       const int64_t m = r0 + r, k = k0 + kq;
-      if (vk && m < R && k + 8 <= ke) {
+      if (EXACT) {
+        // k and ke are multiples of 8: k < ke means the whole vector is in range
+        if (m < R && k < ke) w = *reinterpret_cast<const u32x4*>(X + m * sr + k);
+      } else if (vk && m < R && k + 8 <= ke) {
         w = *reinterpret_cast<const u32x4*>(X + m * sr + k);
       } else {
 #pragma unroll
@@ -626,7 +633,10 @@ __device__ __forceinline__ void fetch_slice(const uint16_t* __restrict__ X, int6
       // pair of neighbouring k for 8 rows, written to LDS as 32-bit words
       const int kq = 2 * (tid & 15) + v, rq = (tid >> 4) * 8;
       const int64_t m = r0 + rq, k = k0 + kq;
-      if (k < ke && m + 8 <= R) {
+      if (EXACT) {
+        // m and R are multiples of 8: m < R means rows m .. m + 7 are in range
+        if (k < ke && m < R) w = *reinterpret_cast<const u32x4*>(X + m + k * sk);
+      } else if (k < ke && m + 8 <= R) {
         w = *reinterpret_cast<const u32x4*>(X + m + k * sk);
       } else {
 #pragma unroll
@@ -676,7 +686,7 @@ __host__ __device__ __forceinline__ int operand_layout(const void* X, const void
   return kElem;
 }
 
-template <int AV, int BV>
+template <int AV, int BV, bool EXACT>
 __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
   const uint16_t* A = static_cast<const uint16_t*>(g.A);
   const uint16_t* B = static_cast<const uint16_t*>(g.B);
@@ -705,11 +715,11 @@ __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
   auto fetch = [&](int64_t k0, Slice& fa, Slice& fb) {
     if (k0 < k1) {
       const int64_t e1 = ke < k1 ? ke : k1;
-      fetch_slice(A, g.sam, g.sak, m0, g.M, k0, e1, avk, avr, tid, fa);
-      fetch_slice(B, g.sbn, g.sbk, n0, g.N, k0, e1, bvk, bvr, tid, fb);
+      fetch_slice<EXACT>(A, g.sam, g.sak, m0, g.M, k0, e1, avk, avr, tid, fa);
+      fetch_slice<EXACT>(B, g.sbn, g.sbk, n0, g.N, k0, e1, bvk, bvr, tid, fb);
     } else {
-      fetch_slice(A2, g.sam, g.sak, m0, g.M, k0 - k1, ke - k1, avk, avr, tid, fa);
-      fetch_slice(B2, g.sbn, g.sbk, n0, g.N, k0 - k1, ke - k1, bvk, bvr, tid, fb);
+      fetch_slice<EXACT>(A2, g.sam, g.sak, m0, g.M, k0 - k1, ke - k1, avk, avr, tid, fa);
+      fetch_slice<EXACT>(B2, g.sbn, g.sbk, n0, g.N, k0 - k1, ke - k1, bvk, bvr, tid, fb);
       if (g.neg2)
 #pragma unroll
         for (int v = 0; v < 2; ++v)
@@ -775,16 +785,25 @@ __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
 // Any layouts, three workgroups per CU (168 VGPRs).
 __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   __shared__ __attribute__((aligned(16))) GemmSmem sm;
-  gemm_body<kAny, kAny>(g, sm);
+  gemm_body<kAny, kAny, false>(g, sm);
 }
 
-// Both operands contiguous along m and n (the weight products Xᵀ dY, which
-// contract over edges): with the layout fixed the kernel fits 128 VGPRs, so
-// four workgroups share a CU (the LDS holds exactly four) and a third more
-// slices are in flight; the loop is bound by the slices' load latency.
+// Fixed layouts with every extent a multiple of 8: without the per-launch
+// choice and the element-by-element path the kernel fits 128 VGPRs, so four
+// workgroups share a CU (the LDS holds exactly four) and a third more slices
+// are in flight; the loop is bound by the slices' load latency.
+// Both operands contiguous along m and n: the weight products Xᵀ dY, which
+// contract over edges.
 __global__ void __launch_bounds__(256, 4) k_gemm_mfma_tt(Gemm g) {
   __shared__ __attribute__((aligned(16))) GemmSmem sm;
-  gemm_body<kVecR, kVecR>(g, sm);
+  gemm_body<kVecR, kVecR, true>(g, sm);
+}
+
+// Both operands contiguous along k: the products of the edges' rows with the
+// SO(2) blocks (y = SO2(x), dx = SO2ᵀ(dy)).
+__global__ void __launch_bounds__(256, 4) k_gemm_mfma_kk(Gemm g) {
+  __shared__ __attribute__((aligned(16))) GemmSmem sm;
+  gemm_body<kVecK, kVecK, true>(g, sm);
 }
 
 // Any operand types, fp32 on the vector ALUs: 64 x 64 tiles, a 4 x 4 block of
@@ -871,8 +890,14 @@ e2a_status launch_gemm(const Gemm& g, hipStream_t st) {
   const dim3 grid(static_cast<unsigned>((g.N + tm - 1) / tm), static_cast<unsigned>((g.M + tm - 1) / tm),
                   static_cast<unsigned>(g.S));
   if constexpr (tm == kTM) {
-    if (operand_layout(g.A, g.A2, g.sam, g.sak) == kVecR && operand_layout(g.B, g.B2, g.sbn, g.sbk) == kVecR)
+    const int av = operand_layout(g.A, g.A2, g.sam, g.sak), bv = operand_layout(g.B, g.B2, g.sbn, g.sbk);
+    // the fixed-layout instances read whole vectors only: k ranges (and the
+    // second segment's start) and the vector extents must be multiples of 8
+    const bool k8 = g.K % 8 == 0 && g.kper % 8 == 0 && (!g.A2 || g.K1 % 8 == 0);
+    if (av == kVecR && bv == kVecR && k8 && g.M % 8 == 0 && g.N % 8 == 0)
       k_gemm_mfma_tt<<<grid, 256, 0, st>>>(g);
+    else if (av == kVecK && bv == kVecK && k8)
+      k_gemm_mfma_kk<<<grid, 256, 0, st>>>(g);
     else
       k_gemm_mfma<<<grid, 256, 0, st>>>(g);
   } else
