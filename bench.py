@@ -164,6 +164,17 @@ def backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, b
                                 "l = 0 terms"}
 
 
+def algorithmic_bytes(w, n_edges):
+    """HBM bytes of one layer call with every array touched once: the node
+    features (storage precision) in and the fp32 output out, the CSR graph,
+    positions, q and k (fp32), and the weights."""
+    s = 2 if w.dtype == "bf16" else 4
+    n, K, C, L = w.n_atoms, (w.L + 1) ** 2, w.C, w.L
+    so2 = sum((1 if m == 0 else 2) * ((L + 1 - m) * C) ** 2 for m in range(L + 1))
+    weights = (so2 + 2 * C * C + 8 * (L + 1) * C) * s
+    return n * K * C * (s + 4) + 4 * n_edges + 8 * (n + 1) + 12 * n + 8 * n * C + weights
+
+
 def so2_flops_per_edge(L, C):
     """The SO(2) mix alone: 2[(L+1)^2 + 4 sum_{m>=1} (L+1-m)^2] C^2 per edge."""
     return 2 * ((L + 1) ** 2 + 4 * sum((L + 1 - m) ** 2 for m in range(1, L + 1))) * C * C
@@ -348,7 +359,9 @@ def main():
         progress(f"forces {bwd['forces_ms']:.1f} ms")
 
     achieved = f_edge * n_edges / (attn_ms * 1e-3) / 1e12
-    traffic = traffic_per_launch()
+    # the committed byte counters were taken on the 100k-atom workload
+    traffic = traffic_per_launch() if args.config == "large" else None
+    alg_bytes = algorithmic_bytes(w, n_edges)
     result = {
         "metric": METRIC,
         "value": n_edges / (ms_step * 1e-3),
@@ -372,6 +385,10 @@ def main():
                      "kernel": "e2a_attention_fwd (fused MFMA kernel + q/k prologue + weight pack)",
                      "flop_per_edge": f_edge},
         "breakdown": {"neighbors_ms": nb_ms, "attention_ms": attn_ms, "attention_ms_median": attn_med,
+                      "attention_alg_bytes": alg_bytes,
+                      "attention_alg_hbm_frac": alg_bytes / (attn_ms * 1e-3) / (PEAK_HBM_GBS * 1e9),
+                      "attention_measured_hbm_frac": (None if traffic is None else
+                                                      traffic / (attn_ms * 1e-3) / (PEAK_HBM_GBS * 1e9)),
                       "attention_edges_per_s": n_edges / (attn_ms * 1e-3),
                       "conv_ms": conv_ms, "conv_edges_per_s": n_edges / (conv_ms * 1e-3),
                       "conv_tflops": (f_edge - 2 * w.C) * n_edges / (conv_ms * 1e-3) / 1e12},
