@@ -383,19 +383,19 @@ struct ForceParams {
   BatchLayout bl;
 };
 
-// Degree l's share of dL/dD for the wave's edge: the lane sums the products
-// over its channels (every 64th), the wave sums the lanes, and lane 0 writes
-// dL/dD[l][m][n] to part.
+// Degree l's share of T_a = <dL/dD, dD/dw_a> for the wave's edge, where
+// dL/dD^l[m][n] = sum_c dx[m][c] h_j[n][c] + yhat[m][c] (alpha G_i)[n][c]: per
+// channel (every 64th for the lane) the tangent blocks are applied to h_j and
+// alpha G_i first, T_a += sum_m dx[m] (D_a h)[m] + yhat[m] (D_a alpha G)[m], so
+// that no (2l + 1)^2 partial of dL/dD is held per lane; the wave sums the
+// three numbers at the end.
 template <int L, int l, typename T>
 __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __restrict__ feat,
-                                             const T* __restrict__ w_rad, int64_t b, int i, int j, float* part,
-                                             int lane) {
+                                             const T* __restrict__ w_rad, int64_t b, int i, int j,
+                                             const float (*D)[wig_size(L)], float (&T3)[3], int lane) {
   constexpr int K = (L + 1) * (L + 1);
   constexpr int w = 2 * l + 1;
   const int C = p.C, H = p.H, dh = C / H;
-  float P[w * w];
-#pragma unroll
-  for (int t = 0; t < w * w; ++t) P[t] = 0.0f;
   for (int c = lane; c < C; c += 64) {
     float rho = 0.0f;
 #pragma unroll
@@ -410,19 +410,29 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
       hv[q] = load_as_f32(feat, (size_t)(((int64_t)j * K + l * l + q) * C + c));
       ag[q] = a * p.grad[((int64_t)i * K + l * l + q) * C + c];
     }
+    // an offset the compiler cannot see through: the tangent entries do not
+    // depend on the channel, and hoisted out of this loop all 3 (2l + 1)^2 of
+    // them would be held in registers
+    int z = 0;
+    asm volatile("" : "+v"(z));
 #pragma unroll
-    for (int m = 0; m < w; ++m)
+    for (int t = 0; t < 3; ++t) {
+      const float* Dt = D[1 + t] + wig_off(l) + z;
+      float s = 0.0f;
 #pragma unroll
-      for (int n = 0; n < w; ++n) P[m * w + n] += dx[m] * hv[n] + yh[m] * ag[n];
+      for (int m = 0; m < w; ++m) {
+        float u = 0.0f, v = 0.0f;
+#pragma unroll
+        for (int n = 0; n < w; ++n) {
+          u += Dt[m * w + n] * hv[n];
+          v += Dt[m * w + n] * ag[n];
+        }
+        s += dx[m] * u + yh[m] * v;
+      }
+      T3[t] += s;
+    }
   }
-#pragma unroll
-  for (int t = 0; t < w * w; ++t) {
-    float v = P[t];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-    if (lane == 0) part[wig_off(l) + t] = v;
-  }
-  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, part, lane);
+  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, D, T3, lane);
 }
 
 // Block l >= 2 of D (component 0) and of its three tangents dD/dw_a
@@ -454,7 +464,6 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
                                                                const T* __restrict__ w_rad) {
   constexpr int WS = wig_size(L);
   __shared__ float Ds[kForceEdges][4][WS];   // D and its three tangents dD/dw_a
-  __shared__ float parts[kForceEdges][WS];   // dL/dD
   __shared__ float fr[kForceEdges][4];       // r_hat, |r|
   __shared__ int ijs[kForceEdges][2];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -497,20 +506,14 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
   __syncthreads();
   if constexpr (L >= 2) force_wigner<L, 2>(D, live, lane);
   if (!live) return;
-  force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], parts[wv], lane);
+  // T_a = <dL/dD, dD/dw_a>: each lane's share, then the wave's sum
+  float T3[3] = {0.0f, 0.0f, 0.0f};
+  force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], D, T3, lane);
   // the edge length's share
   float sv = 0.0f;
   for (int c = lane; c < p.C; c += 64)
     for (int l = 0; l <= L; ++l) sv += p.drp[b * (L + 1) * p.C + l * p.C + c];
   for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
-  // T_a = <dL/dD, dD/dw_a>: the lanes share the entries, then the wave sums
-  float T3[3] = {0.0f, 0.0f, 0.0f};
-  for (int t = lane; t < WS; t += 64) {
-    const float g = parts[wv][t];
-    T3[0] += g * D[1][t];
-    T3[1] += g * D[2][t];
-    T3[2] += g * D[3][t];
-  }
   for (int a = 0; a < 3; ++a)
     for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
   if (lane == 0) {
