@@ -112,12 +112,13 @@ struct GatherParams {
   float* rbf;       // [B][8]
   float* rbfd;      // if set: d e_k / d r, [B][8]
   float* alpha;     // if set: the edges' attention weights, [B][H]
-  const void* w_rad;   // if set: the cotangent rows are written as dy = rho dyhat
+  const void* w_rad;   // the cotangent rows are written as dy = rho dyhat
+  float* dyhat;        // if set: dyhat itself too, fp32, in the batch layout
 };
 
 // Degree l of the gather: one (edge, channel) per work item reads the
 // degree's 2l + 1 feature and cotangent entries once and writes all 2l + 1
-// rows of x and dyhat (or dy = rho dyhat).
+// rows of x and dy = rho dyhat (and of dyhat when asked for).
 template <int L, int l, typename T>
 __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __restrict__ feat, T* __restrict__ X,
                                               T* __restrict__ GT, const float* D, const float* al, const float* rb,
@@ -137,14 +138,14 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
       hv[n] = load_as_f32(hj, (size_t)n * C);
       gv[n] = gi[(int64_t)n * C];
     }
-    float a = al[s * H + c / dh];
-    if (p.w_rad) {
+    const float a0 = al[s * H + c / dh];
+    float rho = 0.0f;
+    {
       const T* wr = static_cast<const T*>(p.w_rad);
-      float rho = 0.0f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) rho += rb[s * 8 + kk] * load_as_f32(wr, (size_t)(kk * (L + 1) + l) * C + c);
-      a *= rho;
     }
+    const float a = a0 * rho;
     const float* Dl = D + s * WS + wig_off(l);
 #pragma unroll
     for (int mi = 0; mi < w; ++mi) {
@@ -157,6 +158,7 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
       const int64_t idx = batch_index(p.bl, L, C, b0 + s, l, mi - l, c);
       store_as(X, idx, x);
       store_as(GT, idx, g * a);
+      if (p.dyhat) p.dyhat[idx] = g * a0;
     }
   }
   if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
@@ -267,90 +269,68 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
   gather_degree<L, 0, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
-// dy = rho dyhat in place and, when Y is set, drho[b][l][c] = sum_m
-// y[l,m][c] dyhat[l,m][c]: when part is set, summed into this range's part of
-// dW_rad, part[z][k][(l, c)] (+)= sum over the range's edges b of
-// rbf[b][k] drho[b][l][c] (added to what the slot holds from earlier batches
-// when acc_parts is set); when drp is set, drp[b][(l, c)] = drho[b][l][c]
-// d rho[l][c] / d r, the edge length's share (rbfd = d e_k / d r).
-// One thread per (degree, channel) and range of edges (consecutive threads
-// take consecutive channels, so the row reads coalesce); each edge's 2l + 1
-// rows are loaded together before any is written back.
-template <int L, int l, typename T>
+// dW_rad partials from the edge batches: drho[b][l][c] = sum_m y[l,m][c]
+// dyhat[l,m][c], summed into this range's part of dW_rad, part[z][k][(l, c)]
+// (+)= sum over the range's edges b of rbf[b][k] drho[b][l][c] (added to
+// what the slot holds from earlier batches when acc_parts is set).  One
+// thread per (degree, channel) and range of edges (consecutive threads take
+// consecutive channels, so the row reads coalesce); each edge's 2l + 1 rows
+// are loaded together.
+template <int L, int l>
 __device__ __forceinline__ void rho_degree(const BatchLayout& bl, int64_t nb, int C, int64_t per, int z, int c,
-                                           const float* __restrict__ rbf, const float* __restrict__ rbfd,
-                                           const T* __restrict__ w_rad, const float* __restrict__ Y,
-                                           T* __restrict__ GT, float* __restrict__ part, bool acc_parts,
-                                           float* __restrict__ drp) {
+                                           const float* __restrict__ rbf, const float* __restrict__ Y,
+                                           const float* __restrict__ dyhat, float* __restrict__ part,
+                                           bool acc_parts) {
   constexpr int w = 2 * l + 1;
   const int lc = l * C + c;
-  float wr[8], acc[8];
+  float acc[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    wr[kk] = load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
-    acc[kk] = 0.0f;
-  }
+  for (int kk = 0; kk < 8; ++kk) acc[kk] = 0.0f;
   const int64_t b1 = (z + 1) * per < nb ? (z + 1) * per : nb;
   for (int64_t b = z * per; b < b1; ++b) {
     float g[w], y[w];
-    int64_t idx[w];
 #pragma unroll
     for (int q = 0; q < w; ++q) {
-      idx[q] = batch_index(bl, L, C, b, l, q - l, c);
-      g[q] = load_as_f32(GT, (size_t)idx[q]);
-      y[q] = Y ? Y[idx[q]] : 0.0f;
+      const int64_t idx = batch_index(bl, L, C, b, l, q - l, c);
+      g[q] = dyhat[idx];
+      y[q] = Y[idx];
     }
-    float rho = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) rho += rbf[b * 8 + kk] * wr[kk];
     float dr = 0.0f;
 #pragma unroll
-    for (int q = 0; q < w; ++q) {
-      dr += y[q] * g[q];
-      store_as(GT, idx[q], rho * g[q]);
-    }
+    for (int q = 0; q < w; ++q) dr += y[q] * g[q];
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) acc[kk] += rbf[b * 8 + kk] * dr;
-    if (drp) {
-      float dro = 0.0f;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) dro += rbfd[b * 8 + kk] * wr[kk];
-      drp[b * (L + 1) * C + lc] = dr * dro;
-    }
   }
-  if (part)
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      float* pp = part + ((int64_t)z * 8 + kk) * (L + 1) * C + lc;
-      *pp = acc_parts ? *pp + acc[kk] : acc[kk];
-    }
+  for (int kk = 0; kk < 8; ++kk) {
+    float* pp = part + ((int64_t)z * 8 + kk) * (L + 1) * C + lc;
+    *pp = acc_parts ? *pp + acc[kk] : acc[kk];
+  }
 }
 
 // The thread's degree ld as a compile-time constant (uniform over a wave when
 // C is a multiple of 64).
-template <int L, int l, typename T>
+template <int L, int l>
 __device__ __forceinline__ void rho_dispatch(int ld, const BatchLayout& bl, int64_t nb, int C, int64_t per, int z,
-                                             int c, const float* __restrict__ rbf, const float* __restrict__ rbfd,
-                                             const T* __restrict__ w_rad, const float* __restrict__ Y,
-                                             T* __restrict__ GT, float* __restrict__ part, bool acc_parts,
-                                             float* __restrict__ drp) {
+                                             int c, const float* __restrict__ rbf, const float* __restrict__ Y,
+                                             const float* __restrict__ dyhat, float* __restrict__ part,
+                                             bool acc_parts) {
   if (ld == l) {
-    rho_degree<L, l, T>(bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
+    rho_degree<L, l>(bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
     return;
   }
-  if constexpr (l < L)
-    rho_dispatch<L, l + 1, T>(ld, bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
+  if constexpr (l < L) rho_dispatch<L, l + 1>(ld, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
 }
 
-template <int L, typename T>
+template <int L>
 __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
-                         const float* __restrict__ rbfd, const T* __restrict__ w_rad, const float* __restrict__ Y,
-                         T* __restrict__ GT, float* __restrict__ part, bool acc_parts, float* __restrict__ drp) {
+                         const float* __restrict__ Y, const float* __restrict__ dyhat, float* __restrict__ part,
+                         bool acc_parts) {
   const int lc = blockIdx.x * blockDim.x + threadIdx.x;
   const int z = blockIdx.y;
   if (lc >= (L + 1) * C) return;
   const int l = lc / C, c = lc - l * C;
-  rho_dispatch<L, 0, T>(l, bl, nb, C, per, z, c, rbf, rbfd, w_rad, Y, GT, part, acc_parts, drp);
+  rho_dispatch<L, 0>(l, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
 }
 
 // ------------------------------------------------------------ positions ----
@@ -374,7 +354,7 @@ struct ForceParams {
   const float* rbf;     // [B][8]
   const float* Y;       // batch tensor: y = SO2(x), fp32
   const float* dX;      // batch tensor: dx = SO2^T(dy), fp32
-  const float* drp;     // [B][(L+1) C]
+  const float* rbfd;    // [B][8]: d e_k / d r
   float* gedge;         // [E][3]: dL/dr of every edge
   float box[3];
   int periodic;
@@ -388,25 +368,32 @@ struct ForceParams {
 // channel (every 64th for the lane) the tangent blocks are applied to h_j and
 // alpha G_i first, T_a += sum_m dx[m] (D_a h)[m] + yhat[m] (D_a alpha G)[m], so
 // that no (2l + 1)^2 partial of dL/dD is held per lane; the wave sums the
-// three numbers at the end.
+// three numbers at the end.  The lane also sums its channels' share of the
+// edge length's term, drho[l][c] d rho[l][c] / d r with drho = sum_m y[m]
+// dyhat[m] and dyhat = D^l (alpha G_i), into svl.
 template <int L, int l, typename T>
 __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __restrict__ feat,
                                              const T* __restrict__ w_rad, int64_t b, int i, int j,
-                                             const float (*D)[wig_size(L)], float (&T3)[3], int lane) {
+                                             const float (*D)[wig_size(L)], float (&T3)[3], float& svl,
+                                             int lane) {
   constexpr int K = (L + 1) * (L + 1);
   constexpr int w = 2 * l + 1;
   const int C = p.C, H = p.H, dh = C / H;
   for (int c = lane; c < C; c += 64) {
-    float rho = 0.0f;
+    float rho = 0.0f, dro = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) rho += p.rbf[b * 8 + kk] * load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
+    for (int kk = 0; kk < 8; ++kk) {
+      const float wr = load_as_f32(w_rad, (size_t)(kk * (L + 1) + l) * C + c);
+      rho += p.rbf[b * 8 + kk] * wr;
+      dro += p.rbfd[b * 8 + kk] * wr;
+    }
     const float a = p.alpha[b * H + c / dh];
-    float dx[w], yh[w], hv[w], ag[w];
+    float dx[w], yv[w], hv[w], ag[w];
 #pragma unroll
     for (int q = 0; q < w; ++q) {
       const int64_t idx = batch_index(p.bl, L, C, b, l, q - l, c);
       dx[q] = p.dX[idx];
-      yh[q] = rho * p.Y[idx];
+      yv[q] = p.Y[idx];
       hv[q] = load_as_f32(feat, (size_t)(((int64_t)j * K + l * l + q) * C + c));
       ag[q] = a * p.grad[((int64_t)i * K + l * l + q) * C + c];
     }
@@ -418,7 +405,8 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
       const float* Dt = D[1 + t] + wig_off(l) + z;
-      float s = 0.0f;
+      // yhat = rho y: rho applied once to the second sum
+      float s1 = 0.0f, s2 = 0.0f;
 #pragma unroll
       for (int m = 0; m < w; ++m) {
         float u = 0.0f, v = 0.0f;
@@ -427,12 +415,25 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
           u += Dt[m * w + n] * hv[n];
           v += Dt[m * w + n] * ag[n];
         }
-        s += dx[m] * u + yh[m] * v;
+        s1 += dx[m] * u;
+        s2 += yv[m] * v;
       }
-      T3[t] += s;
+      T3[t] += s1 + rho * s2;
+    }
+    {
+      const float* D0 = D[0] + wig_off(l) + z;
+      float dr = 0.0f;
+#pragma unroll
+      for (int m = 0; m < w; ++m) {
+        float g = 0.0f;
+#pragma unroll
+        for (int n = 0; n < w; ++n) g += D0[m * w + n] * ag[n];
+        dr += yv[m] * g;
+      }
+      svl += dr * dro;
     }
   }
-  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, D, T3, lane);
+  if constexpr (l < L) force_degree<L, l + 1, T>(p, feat, w_rad, b, i, j, D, T3, svl, lane);
 }
 
 // Block l >= 2 of D (component 0) and of its three tangents dD/dw_a
@@ -508,11 +509,8 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
   if (!live) return;
   // T_a = <dL/dD, dD/dw_a>: each lane's share, then the wave's sum
   float T3[3] = {0.0f, 0.0f, 0.0f};
-  force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], D, T3, lane);
-  // the edge length's share
-  float sv = 0.0f;
-  for (int c = lane; c < p.C; c += 64)
-    for (int l = 0; l <= L; ++l) sv += p.drp[b * (L + 1) * p.C + l * p.C + c];
+  float sv = 0.0f;   // the edge length's share
+  force_degree<L, 0, T>(p, feat, w_rad, b, ijs[wv][0], ijs[wv][1], D, T3, sv, lane);
   for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
   for (int a = 0; a < 3; ++a)
     for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
@@ -985,7 +983,7 @@ Gemm make_gemm(const void* A, int64_t sam, int64_t sak, const void* B, int64_t s
 
 struct WgWs {
   size_t src, X, GT, Y, rbf, part, dwpart, rhopart, wt;
-  size_t rbfd, alpha, drp, dX, gedge;   // position gradient only
+  size_t rbfd, alpha, dX, gedge;   // position gradient only (dX also holds dyhat for the dW_rad batches)
   size_t total;
   int64_t B, part_floats;
 };
@@ -1012,7 +1010,6 @@ WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   w.wt = take(sizeof(float) * (size_t)so2);   // sized for fp32 storage
   w.rbfd = take(sizeof(float) * 8 * (size_t)B);
   w.alpha = take(sizeof(float) * (size_t)B * H);
-  w.drp = take(sizeof(float) * (size_t)B * K0);
   w.dX = take(sizeof(float) * (size_t)per);
   w.gedge = take(sizeof(float) * 3 * (size_t)(e > 0 ? e : 1));
   w.total = off;
@@ -1068,6 +1065,10 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
   }
   if ((!pl.w_rad && !pl.w_so2 && !pl.pos) || E == 0) return E2A_OK;
   const bool need_y = pl.w_rad || pl.pos;   // drho needs SO2(x)
+  // where dW_rad is asked of the batches (builds without the fused radial
+  // pass), the gather also keeps dyhat (in the dx buffer, free until the dx
+  // products) for the drho pass; the force kernel forms its own drho
+  const bool rho_pass = pl.w_rad != nullptr;
 
   int32_t* src = reinterpret_cast<int32_t*>(wb + W.src);
   k_edge_rows<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(a->row_ptr, n, src);
@@ -1120,8 +1121,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     gp.rbf = rbf;
     gp.rbfd = pl.pos ? reinterpret_cast<float*>(wb + W.rbfd) : nullptr;
     gp.alpha = pl.pos ? reinterpret_cast<float*>(wb + W.alpha) : nullptr;
-    // without drho in the batches dyhat serves only as dy: scale it here
-    gp.w_rad = need_y ? nullptr : a->w_rad;
+    gp.w_rad = a->w_rad;
+    gp.dyhat = rho_pass ? reinterpret_cast<float*>(wb + W.dX) : nullptr;
     const size_t smem = sizeof(float) * kEB * (wig_size(L) + H);
     k_wg_gather<L, T><<<static_cast<unsigned>((nb + kEB - 1) / kEB), 256, smem, st>>>(gp, feat, X, GT);
     E2A_LAUNCH_CHECK();
@@ -1160,16 +1161,14 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         if (e != E2A_OK) return e;
       }
     }
-    // dy = rho dyhat, and dW_rad[k][(l, c)] += sum_b rbf[b][k] drho[b][(l, c)]
-    // through per-range partials added in order
-    if (need_y) {
+    // dW_rad[k][(l, c)] += sum_b rbf[b][k] drho[b][(l, c)] through per-range
+    // partials added in order
+    if (rho_pass) {
       const int64_t per = kRhoPer;
       const int64_t nz = (nb + per - 1) / per;
       const dim3 grid(static_cast<unsigned>((K0 + 255) / 256), static_cast<unsigned>(nz));
-      k_wg_rho<L, T><<<grid, 256, 0, st>>>(
-          bl, nb, C, per, rbf, reinterpret_cast<const float*>(wb + W.rbfd), static_cast<const T*>(a->w_rad),
-          need_y ? Y : nullptr, GT, pl.w_rad ? rhopart : nullptr, e0 > 0,
-          pl.pos ? reinterpret_cast<float*>(wb + W.drp) : nullptr);
+      k_wg_rho<L><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, Y, reinterpret_cast<const float*>(wb + W.dX),
+                                        rhopart, e0 > 0);
       E2A_LAUNCH_CHECK();
     }
     if (pl.w_so2) {
@@ -1260,7 +1259,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       fp.rbf = rbf;
       fp.Y = Y;
       fp.dX = dX;
-      fp.drp = reinterpret_cast<const float*>(wb + W.drp);
+      fp.rbfd = reinterpret_cast<const float*>(wb + W.rbfd);
       fp.gedge = reinterpret_cast<float*>(wb + W.gedge);
       for (int d = 0; d < 3; ++d) fp.box[d] = pl.box[d];
       fp.periodic = pl.periodic;

@@ -332,10 +332,10 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   }
   if (st != E2A_OK) return st;
   // dW_rad by the fused kernel's radial pass where the MFMA build covers the
-  // shape, so that the batches need no SO2(x); with the positions asked for
-  // they form SO2(x) anyway and take dW_rad along
+  // shape, so that the batches need neither SO2(x) for it (without the
+  // positions) nor dyhat beside dy (with them)
   const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
-  const bool rad_mfma = grad_w_rad && !grad_pos &&
+  const bool rad_mfma = grad_w_rad &&
                         (a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok));
   if (rad_mfma) {
     BwdPlan rp{};
