@@ -247,7 +247,7 @@ def training_backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad,
     return {"train_backward_ms": ms, "train_backward_tflops": tflops,
             "train_backward_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS, "train_backward_finite": finite,
             "train_backward_kernels": "e2a_attention_bwd_weights: dL/dh and dW_q, dW_k, dW_rad, dW_so2 "
-                                      "(per-edge batches of 65536, GEMMs on the matrix cores)"}
+                                      "(per-edge batches of 262144, GEMMs on the matrix cores)"}
 
 
 def main():

@@ -280,7 +280,7 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
  * there); the query pass runs only when grad_feat, grad_w_q or grad_w_k is
  * set.  W_rad and W_so2 sum over all edges into matrices too large for a
  * workgroup, so the workspace holds per-edge tensors for one batch of at
- * most 65536 edges at a time: rotated features and cotangents (storage
+ * most 262144 edges at a time: rotated features and cotangents (storage
  * precision), SO2(x) in fp32.  The GEMMs run on the matrix cores for bf16
  * storage (bf16 operands, fp32 sums) and in fp32 otherwise; all sums run in
  * a fixed order, so results are bit-reproducible.  Asynchronous.  Errors as

@@ -33,7 +33,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int64_t kWgBatch = 65536;   // edges per batch
+constexpr int64_t kWgBatch = 262144;  // edges per batch (14 GB of batch tensors at L = 4, C = 128)
 constexpr int kEB = 16;               // edges per gather workgroup
 constexpr int64_t kRhoPer = 8;        // edges per k_wg_rho range
 
