@@ -39,6 +39,9 @@ __global__ void k_qk(const T* __restrict__ feat, const T* __restrict__ wq, const
     float aq[16], ak[16];
 #pragma unroll
     for (int a = 0; a < 16; ++a) { aq[a] = 0.0f; ak[a] = 0.0f; }
+    // unrolled so that several weight loads are in flight at once (the sums
+    // still run over cp in order)
+#pragma unroll 8
     for (int cp = 0; cp < C; ++cp) {
       const float wqv = load_as_f32(wq, (size_t)cp * C + c);
       const float wkv = load_as_f32(wk, (size_t)cp * C + c);
