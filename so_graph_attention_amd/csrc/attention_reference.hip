@@ -27,7 +27,7 @@ namespace {
 template <typename T>
 __global__ void k_qk(const T* __restrict__ feat, const T* __restrict__ wq, const T* __restrict__ wk,
                      int64_t n, int C, int ncomp, float* __restrict__ q, float* __restrict__ k) {
-  extern __shared__ float h0[];  // [16][C]
+  extern __shared__ __attribute__((aligned(16))) float h0[];  // [16][C]
   const int64_t i0 = blockIdx.x * 16ll;
   const int nb = (n - i0) < 16 ? static_cast<int>(n - i0) : 16;
   for (int t = threadIdx.x; t < nb * C; t += blockDim.x) {
@@ -39,10 +39,33 @@ __global__ void k_qk(const T* __restrict__ feat, const T* __restrict__ wq, const
     float aq[16], ak[16];
 #pragma unroll
     for (int a = 0; a < 16; ++a) { aq[a] = 0.0f; ak[a] = 0.0f; }
-    // unrolled so that several weight loads are in flight at once (the sums
-    // still run over cp in order)
-#pragma unroll 8
-    for (int cp = 0; cp < C; ++cp) {
+    // four input channels per step: one 16-byte LDS read per atom instead of
+    // four (the sums still run over cp in order)
+    int cp = 0;
+    if (C % 4 == 0) {
+#pragma unroll 2
+      for (; cp < C; cp += 4) {
+        float wqv[4], wkv[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wqv[u] = load_as_f32(wq, (size_t)(cp + u) * C + c);
+          wkv[u] = load_as_f32(wk, (size_t)(cp + u) * C + c);
+        }
+#pragma unroll
+        for (int a = 0; a < 16; ++a) {
+          const float4 hv = *reinterpret_cast<const float4*>(h0 + (a < nb ? a : 0) * C + cp);
+          aq[a] += hv.x * wqv[0];
+          ak[a] += hv.x * wkv[0];
+          aq[a] += hv.y * wqv[1];
+          ak[a] += hv.y * wkv[1];
+          aq[a] += hv.z * wqv[2];
+          ak[a] += hv.z * wkv[2];
+          aq[a] += hv.w * wqv[3];
+          ak[a] += hv.w * wkv[3];
+        }
+      }
+    }
+    for (; cp < C; ++cp) {
       const float wqv = load_as_f32(wq, (size_t)cp * C + c);
       const float wkv = load_as_f32(wk, (size_t)cp * C + c);
 #pragma unroll
