@@ -245,6 +245,15 @@ def test_pos_deterministic_and_with_weights(B):
     a = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=(), pos_grad=True)
     b = gpu_wgrad(B, w, d, out, lse, pos_grad=True)
     assert np.array_equal(a["pos"], b["pos"])
+    # the scalar kernels with fp32 storage, where dW_rad comes from the edge
+    # batches: the same positions with and without it
+    w = make_config("tiny", L=2, C=16, H=2)
+    rp, col, d, G = setup(w, seed=85)
+    out, lse = forward(B, w, d)
+    a = gpu_wgrad(B, w, d, out, lse, variant="reference", feat_grad=False, weights=(), pos_grad=True)
+    b = gpu_wgrad(B, w, d, out, lse, variant="reference", pos_grad=True)
+    c = gpu_wgrad(B, w, d, out, lse, variant="reference", pos_grad=True)
+    assert np.array_equal(a["pos"], b["pos"]) and np.array_equal(b["pos"], c["pos"])
 
 
 def test_wgrad_no_edges_and_isolated_atom(B):
