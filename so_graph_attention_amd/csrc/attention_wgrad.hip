@@ -127,9 +127,10 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
   constexpr int WS = wig_size(L);
   constexpr int w = 2 * l + 1;
   const int C = p.C, H = p.H, dh = C / H;
-  for (int t = tid; t < kEB * C; t += blockDim.x) {
-    const int s = t / C, c = t - s * C;
-    if (ii[s] < 0) continue;
+  const T* wr = static_cast<const T*>(p.w_rad);
+  // one (edge, channel) of the degree; wrc holds the channel's radial weights
+  auto item = [&](int s, int c, const float (&wrc)[8]) {
+    if (ii[s] < 0) return;
     const T* hj = feat + ((int64_t)jj[s] * K + l * l) * C + c;
     const float* gi = p.grad + ((int64_t)ii[s] * K + l * l) * C + c;
     float hv[w], gv[w];
@@ -140,11 +141,8 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
     }
     const float a0 = al[s * H + c / dh];
     float rho = 0.0f;
-    {
-      const T* wr = static_cast<const T*>(p.w_rad);
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) rho += rb[s * 8 + kk] * load_as_f32(wr, (size_t)(kk * (L + 1) + l) * C + c);
-    }
+    for (int kk = 0; kk < 8; ++kk) rho += rb[s * 8 + kk] * wrc[kk];
     const float a = a0 * rho;
     const float* Dl = D + s * WS + wig_off(l);
 #pragma unroll
@@ -159,6 +157,25 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
       store_as(X, idx, x);
       store_as(GT, idx, g * a);
       if (p.dyhat) p.dyhat[idx] = g * a0;
+    }
+  };
+  auto load_wr = [&](int c, float (&wrc)[8]) {
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) wrc[kk] = load_as_f32(wr, (size_t)(kk * (L + 1) + l) * C + c);
+  };
+  if (blockDim.x % C == 0) {
+    // the thread keeps one channel for all its edges (C = 128: two edges a
+    // pass), so its radial weights are loaded once per degree
+    const int c = tid % C, step = blockDim.x / C;
+    float wrc[8];
+    load_wr(c, wrc);
+    for (int s = tid / C; s < kEB; s += step) item(s, c, wrc);
+  } else {
+    for (int t = tid; t < kEB * C; t += blockDim.x) {
+      const int s = t / C, c = t - s * C;
+      float wrc[8];
+      load_wr(c, wrc);
+      item(s, c, wrc);
     }
   }
   if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
