@@ -76,15 +76,16 @@ const char* e2a_last_error_message(void);
 size_t e2a_neighbors_workspace_bytes(int64_t n_atoms);
 
 /*
- * Radius graph N(i) = { j != i : batch_j == batch_i, d_ij < cutoff }
+ * Radius graph N(i) = { j != i : batch_j == batch_i, 0 < d_ij < cutoff }
  * (technical summary section 1: |E| ~ kN neighbour edges; section 2.2:
  * the kernel iterates j in N(i)).
  *
  * The predicate is evaluated in fp32 with every operation correctly rounded
  * and no fused multiply-add: dx = x_j - x_i per axis; in a periodic box
  * dx -= box if dx > box/2, else dx += box if dx < -box/2; d2 = (dx*dx + dy*dy)
- * + dz*dz; neighbour iff d2 < cutoff*cutoff (strict).  The result is exact
- * and deterministic (independent of launch order).
+ * + dz*dz; neighbour iff 0 < d2 < cutoff*cutoff.  Two atoms at one point
+ * (d2 = 0) have no edge direction and are not each other's neighbours.  The
+ * result is exact and deterministic (independent of launch order).
  *
  *   pos          device f32 [n_atoms, 3].  Periodic: each coordinate must lie
  *                in [0, box_d); otherwise E2A_ERR_INVALID_ARG.
@@ -121,7 +122,8 @@ typedef struct e2a_attn_args {
   const float* pos;        /* device f32 [n_atoms, 3]                                 */
   const float* box;        /* HOST f32 [3] or NULL (open); minimum image when set    */
   int64_t n_atoms;
-  const int64_t* row_ptr;  /* device i64 [n_atoms + 1] (CSR by destination)          */
+  const int64_t* row_ptr;  /* device i64 [n_atoms + 1] (CSR by destination);
+                              row_ptr[0] = 0 and row_ptr[n_atoms] = n_edges            */
   const int32_t* col;      /* device i32 [n_edges], neighbour j of each edge          */
   int64_t n_edges;
   float cutoff;            /* radius used by the radial basis envelope               */
@@ -172,7 +174,13 @@ size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int d
  * matrix with row (l_in - m)*C + c_in and column (l_out - m)*C + c_out; one
  * such matrix (W0) for m = 0, two (W1 then W2) for each m >= 1.
  *
- * An atom with no neighbours gets o_i = 0 and lse = -inf.  Asynchronous: no
+ * An atom with no neighbours gets o_i = 0 and lse = -inf.  An edge of zero
+ * length (two atoms at one point, which e2a_build_neighbors never pairs) has
+ * no direction; it takes r_hat = z (the identity frame).  Range: every matrix
+ * product takes bf16 operands (fp32's exponent range) and sums in fp32, so
+ * inputs of any magnitude within fp32's normal range keep the stated
+ * precision; scaling w_so2 or w_rad by a power of two scales o exactly.
+ * Asynchronous: no
  * host synchronisation, no device-memory set or copy commands, only kernel
  * launches on the stream (so a caller may record the call into a HIP graph).
  * Deterministic: the same inputs give bit-identical outputs.  Errors: E2A_ERR_INVALID_ARG (null pointer, C % H != 0,

@@ -15,6 +15,7 @@ from .e2a_oracle import (  # noqa: F401
     edge_messages_vjp,
     edge_messages_weight_vjp,
     edge_rotation,
+    edge_unit,
     min_image,
     neighbor_list,
     neighbor_list_bruteforce,

@@ -39,14 +39,16 @@ def _pair_test_f32(pos32, box32, i, j, rc2):
     """The exact fp32 neighbour predicate for pairs (i, j), evaluated with
     NumPy float32 arithmetic (each operation correctly rounded, no fusion):
     dx = x_j - x_i per axis; periodic wrap by one box length when |dx| > box/2;
-    d2 = (dx*dx + dy*dy) + dz*dz; neighbour iff d2 < rc2 (strict)."""
+    d2 = (dx*dx + dy*dy) + dz*dz; neighbour iff 0 < d2 < rc2.  The lower bound
+    is a reading: two atoms at one point (d2 = 0 in fp32) have no edge
+    direction, so they are not each other's neighbours."""
     d = pos32[j] - pos32[i]                       # float32
     if box32 is not None:
         half = np.float32(0.5) * box32
         d = np.where(d > half, d - box32, np.where(d < -half, d + box32, d)).astype(np.float32)
     sq = d * d
     d2 = (sq[..., 0] + sq[..., 1]) + sq[..., 2]
-    return d2 < rc2
+    return (d2 > 0) & (d2 < rc2)
 
 
 def _csr_from_pairs(n, src_i, dst_j):
@@ -63,7 +65,8 @@ def neighbor_list(pos, cutoff, box=None, batch=None):
     """Radius graph j in N(i), |E| ~ kN (technical summary section 1, "Problem
     Statement"; section 2.2, "Streaming Reduction" iterates j in N(i)).
 
-    Readings (the pages fix none of them): strict d < r_c, no self loop,
+    Readings (the pages fix none of them): strict d < r_c, no self loop, no
+    pair of atoms at one point (d = 0),
     same-batch only, minimum image in a periodic box, the fp32 predicate of
     ``_pair_test_f32``.  Rows are sorted by destination i, then ascending j.
     Candidate pairs come from a KD-tree query at a slightly larger radius
@@ -261,6 +264,18 @@ def so2_blocks(w_so2, L, C):
     return out
 
 
+def edge_unit(rvec):
+    """Length r and unit vector r_hat of edge vectors [..., 3].  A zero-length
+    edge has no direction; the reading taken here gives it r_hat = z (the
+    identity frame), so its message stays finite.  ``neighbor_list`` never
+    pairs two atoms at one point; only a hand-made graph has such an edge."""
+    rvec = np.asarray(rvec, dtype=np.float64)
+    r = np.linalg.norm(rvec, axis=-1)
+    safe = np.where(r > 0, r, 1.0)
+    u = np.where((r > 0)[..., None], rvec / safe[..., None], np.array([0.0, 0.0, 1.0]))
+    return r, u
+
+
 def min_image(rvec, box):
     """Minimum-image difference vector in fp64 (positions in [0, box))."""
     r = np.asarray(rvec, dtype=np.float64)
@@ -292,8 +307,8 @@ def edge_messages(rvec, h_src, w_rad, w_so2, L, C, cutoff, gauge=None, rho=None,
     rvec = np.asarray(rvec, dtype=np.float64)
     h = np.asarray(h_src, dtype=np.float64)
     E = rvec.shape[0]
-    r = np.linalg.norm(rvec, axis=1)
-    R = edge_rotation(rvec / r[:, None])
+    r, rhat = edge_unit(rvec)
+    R = edge_rotation(rhat)
     if gauge is not None:
         R = rotation_z(gauge) @ R
     if blocks is None:
@@ -340,8 +355,8 @@ def edge_messages_vjp(rvec, g, w_rad, w_so2, L, C, cutoff, blocks=None):
     rvec = np.asarray(rvec, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
     E = rvec.shape[0]
-    r = np.linalg.norm(rvec, axis=1)
-    R = edge_rotation(rvec / r[:, None])
+    r, rhat = edge_unit(rvec)
+    R = edge_rotation(rhat)
     if blocks is None:
         blocks = so2_blocks(w_so2, L, C)
     D = [wigner_d(l, R) for l in range(L + 1)]
@@ -583,8 +598,8 @@ def edge_messages_weight_vjp(rvec, h_src, g, w_rad, w_so2, L, C, cutoff, blocks=
     rvec = np.asarray(rvec, dtype=np.float64)
     h = np.asarray(h_src, dtype=np.float64)
     g = np.asarray(g, dtype=np.float64)
-    r = np.linalg.norm(rvec, axis=1)
-    R = edge_rotation(rvec / r[:, None])
+    r, rhat = edge_unit(rvec)
+    R = edge_rotation(rhat)
     if blocks is None:
         blocks = so2_blocks(w_so2, L, C)
     D = [wigner_d(l, R) for l in range(L + 1)]

@@ -63,8 +63,8 @@ __device__ void edge_frame(const BwdParams& p, int64_t a, int64_t b, float* D, f
     }
     r3[d] = dx;
   }
-  const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-  const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+  float u[3];
+  const float r = edge_unit(r3, u);
   float R[3][3];
   edge_rotation(u, R);
   wigner_blocks<L>(R, D);

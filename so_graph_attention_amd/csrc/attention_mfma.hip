@@ -215,8 +215,8 @@ __device__ __forceinline__ f32x16 mfma_bf16(const bf16x8 a, const bf16x8 b, cons
 __device__ __forceinline__ f32x16 mfma_f16(const f16x8 a, const f16x8 b, const f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16_f16(const f16x8 a, const f16x8 b, const f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma16_bf16(const bf16x8 a, const bf16x8 b, const f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 // Node accumulator of one degree lo for this wave's 32 channels: two 16x16
@@ -249,10 +249,10 @@ __host__ __device__ constexpr bool packed_lo() { return 2 * LO + 1 <= 8; }
 // lanes 16 g .. 16 g + 15: groups 0 and 2 carry channels 0-15, groups 1 and 3
 // channels 16-31, so each of the two MFMAs keeps its own groups and zeroes
 // the others.  G (the D rows) is the same register for both.
-__device__ __forceinline__ void rotate_out_step(NodeAcc& acc, const f16x8 g, const f16x8 u, bool grp_odd) {
-  const f16x8 zero = {};
-  acc.a = mfma16_f16(g, grp_odd ? zero : u, acc.a);
-  acc.b = mfma16_f16(g, grp_odd ? u : zero, acc.b);
+__device__ __forceinline__ void rotate_out_step(NodeAcc& acc, const bf16x8 g, const bf16x8 u, bool grp_odd) {
+  const bf16x8 zero = {};
+  acc.a = mfma16_bf16(g, grp_odd ? zero : u, acc.a);
+  acc.b = mfma16_bf16(g, grp_odd ? u : zero, acc.b);
 }
 
 // Row of a 32x32 MFMA result held by accumulator register r of a lane in
@@ -267,7 +267,7 @@ struct MfmaParams {
   const float* k;
   const uint16_t* feat;
   const bf16x8* wpk;
-  const f16x8* radpk;
+  const bf16x8* radpk;    // W_rad as [(L+1) C] vectors of its 8 basis weights (bf16, exact)
   const int32_t* order;   // destination atoms in spatial (Morton) order
   int64_t n_atoms;
   int wg_per_xcd;
@@ -302,7 +302,7 @@ struct Smem {
 // Per-lane constants of one chunk.
 struct Lane {
   float alpha[16];   // softmax weights of the 16 edges whose GEMM rows the lane holds (its head)
-  f16x8 arbf[3];     // radial-basis A operands (all 32 edges; edges 0-15; edges 16-31)
+  bf16x8 arbf[3];    // radial-basis A operands (all 32 edges; edges 0-15; edges 16-31)
   u32x4 mk[2];       // per fp16 pair of the rotate-out operand: keep A's edges (edge groups 0, 16)
   uint32_t flip;     // ~0 on lanes whose packed rows (n >= 8) belong to B
   int nA;            // query pass: edges 0 .. nA-1 belong to A
@@ -379,16 +379,16 @@ __device__ __forceinline__ void rho_pair(const MfmaParams& p, const Smem& s, int
   const int lane = opaque(tid) & 63, wave = tid >> 6;
   const int e = 4 * wave + ((lane & 15) >> 2);   // the edge of A's row lane % 16
   const bool diag = (lane & 3) == (lane >> 4);
-  f16x8 a0 = {}, a1 = {};
+  bf16x8 a0 = {}, a1 = {};
   if (diag) {
-    a0 = to_vec8<f16x8>(s.rbf + e * 8);
-    a1 = to_vec8<f16x8>(s.rbf + (e + 16) * 8);
+    a0 = to_vec8<bf16x8>(s.rbf + e * 8);
+    a1 = to_vec8<bf16x8>(s.rbf + (e + 16) * 8);
   }
-  const f16x8* wl = p.radpk + l * kC + 8 * (lane & 15) + (lane >> 4);
-  const f16x8 b0 = wl[0], b1 = wl[4];
+  const bf16x8* wl = p.radpk + l * kC + 8 * (lane & 15) + (lane >> 4);
+  const bf16x8 b0 = wl[0], b1 = wl[4];
   const f32x4 z = {};
-  const f32x4 r00 = mfma16_f16(a0, b0, z), r01 = mfma16_f16(a0, b1, z);
-  const f32x4 r10 = mfma16_f16(a1, b0, z), r11 = mfma16_f16(a1, b1, z);
+  const f32x4 r00 = mfma16_bf16(a0, b0, z), r01 = mfma16_bf16(a0, b1, z);
+  const f32x4 r10 = mfma16_bf16(a1, b0, z), r11 = mfma16_bf16(a1, b1, z);
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     rho[0][r] = r00[r];
@@ -451,15 +451,16 @@ __device__ __forceinline__ void rotate_in(const MfmaParams& p, const Smem& s, in
 }
 
 // A operand of the rotate-out contraction: row n of D^l rows `mrow`, for the
-// 8 edges eg + crow(q, h), q = 0..7, as fp16.  Rows n >= 2l+1 are zero.
-__device__ __forceinline__ f16x8 dt_frag(const _Float16* row_base, int eg, int h, bool valid) {
+// 8 edges eg + crow(q, h), q = 0..7, read as fp16 and rounded to bf16 (the
+// type of the other operand, whose range is fp32's).  Rows n >= 2l+1 are zero.
+__device__ __forceinline__ bf16x8 dt_frag(const _Float16* row_base, int eg, int h, bool valid) {
   f16x8 v = {};
   if (valid) {
     const f16x4 a = *reinterpret_cast<const f16x4*>(row_base + eg + 4 * h);
     const f16x4 b = *reinterpret_cast<const f16x4*>(row_base + eg + 8 + 4 * h);
     v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   }
-  return v;
+  return __builtin_convertvector(__builtin_convertvector(v, f32x8), bf16x8);
 }
 
 // Rotate-out of one fragment: D^LO row `row`, the 8 edges of group eg that
@@ -468,7 +469,7 @@ __device__ __forceinline__ f16x8 dt_frag(const _Float16* row_base, int eg, int h
 // other destination's edges are zero.  Degree 4: A's edges go to acc[4] and,
 // when the chunk has a B, B's edges to hi.
 template <int L, int LO, int ROW, int EG>
-__device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const Lane& ln, int lane, const f16x8 u,
+__device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const Lane& ln, int lane, const bf16x8 u,
                                         bool has_b) {
   constexpr int W = 2 * LO + 1;
   const int n = lane & 15;
@@ -478,10 +479,10 @@ __device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const L
   const u32x4 g = __builtin_bit_cast(u32x4, dt_frag(drow, EG, lane >> 5, ncol < W));
   const u32x4 mA = ln.mk[EG / 16];
   if constexpr (packed_lo<LO>()) {
-    rotate_out_step(ns.acc[LO], __builtin_bit_cast(f16x8, g & (mA ^ ln.flip)), u, grp_odd);
+    rotate_out_step(ns.acc[LO], __builtin_bit_cast(bf16x8, g & (mA ^ ln.flip)), u, grp_odd);
   } else {
-    rotate_out_step(ns.acc[LO], __builtin_bit_cast(f16x8, g & mA), u, grp_odd);
-    if (has_b) rotate_out_step(ns.hi, __builtin_bit_cast(f16x8, g & ~mA), u, grp_odd);
+    rotate_out_step(ns.acc[LO], __builtin_bit_cast(bf16x8, g & mA), u, grp_odd);
+    if (has_b) rotate_out_step(ns.hi, __builtin_bit_cast(bf16x8, g & ~mA), u, grp_odd);
   }
 }
 
@@ -492,14 +493,14 @@ __device__ __forceinline__ void rot_out(NodeState<L>& ns, const Smem& s, const L
 // share accumulator tiles in pairs: an even degree uses rows 0-7 (k), an odd
 // one rows 8-15.
 template <int L, int LO, int EG>
-__device__ __forceinline__ void rad_acc(NodeState<L>& ns, const Smem& s, int lane, const f16x8 t) {
+__device__ __forceinline__ void rad_acc(NodeState<L>& ns, const Smem& s, int lane, const bf16x8 t) {
   const int row = lane & 15;
   const bool valid = (LO & 1) ? row >= 8 : row < 8;
   const int k = row & 7, h = lane >> 5;
-  f16x8 a = {};
+  bf16x8 a = {};
   if (valid) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) a[q] = static_cast<_Float16>(s.rbf[(EG + crow(q, h)) * 8 + k]);
+    for (int q = 0; q < 8; ++q) a[q] = static_cast<__bf16>(s.rbf[(EG + crow(q, h)) * 8 + k]);
   }
   rotate_out_step(ns.rad[LO / 2], a, t, (lane >> 4) & 1);
 }
@@ -655,7 +656,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
     f32x16 c00 = {}, c01 = {}, c10 = {}, c11 = {};
     // radial-weight fragments of this block's output degrees, fetched now so
     // that they have landed by the epilogue
-    f16x8 brad0 = zero8, brad1 = zero8;
+    bf16x8 brad0 = {}, brad1 = {};
     if (MD != kBwdV && MD != kBwdR && half == 0) {
       brad0 = p.radpk[S::blk_lo(M, b, 0) * kC + c_own];
       if constexpr (M == 0 && S::has1(M, b)) brad1 = p.radpk[S::blk_lo(M, b, 1) * kC + c_own];
@@ -712,19 +713,19 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
             float u[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) u[r] = c0[r];
-            rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
-            rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+            rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<bf16x8>(u), has_b);
+            rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<bf16x8>(u + 8), has_b);
           } else if constexpr (MD == kBwdR) {
             // t = alpha y (D G) per (edge, channel), alpha carrying the edge's scales
             const f32x16 gt = rot_grad<L, lo, 0, 0>(s, ln, lane, f == 0 ? gq0 : gq1, gq1);
             float t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) t[r] = ln.alpha[r] * c0[r] * gt[r];
-            rad_acc<L, lo, 0>(ns, s, lane, to_vec8<f16x8>(t));
-            rad_acc<L, lo, 16>(ns, s, lane, to_vec8<f16x8>(t + 8));
+            rad_acc<L, lo, 0>(ns, s, lane, to_vec8<bf16x8>(t));
+            rad_acc<L, lo, 16>(ns, s, lane, to_vec8<bf16x8>(t + 8));
           } else {
-            const f16x8 brad = f == 0 ? brad0 : brad1;
-            const f32x16 rho = mfma_f16(ln.arbf[0], brad, f32x16{});
+            const bf16x8 brad = f == 0 ? brad0 : brad1;
+            const f32x16 rho = mfma_bf16(ln.arbf[0], brad, f32x16{});
             if constexpr (MD == kBwdQ) {
               // the two operands are (lo0, lo1) for a pair, (A, B) for degree 4
               const f32x16 gt = rot_grad<L, lo, 0, 0>(s, ln, lane, f == 0 ? gq0 : gq1, gq1);
@@ -737,15 +738,15 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
               float u[16];
 #pragma unroll
               for (int r = 0; r < 16; ++r) u[r] = ln.alpha[r] * rho[r] * c0[r];
-              rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<f16x8>(u), has_b);
-              rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<f16x8>(u + 8), has_b);
+              rot_out<L, lo, lo, 0>(ns, s, ln, lane, to_vec8<bf16x8>(u), has_b);
+              rot_out<L, lo, lo, 16>(ns, s, ln, lane, to_vec8<bf16x8>(u + 8), has_b);
             }
           }
         }
       });
     } else {
       constexpr int lo = S::blk_lo(M, b, 0);
-      const f16x8 brad = brad0;
+      const bf16x8 brad = brad0;
       static_for<2>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         const f32x16& C1 = t == 0 ? c00 : c10;
@@ -757,8 +758,8 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
             up[r] = C1[r] - C2[r + 8];
             um[r] = C2[r] + C1[r + 8];
           }
-          rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
-          rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+          rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<bf16x8>(up), has_b);
+          rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<bf16x8>(um), has_b);
         } else if constexpr (MD == kBwdR) {
           // the edge's +M and -M rows summed: drho takes sum over m
           const f32x16 gt = rot_grad<L, lo, M, t>(s, ln, lane, gq0, gq1);
@@ -766,9 +767,9 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
 #pragma unroll
           for (int r = 0; r < 8; ++r)
             ts[r] = ln.alpha[8 * t + r] * ((C1[r] - C2[r + 8]) * gt[r] + (C2[r] + C1[r + 8]) * gt[r + 8]);
-          rad_acc<L, lo, 16 * t>(ns, s, lane, to_vec8<f16x8>(ts));
+          rad_acc<L, lo, 16 * t>(ns, s, lane, to_vec8<bf16x8>(ts));
         } else {
-          const f32x16 rho = mfma_f16(ln.arbf[1 + t], brad, f32x16{});
+          const f32x16 rho = mfma_bf16(ln.arbf[1 + t], brad, f32x16{});
           if constexpr (MD == kBwdQ) {
             // tile rows r and r + 16 are the +M and -M rows of one edge
             const f32x16 gt = rot_grad<L, lo, M, t>(s, ln, lane, gq0, gq1);
@@ -785,8 +786,8 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
               up[r] = sc * (C1[r] - C2[r + 8]);
               um[r] = sc * (C2[r] + C1[r + 8]);
             }
-            rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(up), has_b);
-            rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<f16x8>(um), has_b);
+            rot_out<L, lo, lo + M, 16 * t>(ns, s, ln, lane, to_vec8<bf16x8>(up), has_b);
+            rot_out<L, lo, lo - M, 16 * t>(ns, s, ln, lane, to_vec8<bf16x8>(um), has_b);
           }
         }
       });
@@ -1089,8 +1090,8 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           }
           r3[d] = dx;
         }
-        const float rr = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-        const float u[3] = {r3[0] / rr, r3[1] / rr, r3[2] / rr};
+        float u[3];
+        const float rr = edge_unit(r3, u);
         edge_rotation(u, R);
         d0 = 1.0f;
         radial_basis8(rr, p.cutoff, e8);
@@ -1196,9 +1197,9 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       }
       float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
       const int rr = lnr & 31;
-      ln.arbf[0] = to_vec8<f16x8>(half == 0 ? s.rbf + rr * 8 : z);
-      ln.arbf[1] = to_vec8<f16x8>(half == 0 ? s.rbf + (rr & 15) * 8 : z);
-      ln.arbf[2] = to_vec8<f16x8>(half == 0 ? s.rbf + (16 + (rr & 15)) * 8 : z);
+      ln.arbf[0] = to_vec8<bf16x8>(half == 0 ? s.rbf + rr * 8 : z);
+      ln.arbf[1] = to_vec8<bf16x8>(half == 0 ? s.rbf + (rr & 15) * 8 : z);
+      ln.arbf[2] = to_vec8<bf16x8>(half == 0 ? s.rbf + (16 + (rr & 15)) * 8 : z);
 #pragma unroll
       for (int g = 0; g < 2; ++g)
 #pragma unroll
@@ -1300,15 +1301,16 @@ __global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ 
   *reinterpret_cast<uint4*>(out + v) = o;
 }
 
-// W_rad [8][L+1][C] -> [(L+1) C] vectors of 8 basis weights.
+// W_rad [8][L+1][C] -> [(L+1) C] vectors of 8 basis weights (bf16, copied
+// bit for bit).
 template <int L>
-__global__ void k_pack_rad(const uint16_t* __restrict__ w, f16x8* __restrict__ out) {
+__global__ void k_pack_rad(const uint16_t* __restrict__ w, u32x4* __restrict__ out) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
   if (v >= (L + 1) * kC) return;
-  float vals[8];
+  uint32_t b[8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) vals[q] = __uint_as_float(uint32_t(w[q * (L + 1) * kC + v]) << 16);
-  out[v] = to_vec8<f16x8>(vals);
+  for (int q = 0; q < 8; ++q) b[q] = w[q * (L + 1) * kC + v];
+  out[v] = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
 }
 
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
@@ -1544,7 +1546,7 @@ e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_
   k_pack_so2<L, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
                                                           reinterpret_cast<bf16x8*>(wb + W.w));
   k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_rad),
-                                                            reinterpret_cast<f16x8*>(wb + W.rad));
+                                                            reinterpret_cast<u32x4*>(wb + W.rad));
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
@@ -1560,7 +1562,7 @@ e2a_status base_params(const e2a_attn_args* a, const MfmaWs& W, char* wb, const 
   p.col = a->col;
   p.feat = static_cast<const uint16_t*>(a->feat);
   p.wpk = reinterpret_cast<const bf16x8*>(wb + W.w);
-  p.radpk = reinterpret_cast<const f16x8*>(wb + W.rad);
+  p.radpk = reinterpret_cast<const bf16x8*>(wb + W.rad);
   p.order = reinterpret_cast<const int32_t*>(wb + W.order);
   p.n_atoms = a->n_atoms;
   int dev = 0, n_cu = 0;

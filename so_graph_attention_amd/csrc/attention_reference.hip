@@ -156,22 +156,24 @@ __global__ void __launch_bounds__(256) k_attention_reference(RefParams p, const 
         }
         r3[d] = dx;
       }
-      const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-      const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+      float u[3];
+      const float r = edge_unit(r3, u);
       float R[3][3];
       edge_rotation(u, R);
       wigner_blocks<L>(R, D);
       radial_basis8(r, p.cutoff, rbf);
     }
-    if (p.conv && tid >= 64 && tid < 64 + H) {
-      // convolution: weight 1 for every edge, nothing to rescale
-      const int h = tid - 64;
-      sl[h] = 1.0f;
-      sm[h] = 0.0f;
-      st[h] = 1.0f;
-      sp[h] = 1.0f;
-    } else if (tid >= 64 && tid < 64 + H) {
-      const int h = tid - 64;
+    // threads 64.. take the heads in turn (any H), while thread 0 builds the
+    // edge's geometry
+    for (int h = tid - 64; tid >= 64 && h < H; h += static_cast<int>(blockDim.x) - 64) {
+      if (p.conv) {
+        // convolution: weight 1 for every edge, nothing to rescale
+        sl[h] = 1.0f;
+        sm[h] = 0.0f;
+        st[h] = 1.0f;
+        sp[h] = 1.0f;
+        continue;
+      }
       const int j = p.col[e];
       float s = 0.0f;
       for (int d = 0; d < dh; ++d) s += qi[h * dh + d] * p.k[(int64_t)j * C + h * dh + d];

@@ -244,8 +244,8 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
         }
         r3[d] = dx;
       }
-      const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-      const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+      float u[3];
+      const float r = edge_unit(r3, u);
       float R[3][3];
       edge_rotation(u, R);
       float* De = D + tid * WS;
@@ -502,8 +502,8 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
       }
       r3[d] = dx;
     }
-    const float r = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
-    const float u[3] = {r3[0] / r, r3[1] / r, r3[2] / r};
+    float u[3];
+    const float r = edge_unit(r3, u);
     fr[wv][0] = u[0];
     fr[wv][1] = u[1];
     fr[wv][2] = u[2];
@@ -533,11 +533,14 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
     for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
   if (lane == 0) {
     const float* u = fr[wv];
-    const float ir = 1.0f / u[3];
-    // (T x u) / |r| + s u
-    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + sv * u[0];
-    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + sv * u[1];
-    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + sv * u[2];
+    // (T x u) / |r| + s u; an edge of zero length has no direction to move
+    // along and contributes nothing
+    const bool has_len = u[3] > 0.0f;
+    const float ir = has_len ? 1.0f / u[3] : 0.0f;
+    const float s = has_len ? sv : 0.0f;
+    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + s * u[0];
+    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + s * u[1];
+    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
   }
 }
 

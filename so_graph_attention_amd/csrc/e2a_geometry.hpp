@@ -22,6 +22,24 @@ namespace e2a {
 E2A_HD constexpr int wig_off(int l) { return l * (4 * l * l - 1) / 3; }
 E2A_HD constexpr int wig_size(int L) { return wig_off(L + 1); }
 
+// Length of the edge vector r3 and its unit vector u.  An edge of zero length
+// has no direction; it takes u = z (the identity frame), so that every value
+// derived from it stays finite.  The neighbour build never pairs two atoms at
+// one point, so such an edge only occurs in a caller-built graph.
+E2A_HD float edge_unit(const float r3[3], float u[3]) {
+  const float rr = sqrtf(r3[0] * r3[0] + r3[1] * r3[1] + r3[2] * r3[2]);
+  if (rr > 0.0f) {
+    u[0] = r3[0] / rr;
+    u[1] = r3[1] / rr;
+    u[2] = r3[2] / rr;
+  } else {
+    u[0] = 0.0f;
+    u[1] = 0.0f;
+    u[2] = 1.0f;
+  }
+  return rr;
+}
+
 // Rotation R with R r_hat = z: R = R_y(-theta) R_z(-phi) for r_hat =
 // (sin t cos p, sin t sin p, cos t).  Rows: (ct cp, ct sp, -st), (-sp, cp, 0),
 // (st cp, st sp, ct).  At the poles phi = 0.

@@ -17,6 +17,11 @@ void tangent_blocks(int L, const float* D, float* dD) {
 
 extern "C" {
 
+// Unit vectors and lengths of edge vectors r [n][3] (zero-length edges take z).
+void e2a_host_edge_unit(const float* r, int n, float* u_out, float* len_out) {
+  for (int e = 0; e < n; ++e) len_out[e] = e2a::edge_unit(r + 3 * e, u_out + 3 * e);
+}
+
 void e2a_host_edge_rotation(const float* rhat, int n, float* R_out) {
   for (int e = 0; e < n; ++e) {
     float R[3][3];

@@ -72,7 +72,8 @@ __device__ __forceinline__ bool pair_ok(const float* pi, const float* pj, const 
     const float sq = __fmul_rn(dx, dx);
     d2 = (d == 0) ? sq : __fadd_rn(d2, sq);
   }
-  return d2 < g.rc2;
+  // d2 = 0 (two atoms at one point in fp32) gives no edge: such a pair has no direction
+  return d2 > 0.0f && d2 < g.rc2;
 }
 
 // ---- bounding box ---------------------------------------------------------

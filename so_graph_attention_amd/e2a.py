@@ -146,7 +146,10 @@ def _box_arg(box):
     return arr, ctypes.cast(arr, ctypes.c_void_p)
 
 
-def _need(t: torch.Tensor, name: str, dtype=None, device=None):
+def _need(t: torch.Tensor, name: str, dtype=None, device=None, shape=None, numel=None):
+    """Raises unless t is a contiguous tensor of the given dtype, device and
+    shape (or element count).  Runs before any library call, so a wrong
+    argument never reaches a kernel as a bad pointer."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_contiguous():
@@ -155,120 +158,54 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None):
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} must be on {device}, got {t.device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
 
 
-def e2a_build_neighbors(pos: torch.Tensor, cutoff: float, box=None, batch: Optional[torch.Tensor] = None,
-                        capacity: Optional[int] = None, stream=None):
-    """CSR radius graph (row_ptr int64 [N+1], col int32 [E]) on pos.device."""
-    _need(pos, "pos", torch.float32)
-    n = pos.shape[0]
-    dev = pos.device
-    if batch is not None:
-        _need(batch, "batch", torch.int32, dev)
-    row_ptr = torch.empty(n + 1, dtype=torch.int64, device=dev)
-    ws = torch.empty(max(1, e2a_neighbors_workspace_bytes(n)), dtype=torch.uint8, device=dev)
-    cap = int(capacity) if capacity is not None else max(64, 64 * n)
-    box_arr, box_p = _box_arg(box)
-    while True:
-        col = torch.empty(max(1, cap), dtype=torch.int32, device=dev)
-        ne = ctypes.c_int64(0)
-        st = _lib.e2a_build_neighbors(_ptr(pos), n, _ptr(batch), box_p, ctypes.c_float(cutoff), _ptr(row_ptr),
-                                      _ptr(col), cap, ctypes.byref(ne), _ptr(ws), ws.numel(), _stream(stream))
-        if st == E2A_ERR_CAPACITY and capacity is None:
-            cap = int(ne.value)
-            continue
-        _check(st)
-        return row_ptr, col[: ne.value]
+def _gpu_device(pos: torch.Tensor) -> torch.device:
+    if not isinstance(pos, torch.Tensor):
+        raise TypeError("pos must be a torch.Tensor")
+    if pos.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {pos.device}")
+    return pos.device
 
 
-def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box, variant, out, out_lse,
-           workspace, stream):
-    dev = pos.device
-    n = pos.shape[0]
+def _storage_dtype(feat: torch.Tensor) -> int:
     if feat.dtype == torch.bfloat16:
-        dtype = E2A_DTYPE_BF16
-    elif feat.dtype == torch.float32:
-        dtype = E2A_DTYPE_F32
-    else:
-        raise TypeError("feat must be float32 or bfloat16")
-    _need(pos, "pos", torch.float32, dev)
-    _need(row_ptr, "row_ptr", torch.int64, dev)
-    _need(col, "col", torch.int32, dev)
-    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
-        if t is not None:
-            _need(t, name, feat.dtype, dev)
+        return E2A_DTYPE_BF16
+    if feat.dtype == torch.float32:
+        return E2A_DTYPE_F32
+    raise TypeError("feat must be float32 or bfloat16")
+
+
+def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box, variant,
+               workspace, need_qk=True):
+    """Checks the layer's inputs (device, dtype, shape) and fills the argument
+    struct.  Returns (args, box array that must stay alive for the call)."""
+    dev = _gpu_device(pos)
+    dtype = _storage_dtype(feat)
+    if variant not in VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(VARIANTS)}")
+    n = pos.shape[0]
     K = (L + 1) ** 2
-    if out is None:
-        out = torch.empty((n, K, C), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, dev)
-    if workspace is None:
-        workspace = torch.empty(max(1, e2a_attention_workspace_bytes(n, L, C, H, dtype)), dtype=torch.uint8,
-                                device=dev)
-    box_arr, box_p = _box_arg(box)
-    a = AttnArgs()
-    a.pos = _ptr(pos)
-    a.box = box_p
-    a.n_atoms = n
-    a.row_ptr = _ptr(row_ptr)
-    a.col = _ptr(col)
-    a.n_edges = col.numel()
-    a.cutoff = float(cutoff)
-    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
-    a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
-    a.out = _ptr(out)
-    a.out_lse = _ptr(out_lse)
-    a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel()
-    _check(fn(ctypes.byref(a), _stream(stream)))
-    del box_arr
-    return out
-
-
-def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
-                      cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
-                      workspace=None, stream=None, with_lse: bool = False):
-    """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
-
-    Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
-    if with_lse and out_lse is None:
-        out_lse = torch.empty((pos.shape[0], H), dtype=torch.float32, device=pos.device)
-    out = _layer(_lib.e2a_attention_fwd, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box,
-                 variant, out, out_lse, workspace, stream)
-    return (out, out_lse) if with_lse else out
-
-
-def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: int = 8, cutoff: float, box=None,
-                 variant: str = "auto", out=None, workspace=None, stream=None):
-    """Sum of the same per-edge messages without attention weights (the EAAS
-    convolution stage); returns out [N,(L+1)^2,C] fp32.  H only selects the
-    build (the MFMA kernel is built for H = 8)."""
-    return _layer(_lib.e2a_conv_fwd, pos, row_ptr, col, feat, None, None, w_rad, w_so2, L, C, H, cutoff, box,
-                  variant, out, None, workspace, stream)
-
-
-def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
-    return int(_lib.e2a_attention_bwd_workspace_bytes(n_atoms, n_edges, L, C, H))
-
-
-def _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff, box,
-              variant, workspace):
-    """Checks the backward calls' inputs and fills their argument struct;
-    returns (args, box array to keep alive)."""
-    dev = pos.device
-    n = pos.shape[0]
-    if feat.dtype == torch.bfloat16:
-        dtype = E2A_DTYPE_BF16
-    elif feat.dtype == torch.float32:
-        dtype = E2A_DTYPE_F32
-    else:
-        raise TypeError("feat must be float32 or bfloat16")
-    _need(pos, "pos", torch.float32, dev)
-    _need(row_ptr, "row_ptr", torch.int64, dev)
+    _need(pos, "pos", torch.float32, dev, shape=(n, 3))
+    _need(row_ptr, "row_ptr", torch.int64, dev, shape=(n + 1,))
     _need(col, "col", torch.int32, dev)
-    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
-        _need(t, name, feat.dtype, dev)
-    for name, t in (("out", out), ("out_lse", out_lse), ("grad_out", grad_out)):
-        _need(t, name, torch.float32, dev)
+    if col.dim() != 1:
+        raise ValueError("col must be one-dimensional")
+    _need(feat, "feat", feat.dtype, dev, shape=(n, K, C))
+    if need_qk:
+        _need(w_q, "w_q", feat.dtype, dev, shape=(C, C))
+        _need(w_k, "w_k", feat.dtype, dev, shape=(C, C))
+    _need(w_rad, "w_rad", feat.dtype, dev, shape=(8, L + 1, C))
+    _need(w_so2, "w_so2", feat.dtype, dev, numel=e2a_so2_param_count(L, C))
+    if out is not None:
+        _need(out, "out", torch.float32, dev, shape=(n, K, C))
+    if out_lse is not None:
+        _need(out_lse, "out_lse", torch.float32, dev, shape=(n, H))
+    _need(workspace, "workspace", torch.uint8, dev)
     box_arr, box_p = _box_arg(box)
     a = AttnArgs()
     a.pos = _ptr(pos)
@@ -287,6 +224,86 @@ def _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, gra
     return a, box_arr
 
 
+def e2a_build_neighbors(pos: torch.Tensor, cutoff: float, box=None, batch: Optional[torch.Tensor] = None,
+                        capacity: Optional[int] = None, stream=None):
+    """CSR radius graph (row_ptr int64 [N+1], col int32 [E]) on pos.device."""
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float32, dev, shape=(n, 3))
+    if batch is not None:
+        _need(batch, "batch", torch.int32, dev, shape=(n,))
+    row_ptr = torch.empty(n + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(1, e2a_neighbors_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    cap = int(capacity) if capacity is not None else max(64, 64 * n)
+    box_arr, box_p = _box_arg(box)
+    while True:
+        col = torch.empty(max(1, cap), dtype=torch.int32, device=dev)
+        ne = ctypes.c_int64(0)
+        st = _lib.e2a_build_neighbors(_ptr(pos), n, _ptr(batch), box_p, ctypes.c_float(cutoff), _ptr(row_ptr),
+                                      _ptr(col), cap, ctypes.byref(ne), _ptr(ws), ws.numel(), _stream(stream))
+        if st == E2A_ERR_CAPACITY and capacity is None:
+            cap = int(ne.value)
+            continue
+        _check(st)
+        return row_ptr, col[: ne.value]
+
+
+def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box, variant, out, out_lse,
+           workspace, stream, need_qk):
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    if out is None:
+        out = torch.empty((n, (L + 1) ** 2, C), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_attention_workspace_bytes(n, L, C, H, _storage_dtype(feat))),
+                                dtype=torch.uint8, device=dev)
+    a, box_arr = _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box,
+                            variant, workspace, need_qk=need_qk)
+    _check(fn(ctypes.byref(a), _stream(stream)))
+    del box_arr
+    return out
+
+
+def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
+                      cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
+                      workspace=None, stream=None, with_lse: bool = False):
+    """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
+
+    Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
+    if with_lse and out_lse is None:
+        out_lse = torch.empty((pos.shape[0], H), dtype=torch.float32, device=pos.device)
+    out = _layer(_lib.e2a_attention_fwd, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box,
+                 variant, out, out_lse, workspace, stream, True)
+    return (out, out_lse) if with_lse else out
+
+
+def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: int = 8, cutoff: float, box=None,
+                 variant: str = "auto", out=None, workspace=None, stream=None):
+    """Sum of the same per-edge messages without attention weights (the EAAS
+    convolution stage); returns out [N,(L+1)^2,C] fp32.  H only selects the
+    build (the MFMA kernel is built for H = 8)."""
+    return _layer(_lib.e2a_conv_fwd, pos, row_ptr, col, feat, None, None, w_rad, w_so2, L, C, H, cutoff, box,
+                  variant, out, None, workspace, stream, False)
+
+
+def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
+    return int(_lib.e2a_attention_bwd_workspace_bytes(n_atoms, n_edges, L, C, H))
+
+
+def _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff, box,
+              variant, workspace):
+    """Checks the backward calls' inputs and fills their argument struct;
+    returns (args, box array to keep alive)."""
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    K = (L + 1) ** 2
+    _need(out, "out", torch.float32, dev, shape=(n, K, C))
+    _need(out_lse, "out_lse", torch.float32, dev, shape=(n, H))
+    _need(grad_out, "grad_out", torch.float32, dev, shape=(n, K, C))
+    return _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box, variant,
+                      workspace)
+
+
 def e2a_attention_bwd_weights_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
     return int(_lib.e2a_attention_bwd_weights_workspace_bytes(n_atoms, n_edges, L, C, H))
 
@@ -300,7 +317,7 @@ def e2a_attention_bwd_weights(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, o
     positions, for grad_out = dL/do.  Returns a dict of fp32 tensors: "feat"
     [N,(L+1)^2,C], "w_q", "w_k" [C,C], "w_rad" [8,L+1,C], "w_so2" (flat, the
     layout of w_so2), "pos" [N,3]."""
-    dev = pos.device
+    dev = _gpu_device(pos)
     n = pos.shape[0]
     K = (L + 1) ** 2
     shapes = {"feat": (n, K, C), "w_q": (C, C), "w_k": (C, C), "w_rad": (8, L + 1, C),
@@ -326,43 +343,17 @@ def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_
                       stream=None):
     """dL/dh of the layer for grad_out = dL/do, from the forward's output and
     log-normaliser; returns grad_feat [N,(L+1)^2,C] fp32."""
-    dev = pos.device
+    dev = _gpu_device(pos)
     n = pos.shape[0]
-    if feat.dtype == torch.bfloat16:
-        dtype = E2A_DTYPE_BF16
-    elif feat.dtype == torch.float32:
-        dtype = E2A_DTYPE_F32
-    else:
-        raise TypeError("feat must be float32 or bfloat16")
-    _need(pos, "pos", torch.float32, dev)
-    _need(row_ptr, "row_ptr", torch.int64, dev)
-    _need(col, "col", torch.int32, dev)
-    for name, t in (("feat", feat), ("w_q", w_q), ("w_k", w_k), ("w_rad", w_rad), ("w_so2", w_so2)):
-        _need(t, name, feat.dtype, dev)
-    for name, t in (("out", out), ("out_lse", out_lse), ("grad_out", grad_out)):
-        _need(t, name, torch.float32, dev)
     K = (L + 1) ** 2
     if grad_feat is None:
         grad_feat = torch.empty((n, K, C), dtype=torch.float32, device=dev)
-    _need(grad_feat, "grad_feat", torch.float32, dev)
+    _need(grad_feat, "grad_feat", torch.float32, dev, shape=(n, K, C))
     if workspace is None:
         workspace = torch.empty(max(1, e2a_attention_bwd_workspace_bytes(n, col.numel(), L, C, H)),
                                 dtype=torch.uint8, device=dev)
-    box_arr, box_p = _box_arg(box)
-    a = AttnArgs()
-    a.pos = _ptr(pos)
-    a.box = box_p
-    a.n_atoms = n
-    a.row_ptr = _ptr(row_ptr)
-    a.col = _ptr(col)
-    a.n_edges = col.numel()
-    a.cutoff = float(cutoff)
-    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
-    a.feat, a.w_q, a.w_k, a.w_rad, a.w_so2 = (_ptr(feat), _ptr(w_q), _ptr(w_k), _ptr(w_rad), _ptr(w_so2))
-    a.out = _ptr(out)
-    a.out_lse = _ptr(out_lse)
-    a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel()
+    a, box_arr = _bwd_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, grad_out, L, C, H, cutoff,
+                           box, variant, workspace)
     _check(_lib.e2a_attention_bwd(ctypes.byref(a), _ptr(grad_out), _ptr(grad_feat), _stream(stream)))
     del box_arr
     return grad_feat

@@ -263,6 +263,53 @@ def test_host_wigner_recursion_matches_oracle(hg, L):
         off += k * k
 
 
+@pytest.mark.parametrize("L", [1, 2, 3, 4])
+def test_host_wigner_rows_match_oracle(hg, L):
+    """The row-wise form of the recursion (ir_row, one row per thread: the form
+    the matrix-core kernels and the weight-gradient gather evaluate) against
+    the oracle's least-squares Wigner blocks, on generic directions and on
+    edges exactly along +-z (where the frame's angle phi is undefined and the
+    pole branch of the rotation runs), +-x and +-y."""
+    rng = np.random.default_rng(100 + L)
+    u = rng.standard_normal((150, 3))
+    u /= np.linalg.norm(u, axis=1, keepdims=True)
+    u[:6] = [[0, 0, 1], [0, 0, -1], [1, 0, 0], [-1, 0, 0], [0, 1, 0], [0, -1, 0]]
+    u32 = np.ascontiguousarray(u, dtype=np.float32)
+    R = np.zeros((150, 9), dtype=np.float32)
+    hg.e2a_host_edge_rotation(_cp(u32), 150, _cp(R))
+    nw = sum((2 * l + 1) ** 2 for l in range(L + 1))
+    D = np.zeros((150, nw), dtype=np.float32)
+    hg.e2a_host_wigner_rows(L, _cp(R), 150, _cp(D))
+    Rw = O.edge_rotation(u32.astype(np.float64))
+    off = 0
+    for l in range(L + 1):
+        k = 2 * l + 1
+        want = O.wigner_d(l, Rw)
+        got = D[:, off:off + k * k].reshape(-1, k, k)
+        assert np.max(np.abs(got - want)) < 2e-6, l
+        # the aligned harmonics keep only m = 0 (Lemma 4.1) through the device blocks
+        Y = O.real_sph_harm(l, u32.astype(np.float64))[:, l * l:(l + 1) ** 2]
+        yz = np.einsum("emn,en->em", got.astype(np.float64), Y)
+        ref = np.zeros(k)
+        ref[l] = np.sqrt((2 * l + 1) / (4 * np.pi))
+        assert np.max(np.abs(yz - ref)) < 5e-6, l
+        off += k * k
+
+
+def test_host_edge_unit_zero_length(hg):
+    """A zero-length edge takes r_hat = z (length 0); other edges their own
+    direction, as the oracle's edge_unit gives them."""
+    r = np.array([[0, 0, 0], [3, 4, 0], [0, 0, -2], [1e-20, 0, 0]], dtype=np.float32)
+    u = np.zeros((4, 3), dtype=np.float32)
+    ln = np.zeros(4, dtype=np.float32)
+    hg.e2a_host_edge_unit(_cp(r), 4, _cp(u), _cp(ln))
+    r64, u64 = O.edge_unit(r.astype(np.float64))
+    assert np.array_equal(u[0], [0, 0, 1]) and ln[0] == 0.0
+    assert np.max(np.abs(u[1:3] - u64[1:3])) < 1e-7
+    assert np.allclose(ln[1:3], r64[1:3])
+    assert np.all(np.isfinite(u))
+
+
 def test_host_radial_basis_matches_oracle(hg):
     r = np.ascontiguousarray(np.linspace(0.5, 5.0, 97), dtype=np.float32)
     e = np.zeros((97, 8), dtype=np.float32)
@@ -314,3 +361,60 @@ def test_host_wigner_tangents_match_oracle(hg):
             got = dD[:, a, off:off + k * k].reshape(-1, k, k)
             assert np.max(np.abs(got - want)) <= 2e-5 * max(1.0, np.max(np.abs(want))), (a, l)
             off += k * k
+
+
+# ------------------------------------------------------ binding checks ------
+def _fake_layer_tensors(n=4, L=1, C=16, H=1, dev="cpu"):
+    import torch
+    K = (L + 1) ** 2
+    t = dict(pos=torch.zeros(n, 3), row_ptr=torch.zeros(n + 1, dtype=torch.int64),
+             col=torch.zeros(0, dtype=torch.int32), feat=torch.zeros(n, K, C), w_q=torch.zeros(C, C),
+             w_k=torch.zeros(C, C), w_rad=torch.zeros(8, L + 1, C),
+             w_so2=torch.zeros(B.e2a_so2_param_count(L, C)))
+    return t
+
+
+def test_binding_refuses_cpu_tensors():
+    """Host tensors never reach the library as device pointers: every entry
+    point raises before its ctypes call."""
+    import torch
+    t = _fake_layer_tensors()
+    with pytest.raises(ValueError, match="GPU"):
+        B.e2a_attention_fwd(t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_q"], t["w_k"], t["w_rad"],
+                            t["w_so2"], L=1, C=16, H=1, cutoff=5.0)
+    with pytest.raises(ValueError, match="GPU"):
+        B.e2a_conv_fwd(t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_rad"], t["w_so2"], L=1, C=16, cutoff=5.0)
+    with pytest.raises(ValueError, match="GPU"):
+        B.e2a_build_neighbors(t["pos"], 5.0)
+    o = torch.zeros(4, 4, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        B.e2a_attention_bwd(t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_q"], t["w_k"], t["w_rad"],
+                            t["w_so2"], o, torch.zeros(4, 1), o, L=1, C=16, H=1, cutoff=5.0)
+    with pytest.raises(ValueError, match="GPU"):
+        B.e2a_attention_bwd_weights(t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_q"], t["w_k"], t["w_rad"],
+                                    t["w_so2"], o, torch.zeros(4, 1), o, L=1, C=16, H=1, cutoff=5.0)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("pos", (4, 2)), ("row_ptr", (4,)), ("feat", (4, 3, 16)), ("w_q", (16, 8)), ("w_k", (8, 16)),
+    ("w_rad", (6, 2, 16)), ("w_so2", (100,)),
+])
+def test_binding_checks_shapes_before_the_call(monkeypatch, name, bad):
+    """With the device check passed (the tensors stand in for device ones), a
+    wrong shape raises before the library is called."""
+    import torch
+    monkeypatch.setattr(B, "_gpu_device", lambda pos: torch.device("cpu"))
+
+    class NoCall:
+        def __getattr__(self, attr):
+            raise AssertionError(f"library called: {attr}")
+
+    monkeypatch.setattr(B, "_lib", NoCall())
+    monkeypatch.setattr(B, "e2a_attention_workspace_bytes", lambda *a: 16)
+    monkeypatch.setattr(B, "e2a_so2_param_count", lambda L, C: 1536)
+    t = _fake_layer_tensors()
+    dt = t["row_ptr"].dtype if name == "row_ptr" else torch.float32
+    t[name] = torch.zeros(bad, dtype=dt)
+    with pytest.raises(ValueError, match=name):
+        B._layer(B.lib, t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_q"], t["w_k"], t["w_rad"], t["w_so2"],
+                 1, 16, 1, 5.0, None, "auto", None, None, None, None, True)

@@ -343,6 +343,45 @@ def test_p10_fp32_predicate_boundary():
     assert all(i not in nb[i] for i in range(4))
 
 
+def test_p10_coincident_atoms_are_not_neighbours():
+    """Two atoms at one point (d2 = 0 in fp32) have no edge direction and are
+    not each other's neighbours (the reading of the predicate's lower bound);
+    each still sees the third atom 1 A away, which sees both.  Expected lists
+    written out by hand."""
+    pos = np.array([[1, 1, 1], [1, 1, 1], [2, 1, 1], [1, 1, 1]], dtype=np.float32)
+    for fn in (O.neighbor_list, O.neighbor_list_bruteforce):
+        rp, col = fn(pos, 5.0)
+        assert rp.tolist() == [0, 1, 2, 5, 6]
+        assert col.tolist() == [2, 2, 0, 1, 3, 2]
+    # periodic: a wrapped image at distance 0 is the same point
+    box = np.full(3, 10.0, dtype=np.float32)
+    pos = np.array([[0, 5, 5], [0, 5, 5], [9, 5, 5]], dtype=np.float32)
+    rp, col = O.neighbor_list_bruteforce(pos, 4.0, box)
+    assert rp.tolist() == [0, 1, 2, 4]
+    assert col.tolist() == [2, 2, 0, 1]
+
+
+def test_zero_length_edge_is_the_limit_along_z():
+    """A zero-length edge takes r_hat = z: its message equals the limit of
+    edges (0, 0, t) as t -> 0 (a continuous limit along that direction:
+    the frame is fixed, the radial basis is smooth in r)."""
+    rng = np.random.default_rng(12)
+    L, C = 3, 4
+    h = rng.standard_normal((1, (L + 1) ** 2, C))
+    w_rad = rng.standard_normal((8, L + 1, C))
+    w_so2 = rng.standard_normal(sum((1 if m == 0 else 2) * ((L + 1 - m) * C) ** 2 for m in range(L + 1)))
+    v0 = O.edge_messages(np.zeros((1, 3)), h, w_rad, w_so2, L, C, 5.0)
+    assert np.all(np.isfinite(v0))
+    # the gap shrinks in proportion to t (the radial basis has a nonzero slope)
+    gaps = [rel(v0, O.edge_messages(np.array([[0.0, 0.0, t]]), h, w_rad, w_so2, L, C, 5.0)) for t in (1e-6, 1e-9)]
+    assert gaps[0] < 1e-5 and gaps[1] < 1e-8 and 300 < gaps[0] / gaps[1] < 3000
+    # and differs from the limit along another direction (the reading matters)
+    v2 = O.edge_messages(np.array([[1e-9, 0.0, 0.0]]), h, w_rad, w_so2, L, C, 5.0)
+    assert rel(v0, v2) > 1e-3
+    r, u = O.edge_unit(np.array([[0.0, 0.0, 0.0], [0.0, 3.0, 4.0]]))
+    assert r.tolist() == [0.0, 5.0] and np.allclose(u, [[0, 0, 1], [0, 0.6, 0.8]])
+
+
 # ---------------------------------------------------------------- P11 -------
 def _cg_complex(j1, m1, j2, m2, J, M):
     """Clebsch-Gordan <j1 m1 j2 m2 | J M> by Racah's formula."""

@@ -7,8 +7,10 @@ path (through the tests and the benchmark) can take their inputs from it.
 from .generators import (  # noqa: F401
     CONFIGS,
     Workload,
+    axis_lattice_geometry,
     bf16_round,
     bf16_to_f32,
+    coincident_geometry,
     f32_to_bf16_bits,
     make_config,
     so2_param_count,

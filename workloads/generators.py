@@ -433,3 +433,22 @@ def isolated_atom_variant(w: Workload, far: float = 1000.0) -> Workload:
     return Workload(name=w.name + "+isolated", pos=pos, box=None, batch=batch, cutoff=w.cutoff,
                     L=w.L, C=w.C, H=w.H, dtype=w.dtype, feat=feat, w_q=w.w_q, w_k=w.w_k,
                     w_rad=w.w_rad, w_so2=w.w_so2, meta=dict(w.meta))
+
+
+def axis_lattice_geometry(n_side: int = 4, spacing: float = 1.5):
+    """Open-boundary cubic lattice of n_side^3 atoms with the given spacing
+    (exact in fp32): every lattice row gives edges exactly along +-x, +-y and
+    +-z, so the edge frame meets its poles (r_hat = +-z) and the axes.
+    Returns a ``make_config`` geometry tuple."""
+    g = np.arange(n_side, dtype=np.float64) * spacing
+    pos = np.stack(np.meshgrid(g, g, g, indexing="ij"), axis=-1).reshape(-1, 3) + 1.0
+    return pos.astype(np.float32), None, None, {"kind": "axis lattice", "spacing": spacing}
+
+
+def coincident_geometry(rng: np.random.Generator, n: int = 64, n_dup: int = 6, side: float = 9.0):
+    """``n`` atoms uniform in an open cube, then ``n_dup`` of them duplicated
+    at exactly the same fp32 coordinates (two atoms at one point)."""
+    pos = rng.uniform(0.0, side, size=(n, 3)).astype(np.float32)
+    dup = rng.choice(n, size=n_dup, replace=False)
+    pos = np.concatenate([pos, pos[dup]])
+    return pos, None, None, {"kind": "coincident", "duplicated": dup.tolist()}
