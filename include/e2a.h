@@ -190,6 +190,24 @@ size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int d
 e2a_status e2a_attention_fwd(const e2a_attn_args* args, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as e2a_attention_fwd, with the same arguments, inputs, outputs,
+ * results (bit for bit) and errors, but its scratch comes from a fixed array
+ * of E2A_NOALLOC_SCRATCH_BYTES that the library keeps on each GPU it runs on
+ * (loaded with the library, held until the process ends).  args->workspace
+ * and args->workspace_bytes are ignored.  The call allocates nothing: no
+ * hipMalloc, hipFree or allocating library routine.  Sizes whose workspace
+ * (e2a_attention_workspace_bytes) exceeds E2A_NOALLOC_SCRATCH_BYTES give
+ * E2A_ERR_INVALID_ARG before anything runs (64 MiB holds up to about 61,000
+ * atoms at L = 4, C = 128).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs to start at zero.
+ */
+#define E2A_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+e2a_status e2a_attention_fwd_noalloc(const e2a_attn_args* args, void* stream);
+
+/*
  * The EAAS convolution stage: o_i = sum_{j in N(i)} v_ij, the same per-edge
  * messages v_ij as e2a_attention_fwd (rotate in, per-m SO(2) mix, radial
  * scale, rotate out) summed over the neighbourhood with no attention weights

@@ -12,6 +12,7 @@ _EXPORTS = (
     "e2a_attention_bwd_weights",
     "e2a_attention_bwd_weights_workspace_bytes",
     "e2a_attention_fwd",
+    "e2a_attention_fwd_noalloc",
     "e2a_attention_workspace_bytes",
     "e2a_build_neighbors",
     "e2a_conv_fwd",

@@ -2,6 +2,7 @@
 // carving and dispatch.  See include/e2a.h for the contract of each call.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "e2a_internal.hpp"
 
@@ -271,6 +272,63 @@ extern "C" {
 e2a_status e2a_attention_fwd(const e2a_attn_args* a, void* stream) {
   clear_error();
   return run_layer(a, stream, false);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of e2a_attention_fwd_noalloc: one array per GPU, loaded with the
+// library's code object and held until the process ends.  In host code the
+// name `scratch` is only a stand-in for the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = E2A_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (looked up on the first
+// call on that device, with the device current).
+e2a_status scratch_of_current_device(void** out) {
+  int dev = 0;
+  E2A_HIP_CHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(E2A_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    E2A_HIP_CHECK(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(E2A_ERR_HIP, "hipGetSymbolAddress returned a null scratch address on device %d", dev);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return E2A_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+e2a_status e2a_attention_fwd_noalloc(const e2a_attn_args* a, void* stream) {
+  clear_error();
+  if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
+  // 0 for shapes no entry point takes: run_layer then names the bad argument
+  const size_t need = e2a_attention_workspace_bytes(a->n_atoms, a->L, a->C, a->H, a->dtype);
+  if (need > kNoAllocScratchBytes)
+    return fail(E2A_ERR_INVALID_ARG,
+                "n_atoms=%lld, L=%d, C=%d needs %zu bytes of scratch; e2a_attention_fwd_noalloc holds %zu "
+                "(use e2a_attention_fwd with a workspace)",
+                (long long)a->n_atoms, a->L, a->C, need, kNoAllocScratchBytes);
+  e2a_attn_args b = *a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (need > 0 && a->n_atoms > 0) {
+    e2a_status st = scratch_of_current_device(&b.workspace);
+    if (st != E2A_OK) return st;
+    b.workspace_bytes = kNoAllocScratchBytes;
+  }
+  return run_layer(&b, stream, false);
 }
 
 e2a_status e2a_conv_fwd(const e2a_attn_args* a, void* stream) {

@@ -29,7 +29,8 @@ VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
 EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
             "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
             "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd",
-            "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights"]
+            "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights", "e2a_attention_fwd_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class E2AError(RuntimeError):
@@ -72,6 +73,8 @@ def _load():
                                                   ctypes.c_int]
     lib.e2a_attention_fwd.restype = ctypes.c_int32
     lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.e2a_attention_fwd_noalloc.restype = ctypes.c_int32
+    lib.e2a_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_conv_fwd.restype = ctypes.c_int32
     lib.e2a_conv_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -205,7 +208,8 @@ def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L,
         _need(out, "out", torch.float32, dev, shape=(n, K, C))
     if out_lse is not None:
         _need(out_lse, "out_lse", torch.float32, dev, shape=(n, H))
-    _need(workspace, "workspace", torch.uint8, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, dev)
     box_arr, box_p = _box_arg(box)
     a = AttnArgs()
     a.pos = _ptr(pos)
@@ -220,7 +224,7 @@ def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L,
     a.out = _ptr(out)
     a.out_lse = _ptr(out_lse)
     a.workspace = _ptr(workspace)
-    a.workspace_bytes = workspace.numel()
+    a.workspace_bytes = 0 if workspace is None else workspace.numel()
     return a, box_arr
 
 
@@ -274,6 +278,25 @@ def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int
         out_lse = torch.empty((pos.shape[0], H), dtype=torch.float32, device=pos.device)
     out = _layer(_lib.e2a_attention_fwd, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box,
                  variant, out, out_lse, workspace, stream, True)
+    return (out, out_lse) if with_lse else out
+
+
+def e2a_attention_fwd_noalloc(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
+                              cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None, stream=None,
+                              with_lse: bool = False):
+    """e2a_attention_fwd on the library's fixed per-GPU scratch (the C call
+    allocates nothing; pass ``out`` and ``out_lse`` to allocate nothing here
+    either).  Calls that overlap on one GPU race on that scratch."""
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    if out is None:
+        out = torch.empty((n, (L + 1) ** 2, C), dtype=torch.float32, device=dev)
+    if with_lse and out_lse is None:
+        out_lse = torch.empty((n, H), dtype=torch.float32, device=dev)
+    a, box_arr = _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box,
+                            variant, None)
+    _check(_lib.e2a_attention_fwd_noalloc(ctypes.byref(a), _stream(stream)))
+    del box_arr
     return (out, out_lse) if with_lse else out
 
 

@@ -119,6 +119,20 @@ def test_attention_rejects_on_host(kw, status):
     assert B.last_error_message()
 
 
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """e2a_attention_fwd_noalloc refuses, on the host and before any device
+    call, a system whose workspace exceeds its fixed scratch; shape errors
+    come first, as in e2a_attention_fwd."""
+    a = attn_args(n_atoms=200000, L=4, C=128, H=8, dtype=1, workspace=None, workspace_bytes=0)
+    assert B.lib().e2a_attention_fwd_noalloc(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "scratch" in B.last_error_message()
+    assert B.e2a_attention_workspace_bytes(200000, 4, 128, 8, 1) > B.NOALLOC_SCRATCH_BYTES
+    a = attn_args(L=7, workspace=None)
+    assert B.lib().e2a_attention_fwd_noalloc(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "L=7" in B.last_error_message()
+    assert B.lib().e2a_attention_fwd_noalloc(None, None) == B.E2A_ERR_INVALID_ARG
+
+
 def test_attention_null_args():
     assert B.lib().e2a_attention_fwd(None, None) == B.E2A_ERR_INVALID_ARG
 
