@@ -10,7 +10,14 @@ measured with HIP events on the stream it runs on, gives the roofline block.
 The fp64 oracle is timed on the host's cores on a bounded sample of
 destination atoms as the CPU baseline.  The convolution stage (e2a_conv_fwd,
 the same messages summed without attention) is timed separately and reported
-in the breakdown, and so is the feature gradient (e2a_attention_bwd).
+in the breakdown, and so are the gradients.
+
+The line checks itself: "parity" compares the timed step's output with the
+oracle on seeded destinations (plus the first, last, highest- and
+lowest-degree atoms) and the GPU neighbour list with the oracle's, entry by
+entry; "breakdown.configs" times the layer on the other four workloads (the
+64-atom system, the drug-like batch, the water box, the solvated protein)
+with the same checks.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -28,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "neighbour edges/sec per attention layer (1 MI355X); achieved TFLOPS % of roofline"
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_large_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "so_graph_attention_amd", "csrc", "attention_mfma.hip")
@@ -164,6 +172,97 @@ def backward_leg(B, torch, dev, w, pos, rp, col, feat, w_q, w_k, w_rad, w_so2, b
                                 "l = 0 terms"}
 
 
+def sample_dest(rp, n_sample, seed):
+    """Seeded destinations plus the first, last, highest- and lowest-degree atoms."""
+    n = rp.size - 1
+    deg = np.diff(rp)
+    pick = set(np.random.default_rng(seed).choice(n, size=min(n, n_sample), replace=False).tolist())
+    pick |= {0, n - 1, int(np.argmax(deg)), int(np.argmin(deg))}
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+def parity_check(w, rp_gpu, col_gpu, out, lse, n_sample=64, seed=11):
+    """The GPU's neighbour list against the oracle's (bit for bit) and its
+    output and log-normaliser against the oracle's on sampled destinations."""
+    import oracle as O
+    rp_o, col_o = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    exact = bool(np.array_equal(rp_gpu, rp_o) and np.array_equal(col_gpu, col_o))
+    dest = sample_dest(rp_o, n_sample, seed) if n_sample < w.n_atoms else np.arange(w.n_atoms)
+    want, want_lse = O.attention(w.pos, rp_o, col_o, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"),
+                                 w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, box=w.box, dest=dest)
+    got = out[dest].astype(np.float64)
+    rel = float(np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300))
+    fin = np.isfinite(want_lse)
+    lse_err = float(np.max(np.abs(lse[dest][fin] - want_lse[fin]))) if fin.any() else 0.0
+    tol = 2e-2 if w.dtype == "bf16" else 1e-5
+    return {"rel_l2": rel, "tol": tol, "ok": bool(exact and rel <= tol), "n_dest": int(dest.size),
+            "lse_max_abs_err": lse_err, "neighbours_bit_exact": exact,
+            "sample": "all destinations" if dest.size == w.n_atoms else
+                      f"{dest.size} destinations: {n_sample} seeded (seed {seed}) plus first, last, "
+                      f"highest- and lowest-degree atoms"}
+
+
+def config_leg(B, torch, dev, name, iters=10):
+    """One more workload: the neighbour build and the layer, timed with HIP
+    events (median over `iters` calls after warm-up), checked like the
+    headline step."""
+    from workloads import make_config
+    w = make_config(name)
+    box = None if w.box is None else w.box.tolist()
+
+    def stored(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    pos = torch.from_numpy(w.pos).to(dev)
+    batch = None if w.batch is None else torch.from_numpy(w.batch.astype(np.int32)).to(dev)
+    feat, w_q, w_k, w_rad, w_so2 = (stored(getattr(w, n)) for n in ("feat", "w_q", "w_k", "w_rad", "w_so2"))
+    stream = torch.cuda.current_stream()
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch)
+    e = int(col.numel())
+    dtype_code = B.E2A_DTYPE_BF16 if w.dtype == "bf16" else B.E2A_DTYPE_F32
+    out = torch.empty((w.n_atoms, (w.L + 1) ** 2, w.C), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.n_atoms, w.H), dtype=torch.float32, device=dev)
+    ws = torch.empty(B.e2a_attention_workspace_bytes(w.n_atoms, w.L, w.C, w.H, dtype_code), dtype=torch.uint8,
+                     device=dev)
+
+    def call():
+        B.e2a_attention_fwd(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff,
+                            box=box, out=out, out_lse=lse, workspace=ws)
+
+    def nb():
+        B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch, capacity=e)
+
+    for _ in range(3):
+        call()
+        nb()
+    ts, tn = [], []
+    for _ in range(iters):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(stream)
+        nb()
+        ev[1].record(stream)
+        call()
+        ev[2].record(stream)
+        torch.cuda.synchronize()
+        tn.append(ev[0].elapsed_time(ev[1]))
+        ts.append(ev[1].elapsed_time(ev[2]))
+    ms = float(np.median(ts))
+    f = flops_per_edge(w.L, w.C)
+    tflops = f * e / (ms * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    res = {"workload": f"{name}: {w.n_atoms} atoms, "
+                       + ("periodic box %.4g A" % w.box[0] if w.box is not None else "open boundaries")
+                       + f", cutoff {w.cutoff:g} A, L={w.L}, C={w.C}, H={w.H}, {w.dtype} storage",
+           "n_atoms": w.n_atoms, "n_edges": e, "neighbors_ms": float(np.median(tn)), "attention_ms": ms,
+           "edges_per_s": e / (ms * 1e-3), "step_edges_per_s": e / ((ms + float(np.median(tn))) * 1e-3),
+           "tflops": tflops, "peak": peak, "frac": tflops / peak,
+           "kernel": "MFMA (bf16 operands)" if w.dtype == "bf16" else "scalar fp32 (VALU)"}
+    res["parity"] = parity_check(w, rp.cpu().numpy(), col.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy())
+    return res
+
+
 def algorithmic_bytes(w, n_edges):
     """HBM bytes of one layer call with every array touched once: the node
     features (storage precision) in and the fp32 output out, the CSR graph,
@@ -260,6 +359,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other four workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).",
@@ -327,11 +427,35 @@ def main():
     attn_med = float(np.median(attn_all))
     progress(f"step {ms_step:.3f} ms (neighbours {nb_ms:.3f} ms, attention {attn_ms:.3f} ms)")
 
+    # self-check of the timed step: its output (and one more call's
+    # log-normaliser) against the oracle, its neighbour list bit for bit
+    progress("parity of the timed step against the oracle")
+    lse = torch.empty((n, w.H), dtype=torch.float32, device=dev)
+    out_chk = torch.empty_like(out)
+    torch.cuda.reset_peak_memory_stats(dev)
+    held = torch.cuda.memory_allocated(dev)
+    B.e2a_attention_fwd(pos, rp, col, feat, w_q, w_k, w_rad, w_so2, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box,
+                        variant=args.variant, out=out_chk, out_lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    peak_delta = torch.cuda.max_memory_allocated(dev) - held
+    same = bool(torch.equal(out_chk, out))
+    parity = parity_check(w, rp.cpu().numpy(), col.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy())
+    parity["launches_bit_identical"] = same
+    progress(f"rel-L2 {parity['rel_l2']:.2e} on {parity['n_dest']} destinations, neighbours bit-exact "
+             f"{parity['neighbours_bit_exact']}")
+    memory = {"workspace_bytes": int(ws.numel()), "out_bytes": int(out.numel() * 4),
+              "allocated_during_call_bytes": int(peak_delta),
+              "edge_materialised_bytes": int(n_edges * K * w.C * 4),
+              "note": "the library allocates nothing; its scratch is the caller's O(N) workspace, against "
+                      "E x (L+1)^2 x C fp32 values for one materialised per-edge message tensor"}
+
     # the convolution stage (same messages, no attention weights), timed on
     # its own after the steps; it is not part of the headline step
+    conv_out = torch.empty_like(out)
+
     def conv():
         B.e2a_conv_fwd(pos, rp, col, feat, w_rad, w_so2, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box,
-                       variant=args.variant, out=out, workspace=ws)
+                       variant=args.variant, out=conv_out, workspace=ws)
 
     for _ in range(2):
         conv()
@@ -395,6 +519,16 @@ def main():
     }
     if bwd is not None:
         result["breakdown"].update(bwd)
+    result["parity"] = parity
+    result["breakdown"]["memory"] = memory
+    if not args.no_configs:
+        result["breakdown"]["configs"] = {}
+        for name in ("tiny", "drug", "water", "protein"):
+            progress(f"workload {name}")
+            r = config_leg(B, torch, dev, name)
+            progress(f"{name}: {r['attention_ms']:.3f} ms, {r['frac']:.3f} of peak, rel-L2 "
+                     f"{r['parity']['rel_l2']:.2e}, neighbours bit-exact {r['parity']['neighbours_bit_exact']}")
+            result["breakdown"]["configs"][name] = r
     if not args.no_cpu_baseline:
         progress(f"oracle CPU baseline (~{args.cpu_seconds:.0f} s)")
         rp_h = rp.cpu().numpy()
