@@ -18,7 +18,10 @@ invariance, rotation equivariance, permutation invariance, an L=1 closed form,
 softmax limits, online == two-pass, brute-force neighbours, and equality with a
 dense Clebsch-Gordan tensor product; the convolution against the attention
 layer with uniform weights; the message adjoint by the exact adjoint identity
-and the feature gradient by central finite differences of the layer).  The conventions those invariants leave
+and the feature gradient by central finite differences of the layer; the
+block's norm against a library RMS norm, its gate against a library SiLU,
+and the block's equivariance, permutation equivariance and residual
+identity).  The conventions those invariants leave
 free (edge direction, W2 sign, radial basis widths, 1/sqrt(d_h), head split, no
 self loop) are readings, not facts the pages fix.
 """
@@ -793,3 +796,81 @@ def attention_online(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, c
             out[a] = acc / l_run[head_of_c][None, :]
             lse[a] = m_run + np.log(l_run)
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# One block around the layer
+# ---------------------------------------------------------------------------
+#
+# The pages place the on-the-fly attention layer inside the E2Former-V2 model
+# (abstract; technical summary section 2 "Methodology") but print none of the
+# block around it.  The readings below are the plainest equivariant block:
+# a pre-norm residual block, h1 = h + Proj(Attn(Norm1(h))), then
+# h2 = h1 + FFN(Norm2(h1)); every node-wise map acts on channels only and is
+# the same for every m of a degree (or gates by invariant scalars), so it
+# commutes with rotations.
+
+NORM_EPS = 1e-6
+
+
+def degree_rms_norm(h, gamma, L, eps=NORM_EPS):
+    """Per-degree RMS normalisation (a reading): for each atom and degree l,
+    n[l,m,c] = gamma[l,c] h[l,m,c] / sqrt(mean over (m, c) of h[l,m,c]^2 + eps).
+    Rotations mix m within a degree and keep that mean, so the map is
+    equivariant.  h [N,(L+1)^2,C], gamma [L+1,C].  fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    g = np.asarray(gamma, dtype=np.float64)
+    out = np.empty_like(h)
+    for l in range(L + 1):
+        blk = h[:, l * l:(l + 1) ** 2, :]
+        rms = np.sqrt(np.mean(blk * blk, axis=(1, 2)) + eps)
+        out[:, l * l:(l + 1) ** 2, :] = blk / rms[:, None, None] * g[l][None, None, :]
+    return out
+
+
+def degree_linear(x, w, L):
+    """Per-degree channel map y[l,m,:] = x[l,m,:] W[l] (a reading of the
+    node-wise projection: one C_in x C_out matrix per degree, no bias).
+    x [N,(L+1)^2,C_in], w [L+1,C_in,C_out].  fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    out = np.empty(x.shape[:2] + (w.shape[2],))
+    for l in range(L + 1):
+        out[:, l * l:(l + 1) ** 2, :] = x[:, l * l:(l + 1) ** 2, :] @ w[l]
+    return out
+
+
+def gated_ffn(n, w1, w_gate, w2, L, C):
+    """Gated feed-forward (a reading): u = degree_linear(n, W1);
+    z = n[l=0] W_gate (C -> L C); act[l=0] = SiLU(u[0]);
+    act[l>=1][m][c] = u[l][m][c] sigmoid(z[(l-1) C + c]) (an invariant gate
+    per channel, shared by every m of the degree); f = degree_linear(act, W2).
+    n [N,(L+1)^2,C]; w1, w2 [L+1,C,C]; w_gate [C, L C].  fp64."""
+    n = np.asarray(n, dtype=np.float64)
+    u = degree_linear(n, w1, L)
+    z = n[:, 0, :] @ np.asarray(w_gate, dtype=np.float64)
+    act = np.empty_like(u)
+    s = u[:, 0, :]
+    act[:, 0, :] = s / (1.0 + np.exp(-s))
+    for l in range(1, L + 1):
+        gate = 1.0 / (1.0 + np.exp(-z[:, (l - 1) * C:l * C]))
+        act[:, l * l:(l + 1) ** 2, :] = u[:, l * l:(l + 1) ** 2, :] * gate[:, None, :]
+    return degree_linear(act, w2, L)
+
+
+def block(pos, row_ptr, col, h, bw, L, C, H, cutoff, box=None, dest=None):
+    """One block: h1 = h + degree_linear(attention(Norm1(h)), W_o);
+    out = h1 + gated_ffn(Norm2(h1)).  ``bw`` holds the block's weights:
+    norm1, norm2 [L+1,C]; w_q, w_k [C,C]; w_rad [8,L+1,C]; w_so2 (flat);
+    w_o, w_1, w_2 [L+1,C,C]; w_gate [C,L C].  The residual stream h is read
+    as given (fp64).  ``dest`` selects the output rows (the attention reads
+    Norm1 of every neighbour).  Returns [len(dest),(L+1)^2,C] fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    n = h.shape[0]
+    dest = np.arange(n) if dest is None else np.asarray(dest, dtype=np.int64)
+    n1 = degree_rms_norm(h, bw["norm1"], L)
+    a, _ = attention(pos, row_ptr, col, n1, bw["w_q"], bw["w_k"], bw["w_rad"], bw["w_so2"], L, C, H, cutoff,
+                     box=box, dest=dest)
+    h1 = h[dest] + degree_linear(a, bw["w_o"], L)
+    n2 = degree_rms_norm(h1, bw["norm2"], L)
+    return h1 + gated_ffn(n2, bw["w_1"], bw["w_gate"], bw["w_2"], L, C)

@@ -9,9 +9,11 @@ from .generators import (  # noqa: F401
     Workload,
     axis_lattice_geometry,
     bf16_round,
+    block_weights_f32,
     bf16_to_f32,
     coincident_geometry,
     f32_to_bf16_bits,
+    make_block_weights,
     make_config,
     so2_param_count,
 )

@@ -452,3 +452,52 @@ def coincident_geometry(rng: np.random.Generator, n: int = 64, n_dup: int = 6, s
     dup = rng.choice(n, size=n_dup, replace=False)
     pos = np.concatenate([pos, pos[dup]])
     return pos, None, None, {"kind": "coincident", "duplicated": dup.tolist()}
+
+
+BLOCK_NODE_WEIGHTS = ("norm1", "w_o", "norm2", "w_1", "w_gate", "w_2")
+ATTN_WEIGHTS = ("w_q", "w_k", "w_rad", "w_so2")
+
+
+def make_block_weights(w: Workload, index: int = 0) -> dict:
+    """Weights of block ``index`` around the attention layer of workload w,
+    in w's storage (fp32, or bf16 bits).  Drawn from their own seeded stream
+    (seed (base seed, 1000 + index)), so the workload's own draws do not
+    change: norm gains 1 + 0.1 N(0,1) [L+1, C]; W_o, W_1, W_2 [L+1, C, C] and
+    W_gate [C, L C] ~ N(0, 1/C).  Block 0 takes the workload's attention
+    weights; later blocks draw their own (W_q, W_k, W_rad, W_so2, same
+    shapes and scales)."""
+    base = CONFIGS[w.name][0] if w.name in CONFIGS else 0
+    rng = np.random.default_rng((base, 1000 + index))
+    L, C = w.L, w.C
+
+    def store(x):
+        x = np.asarray(x, dtype=np.float32)
+        return f32_to_bf16_bits(x) if w.dtype == "bf16" else x
+
+    out = {
+        "norm1": store(1.0 + 0.1 * rng.standard_normal((L + 1, C))),
+        "w_o": _draw_weight(rng, (L + 1, C, C), C, w.dtype),
+        "norm2": store(1.0 + 0.1 * rng.standard_normal((L + 1, C))),
+        "w_1": _draw_weight(rng, (L + 1, C, C), C, w.dtype),
+        "w_gate": _draw_weight(rng, (C, L * C), C, w.dtype),
+        "w_2": _draw_weight(rng, (L + 1, C, C), C, w.dtype),
+    }
+    if index == 0:
+        for k in ATTN_WEIGHTS:
+            out[k] = getattr(w, k)
+    else:
+        out["w_q"] = _draw_weight(rng, (C, C), C, w.dtype)
+        out["w_k"] = _draw_weight(rng, (C, C), C, w.dtype)
+        out["w_rad"] = _draw_weight(rng, (N_RBF, L + 1, C), C, w.dtype)
+        blocks = []
+        for m in range(L + 1):
+            k = (L + 1 - m) * C
+            for _ in range(1 if m == 0 else 2):
+                blocks.append(_draw_weight(rng, (k * k,), C, w.dtype))
+        out["w_so2"] = np.concatenate(blocks)
+    return out
+
+
+def block_weights_f32(bw: dict) -> dict:
+    """fp32 values of stored block weights (bf16 bits widened exactly)."""
+    return {k: (bf16_to_f32(v) if v.dtype == np.uint16 else np.asarray(v, dtype=np.float32)) for k, v in bw.items()}
