@@ -224,6 +224,62 @@ e2a_status e2a_attention_fwd_noalloc(const e2a_attn_args* args, void* stream);
 e2a_status e2a_conv_fwd(const e2a_attn_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* One block around the layer                                               */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The pages place the fused attention layer inside the E2Former-V2 model
+ * (abstract; technical summary section 2, "Methodology") but print none of
+ * the block around it.  This is the plainest equivariant reading, a pre-norm
+ * residual block on an fp32 residual stream h (K = (L+1)^2 components):
+ *
+ *   Norm(x)[l,m,c] = g[l,c] x[l,m,c] / sqrt(mean_{m,c} x[l,m,c]^2 + 1e-6)
+ *   h1  = h + Proj(Attn(Norm1(h))),  Proj(a)[l,m,:] = a[l,m,:] W_o[l]
+ *   u   = Norm2(h1)[l,m,:] W_1[l],   z = Norm2(h1)[0,0,:] W_gate
+ *   act = SiLU(u) for l = 0;  u[l,m,c] sigmoid(z[(l-1) C + c]) for l >= 1
+ *   out = h1 + act[l,m,:] W_2[l]
+ *
+ * Attn is e2a_attention_fwd on Norm1(h) stored in `dtype` (bf16 rounds it),
+ * with the attention fields of this struct; stacking blocks is calling this
+ * once per block with that block's weights (h_out of one is h_in of the next).
+ * Node-wise products take bf16 operands on the matrix cores for bf16 storage
+ * (C a multiple of 32) and fp32 otherwise; sums are fp32.
+ */
+typedef struct e2a_block_args {
+  const float* pos;        /* device f32 [n_atoms, 3]                                 */
+  const float* box;        /* HOST f32 [3] or NULL (open)                             */
+  int64_t n_atoms;
+  const int64_t* row_ptr;  /* device i64 [n_atoms + 1], as for e2a_attention_fwd      */
+  const int32_t* col;      /* device i32 [n_edges]                                    */
+  int64_t n_edges;
+  float cutoff;
+  int L, C, H, n_rbf, dtype, variant;   /* as for e2a_attention_fwd                */
+  const float* h_in;       /* device f32 [n_atoms, K, C] residual stream in           */
+  float* h_out;            /* device f32 [n_atoms, K, C]; may equal h_in              */
+  /* weights, device, stored in `dtype` */
+  const void* norm1;       /* [L+1, C]                                                */
+  const void* w_q;         /* [C, C]          attention, as in e2a_attn_args          */
+  const void* w_k;         /* [C, C]                                                  */
+  const void* w_rad;       /* [n_rbf, L+1, C]                                         */
+  const void* w_so2;       /* [e2a_so2_param_count(L, C)]                             */
+  const void* w_o;         /* [L+1, C, C]     projection of the layer's output        */
+  const void* norm2;       /* [L+1, C]                                                */
+  const void* w_1;         /* [L+1, C, C]     FFN in                                  */
+  const void* w_gate;      /* [C, L*C]        gate logits of degrees 1..L (NULL if L=0) */
+  const void* w_2;         /* [L+1, C, C]     FFN out                                 */
+  void* workspace;         /* device, e2a_block_workspace_bytes(...) bytes            */
+  size_t workspace_bytes;
+} e2a_block_args;
+
+/* Bytes of device workspace e2a_block_fwd needs (0 for invalid sizes). */
+size_t e2a_block_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype);
+
+/* One block (above).  Asynchronous and deterministic; no memory set or copy
+ * commands.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG for a NULL
+ * h_in, h_out or node-wise weight. */
+e2a_status e2a_block_fwd(const e2a_block_args* args, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Feature gradient                                                         */
 /* ------------------------------------------------------------------------ */
 

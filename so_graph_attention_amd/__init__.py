@@ -14,6 +14,8 @@ _EXPORTS = (
     "e2a_attention_fwd",
     "e2a_attention_fwd_noalloc",
     "e2a_attention_workspace_bytes",
+    "e2a_block_fwd",
+    "e2a_block_workspace_bytes",
     "e2a_build_neighbors",
     "e2a_conv_fwd",
     "e2a_neighbors_workspace_bytes",

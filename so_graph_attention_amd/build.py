@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 
 ARCH = os.environ.get("E2A_OFFLOAD_ARCH", "gfx950")
 HIP_SOURCES = ["e2a_api.hip", "neighbors.hip", "attention_reference.hip", "attention_mfma.hip",
-               "attention_backward.hip", "attention_wgrad.hip"]
+               "attention_backward.hip", "attention_wgrad.hip", "block.hip"]
 # Packed fp32 VALU forms are kept off for every HIP translation unit.
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
           "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]

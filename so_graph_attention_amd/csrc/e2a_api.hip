@@ -215,7 +215,7 @@ namespace {
 // Shared body of the attention and convolution entry points: host-side
 // argument checks, then the launches.  The convolution needs no W_q / W_k and
 // writes no log-normaliser.
-e2a_status run_layer(const e2a_attn_args* a, void* stream, bool conv) {
+e2a_status check_layer_args(const e2a_attn_args* a, bool conv) {
   if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
   if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
   if (a->n_edges < 0) return fail(E2A_ERR_INVALID_ARG, "n_edges < 0");
@@ -244,7 +244,15 @@ e2a_status run_layer(const e2a_attn_args* a, void* stream, bool conv) {
   const AttnWs ws = attn_ws_layout(a->n_atoms, a->L, a->C, a->H, a->dtype);
   if (a->n_atoms > 0 && (!a->workspace || a->workspace_bytes < ws.total))
     return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", a->workspace_bytes, ws.total);
+  return E2A_OK;
+}
+
+e2a_status run_layer(const e2a_attn_args* a, void* stream, bool conv) {
+  e2a_status chk = check_layer_args(a, conv);
+  if (chk != E2A_OK) return chk;
   if (a->n_atoms == 0) return E2A_OK;
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  const AttnWs ws = attn_ws_layout(a->n_atoms, a->L, a->C, a->H, a->dtype);
 
   AttnPlan pl{};
   pl.a = a;
@@ -334,6 +342,80 @@ e2a_status e2a_attention_fwd_noalloc(const e2a_attn_args* a, void* stream) {
 e2a_status e2a_conv_fwd(const e2a_attn_args* a, void* stream) {
   clear_error();
   return run_layer(a, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+e2a_status block_attention(const e2a_attn_args* a, hipStream_t s) { return run_layer(a, s, false); }
+
+BlockWs block_layout_full(int64_t n, int L, int C, int H, int dtype) {
+  BlockWs w = block_ws_layout(n, L, C, H, dtype);
+  w.attn_ws_bytes = attn_ws_layout(n, L, C, H, dtype).total;
+  w.total = align_up(w.attn_ws + w.attn_ws_bytes, 256);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t e2a_block_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype) {
+  if (n_atoms < 0 || L < 0 || L > 4 || C <= 0 || H <= 0 || (dtype != E2A_DTYPE_F32 && dtype != E2A_DTYPE_BF16))
+    return 0;
+  return block_layout_full(n_atoms, L, C, H, dtype).total;
+}
+
+e2a_status e2a_block_fwd(const e2a_block_args* b, void* stream) {
+  clear_error();
+  if (!b) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
+  if (b->n_atoms < 0 || b->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
+  if (b->L < 0 || b->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", b->L);
+  if (b->C <= 0 || b->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
+  if (b->dtype != E2A_DTYPE_F32 && b->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", b->dtype);
+  if (b->n_atoms > 0) {
+    const void* ptrs[] = {b->h_in, b->h_out, b->norm1, b->w_o, b->norm2, b->w_1, b->w_2};
+    const char* names[] = {"h_in", "h_out", "norm1", "w_o", "norm2", "w_1", "w_2"};
+    for (int t = 0; t < 7; ++t)
+      if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
+    if (b->L > 0 && !b->w_gate) return fail(E2A_ERR_INVALID_ARG, "w_gate is NULL");
+  }
+  const BlockWs ws = block_layout_full(b->n_atoms, b->L, b->C, b->H, b->dtype);
+  if (b->n_atoms > 0 && (!b->workspace || b->workspace_bytes < ws.total))
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", b->workspace_bytes, ws.total);
+  // the layer's own argument checks (pointers, shapes, variant) on a dry
+  // copy of its arguments, before anything is launched
+  e2a_attn_args a{};
+  a.pos = b->pos;
+  a.box = b->box;
+  a.n_atoms = b->n_atoms;
+  a.row_ptr = b->row_ptr;
+  a.col = b->col;
+  a.n_edges = b->n_edges;
+  a.cutoff = b->cutoff;
+  a.L = b->L;
+  a.C = b->C;
+  a.H = b->H;
+  a.n_rbf = b->n_rbf;
+  a.dtype = b->dtype;
+  a.variant = b->variant;
+  a.w_q = b->w_q;
+  a.w_k = b->w_k;
+  a.w_rad = b->w_rad;
+  a.w_so2 = b->w_so2;
+  a.feat = b->workspace;
+  a.out = reinterpret_cast<float*>(b->workspace);
+  a.workspace = b->workspace;
+  a.workspace_bytes = ws.attn_ws_bytes;
+  e2a_status st = check_layer_args(&a, false);
+  if (st != E2A_OK) return st;
+  if (b->n_atoms == 0) return E2A_OK;
+  BlockPlan p{};
+  p.b = b;
+  p.ws = ws;
+  p.attention = block_attention;
+  return launch_block(p, static_cast<hipStream_t>(stream));
 }
 
 size_t e2a_attention_bwd_workspace_bytes(int64_t n_atoms, int64_t n_edges, int L, int C, int H) {

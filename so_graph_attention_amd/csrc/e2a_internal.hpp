@@ -108,6 +108,21 @@ e2a_status launch_bwd_qk(const BwdPlan& p, hipStream_t s);
 // dW_rad by the matrix-core radial pass (the MFMA build's shapes), into w_rad.
 e2a_status launch_radial_mfma(const BwdPlan& p, float* w_rad, hipStream_t s);
 
+// One block around the layer (block.hip).
+struct BlockWs {
+  size_t n1, attn, h1, n2, z, wf;   // Norm1, layer output / FFN hidden, h1, Norm2 / gated act, gate logits, fp32 weights
+  size_t attn_ws, attn_ws_bytes;    // the layer's own workspace
+  size_t total;
+};
+BlockWs block_ws_layout(int64_t n, int L, int C, int H, int dtype);
+bool block_uses_mfma(int C, int dtype);
+struct BlockPlan {
+  const e2a_block_args* b;
+  BlockWs ws;
+  e2a_status (*attention)(const e2a_attn_args* a, hipStream_t s);   // the checked forward
+};
+e2a_status launch_block(const BlockPlan& p, hipStream_t s);
+
 // Weight gradients (attention_wgrad.hip), after ds and dq, dk are formed.
 struct WgradPlan {
   const e2a_attn_args* a;

@@ -29,7 +29,8 @@ VARIANTS = {"auto": 0, "reference": 1, "mfma": 2}
 EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_neighbors_workspace_bytes",
             "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
             "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd",
-            "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights", "e2a_attention_fwd_noalloc"]
+            "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights", "e2a_attention_fwd_noalloc",
+            "e2a_block_workspace_bytes", "e2a_block_fwd"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -49,6 +50,23 @@ class AttnArgs(ctypes.Structure):
         ("w_rad", ctypes.c_void_p), ("w_so2", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("out_lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
     ]
+
+
+class BlockArgs(ctypes.Structure):
+    _fields_ = [
+        ("pos", ctypes.c_void_p), ("box", ctypes.c_void_p), ("n_atoms", ctypes.c_int64),
+        ("row_ptr", ctypes.c_void_p), ("col", ctypes.c_void_p), ("n_edges", ctypes.c_int64),
+        ("cutoff", ctypes.c_float), ("L", ctypes.c_int), ("C", ctypes.c_int), ("H", ctypes.c_int),
+        ("n_rbf", ctypes.c_int), ("dtype", ctypes.c_int), ("variant", ctypes.c_int),
+        ("h_in", ctypes.c_void_p), ("h_out", ctypes.c_void_p),
+        ("norm1", ctypes.c_void_p), ("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p), ("w_rad", ctypes.c_void_p),
+        ("w_so2", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_1", ctypes.c_void_p),
+        ("w_gate", ctypes.c_void_p), ("w_2", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+BLOCK_WEIGHTS = ("norm1", "w_q", "w_k", "w_rad", "w_so2", "w_o", "norm2", "w_1", "w_gate", "w_2")
 
 
 def _load():
@@ -75,6 +93,11 @@ def _load():
     lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_attention_fwd_noalloc.restype = ctypes.c_int32
     lib.e2a_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.e2a_block_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_block_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                              ctypes.c_int]
+    lib.e2a_block_fwd.restype = ctypes.c_int32
+    lib.e2a_block_fwd.argtypes = [ctypes.POINTER(BlockArgs), ctypes.c_void_p]
     lib.e2a_conv_fwd.restype = ctypes.c_int32
     lib.e2a_conv_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_attention_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -380,3 +403,55 @@ def e2a_attention_bwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_
     _check(_lib.e2a_attention_bwd(ctypes.byref(a), _ptr(grad_out), _ptr(grad_feat), _stream(stream)))
     del box_arr
     return grad_feat
+
+
+def e2a_block_workspace_bytes(n_atoms: int, L: int, C: int, H: int, dtype: int) -> int:
+    return int(_lib.e2a_block_workspace_bytes(n_atoms, L, C, H, dtype))
+
+
+def e2a_block_fwd(pos, row_ptr, col, h, weights: dict, *, L: int, C: int, H: int, cutoff: float, box=None,
+                  variant: str = "auto", out=None, workspace=None, stream=None):
+    """One block around the layer (include/e2a.h, e2a_block_fwd): h fp32
+    [N,(L+1)^2,C] in, the block's output out.  ``weights`` maps the names in
+    BLOCK_WEIGHTS to tensors in the storage dtype (w_gate may be absent for
+    L = 0); all on h's device."""
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    K = (L + 1) ** 2
+    w0 = weights["w_o"]
+    dtype = _storage_dtype(w0)
+    if variant not in VARIANTS:
+        raise ValueError(f"variant must be one of {sorted(VARIANTS)}")
+    _need(pos, "pos", torch.float32, dev, shape=(n, 3))
+    _need(row_ptr, "row_ptr", torch.int64, dev, shape=(n + 1,))
+    _need(col, "col", torch.int32, dev)
+    _need(h, "h", torch.float32, dev, shape=(n, K, C))
+    shapes = {"norm1": (L + 1, C), "w_q": (C, C), "w_k": (C, C), "w_rad": (8, L + 1, C), "w_o": (L + 1, C, C),
+              "norm2": (L + 1, C), "w_1": (L + 1, C, C), "w_gate": (C, L * C), "w_2": (L + 1, C, C)}
+    for name in BLOCK_WEIGHTS:
+        t = weights.get(name)
+        if name == "w_gate" and L == 0 and t is None:
+            continue
+        if name == "w_so2":
+            _need(t, name, w0.dtype, dev, numel=e2a_so2_param_count(L, C))
+        else:
+            _need(t, name, w0.dtype, dev, shape=shapes[name])
+    if out is None:
+        out = torch.empty_like(h)
+    _need(out, "out", torch.float32, dev, shape=(n, K, C))
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_block_workspace_bytes(n, L, C, H, dtype)), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    box_arr, box_p = _box_arg(box)
+    a = BlockArgs()
+    a.pos, a.box, a.n_atoms = _ptr(pos), box_p, n
+    a.row_ptr, a.col, a.n_edges = _ptr(row_ptr), _ptr(col), col.numel()
+    a.cutoff = float(cutoff)
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = L, C, H, 8, dtype, VARIANTS[variant]
+    a.h_in, a.h_out = _ptr(h), _ptr(out)
+    for name in BLOCK_WEIGHTS:
+        setattr(a, name, _ptr(weights.get(name)))
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    _check(_lib.e2a_block_fwd(ctypes.byref(a), _stream(stream)))
+    del box_arr
+    return out

@@ -432,3 +432,47 @@ def test_binding_checks_shapes_before_the_call(monkeypatch, name, bad):
     with pytest.raises(ValueError, match=name):
         B._layer(B.lib, t["pos"], t["row_ptr"], t["col"], t["feat"], t["w_q"], t["w_k"], t["w_rad"], t["w_so2"],
                  1, 16, 1, 5.0, None, "auto", None, None, None, None, True)
+
+
+def block_args(**kw):
+    a = B.BlockArgs()
+    for f in ("pos", "row_ptr", "col", "h_in", "h_out", "norm1", "w_q", "w_k", "w_rad", "w_so2", "w_o", "norm2",
+              "w_1", "w_gate", "w_2", "workspace"):
+        setattr(a, f, FAKE)
+    a.n_atoms, a.n_edges, a.cutoff = 10, 20, 5.0
+    a.L, a.C, a.H, a.n_rbf, a.dtype, a.variant = 1, 16, 1, 8, 0, 0
+    a.workspace_bytes = 1 << 30
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h_in=None), B.E2A_ERR_INVALID_ARG),
+    (dict(h_out=None), B.E2A_ERR_INVALID_ARG),
+    (dict(norm1=None), B.E2A_ERR_INVALID_ARG),
+    (dict(w_gate=None), B.E2A_ERR_INVALID_ARG),          # L = 1 needs the gate
+    (dict(w_so2=None), B.E2A_ERR_INVALID_ARG),           # the layer's own check
+    (dict(w_q=None), B.E2A_ERR_INVALID_ARG),
+    (dict(C=16, H=3), B.E2A_ERR_INVALID_ARG),
+    (dict(L=5), B.E2A_ERR_INVALID_ARG),
+    (dict(dtype=4), B.E2A_ERR_INVALID_ARG),
+    (dict(variant=2), B.E2A_ERR_UNSUPPORTED),            # no MFMA layer for L=1, C=16, fp32
+    (dict(workspace_bytes=16), B.E2A_ERR_INVALID_ARG),
+])
+def test_block_rejects_on_host(kw, status):
+    a = block_args(**kw)
+    st = B.lib().e2a_block_fwd(ctypes.byref(a), None)
+    assert st == status, (st, B.last_error_message())
+    assert B.last_error_message()
+    assert B.lib().e2a_block_fwd(None, None) == B.E2A_ERR_INVALID_ARG
+
+
+def test_block_gate_optional_at_l0_and_workspace_query():
+    a = block_args(L=0, w_gate=None, workspace=None)
+    assert B.lib().e2a_block_fwd(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "workspace" in B.last_error_message()          # not the gate
+    n, L, C = 1000, 3, 128
+    got = B.e2a_block_workspace_bytes(n, L, C, 8, B.E2A_DTYPE_BF16)
+    assert got >= B.e2a_attention_workspace_bytes(n, L, C, 8, 1) + n * 16 * C * (2 + 4 + 4 + 2)
+    assert B.e2a_block_workspace_bytes(n, 5, C, 8, 1) == 0
