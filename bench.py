@@ -263,6 +263,56 @@ def config_leg(B, torch, dev, name, iters=10):
     return res
 
 
+def block_leg(B, torch, dev, w, pos, rp, col, box, attn_ms):
+    """One block around the layer (e2a_block_fwd) and two stacked blocks on
+    the same workload, each block with its own seeded weights: one warm-up
+    and three timed calls, HIP events on the stream."""
+    from workloads import make_block_weights
+    h = torch.from_numpy(np.ascontiguousarray(w.as_f32("feat"))).to(dev)
+
+    def dev_w(bw):
+        out = {}
+        for k, v in bw.items():
+            if v.dtype == np.uint16:
+                out[k] = torch.from_numpy(np.ascontiguousarray(v).view(np.int16)).view(torch.bfloat16).to(dev)
+            else:
+                out[k] = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float32)).to(dev)
+        return out
+
+    bws = [dev_w(make_block_weights(w, i)) for i in range(2)]
+    dtype_code = B.E2A_DTYPE_BF16 if w.dtype == "bf16" else B.E2A_DTYPE_F32
+    ws = torch.empty(B.e2a_block_workspace_bytes(w.n_atoms, w.L, w.C, w.H, dtype_code), dtype=torch.uint8,
+                     device=dev)
+    x1 = torch.empty_like(h)
+    x2 = torch.empty_like(h)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        B.e2a_block_fwd(pos, rp, col, h, bws[0], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, out=x1,
+                        workspace=ws)
+
+    def two():
+        one()
+        B.e2a_block_fwd(pos, rp, col, x1, bws[1], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, out=x2,
+                        workspace=ws)
+
+    res = {}
+    for name, fn in (("block_ms", one), ("two_blocks_ms", two)):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for _ in range(3):
+            fn()
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        res[name] = ev[0].elapsed_time(ev[1]) / 3
+    res["block_nodewise_ms"] = res["block_ms"] - attn_ms
+    res["block_finite"] = bool(torch.isfinite(x2).all())
+    res["block_kernels"] = ("e2a_block_fwd: per-degree RMS norm, the fused layer, per-degree projection + residual "
+                            "(bf16 MFMA GEMM), norm, gated FFN (bf16 MFMA GEMMs) + residual")
+    return res
+
+
 def algorithmic_bytes(w, n_edges):
     """HBM bytes of one layer call with every array touched once: the node
     features (storage precision) in and the fp32 output out, the CSR graph,
@@ -360,6 +410,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other four workloads")
+    ap.add_argument("--no-block", action="store_true", help="skip the block around the layer")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path (run with --gpus 1).",
@@ -519,6 +570,11 @@ def main():
     }
     if bwd is not None:
         result["breakdown"].update(bwd)
+    if not args.no_block:
+        progress("timing one block and two stacked blocks")
+        result["breakdown"].update(block_leg(B, torch, dev, w, pos, rp, col, box, attn_ms))
+        progress(f"block {result['breakdown']['block_ms']:.1f} ms, two blocks "
+                 f"{result['breakdown']['two_blocks_ms']:.1f} ms")
     result["parity"] = parity
     result["breakdown"]["memory"] = memory
     if not args.no_configs:

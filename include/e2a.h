@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define E2A_ABI_VERSION 1
+#define E2A_ABI_VERSION 2
 
 typedef int32_t e2a_status;
 enum {
@@ -146,7 +146,39 @@ typedef struct e2a_attn_args {
   /* scratch */
   void* workspace;         /* device, e2a_attention_workspace_bytes(...) bytes        */
   size_t workspace_bytes;
+  /* optional, device (NULL: the call makes its own) */
+  const void* w_so2_packed;  /* e2a_pack_so2_weights of w_so2 (matrix-core path only;
+                                the scalar path ignores it)                            */
+  const int32_t* order;      /* [n_atoms] the order destinations are visited in, a
+                                permutation of 0..n_atoms-1 (e2a_destination_order);
+                                results depend on it (which atoms share edge tiles)   */
 } e2a_attn_args;
+
+/*
+ * Packed SO(2) weights, for callers that run the layer many times on the same
+ * weights (every forward call otherwise repacks them).  The matrix-core path
+ * streams w_so2 as MFMA B fragments: per |m|, output degree, wave column
+ * group and k-step, 64 lanes x 8 bf16 (one 16-byte load per lane).
+ * e2a_so2_packed_bytes gives the image's size for (L, C, dtype), 0 where no
+ * matrix-core build exists (then the packer returns E2A_ERR_UNSUPPORTED).
+ * The image is valid for every call with these weights; the library does not
+ * check that it matches w_so2.  Asynchronous.
+ */
+size_t e2a_so2_packed_bytes(int L, int C, int dtype);
+e2a_status e2a_pack_so2_weights(const void* w_so2, void* w_packed, int L, int C, int dtype, void* stream);
+
+/*
+ * Spatial order of the destinations the layer uses by default (the Morton
+ * code of a 64^3 grid over the bounding box of pos, stably sorted, ties by
+ * atom index): atoms close in the order are close in space, so workgroups
+ * working on neighbouring destinations share neighbour features in cache.
+ * For callers that run several layers on one geometry (stacked blocks), or
+ * that keep the order between neighbour-list rebuilds.  order: device i32
+ * [n_atoms]; workspace of e2a_destination_order_workspace_bytes(n_atoms).
+ */
+size_t e2a_destination_order_workspace_bytes(int64_t n_atoms);
+e2a_status e2a_destination_order(const float* pos, int64_t n_atoms, int32_t* order, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace e2a_attention_fwd needs. */
 size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype);
@@ -269,6 +301,8 @@ typedef struct e2a_block_args {
   const void* w_2;         /* [L+1, C, C]     FFN out                                 */
   void* workspace;         /* device, e2a_block_workspace_bytes(...) bytes            */
   size_t workspace_bytes;
+  const void* w_so2_packed;  /* optional, as in e2a_attn_args                          */
+  const int32_t* order;      /* optional, as in e2a_attn_args                          */
 } e2a_block_args;
 
 /* Bytes of device workspace e2a_block_fwd needs (0 for invalid sizes). */
@@ -276,7 +310,8 @@ size_t e2a_block_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype
 
 /* One block (above).  Asynchronous and deterministic; no memory set or copy
  * commands.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG for a NULL
- * h_in, h_out or node-wise weight. */
+ * h_in, h_out or node-wise weight, and E2A_ERR_UNSUPPORTED for C not a
+ * multiple of 4 or n_atoms (2L+1) >= 2^31. */
 e2a_status e2a_block_fwd(const e2a_block_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -18,7 +18,11 @@ _EXPORTS = (
     "e2a_block_workspace_bytes",
     "e2a_build_neighbors",
     "e2a_conv_fwd",
+    "e2a_destination_order",
+    "e2a_destination_order_workspace_bytes",
     "e2a_neighbors_workspace_bytes",
+    "e2a_pack_so2_weights",
+    "e2a_so2_packed_bytes",
     "e2a_so2_param_count",
     "e2a_version",
     "library_path",

@@ -1505,13 +1505,11 @@ __global__ void __launch_bounds__(1024) k_grad_norm(const float* __restrict__ gs
   }
 }
 
-// Spatial order of the destinations (Morton code of a 64^3 grid over the
-// bounding box, stably sorted with the atom index as the tie-break) and the
-// packed forward weights.
-template <int L>
-e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_t st) {
-  using S = Shape<L>;
-  int32_t* order = reinterpret_cast<int32_t*>(wb + W.order);
+// Spatial order of the destinations: the Morton code of a 64^3 grid over the
+// bounding box, stably sorted with the atom index as the tie-break, so the
+// order (and with it which atoms share edge chunks) is the same on every
+// launch.  `order` and the scratch come from the layout W.
+e2a_status spatial_order(const float* pos, int64_t n, const MfmaWs& W, char* wb, int32_t* order, hipStream_t st) {
   int32_t* key = reinterpret_cast<int32_t*>(wb + W.key);
   int32_t* key2 = reinterpret_cast<int32_t*>(wb + W.key2);
   int32_t* val2 = reinterpret_cast<int32_t*>(wb + W.val2);
@@ -1520,14 +1518,13 @@ e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
   float* bbox = reinterpret_cast<float*>(wb + W.bbox);
   float* bbox_part = reinterpret_cast<float*>(wb + W.bbox_part);
-  const int64_t n = a->n_atoms;
   const int64_t nb = (n + 255) / 256;
   const int64_t nblk = sort_blocks(n);
   {
-    const e2a_status sb = launch_bbox(a->pos, n, bbox_part, bbox, st);
+    const e2a_status sb = launch_bbox(pos, n, bbox_part, bbox, st);
     if (sb != E2A_OK) return sb;
   }
-  k_ord_keys<<<nb, 256, 0, st>>>(a->pos, n, bbox, key, order);
+  k_ord_keys<<<nb, 256, 0, st>>>(pos, n, bbox, key, order);
   E2A_LAUNCH_CHECK();
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass * kRadixBits;
@@ -1542,9 +1539,23 @@ e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_
     k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout);
     E2A_LAUNCH_CHECK();
   }
-  const int64_t nv = S::wtotal();
-  k_pack_so2<L, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
-                                                          reinterpret_cast<bf16x8*>(wb + W.w));
+  return E2A_OK;
+}
+
+// The destination order (the caller's, or the spatial order computed here)
+// and the packed forward weights (the caller's image, or packed here).
+template <int L>
+e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_t st) {
+  using S = Shape<L>;
+  if (!a->order) {
+    const e2a_status so = spatial_order(a->pos, a->n_atoms, W, wb, reinterpret_cast<int32_t*>(wb + W.order), st);
+    if (so != E2A_OK) return so;
+  }
+  if (!a->w_so2_packed) {
+    const int64_t nv = S::wtotal();
+    k_pack_so2<L, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
+                                                            reinterpret_cast<bf16x8*>(wb + W.w));
+  }
   k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_rad),
                                                             reinterpret_cast<u32x4*>(wb + W.rad));
   E2A_LAUNCH_CHECK();
@@ -1561,9 +1572,9 @@ e2a_status base_params(const e2a_attn_args* a, const MfmaWs& W, char* wb, const 
   p.row_ptr = a->row_ptr;
   p.col = a->col;
   p.feat = static_cast<const uint16_t*>(a->feat);
-  p.wpk = reinterpret_cast<const bf16x8*>(wb + W.w);
+  p.wpk = a->w_so2_packed ? static_cast<const bf16x8*>(a->w_so2_packed) : reinterpret_cast<const bf16x8*>(wb + W.w);
   p.radpk = reinterpret_cast<const bf16x8*>(wb + W.rad);
-  p.order = reinterpret_cast<const int32_t*>(wb + W.order);
+  p.order = a->order ? a->order : reinterpret_cast<const int32_t*>(wb + W.order);
   p.n_atoms = a->n_atoms;
   int dev = 0, n_cu = 0;
   E2A_HIP_CHECK(hipGetDevice(&dev));
@@ -1713,6 +1724,42 @@ e2a_status launch_radial_mfma(const BwdPlan& pl, float* w_rad, hipStream_t s) {
     case 4: return launch_radial_typed<4>(pl, w_rad, s);
     default: return fail(E2A_ERR_UNSUPPORTED, "MFMA radial pass: L=%d", pl.a->L);
   }
+}
+
+size_t mfma_packed_bytes(int L) {
+  switch (L) {
+    case 1: return Shape<1>::wtotal() * 16;
+    case 2: return Shape<2>::wtotal() * 16;
+    case 3: return Shape<3>::wtotal() * 16;
+    case 4: return Shape<4>::wtotal() * 16;
+    default: return 0;
+  }
+}
+
+e2a_status pack_so2_mfma(const void* w_so2, void* out, int L, hipStream_t st) {
+  auto go = [&](auto lc) {
+    constexpr int LL = decltype(lc)::value;
+    const int64_t nv = Shape<LL>::wtotal();
+    k_pack_so2<LL, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(w_so2),
+                                                             static_cast<bf16x8*>(out));
+  };
+  switch (L) {
+    case 1: go(std::integral_constant<int, 1>{}); break;
+    case 2: go(std::integral_constant<int, 2>{}); break;
+    case 3: go(std::integral_constant<int, 3>{}); break;
+    case 4: go(std::integral_constant<int, 4>{}); break;
+    default: return fail(E2A_ERR_UNSUPPORTED, "packed SO(2) image: L=%d", L);
+  }
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
+size_t order_workspace_bytes(int64_t n) { return mfma_ws_layout<1>(n, false).total; }
+
+e2a_status destination_order(const float* pos, int64_t n, int32_t* order, void* ws, hipStream_t st) {
+  if (n == 0) return E2A_OK;
+  const MfmaWs W = mfma_ws_layout<1>(n, false);
+  return spatial_order(pos, n, W, static_cast<char*>(ws), order, st);
 }
 
 bool mfma_supported(int L, int C, int H, int dtype) {

@@ -312,6 +312,9 @@ e2a_status launch_qk(const AttnPlan& pl, hipStream_t s) {
   const e2a_attn_args* a = pl.a;
   if (a->n_atoms == 0) return E2A_OK;
   const int ncomp = (a->L + 1) * (a->L + 1);
+  if (block_uses_mfma(a->C, a->dtype))
+    return launch_qk_mfma(static_cast<const uint16_t*>(a->feat), static_cast<const uint16_t*>(a->w_q),
+                          static_cast<const uint16_t*>(a->w_k), pl.wqk_t, a->n_atoms, ncomp, a->C, pl.q, pl.k, s);
   const int threads = std::min(256, ((a->C + 63) / 64) * 64);
   const dim3 grid((a->n_atoms + 15) / 16);
   const size_t smem = sizeof(float) * 16 * a->C;

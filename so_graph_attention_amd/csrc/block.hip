@@ -46,8 +46,20 @@ __device__ __forceinline__ int degree_of(int comp) {
 }
 
 // out[a][l*l + m][c] = gamma[l][c] h[a][l*l + m][c] / sqrt(mean_{m,c} h^2 + eps),
-// one wave per atom, fp32 sums.  OutT is the storage of the result (bf16 for
-// the attention layer's input, or fp32).
+// one wave per atom, fp32 sums, 16-byte loads (C is a multiple of 4).  OutT
+// is the storage of the result (bf16 for the attention layer's input, or fp32).
+template <typename OutT>
+__device__ __forceinline__ void store4(OutT* p, const float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* p, const float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* p, const float4 v) {
+  *reinterpret_cast<uint2*>(p) = uint2{f32_to_bf16_rne(v.x) | (uint32_t(f32_to_bf16_rne(v.y)) << 16),
+                                       f32_to_bf16_rne(v.z) | (uint32_t(f32_to_bf16_rne(v.w)) << 16)};
+}
+
 template <typename GT, typename OutT>
 __global__ void __launch_bounds__(256) k_degree_norm(const float* __restrict__ h, const GT* __restrict__ gamma,
                                                      OutT* __restrict__ out, int64_t n, int L, int C) {
@@ -55,47 +67,69 @@ __global__ void __launch_bounds__(256) k_degree_norm(const float* __restrict__ h
   const int64_t a = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (a >= n) return;
   const int K = (L + 1) * (L + 1);
+  const unsigned c4 = static_cast<unsigned>(C / 4);
   const float* ha = h + a * K * C;
+  OutT* oa = out + a * K * C;
   for (int l = 0; l <= L; ++l) {
-    const int cnt = (2 * l + 1) * C;
-    const float* hl = ha + l * l * C;
+    const unsigned cnt4 = static_cast<unsigned>((2 * l + 1) * C / 4);
+    const float4* hl = reinterpret_cast<const float4*>(ha + l * l * C);
     float ss = 0.0f;
-    for (int t = lane; t < cnt; t += 64) ss += hl[t] * hl[t];
+    for (unsigned t = lane; t < cnt4; t += 64) {
+      const float4 v = hl[t];
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(cnt) + kNormEps);
-    for (int t = lane; t < cnt; t += 64) {
-      const float g = load_as_f32(gamma, (size_t)l * C + t % C);
-      store_as(out, (size_t)(a * K + l * l) * C + t, hl[t] * inv * g);
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(4 * cnt4) + kNormEps);
+    for (unsigned t = lane; t < cnt4; t += 64) {
+      const float4 v = hl[t];
+      const unsigned c = (t % c4) * 4;
+      float4 o;
+      o.x = v.x * inv * load_as_f32(gamma, (size_t)l * C + c);
+      o.y = v.y * inv * load_as_f32(gamma, (size_t)l * C + c + 1);
+      o.z = v.z * inv * load_as_f32(gamma, (size_t)l * C + c + 2);
+      o.w = v.w * inv * load_as_f32(gamma, (size_t)l * C + c + 3);
+      store4(oa + l * l * C + 4 * t, o);
     }
   }
 }
 
-// act[a][comp][c] = SiLU(u) for l = 0, u * sigmoid(z[a][(l-1) C + c]) for l >= 1.
+// act[a][comp][c] = SiLU(u) for l = 0, u * sigmoid(z[a][(l-1) C + c]) for l >= 1;
+// atoms in turn per workgroup, four channels per thread.
 template <typename OutT>
 __global__ void __launch_bounds__(256) k_gate(const float* __restrict__ u, const float* __restrict__ z,
                                               OutT* __restrict__ act, int64_t n, int L, int C) {
   const int K = (L + 1) * (L + 1);
-  const int64_t total = n * K * C;
-  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t a = t / (K * C);
-    const int rem = static_cast<int>(t % (K * C));
-    const int comp = rem / C, c = rem % C;
-    const float x = u[t];
-    float v;
-    if (comp == 0) {
-      v = x / (1.0f + expf(-x));
-    } else {
-      const int l = degree_of(comp);
-      const float g = z[a * L * C + (l - 1) * C + c];
-      v = x / (1.0f + expf(-g));
+  const unsigned kc4 = static_cast<unsigned>(K * C / 4), c4 = static_cast<unsigned>(C / 4);
+  for (int64_t a = blockIdx.x; a < n; a += gridDim.x) {
+    const float4* ua = reinterpret_cast<const float4*>(u + a * K * C);
+    const float* za = z + a * L * C;
+    for (unsigned t = threadIdx.x; t < kc4; t += blockDim.x) {
+      const unsigned comp = t / c4, c = (t % c4) * 4;
+      const float4 x = ua[t];
+      float4 v;
+      if (comp == 0) {
+        v.x = x.x / (1.0f + expf(-x.x));
+        v.y = x.y / (1.0f + expf(-x.y));
+        v.z = x.z / (1.0f + expf(-x.z));
+        v.w = x.w / (1.0f + expf(-x.w));
+      } else {
+        const float* g = za + (degree_of(static_cast<int>(comp)) - 1) * C + c;
+        v.x = x.x / (1.0f + expf(-g[0]));
+        v.y = x.y / (1.0f + expf(-g[1]));
+        v.z = x.z / (1.0f + expf(-g[2]));
+        v.w = x.w / (1.0f + expf(-g[3]));
+      }
+      store4(act + a * K * C + 4 * t, v);
     }
-    store_as(act, (size_t)t, v);
   }
 }
 
 // Rows of the per-degree GEMM: degree l has n (2l+1) rows; row r is atom
-// r / (2l+1), component l*l + r % (2l+1).  Tiles of kRows rows are numbered
-// degree by degree (tile_start[l] is the first tile of degree l).
+// r / (2l+1), component l*l + r % (2l+1).  Tiles are numbered by groups of
+// `group` consecutive atoms, and within a group by degree l_lo..l_hi, in
+// tiles of at most tile_rows rows.  (Measured at 100k atoms: one group of all
+// atoms, i.e. degree by degree, runs faster than groups of 32 atoms, whose
+// degree-0 tiles are three quarters empty.)
 struct DegGemm {
   const void* x;            // [n][kx][cin], fp32 or bf16 (XT)
   const uint16_t* wb;       // bf16 weights, degree l at wb + l * w_deg_stride, [cin][cout]
@@ -108,77 +142,178 @@ struct DegGemm {
   int y_comp0;              // y component of degree l's row m: comp(l, m) - y_comp0 (ky = 1: 0)
   int cin, cout;
   int l_lo, l_hi;           // degrees computed
-  int tile_start[6];        // first tile of degree l_lo + i; tile_start[l_hi - l_lo + 1] = total
+  int tile_start[6];        // first tile of degree l_lo + i within a group; [l_hi - l_lo + 1] = tiles per group
+  const uint16_t* wb2;      // optional second bf16 product (grid z = 1): the same x times wb2 into y2
+  float* y2;
+  int tile_rows;            // rows per tile (set by the launcher)
+  int64_t group;            // atoms per tile group (set by the launcher)
 };
 
 constexpr int kRows = 64;
 constexpr int kCols = 64;
-
-__device__ __forceinline__ void tile_degree(const DegGemm& g, int tile, int& l, int64_t& row0) {
+// Degree, first row and end row (exclusive) of tile `tile`.
+__device__ __forceinline__ void tile_degree(const DegGemm& g, int tile, int& l, int64_t& row0, int64_t& row_end) {
+  const int per = g.tile_start[g.l_hi - g.l_lo + 1];
+  const int64_t grp = tile / per;
+  const int in = tile % per;
   int i = 0;
-  while (tile >= g.tile_start[i + 1]) ++i;
+  while (in >= g.tile_start[i + 1]) ++i;
   l = g.l_lo + i;
-  row0 = (int64_t)(tile - g.tile_start[i]) * kRows;
+  const int64_t w = 2 * l + 1;
+  const int64_t g0 = grp * g.group * w;
+  row0 = g0 + (int64_t)(in - g.tile_start[i]) * g.tile_rows;
+  int64_t e = g0 + g.group * w;
+  if (e > row0 + g.tile_rows) e = row0 + g.tile_rows;
+  if (e > g.n * w) e = g.n * w;
+  row_end = e;
 }
 
-// bf16 matrix-core path: a 64 x 64 output tile per workgroup, four waves of
-// one 32 x 32 v_mfma_f32_32x32x16_bf16 accumulator; the tile's rows of x and
-// the weight columns are staged in LDS as bf16 with k contiguous.
+// bf16 matrix-core path: a 128 x 128 output tile per workgroup, four waves of
+// 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16 accumulators).  The tile's rows of
+// x (rounded to bf16) and the weight columns (from the transposed copy wt,
+// k contiguous) are staged in LDS with k contiguous, so both operands are
+// 16-byte LDS reads.
+constexpr int kMRows = 128;
+constexpr int kMCols = 128;
+
+// Eight consecutive values of x as loaded (fp32 or bf16 bits).
+template <typename XT>
+struct XT8;
+template <>
+struct XT8<float> {
+  float4 a, b;
+};
+template <>
+struct XT8<uint16_t> {
+  uint4 a;
+};
+__device__ __forceinline__ XT8<float> load8(const float* p) {
+  return XT8<float>{*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+__device__ __forceinline__ XT8<uint16_t> load8(const uint16_t* p) {
+  return XT8<uint16_t>{*reinterpret_cast<const uint4*>(p)};
+}
+__device__ __forceinline__ void store8_bf16(const XT8<float>& x, uint16_t* dst) {
+  const float v[8] = {x.a.x, x.a.y, x.a.z, x.a.w, x.b.x, x.b.y, x.b.z, x.b.w};
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = f32_to_bf16_rne(v[2 * q]) | (uint32_t(f32_to_bf16_rne(v[2 * q + 1])) << 16);
+  *reinterpret_cast<uint4*>(dst) = uint4{w[0], w[1], w[2], w[3]};
+}
+__device__ __forceinline__ void store8_bf16(const XT8<uint16_t>& x, uint16_t* dst) {
+  *reinterpret_cast<uint4*>(dst) = x.a;
+}
+
 template <typename XT>
 __global__ void __launch_bounds__(256) k_deg_gemm_mfma(DegGemm g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int cin = g.cin, ldk = g.cin + 8;
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);   // [kRows][ldk]
-  uint16_t* Bs = As + kRows * ldk;                    // [kCols][ldk]: column n's k values
+  const int cin = g.cin, ldk = g.cin + 8, kg = g.cin / 8;
+  uint16_t* As = reinterpret_cast<uint16_t*>(smem);   // [kMRows][ldk]
   int l;
-  int64_t row0;
-  tile_degree(g, blockIdx.x, l, row0);
-  const int w = 2 * l + 1;
-  const int64_t nrows = g.n * w;
-  const int col0 = blockIdx.y * kCols;
+  int64_t row0, row_end;
+  tile_degree(g, blockIdx.x, l, row0, row_end);
+  const unsigned w = 2 * l + 1;
+  const unsigned nrows = static_cast<unsigned>(row_end);   // < 2^31 (checked on the host)
+  const int col0 = blockIdx.y * kMCols;
   const int tid = threadIdx.x;
-  // x rows -> bf16, 8 consecutive k per thread and step
-  for (int t = tid; t < kRows * cin / 8; t += 256) {
-    const int r = t / (cin / 8), k8 = (t % (cin / 8)) * 8;
-    const int64_t row = row0 + r;
-    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (row < nrows) {
-      const int64_t a = row / w;
-      const int comp = l * l + static_cast<int>(row % w);
-      const size_t base = (size_t)(a * g.kx + comp) * cin + k8;
+  // the tile's rows of x: a lane's 8 k values per step, all loads in flight
+  // before the conversions and LDS stores
+  constexpr int kSteps = kMRows * 16 / 256;   // cin <= 128: at most 8 steps of 8 k
+  XT8<XT> xv[kSteps];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = load_as_f32(static_cast<const XT*>(g.x), base + q);
+  for (int q = 0; q < kSteps; ++q) {
+    const int t = tid + 256 * q;
+    const int r = t / kg, k8 = (t % kg) * 8;
+    const unsigned row = static_cast<unsigned>(row0) + r;
+    if (t < kMRows * kg && row < nrows) {
+      const unsigned a = row / w, comp = l * l + row % w;
+      xv[q] = load8(static_cast<const XT*>(g.x) + ((size_t)a * g.kx + comp) * cin + k8);
+    } else {
+      xv[q] = XT8<XT>{};
     }
+  }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) As[r * ldk + k8 + q] = f32_to_bf16_rne(v[q]);
+  for (int q = 0; q < kSteps; ++q) {
+    const int t = tid + 256 * q;
+    if (t < kMRows * kg) store8_bf16(xv[q], As + (t / kg) * ldk + (t % kg) * 8);
   }
-  // weight columns col0 .. col0 + 63 of degree l, transposed into [n][k]
-  const uint16_t* W = g.wb + (int64_t)l * g.w_deg_stride;
-  for (int t = tid; t < cin * kCols; t += 256) {
-    const int k = t / kCols, nn = t % kCols;
-    const int col = col0 + nn;
-    Bs[nn * ldk + k] = col < g.cout ? W[(size_t)k * g.cout + col] : uint16_t(0);
-  }
+  // wt: [cout][cin] per degree (the transposed weights, k contiguous); the
+  // B fragments come straight from it (L2-resident), 16 bytes per lane
+  const uint16_t* Wt = (blockIdx.z ? g.wb2 : g.wb) + (int64_t)l * g.w_deg_stride;
+  float* Y = blockIdx.z ? g.y2 : g.y;
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
-  const int wr = 32 * (wave >> 1), wc = 32 * (wave & 1);
-  f32x16 acc = {};
-  for (int k0 = 0; k0 < cin; k0 += 16) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(As + (wr + (lane & 31)) * ldk + k0 + 8 * half);
-    const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bs + (wc + (lane & 31)) * ldk + k0 + 8 * half);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
-  }
-  const int col = col0 + wc + (lane & 31);
-  if (col >= g.cout) return;
+  const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
+  const uint16_t* bcol[2];
+  bool bok[2];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int64_t row = row0 + wr + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (row >= nrows) continue;
-    const int64_t a = row / w;
-    const int comp = l * l + static_cast<int>(row % w) - g.y_comp0;
-    const size_t o = (size_t)(a * g.ky + comp) * g.cout + col;
-    g.y[o] = (g.res ? g.res[o] : 0.0f) + acc[r];
+  for (int i = 0; i < 2; ++i) {
+    const int col = col0 + wc + 32 * i + (lane & 31);
+    bok[i] = col < g.cout;
+    bcol[i] = Wt + (size_t)(bok[i] ? col : 0) * cin + 8 * half;
   }
+  f32x16 acc[2][2] = {};
+  for (int k0 = 0; k0 < cin; k0 += 16) {
+    bf16x8 a[2], b[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      a[i] = *reinterpret_cast<const bf16x8*>(As + (wr + 32 * i + (lane & 31)) * ldk + k0 + 8 * half);
+      b[i] = bok[i] ? *reinterpret_cast<const bf16x8*>(bcol[i] + k0) : bf16x8{};
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j2], acc[i][j2], 0, 0, 0);
+  }
+  // output offsets of the lane's 32 rows (two row tiles), then residual
+  // loads in flight together, then the stores
+  size_t off[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const unsigned row = static_cast<unsigned>(row0) + wr + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+      const unsigned a = row / w, comp = l * l + row % w - g.y_comp0;
+      off[i][r] = row < nrows ? ((size_t)a * g.ky + comp) * g.cout : ~size_t(0);
+    }
+#pragma unroll
+  for (int j2 = 0; j2 < 2; ++j2) {
+    const int col = col0 + wc + 32 * j2 + (lane & 31);
+    if (col >= g.cout) continue;
+    if (g.res) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (off[i][r] != ~size_t(0)) acc[i][j2][r] += g.res[off[i][r] + col];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (off[i][r] != ~size_t(0)) Y[off[i][r] + col] = acc[i][j2][r];
+  }
+}
+
+// wt[d][n][k] = w[d][k][n] (bf16), for the matrix-core GEMM's k-contiguous
+// weight columns.
+__global__ void k_transpose_bf16(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt, int nmat, int rows,
+                                 int cols) {
+  __shared__ uint16_t tile[32][33];
+  const int m = blockIdx.z;
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const uint16_t* src = w + (size_t)m * rows * cols;
+  uint16_t* dst = wt + (size_t)m * rows * cols;
+  for (int t = threadIdx.x; t < 32 * 32; t += blockDim.x) {
+    const int r = t / 32, c = t % 32;
+    if (r0 + r < rows && c0 + c < cols) tile[r][c] = src[(size_t)(r0 + r) * cols + c0 + c];
+  }
+  __syncthreads();
+  for (int t = threadIdx.x; t < 32 * 32; t += blockDim.x) {
+    const int c = t / 32, r = t % 32;
+    if (r0 + r < rows && c0 + c < cols) dst[(size_t)(c0 + c) * rows + r0 + r] = tile[r][c];
+  }
+  (void)nmat;
 }
 
 // fp32 path (fp32 storage, or shapes without a matrix-core tile): the same
@@ -190,10 +325,9 @@ __global__ void __launch_bounds__(256) k_deg_gemm_valu(DegGemm g) {
   float* As = reinterpret_cast<float*>(smem);   // [kRows][cin]
   float* Bs = As + kRows * cin;                 // [cin][kCols]
   int l;
-  int64_t row0;
-  tile_degree(g, blockIdx.x, l, row0);
+  int64_t row0, nrows;
+  tile_degree(g, blockIdx.x, l, row0, nrows);
   const int w = 2 * l + 1;
-  const int64_t nrows = g.n * w;
   const int col0 = blockIdx.y * kCols;
   const int tid = threadIdx.x;
   for (int t = tid; t < kRows * cin; t += 256) {
@@ -266,7 +400,9 @@ BlockWs block_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   w.n2 = take(s * nkc);                    // Norm2, later the gated activations
   w.z = take(sizeof(float) * (size_t)n * (L > 0 ? L : 1) * C);
   const size_t nw = (size_t)(L + 1) * C * C;
-  w.wf = block_uses_mfma(C, dtype) ? take(0) : take(sizeof(float) * (3 * nw + (size_t)C * L * C));
+  // node-wise weights: transposed bf16 copies (matrix cores) or fp32 copies (VALU)
+  w.wf = block_uses_mfma(C, dtype) ? take(sizeof(uint16_t) * (3 * nw + (size_t)C * L * C))
+                                   : take(sizeof(float) * (3 * nw + (size_t)C * L * C));
   w.attn_ws = off;
   w.attn_ws_bytes = 0;   // set by the caller from the attention workspace query
   w.total = off;
@@ -293,15 +429,22 @@ e2a_status launch_norm(const float* h, const void* gamma, void* out, int64_t n, 
 // fp32; weights as bf16 (mfma) or fp32 (valu).
 e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (g.n == 0) return E2A_OK;
-  int tiles = 0;
+  g.tile_rows = mfma ? kMRows : kRows;
+  const int tcols = mfma ? kMCols : kCols;
+  g.group = g.n;
+  int64_t per = 0;
   for (int l = g.l_lo; l <= g.l_hi; ++l) {
-    g.tile_start[l - g.l_lo] = tiles;
-    tiles += static_cast<int>((g.n * (2 * l + 1) + kRows - 1) / kRows);
+    if (per > INT32_MAX) break;
+    g.tile_start[l - g.l_lo] = static_cast<int>(per);
+    per += (g.group * (2 * l + 1) + g.tile_rows - 1) / g.tile_rows;
   }
-  g.tile_start[g.l_hi - g.l_lo + 1] = tiles;
-  const dim3 grid(tiles, (g.cout + kCols - 1) / kCols);
+  if (per > INT32_MAX) return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: %lld tiles", (long long)per);
+  g.tile_start[g.l_hi - g.l_lo + 1] = static_cast<int>(per);
+  const int64_t tiles = (g.n + g.group - 1) / g.group * per;
+  if (tiles > INT32_MAX) return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: %lld tiles", (long long)tiles);
+  const dim3 grid(static_cast<unsigned>(tiles), (g.cout + tcols - 1) / tcols, mfma && g.wb2 ? 2 : 1);
   if (mfma) {
-    const size_t smem = sizeof(uint16_t) * (size_t)(kRows + kCols) * (g.cin + 8);
+    const size_t smem = sizeof(uint16_t) * (size_t)kMRows * (g.cin + 8);
     if (x_bf16) {
       E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_deg_gemm_mfma<uint16_t>),
                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
@@ -327,6 +470,16 @@ e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   return E2A_OK;
 }
 
+// dst[m][c][r] = src[m][r][c] for nmat bf16 matrices of rows x cols.
+e2a_status launch_transpose(const void* src, uint16_t* dst, int nmat, int rows, int cols, hipStream_t s) {
+  if (nmat == 0 || rows == 0 || cols == 0) return E2A_OK;
+  const dim3 grid((cols + 31) / 32, (rows + 31) / 32, nmat);
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), dst, nmat, rows,
+                     cols);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
 e2a_status launch_widen(const void* src, float* dst, int64_t n, int dtype, hipStream_t s) {
   if (n == 0) return E2A_OK;
   const dim3 grid((n + 255) / 256);
@@ -339,6 +492,25 @@ e2a_status launch_widen(const void* src, float* dst, int64_t n, int dtype, hipSt
 }
 
 }  // namespace
+
+e2a_status launch_qk_mfma(const uint16_t* feat, const uint16_t* wq, const uint16_t* wk, uint16_t* wqk_t, int64_t n,
+                          int K, int C, float* q, float* k, hipStream_t s) {
+  e2a_status st = launch_transpose(wq, wqk_t, 1, C, C, s);
+  if (st == E2A_OK) st = launch_transpose(wk, wqk_t + (size_t)C * C, 1, C, C, s);
+  if (st != E2A_OK) return st;
+  DegGemm g{};
+  g.x = feat;
+  g.n = n;
+  g.kx = K;
+  g.ky = 1;
+  g.cin = g.cout = C;
+  g.l_lo = g.l_hi = 0;
+  g.wb = wqk_t;
+  g.y = q;
+  g.wb2 = wqk_t + (size_t)C * C;
+  g.y2 = k;
+  return launch_deg_gemm(g, true, true, s);
+}
 
 e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   const e2a_block_args* b = p.b;
@@ -355,9 +527,22 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   const bool mfma = block_uses_mfma(C, dtype);
   const bool bf = dtype == E2A_DTYPE_BF16;
   const int64_t nw = (int64_t)(L + 1) * C * C;
-  // fp32 copies of the node-wise weights for the VALU path
+  // fp32 copies of the node-wise weights for the VALU path, transposed bf16
+  // copies (k contiguous) for the matrix cores
   const float *wo_f = nullptr, *w1_f = nullptr, *w2_f = nullptr, *wg_f = nullptr;
-  if (!mfma) {
+  const uint16_t *wo_t = nullptr, *w1_t = nullptr, *w2_t = nullptr, *wg_t = nullptr;
+  if (mfma) {
+    uint16_t* wt = reinterpret_cast<uint16_t*>(base + W.wf);
+    e2a_status st = launch_transpose(b->w_o, wt, L + 1, C, C, s);
+    if (st == E2A_OK) st = launch_transpose(b->w_1, wt + nw, L + 1, C, C, s);
+    if (st == E2A_OK) st = launch_transpose(b->w_2, wt + 2 * nw, L + 1, C, C, s);
+    if (st == E2A_OK && L > 0) st = launch_transpose(b->w_gate, wt + 3 * nw, 1, C, L * C, s);
+    if (st != E2A_OK) return st;
+    wo_t = wt;
+    w1_t = wt + nw;
+    w2_t = wt + 2 * nw;
+    wg_t = wt + 3 * nw;
+  } else {
     float* wf = reinterpret_cast<float*>(base + W.wf);
     e2a_status st = launch_widen(b->w_o, wf, nw, dtype, s);
     if (st == E2A_OK) st = launch_widen(b->w_1, wf + nw, nw, dtype, s);
@@ -394,6 +579,8 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   a.w_so2 = b->w_so2;
   a.out = attn;
   a.out_lse = nullptr;
+  a.w_so2_packed = b->w_so2_packed;
+  a.order = b->order;
   a.workspace = base + W.attn_ws;
   a.workspace_bytes = W.attn_ws_bytes;
   st = p.attention(&a, s);
@@ -407,7 +594,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   g.l_hi = L;
   g.w_deg_stride = (int64_t)C * C;
   g.x = attn;
-  g.wb = static_cast<const uint16_t*>(b->w_o);
+  g.wb = wo_t;
   g.wf = wo_f;
   g.y = h1;
   g.res = b->h_in;
@@ -419,7 +606,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   // u = n2 W1 (into the attention output's space), z = n2[l = 0] W_gate
   float* u = attn;
   g.x = n2;
-  g.wb = static_cast<const uint16_t*>(b->w_1);
+  g.wb = w1_t;
   g.wf = w1_f;
   g.y = u;
   g.res = nullptr;
@@ -435,7 +622,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     gz.cout = L * C;
     gz.l_lo = gz.l_hi = 0;
     gz.w_deg_stride = 0;
-    gz.wb = static_cast<const uint16_t*>(b->w_gate);
+    gz.wb = wg_t;
     gz.wf = wg_f;
     gz.y = z;
     st = launch_deg_gemm(gz, mfma, bf, s);
@@ -443,8 +630,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   }
   // act = gate(u, z), in n2's space (Norm2 is no longer needed)
   {
-    const int64_t total = n * K * C;
-    const dim3 grid(static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 65536)));
+    const dim3 grid(static_cast<unsigned>(std::min<int64_t>(n, 8192)));
     if (bf)
       hipLaunchKernelGGL(k_gate<uint16_t>, grid, dim3(256), 0, s, u, z, static_cast<uint16_t*>(n2), n, L, C);
     else
@@ -453,7 +639,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   }
   // out = h1 + act W2
   g.x = n2;
-  g.wb = static_cast<const uint16_t*>(b->w_2);
+  g.wb = w2_t;
   g.wf = w2_f;
   g.y = b->h_out;
   g.res = h1;

@@ -25,7 +25,7 @@ void clear_error() { g_msg[0] = '\0'; }
 namespace {
 
 struct AttnWs {
-  size_t q, k, w, total;
+  size_t q, k, wqk_t, w, total;
 };
 
 AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
@@ -34,13 +34,14 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, 256); return o; };
   w.q = take(sizeof(float) * (size_t)n * C);
   w.k = take(sizeof(float) * (size_t)n * C);
+  w.wqk_t = take(block_uses_mfma(C, dtype) ? sizeof(uint16_t) * 2 * (size_t)C * C : 0);
   w.w = take(mfma_supported(L, C, H, dtype) ? mfma_workspace_bytes(n, L, C, false) : 0);
   w.total = off;
   return w;
 }
 
 struct BwdWs {
-  size_t q, k, dq, ds, wqkt, mfma, total;
+  size_t q, k, dq, ds, wqkt, wqk_bf, mfma, total;
 };
 
 // The matrix-core region is sized whenever (L, C, H) has a bf16 build, so
@@ -54,6 +55,7 @@ BwdWs bwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   w.dq = take(sizeof(float) * (size_t)n * C);
   w.ds = take(sizeof(float) * (size_t)e * H);
   w.wqkt = take(sizeof(float) * 2 * (size_t)C * C);
+  w.wqk_bf = take(sizeof(uint16_t) * 2 * (size_t)C * C);
   w.mfma = take(mfma_supported(L, C, H, E2A_DTYPE_BF16) ? mfma_workspace_bytes(n, L, C, true) : 0);
   w.total = off;
   return w;
@@ -120,6 +122,7 @@ e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* gr
   qk.a = a;
   qk.q = reinterpret_cast<float*>(base + ws.q);
   qk.k = reinterpret_cast<float*>(base + ws.k);
+  qk.wqk_t = reinterpret_cast<uint16_t*>(base + ws.wqk_bf);
   BwdPlan pl{};
   pl.a = a;
   pl.grad_out = grad_out;
@@ -203,6 +206,36 @@ int64_t e2a_so2_param_count(int L, int C) {
   return n;
 }
 
+size_t e2a_so2_packed_bytes(int L, int C, int dtype) {
+  if (L < 1 || L > 4 || !mfma_supported(L, C, 8, dtype)) return 0;
+  return mfma_packed_bytes(L);
+}
+
+e2a_status e2a_pack_so2_weights(const void* w_so2, void* w_packed, int L, int C, int dtype, void* stream) {
+  clear_error();
+  if (L < 0 || L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", L);
+  if (e2a_so2_packed_bytes(L, C, dtype) == 0)
+    return fail(E2A_ERR_UNSUPPORTED, "no matrix-core build (packed image) for L=%d C=%d dtype=%d", L, C, dtype);
+  if (!w_so2 || !w_packed) return fail(E2A_ERR_INVALID_ARG, "w_so2 and w_packed must be set");
+  return pack_so2_mfma(w_so2, w_packed, L, static_cast<hipStream_t>(stream));
+}
+
+size_t e2a_destination_order_workspace_bytes(int64_t n_atoms) {
+  return n_atoms < 0 ? 0 : order_workspace_bytes(n_atoms);
+}
+
+e2a_status e2a_destination_order(const float* pos, int64_t n_atoms, int32_t* order, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  clear_error();
+  if (n_atoms < 0 || n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
+  if (n_atoms == 0) return E2A_OK;
+  if (!pos || !order) return fail(E2A_ERR_INVALID_ARG, "pos and order must be set");
+  const size_t need = order_workspace_bytes(n_atoms);
+  if (!workspace || workspace_bytes < need)
+    return fail(E2A_ERR_INVALID_ARG, "workspace too small: %zu < %zu", workspace_bytes, need);
+  return destination_order(pos, n_atoms, order, workspace, static_cast<hipStream_t>(stream));
+}
+
 size_t e2a_attention_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype) {
   if (n_atoms < 0 || L < 0 || L > 4 || C <= 0 || H <= 0) return 0;
   return attn_ws_layout(n_atoms, L, C, H, dtype).total;
@@ -259,6 +292,7 @@ e2a_status run_layer(const e2a_attn_args* a, void* stream, bool conv) {
   char* base = static_cast<char*>(a->workspace);
   pl.q = reinterpret_cast<float*>(base + ws.q);
   pl.k = reinterpret_cast<float*>(base + ws.k);
+  pl.wqk_t = reinterpret_cast<uint16_t*>(base + ws.wqk_t);
   pl.mfma_ws = base + ws.w;
   pl.periodic = a->box != nullptr;
   pl.conv = conv;
@@ -374,6 +408,9 @@ e2a_status e2a_block_fwd(const e2a_block_args* b, void* stream) {
   if (b->L < 0 || b->L > 4) return fail(E2A_ERR_INVALID_ARG, "L=%d outside 0..4", b->L);
   if (b->C <= 0 || b->H <= 0) return fail(E2A_ERR_INVALID_ARG, "C and H must be positive");
   if (b->dtype != E2A_DTYPE_F32 && b->dtype != E2A_DTYPE_BF16) return fail(E2A_ERR_INVALID_ARG, "dtype=%d", b->dtype);
+  if (b->C % 4 != 0) return fail(E2A_ERR_UNSUPPORTED, "block: C=%d is not a multiple of 4", b->C);
+  if (b->n_atoms * (2 * b->L + 1) >= (int64_t)INT32_MAX)
+    return fail(E2A_ERR_UNSUPPORTED, "block: n_atoms * (2L+1) must stay below 2^31");
   if (b->n_atoms > 0) {
     const void* ptrs[] = {b->h_in, b->h_out, b->norm1, b->w_o, b->norm2, b->w_1, b->w_2};
     const char* names[] = {"h_in", "h_out", "norm1", "w_o", "norm2", "w_1", "w_2"};
@@ -468,6 +505,7 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
     qk.a = a;
     qk.q = reinterpret_cast<float*>(base + ws.b.q);
     qk.k = reinterpret_cast<float*>(base + ws.b.k);
+    qk.wqk_t = reinterpret_cast<uint16_t*>(base + ws.b.wqk_bf);
     st = launch_qk(qk, s);
   }
   if (st != E2A_OK) return st;

@@ -73,6 +73,7 @@ struct AttnPlan {
   const e2a_attn_args* a;
   float* q;           // workspace f32 [N, C]
   float* k;           // workspace f32 [N, C]
+  uint16_t* wqk_t;    // workspace bf16 [2][C][C]: W_q^T, W_k^T for the matrix-core q/k (bf16 storage)
   void* mfma_ws;      // workspace of the MFMA path (packed weights, atom order)
   float box[3];
   int periodic;
@@ -83,6 +84,12 @@ e2a_status launch_attention_reference(const AttnPlan& p, hipStream_t s);
 bool mfma_supported(int L, int C, int H, int dtype);
 size_t mfma_workspace_bytes(int64_t n, int L, int C, bool backward);
 e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
+// The MFMA build's packed SO(2) image (bytes, and the packing), and the
+// spatial destination order it uses unless the caller gives one.
+size_t mfma_packed_bytes(int L);
+e2a_status pack_so2_mfma(const void* w_so2, void* out, int L, hipStream_t s);
+size_t order_workspace_bytes(int64_t n);
+e2a_status destination_order(const float* pos, int64_t n, int32_t* order, void* ws, hipStream_t s);
 // Feature gradient (attention_backward.hip).
 struct BwdPlan {
   const e2a_attn_args* a;
@@ -122,6 +129,10 @@ struct BlockPlan {
   e2a_status (*attention)(const e2a_attn_args* a, hipStream_t s);   // the checked forward
 };
 e2a_status launch_block(const BlockPlan& p, hipStream_t s);
+// q = h0 W_q, k = h0 W_k on the matrix cores (bf16 storage, C a multiple of 32):
+// bf16 products are exact, sums fp32.
+e2a_status launch_qk_mfma(const uint16_t* feat, const uint16_t* wq, const uint16_t* wk, uint16_t* wqk_t, int64_t n,
+                          int K, int C, float* q, float* k, hipStream_t s);
 
 // Weight gradients (attention_wgrad.hip), after ds and dq, dk are formed.
 struct WgradPlan {

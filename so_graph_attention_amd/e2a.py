@@ -30,7 +30,8 @@ EXPORTED = ["e2a_version", "e2a_status_string", "e2a_last_error_message", "e2a_n
             "e2a_build_neighbors", "e2a_so2_param_count", "e2a_attention_workspace_bytes", "e2a_attention_fwd",
             "e2a_conv_fwd", "e2a_attention_bwd_workspace_bytes", "e2a_attention_bwd",
             "e2a_attention_bwd_weights_workspace_bytes", "e2a_attention_bwd_weights", "e2a_attention_fwd_noalloc",
-            "e2a_block_workspace_bytes", "e2a_block_fwd"]
+            "e2a_block_workspace_bytes", "e2a_block_fwd", "e2a_so2_packed_bytes", "e2a_pack_so2_weights",
+            "e2a_destination_order_workspace_bytes", "e2a_destination_order"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
@@ -49,6 +50,7 @@ class AttnArgs(ctypes.Structure):
         ("feat", ctypes.c_void_p), ("w_q", ctypes.c_void_p), ("w_k", ctypes.c_void_p),
         ("w_rad", ctypes.c_void_p), ("w_so2", ctypes.c_void_p), ("out", ctypes.c_void_p),
         ("out_lse", ctypes.c_void_p), ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("w_so2_packed", ctypes.c_void_p), ("order", ctypes.c_void_p),
     ]
 
 
@@ -63,6 +65,7 @@ class BlockArgs(ctypes.Structure):
         ("w_so2", ctypes.c_void_p), ("w_o", ctypes.c_void_p), ("norm2", ctypes.c_void_p), ("w_1", ctypes.c_void_p),
         ("w_gate", ctypes.c_void_p), ("w_2", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("w_so2_packed", ctypes.c_void_p), ("order", ctypes.c_void_p),
     ]
 
 
@@ -93,6 +96,16 @@ def _load():
     lib.e2a_attention_fwd.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
     lib.e2a_attention_fwd_noalloc.restype = ctypes.c_int32
     lib.e2a_attention_fwd_noalloc.argtypes = [ctypes.POINTER(AttnArgs), ctypes.c_void_p]
+    lib.e2a_so2_packed_bytes.restype = ctypes.c_size_t
+    lib.e2a_so2_packed_bytes.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.e2a_pack_so2_weights.restype = ctypes.c_int32
+    lib.e2a_pack_so2_weights.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_void_p]
+    lib.e2a_destination_order_workspace_bytes.restype = ctypes.c_size_t
+    lib.e2a_destination_order_workspace_bytes.argtypes = [ctypes.c_int64]
+    lib.e2a_destination_order.restype = ctypes.c_int32
+    lib.e2a_destination_order.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]
     lib.e2a_block_workspace_bytes.restype = ctypes.c_size_t
     lib.e2a_block_workspace_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                               ctypes.c_int]
@@ -207,7 +220,7 @@ def _storage_dtype(feat: torch.Tensor) -> int:
 
 
 def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box, variant,
-               workspace, need_qk=True):
+               workspace, need_qk=True, w_so2_packed=None, order=None):
     """Checks the layer's inputs (device, dtype, shape) and fills the argument
     struct.  Returns (args, box array that must stay alive for the call)."""
     dev = _gpu_device(pos)
@@ -233,6 +246,10 @@ def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L,
         _need(out_lse, "out_lse", torch.float32, dev, shape=(n, H))
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, dev)
+    if w_so2_packed is not None:
+        _need(w_so2_packed, "w_so2_packed", torch.uint8, dev, numel=e2a_so2_packed_bytes(L, C, dtype))
+    if order is not None:
+        _need(order, "order", torch.int32, dev, shape=(n,))
     box_arr, box_p = _box_arg(box)
     a = AttnArgs()
     a.pos = _ptr(pos)
@@ -248,6 +265,8 @@ def _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L,
     a.out_lse = _ptr(out_lse)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel()
+    a.w_so2_packed = _ptr(w_so2_packed)
+    a.order = _ptr(order)
     return a, box_arr
 
 
@@ -276,7 +295,7 @@ def e2a_build_neighbors(pos: torch.Tensor, cutoff: float, box=None, batch: Optio
 
 
 def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box, variant, out, out_lse,
-           workspace, stream, need_qk):
+           workspace, stream, need_qk, w_so2_packed=None, order=None):
     dev = _gpu_device(pos)
     n = pos.shape[0]
     if out is None:
@@ -285,7 +304,7 @@ def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff,
         workspace = torch.empty(max(1, e2a_attention_workspace_bytes(n, L, C, H, _storage_dtype(feat))),
                                 dtype=torch.uint8, device=dev)
     a, box_arr = _fill_args(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, out, out_lse, L, C, H, cutoff, box,
-                            variant, workspace, need_qk=need_qk)
+                            variant, workspace, need_qk=need_qk, w_so2_packed=w_so2_packed, order=order)
     _check(fn(ctypes.byref(a), _stream(stream)))
     del box_arr
     return out
@@ -293,14 +312,14 @@ def _layer(fn, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff,
 
 def e2a_attention_fwd(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *, L: int, C: int, H: int,
                       cutoff: float, box=None, variant: str = "auto", out=None, out_lse=None,
-                      workspace=None, stream=None, with_lse: bool = False):
+                      workspace=None, stream=None, with_lse: bool = False, w_so2_packed=None, order=None):
     """Run the fused layer; returns out [N,(L+1)^2,C] fp32 (and lse [N,H] if requested).
 
     Storage dtype follows ``feat`` (float32 or bfloat16); all weights must match it."""
     if with_lse and out_lse is None:
         out_lse = torch.empty((pos.shape[0], H), dtype=torch.float32, device=pos.device)
     out = _layer(_lib.e2a_attention_fwd, pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, L, C, H, cutoff, box,
-                 variant, out, out_lse, workspace, stream, True)
+                 variant, out, out_lse, workspace, stream, True, w_so2_packed, order)
     return (out, out_lse) if with_lse else out
 
 
@@ -324,12 +343,12 @@ def e2a_attention_fwd_noalloc(pos, row_ptr, col, feat, w_q, w_k, w_rad, w_so2, *
 
 
 def e2a_conv_fwd(pos, row_ptr, col, feat, w_rad, w_so2, *, L: int, C: int, H: int = 8, cutoff: float, box=None,
-                 variant: str = "auto", out=None, workspace=None, stream=None):
+                 variant: str = "auto", out=None, workspace=None, stream=None, w_so2_packed=None, order=None):
     """Sum of the same per-edge messages without attention weights (the EAAS
     convolution stage); returns out [N,(L+1)^2,C] fp32.  H only selects the
     build (the MFMA kernel is built for H = 8)."""
     return _layer(_lib.e2a_conv_fwd, pos, row_ptr, col, feat, None, None, w_rad, w_so2, L, C, H, cutoff, box,
-                  variant, out, None, workspace, stream, False)
+                  variant, out, None, workspace, stream, False, w_so2_packed, order)
 
 
 def e2a_attention_bwd_workspace_bytes(n_atoms: int, n_edges: int, L: int, C: int, H: int) -> int:
@@ -410,7 +429,7 @@ def e2a_block_workspace_bytes(n_atoms: int, L: int, C: int, H: int, dtype: int) 
 
 
 def e2a_block_fwd(pos, row_ptr, col, h, weights: dict, *, L: int, C: int, H: int, cutoff: float, box=None,
-                  variant: str = "auto", out=None, workspace=None, stream=None):
+                  variant: str = "auto", out=None, workspace=None, stream=None, w_so2_packed=None, order=None):
     """One block around the layer (include/e2a.h, e2a_block_fwd): h fp32
     [N,(L+1)^2,C] in, the block's output out.  ``weights`` maps the names in
     BLOCK_WEIGHTS to tensors in the storage dtype (w_gate may be absent for
@@ -452,6 +471,49 @@ def e2a_block_fwd(pos, row_ptr, col, h, weights: dict, *, L: int, C: int, H: int
     for name in BLOCK_WEIGHTS:
         setattr(a, name, _ptr(weights.get(name)))
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    if w_so2_packed is not None:
+        _need(w_so2_packed, "w_so2_packed", torch.uint8, dev, numel=e2a_so2_packed_bytes(L, C, dtype))
+    if order is not None:
+        _need(order, "order", torch.int32, dev, shape=(n,))
+    a.w_so2_packed, a.order = _ptr(w_so2_packed), _ptr(order)
     _check(_lib.e2a_block_fwd(ctypes.byref(a), _stream(stream)))
     del box_arr
     return out
+
+
+def e2a_so2_packed_bytes(L: int, C: int, dtype: int) -> int:
+    return int(_lib.e2a_so2_packed_bytes(L, C, dtype))
+
+
+def e2a_pack_so2_weights(w_so2, *, L: int, C: int, out=None, stream=None):
+    """The matrix-core image of w_so2 (bf16), as a uint8 tensor on its device,
+    for the forward's w_so2_packed argument."""
+    dev = _gpu_device(w_so2)
+    dtype = _storage_dtype(w_so2)
+    _need(w_so2, "w_so2", w_so2.dtype, dev, numel=e2a_so2_param_count(L, C))
+    nb = e2a_so2_packed_bytes(L, C, dtype)
+    if out is None:
+        out = torch.empty(max(1, nb), dtype=torch.uint8, device=dev)
+    _need(out, "out", torch.uint8, dev)
+    _check(_lib.e2a_pack_so2_weights(_ptr(w_so2), _ptr(out), L, C, dtype, _stream(stream)))
+    return out
+
+
+def e2a_destination_order_workspace_bytes(n_atoms: int) -> int:
+    return int(_lib.e2a_destination_order_workspace_bytes(n_atoms))
+
+
+def e2a_destination_order(pos, *, order=None, workspace=None, stream=None):
+    """The layer's default spatial order of the destinations (int32 [N])."""
+    dev = _gpu_device(pos)
+    n = pos.shape[0]
+    _need(pos, "pos", torch.float32, dev, shape=(n, 3))
+    if order is None:
+        order = torch.empty(n, dtype=torch.int32, device=dev)
+    _need(order, "order", torch.int32, dev, shape=(n,))
+    if workspace is None:
+        workspace = torch.empty(max(1, e2a_destination_order_workspace_bytes(n)), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev)
+    _check(_lib.e2a_destination_order(_ptr(pos), n, _ptr(order), _ptr(workspace), workspace.numel(),
+                                      _stream(stream)))
+    return order

@@ -2,6 +2,8 @@
 
   python -m so_graph_attention_amd.profiling attention [--config large] [--iters 2]
       the fused layer on one workload, `iters` launches after one warm-up;
+  python -m so_graph_attention_amd.profiling block [--config large] [--iters 2]
+      one block around the layer (e2a_block_fwd) on one workload;
   python -m so_graph_attention_amd.profiling copy [--mib 1024] [--iters 2]
       a plain device-to-device copy of known size, whose FETCH_SIZE /
       WRITE_SIZE readings calibrate the byte counters of the layer's run.
@@ -47,6 +49,33 @@ def run_attention(config: str, iters: int, variant: str):
     print(f"attention {config}: {w.n_atoms} atoms, {col.numel()} edges, {iters + 1} launches", flush=True)
 
 
+def run_block(config: str, iters: int):
+    import torch
+
+    import so_graph_attention_amd.e2a as B
+    from workloads import make_block_weights, make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(config)
+
+    def stored(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+    pos = torch.from_numpy(w.pos).to(dev)
+    box = None if w.box is None else w.box.tolist()
+    batch = None if w.batch is None else torch.from_numpy(w.batch.astype(np.int32)).to(dev)
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch)
+    bw = {k: stored(v) for k, v in make_block_weights(w).items()}
+    h = torch.from_numpy(np.ascontiguousarray(w.as_f32("feat"))).to(dev)
+    out = torch.empty_like(h)
+    for _ in range(iters + 1):
+        B.e2a_block_fwd(pos, rp, col, h, bw, L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box, out=out)
+    torch.cuda.synchronize()
+    print(f"block {config}: {w.n_atoms} atoms, {col.numel()} edges, {iters + 1} calls", flush=True)
+
+
 def run_copy(mib: int, iters: int):
     import torch
 
@@ -66,12 +95,17 @@ def main():
     a.add_argument("--config", default="large")
     a.add_argument("--iters", type=int, default=2)
     a.add_argument("--variant", default="auto")
+    b = sub.add_parser("block")
+    b.add_argument("--config", default="large")
+    b.add_argument("--iters", type=int, default=2)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--iters", type=int, default=2)
     args = ap.parse_args()
     if args.what == "attention":
         run_attention(args.config, args.iters, args.variant)
+    elif args.what == "block":
+        run_block(args.config, args.iters)
     else:
         run_copy(args.mib, args.iters)
 

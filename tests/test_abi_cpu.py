@@ -34,7 +34,7 @@ def test_header_declarations_are_exported():
 
 
 def test_version_and_status_strings():
-    assert B.e2a_version() == 1
+    assert B.e2a_version() == 2
     assert B.status_string(0) == "E2A_OK"
     assert B.status_string(2) == "E2A_ERR_CAPACITY"
     assert B.status_string(99) == "E2A_ERR_UNKNOWN"
@@ -476,3 +476,20 @@ def test_block_gate_optional_at_l0_and_workspace_query():
     got = B.e2a_block_workspace_bytes(n, L, C, 8, B.E2A_DTYPE_BF16)
     assert got >= B.e2a_attention_workspace_bytes(n, L, C, 8, 1) + n * 16 * C * (2 + 4 + 4 + 2)
     assert B.e2a_block_workspace_bytes(n, 5, C, 8, 1) == 0
+
+
+def test_packer_and_order_queries():
+    """The packed image holds the SO(2) weights once (no padding), only where a
+    matrix-core build exists; the packer refuses other shapes on the host."""
+    assert B.e2a_so2_packed_bytes(4, 128, B.E2A_DTYPE_BF16) == 2 * B.e2a_so2_param_count(4, 128)
+    assert B.e2a_so2_packed_bytes(3, 128, B.E2A_DTYPE_BF16) == 2 * B.e2a_so2_param_count(3, 128)
+    assert B.e2a_so2_packed_bytes(4, 128, B.E2A_DTYPE_F32) == 0
+    assert B.e2a_so2_packed_bytes(1, 16, B.E2A_DTYPE_BF16) == 0
+    assert B.e2a_so2_packed_bytes(0, 128, B.E2A_DTYPE_BF16) == 0
+    assert B.lib().e2a_pack_so2_weights(FAKE, FAKE, 1, 16, 1, None) == B.E2A_ERR_UNSUPPORTED
+    assert B.lib().e2a_pack_so2_weights(None, FAKE, 4, 128, 1, None) == B.E2A_ERR_INVALID_ARG
+    assert B.lib().e2a_pack_so2_weights(FAKE, FAKE, 7, 128, 1, None) == B.E2A_ERR_INVALID_ARG
+    assert B.e2a_destination_order_workspace_bytes(100000) > 100000 * 12
+    assert B.lib().e2a_destination_order(FAKE, 10, FAKE, None, 0, None) == B.E2A_ERR_INVALID_ARG
+    assert B.lib().e2a_destination_order(None, 10, FAKE, FAKE, 1 << 30, None) == B.E2A_ERR_INVALID_ARG
+    assert B.lib().e2a_destination_order(None, 0, None, None, 0, None) == B.E2A_OK
