@@ -21,6 +21,10 @@
  *     library never frees them and keeps none of them after the call returns.
  *     The library allocates no device memory: scratch comes in through a
  *     caller-owned workspace whose size a *_workspace_bytes() query gives.
+ *     The kernels read arrays in 16-byte vectors: every device array of the
+ *     layer's argument struct, and the cotangent of the backward calls, must
+ *     start on a 16-byte boundary (hipMalloc and PyTorch's allocator give
+ *     256); a misaligned one is refused with E2A_ERR_INVALID_ARG.
  *   - "stream" is a hipStream_t passed as void* (NULL = the default stream).
  *     All device work is enqueued on it, in order.
  *   - Every function that can fail returns an e2a_status.  Argument checks run

@@ -293,9 +293,9 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
 // thread per (degree, channel) and range of edges (consecutive threads take
 // consecutive channels, so the row reads coalesce); each edge's 2l + 1 rows
 // are loaded together.
-template <int L, int l>
+template <int L, int l, typename YT>
 __device__ __forceinline__ void rho_degree(const BatchLayout& bl, int64_t nb, int C, int64_t per, int z, int c,
-                                           const float* __restrict__ rbf, const float* __restrict__ Y,
+                                           const float* __restrict__ rbf, const YT* __restrict__ Y,
                                            const float* __restrict__ dyhat, float* __restrict__ part,
                                            bool acc_parts) {
   constexpr int w = 2 * l + 1;
@@ -310,7 +310,7 @@ __device__ __forceinline__ void rho_degree(const BatchLayout& bl, int64_t nb, in
     for (int q = 0; q < w; ++q) {
       const int64_t idx = batch_index(bl, L, C, b, l, q - l, c);
       g[q] = dyhat[idx];
-      y[q] = Y[idx];
+      y[q] = load_as_f32(Y, (size_t)idx);
     }
     float dr = 0.0f;
 #pragma unroll
@@ -327,27 +327,27 @@ __device__ __forceinline__ void rho_degree(const BatchLayout& bl, int64_t nb, in
 
 // The thread's degree ld as a compile-time constant (uniform over a wave when
 // C is a multiple of 64).
-template <int L, int l>
+template <int L, int l, typename YT>
 __device__ __forceinline__ void rho_dispatch(int ld, const BatchLayout& bl, int64_t nb, int C, int64_t per, int z,
-                                             int c, const float* __restrict__ rbf, const float* __restrict__ Y,
+                                             int c, const float* __restrict__ rbf, const YT* __restrict__ Y,
                                              const float* __restrict__ dyhat, float* __restrict__ part,
                                              bool acc_parts) {
   if (ld == l) {
-    rho_degree<L, l>(bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
+    rho_degree<L, l, YT>(bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
     return;
   }
-  if constexpr (l < L) rho_dispatch<L, l + 1>(ld, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
+  if constexpr (l < L) rho_dispatch<L, l + 1, YT>(ld, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
 }
 
-template <int L>
+template <int L, typename YT>
 __global__ void k_wg_rho(BatchLayout bl, int64_t nb, int C, int64_t per, const float* __restrict__ rbf,
-                         const float* __restrict__ Y, const float* __restrict__ dyhat, float* __restrict__ part,
+                         const YT* __restrict__ Y, const float* __restrict__ dyhat, float* __restrict__ part,
                          bool acc_parts) {
   const int lc = blockIdx.x * blockDim.x + threadIdx.x;
   const int z = blockIdx.y;
   if (lc >= (L + 1) * C) return;
   const int l = lc / C, c = lc - l * C;
-  rho_dispatch<L, 0>(l, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
+  rho_dispatch<L, 0, YT>(l, bl, nb, C, per, z, c, rbf, Y, dyhat, part, acc_parts);
 }
 
 // ------------------------------------------------------------ positions ----
@@ -369,8 +369,8 @@ struct ForceParams {
   const float* grad;    // G [N, K, C]
   const float* alpha;   // [B][H]
   const float* rbf;     // [B][8]
-  const float* Y;       // batch tensor: y = SO2(x), fp32
-  const float* dX;      // batch tensor: dx = SO2^T(dy), fp32
+  const void* Y;        // batch tensor: y = SO2(x) (fp32, or bf16 for the matrix-core kernel)
+  const void* dX;       // batch tensor: dx = SO2^T(dy) (the same type)
   const float* rbfd;    // [B][8]: d e_k / d r
   float* gedge;         // [E][3]: dL/dr of every edge
   float box[3];
@@ -409,8 +409,8 @@ __device__ __forceinline__ void force_degree(const ForceParams& p, const T* __re
 #pragma unroll
     for (int q = 0; q < w; ++q) {
       const int64_t idx = batch_index(p.bl, L, C, b, l, q - l, c);
-      dx[q] = p.dX[idx];
-      yv[q] = p.Y[idx];
+      dx[q] = static_cast<const float*>(p.dX)[idx];
+      yv[q] = static_cast<const float*>(p.Y)[idx];
       hv[q] = load_as_f32(feat, (size_t)(((int64_t)j * K + l * l + q) * C + c));
       ag[q] = a * p.grad[((int64_t)i * K + l * l + q) * C + c];
     }
@@ -473,6 +473,55 @@ __device__ __forceinline__ void force_wigner(float (*D)[wig_size(L)], bool live,
   if constexpr (l < L) force_wigner<L, l + 1>(D, live, lane);
 }
 
+// Edge e's ends (i, j), its direction and length (fr = r_hat, |r|), and
+// D^0, D^1 with the three tangents dD^1/dw_a (components 1 .. 3 of D).
+template <int L>
+__device__ __forceinline__ void force_edge_setup(const ForceParams& p, int64_t e, float (*D)[wig_size(L)], float* fr,
+                                                 int* ij) {
+  const int i = p.src[e], j = p.col[e];
+  ij[0] = i;
+  ij[1] = j;
+  float r3[3];
+  for (int d = 0; d < 3; ++d) {
+    float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * (int64_t)i + d];
+    if (p.periodic) {
+      if (dx > 0.5f * p.box[d]) dx -= p.box[d];
+      else if (dx < -0.5f * p.box[d]) dx += p.box[d];
+    }
+    r3[d] = dx;
+  }
+  float u[3];
+  const float r = edge_unit(r3, u);
+  fr[0] = u[0];
+  fr[1] = u[1];
+  fr[2] = u[2];
+  fr[3] = r;
+  float R[3][3];
+  edge_rotation(u, R);
+  D[0][0] = 1.0f;
+  D[1][0] = D[2][0] = D[3][0] = 0.0f;
+  if constexpr (L >= 1) {
+    wigner_l1(R, &D[0][wig_off(1)], 3);
+    for (int a = 0; a < 3; ++a) {
+      float dR[3][3];
+      frame_tangent(R, a, dR);
+      wigner_l1(dR, &D[1 + a][wig_off(1)], 3);
+    }
+  }
+}
+
+// dL/dr of the edge from T_a and s (lane 0): (T x u) / |r| + s u; an edge
+// of zero length has no direction to move along and contributes nothing.
+__device__ __forceinline__ void force_write(const ForceParams& p, int64_t e, const float* u, const float (&T3)[3],
+                                            float sv) {
+  const bool has_len = u[3] > 0.0f;
+  const float ir = has_len ? 1.0f / u[3] : 0.0f;
+  const float s = has_len ? sv : 0.0f;
+  p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + s * u[0];
+  p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + s * u[1];
+  p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
+}
+
 // One edge per wave, four per workgroup.  Lane 0 sets up the frame, D^1 and
 // its tangents; the degrees 2 .. L follow one row per lane; then the
 // products, summed over the channels within the wave.
@@ -489,38 +538,7 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
   const bool live = b < nb;                  // every wave still takes part in the barriers
   const int64_t e = p.e0 + b;
   float (*D)[WS] = Ds[wv];
-  if (lane == 0 && live) {
-    const int i = p.src[e], j = p.col[e];
-    ijs[wv][0] = i;
-    ijs[wv][1] = j;
-    float r3[3];
-    for (int d = 0; d < 3; ++d) {
-      float dx = p.pos[3 * (int64_t)j + d] - p.pos[3 * (int64_t)i + d];
-      if (p.periodic) {
-        if (dx > 0.5f * p.box[d]) dx -= p.box[d];
-        else if (dx < -0.5f * p.box[d]) dx += p.box[d];
-      }
-      r3[d] = dx;
-    }
-    float u[3];
-    const float r = edge_unit(r3, u);
-    fr[wv][0] = u[0];
-    fr[wv][1] = u[1];
-    fr[wv][2] = u[2];
-    fr[wv][3] = r;
-    float R[3][3];
-    edge_rotation(u, R);
-    D[0][0] = 1.0f;
-    D[1][0] = D[2][0] = D[3][0] = 0.0f;
-    if constexpr (L >= 1) {
-      wigner_l1(R, &D[0][wig_off(1)], 3);
-      for (int a = 0; a < 3; ++a) {
-        float dR[3][3];
-        frame_tangent(R, a, dR);
-        wigner_l1(dR, &D[1 + a][wig_off(1)], 3);
-      }
-    }
-  }
+  if (lane == 0 && live) force_edge_setup<L>(p, e, D, fr[wv], ijs[wv]);
   __syncthreads();
   if constexpr (L >= 2) force_wigner<L, 2>(D, live, lane);
   if (!live) return;
@@ -531,17 +549,150 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
   for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
   for (int a = 0; a < 3; ++a)
     for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
-  if (lane == 0) {
-    const float* u = fr[wv];
-    // (T x u) / |r| + s u; an edge of zero length has no direction to move
-    // along and contributes nothing
-    const bool has_len = u[3] > 0.0f;
-    const float ir = has_len ? 1.0f / u[3] : 0.0f;
-    const float s = has_len ? sv : 0.0f;
-    p.gedge[e * 3 + 0] = (T3[1] * u[2] - T3[2] * u[1]) * ir + s * u[0];
-    p.gedge[e * 3 + 1] = (T3[2] * u[0] - T3[0] * u[2]) * ir + s * u[1];
-    p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
+  if (lane == 0) force_write(p, e, fr[wv], T3, sv);
+}
+
+// The same T_a and s on the matrix cores (bf16 storage, C a multiple of 32),
+// with the sums over channels taken first:
+//   P^l[m][n] = sum_c dx[l,m][c] h_j[l,n][c] + rho[l][c] alpha[c] y[l,m][c] G_i[l,n][c],
+//   M^l[m][n] = sum_c (d rho / d r)[l][c] alpha[c] y[l,m][c] G_i[l,n][c],
+//   T_a = sum_l <P^l, dD^l/dw_a>,   s = sum_l <M^l, D^l>.
+// All K x K row pairs of an edge form one product: rows (l, m) -> l^2 + l + m
+// on both sides, v_mfma_f32_32x32x16_bf16 over 16 channels a step, each lane
+// reading its own fragment (row lane % 32, channels 16 t + 8 (lane / 32) ..
+// + 7) from global memory; only pairs within one degree are used.  The
+// factors rho alpha and (d rho / d r) alpha of every (l, c) are formed per
+// edge in LDS from the radial weights, which the workgroup stages once for
+// its 32 edges.  y and dx arrive in bf16; rho alpha y and G_i are rounded to
+// bf16 for the products, whose sums are fp32.
+constexpr int kFmWaves = 4, kFmIters = 8;   // 32 edges per workgroup, one per wave at a time
+template <int L>
+__global__ void __launch_bounds__(64 * kFmWaves) k_wg_force_mfma(ForceParams p, int64_t nb,
+                                                                 const uint16_t* __restrict__ feat,
+                                                                 const uint16_t* __restrict__ w_rad) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  typedef float f32x8v __attribute__((ext_vector_type(8)));
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  constexpr int K = (L + 1) * (L + 1);
+  constexpr int WS = wig_size(L);
+  static_assert(K <= 32, "the rows (l, m) of an edge fit one 32-row tile");
+  extern __shared__ __attribute__((aligned(16))) float fsm[];
+  __shared__ float Ds[kFmWaves][4][WS];   // D and its three tangents, per wave
+  __shared__ float frs[kFmWaves][4];
+  __shared__ int ijs[kFmWaves][2];
+  const int C = p.C, H = p.H, dh = C / H;
+  const int LC = (L + 1) * C;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  float* wr = fsm;                         // [8][L + 1][C] radial weights
+  float* tab = fsm + 8 * LC + wv * 2 * LC; // [2][L + 1][C]: rho alpha, (d rho / d r) alpha
+  for (int t = tid; t < 8 * LC; t += blockDim.x) wr[t] = bf16_to_f32(w_rad[t]);
+  float (*D)[WS] = Ds[wv];
+  // the lane's operand row (l, m) and output column
+  const int row = lane & 31, hk = lane >> 5;
+  const bool rv = row < K;
+  int lr = 0;
+  while ((lr + 1) * (lr + 1) <= row && lr < L) ++lr;
+  const int mr = row - lr * lr - lr;
+  int lc = 0;
+  while ((lc + 1) * (lc + 1) <= row && lc < L) ++lc;   // the column's degree (column = row index)
+  const uint16_t* dXb = static_cast<const uint16_t*>(p.dX);
+  const uint16_t* Yb = static_cast<const uint16_t*>(p.Y);
+  for (int it = 0; it < kFmIters; ++it) {
+    const int64_t b = ((int64_t)blockIdx.x * kFmIters + it) * kFmWaves + wv;
+    const bool live = b < nb;
+    const int64_t e = p.e0 + b;
+    if (lane == 0 && live) force_edge_setup<L>(p, e, D, frs[wv], ijs[wv]);
+    __syncthreads();   // the first pass also orders the radial weights' fill
+    if constexpr (L >= 2) force_wigner<L, 2>(D, live, lane);
+    if (live) {
+      float rb[8], rd[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        rb[k] = p.rbf[b * 8 + k];
+        rd[k] = p.rbfd[b * 8 + k];
+      }
+      for (int t = lane; t < LC; t += 64) {
+        float r = 0.0f, d = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          r += rb[k] * wr[k * LC + t];
+          d += rd[k] * wr[k * LC + t];
+        }
+        const float a = p.alpha[b * H + (t % C) / dh];
+        tab[t] = r * a;
+        tab[LC + t] = d * a;
+      }
+    }
+    __syncthreads();
+    if (!live) continue;
+    const int i = ijs[wv][0], j = ijs[wv][1];
+    const int64_t bi = rv ? batch_index(p.bl, L, C, b, lr, mr, 0) : 0;
+    const uint16_t* dxr = dXb + bi;
+    const uint16_t* yr = Yb + bi;
+    const uint16_t* hr = feat + ((int64_t)j * K + row) * C;
+    const float* gr = p.grad + ((int64_t)i * K + row) * C;
+    const float* ra = tab + lr * C;
+    f32x16 accT = {}, accS = {};
+    for (int c0 = 8 * hk; c0 < C; c0 += 16) {
+      bf16x8 adx = {}, bh = {}, a1 = {}, a2 = {}, bg = {};
+      if (rv) {
+        adx = *reinterpret_cast<const bf16x8*>(dxr + c0);
+        bh = *reinterpret_cast<const bf16x8*>(hr + c0);
+        const u32x4v yw = *reinterpret_cast<const u32x4v*>(yr + c0);
+        const f32x4v g0 = *reinterpret_cast<const f32x4v*>(gr + c0);
+        const f32x4v g1 = *reinterpret_cast<const f32x4v*>(gr + c0 + 4);
+        const f32x4v r0 = *reinterpret_cast<const f32x4v*>(ra + c0);
+        const f32x4v r1 = *reinterpret_cast<const f32x4v*>(ra + c0 + 4);
+        const f32x4v d0 = *reinterpret_cast<const f32x4v*>(ra + LC + c0);
+        const f32x4v d1 = *reinterpret_cast<const f32x4v*>(ra + LC + c0 + 4);
+        f32x8v yv, gv, rv8, dv8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          yv[2 * q] = __uint_as_float(yw[q] << 16);
+          yv[2 * q + 1] = __uint_as_float(yw[q] & 0xffff0000u);
+          gv[q] = g0[q];
+          gv[4 + q] = g1[q];
+          rv8[q] = r0[q];
+          rv8[4 + q] = r1[q];
+          dv8[q] = d0[q];
+          dv8[4 + q] = d1[q];
+        }
+        a1 = __builtin_convertvector(yv * rv8, bf16x8);
+        a2 = __builtin_convertvector(yv * dv8, bf16x8);
+        bg = __builtin_convertvector(gv, bf16x8);
+      }
+      accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adx, bh, accT, 0, 0, 0);
+      accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, accT, 0, 0, 0);
+      accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bg, accS, 0, 0, 0);
+    }
+    // register r holds (row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32)
+    float T3[3] = {0.0f, 0.0f, 0.0f};
+    float sv = 0.0f;
+    if (row < K) {
+      const int wn = 2 * lc + 1, n = row - lc * lc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ir = 8 * (r >> 2) + 4 * hk + (r & 3);
+        if (ir >= lc * lc && ir < (lc + 1) * (lc + 1)) {
+          const int off = wig_off(lc) + (ir - lc * lc) * wn + n;
+          T3[0] += accT[r] * D[1][off];
+          T3[1] += accT[r] * D[2][off];
+          T3[2] += accT[r] * D[3][off];
+          sv += accS[r] * D[0][off];
+        }
+      }
+    }
+    for (int o = 32; o > 0; o >>= 1) sv += __shfl_xor(sv, o);
+    for (int a = 0; a < 3; ++a)
+      for (int o = 32; o > 0; o >>= 1) T3[a] += __shfl_xor(T3[a], o);
+    if (lane == 0) force_write(p, e, frs[wv], T3, sv);
   }
+}
+
+size_t force_mfma_smem(int L, int C) { return sizeof(float) * (size_t)(8 + 2 * kFmWaves) * (L + 1) * C; }
+// Dynamic and static LDS within the 64 KB a launch gets without a raised limit.
+bool force_mfma_fits(int L, int C) {
+  return force_mfma_smem(L, C) + sizeof(float) * kFmWaves * 4 * (size_t)wig_size(L) + 256 <= 65536;
 }
 
 // dL/dx_a = sum over edges (i, a) of dL/dr minus sum over edges (a, j): the
@@ -588,6 +739,7 @@ struct Gemm {
   float alpha;
   float* C;
   int64_t ldc;
+  uint16_t* Cb;    // if set: the output is written here as bf16 (C = alpha AB, C unused)
   float* part;     // [S][M][N] when S > 1
   const void* A2;  // if set: second segment (the matrix-core kernel only)
   const void* B2;
@@ -794,6 +946,8 @@ __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
           if (g.S > 1) {
             float* pp = g.part + ((int64_t)bz * g.M + m) * g.N + n;
             *pp = g.part_acc ? *pp + g.alpha * v : g.alpha * v;
+          } else if (g.Cb) {
+            g.Cb[m * g.ldc + n] = f32_to_bf16_rne(g.alpha * v);
           } else if (g.overwrite) {
             g.C[m * g.ldc + n] = g.alpha * v;
           } else {
@@ -893,7 +1047,8 @@ __global__ void k_gemm_reduce(Gemm g) {
   float s = 0.0f;
   for (int z = 0; z < g.S; ++z) s += g.part[z * g.M * g.N + t];
   const int64_t m = t / g.N, n = t - m * g.N;
-  if (g.overwrite) g.C[m * g.ldc + n] = s;
+  if (g.Cb) g.Cb[m * g.ldc + n] = f32_to_bf16_rne(s);
+  else if (g.overwrite) g.C[m * g.ldc + n] = s;
   else g.C[m * g.ldc + n] += s;
 }
 
@@ -1096,6 +1251,19 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
   T* X = reinterpret_cast<T*>(wb + W.X);
   T* GT = reinterpret_cast<T*>(wb + W.GT);
   float* Y = reinterpret_cast<float*>(wb + W.Y);
+  // y = SO2(x) and dx = SO2^T(dy) are kept in bf16 where every block takes
+  // the one-launch pair path (bf16 storage, C a multiple of 32) and the
+  // matrix-core force kernel, which reads them as its operands, fits
+  const bool yb = kPairs && C % kBK == 0 && force_mfma_fits(L, C);
+  auto to_out = [&](Gemm g, size_t buf, int64_t off) {
+    if (yb) {
+      g.Cb = reinterpret_cast<uint16_t*>(wb + buf) + off;
+      g.C = nullptr;
+    } else {
+      g.C = reinterpret_cast<float*>(wb + buf) + off;
+    }
+    return g;
+  };
   float* rbf = reinterpret_cast<float*>(wb + W.rbf);
   const BatchLayout bl = batch_layout(W.B, L, C);
   const T* wso2 = static_cast<const T*>(a->w_so2);
@@ -1155,7 +1323,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       const T* W1 = wt + woff[m];   // W1^T (W0^T for m = 0), [n][k]
       e2a_status e;
       if (m == 0) {
-        e = gemm<T, T>(make_gemm(Xp, km, 1, W1, 1, km, nb, km, km, 1.0f, Yp, km, part, true), W.part_floats, st);
+        e = gemm<T, T>(to_out(make_gemm(Xp, km, 1, W1, 1, km, nb, km, km, 1.0f, nullptr, km, part, true), W.Y,
+                              bl.moff[m]),
+                       W.part_floats, st);
         if (e != E2A_OK) return e;
         continue;
       }
@@ -1165,8 +1335,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       if (kPairs && km % kBK == 0) {
         // one launch per output: Yp = [Xp | Xm] [W1; -W2], Ym = [Xp | Xm] [W2; W1]
         for (int t = 0; t < 2; ++t) {
-          Gemm g = make_gemm(Xp, km, 1, t == 0 ? W1 : W2, 1, km, nb, km, 2 * km, 1.0f, t == 0 ? Yp : Ym, km, part,
-                             true);
+          Gemm g = to_out(make_gemm(Xp, km, 1, t == 0 ? W1 : W2, 1, km, nb, km, 2 * km, 1.0f, nullptr, km, part,
+                                    true),
+                          W.Y, bl.moff[m] + (t == 0 ? 0 : bl.B * km));
           pair_segments(g, Xm, t == 0 ? W2 : W1, km, t == 0);
           e = gemm<T, T>(g, W.part_floats, st);
           if (e != E2A_OK) return e;
@@ -1187,8 +1358,12 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       const int64_t per = kRhoPer;
       const int64_t nz = (nb + per - 1) / per;
       const dim3 grid(static_cast<unsigned>((K0 + 255) / 256), static_cast<unsigned>(nz));
-      k_wg_rho<L><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, Y, reinterpret_cast<const float*>(wb + W.dX),
-                                        rhopart, e0 > 0);
+      const float* dyh = reinterpret_cast<const float*>(wb + W.dX);
+      if (yb)
+        k_wg_rho<L, uint16_t><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, reinterpret_cast<const uint16_t*>(wb + W.Y),
+                                                    dyh, rhopart, e0 > 0);
+      else
+        k_wg_rho<L, float><<<grid, 256, 0, st>>>(bl, nb, C, per, rbf, Y, dyh, rhopart, e0 > 0);
       E2A_LAUNCH_CHECK();
     }
     if (pl.w_so2) {
@@ -1243,7 +1418,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         float* dXp = dX + bl.moff[m];
         e2a_status e;
         if (m == 0) {
-          e = gemm<T, T>(make_gemm(DYp, km, 1, W1, 1, km, nb, km, km, 1.0f, dXp, km, part, true), W.part_floats, st);
+          e = gemm<T, T>(to_out(make_gemm(DYp, km, 1, W1, 1, km, nb, km, km, 1.0f, nullptr, km, part, true), W.dX,
+                                bl.moff[m]),
+                         W.part_floats, st);
           if (e != E2A_OK) return e;
           continue;
         }
@@ -1253,8 +1430,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         if (kPairs && km % kBK == 0) {
           // one launch per output: dXp = [dYp | dYm] [W1^T; W2^T], dXm = [dYm | dYp] [W1^T; -W2^T]
           for (int t = 0; t < 2; ++t) {
-            Gemm g = make_gemm(t == 0 ? DYp : DYm, km, 1, W1, 1, km, nb, km, 2 * km, 1.0f, t == 0 ? dXp : dXm, km,
-                               part, true);
+            Gemm g = to_out(make_gemm(t == 0 ? DYp : DYm, km, 1, W1, 1, km, nb, km, 2 * km, 1.0f, nullptr, km, part,
+                                      true),
+                            W.dX, bl.moff[m] + (t == 0 ? 0 : bl.B * km));
             pair_segments(g, t == 0 ? DYm : DYp, W2, km, t == 1);
             e = gemm<T, T>(g, W.part_floats, st);
             if (e != E2A_OK) return e;
@@ -1277,8 +1455,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       fp.grad = pl.grad_out;
       fp.alpha = reinterpret_cast<const float*>(wb + W.alpha);
       fp.rbf = rbf;
-      fp.Y = Y;
-      fp.dX = dX;
+      fp.Y = wb + W.Y;
+      fp.dX = wb + W.dX;
       fp.rbfd = reinterpret_cast<const float*>(wb + W.rbfd);
       fp.gedge = reinterpret_cast<float*>(wb + W.gedge);
       for (int d = 0; d < 3; ++d) fp.box[d] = pl.box[d];
@@ -1287,6 +1465,15 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       fp.H = H;
       fp.e0 = e0;
       fp.bl = bl;
+      if constexpr (kPairs) {
+        if (yb) {
+          constexpr int64_t per = kFmWaves * kFmIters;
+          k_wg_force_mfma<L><<<static_cast<unsigned>((nb + per - 1) / per), 64 * kFmWaves, force_mfma_smem(L, C),
+                               st>>>(fp, nb, feat, static_cast<const uint16_t*>(a->w_rad));
+          E2A_LAUNCH_CHECK();
+          continue;
+        }
+      }
       k_wg_force<L, T><<<static_cast<unsigned>((nb + kForceEdges - 1) / kForceEdges), 64 * kForceEdges, 0, st>>>(
           fp, nb, feat, static_cast<const T*>(a->w_rad));
       E2A_LAUNCH_CHECK();

@@ -84,6 +84,21 @@ WBwdWs wbwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
 
 // Checks shared by the backward calls (all inputs; the outputs are checked
 // by each call).
+// Device arrays are read in 16-byte vectors: every array argument must start
+// on a 16-byte boundary (hipMalloc and PyTorch's allocator give 256).
+bool misaligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) != 0; }
+
+e2a_status check_alignment(const e2a_attn_args* a, const void* grad_out) {
+  const void* ptrs[] = {a->pos,     a->row_ptr, a->col, a->feat,         a->w_q,    a->w_k,
+                        a->w_rad,   a->w_so2,   a->out, a->out_lse,      a->workspace,
+                        a->w_so2_packed, a->order, grad_out};
+  const char* names[] = {"pos",   "row_ptr", "col", "feat",         "w_q",   "w_k",      "w_rad",
+                         "w_so2", "out",     "out_lse", "workspace", "w_so2_packed", "order", "grad_out"};
+  for (size_t t = 0; t < sizeof(ptrs) / sizeof(ptrs[0]); ++t)
+    if (misaligned(ptrs[t])) return fail(E2A_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[t]);
+  return E2A_OK;
+}
+
 e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
   if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
   if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
@@ -107,6 +122,8 @@ e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
     for (int t = 0; t < 10; ++t)
       if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
     if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+    const e2a_status al = check_alignment(a, grad_out);
+    if (al != E2A_OK) return al;
   }
   if (a->box)
     for (int d = 0; d < 3; ++d)
@@ -267,6 +284,8 @@ e2a_status check_layer_args(const e2a_attn_args* a, bool conv) {
     for (int t = 0; t < need; ++t)
       if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
     if (a->n_edges > 0 && !a->col) return fail(E2A_ERR_INVALID_ARG, "col is NULL");
+    const e2a_status al = check_alignment(a, nullptr);
+    if (al != E2A_OK) return al;
   }
   if (a->box)
     for (int d = 0; d < 3; ++d)

@@ -111,6 +111,10 @@ def attn_args(**kw):
     (dict(variant=2), B.E2A_ERR_UNSUPPORTED),          # no MFMA build for L=1, C=16, fp32
     (dict(workspace_bytes=8), B.E2A_ERR_INVALID_ARG),
     (dict(workspace=None), B.E2A_ERR_INVALID_ARG),
+    (dict(feat=FAKE + 8), B.E2A_ERR_INVALID_ARG),       # arrays start on 16-byte boundaries
+    (dict(w_so2=FAKE + 2), B.E2A_ERR_INVALID_ARG),
+    (dict(out=FAKE + 4), B.E2A_ERR_INVALID_ARG),
+    (dict(pos=FAKE + 12), B.E2A_ERR_INVALID_ARG),
 ])
 def test_attention_rejects_on_host(kw, status):
     a = attn_args(**kw)
@@ -176,6 +180,7 @@ def test_conv_does_not_need_qk_weights():
     (dict(variant=2), (FAKE, FAKE), B.E2A_ERR_UNSUPPORTED),         # no MFMA backward
     (dict(C=16, H=3), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),
     (dict(workspace_bytes=8), (FAKE, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(), (FAKE + 4, FAKE), B.E2A_ERR_INVALID_ARG),              # a misaligned cotangent
 ])
 def test_backward_rejects_on_host(kw, grads, status):
     kw = dict(out_lse=FAKE, **kw) if "out_lse" not in kw else kw
@@ -194,6 +199,8 @@ def test_backward_rejects_on_host(kw, grads, status):
     (dict(variant=2), (FAKE, None, FAKE), B.E2A_ERR_UNSUPPORTED),
     (dict(C=16, H=3), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
     (dict(workspace_bytes=8), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
+    (dict(), (FAKE + 8, None, FAKE), B.E2A_ERR_INVALID_ARG),         # a misaligned cotangent
+    (dict(feat=FAKE + 2), (FAKE, None, FAKE), B.E2A_ERR_INVALID_ARG),
 ])
 def test_weight_backward_rejects_on_host(kw, grads, status):
     """e2a_attention_bwd_weights (grad_out, grad_feat, grad_w_so2 here; the
@@ -493,3 +500,9 @@ def test_packer_and_order_queries():
     assert B.lib().e2a_destination_order(FAKE, 10, FAKE, None, 0, None) == B.E2A_ERR_INVALID_ARG
     assert B.lib().e2a_destination_order(None, 10, FAKE, FAKE, 1 << 30, None) == B.E2A_ERR_INVALID_ARG
     assert B.lib().e2a_destination_order(None, 0, None, None, 0, None) == B.E2A_OK
+
+
+def test_misaligned_arrays_are_named_in_the_message():
+    a = attn_args(feat=FAKE + 8)
+    assert B.lib().e2a_attention_fwd(ctypes.byref(a), None) == B.E2A_ERR_INVALID_ARG
+    assert "feat" in B.last_error_message() and "16-byte" in B.last_error_message()
