@@ -522,6 +522,31 @@ __device__ __forceinline__ void force_write(const ForceParams& p, int64_t e, con
   p.gedge[e * 3 + 2] = (T3[0] * u[1] - T3[1] * u[0]) * ir + s * u[2];
 }
 
+// LDS written by some lanes of a wave and then read by others: the wave's
+// LDS operations complete in order, so only the compiler has to be kept from
+// moving them across this point.
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// force_wigner for one wave's own edge, without workgroup barriers.
+template <int L, int l>
+__device__ __forceinline__ void force_wigner_wave(float (*D)[wig_size(L)], int lane) {
+  constexpr int w = 2 * l + 1;
+  if (lane < 4 * w) {
+    const int comp = lane / w, m = lane - comp * w - l;
+    float o[w];
+    wigner_tangent_row<l>(m, D[0], D[comp], o);
+    const float h = comp == 0 ? 0.5f : 1.0f;
+#pragma unroll
+    for (int n = 0; n < w; ++n) D[comp][wig_off(l) + (m + l) * w + n] = o[n] * h;
+  }
+  wave_sync();
+  if constexpr (l < L) force_wigner_wave<L, l + 1>(D, lane);
+}
+
 // One edge per wave, four per workgroup.  Lane 0 sets up the frame, D^1 and
 // its tangents; the degrees 2 .. L follow one row per lane; then the
 // products, summed over the channels within the wave.
@@ -564,10 +589,13 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
 // factors rho alpha and (d rho / d r) alpha of every (l, c) are formed per
 // edge in LDS from the radial weights, which the workgroup stages once for
 // its 32 edges.  y and dx arrive in bf16; rho alpha y and G_i are rounded to
-// bf16 for the products, whose sums are fp32.
+// bf16 for the products, whose sums are fp32.  Each wave works through its
+// own edges with no workgroup barrier after the staging, so that the waves'
+// latency-bound set-up and their loads overlap.
 constexpr int kFmWaves = 4, kFmIters = 8;   // 32 edges per workgroup, one per wave at a time
-template <int L>
-__global__ void __launch_bounds__(64 * kFmWaves) k_wg_force_mfma(ForceParams p, int64_t nb,
+constexpr int kFmBatch = 2;                 // channel steps whose loads are issued together
+template <int L, int CT>
+__global__ void __launch_bounds__(64 * kFmWaves, 2) k_wg_force_mfma(ForceParams p, int64_t nb,
                                                                  const uint16_t* __restrict__ feat,
                                                                  const uint16_t* __restrict__ w_rad) {
   typedef float f32x4v __attribute__((ext_vector_type(4)));
@@ -580,31 +608,34 @@ __global__ void __launch_bounds__(64 * kFmWaves) k_wg_force_mfma(ForceParams p, 
   __shared__ float Ds[kFmWaves][4][WS];   // D and its three tangents, per wave
   __shared__ float frs[kFmWaves][4];
   __shared__ int ijs[kFmWaves][2];
-  const int C = p.C, H = p.H, dh = C / H;
+  const int C = CT > 0 ? CT : p.C, H = p.H, dh = C / H;
   const int LC = (L + 1) * C;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   float* wr = fsm;                         // [8][L + 1][C] radial weights
   float* tab = fsm + 8 * LC + wv * 2 * LC; // [2][L + 1][C]: rho alpha, (d rho / d r) alpha
   for (int t = tid; t < 8 * LC; t += blockDim.x) wr[t] = bf16_to_f32(w_rad[t]);
+  __syncthreads();
   float (*D)[WS] = Ds[wv];
-  // the lane's operand row (l, m) and output column
+  // The lane's operand row (l, m) and its degree.  Rows K .. 31 of A and
+  // columns K .. 31 of B only reach output rows and columns that are never
+  // read, so their lanes load row K - 1 instead (valid memory, and no branch
+  // around the loads).
   const int row = lane & 31, hk = lane >> 5;
-  const bool rv = row < K;
+  const int rowc = row < K ? row : K - 1;
   int lr = 0;
-  while ((lr + 1) * (lr + 1) <= row && lr < L) ++lr;
-  const int mr = row - lr * lr - lr;
-  int lc = 0;
-  while ((lc + 1) * (lc + 1) <= row && lc < L) ++lc;   // the column's degree (column = row index)
+  while ((lr + 1) * (lr + 1) <= rowc) ++lr;
+  const int mr = rowc - lr * lr - lr;
   const uint16_t* dXb = static_cast<const uint16_t*>(p.dX);
   const uint16_t* Yb = static_cast<const uint16_t*>(p.Y);
   for (int it = 0; it < kFmIters; ++it) {
     const int64_t b = ((int64_t)blockIdx.x * kFmIters + it) * kFmWaves + wv;
-    const bool live = b < nb;
+    if (b >= nb) break;
     const int64_t e = p.e0 + b;
-    if (lane == 0 && live) force_edge_setup<L>(p, e, D, frs[wv], ijs[wv]);
-    __syncthreads();   // the first pass also orders the radial weights' fill
-    if constexpr (L >= 2) force_wigner<L, 2>(D, live, lane);
-    if (live) {
+    wave_sync();   // the previous edge's reads of D and the tables are done
+    if (lane == 0) force_edge_setup<L>(p, e, D, frs[wv], ijs[wv]);
+    wave_sync();
+    if constexpr (L >= 2) force_wigner_wave<L, 2>(D, lane);
+    {
       float rb[8], rd[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -623,53 +654,76 @@ __global__ void __launch_bounds__(64 * kFmWaves) k_wg_force_mfma(ForceParams p, 
         tab[LC + t] = d * a;
       }
     }
-    __syncthreads();
-    if (!live) continue;
+    wave_sync();
     const int i = ijs[wv][0], j = ijs[wv][1];
-    const int64_t bi = rv ? batch_index(p.bl, L, C, b, lr, mr, 0) : 0;
+    const int64_t bi = batch_index(p.bl, L, C, b, lr, mr, 0);
     const uint16_t* dxr = dXb + bi;
     const uint16_t* yr = Yb + bi;
-    const uint16_t* hr = feat + ((int64_t)j * K + row) * C;
-    const float* gr = p.grad + ((int64_t)i * K + row) * C;
+    const uint16_t* hr = feat + ((int64_t)j * K + rowc) * C;
+    const float* gr = p.grad + ((int64_t)i * K + rowc) * C;
     const float* ra = tab + lr * C;
     f32x16 accT = {}, accS = {};
-    for (int c0 = 8 * hk; c0 < C; c0 += 16) {
-      bf16x8 adx = {}, bh = {}, a1 = {}, a2 = {}, bg = {};
-      if (rv) {
-        adx = *reinterpret_cast<const bf16x8*>(dxr + c0);
-        bh = *reinterpret_cast<const bf16x8*>(hr + c0);
-        const u32x4v yw = *reinterpret_cast<const u32x4v*>(yr + c0);
-        const f32x4v g0 = *reinterpret_cast<const f32x4v*>(gr + c0);
-        const f32x4v g1 = *reinterpret_cast<const f32x4v*>(gr + c0 + 4);
-        const f32x4v r0 = *reinterpret_cast<const f32x4v*>(ra + c0);
-        const f32x4v r1 = *reinterpret_cast<const f32x4v*>(ra + c0 + 4);
-        const f32x4v d0 = *reinterpret_cast<const f32x4v*>(ra + LC + c0);
-        const f32x4v d1 = *reinterpret_cast<const f32x4v*>(ra + LC + c0 + 4);
-        f32x8v yv, gv, rv8, dv8;
+    // One step: 16 channels from c0 = 16 t + 8 (lane / 32) of the loaded rows.
+    auto step = [&](int c0, const bf16x8& adx, const bf16x8& bh, const u32x4v& yw, const f32x4v& g0,
+                    const f32x4v& g1) {
+      const f32x4v r0 = *reinterpret_cast<const f32x4v*>(ra + c0);
+      const f32x4v r1 = *reinterpret_cast<const f32x4v*>(ra + c0 + 4);
+      const f32x4v d0 = *reinterpret_cast<const f32x4v*>(ra + LC + c0);
+      const f32x4v d1 = *reinterpret_cast<const f32x4v*>(ra + LC + c0 + 4);
+      f32x8v yv, gv, rv8, dv8;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          yv[2 * q] = __uint_as_float(yw[q] << 16);
-          yv[2 * q + 1] = __uint_as_float(yw[q] & 0xffff0000u);
-          gv[q] = g0[q];
-          gv[4 + q] = g1[q];
-          rv8[q] = r0[q];
-          rv8[4 + q] = r1[q];
-          dv8[q] = d0[q];
-          dv8[4 + q] = d1[q];
-        }
-        a1 = __builtin_convertvector(yv * rv8, bf16x8);
-        a2 = __builtin_convertvector(yv * dv8, bf16x8);
-        bg = __builtin_convertvector(gv, bf16x8);
+      for (int q = 0; q < 4; ++q) {
+        yv[2 * q] = __uint_as_float(yw[q] << 16);
+        yv[2 * q + 1] = __uint_as_float(yw[q] & 0xffff0000u);
+        gv[q] = g0[q];
+        gv[4 + q] = g1[q];
+        rv8[q] = r0[q];
+        rv8[4 + q] = r1[q];
+        dv8[q] = d0[q];
+        dv8[4 + q] = d1[q];
       }
+      const bf16x8 a1 = __builtin_convertvector(yv * rv8, bf16x8);
+      const bf16x8 a2 = __builtin_convertvector(yv * dv8, bf16x8);
+      const bf16x8 bg = __builtin_convertvector(gv, bf16x8);
       accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adx, bh, accT, 0, 0, 0);
       accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, accT, 0, 0, 0);
       accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bg, accS, 0, 0, 0);
+    };
+    if constexpr (CT > 0) {
+      // C known at compile time: the steps' loads are issued kFmBatch at a
+      // time ahead of their products, a few round trips per edge instead of
+      // one per step
+      constexpr int NS = CT / 16, NB = kFmBatch < NS ? kFmBatch : NS;
+      static_assert(NS % NB == 0, "whole batches of steps");
+#pragma unroll
+      for (int t0 = 0; t0 < NS; t0 += NB) {
+        bf16x8 ldx[NB], lh[NB];
+        u32x4v ly[NB];
+        f32x4v lg0[NB], lg1[NB];
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const int c0 = 16 * (t0 + t) + 8 * hk;
+          ldx[t] = *reinterpret_cast<const bf16x8*>(dxr + c0);
+          lh[t] = *reinterpret_cast<const bf16x8*>(hr + c0);
+          ly[t] = *reinterpret_cast<const u32x4v*>(yr + c0);
+          lg0[t] = *reinterpret_cast<const f32x4v*>(gr + c0);
+          lg1[t] = *reinterpret_cast<const f32x4v*>(gr + c0 + 4);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) step(16 * (t0 + t) + 8 * hk, ldx[t], lh[t], ly[t], lg0[t], lg1[t]);
+      }
+    } else {
+      for (int c0 = 8 * hk; c0 < C; c0 += 16)
+        step(c0, *reinterpret_cast<const bf16x8*>(dxr + c0), *reinterpret_cast<const bf16x8*>(hr + c0),
+             *reinterpret_cast<const u32x4v*>(yr + c0), *reinterpret_cast<const f32x4v*>(gr + c0),
+             *reinterpret_cast<const f32x4v*>(gr + c0 + 4));
     }
     // register r holds (row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32)
     float T3[3] = {0.0f, 0.0f, 0.0f};
     float sv = 0.0f;
     if (row < K) {
-      const int wn = 2 * lc + 1, n = row - lc * lc;
+      const int lc = lr, wn = 2 * lc + 1, n = row - lc * lc;   // the column's degree (column index = row)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int ir = 8 * (r >> 2) + 4 * hk + (r & 3);
@@ -1468,8 +1522,14 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       if constexpr (kPairs) {
         if (yb) {
           constexpr int64_t per = kFmWaves * kFmIters;
-          k_wg_force_mfma<L><<<static_cast<unsigned>((nb + per - 1) / per), 64 * kFmWaves, force_mfma_smem(L, C),
-                               st>>>(fp, nb, feat, static_cast<const uint16_t*>(a->w_rad));
+          const unsigned grid = static_cast<unsigned>((nb + per - 1) / per);
+          const size_t smem = force_mfma_smem(L, C);
+          if (C == 128)
+            k_wg_force_mfma<L, 128><<<grid, 64 * kFmWaves, smem, st>>>(fp, nb, feat,
+                                                                      static_cast<const uint16_t*>(a->w_rad));
+          else
+            k_wg_force_mfma<L, 0><<<grid, 64 * kFmWaves, smem, st>>>(fp, nb, feat,
+                                                                    static_cast<const uint16_t*>(a->w_rad));
           E2A_LAUNCH_CHECK();
           continue;
         }
