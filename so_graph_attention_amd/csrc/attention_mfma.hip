@@ -70,6 +70,12 @@ constexpr int kBwdR = 4;
 constexpr int kMaxRadWg = 2048;   // radial pass: at most this many workgroups (partial slots)
 // The convolution stage: the forward with every edge weight 1.
 constexpr int kConv = 3;
+// The query pass with the radial pass's accumulation in the same epilogue:
+// both contract y (D G) from one recomputation, so a call that wants ds and
+// dW_rad runs the mix once instead of twice.
+constexpr int kBwdQR = 5;
+__host__ __device__ constexpr bool q_like(int md) { return md == kBwdQ || md == kBwdQR; }
+__host__ __device__ constexpr bool r_like(int md) { return md == kBwdR || md == kBwdQR; }
 
 // Wigner-D rows in LDS are padded to a multiple of 4 floats (16-byte reads).
 __host__ __device__ constexpr int dpad(int l) { return ((2 * l + 1) + 3) / 4 * 4; }
@@ -664,7 +670,7 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
     // query pass: the destinations' cotangent of the block's output degrees
     // (a pair of degrees below 4, or degree 4 alone: two operands at most)
     f16x8 gq0 = zero8, gq1 = zero8;
-    if constexpr (MD == kBwdQ || MD == kBwdR) {
+    if constexpr (q_like(MD) || r_like(MD)) {
       if constexpr (M == 0 && S::has1(M, b)) {
         grad_frags<L, S::blk_lo(M, b, 0)>(p, ln, lane, wave, gq0, gq1);
         grad_frags<L, S::blk_lo(M, b, 1)>(p, ln, lane, wave, gq1, gq1);
@@ -726,13 +732,21 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
           } else {
             const bf16x8 brad = f == 0 ? brad0 : brad1;
             const f32x16 rho = mfma_bf16(ln.arbf[0], brad, f32x16{});
-            if constexpr (MD == kBwdQ) {
+            if constexpr (q_like(MD)) {
               // the two operands are (lo0, lo1) for a pair, (A, B) for degree 4
               const f32x16 gt = rot_grad<L, lo, 0, 0>(s, ln, lane, f == 0 ? gq0 : gq1, gq1);
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 ns.dal[r] += rho[r] * c0[r] * gt[r];
                 pin(ns.dal[r]);
+              }
+              if constexpr (MD == kBwdQR) {
+                // the radial pass's t, as that pass forms it
+                float t[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) t[r] = ln.alpha[r] * c0[r] * gt[r];
+                rad_acc<L, lo, 0>(ns, s, lane, to_vec8<bf16x8>(t));
+                rad_acc<L, lo, 16>(ns, s, lane, to_vec8<bf16x8>(t + 8));
               }
             } else {
               float u[16];
@@ -770,13 +784,20 @@ __device__ __forceinline__ void mma_block(const MfmaParams& p, const Smem& s, __
           rad_acc<L, lo, 16 * t>(ns, s, lane, to_vec8<bf16x8>(ts));
         } else {
           const f32x16 rho = mfma_bf16(ln.arbf[1 + t], brad, f32x16{});
-          if constexpr (MD == kBwdQ) {
+          if constexpr (q_like(MD)) {
             // tile rows r and r + 16 are the +M and -M rows of one edge
             const f32x16 gt = rot_grad<L, lo, M, t>(s, ln, lane, gq0, gq1);
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
               ns.dal[8 * t + r] += rho[r] * ((C1[r] - C2[r + 8]) * gt[r] + (C2[r] + C1[r + 8]) * gt[r + 8]);
               pin(ns.dal[8 * t + r]);
+            }
+            if constexpr (MD == kBwdQR) {
+              float ts[8];
+#pragma unroll
+              for (int r = 0; r < 8; ++r)
+                ts[r] = ln.alpha[8 * t + r] * ((C1[r] - C2[r + 8]) * gt[r] + (C2[r] + C1[r + 8]) * gt[r + 8]);
+              rad_acc<L, lo, 16 * t>(ns, s, lane, to_vec8<bf16x8>(ts));
             }
           } else {
             float up[8], um[8];
@@ -960,7 +981,7 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   const int xcd = blockIdx.x & 7;
   const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
   stretch<L, MD>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
-  if constexpr (MD == kBwdR) {
+  if constexpr (r_like(MD)) {
     // lane l holds rows 4 (l / 16) + i (basis k of an even or odd degree),
     // channel 32 wave + l % 16 (a) and + 16 (b)
     const int lane = tid0 & 63;
@@ -992,7 +1013,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
   };
   // atoms without neighbours: zero output, log-normaliser -inf (the query
   // pass writes no output)
-  for (int64_t sl = s_lo + tid0 * step; MD != kBwdQ && MD != kBwdR && sl < s_hi; sl += kThreads * step) {
+  for (int64_t sl = s_lo + tid0 * step; !q_like(MD) && !r_like(MD) && sl < s_hi; sl += kThreads * step) {
     if (degree(sl) == 0) {
       const int64_t i = p.order[sl];
       for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
@@ -1134,7 +1155,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     if (tid < 2 * kH) {
       const int d = tid / kH, h = tid % kH;
       const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
-      if constexpr (MD == kBwdQ || MD == kBwdV || MD == kBwdR) {
+      if constexpr (q_like(MD) || MD == kBwdV || r_like(MD)) {
         // feature gradient: alpha from the forward's log-normaliser of the
         // destination of the forward edge (the neighbour, in the value pass)
         for (int e = b0; e < b1; ++e) {
@@ -1208,18 +1229,18 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           ln.mk[g][q] = (t0 < nA ? 0x0000FFFFu : 0u) | (t0 + 1 < nA ? 0xFFFF0000u : 0u);
         }
       ln.flip = (lnr & 8) ? ~0u : 0u;
-      if constexpr (MD == kBwdQ || MD == kBwdR) {
+      if constexpr (q_like(MD) || r_like(MD)) {
         ln.nA = nA;
         ln.ia = ia;
         ln.ib = ib;
         ln.gsA = p.gsc[ia];
         ln.gsB = p.gsc[ib];
       }
-      if constexpr (MD == kBwdQ) {
+      if constexpr (q_like(MD)) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) ns.dal[r] = 0.0f;
       }
-      if constexpr (MD == kBwdR) {
+      if constexpr (r_like(MD)) {
         // the rotated cotangent is in its atom's fp16 scale: undo it per
         // edge, then apply the global power of two that keeps alpha y (D G)
         // in fp16's range (divided out when the partials are added)
@@ -1229,7 +1250,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       }
     }
     do_block<L, 0, MD>(p, s, wrsrc, tid, wave, ln, has_b, ns, ring);
-    if constexpr (MD == kBwdQ) {
+    if constexpr (q_like(MD)) {
       // dalpha[edge][head]: the lane's partials summed over the head's 16
       // channels (a row of 16 lanes), lane r of the row ending with edge
       // crow(r, half); s.q is free since the logits
@@ -1618,6 +1639,18 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   return pl.conv ? launch_mode<L, kConv>(p, st) : launch_mode<L, kFwd>(p, st);
 }
 
+// dW_rad[k][l][c] = (sum over workgroups, in order, of their partials) / gnorm.
+template <int L>
+__global__ void k_rad_reduce(const float* __restrict__ part, int n_wg, const float* __restrict__ gnorm,
+                             float* __restrict__ w_rad) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int N = 8 * (L + 1) * kC;
+  if (t >= N) return;
+  float v = 0.0f;
+  for (int g = 0; g < n_wg; ++g) v += part[(int64_t)g * N + t];
+  w_rad[t] = v / *gnorm;
+}
+
 // Feature gradient on the matrix cores: delta, the query pass (ds), the
 // value pass (the transposed messages into grad_feat) and the l = 0 terms.
 template <int L>
@@ -1655,8 +1688,30 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
   p.delta = delta;
   p.ds = pl.ds;
-  e = launch_mode<L, kBwdQ>(p, st);
-  if (e != E2A_OK) return e;
+  if (pl.w_rad) {
+    // dW_rad in the same pass (the radial pass's partials and reduction)
+    if (8 * p.wg_per_xcd > kMaxRadWg) p.wg_per_xcd = kMaxRadWg / 8;
+    p.rad_part = reinterpret_cast<float*>(wb + W.radpart);
+    e = launch_mode<L, kBwdQR>(p, st);
+    if (e != E2A_OK) return e;
+    constexpr int N = 8 * (L + 1) * kC;
+    k_rad_reduce<L><<<(N + 255) / 256, 256, 0, st>>>(p.rad_part, 8 * p.wg_per_xcd, p.gnorm, pl.w_rad);
+    E2A_LAUNCH_CHECK();
+    // the value pass below keeps the query pass's workgroup count
+    e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
+    if (e != E2A_OK) return e;
+    p.q = pl.q;
+    p.k = pl.k;
+    p.lse = a->out_lse;
+    p.gpk = reinterpret_cast<const f16x8*>(wb + W.gpk);
+    p.gsc = reinterpret_cast<const float*>(wb + W.gsc);
+    p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
+    p.delta = delta;
+    p.ds = pl.ds;
+  } else {
+    e = launch_mode<L, kBwdQ>(p, st);
+    if (e != E2A_OK) return e;
+  }
   if (!pl.grad_feat) return pl.wdq ? launch_bwd_qk(pl, st) : E2A_OK;
   // value pass: the cotangent in bf16 takes the features' place
   p.feat = reinterpret_cast<const uint16_t*>(wb + W.gbf);
@@ -1665,18 +1720,6 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   e = launch_mode<L, kBwdV>(p, st);
   if (e != E2A_OK) return e;
   return launch_bwd_qk(pl, st);
-}
-
-// dW_rad[k][l][c] = (sum over workgroups, in order, of their partials) / gnorm.
-template <int L>
-__global__ void k_rad_reduce(const float* __restrict__ part, int n_wg, const float* __restrict__ gnorm,
-                             float* __restrict__ w_rad) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  constexpr int N = 8 * (L + 1) * kC;
-  if (t >= N) return;
-  float v = 0.0f;
-  for (int g = 0; g < n_wg; ++g) v += part[(int64_t)g * N + t];
-  w_rad[t] = v / *gnorm;
 }
 
 // dW_rad on the matrix cores: the cotangent's copies, then the radial pass

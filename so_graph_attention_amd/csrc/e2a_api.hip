@@ -132,9 +132,10 @@ e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
 }
 
 // q, k, then the query pass (ds) and, with grad_feat, the value pass and the
-// l = 0 terms; dq and dk to wdq, wdk when those are set.
+// l = 0 terms; dq and dk to wdq, wdk when those are set; dW_rad from the
+// query pass into w_rad when that is set (matrix-core path only).
 e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* grad_feat, float* wdq, float* wdk,
-                        char* base, const BwdWs& ws, hipStream_t s) {
+                        char* base, const BwdWs& ws, hipStream_t s, float* w_rad = nullptr) {
   AttnPlan qk{};
   qk.a = a;
   qk.q = reinterpret_cast<float*>(base + ws.q);
@@ -158,6 +159,7 @@ e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* gr
   if (st != E2A_OK) return st;
   const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
   const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
+  pl.w_rad = use_mfma ? w_rad : nullptr;
   return use_mfma ? launch_backward_mfma(pl, s) : launch_attention_backward(pl, s);
 }
 
@@ -514,9 +516,18 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   float* dq = reinterpret_cast<float*>(base + ws.dq);
   float* dk = reinterpret_cast<float*>(base + ws.dk);
   const bool want_qk = grad_w_q || grad_w_k;
+  // dW_rad by the fused kernel's radial accumulation where the MFMA build
+  // covers the shape, so that the batches need neither SO2(x) for it
+  // (without the positions) nor dyhat beside dy (with them); when the query
+  // pass runs anyway it accumulates dW_rad itself
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  const bool rad_mfma = grad_w_rad &&
+                        (a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok));
+  const bool rad_in_query = rad_mfma && (grad_feat || want_qk);
   if (grad_feat || want_qk) {
     // the softmax gradient ds (and dL/dh when asked for); dq, dk from it
-    st = run_backward(a, grad_out, grad_feat, want_qk ? dq : nullptr, want_qk ? dk : nullptr, base, ws.b, s);
+    st = run_backward(a, grad_out, grad_feat, want_qk ? dq : nullptr, want_qk ? dk : nullptr, base, ws.b, s,
+                      rad_in_query ? grad_w_rad : nullptr);
   } else {
     // dW_rad, dW_so2 and the positions need only q and k (for the
     // attention weights)
@@ -528,13 +539,7 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
     st = launch_qk(qk, s);
   }
   if (st != E2A_OK) return st;
-  // dW_rad by the fused kernel's radial pass where the MFMA build covers the
-  // shape, so that the batches need neither SO2(x) for it (without the
-  // positions) nor dyhat beside dy (with them)
-  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
-  const bool rad_mfma = grad_w_rad &&
-                        (a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok));
-  if (rad_mfma) {
+  if (rad_mfma && !rad_in_query) {
     BwdPlan rp{};
     rp.a = a;
     rp.grad_out = grad_out;

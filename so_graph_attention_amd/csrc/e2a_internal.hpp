@@ -103,6 +103,7 @@ struct BwdPlan {
   void* mfma_ws;           // workspace of the matrix-core path
   float* wdq;              // if set: dq_j = sum_j' ds_jj' k_j' / sqrt(C/H), f32 [N, C]
   float* wdk;              // if set: dk_j = sum_i ds_ij q_i / sqrt(C/H), f32 [N, C]
+  float* w_rad;            // if set (matrix-core path): dW_rad from the query pass itself, f32 [8, L+1, C]
   float box[3];
   int periodic;
 };
