@@ -275,6 +275,9 @@ struct MfmaParams {
   const bf16x8* wpk;
   const bf16x8* radpk;    // W_rad as [(L+1) C] vectors of its 8 basis weights (bf16, exact)
   const int32_t* order;   // destination atoms in spatial (Morton) order
+  const int32_t* sched;   // balanced deal: per workgroup, its slots of `order` in turn (null: cyclic)
+  const int32_t* sched_n; // per workgroup, the number of slots in its row of sched
+  int64_t sched_len;      // row length of sched
   int64_t n_atoms;
   int wg_per_xcd;
   float* out;
@@ -929,17 +932,19 @@ struct ChunkPlan {
   bool a_done, b_done;
 };
 
-// The destinations s_lo, s_lo + step, ... (< s_hi) of the spatial order:
-// their concatenated neighbour lists in chunks of 32 edge slots; a chunk
-// holds the rest of the current atom A and, when A ends inside it, the start
-// of the next atom B.  Only the last chunk is padded.
+// The workgroup's destinations at positions s_lo, s_lo + step, ... (< s_hi)
+// of its sequence (the spatial order itself, or its row `seq` of the
+// balanced deal): their concatenated neighbour lists in chunks of 32 edge
+// slots; a chunk holds the rest of the current atom A and, when A ends inside
+// it, the start of the next atom B.  Only the last chunk is padded.
 template <int L, int MD>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
-                                        int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
-                                        WRing& ring);
+                                        int wave, const int32_t* seq, int64_t s_lo, int64_t s_hi, int64_t step,
+                                        NodeState<L>& ns, WRing& ring);
 
-// A persistent workgroup processes every wg_per_xcd-th destination of its
-// XCD's range.
+// A persistent workgroup processes its share of its XCD's range of the
+// spatial order: every wg_per_xcd-th destination (cyclic deal), or its row of
+// the balanced deal.
 template <int L, int MD>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) k_attn_mfma(MfmaParams p) {
   using S = Shape<L>;
@@ -975,12 +980,19 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   }
 
   // Workgroups are dealt to the 8 XCDs round-robin.  Each XCD owns one
-  // eighth of the spatial order, dealt cyclically to its workgroups: at any
-  // time they work on neighbouring destinations, which share most of their
-  // neighbours' features in the XCD's L2.
+  // eighth of the spatial order, dealt to its workgroups in rounds of
+  // consecutive destinations: at any time they work on neighbouring
+  // destinations, which share most of their neighbours' features in the
+  // XCD's L2.  The balanced deal (k_deal) chooses which workgroup takes which
+  // destination of a round; without it workgroup w takes the w-th.
   const int xcd = blockIdx.x & 7;
   const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
-  stretch<L, MD>(p, s, wrsrc, tid0, wave, x_lo + (blockIdx.x >> 3), x_hi, p.wg_per_xcd, ns, ring);
+  const bool dealt = p.sched != nullptr;
+  const int32_t* seq = dealt ? p.sched + (int64_t)blockIdx.x * p.sched_len : nullptr;
+  const int64_t s_lo = dealt ? 0 : x_lo + (blockIdx.x >> 3);
+  const int64_t s_hi = dealt ? p.sched_n[blockIdx.x] : x_hi;
+  const int64_t step = dealt ? 1 : p.wg_per_xcd;
+  stretch<L, MD>(p, s, wrsrc, tid0, wave, seq, s_lo, s_hi, step, ns, ring);
   if constexpr (r_like(MD)) {
     // lane l holds rows 4 (l / 16) + i (basis k of an even or odd degree),
     // channel 32 wave + l % 16 (a) and + 16 (b)
@@ -1003,19 +1015,21 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
 
 template <int L, int MD>
 __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __amdgpu_buffer_rsrc_t wrsrc, int tid0,
-                                        int wave, int64_t s_lo, int64_t s_hi, int64_t step, NodeState<L>& ns,
-                                        WRing& ring) {
+                                        int wave, const int32_t* seq, int64_t s_lo, int64_t s_hi, int64_t step,
+                                        NodeState<L>& ns, WRing& ring) {
   using S = Shape<L>;
   constexpr int K = S::K;
+  // the atom at position sl of the workgroup's sequence
+  auto atom_at = [&](int64_t sl) -> int64_t { return p.order[seq ? seq[sl] : sl]; };
   auto degree = [&](int64_t sl) {
-    const int64_t i = p.order[sl];
+    const int64_t i = atom_at(sl);
     return p.row_ptr[i + 1] - p.row_ptr[i];
   };
   // atoms without neighbours: zero output, log-normaliser -inf (the query
   // pass writes no output)
   for (int64_t sl = s_lo + tid0 * step; !q_like(MD) && !r_like(MD) && sl < s_hi; sl += kThreads * step) {
     if (degree(sl) == 0) {
-      const int64_t i = p.order[sl];
+      const int64_t i = atom_at(sl);
       for (int q = 0; q < K * kC; ++q) p.out[i * K * kC + q] = 0.0f;
       if (p.out_lse)
         for (int h = 0; h < kH; ++h) p.out_lse[i * kH + h] = -INFINITY;
@@ -1031,7 +1045,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     c.a0 = a0;
     c.sb = s_hi;
     if (sa >= s_hi) return c;
-    c.ia = p.order[sa];
+    c.ia = atom_at(sa);
     const int64_t deg_a = p.row_ptr[c.ia + 1] - p.row_ptr[c.ia];
     c.nA = static_cast<int>(deg_a - a0 < kET ? deg_a - a0 : kET);
     c.a_done = a0 + c.nA == deg_a;
@@ -1039,7 +1053,7 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
     if (c.a_done && c.nA < kET) {
       c.sb = next_nz(sa + step);
       if (c.sb < s_hi) {
-        c.ib = p.order[c.sb];
+        c.ib = atom_at(c.sb);
         const int64_t deg_b = p.row_ptr[c.ib + 1] - p.row_ptr[c.ib];
         c.nB = static_cast<int>(deg_b < kET - c.nA ? deg_b : kET - c.nA);
         c.b_done = c.nB == deg_b;
@@ -1334,6 +1348,65 @@ __global__ void k_pack_rad(const uint16_t* __restrict__ w, u32x4* __restrict__ o
   out[v] = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
 }
 
+// The balanced deal of destinations to the workgroups of an XCD sorts each
+// round in one wave, so it serves up to 64 workgroups per XCD (two per CU
+// on MI355X's 32 CUs per XCD); beyond that the kernel deals cyclically.
+constexpr int kDealMaxWpx = 64;
+
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), m);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+// Ascending bitonic sort of one key per lane across the 64 lanes of a wave.
+__device__ __forceinline__ uint64_t wave_sort64(uint64_t key, int lane) {
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint64_t o = shfl_xor64(key, j);
+      const bool keep_min = ((lane & j) == 0) == ((lane & k) == 0);
+      key = keep_min ? (o < key ? o : key) : (o > key ? o : key);
+    }
+  return key;
+}
+
+// The balanced deal, one wave per (round, XCD).  Round r of XCD range
+// [x_lo, x_hi) holds the slots x_lo + r wpx + t (t < wpx) of the order, as in
+// the cyclic deal, but ranked by degree (most edges first, ties by slot): in
+// even rounds the workgroup w takes rank w, in odd rounds rank wpx - 1 - w,
+// so that a workgroup's heavy and light destinations alternate and the
+// workgroups end with about the same number of edges.  Rounds are
+// independent of each other, and the deal depends only on the degrees in
+// order, so it (and with it every result) is the same on every launch.  Row
+// xcd + 8 w of sched lists workgroup w's slots in round order; only the last
+// round can leave a workgroup without one, and sched_n counts them.
+__global__ void __launch_bounds__(64) k_deal(const int32_t* __restrict__ order, const int64_t* __restrict__ row_ptr,
+                                             int64_t n, int wpx, int64_t R, int32_t* __restrict__ sched,
+                                             int32_t* __restrict__ sched_n) {
+  const int64_t r = blockIdx.x;
+  const int xcd = blockIdx.y, lane = threadIdx.x;
+  const int64_t x_lo = xcd * n / 8, x_hi = (xcd + 1) * n / 8;
+  const int64_t rounds = (x_hi - x_lo + wpx - 1) / wpx;
+  const int64_t slot = x_lo + r * wpx + lane;
+  const bool valid = lane < wpx && slot < x_hi;
+  uint64_t key = ~0ull;
+  if (valid) {
+    const int64_t a = order[slot];
+    const int64_t d = row_ptr[a + 1] - row_ptr[a];
+    key = (static_cast<uint64_t>(0x7fffffff - d) << 32) | static_cast<uint64_t>(slot - x_lo);
+  }
+  key = wave_sort64(key, lane);
+  if (lane < wpx) {
+    const int w = (r & 1) ? wpx - 1 - lane : lane;
+    const bool got = key != ~0ull;
+    sched[(int64_t)(xcd + 8 * w) * R + r] = got ? static_cast<int32_t>(x_lo + (key & 0xffffffffu)) : -1;
+    const int64_t last = rounds > 0 ? rounds - 1 : 0;
+    if (r == last) sched_n[xcd + 8 * w] = static_cast<int32_t>(last + (got ? 1 : 0));
+  }
+}
+
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
 constexpr int kRadixBits = 9;                        // two radix passes over 18-bit keys
 constexpr int kRadix = 1 << kRadixBits;
@@ -1425,6 +1498,7 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 
 struct MfmaWs {
   size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
+  size_t sched, sched_n;   // the balanced deal: per-workgroup rows of slots and their lengths
   size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
   size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales,
   size_t gnorm;            // and the value pass's cotangent scale,
@@ -1451,6 +1525,8 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
   m.bbox = take(8 * sizeof(float));
   m.bbox_part = take(sizeof(float) * kBboxPartialFloats);
+  m.sched = take(sizeof(int32_t) * (n + 8 + 8 * kDealMaxWpx));
+  m.sched_n = take(sizeof(int32_t) * 8 * kDealMaxWpx);
   if (backward) {
     m.wt = take(S::wtotal() * 16);
     m.gbf = take(sizeof(uint16_t) * n * S::K * kC);
@@ -1612,6 +1688,28 @@ e2a_status base_params(const e2a_attn_args* a, const MfmaWs& W, char* wb, const 
   return E2A_OK;
 }
 
+// The balanced deal for p's workgroups over the destination order p.order
+// (from the caller or spatial_order), into the workspace; p then reads it.
+// Set p.wg_per_xcd first.  With a mean degree below the 32-edge chunk the
+// cyclic deal stays: a chunk holds at most two destinations, so there the
+// work follows the number of chunks rather than of edges, and an edge-
+// balanced deal pairs light destinations into half-empty chunks (measured
+// slower on the drug-like batch, faster on the denser systems).
+e2a_status deal(const MfmaWs& W, char* wb, MfmaParams& p, int64_t n_edges, hipStream_t st) {
+  const int64_t n = p.n_atoms;
+  if (n == 0 || p.wg_per_xcd > kDealMaxWpx || n_edges < (int64_t)kET * n) return E2A_OK;   // cyclic deal
+  const int wpx = p.wg_per_xcd;
+  const int64_t R = ((n + 7) / 8 + wpx - 1) / wpx;
+  int32_t* sched = reinterpret_cast<int32_t*>(wb + W.sched);
+  int32_t* sched_n = reinterpret_cast<int32_t*>(wb + W.sched_n);
+  k_deal<<<dim3(static_cast<unsigned>(R), 8), 64, 0, st>>>(p.order, p.row_ptr, n, wpx, R, sched, sched_n);
+  E2A_LAUNCH_CHECK();
+  p.sched = sched;
+  p.sched_n = sched_n;
+  p.sched_len = R;
+  return E2A_OK;
+}
+
 template <int L, int MD>
 e2a_status launch_mode(const MfmaParams& p, hipStream_t st) {
   using S = Shape<L>;
@@ -1631,6 +1729,8 @@ e2a_status launch_typed(const AttnPlan& pl, hipStream_t st) {
   if (e != E2A_OK) return e;
   MfmaParams p;
   e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
+  if (e != E2A_OK) return e;
+  e = deal(W, wb, p, a->n_edges, st);
   if (e != E2A_OK) return e;
   p.q = pl.q;
   p.k = pl.k;
@@ -1679,6 +1779,10 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   MfmaParams p;
   e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
   if (e != E2A_OK) return e;
+  // with dW_rad the partials take one slot per workgroup
+  if (pl.w_rad && 8 * p.wg_per_xcd > kMaxRadWg) p.wg_per_xcd = kMaxRadWg / 8;
+  e = deal(W, wb, p, a->n_edges, st);
+  if (e != E2A_OK) return e;
   p.q = pl.q;
   p.k = pl.k;
   p.lse = a->out_lse;
@@ -1690,24 +1794,12 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.ds = pl.ds;
   if (pl.w_rad) {
     // dW_rad in the same pass (the radial pass's partials and reduction)
-    if (8 * p.wg_per_xcd > kMaxRadWg) p.wg_per_xcd = kMaxRadWg / 8;
     p.rad_part = reinterpret_cast<float*>(wb + W.radpart);
     e = launch_mode<L, kBwdQR>(p, st);
     if (e != E2A_OK) return e;
     constexpr int N = 8 * (L + 1) * kC;
     k_rad_reduce<L><<<(N + 255) / 256, 256, 0, st>>>(p.rad_part, 8 * p.wg_per_xcd, p.gnorm, pl.w_rad);
     E2A_LAUNCH_CHECK();
-    // the value pass below keeps the query pass's workgroup count
-    e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
-    if (e != E2A_OK) return e;
-    p.q = pl.q;
-    p.k = pl.k;
-    p.lse = a->out_lse;
-    p.gpk = reinterpret_cast<const f16x8*>(wb + W.gpk);
-    p.gsc = reinterpret_cast<const float*>(wb + W.gsc);
-    p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
-    p.delta = delta;
-    p.ds = pl.ds;
   } else {
     e = launch_mode<L, kBwdQ>(p, st);
     if (e != E2A_OK) return e;
@@ -1742,6 +1834,8 @@ e2a_status launch_radial_typed(const BwdPlan& pl, float* w_rad, hipStream_t st) 
   e = base_params<L>(a, W, wb, pl.box, pl.periodic, p);
   if (e != E2A_OK) return e;
   if (8 * p.wg_per_xcd > kMaxRadWg) p.wg_per_xcd = kMaxRadWg / 8;
+  e = deal(W, wb, p, a->n_edges, st);
+  if (e != E2A_OK) return e;
   p.q = pl.q;
   p.k = pl.k;
   p.lse = a->out_lse;

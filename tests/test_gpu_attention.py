@@ -174,6 +174,35 @@ def test_mfma_kernel_chunk_packing_degrees(B, L):
     assert np.max(np.abs(lse[~iso] - want_lse[~iso])) <= 1e-4
 
 
+def test_mfma_kernel_balanced_deal_full_output(B):
+    """A system whose mean degree is above the 32-edge chunk (clusters of 33
+    to 60 atoms), so destinations are dealt to workgroups by degree in
+    rounds: several rounds, both directions and a ragged last round.  Every
+    output is compared with the oracle, and a second launch must agree bit
+    for bit."""
+    rng = np.random.default_rng(5)
+    sizes = [int(g) for g in rng.integers(33, 61, size=20)]
+    cutoff = float(np.float32(5.0))
+    geom = cluster_geometry(sizes, cutoff, seed=23)
+    w = make_config("tiny", L=4, C=128, H=8, dtype="bf16", geometry=geom)
+    w.cutoff = cutoff
+    rp, col = O.neighbor_list(w.pos, w.cutoff, w.box, w.batch)
+    assert col.size >= 32 * w.n_atoms
+    log(f"[attn] mfma balanced deal: {w.n_atoms} atoms, {col.size} edges")
+    d = to_device(w)
+    d["row_ptr"] = torch.from_numpy(rp).cuda()
+    d["col"] = torch.from_numpy(col).cuda()
+    out, lse = run_gpu(B, w, d, "mfma")
+    out2, lse2 = run_gpu(B, w, d, "mfma")
+    assert np.array_equal(out, out2) and np.array_equal(lse, lse2)
+    want, want_lse = oracle_out(w, rp, col, None)
+    err = rel_l2(out, want)
+    log(f"[attn] mfma balanced deal rel-L2 {err:.3e}")
+    assert np.all(np.isfinite(out))
+    assert err <= TOL_BF16
+    assert np.max(np.abs(lse - want_lse)) <= 1e-4
+
+
 @pytest.mark.parametrize("name", ["drug", "protein"])
 def test_mfma_kernel_is_deterministic(B, name):
     """Two launches on the same inputs give bit-identical outputs: the spatial
