@@ -1011,23 +1011,143 @@ __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
       }
 }
 
+// The weight products Xᵀ dY with both operands contiguous along m (and n):
+// each 32-deep k slice is copied to LDS as it lies in memory, [k][m], every
+// k row's 128 values (256 bytes) read by 16 neighbouring lanes, and the
+// MFMA fragments (8 consecutive k of one row) come from gfx950's LDS
+// transpose reads.  ds_read_b64_tr_b16 gives lane i of each 16-lane group,
+// in slot q, element i % 4 of the 4 elements at lane 4 q + i / 4's address,
+// so a lane 16 g + s of the wave (q = s / 4, p = s % 4) that points at row
+// k0 + q, column c0 + 16 (g % 2) + 4 p receives T[k0 + q'][c0 + 16 (g % 2) + i]
+// for q' = 0..3: four consecutive k of its own fragment row; k0 = 8 (g / 2)
+// and + 4 for the second read.
+constexpr int kTrPad = 16;   // row stride 144 values (288 bytes)
+struct GemmSmemTr {
+  uint16_t a[2][kBK][kTM + kTrPad];
+  uint16_t b[2][kBK][kTM + kTrPad];
+};
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 tr_frag(const uint16_t (*T)[kTM + kTrPad], int k0, int c0, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (sl >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (sl & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T[row][col]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&T[row + 4][col]));
+  const i16x4 v[2] = {lo, hi};
+  bf16x8 r;
+  __builtin_memcpy(&r, v, 16);
+  return r;
+}
+
+__device__ __forceinline__ void gemm_body_tr(const Gemm& g, GemmSmemTr& sm) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint16_t* A = static_cast<const uint16_t*>(g.A);
+  const uint16_t* B = static_cast<const uint16_t*>(g.B);
+  const uint16_t* A2 = static_cast<const uint16_t*>(g.A2);
+  const uint16_t* B2 = static_cast<const uint16_t*>(g.B2);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+  const uint32_t id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const uint32_t q8 = total / 8, r8 = total % 8, xcd = id % 8, local = id / 8;
+  const uint32_t wi = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
+  const uint32_t bx = wi % nx, by = (wi / nx) % ny, bz = wi / (nx * ny);
+  const int64_t m0 = (int64_t)by * kTM, n0 = (int64_t)bx * kTM;
+  const int64_t kb = (int64_t)bz * g.kper;
+  const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
+  const int64_t k1 = A2 ? g.K1 : g.K;
+  // thread t copies k rows t / 16 and t / 16 + 16 of the slice, columns
+  // 8 (t % 16) .. + 7 (A(m, k) = A[m + k sak], B(k, n) = B[n + k sbk])
+  const int kr = tid >> 4, cq = (tid & 15) * 8;
+  auto fetch = [&](int64_t k0, u32x4 (&fa)[2], u32x4 (&fb)[2]) {
+    const bool seg2 = k0 >= k1;
+    const uint16_t* X = seg2 ? A2 : A;
+    const uint16_t* Y = seg2 ? B2 : B;
+    const int64_t kk0 = seg2 ? k0 - k1 : k0, kend = seg2 ? ke - k1 : (ke < k1 ? ke : k1);
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const int64_t k = kk0 + kr + 16 * v;
+      const bool kin = k < kend;
+      fa[v] = (kin && m0 + cq < g.M) ? *reinterpret_cast<const u32x4*>(X + m0 + cq + k * g.sak) : u32x4{0, 0, 0, 0};
+      fb[v] = (kin && n0 + cq < g.N) ? *reinterpret_cast<const u32x4*>(Y + n0 + cq + k * g.sbk) : u32x4{0, 0, 0, 0};
+      if (seg2 && g.neg2) fb[v] ^= 0x80008000u;   // bf16 sign bits
+    }
+  };
+  auto commit = [&](const u32x4 (&fa)[2], const u32x4 (&fb)[2], int bsel) {
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      *reinterpret_cast<u32x4*>(&sm.a[bsel][kr + 16 * v][cq]) = fa[v];
+      *reinterpret_cast<u32x4*>(&sm.b[bsel][kr + 16 * v][cq]) = fb[v];
+    }
+  };
+  f32x16 acc[2][2] = {};
+  u32x4 fa[2], fb[2];
+  int buf = 0;
+  if (kb < ke) {
+    fetch(kb, fa, fb);
+    commit(fa, fb, 0);
+  }
+  __syncthreads();
+  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    const bool more = k0 + kBK < ke;
+    if (more) fetch(k0 + kBK, fa, fb);
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 16) {
+      bf16x8 af[2], bfr[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        af[t] = tr_frag(sm.a[buf], ks, wm * 64 + t * 32, lane);
+        bfr[t] = tr_frag(sm.b[buf], ks, wn * 64 + t * 32, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+    if (more) commit(fa, fb, buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // register r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (m < g.M && n < g.N) {
+          const float v = acc[i][j][r];
+          if (g.S > 1) {
+            float* pp = g.part + ((int64_t)bz * g.M + m) * g.N + n;
+            *pp = g.part_acc ? *pp + g.alpha * v : g.alpha * v;
+          } else if (g.overwrite) {
+            g.C[m * g.ldc + n] = g.alpha * v;
+          } else {
+            g.C[m * g.ldc + n] += g.alpha * v;
+          }
+        }
+      }
+}
+
+__global__ void __launch_bounds__(256, 4) k_gemm_mfma_tr(Gemm g) {
+  __shared__ __attribute__((aligned(16))) GemmSmemTr sm;
+  gemm_body_tr(g, sm);
+}
+
 // Any layouts, three workgroups per CU (168 VGPRs).
 __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   __shared__ __attribute__((aligned(16))) GemmSmem sm;
   gemm_body<kAny, kAny, false>(g, sm);
 }
 
-// Fixed layouts with every extent a multiple of 8: without the per-launch
+// Fixed layout with every extent a multiple of 8: without the per-launch
 // choice and the element-by-element path the kernel fits 128 VGPRs, so four
 // workgroups share a CU (the LDS holds exactly four) and a third more slices
 // are in flight; the loop is bound by the slices' load latency.
-// Both operands contiguous along m and n: the weight products Xᵀ dY, which
-// contract over edges.
-__global__ void __launch_bounds__(256, 4) k_gemm_mfma_tt(Gemm g) {
-  __shared__ __attribute__((aligned(16))) GemmSmem sm;
-  gemm_body<kVecR, kVecR, true>(g, sm);
-}
-
 // Both operands contiguous along k: the products of the edges' rows with the
 // SO(2) blocks (y = SO2(x), dx = SO2ᵀ(dy)).
 __global__ void __launch_bounds__(256, 4) k_gemm_mfma_kk(Gemm g) {
@@ -1125,7 +1245,7 @@ e2a_status launch_gemm(const Gemm& g, hipStream_t st) {
     // second segment's start) and the vector extents must be multiples of 8
     const bool k8 = g.K % 8 == 0 && g.kper % 8 == 0 && (!g.A2 || g.K1 % 8 == 0);
     if (av == kVecR && bv == kVecR && k8 && g.M % 8 == 0 && g.N % 8 == 0)
-      k_gemm_mfma_tt<<<grid, 256, 0, st>>>(g);
+      k_gemm_mfma_tr<<<grid, 256, 0, st>>>(g);
     else if (av == kVecK && bv == kVecK && k8)
       k_gemm_mfma_kk<<<grid, 256, 0, st>>>(g);
     else
@@ -1169,7 +1289,7 @@ e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
 // The SO(2) weight gradients sum over every batch: each of the 2L + 1
 // matrices keeps dw_splits(m) partials for the whole call, which every batch's
 // products add to, and one reduction at the end.  These products run on
-// k_gemm_mfma_tt, four workgroups per CU (128 VGPRs a lane, 40 KB of LDS
+// k_gemm_mfma_tr, four workgroups per CU (122 VGPRs a lane, 36 KB of LDS
 // each), 1024 on the 256 CUs, and a launch with a few workgroups more than
 // that takes a second round: the split count fills the 1024 slots without
 // passing them (tiles x S <= 1024).
