@@ -181,6 +181,114 @@ __device__ __forceinline__ void gather_degree(const GatherParams& p, const T* __
   if constexpr (l < L) gather_degree<L, l + 1, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
+// The same for bf16 storage with 16-byte accesses: one (edge, 8 channels)
+// per work item, so that feature rows are read, and x and dy rows written,
+// 16 bytes a lane, and every D entry read from LDS serves 8 channels.  Each
+// channel's sums run in the order of gather_degree, so the results are the
+// same bit for bit.  Needs C / 8 to divide the workgroup and a head to span
+// a multiple of 8 channels.
+template <int L, int l>
+__device__ __forceinline__ void gather_degree_vec(const GatherParams& p, const uint16_t* __restrict__ feat,
+                                                  uint16_t* __restrict__ X, uint16_t* __restrict__ GT,
+                                                  const float* D, const float* al, const float* rb, const int* ii,
+                                                  const int* jj, int64_t b0, int tid) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int K = (L + 1) * (L + 1);
+  constexpr int WS = wig_size(L);
+  constexpr int w = 2 * l + 1;
+  const int C = p.C, H = p.H, dh = C / H;
+  const int per = C / 8;                       // work items per edge
+  const int o = tid % per, c0 = 8 * o;
+  const uint16_t* wr = static_cast<const uint16_t*>(p.w_rad);
+  auto lo16 = [](uint32_t u) { return __uint_as_float(u << 16); };
+  auto hi16 = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+  for (int s = tid / per; s < kEB; s += blockDim.x / per) {
+    if (ii[s] < 0) continue;
+    const float* Dl = D + s * WS + wig_off(l);
+    // x = D h_j, the feature rows kept packed
+    {
+      const uint16_t* hj = feat + ((int64_t)jj[s] * K + l * l) * C + c0;
+      u32x4 hw[w];
+#pragma unroll
+      for (int n = 0; n < w; ++n) hw[n] = *reinterpret_cast<const u32x4*>(hj + (size_t)n * C);
+#pragma unroll 1
+      for (int mi = 0; mi < w; ++mi) {
+        float x[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) x[q] = 0.0f;
+#pragma unroll
+        for (int n = 0; n < w; ++n) {
+          const float d = Dl[mi * w + n];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            x[2 * q] += d * lo16(hw[n][q]);
+            x[2 * q + 1] += d * hi16(hw[n][q]);
+          }
+        }
+        u32x4 xo;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          xo[q] = static_cast<uint32_t>(f32_to_bf16_rne(x[2 * q])) |
+                  (static_cast<uint32_t>(f32_to_bf16_rne(x[2 * q + 1])) << 16);
+        *reinterpret_cast<u32x4*>(X + batch_index(p.bl, L, C, b0 + s, l, mi - l, c0)) = xo;
+      }
+    }
+    // dy = rho D (alpha G_i)
+    const float a0 = al[s * H + c0 / dh];
+    float a[8];
+    {
+      // the 8 channels' radial weights (L1-resident across the edges)
+      float rho[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) rho[q] = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        const u32x4 u = *reinterpret_cast<const u32x4*>(wr + (size_t)(kk * (L + 1) + l) * C + c0);
+        const float r = rb[s * 8 + kk];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          rho[2 * q] += r * lo16(u[q]);
+          rho[2 * q + 1] += r * hi16(u[q]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) a[q] = a0 * rho[q];
+    }
+    const float* gi = p.grad + ((int64_t)ii[s] * K + l * l) * C + c0;
+    f32x4 gw[w][2];
+#pragma unroll
+    for (int n = 0; n < w; ++n) {
+      gw[n][0] = *reinterpret_cast<const f32x4*>(gi + (size_t)n * C);
+      gw[n][1] = *reinterpret_cast<const f32x4*>(gi + (size_t)n * C + 4);
+    }
+#pragma unroll 1
+    for (int mi = 0; mi < w; ++mi) {
+      float g[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) g[q] = 0.0f;
+#pragma unroll
+      for (int n = 0; n < w; ++n) {
+        const float d = Dl[mi * w + n];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) g[q] += d * gw[n][q >> 2][q & 3];
+      }
+      const int64_t idx = batch_index(p.bl, L, C, b0 + s, l, mi - l, c0);
+      u32x4 go;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        go[q] = static_cast<uint32_t>(f32_to_bf16_rne(g[2 * q] * a[2 * q])) |
+                (static_cast<uint32_t>(f32_to_bf16_rne(g[2 * q + 1] * a[2 * q + 1])) << 16);
+      *reinterpret_cast<u32x4*>(GT + idx) = go;
+      if (p.dyhat) {
+        *reinterpret_cast<f32x4*>(p.dyhat + idx) = f32x4{g[0] * a0, g[1] * a0, g[2] * a0, g[3] * a0};
+        *reinterpret_cast<f32x4*>(p.dyhat + idx + 4) = f32x4{g[4] * a0, g[5] * a0, g[6] * a0, g[7] * a0};
+      }
+    }
+  }
+  if constexpr (l < L) gather_degree_vec<L, l + 1>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
+}
+
 // D^l (l = 2..L) of the workgroup's edges from D^1 and D^{l-1}, one (edge,
 // row) per thread and level (the row recursion of the fused kernel).
 template <int L, int l>
@@ -206,6 +314,12 @@ __device__ __forceinline__ void gather_wigner(float* D, const int* ii, int tid) 
     __syncthreads();
     gather_wigner<L, l + 1>(D, ii, tid);
   }
+}
+
+// The 16-byte gather applies: C / 8 items per edge dividing the workgroup,
+// heads of a multiple of 8 channels.
+__host__ __device__ inline bool gather_vec_ok(int C, int H, int threads) {
+  return C % 8 == 0 && threads % (C / 8) == 0 && (C / H) % 8 == 0;
 }
 
 // x = D h_j and dyhat = D (alpha G_i) (or rho dyhat) for kEB edges of the
@@ -283,6 +397,12 @@ __global__ void __launch_bounds__(256) k_wg_gather(GatherParams p, const T* __re
   }
   __syncthreads();
   gather_wigner<L, 2>(D, ii, tid);
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    if (gather_vec_ok(C, H, blockDim.x)) {
+      gather_degree_vec<L, 0>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
+      return;
+    }
+  }
   gather_degree<L, 0, T>(p, feat, X, GT, D, al, rb, ii, jj, b0, tid);
 }
 
