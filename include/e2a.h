@@ -235,7 +235,7 @@ e2a_status e2a_attention_fwd(const e2a_attn_args* args, void* stream);
  * and args->workspace_bytes are ignored.  The call allocates nothing: no
  * hipMalloc, hipFree or allocating library routine.  Sizes whose workspace
  * (e2a_attention_workspace_bytes) exceeds E2A_NOALLOC_SCRATCH_BYTES give
- * E2A_ERR_INVALID_ARG before anything runs (64 MiB holds up to about 61,000
+ * E2A_ERR_INVALID_ARG before anything runs (64 MiB holds up to about 60,000
  * atoms at L = 4, C = 128).  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (other streams, other host threads) race and
  * must be ordered by the caller.  Nothing in the array needs to start at zero.

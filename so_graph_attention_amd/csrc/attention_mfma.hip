@@ -275,6 +275,7 @@ struct MfmaParams {
   const bf16x8* wpk;
   const bf16x8* radpk;    // W_rad as [(L+1) C] vectors of its 8 basis weights (bf16, exact)
   const int32_t* order;   // destination atoms in spatial (Morton) order
+  const int64_t* xcd_lo;  // [9] the XCD ranges of the order, split by edges (null: by atoms)
   const int32_t* sched;   // balanced deal: per workgroup, its slots of `order` in turn (null: cyclic)
   const int32_t* sched_n; // per workgroup, the number of slots in its row of sched
   int64_t sched_len;      // row length of sched
@@ -986,7 +987,8 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2
   // XCD's L2.  The balanced deal (k_deal) chooses which workgroup takes which
   // destination of a round; without it workgroup w takes the w-th.
   const int xcd = blockIdx.x & 7;
-  const int64_t x_lo = xcd * p.n_atoms / 8, x_hi = (xcd + 1) * p.n_atoms / 8;
+  const int64_t x_lo = p.xcd_lo ? p.xcd_lo[xcd] : xcd * p.n_atoms / 8;
+  const int64_t x_hi = p.xcd_lo ? p.xcd_lo[xcd + 1] : (xcd + 1) * p.n_atoms / 8;
   const bool dealt = p.sched != nullptr;
   const int32_t* seq = dealt ? p.sched + (int64_t)blockIdx.x * p.sched_len : nullptr;
   const int64_t s_lo = dealt ? 0 : x_lo + (blockIdx.x >> 3);
@@ -1383,11 +1385,12 @@ __device__ __forceinline__ uint64_t wave_sort64(uint64_t key, int lane) {
 // xcd + 8 w of sched lists workgroup w's slots in round order; only the last
 // round can leave a workgroup without one, and sched_n counts them.
 __global__ void __launch_bounds__(64) k_deal(const int32_t* __restrict__ order, const int64_t* __restrict__ row_ptr,
-                                             int64_t n, int wpx, int64_t R, int32_t* __restrict__ sched,
-                                             int32_t* __restrict__ sched_n) {
+                                             const int64_t* __restrict__ xcd_lo, int64_t n, int wpx, int64_t R,
+                                             int32_t* __restrict__ sched, int32_t* __restrict__ sched_n) {
   const int64_t r = blockIdx.x;
   const int xcd = blockIdx.y, lane = threadIdx.x;
-  const int64_t x_lo = xcd * n / 8, x_hi = (xcd + 1) * n / 8;
+  const int64_t x_lo = xcd_lo ? xcd_lo[xcd] : xcd * n / 8;
+  const int64_t x_hi = xcd_lo ? xcd_lo[xcd + 1] : (xcd + 1) * n / 8;
   const int64_t rounds = (x_hi - x_lo + wpx - 1) / wpx;
   const int64_t slot = x_lo + r * wpx + lane;
   const bool valid = lane < wpx && slot < x_hi;
@@ -1405,6 +1408,41 @@ __global__ void __launch_bounds__(64) k_deal(const int32_t* __restrict__ order, 
     const int64_t last = rounds > 0 ? rounds - 1 : 0;
     if (r == last) sched_n[xcd + 8 * w] = static_cast<int32_t>(last + (got ? 1 : 0));
   }
+}
+
+// The XCD ranges of the order split by edges: the degree of every slot of
+// the order, their prefix sums (k_scan), and the first slot whose prefix
+// reaches x E / 8 for x = 1..7, each kept within n / 16 of the split by atoms
+// x n / 8 (so that no range holds more than about a quarter of the atoms).
+// Every XCD then streams about the same number of edges.
+__global__ void k_slot_degree(const int32_t* __restrict__ order, const int64_t* __restrict__ row_ptr, int64_t n,
+                              int32_t* __restrict__ deg) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n) {
+    const int64_t a = order[t];
+    deg[t] = static_cast<int32_t>(row_ptr[a + 1] - row_ptr[a]);
+  }
+}
+
+__global__ void __launch_bounds__(64) k_xcd_split(const int32_t* __restrict__ pre, int64_t n,
+                                                  int64_t* __restrict__ xcd_lo) {
+  const int x = threadIdx.x;
+  if (x > 8) return;
+  int64_t b = x * n / 8;
+  if (x > 0 && x < 8) {
+    const int64_t target = (int64_t)x * pre[n] / 8;
+    int64_t lo = 0, hi = n;   // first t with pre[t] >= target
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) / 2;
+      if (pre[mid] < target) lo = mid + 1;
+      else hi = mid;
+    }
+    const int64_t h = (n + 15) / 16;
+    const int64_t c = x * n / 8;
+    b = lo < c - h ? c - h : (lo > c + h ? c + h : lo);
+    b = b < 0 ? 0 : (b > n ? n : b);
+  }
+  xcd_lo[x] = b;
 }
 
 constexpr int kOrderBits = 6;                       // Morton cells per axis = 64
@@ -1499,6 +1537,7 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 struct MfmaWs {
   size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
   size_t sched, sched_n;   // the balanced deal: per-workgroup rows of slots and their lengths
+  size_t xdeg, xpre, xbsum, xlo;   // the XCD ranges split by edges
   size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
   size_t gpk, gsc;         // and the query pass's scaled fp16 cotangent with its scales,
   size_t gnorm;            // and the value pass's cotangent scale,
@@ -1525,8 +1564,13 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
   m.bbox = take(8 * sizeof(float));
   m.bbox_part = take(sizeof(float) * kBboxPartialFloats);
-  m.sched = take(sizeof(int32_t) * (n + 8 + 8 * kDealMaxWpx));
+  // a range of the edge split holds at most 2 ceil(n / 8) + 2 slots
+  m.sched = take(sizeof(int32_t) * (2 * n + 32 + 8 * kDealMaxWpx));
   m.sched_n = take(sizeof(int32_t) * 8 * kDealMaxWpx);
+  m.xdeg = take(sizeof(int32_t) * n);
+  m.xpre = take(sizeof(int32_t) * (n + 1));
+  m.xbsum = take(sizeof(int64_t) * scan_bsum_count(n));
+  m.xlo = take(sizeof(int64_t) * 9);
   if (backward) {
     m.wt = take(S::wtotal() * 16);
     m.gbf = take(sizeof(uint16_t) * n * S::K * kC);
@@ -1697,12 +1741,30 @@ e2a_status base_params(const e2a_attn_args* a, const MfmaWs& W, char* wb, const 
 // slower on the drug-like batch, faster on the denser systems).
 e2a_status deal(const MfmaWs& W, char* wb, MfmaParams& p, int64_t n_edges, hipStream_t st) {
   const int64_t n = p.n_atoms;
-  if (n == 0 || p.wg_per_xcd > kDealMaxWpx || n_edges < (int64_t)kET * n) return E2A_OK;   // cyclic deal
+  if (n == 0 || n_edges < (int64_t)kET * n) return E2A_OK;   // cyclic deal, XCD ranges by atoms
+  // the XCD ranges split by edges (prefix sums in int32: E < 2^31); below a
+  // chunk's mean degree the imbalance is within the XCDs' ranges and the
+  // three extra launches did not pay (drug-like batch)
+  if (n_edges < INT32_MAX) {
+    int32_t* deg = reinterpret_cast<int32_t*>(wb + W.xdeg);
+    int32_t* pre = reinterpret_cast<int32_t*>(wb + W.xpre);
+    int64_t* xlo = reinterpret_cast<int64_t*>(wb + W.xlo);
+    k_slot_degree<<<static_cast<unsigned>((n + 255) / 256), 256, 0, st>>>(p.order, p.row_ptr, n, deg);
+    E2A_LAUNCH_CHECK();
+    const e2a_status e = exclusive_scan_i32(deg, n, pre, reinterpret_cast<int64_t*>(wb + W.xbsum), st);
+    if (e != E2A_OK) return e;
+    k_xcd_split<<<1, 64, 0, st>>>(pre, n, xlo);
+    E2A_LAUNCH_CHECK();
+    p.xcd_lo = xlo;
+  }
+  if (p.wg_per_xcd > kDealMaxWpx) return E2A_OK;   // cyclic deal
   const int wpx = p.wg_per_xcd;
-  const int64_t R = ((n + 7) / 8 + wpx - 1) / wpx;
+  const int64_t span = p.xcd_lo ? 2 * ((n + 7) / 8) + 2 : (n + 7) / 8;   // slots of the largest range
+  const int64_t R = (span + wpx - 1) / wpx;
   int32_t* sched = reinterpret_cast<int32_t*>(wb + W.sched);
   int32_t* sched_n = reinterpret_cast<int32_t*>(wb + W.sched_n);
-  k_deal<<<dim3(static_cast<unsigned>(R), 8), 64, 0, st>>>(p.order, p.row_ptr, n, wpx, R, sched, sched_n);
+  k_deal<<<dim3(static_cast<unsigned>(R), 8), 64, 0, st>>>(p.order, p.row_ptr, p.xcd_lo, n, wpx, R, sched,
+                                                           sched_n);
   E2A_LAUNCH_CHECK();
   p.sched = sched;
   p.sched_n = sched_n;
