@@ -1258,6 +1258,184 @@ __global__ void __launch_bounds__(256, 4) k_gemm_mfma_tr(Gemm g) {
   gemm_body_tr(g, sm);
 }
 
+// Complex pairs of products: with operands A1, A2 and B1, B2,
+//   P = aP (A1 B1 + s1 A2 B2),   Q = aQ (A1 B2 + s2 A2 B1)   (s1, s2 = +-1),
+// the shape of every m > 0 block of the SO(2) mix and of its gradients
+// (y+ = x+ W1 - x- W2, y- = x+ W2 + x- W1; dx+ = dy+ W1^T + dy- W2^T,
+// dx- = -(dy+ W2^T - dy- W1^T); dW1 += x+^T dy+ + x-^T dy-,
+// dW2 += x+^T dy- - x-^T dy+), from one read of the four operands' slices
+// instead of two launches that each read all four.  KK: A(m, k) =
+// A[m sa + k], B(k, n) = B[n sb + k] (the edge-row products, bf16 outputs,
+// one k range); TR: A(m, k) = A[m + k sa], B(k, n) = B[n + k sb] (the weight
+// products, fragments by LDS transpose reads, split-k partials).  Twice the
+// accumulators of the single products: two workgroups per CU.
+struct GemmCx {
+  const uint16_t* A1;
+  const uint16_t* A2;
+  const uint16_t* B1;
+  const uint16_t* B2;
+  int64_t sa, sb;
+  int64_t M, N, K;
+  float aP, aQ;
+  bool s1neg, s2neg;
+  uint16_t* P_bf;      // KK outputs, row stride ldc
+  uint16_t* Q_bf;
+  int64_t ldc;
+  float* P_part;       // TR: [S][M][N] partials of P and Q
+  float* Q_part;
+  bool part_acc;
+  int64_t kper;
+};
+
+constexpr size_t kCxSmemKK = 4 * 2 * (size_t)kTM * (kBK + kPad) * sizeof(uint16_t);
+constexpr size_t kCxSmemTR = 4 * 2 * (size_t)kBK * (kTM + kTrPad) * sizeof(uint16_t);
+
+template <bool TR>
+__device__ __forceinline__ void gemm_body_cx(const GemmCx& g, uint16_t* smem) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const uint32_t nx = gridDim.x, ny = gridDim.y, total = nx * ny * gridDim.z;
+  const uint32_t id = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
+  const uint32_t q8 = total / 8, r8 = total % 8, xcd = id % 8, local = id / 8;
+  const uint32_t wi = (xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8) + local;
+  const uint32_t bx = wi % nx, by = (wi / nx) % ny, bz = wi / (nx * ny);
+  const int64_t m0 = (int64_t)by * kTM, n0 = (int64_t)bx * kTM;
+  const int64_t kb = (int64_t)bz * g.kper;
+  const int64_t ke = kb + g.kper < g.K ? kb + g.kper : g.K;
+  // slice buffers: operand o (A1, A2, B1, B2), buffer b
+  constexpr int RS = TR ? kTM + kTrPad : kBK + kPad;       // row length
+  constexpr int SL = TR ? kBK * RS : kTM * RS;             // values per slice buffer
+  auto slice = [&](int o, int b) { return smem + (size_t)(2 * o + b) * SL; };
+  const uint16_t* ops[4] = {g.A1, g.A2, g.B1, g.B2};
+  u32x4 f[4][2];
+  auto fetch = [&](int64_t k0) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      const int64_t r0 = o < 2 ? m0 : n0, R = o < 2 ? g.M : g.N, st = o < 2 ? g.sa : g.sb;
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        u32x4 w = {0u, 0u, 0u, 0u};
+        if constexpr (TR) {
+          const int64_t k = k0 + (tid >> 4) + 16 * v, c = r0 + (tid & 15) * 8;
+          if (k < ke && c < R) w = *reinterpret_cast<const u32x4*>(ops[o] + c + k * st);
+        } else {
+          const int idx = tid + 256 * v;
+          const int64_t r = r0 + (idx >> 2), k = k0 + (idx & 3) * 8;
+          if (r < R && k < ke) w = *reinterpret_cast<const u32x4*>(ops[o] + r * st + k);
+        }
+        f[o][v] = w;
+      }
+    }
+  };
+  auto commit = [&](int b) {
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+      uint16_t* d = slice(o, b);
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        if constexpr (TR) {
+          *reinterpret_cast<u32x4*>(d + ((tid >> 4) + 16 * v) * RS + (tid & 15) * 8) = f[o][v];
+        } else {
+          const int idx = tid + 256 * v;
+          *reinterpret_cast<u32x4*>(d + (idx >> 2) * RS + (idx & 3) * 8) = f[o][v];
+        }
+      }
+    }
+  };
+  auto frag = [&](int o, int b, int ks, int c0) -> bf16x8 {
+    const uint16_t* d = slice(o, b);
+    if constexpr (TR) {
+      return tr_frag(reinterpret_cast<const uint16_t(*)[kTM + kTrPad]>(d), ks, c0, lane);
+    } else {
+      return *reinterpret_cast<const bf16x8*>(d + (c0 + (lane & 31)) * RS + ks + 8 * (lane >> 5));
+    }
+  };
+  auto neg = [](bf16x8 x) {
+    u32x4 u = __builtin_bit_cast(u32x4, x);
+    u ^= 0x80008000u;
+    return __builtin_bit_cast(bf16x8, u);
+  };
+  f32x16 accP[2][2] = {}, accQ[2][2] = {};
+  int buf = 0;
+  if (kb < ke) {
+    fetch(kb);
+    commit(0);
+  }
+  __syncthreads();
+  for (int64_t k0 = kb; k0 < ke; k0 += kBK) {
+    const bool more = k0 + kBK < ke;
+    if (more) fetch(k0 + kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 16) {
+      bf16x8 a1[2], a2[2], b1[2], b2[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a1[t] = frag(0, buf, ks, wm * 64 + t * 32);
+        a2[t] = frag(1, buf, ks, wm * 64 + t * 32);
+        b1[t] = frag(2, buf, ks, wn * 64 + t * 32);
+        b2[t] = frag(3, buf, ks, wn * 64 + t * 32);
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bf16x8 b2s = g.s1neg ? neg(b2[j]) : b2[j];
+        const bf16x8 b1s = g.s2neg ? neg(b1[j]) : b1[j];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          accP[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], accP[i][j], 0, 0, 0);
+          accP[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[i], b2s, accP[i][j], 0, 0, 0);
+          accQ[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b2[j], accQ[i][j], 0, 0, 0);
+          accQ[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2[i], b1s, accQ[i][j], 0, 0, 0);
+        }
+      }
+    }
+    if (more) commit(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+  // register r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t m = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t n = n0 + wn * 64 + j * 32 + (lane & 31);
+        if (m < g.M && n < g.N) {
+          const float vp = g.aP * accP[i][j][r], vq = g.aQ * accQ[i][j][r];
+          if constexpr (TR) {
+            float* pp = g.P_part + ((int64_t)bz * g.M + m) * g.N + n;
+            float* pq = g.Q_part + ((int64_t)bz * g.M + m) * g.N + n;
+            *pp = g.part_acc ? *pp + vp : vp;
+            *pq = g.part_acc ? *pq + vq : vq;
+          } else {
+            g.P_bf[m * g.ldc + n] = f32_to_bf16_rne(vp);
+            g.Q_bf[m * g.ldc + n] = f32_to_bf16_rne(vq);
+          }
+        }
+      }
+}
+
+template <bool TR>
+__global__ void __launch_bounds__(256, 2) k_gemm_cx(GemmCx g) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t cx_smem[];
+  gemm_body_cx<TR>(g, cx_smem);
+}
+
+// One complex pair over S k ranges (TR: partials; KK: S = 1).
+template <bool TR>
+e2a_status launch_gemm_cx(const GemmCx& g, int S, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>((g.N + kTM - 1) / kTM), static_cast<unsigned>((g.M + kTM - 1) / kTM),
+                  static_cast<unsigned>(S));
+  const size_t smem = TR ? kCxSmemTR : kCxSmemKK;
+  E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_cx<TR>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)));
+  k_gemm_cx<TR><<<grid, 256, smem, st>>>(g);
+  E2A_LAUNCH_CHECK();
+  return E2A_OK;
+}
+
 // Any layouts, three workgroups per CU (168 VGPRs).
 __global__ void __launch_bounds__(256, 3) k_gemm_mfma(Gemm g) {
   __shared__ __attribute__((aligned(16))) GemmSmem sm;
@@ -1408,16 +1586,26 @@ e2a_status gemm(Gemm g, int64_t part_floats, hipStream_t st) {
 
 // The SO(2) weight gradients sum over every batch: each of the 2L + 1
 // matrices keeps dw_splits(m) partials for the whole call, which every batch's
-// products add to, and one reduction at the end.  These products run on
+// products add to, and one reduction at the end.  The m = 0 products run on
 // k_gemm_mfma_tr, four workgroups per CU (122 VGPRs a lane, 36 KB of LDS
 // each), 1024 on the 256 CUs, and a launch with a few workgroups more than
 // that takes a second round: the split count fills the 1024 slots without
-// passing them (tiles x S <= 1024).
+// passing them (tiles x S <= 1024).  The m > 0 pairs (bf16) run on
+// k_gemm_cx<true>, two workgroups per CU: dw_splits_pair fills 512 slots.
 constexpr int64_t kGemmSlots = 1024;
 int64_t dw_splits(int L, int C, int m) {
   const int64_t km = (int64_t)(L + 1 - m) * C;
   const int64_t t = (km + kTM - 1) / kTM;
   const int64_t S = kGemmSlots / (t * t);
+  return S < 1 ? 1 : S;
+}
+// The complex-pair kernel (m > 0, bf16) runs two workgroups per CU: 512
+// slots, and as many k ranges as fill them (at most dw_splits, which sizes
+// the partial buffers).
+int64_t dw_splits_pair(int L, int C, int m) {
+  const int64_t km = (int64_t)(L + 1 - m) * C;
+  const int64_t t = (km + kTM - 1) / kTM;
+  const int64_t S = kGemmSlots / 2 / (t * t);
   return S < 1 ? 1 : S;
 }
 
@@ -1626,6 +1814,25 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       const T* Xm = Xp + bl.B * km;
       float* Ym = Yp + bl.B * km;
       const T* W2 = W1 + km * km;
+      if (yb) {
+        // y+ = x+ W1 - x- W2 and y- = x+ W2 + x- W1 from one read of the four slices
+        GemmCx g{};
+        g.A1 = reinterpret_cast<const uint16_t*>(Xp);
+        g.A2 = reinterpret_cast<const uint16_t*>(Xm);
+        g.B1 = reinterpret_cast<const uint16_t*>(W1);
+        g.B2 = reinterpret_cast<const uint16_t*>(W2);
+        g.sa = g.sb = km;
+        g.M = nb;
+        g.N = g.K = g.kper = km;
+        g.aP = g.aQ = 1.0f;
+        g.s1neg = true;
+        g.P_bf = reinterpret_cast<uint16_t*>(wb + W.Y) + bl.moff[m];
+        g.Q_bf = g.P_bf + bl.B * km;
+        g.ldc = km;
+        e = launch_gemm_cx<false>(g, 1, st);
+        if (e != E2A_OK) return e;
+        continue;
+      }
       if (kPairs && km % kBK == 0) {
         // one launch per output: Yp = [Xp | Xm] [W1; -W2], Ym = [Xp | Xm] [W2; W1]
         for (int t = 0; t < 2; ++t) {
@@ -1673,6 +1880,27 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         // A(m', k) = X[k][m'] (transposed rows), B(k, n) = dY[k][n]
         const T* Xm = Xp + bl.B * km;
         const T* DYm = DYp + bl.B * km;
+        if (kPairs && m > 0) {
+          // dW1 (+)= x+^T dy+ + x-^T dy-, dW2 (+)= x+^T dy- - x-^T dy+ in one launch
+          GemmCx g{};
+          g.A1 = reinterpret_cast<const uint16_t*>(Xp);
+          g.A2 = reinterpret_cast<const uint16_t*>(Xm);
+          g.B1 = reinterpret_cast<const uint16_t*>(DYp);
+          g.B2 = reinterpret_cast<const uint16_t*>(DYm);
+          g.sa = g.sb = km;
+          g.M = g.N = km;
+          g.K = nb;
+          g.aP = g.aQ = 1.0f;
+          g.s2neg = true;
+          g.P_part = p1;
+          g.Q_part = p2;
+          g.part_acc = e0 > 0;
+          const int64_t Sp = dw_splits_pair(L, C, m);
+          g.kper = ((nb + Sp - 1) / Sp + kBK - 1) / kBK * kBK;
+          const e2a_status e = launch_gemm_cx<true>(g, static_cast<int>(Sp), st);
+          if (e != E2A_OK) return e;
+          continue;
+        }
         if (kPairs && nb % kBK == 0) {
           // one launch per matrix: p1 (+)= [Xp; Xm]^T [dYp; dYm], p2 (+)= [Xp; Xm]^T [dYm; -dYp]
           for (int t = 0; t < (m == 0 ? 1 : 2); ++t) {
@@ -1721,6 +1949,26 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         const T* DYm = DYp + bl.B * km;
         const T* W2 = W1 + km * km;
         float* dXm = dXp + bl.B * km;
+        if (yb) {
+          // dx+ = dy+ W1^T + dy- W2^T and dx- = -(dy+ W2^T - dy- W1^T) in one launch
+          GemmCx g{};
+          g.A1 = reinterpret_cast<const uint16_t*>(DYp);
+          g.A2 = reinterpret_cast<const uint16_t*>(DYm);
+          g.B1 = reinterpret_cast<const uint16_t*>(W1);
+          g.B2 = reinterpret_cast<const uint16_t*>(W2);
+          g.sa = g.sb = km;
+          g.M = nb;
+          g.N = g.K = g.kper = km;
+          g.aP = 1.0f;
+          g.aQ = -1.0f;
+          g.s2neg = true;
+          g.P_bf = reinterpret_cast<uint16_t*>(wb + W.dX) + bl.moff[m];
+          g.Q_bf = g.P_bf + bl.B * km;
+          g.ldc = km;
+          e = launch_gemm_cx<false>(g, 1, st);
+          if (e != E2A_OK) return e;
+          continue;
+        }
         if (kPairs && km % kBK == 0) {
           // one launch per output: dXp = [dYp | dYm] [W1^T; W2^T], dXm = [dYm | dYp] [W1^T; -W2^T]
           for (int t = 0; t < 2; ++t) {
@@ -1802,7 +2050,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       for (int w = 0; w < (m == 0 ? 1 : 2); ++w) {
         Gemm r = make_gemm(nullptr, 0, 0, nullptr, 0, 0, km, km, 0, 1.0f, pl.w_so2 + woff[m] + w * km * km, km,
                            const_cast<float*>(dwp));
-        r.S = static_cast<int>(S);
+        // the k ranges the batches used (the buffers keep S slots per matrix)
+        r.S = static_cast<int>(kPairs && m > 0 ? dw_splits_pair(L, C, m) : S);
         r.overwrite = true;
         const e2a_status e = reduce_parts(r, st);
         if (e != E2A_OK) return e;
