@@ -1915,6 +1915,18 @@ e2a_status launch_radial_typed(const BwdPlan& pl, float* w_rad, hipStream_t st) 
 
 }  // namespace
 
+const uint16_t* mfma_grad_bf16(const void* mfma_ws, int64_t n, int L) {
+  size_t off = 0;
+  switch (L) {
+    case 1: off = mfma_ws_layout<1>(n, true).gbf; break;
+    case 2: off = mfma_ws_layout<2>(n, true).gbf; break;
+    case 3: off = mfma_ws_layout<3>(n, true).gbf; break;
+    case 4: off = mfma_ws_layout<4>(n, true).gbf; break;
+    default: return nullptr;
+  }
+  return reinterpret_cast<const uint16_t*>(static_cast<const char*>(mfma_ws) + off);
+}
+
 e2a_status launch_radial_mfma(const BwdPlan& pl, float* w_rad, hipStream_t s) {
   switch (pl.a->L) {
     case 1: return launch_radial_typed<1>(pl, w_rad, s);

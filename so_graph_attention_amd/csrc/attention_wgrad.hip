@@ -90,6 +90,13 @@ __global__ void k_transpose_block(const T* __restrict__ w, int64_t km, T* __rest
   wt[n * km + k] = w[t];
 }
 
+// G in bf16, round to nearest even (the force kernel's operand, when the
+// call has no copy from its feature gradient).
+__global__ void k_to_bf16(const float* __restrict__ g, uint16_t* __restrict__ out, int64_t n) {
+  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (i < n) out[i] = f32_to_bf16_rne(g[i]);
+}
+
 __global__ void k_zero(float* __restrict__ p, int64_t n) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0.0f;
@@ -492,6 +499,7 @@ struct ForceParams {
   const void* Y;        // batch tensor: y = SO2(x) (fp32, or bf16 for the matrix-core kernel)
   const void* dX;       // batch tensor: dx = SO2^T(dy) (the same type)
   const float* rbfd;    // [B][8]: d e_k / d r
+  const uint16_t* gbf;  // G in bf16 [N, K, C] (the matrix-core kernel)
   float* gedge;         // [E][3]: dL/dr of every edge
   float box[3];
   int periodic;
@@ -708,8 +716,9 @@ __global__ void __launch_bounds__(64 * kForceEdges) k_wg_force(ForceParams p, in
 // + 7) from global memory; only pairs within one degree are used.  The
 // factors rho alpha and (d rho / d r) alpha of every (l, c) are formed per
 // edge in LDS from the radial weights, which the workgroup stages once for
-// its 32 edges.  y and dx arrive in bf16; rho alpha y and G_i are rounded to
-// bf16 for the products, whose sums are fp32.  Each wave works through its
+// its 32 edges.  y and dx arrive in bf16, and G_i as the bf16 copy (round
+// to nearest even) the call's feature gradient made or run_wgrad makes;
+// rho alpha y is rounded to bf16 for the products, whose sums are fp32.  Each wave works through its
 // own edges with no workgroup barrier after the staging, so that the waves'
 // latency-bound set-up and their loads overlap.
 constexpr int kFmWaves = 4, kFmIters = 8;   // 32 edges per workgroup, one per wave at a time
@@ -780,23 +789,20 @@ __global__ void __launch_bounds__(64 * kFmWaves, 2) k_wg_force_mfma(ForceParams 
     const uint16_t* dxr = dXb + bi;
     const uint16_t* yr = Yb + bi;
     const uint16_t* hr = feat + ((int64_t)j * K + rowc) * C;
-    const float* gr = p.grad + ((int64_t)i * K + rowc) * C;
+    const uint16_t* gr = p.gbf + ((int64_t)i * K + rowc) * C;
     const float* ra = tab + lr * C;
     f32x16 accT = {}, accS = {};
     // One step: 16 channels from c0 = 16 t + 8 (lane / 32) of the loaded rows.
-    auto step = [&](int c0, const bf16x8& adx, const bf16x8& bh, const u32x4v& yw, const f32x4v& g0,
-                    const f32x4v& g1) {
+    auto step = [&](int c0, const bf16x8& adx, const bf16x8& bh, const u32x4v& yw, const bf16x8& bg) {
       const f32x4v r0 = *reinterpret_cast<const f32x4v*>(ra + c0);
       const f32x4v r1 = *reinterpret_cast<const f32x4v*>(ra + c0 + 4);
       const f32x4v d0 = *reinterpret_cast<const f32x4v*>(ra + LC + c0);
       const f32x4v d1 = *reinterpret_cast<const f32x4v*>(ra + LC + c0 + 4);
-      f32x8v yv, gv, rv8, dv8;
+      f32x8v yv, rv8, dv8;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         yv[2 * q] = __uint_as_float(yw[q] << 16);
         yv[2 * q + 1] = __uint_as_float(yw[q] & 0xffff0000u);
-        gv[q] = g0[q];
-        gv[4 + q] = g1[q];
         rv8[q] = r0[q];
         rv8[4 + q] = r1[q];
         dv8[q] = d0[q];
@@ -804,7 +810,6 @@ __global__ void __launch_bounds__(64 * kFmWaves, 2) k_wg_force_mfma(ForceParams 
       }
       const bf16x8 a1 = __builtin_convertvector(yv * rv8, bf16x8);
       const bf16x8 a2 = __builtin_convertvector(yv * dv8, bf16x8);
-      const bf16x8 bg = __builtin_convertvector(gv, bf16x8);
       accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(adx, bh, accT, 0, 0, 0);
       accT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bg, accT, 0, 0, 0);
       accS = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a2, bg, accS, 0, 0, 0);
@@ -819,25 +824,23 @@ __global__ void __launch_bounds__(64 * kFmWaves, 2) k_wg_force_mfma(ForceParams 
       for (int t0 = 0; t0 < NS; t0 += NB) {
         bf16x8 ldx[NB], lh[NB];
         u32x4v ly[NB];
-        f32x4v lg0[NB], lg1[NB];
+        bf16x8 lg[NB];
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           const int c0 = 16 * (t0 + t) + 8 * hk;
           ldx[t] = *reinterpret_cast<const bf16x8*>(dxr + c0);
           lh[t] = *reinterpret_cast<const bf16x8*>(hr + c0);
           ly[t] = *reinterpret_cast<const u32x4v*>(yr + c0);
-          lg0[t] = *reinterpret_cast<const f32x4v*>(gr + c0);
-          lg1[t] = *reinterpret_cast<const f32x4v*>(gr + c0 + 4);
+          lg[t] = *reinterpret_cast<const bf16x8*>(gr + c0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int t = 0; t < NB; ++t) step(16 * (t0 + t) + 8 * hk, ldx[t], lh[t], ly[t], lg0[t], lg1[t]);
+        for (int t = 0; t < NB; ++t) step(16 * (t0 + t) + 8 * hk, ldx[t], lh[t], ly[t], lg[t]);
       }
     } else {
       for (int c0 = 8 * hk; c0 < C; c0 += 16)
         step(c0, *reinterpret_cast<const bf16x8*>(dxr + c0), *reinterpret_cast<const bf16x8*>(hr + c0),
-             *reinterpret_cast<const u32x4v*>(yr + c0), *reinterpret_cast<const f32x4v*>(gr + c0),
-             *reinterpret_cast<const f32x4v*>(gr + c0 + 4));
+             *reinterpret_cast<const u32x4v*>(yr + c0), *reinterpret_cast<const bf16x8*>(gr + c0));
     }
     // register r holds (row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32)
     float T3[3] = {0.0f, 0.0f, 0.0f};
@@ -1641,6 +1644,7 @@ Gemm make_gemm(const void* A, int64_t sam, int64_t sak, const void* B, int64_t s
 struct WgWs {
   size_t src, X, GT, Y, rbf, part, dwpart, rhopart, wt;
   size_t rbfd, alpha, dX, gedge;   // position gradient only (dX also holds dyhat for the dW_rad batches)
+  size_t gbf;                      // the cotangent in bf16 for the matrix-core force kernel
   size_t total;
   int64_t B, part_floats;
 };
@@ -1669,10 +1673,10 @@ WgWs wg_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   w.alpha = take(sizeof(float) * (size_t)B * H);
   w.dX = take(sizeof(float) * (size_t)per);
   w.gedge = take(sizeof(float) * 3 * (size_t)(e > 0 ? e : 1));
+  w.gbf = take(sizeof(uint16_t) * (size_t)n * (L + 1) * (L + 1) * C);
   w.total = off;
   w.B = B;
   w.part_floats = pf;
-  (void)n;
   return w;
 }
 
@@ -1746,6 +1750,13 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     }
     return g;
   };
+  if (pl.pos && yb && !pl.grad_bf) {
+    // the matrix-core force kernel reads G in bf16; this call has no copy yet
+    const int64_t cnt = n * K * C;
+    k_to_bf16<<<static_cast<unsigned>((cnt + 255) / 256), 256, 0, st>>>(pl.grad_out,
+                                                                       reinterpret_cast<uint16_t*>(wb + W.gbf), cnt);
+    E2A_LAUNCH_CHECK();
+  }
   float* rbf = reinterpret_cast<float*>(wb + W.rbf);
   const BatchLayout bl = batch_layout(W.B, L, C);
   const T* wso2 = static_cast<const T*>(a->w_so2);
@@ -2000,6 +2011,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
       fp.Y = wb + W.Y;
       fp.dX = wb + W.dX;
       fp.rbfd = reinterpret_cast<const float*>(wb + W.rbfd);
+      fp.gbf = pl.grad_bf ? pl.grad_bf : reinterpret_cast<const uint16_t*>(wb + W.gbf);
       fp.gedge = reinterpret_cast<float*>(wb + W.gedge);
       for (int d = 0; d < 3; ++d) fp.box[d] = pl.box[d];
       fp.periodic = pl.periodic;

@@ -99,6 +99,13 @@ e2a_status check_alignment(const e2a_attn_args* a, const void* grad_out) {
   return E2A_OK;
 }
 
+// The matrix-core build covers the call (the feature gradient then runs the
+// fused kernel's passes).
+bool rad_mfma_path(const e2a_attn_args* a) {
+  const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
+  return a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
+}
+
 e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
   if (!a) return fail(E2A_ERR_INVALID_ARG, "args is NULL");
   if (a->n_atoms < 0 || a->n_atoms > INT32_MAX) return fail(E2A_ERR_INVALID_ARG, "n_atoms out of range");
@@ -563,6 +570,8 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   wp.w_rad = rad_mfma ? nullptr : grad_w_rad;
   wp.w_so2 = grad_w_so2;
   wp.pos = grad_pos;
+  // the matrix-core feature gradient left the cotangent in bf16 (k_prep_grad)
+  if ((grad_feat || want_qk) && rad_mfma_path(a)) wp.grad_bf = mfma_grad_bf16(base + ws.b.mfma, a->n_atoms, a->L);
   wp.ws = base + ws.wg;
   wp.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) wp.box[d] = a->box ? a->box[d] : 0.0f;

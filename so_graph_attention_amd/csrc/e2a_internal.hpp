@@ -89,6 +89,9 @@ e2a_status launch_attention_mfma(const AttnPlan& p, hipStream_t s);
 size_t mfma_packed_bytes(int L);
 e2a_status pack_so2_mfma(const void* w_so2, void* out, int L, hipStream_t s);
 size_t order_workspace_bytes(int64_t n);
+// The bf16 copy of the cotangent the matrix-core feature gradient leaves in
+// its workspace (mfma_ws of a BwdPlan).
+const uint16_t* mfma_grad_bf16(const void* mfma_ws, int64_t n, int L);
 e2a_status destination_order(const float* pos, int64_t n, int32_t* order, void* ws, hipStream_t s);
 // Feature gradient (attention_backward.hip).
 struct BwdPlan {
@@ -148,6 +151,7 @@ struct WgradPlan {
   float* w_rad;
   float* w_so2;
   float* pos;              // dL/dx [N, 3] (optional)
+  const uint16_t* grad_bf; // G in bf16 (round to nearest even) if the call already made it, else null
   void* ws;                // wgrad_workspace_bytes(...)
   float box[3];
   int periodic;
