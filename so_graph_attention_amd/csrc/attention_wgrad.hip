@@ -1891,8 +1891,9 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         // A(m', k) = X[k][m'] (transposed rows), B(k, n) = dY[k][n]
         const T* Xm = Xp + bl.B * km;
         const T* DYm = DYp + bl.B * km;
-        if (kPairs && m > 0) {
+        if (kPairs && m > 0 && km % 8 == 0) {
           // dW1 (+)= x+^T dy+ + x-^T dy-, dW2 (+)= x+^T dy- - x-^T dy+ in one launch
+          // (16-byte rows: km a multiple of 8)
           GemmCx g{};
           g.A1 = reinterpret_cast<const uint16_t*>(Xp);
           g.A2 = reinterpret_cast<const uint16_t*>(Xm);
@@ -2063,7 +2064,7 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         Gemm r = make_gemm(nullptr, 0, 0, nullptr, 0, 0, km, km, 0, 1.0f, pl.w_so2 + woff[m] + w * km * km, km,
                            const_cast<float*>(dwp));
         // the k ranges the batches used (the buffers keep S slots per matrix)
-        r.S = static_cast<int>(kPairs && m > 0 ? dw_splits_pair(L, C, m) : S);
+        r.S = static_cast<int>(kPairs && m > 0 && km % 8 == 0 ? dw_splits_pair(L, C, m) : S);
         r.overwrite = true;
         const e2a_status e = reduce_parts(r, st);
         if (e != E2A_OK) return e;

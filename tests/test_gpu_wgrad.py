@@ -122,6 +122,23 @@ def test_wgrad_bf16_tiny_full(B, L):
     check(got, oracle_wgrad(w, rp, col, G), TOL_BF16, f"bf16 L={L}")
 
 
+@pytest.mark.parametrize("L,C,H", [(2, 12, 3), (3, 24, 3)])
+def test_wgrad_bf16_off_matrix_core_shapes(B, L, C, H):
+    """bf16 storage with C not a multiple of 32 (the scalar layer kernels,
+    the generic GEMM for y and dx, the scalar force kernel): C = 12 has
+    blocks of 12 (L + 1 - m) channels, some not a multiple of 8, which must
+    take the element-by-element GEMM paths; C = 24 runs the weight products
+    as complex pairs with ragged tiles.  Every weight gradient and every
+    position gradient against the oracle."""
+    log(f"[wgrad] bf16 L={L} C={C} H={H}")
+    w = make_config("tiny", L=L, C=C, H=H, dtype="bf16")
+    rp, col, d, G = setup(w, seed=83)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, pos_grad=True)
+    check(got, oracle_wgrad(w, rp, col, G), TOL_BF16, f"bf16 L={L} C={C}")
+    check_pos(got["pos"], oracle_pos(w, rp, col, G), TOL_BF16, f"bf16 L={L} C={C}")
+
+
 def test_wgrad_bf16_drug_sparse_cotangent(B):
     """The drug-like workload (347k edges: 6 batches), with the MFMA forward's
     log-normaliser; G nonzero on 24 sampled destinations."""
