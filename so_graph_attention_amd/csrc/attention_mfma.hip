@@ -1305,11 +1305,22 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
 // and n = (l_out - m) C + 32 wave + lane % 32.  With TR set, the image of the
 // transposed mix the value pass needs: W0^T for m = 0, and W1^T, -W2^T for
 // m > 0 (so that the kernel's complex product gives dx_+ = dy_+ W1^T + dy_- W2^T
-// and dx_- = -dy_+ W2^T + dy_- W1^T).
+// and dx_- = -dy_+ W2^T + dy_- W1^T).  With wrad set, the first (L+1) C
+// threads also pack W_rad into radout (k_pack_rad's work, in the same launch).
+template <int L>
+__device__ __forceinline__ void pack_rad_entry(const uint16_t* __restrict__ w, u32x4* __restrict__ out, int v) {
+  uint32_t b[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) b[q] = w[q * (L + 1) * kC + v];
+  out[v] = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+}
+
 template <int L, bool TR>
-__global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ out) {
+__global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ out,
+                           const uint16_t* __restrict__ wrad = nullptr, u32x4* __restrict__ radout = nullptr) {
   using S = Shape<L>;
   const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (wrad && v < (L + 1) * kC) pack_rad_entry<L>(wrad, radout, static_cast<int>(v));
   if (v >= S::wtotal()) return;
   int m = 0;
   while (m < L && v >= S::woff(m + 1)) ++m;
@@ -1343,11 +1354,7 @@ __global__ void k_pack_so2(const uint16_t* __restrict__ w, bf16x8* __restrict__ 
 template <int L>
 __global__ void k_pack_rad(const uint16_t* __restrict__ w, u32x4* __restrict__ out) {
   const int v = blockIdx.x * blockDim.x + threadIdx.x;
-  if (v >= (L + 1) * kC) return;
-  uint32_t b[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) b[q] = w[q * (L + 1) * kC + v];
-  out[v] = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+  if (v < (L + 1) * kC) pack_rad_entry<L>(w, out, v);
 }
 
 // The balanced deal of destinations to the workgroups of an XCD sorts each
@@ -1457,50 +1464,83 @@ __device__ __forceinline__ uint32_t spread3(uint32_t v) {
   return r;
 }
 
-__global__ void k_ord_keys(const float* __restrict__ pos, int64_t n, const float* __restrict__ bbox,
-                           int32_t* __restrict__ key, int32_t* __restrict__ val) {
-  const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  uint32_t c[3];
+// Morton keys of one sort block (kSortBlock atoms, 256 threads) with the
+// first radix pass's digit counts of the block, hist[d * nblk + b].  Each
+// block first reduces the bounding box from the nparts partial boxes
+// (min and max are exact in any order, so every block gets the same box),
+// and the grid clears hist_next, which the first scatter fills.
+__global__ void __launch_bounds__(256) k_ord_keys(const float* __restrict__ pos, int64_t n,
+                                                  const float* __restrict__ bbox_part, int nparts,
+                                                  int32_t* __restrict__ key, int32_t* __restrict__ val,
+                                                  int32_t* __restrict__ hist, int32_t* __restrict__ hist_next,
+                                                  int64_t nblk) {
+  __shared__ float bmin[3][256], bmax[3][256];
+  __shared__ int32_t h[kRadix];
+  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) h[d] = 0;
+  {
+    float mn[3] = {INFINITY, INFINITY, INFINITY}, mx[3] = {-INFINITY, -INFINITY, -INFINITY};
+    for (int b = threadIdx.x; b < nparts; b += blockDim.x)
 #pragma unroll
-  for (int d = 0; d < 3; ++d) {
-    const float ext = fmaxf(bbox[3 + d] - bbox[d], 1e-6f);
-    float f = (pos[3 * i + d] - bbox[d]) / ext * float(1 << kOrderBits);
-    f = fminf(fmaxf(f, 0.0f), float((1 << kOrderBits) - 1));
-    c[d] = static_cast<uint32_t>(f);
+      for (int d = 0; d < 3; ++d) {
+        mn[d] = fminf(mn[d], bbox_part[8 * b + d]);
+        mx[d] = fmaxf(mx[d], bbox_part[8 * b + 3 + d]);
+      }
+#pragma unroll
+    for (int d = 0; d < 3; ++d) { bmin[d][threadIdx.x] = mn[d]; bmax[d][threadIdx.x] = mx[d]; }
+    __syncthreads();
+    for (int st = 128; st > 0; st >>= 1) {
+      if (threadIdx.x < st)
+#pragma unroll
+        for (int d = 0; d < 3; ++d) {
+          bmin[d][threadIdx.x] = fminf(bmin[d][threadIdx.x], bmin[d][threadIdx.x + st]);
+          bmax[d][threadIdx.x] = fmaxf(bmax[d][threadIdx.x], bmax[d][threadIdx.x + st]);
+        }
+      __syncthreads();
+    }
   }
-  key[i] = static_cast<int32_t>(spread3(c[0]) | (spread3(c[1]) << 1) | (spread3(c[2]) << 2));
-  val[i] = static_cast<int32_t>(i);
+  for (int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; t < kRadix * nblk;
+       t += (int64_t)gridDim.x * blockDim.x)
+    hist_next[t] = 0;
+  const int64_t base = blockIdx.x * (int64_t)kSortBlock;
+  for (int r = threadIdx.x; r < kSortBlock; r += blockDim.x) {
+    const int64_t i = base + r;
+    if (i >= n) break;
+    uint32_t c[3];
+#pragma unroll
+    for (int d = 0; d < 3; ++d) {
+      const float lo = bmin[d][0];
+      const float ext = fmaxf(bmax[d][0] - lo, 1e-6f);
+      float f = (pos[3 * i + d] - lo) / ext * float(1 << kOrderBits);
+      f = fminf(fmaxf(f, 0.0f), float((1 << kOrderBits) - 1));
+      c[d] = static_cast<uint32_t>(f);
+    }
+    const int32_t k = static_cast<int32_t>(spread3(c[0]) | (spread3(c[1]) << 1) | (spread3(c[2]) << 2));
+    key[i] = k;
+    val[i] = static_cast<int32_t>(i);
+    atomicAdd(&h[k & (kRadix - 1)], 1);
+  }
+  __syncthreads();
+  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
 }
 
 // LSD radix sort of (Morton key, atom index) pairs, one kRadixBits digit per
 // pass.  The sort is stable, so the order (and with it the way atoms share
 // edge chunks in the layer kernel) is the same on every launch.
 //
-// Per-block digit counts, digit-major: hist[d * nblk + b].
-__global__ void k_radix_hist(const int32_t* __restrict__ key, int64_t n, int shift, int32_t* __restrict__ hist,
-                             int64_t nblk) {
-  __shared__ int32_t h[kRadix];
-  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) h[d] = 0;
-  __syncthreads();
-  const int64_t base = blockIdx.x * (int64_t)kSortBlock;
-  for (int t = threadIdx.x; t < kSortBlock; t += blockDim.x) {
-    const int64_t i = base + t;
-    if (i < n) atomicAdd(&h[(key[i] >> shift) & (kRadix - 1)], 1);
-  }
-  __syncthreads();
-  for (int d = threadIdx.x; d < kRadix; d += blockDim.x) hist[(int64_t)d * nblk + blockIdx.x] = h[d];
-}
-
 // Stable scatter: element i of block b (digit d) goes to off[d * nblk + b]
 // plus the number of earlier elements of the block with digit d.  The block's
 // 1024 elements go in 4 rounds of 256 in index order; within a round the waves
 // take turns, and inside a wave the lanes holding the same digit are found with
 // one ballot per digit bit.
+//
+// With hist_next set, each element also counts its next digit for the sort
+// block it lands in, hist_next[d' * nblk + at / kSortBlock] (the next pass's
+// counts, so no separate counting launch is needed; hist_next starts at 0).
 __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict__ key_in,
                                                        const int32_t* __restrict__ val_in, int64_t n, int shift,
                                                        const int32_t* __restrict__ off, int64_t nblk,
-                                                       int32_t* __restrict__ key_out, int32_t* __restrict__ val_out) {
+                                                       int32_t* __restrict__ key_out, int32_t* __restrict__ val_out,
+                                                       int32_t* __restrict__ hist_next) {
   __shared__ int32_t next[kRadix];
   for (int d = threadIdx.x; d < kRadix; d += blockDim.x) next[d] = off[(int64_t)d * nblk + blockIdx.x];
   __syncthreads();
@@ -1526,6 +1566,8 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
         const int32_t at = next[d] + rank;
         key_out[at] = k;
         val_out[at] = v;
+        if (hist_next)
+          atomicAdd(&hist_next[(int64_t)((k >> (shift + kRadixBits)) & (kRadix - 1)) * nblk + at / kSortBlock], 1);
       }
       __syncthreads();
       if (wave == w && valid && rank == 0) next[d] += count;
@@ -1535,7 +1577,7 @@ __global__ void __launch_bounds__(256) k_radix_scatter(const int32_t* __restrict
 }
 
 struct MfmaWs {
-  size_t w, rad, order, key, key2, val2, hist, off, bsum, bbox, bbox_part;
+  size_t w, rad, order, key, key2, val2, hist, hist2, off, bsum, bbox_part;
   size_t sched, sched_n;   // the balanced deal: per-workgroup rows of slots and their lengths
   size_t xdeg, xpre, xbsum, xlo;   // the XCD ranges split by edges
   size_t wt, gbf, delta;   // feature gradient only: transposed image, bf16 cotangent, delta,
@@ -1560,9 +1602,9 @@ MfmaWs mfma_ws_layout(int64_t n, bool backward) {
   m.key2 = take(sizeof(int32_t) * n);
   m.val2 = take(sizeof(int32_t) * n);
   m.hist = take(sizeof(int32_t) * kRadix * sort_blocks(n));
+  m.hist2 = take(sizeof(int32_t) * kRadix * sort_blocks(n));
   m.off = take(sizeof(int32_t) * (kRadix * sort_blocks(n) + 1));   // the scan also writes the total
   m.bsum = take(sizeof(int64_t) * scan_bsum_count(kRadix * sort_blocks(n)));
-  m.bbox = take(8 * sizeof(float));
   m.bbox_part = take(sizeof(float) * kBboxPartialFloats);
   // a range of the edge split holds at most 2 ceil(n / 8) + 2 slots
   m.sched = take(sizeof(int32_t) * (2 * n + 32 + 8 * kDealMaxWpx));
@@ -1651,21 +1693,19 @@ __global__ void __launch_bounds__(1024) k_grad_norm(const float* __restrict__ gs
 // order (and with it which atoms share edge chunks) is the same on every
 // launch.  `order` and the scratch come from the layout W.
 e2a_status spatial_order(const float* pos, int64_t n, const MfmaWs& W, char* wb, int32_t* order, hipStream_t st) {
+  if (n == 0) return E2A_OK;
   int32_t* key = reinterpret_cast<int32_t*>(wb + W.key);
   int32_t* key2 = reinterpret_cast<int32_t*>(wb + W.key2);
   int32_t* val2 = reinterpret_cast<int32_t*>(wb + W.val2);
   int32_t* hist = reinterpret_cast<int32_t*>(wb + W.hist);
+  int32_t* hist2 = reinterpret_cast<int32_t*>(wb + W.hist2);
   int32_t* off = reinterpret_cast<int32_t*>(wb + W.off);
   int64_t* bsum = reinterpret_cast<int64_t*>(wb + W.bsum);
-  float* bbox = reinterpret_cast<float*>(wb + W.bbox);
   float* bbox_part = reinterpret_cast<float*>(wb + W.bbox_part);
-  const int64_t nb = (n + 255) / 256;
   const int64_t nblk = sort_blocks(n);
-  {
-    const e2a_status sb = launch_bbox(pos, n, bbox_part, bbox, st);
-    if (sb != E2A_OK) return sb;
-  }
-  k_ord_keys<<<nb, 256, 0, st>>>(pos, n, bbox, key, order);
+  const int nparts = launch_bbox_partial(pos, n, bbox_part, st);
+  E2A_LAUNCH_CHECK();
+  k_ord_keys<<<nblk, 256, 0, st>>>(pos, n, bbox_part, nparts, key, order, hist, hist2, nblk);
   E2A_LAUNCH_CHECK();
   for (int pass = 0; pass < 2; ++pass) {
     const int shift = pass * kRadixBits;
@@ -1673,11 +1713,9 @@ e2a_status spatial_order(const float* pos, int64_t n, const MfmaWs& W, char* wb,
     const int32_t* vin = pass == 0 ? order : val2;
     int32_t* kout = pass == 0 ? key2 : key;
     int32_t* vout = pass == 0 ? val2 : order;
-    k_radix_hist<<<nblk, 256, 0, st>>>(kin, n, shift, hist, nblk);
-    E2A_LAUNCH_CHECK();
-    e2a_status ss = exclusive_scan_i32(hist, kRadix * nblk, off, bsum, st);
+    e2a_status ss = exclusive_scan_i32(pass == 0 ? hist : hist2, kRadix * nblk, off, bsum, st);
     if (ss != E2A_OK) return ss;
-    k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout);
+    k_radix_scatter<<<nblk, 256, 0, st>>>(kin, vin, n, shift, off, nblk, kout, vout, pass == 0 ? hist2 : nullptr);
     E2A_LAUNCH_CHECK();
   }
   return E2A_OK;
@@ -1692,13 +1730,16 @@ e2a_status prepare(const e2a_attn_args* a, const MfmaWs& W, char* wb, hipStream_
     const e2a_status so = spatial_order(a->pos, a->n_atoms, W, wb, reinterpret_cast<int32_t*>(wb + W.order), st);
     if (so != E2A_OK) return so;
   }
+  const uint16_t* wrad = static_cast<const uint16_t*>(a->w_rad);
+  u32x4* radout = reinterpret_cast<u32x4*>(wb + W.rad);
   if (!a->w_so2_packed) {
+    static_assert(S::wtotal() >= (L + 1) * kC, "the weight image outnumbers W_rad's vectors");
     const int64_t nv = S::wtotal();
     k_pack_so2<L, false><<<(nv + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_so2),
-                                                            reinterpret_cast<bf16x8*>(wb + W.w));
+                                                            reinterpret_cast<bf16x8*>(wb + W.w), wrad, radout);
+  } else {
+    k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(wrad, radout);
   }
-  k_pack_rad<L><<<((L + 1) * kC + 255) / 256, 256, 0, st>>>(static_cast<const uint16_t*>(a->w_rad),
-                                                            reinterpret_cast<u32x4*>(wb + W.rad));
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }

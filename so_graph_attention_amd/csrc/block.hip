@@ -296,13 +296,14 @@ __global__ void __launch_bounds__(256) k_deg_gemm_mfma(DegGemm g) {
 }
 
 // wt[d][n][k] = w[d][k][n] (bf16), for the matrix-core GEMM's k-contiguous
-// weight columns.
-__global__ void k_transpose_bf16(const uint16_t* __restrict__ w, uint16_t* __restrict__ wt, int nmat, int rows,
-                                 int cols) {
+// weight columns.  With w2 set, matrix 1 comes from w2 instead (two separate
+// matrices in one launch).
+__global__ void k_transpose_bf16(const uint16_t* __restrict__ w, const uint16_t* __restrict__ w2,
+                                 uint16_t* __restrict__ wt, int nmat, int rows, int cols) {
   __shared__ uint16_t tile[32][33];
   const int m = blockIdx.z;
   const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
-  const uint16_t* src = w + (size_t)m * rows * cols;
+  const uint16_t* src = (w2 && m == 1) ? w2 : w + (size_t)m * rows * cols;
   uint16_t* dst = wt + (size_t)m * rows * cols;
   for (int t = threadIdx.x; t < 32 * 32; t += blockDim.x) {
     const int r = t / 32, c = t % 32;
@@ -470,12 +471,14 @@ e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   return E2A_OK;
 }
 
-// dst[m][c][r] = src[m][r][c] for nmat bf16 matrices of rows x cols.
-e2a_status launch_transpose(const void* src, uint16_t* dst, int nmat, int rows, int cols, hipStream_t s) {
+// dst[m][c][r] = src[m][r][c] for nmat bf16 matrices of rows x cols (with
+// src2 set: two matrices, the second from src2).
+e2a_status launch_transpose(const void* src, uint16_t* dst, int nmat, int rows, int cols, hipStream_t s,
+                            const void* src2 = nullptr) {
   if (nmat == 0 || rows == 0 || cols == 0) return E2A_OK;
   const dim3 grid((cols + 31) / 32, (rows + 31) / 32, nmat);
-  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src), dst, nmat, rows,
-                     cols);
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, s, static_cast<const uint16_t*>(src),
+                     static_cast<const uint16_t*>(src2), dst, nmat, rows, cols);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
@@ -495,8 +498,7 @@ e2a_status launch_widen(const void* src, float* dst, int64_t n, int dtype, hipSt
 
 e2a_status launch_qk_mfma(const uint16_t* feat, const uint16_t* wq, const uint16_t* wk, uint16_t* wqk_t, int64_t n,
                           int K, int C, float* q, float* k, hipStream_t s) {
-  e2a_status st = launch_transpose(wq, wqk_t, 1, C, C, s);
-  if (st == E2A_OK) st = launch_transpose(wk, wqk_t + (size_t)C * C, 1, C, C, s);
+  const e2a_status st = launch_transpose(wq, wqk_t, 2, C, C, s, wk);
   if (st != E2A_OK) return st;
   DegGemm g{};
   g.x = feat;

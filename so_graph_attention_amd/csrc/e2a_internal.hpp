@@ -67,6 +67,9 @@ int64_t scan_bsum_count(int64_t n);
 // coordinate is not finite); partial needs kBboxPartialFloats floats.
 constexpr int kBboxPartialFloats = 8 * 256;
 e2a_status launch_bbox(const float* pos, int64_t n, float* partial, float* out, hipStream_t s);
+// The first stage alone (partial boxes of up to 256 blocks, 8 floats each:
+// min, max, non-finite flag); returns the number of partials.
+int launch_bbox_partial(const float* pos, int64_t n, float* partial, hipStream_t s);
 
 // Attention (attention_*.hip).
 struct AttnPlan {

@@ -235,11 +235,69 @@ __global__ void k_scan_apply(const int32_t* __restrict__ in, int64_t n, const in
   }
 }
 
+// Inputs up to kScanSingle entries: one block of 1024 threads, in tiles of
+// 4096 entries (4 consecutive per thread), each scanned across the block and
+// offset by the total of the tiles before it.  One launch instead of three.
+constexpr int64_t kScanSingle = 65536;
+
+__device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int o) {
+  const int lo = __shfl_up(static_cast<int>(static_cast<uint64_t>(v)), o);
+  const int hi = __shfl_up(static_cast<int>(static_cast<uint64_t>(v) >> 32), o);
+  return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
+}
+
+template <typename T>
+__global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict__ in, int64_t n, T* __restrict__ out) {
+  __shared__ int64_t wsum[16];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t carry = 0;
+  for (int64_t base = 0; base < n; base += 4096) {
+    int64_t v[4];
+    int64_t loc = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = base + threadIdx.x * 4 + k;
+      v[k] = t < n ? in[t] : 0;
+      loc += v[k];
+    }
+    int64_t inc = loc;   // inclusive sum over the wave's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int64_t u = shfl_up_i64(inc, o);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) wsum[wave] = inc;
+    __syncthreads();
+    int64_t before = 0, tile = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+      const int64_t x = wsum[w];
+      before += w < wave ? x : 0;
+      tile += x;
+    }
+    __syncthreads();   // wsum is rewritten by the next tile
+    int64_t run = carry + before + inc - loc;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t t = base + threadIdx.x * 4 + k;
+      if (t < n) out[t] = static_cast<T>(run);
+      run += v[k];
+    }
+    carry += tile;
+  }
+  if (threadIdx.x == 0) out[n] = static_cast<T>(carry);
+}
+
 template <typename T>
 e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, hipStream_t s) {
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
   if (nb == 0) {
     E2A_HIP_CHECK(hipMemsetAsync(out, 0, sizeof(T), s));
+    return E2A_OK;
+  }
+  if (n <= kScanSingle) {
+    k_scan_single<T><<<1, 1024, 0, s>>>(in, n, out);
+    E2A_LAUNCH_CHECK();
     return E2A_OK;
   }
   k_scan_reduce<<<nb, 256, 0, s>>>(in, n, bsum);
@@ -492,9 +550,14 @@ WsLayout ws_layout(int64_t n) {
 
 size_t neighbors_workspace_bytes(int64_t n) { return ws_layout(n).total; }
 
-e2a_status launch_bbox(const float* pos, int64_t n, float* partial, float* out, hipStream_t s) {
+int launch_bbox_partial(const float* pos, int64_t n, float* partial, hipStream_t s) {
   const int nparts = static_cast<int>(std::min<int64_t>(kBboxBlocks, (n + 255) / 256));
   k_bbox_partial<<<nparts, 256, 0, s>>>(pos, n, partial);
+  return nparts;
+}
+
+e2a_status launch_bbox(const float* pos, int64_t n, float* partial, float* out, hipStream_t s) {
+  const int nparts = launch_bbox_partial(pos, n, partial, s);
   k_bbox_final<<<1, 256, 0, s>>>(partial, nparts, out);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
