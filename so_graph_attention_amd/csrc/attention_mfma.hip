@@ -1895,7 +1895,9 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.gnorm = reinterpret_cast<const float*>(wb + W.gnorm);
   p.delta = delta;
   p.ds = pl.ds;
-  if (pl.w_rad) {
+  if (pl.ds_later) {
+    // the call forms ds from its edge batches and adds the l = 0 terms then
+  } else if (pl.w_rad) {
     // dW_rad in the same pass (the radial pass's partials and reduction)
     p.rad_part = reinterpret_cast<float*>(wb + W.radpart);
     e = launch_mode<L, kBwdQR>(p, st);
@@ -1914,7 +1916,7 @@ e2a_status launch_bwd_typed(const BwdPlan& pl, hipStream_t st) {
   p.out = pl.grad_feat;
   e = launch_mode<L, kBwdV>(p, st);
   if (e != E2A_OK) return e;
-  return launch_bwd_qk(pl, st);
+  return pl.ds_later ? E2A_OK : launch_bwd_qk(pl, st);
 }
 
 // dW_rad on the matrix cores: the cotangent's copies, then the radial pass
@@ -1966,6 +1968,18 @@ const uint16_t* mfma_grad_bf16(const void* mfma_ws, int64_t n, int L) {
     default: return nullptr;
   }
   return reinterpret_cast<const uint16_t*>(static_cast<const char*>(mfma_ws) + off);
+}
+
+const float* mfma_delta(const void* mfma_ws, int64_t n, int L) {
+  size_t off = 0;
+  switch (L) {
+    case 1: off = mfma_ws_layout<1>(n, true).delta; break;
+    case 2: off = mfma_ws_layout<2>(n, true).delta; break;
+    case 3: off = mfma_ws_layout<3>(n, true).delta; break;
+    case 4: off = mfma_ws_layout<4>(n, true).delta; break;
+    default: return nullptr;
+  }
+  return reinterpret_cast<const float*>(static_cast<const char*>(mfma_ws) + off);
 }
 
 e2a_status launch_radial_mfma(const BwdPlan& pl, float* w_rad, hipStream_t s) {

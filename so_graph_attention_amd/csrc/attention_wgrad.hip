@@ -897,6 +897,65 @@ __global__ void k_pos_assemble(const int64_t* __restrict__ row_ptr, const int32_
   for (int d = 0; d < 3; ++d) grad_pos[a * 3 + d] = g[d];
 }
 
+// The softmax gradient of the batch's edges from the batch tensors, for a
+// call that asks for dL/dh and the positions but no weights (so no query
+// pass runs).  With y = SO2(x) and dy = rho D (alpha G_i) in the batch
+// layout, the sum of y dy over every (l, m) and the head's channels is
+// alpha_h dL/dalpha_h (the rotate-out puts D^T (rho y) where G_i meets it), so
+//   ds_h = sum y dy - alpha_h delta_{i,h},
+// the quantity the query pass forms from its own products (softmax backward,
+// technical summary section 2.2).  C = 128, H = 8, bf16 y and dy.  One wave
+// per edge: the edge's 2L + 1 rows (m = 0, then +m and -m for m = 1 .. L)
+// are read as 16-byte vectors, lane l taking vectors l, l + 64, ... of their
+// concatenation; every row holds a whole multiple of 16 vectors (128
+// channels), so vector v carries channels of head (v mod 16) / 2 and a
+// lane's head is (l mod 16) / 2 throughout.  The eight lanes of a head are
+// then summed (exchanges across bits 0, 4 and 5 of the lane index).
+constexpr int kDsEdges = 4;   // edges (waves) per workgroup
+template <int L>
+__global__ void __launch_bounds__(64 * kDsEdges) k_wg_ds(BatchLayout bl, int64_t nb, int64_t e0,
+                                                         const int32_t* __restrict__ src,
+                                                         const uint16_t* __restrict__ Y,
+                                                         const uint16_t* __restrict__ DY,
+                                                         const float* __restrict__ alpha,
+                                                         const float* __restrict__ delta, float* __restrict__ ds) {
+  constexpr int C = 128, H = 8;
+  constexpr int NV = (L + 1) * (L + 1) * C / 8;   // vectors of one edge
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * kDsEdges + (threadIdx.x >> 6);
+  if (b >= nb) return;
+  float acc = 0.0f;
+  for (int v = lane; v < NV; v += 64) {
+    // row r of the edge (r = 0: m = 0; r = 2m - 1, 2m: +m, -m) and the
+    // vector's place in it
+    int m = 0, neg = 0, w = v;
+    while (w >= (L + 1 - m) * (C / 8)) {
+      w -= (L + 1 - m) * (C / 8);
+      if (m == 0 || neg) { ++m; neg = 0; }
+      else neg = 1;
+    }
+    const int64_t km = (int64_t)(L + 1 - m) * C;
+    const int64_t at = bl.moff[m] + (neg ? bl.B * km : 0) + b * km + 8 * (int64_t)w;
+    const uint4 yv = *reinterpret_cast<const uint4*>(Y + at);
+    const uint4 dv = *reinterpret_cast<const uint4*>(DY + at);
+    const uint32_t yw[4] = {yv.x, yv.y, yv.z, yv.w}, dw[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc += __uint_as_float(yw[q] << 16) * __uint_as_float(dw[q] << 16);
+      acc += __uint_as_float(yw[q] & 0xffff0000u) * __uint_as_float(dw[q] & 0xffff0000u);
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 16);
+  acc += __shfl_xor(acc, 32);
+  if (lane < 16 && (lane & 1) == 0) {
+    const int h = lane >> 1;
+    const int64_t e = e0 + b;
+    const float a = alpha[b * H + h];
+    ds[e * H + h] = acc - a * delta[(int64_t)src[e] * H + h];
+  }
+}
+
 // ---------------------------------------------------------------- GEMMs ----
 // C[m * ldc + n] += alpha * sum_k A(m, k) B(k, n), A(m, k) = A[m sam + k sak],
 // B(k, n) = B[k sbk + n sbn].  With A2 set the k range is two segments: k <
@@ -2000,6 +2059,16 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
           e = gemm<T, T>(make_gemm(t.dy, km, 1, t.w, 1, km, nb, km, km, t.s, t.x, km, part, t.first),
                          W.part_floats, st);
           if (e != E2A_OK) return e;
+        }
+      }
+      if (pl.ds) {
+        if (!(yb && C == 128 && H == 8 && L >= 1))
+          return fail(E2A_ERR_UNSUPPORTED, "ds from the edge batches needs bf16, C = 128, H = 8 and L >= 1");
+        if constexpr (kPairs && L >= 1) {
+          k_wg_ds<L><<<static_cast<unsigned>((nb + kDsEdges - 1) / kDsEdges), 64 * kDsEdges, 0, st>>>(
+              bl, nb, e0, src, reinterpret_cast<const uint16_t*>(wb + W.Y), reinterpret_cast<const uint16_t*>(GT),
+              reinterpret_cast<const float*>(wb + W.alpha), pl.delta, pl.ds);
+          E2A_LAUNCH_CHECK();
         }
       }
       ForceParams fp{};

@@ -138,22 +138,15 @@ e2a_status check_bwd_args(const e2a_attn_args* a, const float* grad_out) {
   return E2A_OK;
 }
 
-// q, k, then the query pass (ds) and, with grad_feat, the value pass and the
-// l = 0 terms; dq and dk to wdq, wdk when those are set; dW_rad from the
-// query pass into w_rad when that is set (matrix-core path only).
-e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* grad_feat, float* wdq, float* wdk,
-                        char* base, const BwdWs& ws, hipStream_t s, float* w_rad = nullptr) {
-  AttnPlan qk{};
-  qk.a = a;
-  qk.q = reinterpret_cast<float*>(base + ws.q);
-  qk.k = reinterpret_cast<float*>(base + ws.k);
-  qk.wqk_t = reinterpret_cast<uint16_t*>(base + ws.wqk_bf);
+// The feature gradient's plan over the workspace layout ws.
+BwdPlan bwd_plan(const e2a_attn_args* a, const float* grad_out, float* grad_feat, float* wdq, float* wdk, char* base,
+                 const BwdWs& ws) {
   BwdPlan pl{};
   pl.a = a;
   pl.grad_out = grad_out;
   pl.grad_feat = grad_feat;
-  pl.q = qk.q;
-  pl.k = qk.k;
+  pl.q = reinterpret_cast<float*>(base + ws.q);
+  pl.k = reinterpret_cast<float*>(base + ws.k);
   pl.dq = reinterpret_cast<float*>(base + ws.dq);
   pl.ds = reinterpret_cast<float*>(base + ws.ds);
   pl.wqkt = reinterpret_cast<float*>(base + ws.wqkt);
@@ -162,11 +155,28 @@ e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* gr
   pl.wdk = wdk;
   pl.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) pl.box[d] = a->box ? a->box[d] : 0.0f;
+  return pl;
+}
+
+// q, k, then the query pass (ds) and, with grad_feat, the value pass and the
+// l = 0 terms; dq and dk to wdq, wdk when those are set; dW_rad from the
+// query pass into w_rad when that is set (matrix-core path only).  With
+// ds_later (matrix-core path) the query pass and the l = 0 terms are left
+// out: the caller forms ds itself and then calls launch_bwd_qk.
+e2a_status run_backward(const e2a_attn_args* a, const float* grad_out, float* grad_feat, float* wdq, float* wdk,
+                        char* base, const BwdWs& ws, hipStream_t s, float* w_rad = nullptr, bool ds_later = false) {
+  AttnPlan qk{};
+  qk.a = a;
+  qk.q = reinterpret_cast<float*>(base + ws.q);
+  qk.k = reinterpret_cast<float*>(base + ws.k);
+  qk.wqk_t = reinterpret_cast<uint16_t*>(base + ws.wqk_bf);
+  BwdPlan pl = bwd_plan(a, grad_out, grad_feat, wdq, wdk, base, ws);
   e2a_status st = launch_qk(qk, s);
   if (st != E2A_OK) return st;
   const bool mfma_ok = mfma_supported(a->L, a->C, a->H, a->dtype);
   const bool use_mfma = a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok);
   pl.w_rad = use_mfma ? w_rad : nullptr;
+  pl.ds_later = use_mfma && ds_later;
   return use_mfma ? launch_backward_mfma(pl, s) : launch_attention_backward(pl, s);
 }
 
@@ -531,10 +541,15 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   const bool rad_mfma = grad_w_rad &&
                         (a->variant == E2A_VARIANT_MFMA || (a->variant == E2A_VARIANT_AUTO && mfma_ok));
   const bool rad_in_query = rad_mfma && (grad_feat || want_qk);
+  // dL/dh with the positions and no weight but W_so2 (the forces): the edge
+  // batches hold y and dy, from which ds follows without a query pass (one
+  // read of the two against one more pass of the fused kernel)
+  const bool ds_batches = grad_pos && grad_feat && !want_qk && !grad_w_rad && rad_mfma_path(a) &&
+                          a->dtype == E2A_DTYPE_BF16 && a->C == 128 && a->H == 8 && a->L >= 1;
   if (grad_feat || want_qk) {
     // the softmax gradient ds (and dL/dh when asked for); dq, dk from it
     st = run_backward(a, grad_out, grad_feat, want_qk ? dq : nullptr, want_qk ? dk : nullptr, base, ws.b, s,
-                      rad_in_query ? grad_w_rad : nullptr);
+                      rad_in_query ? grad_w_rad : nullptr, ds_batches);
   } else {
     // dW_rad, dW_so2 and the positions need only q and k (for the
     // attention weights)
@@ -572,10 +587,17 @@ e2a_status e2a_attention_bwd_weights(const e2a_attn_args* a, const float* grad_o
   wp.pos = grad_pos;
   // the matrix-core feature gradient left the cotangent in bf16 (k_prep_grad)
   if ((grad_feat || want_qk) && rad_mfma_path(a)) wp.grad_bf = mfma_grad_bf16(base + ws.b.mfma, a->n_atoms, a->L);
+  if (ds_batches) {
+    wp.ds = reinterpret_cast<float*>(base + ws.b.ds);
+    wp.delta = mfma_delta(base + ws.b.mfma, a->n_atoms, a->L);
+  }
   wp.ws = base + ws.wg;
   wp.periodic = a->box != nullptr;
   for (int d = 0; d < 3; ++d) wp.box[d] = a->box ? a->box[d] : 0.0f;
-  return launch_weight_grads(wp, s);
+  st = launch_weight_grads(wp, s);
+  if (st != E2A_OK || !ds_batches) return st;
+  // the l = 0 terms of dL/dh from the batches' ds
+  return launch_bwd_qk(bwd_plan(a, grad_out, grad_feat, nullptr, nullptr, base, ws.b), s);
 }
 
 }  // extern "C"

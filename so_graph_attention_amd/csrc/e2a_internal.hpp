@@ -95,6 +95,8 @@ size_t order_workspace_bytes(int64_t n);
 // The bf16 copy of the cotangent the matrix-core feature gradient leaves in
 // its workspace (mfma_ws of a BwdPlan).
 const uint16_t* mfma_grad_bf16(const void* mfma_ws, int64_t n, int L);
+// ... and where it keeps delta = sum G o per atom and head [N, H].
+const float* mfma_delta(const void* mfma_ws, int64_t n, int L);
 e2a_status destination_order(const float* pos, int64_t n, int32_t* order, void* ws, hipStream_t s);
 // Feature gradient (attention_backward.hip).
 struct BwdPlan {
@@ -110,6 +112,8 @@ struct BwdPlan {
   float* wdq;              // if set: dq_j = sum_j' ds_jj' k_j' / sqrt(C/H), f32 [N, C]
   float* wdk;              // if set: dk_j = sum_i ds_ij q_i / sqrt(C/H), f32 [N, C]
   float* w_rad;            // if set (matrix-core path): dW_rad from the query pass itself, f32 [8, L+1, C]
+  bool ds_later;           // matrix-core path: no query pass and no l = 0 terms (ds is formed later,
+                           // and launch_bwd_qk is called after it)
   float box[3];
   int periodic;
 };
@@ -155,6 +159,9 @@ struct WgradPlan {
   float* w_so2;
   float* pos;              // dL/dx [N, 3] (optional)
   const uint16_t* grad_bf; // G in bf16 (round to nearest even) if the call already made it, else null
+  float* ds;               // if set (with pos; bf16, C = 128, H = 8): the softmax gradient [E, H] of every
+                           // edge, formed from the batches' y and dy instead of a query pass
+  const float* delta;      // with ds: delta = sum G o per atom and head [N, H]
   void* ws;                // wgrad_workspace_bytes(...)
   float box[3];
   int periodic;

@@ -297,3 +297,59 @@ def test_wgrad_no_edges_and_isolated_atom(B):
     assert np.all(got["pos"][-1] == 0)
     check_pos(got["pos"], oracle_pos(w, rp, col, G), TOL_F32, "f32 cluster + isolated atom")
     check(got, oracle_wgrad(w, rp, col, G), TOL_F32, "f32 cluster + isolated atom")
+
+
+def oracle_feat(w, rp, col, G, dest=None):
+    return O.attention_backward(w.pos, rp, col, w.as_f32("feat"), w.as_f32("w_q"), w.as_f32("w_k"),
+                                w.as_f32("w_rad"), w.as_f32("w_so2"), w.L, w.C, w.H, w.cutoff, G, box=w.box,
+                                dest=dest)
+
+
+def check_forces_call(B, w, d, out, lse, got, want_feat, rows, tag):
+    """dL/dh of a forces call (positions, no weight but W_so2): against the
+    oracle on `rows`; rows l >= 1 (the value pass) equal e2a_attention_bwd's
+    bit for bit, row 0 (through the softmax gradient, here formed from the
+    edge batches) within the bf16 bound of it."""
+    box = None if w.box is None else w.box.tolist()
+    err = rel_l2(got["feat"][rows], want_feat)
+    log(f"[wgrad] {tag} forces call dL/dh: rel-L2 {err:.3e} against the oracle")
+    assert np.all(np.isfinite(got["feat"])) and err <= TOL_BF16, err
+    ref = B.e2a_attention_bwd(d["pos"], d["row_ptr"], d["col"], d["feat"], d["w_q"], d["w_k"], d["w_rad"],
+                              d["w_so2"], out, lse, d["G"], L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=box)
+    torch.cuda.synchronize()
+    ref = ref.cpu().numpy()
+    assert np.array_equal(got["feat"][:, 1:], ref[:, 1:])
+    err0 = rel_l2(got["feat"][:, 0], ref[:, 0])
+    log(f"[wgrad] {tag} forces call dL/dh row 0: rel-L2 {err0:.3e} against e2a_attention_bwd")
+    assert err0 <= TOL_BF16, err0
+
+
+@pytest.mark.parametrize("L", [1, 4])
+def test_forces_call_softmax_gradient_from_batches(B, L):
+    """dL/dh with the positions and no weight gradient (bf16, C = 128,
+    H = 8): the softmax gradient comes from the batches' y and dy instead of
+    a query pass.  Every atom of a 64-atom system; the positions equal those
+    of the call without dL/dh, bit for bit."""
+    log(f"[wgrad] forces call bf16 tiny L={L}")
+    w = make_config("tiny", L=L, C=128, H=8, dtype="bf16")
+    rp, col, d, G = setup(w, seed=86)
+    out, lse = forward(B, w, d)
+    got = gpu_wgrad(B, w, d, out, lse, weights=(), pos_grad=True)
+    check_forces_call(B, w, d, out, lse, got, oracle_feat(w, rp, col, G), slice(None), f"L={L}")
+    pos_only = gpu_wgrad(B, w, d, out, lse, feat_grad=False, weights=(), pos_grad=True)
+    assert np.array_equal(got["pos"], pos_only["pos"])
+    with_so2 = gpu_wgrad(B, w, d, out, lse, weights=("w_so2",), pos_grad=True)
+    assert np.array_equal(with_so2["feat"], got["feat"]) and np.array_equal(with_so2["pos"], got["pos"])
+
+
+def test_forces_call_drug_sampled(B):
+    """The same on the drug-like workload (347k edges, 2 batches), with the
+    MFMA forward's log-normaliser: dL/dh on 24 sampled atoms against the
+    oracle."""
+    log("[wgrad] forces call bf16 drug")
+    w = make_config("drug")
+    rp, col, d, G = setup(w, seed=87)
+    out, lse = forward(B, w, d, variant="mfma")
+    got = gpu_wgrad(B, w, d, out, lse, weights=(), pos_grad=True)
+    dest = sample_dest(rp, 24, seed=24)
+    check_forces_call(B, w, d, out, lse, got, oracle_feat(w, rp, col, G, dest), dest, "drug")
