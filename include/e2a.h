@@ -399,10 +399,17 @@ size_t e2a_attention_bwd_weights_workspace_bytes(int64_t n_atoms, int64_t n_edge
  *
  * dL/dh and ds come from the same kernels as e2a_attention_bwd (variant as
  * there); the query pass runs only when grad_feat, grad_w_q or grad_w_k is
- * set.  W_rad and W_so2 sum over all edges into matrices too large for a
- * workgroup, so the workspace holds per-edge tensors for one batch of at
- * most 262144 edges at a time: rotated features and cotangents (storage
- * precision), SO2(x) in fp32.  The GEMMs run on the matrix cores for bf16
+ * set.  One exception: with grad_feat and grad_pos set, neither grad_w_q,
+ * grad_w_k nor grad_w_rad, bf16 storage, C = 128, H = 8 and the matrix-core
+ * variant, ds_ij is formed from the edge batches instead (the sum over a
+ * head's channels and every (l, m) of y dy is alpha_ij dL/dalpha_ij, so
+ * ds = sum y dy - alpha delta_i) with y and dy in bf16; then dL/dh's rows
+ * l >= 1 equal e2a_attention_bwd's bit for bit and row 0 agrees to within
+ * the bf16 rounding of y and dy.  W_rad and W_so2 sum over all edges into
+ * matrices too large for a workgroup, so the workspace holds per-edge
+ * tensors for one batch of at most 262144 edges at a time: rotated features
+ * and cotangents (storage precision), SO2(x) in fp32 (bf16 where the
+ * matrix-core kernels read it).  The GEMMs run on the matrix cores for bf16
  * storage (bf16 operands, fp32 sums) and in fp32 otherwise; all sums run in
  * a fixed order, so results are bit-reproducible.  Asynchronous.  Errors as
  * e2a_attention_bwd, plus E2A_ERR_INVALID_ARG when no output is set.
