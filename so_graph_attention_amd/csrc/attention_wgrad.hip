@@ -1809,6 +1809,8 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
     }
     return g;
   };
+  if (pl.ds && !(pl.pos && pl.delta && yb && C == 128 && H == 8 && L >= 1))
+    return fail(E2A_ERR_UNSUPPORTED, "ds from the edge batches needs the positions, bf16, C = 128, H = 8, L >= 1");
   if (pl.pos && yb && !pl.grad_bf) {
     // the matrix-core force kernel reads G in bf16; this call has no copy yet
     const int64_t cnt = n * K * C;
@@ -2062,8 +2064,6 @@ e2a_status run_wgrad(const WgradPlan& pl, hipStream_t st) {
         }
       }
       if (pl.ds) {
-        if (!(yb && C == 128 && H == 8 && L >= 1))
-          return fail(E2A_ERR_UNSUPPORTED, "ds from the edge batches needs bf16, C = 128, H = 8 and L >= 1");
         if constexpr (kPairs && L >= 1) {
           k_wg_ds<L><<<static_cast<unsigned>((nb + kDsEdges - 1) / kDsEdges), 64 * kDsEdges, 0, st>>>(
               bl, nb, e0, src, reinterpret_cast<const uint16_t*>(wb + W.Y), reinterpret_cast<const uint16_t*>(GT),
