@@ -394,25 +394,33 @@ __global__ void k_wqk_transpose(const T* __restrict__ w_q, const T* __restrict__
   wt[(int64_t)C * C + cp * C + c] = load_as_f32(w_k, t);
 }
 
-// The l = 0 terms of the gradient after the matrix-core passes, one
-// workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj' k_j' / sqrt(C/H),
-// dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found in the ascending
-// row of i, once per edge, in tiles of blockDim edges), and, when grad_feat
-// is set, grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T (wt = W_q^T, W_k^T);
-// dq_j and dk_j themselves go to wdq, wdk when those are set (the weight
-// gradients' inputs).
-__global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const float* __restrict__ wt, int K) {
+// The l = 0 terms of the gradient after the matrix-core passes, in two
+// launches.  First one workgroup per atom j: dq_j = sum_{j' in N(j)} ds_jj'
+// k_j' / sqrt(C/H), dk_j = sum_{i in N(j)} ds_ij q_i / sqrt(C/H) (ds_ij found
+// in the ascending row of i, once per edge, in tiles of blockDim edges), into
+// dqo and dko (wdq, wdk when the weight gradients want them, else scratch).
+// The edges of a tile are split over G = blockDim / C thread groups (one
+// channel per thread; G = 1 and several channels per thread when C exceeds
+// blockDim), two edges in flight per thread, and the groups' sums meet in
+// LDS.  Then, when grad_feat is set, grad_feat[j][0] += dq_j W_q^T +
+// dk_j W_k^T over tiles of kQkAtoms atoms, which share each read of W_q^T
+// and W_k^T (wt).
+__global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, float* __restrict__ dqo, float* __restrict__ dko) {
   const int C = p.C, H = p.H, dh = C / H;
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int G = C <= nthr ? nthr / C : 1;          // edge groups
+  const int g = tid / C, c0 = tid - g * C;         // this thread's group and channel (G > 1)
   extern __shared__ float smem[];
-  float* dq = smem;
-  float* dk = smem + C;
-  int64_t* rev = reinterpret_cast<int64_t*>(smem + 2 * C);   // [blockDim]: place of j in row i, or -1
+  float* part = smem;                              // [2][G][C] group sums (G > 1); [2][C] sums (G = 1)
+  int64_t* rev = reinterpret_cast<int64_t*>(smem + 2 * (G > 1 ? nthr : C));   // [blockDim]: j in row i, or -1
   const int64_t j = blockIdx.x;
   const float inv = 1.0f / sqrtf(static_cast<float>(dh));
   const int64_t t0 = p.row_ptr[j], t1 = p.row_ptr[j + 1];
-  for (int c = threadIdx.x; c < C; c += blockDim.x) dq[c] = dk[c] = 0.0f;
-  for (int64_t base = t0; base < t1; base += blockDim.x) {
-    const int64_t t = base + threadIdx.x;
+  if (G == 1)
+    for (int c = tid; c < C; c += nthr) part[c] = part[C + c] = 0.0f;
+  float aq = 0.0f, ak = 0.0f;
+  for (int64_t base = t0; base < t1; base += nthr) {
+    const int64_t t = base + tid;
     if (t < t1) {
       const int i = p.col[t];
       const int64_t end = p.row_ptr[i + 1];
@@ -422,37 +430,123 @@ __global__ void __launch_bounds__(256) k_bwd_qk(BwdParams p, const float* __rest
         if (p.col[mid] < j) lo = mid + 1;
         else hi = mid;
       }
-      rev[threadIdx.x] = (lo < end && p.col[lo] == j) ? lo : -1;
+      rev[tid] = (lo < end && p.col[lo] == j) ? lo : -1;
     }
     __syncthreads();
-    const int64_t nt = t1 - base < (int64_t)blockDim.x ? t1 - base : (int64_t)blockDim.x;
-    for (int c = threadIdx.x; c < C; c += blockDim.x) {
-      const int h = c / dh;
-      float aq = 0.0f, ak = 0.0f;
-      for (int u = 0; u < nt; ++u) {
-        const int i = p.col[base + u];
-        aq += p.ds[(base + u) * H + h] * p.k[(int64_t)i * C + c];
-        const int64_t e = rev[u];
-        if (e >= 0) ak += p.ds[e * H + h] * p.q[(int64_t)i * C + c];
+    const int nt = t1 - base < (int64_t)nthr ? static_cast<int>(t1 - base) : nthr;
+    if (G > 1) {
+      if (g < G) {
+        const int h = c0 / dh;
+        int u = g;
+        for (; u + G < nt; u += 2 * G) {   // two edges' loads in flight
+          const int i0 = p.col[base + u], i1 = p.col[base + u + G];
+          const int64_t e0 = rev[u], e1 = rev[u + G];
+          const float s0 = p.ds[(base + u) * H + h], s1 = p.ds[(base + u + G) * H + h];
+          const float k0 = p.k[(int64_t)i0 * C + c0], k1 = p.k[(int64_t)i1 * C + c0];
+          const float r0 = e0 >= 0 ? p.ds[e0 * H + h] * p.q[(int64_t)i0 * C + c0] : 0.0f;
+          const float r1 = e1 >= 0 ? p.ds[e1 * H + h] * p.q[(int64_t)i1 * C + c0] : 0.0f;
+          aq += s0 * k0;
+          ak += r0;
+          aq += s1 * k1;
+          ak += r1;
+        }
+        if (u < nt) {
+          const int i = p.col[base + u];
+          aq += p.ds[(base + u) * H + h] * p.k[(int64_t)i * C + c0];
+          const int64_t e = rev[u];
+          if (e >= 0) ak += p.ds[e * H + h] * p.q[(int64_t)i * C + c0];
+        }
       }
-      dq[c] += aq;
-      dk[c] += ak;
+    } else {
+      for (int c = tid; c < C; c += nthr) {   // each thread owns its channels' sums
+        const int h = c / dh;
+        float sq = 0.0f, sk = 0.0f;
+        for (int u = 0; u < nt; ++u) {
+          const int i = p.col[base + u];
+          sq += p.ds[(base + u) * H + h] * p.k[(int64_t)i * C + c];
+          const int64_t e = rev[u];
+          if (e >= 0) sk += p.ds[e * H + h] * p.q[(int64_t)i * C + c];
+        }
+        part[c] += sq;
+        part[C + c] += sk;
+      }
     }
     __syncthreads();
   }
-  __syncthreads();
-  if (p.wdq)
-    for (int c = threadIdx.x; c < C; c += blockDim.x) {
-      p.wdq[j * C + c] = dq[c] * inv;
-      p.wdk[j * C + c] = dk[c] * inv;
+  if (G > 1) {
+    if (g < G) {
+      part[g * C + c0] = aq;
+      part[(G + g) * C + c0] = ak;
     }
-  if (!p.grad_feat) return;
+    __syncthreads();
+    for (int c = tid; c < C; c += nthr) {
+      float sq = 0.0f, sk = 0.0f;
+      for (int q = 0; q < G; ++q) {
+        sq += part[q * C + c];
+        sk += part[(G + q) * C + c];
+      }
+      dqo[j * C + c] = sq * inv;
+      dko[j * C + c] = sk * inv;
+    }
+  } else {
+    for (int c = tid; c < C; c += nthr) {
+      dqo[j * C + c] = part[c] * inv;
+      dko[j * C + c] = part[C + c] * inv;
+    }
+  }
+}
+
+// grad_feat[j][0] += dq_j W_q^T + dk_j W_k^T for kQkAtoms atoms per
+// workgroup: the atoms' dq, dk rows in LDS, W_q^T and W_k^T (wt) read once
+// per thread group; group g (G = blockDim / C of them, one channel per
+// thread) takes atoms g, g + G, ... (at most kQkRows); with C beyond
+// blockDim each thread takes channels tid, tid + blockDim, ... atom by atom.
+constexpr int kQkAtoms = 32;
+constexpr int kQkRows = 16;
+__global__ void __launch_bounds__(256) k_bwd_qk_proj(const float* __restrict__ dqo, const float* __restrict__ dko,
+                                                     const float* __restrict__ wt, int64_t n, int C, int K,
+                                                     float* __restrict__ grad_feat) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int G = C <= nthr ? nthr / C : 1;
+  const int g = tid / C, c0 = tid - g * C;
+  extern __shared__ float smem[];
+  const int64_t j0 = (int64_t)blockIdx.x * kQkAtoms;
+  const int na = n - j0 < kQkAtoms ? static_cast<int>(n - j0) : kQkAtoms;
   const float* wqt = wt;
   const float* wkt = wt + (size_t)C * C;
-  for (int c = threadIdx.x; c < C; c += blockDim.x) {
-    float v = 0.0f;
-    for (int cp = 0; cp < C; ++cp) v += dq[cp] * wqt[(size_t)cp * C + c] + dk[cp] * wkt[(size_t)cp * C + c];
-    p.grad_feat[j * K * C + c] += v * inv;
+  if (G > 1) {
+    float* dq = smem;                 // [kQkAtoms][C]
+    float* dk = smem + kQkAtoms * C;  // [kQkAtoms][C]
+    for (int t = tid; t < na * C; t += nthr) {
+      dq[t] = dqo[j0 * C + t];
+      dk[t] = dko[j0 * C + t];
+    }
+    __syncthreads();
+    if (g >= G) return;
+    float acc[kQkRows];
+#pragma unroll
+    for (int r = 0; r < kQkRows; ++r) acc[r] = 0.0f;
+    for (int cp = 0; cp < C; ++cp) {
+      const float wq = wqt[(size_t)cp * C + c0], wk = wkt[(size_t)cp * C + c0];
+#pragma unroll
+      for (int r = 0; r < kQkRows; ++r) {
+        const int a = g + r * G;
+        if (a < na) acc[r] += dq[a * C + cp] * wq + dk[a * C + cp] * wk;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kQkRows; ++r) {
+      const int a = g + r * G;
+      if (a < na) grad_feat[(j0 + a) * K * C + c0] += acc[r];
+    }
+  } else {
+    for (int a = 0; a < na; ++a)
+      for (int c = tid; c < C; c += nthr) {
+        float v = 0.0f;
+        for (int cp = 0; cp < C; ++cp)
+          v += dqo[(j0 + a) * C + cp] * wqt[(size_t)cp * C + c] + dko[(j0 + a) * C + cp] * wkt[(size_t)cp * C + c];
+        grad_feat[(j0 + a) * K * C + c] += v;
+      }
   }
 }
 
@@ -539,8 +633,19 @@ e2a_status launch_bwd_qk(const BwdPlan& pl, hipStream_t s) {
     hipLaunchKernelGGL(k_wqk_transpose<float>, dim3((cc + 255) / 256), dim3(256), 0, s,
                        static_cast<const float*>(a->w_q), static_cast<const float*>(a->w_k), a->C, pl.wqkt);
   E2A_LAUNCH_CHECK();
-  const size_t smem = sizeof(float) * 2 * a->C + sizeof(int64_t) * 256;
-  hipLaunchKernelGGL(k_bwd_qk, dim3(a->n_atoms), dim3(256), smem, s, p, pl.wqkt, K);
+  // dq, dk to the weight gradients' arrays, or to scratch when only dL/dh wants them
+  float* dqo = pl.wdq ? pl.wdq : pl.dq;
+  float* dko = pl.wdk ? pl.wdk : pl.dk;
+  const int G = a->C <= 256 ? 256 / a->C : 1;
+  const size_t smem = sizeof(float) * 2 * (G > 1 ? 256 : (size_t)a->C) + sizeof(int64_t) * 256;
+  if (smem > 64 * 1024) return fail(E2A_ERR_UNSUPPORTED, "l = 0 gradient terms: C=%d too large for LDS", a->C);
+  hipLaunchKernelGGL(k_bwd_qk, dim3(static_cast<unsigned>(a->n_atoms)), dim3(256), smem, s, p, dqo, dko);
+  E2A_LAUNCH_CHECK();
+  if (pl.grad_feat) {
+    const size_t psmem = G > 1 ? sizeof(float) * 2 * kQkAtoms * (size_t)a->C : 0;
+    hipLaunchKernelGGL(k_bwd_qk_proj, dim3(static_cast<unsigned>((a->n_atoms + kQkAtoms - 1) / kQkAtoms)), dim3(256),
+                       psmem, s, dqo, dko, pl.wqkt, a->n_atoms, a->C, K, pl.grad_feat);
+  }
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }

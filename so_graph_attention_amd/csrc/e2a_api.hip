@@ -41,7 +41,7 @@ AttnWs attn_ws_layout(int64_t n, int L, int C, int H, int dtype) {
 }
 
 struct BwdWs {
-  size_t q, k, dq, ds, wqkt, wqk_bf, mfma, total;
+  size_t q, k, dq, dk, ds, wqkt, wqk_bf, mfma, total;
 };
 
 // The matrix-core region is sized whenever (L, C, H) has a bf16 build, so
@@ -53,6 +53,7 @@ BwdWs bwd_ws_layout(int64_t n, int64_t e, int L, int C, int H) {
   w.q = take(sizeof(float) * (size_t)n * C);
   w.k = take(sizeof(float) * (size_t)n * C);
   w.dq = take(sizeof(float) * (size_t)n * C);
+  w.dk = take(sizeof(float) * (size_t)n * C);
   w.ds = take(sizeof(float) * (size_t)e * H);
   w.wqkt = take(sizeof(float) * 2 * (size_t)C * C);
   w.wqk_bf = take(sizeof(uint16_t) * 2 * (size_t)C * C);
@@ -148,6 +149,7 @@ BwdPlan bwd_plan(const e2a_attn_args* a, const float* grad_out, float* grad_feat
   pl.q = reinterpret_cast<float*>(base + ws.q);
   pl.k = reinterpret_cast<float*>(base + ws.k);
   pl.dq = reinterpret_cast<float*>(base + ws.dq);
+  pl.dk = reinterpret_cast<float*>(base + ws.dk);
   pl.ds = reinterpret_cast<float*>(base + ws.ds);
   pl.wqkt = reinterpret_cast<float*>(base + ws.wqkt);
   pl.mfma_ws = base + ws.mfma;

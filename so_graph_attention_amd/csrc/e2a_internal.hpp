@@ -106,6 +106,7 @@ struct BwdPlan {
   float* q;                // workspace f32 [N, C]
   float* k;                // workspace f32 [N, C]
   float* dq;               // workspace f32 [N, C]
+  float* dk;               // workspace f32 [N, C] (matrix-core path: dk when wdk is not set)
   float* ds;               // workspace f32 [E, H]
   float* wqkt;             // workspace f32 [2][C][C]: W_q^T, W_k^T
   void* mfma_ws;           // workspace of the matrix-core path
