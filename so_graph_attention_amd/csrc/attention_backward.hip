@@ -509,7 +509,7 @@ __global__ void __launch_bounds__(256) k_bwd_qk_proj(const float* __restrict__ d
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int G = C <= nthr ? nthr / C : 1;
   const int g = tid / C, c0 = tid - g * C;
-  extern __shared__ float smem[];
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   const int64_t j0 = (int64_t)blockIdx.x * kQkAtoms;
   const int na = n - j0 < kQkAtoms ? static_cast<int>(n - j0) : kQkAtoms;
   const float* wqt = wt;
@@ -526,7 +526,29 @@ __global__ void __launch_bounds__(256) k_bwd_qk_proj(const float* __restrict__ d
     float acc[kQkRows];
 #pragma unroll
     for (int r = 0; r < kQkRows; ++r) acc[r] = 0.0f;
-    for (int cp = 0; cp < C; ++cp) {
+    int cp = 0;
+    if (C % 4 == 0)   // four k at a time: one 16-byte LDS read per row and matrix
+      for (; cp < C; cp += 4) {
+        float wq[4], wk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wq[u] = wqt[(size_t)(cp + u) * C + c0];
+          wk[u] = wkt[(size_t)(cp + u) * C + c0];
+        }
+#pragma unroll
+        for (int r = 0; r < kQkRows; ++r) {
+          const int a = g + r * G;
+          if (a < na) {
+            const float4 q4 = *reinterpret_cast<const float4*>(dq + a * C + cp);
+            const float4 k4 = *reinterpret_cast<const float4*>(dk + a * C + cp);
+            acc[r] += q4.x * wq[0] + k4.x * wk[0];
+            acc[r] += q4.y * wq[1] + k4.y * wk[1];
+            acc[r] += q4.z * wq[2] + k4.z * wk[2];
+            acc[r] += q4.w * wq[3] + k4.w * wk[3];
+          }
+        }
+      }
+    for (; cp < C; ++cp) {
       const float wq = wqt[(size_t)cp * C + c0], wk = wkt[(size_t)cp * C + c0];
 #pragma unroll
       for (int r = 0; r < kQkRows; ++r) {
