@@ -1644,10 +1644,15 @@ __global__ void __launch_bounds__(256) k_prep_grad(const float* __restrict__ g, 
   const float* gi = g + i * S::K * kC;
   uint16_t* bi = gbf + i * S::K * kC;
   float mx = 0.0f;
-  for (int t = tid; t < S::K * kC; t += 256) {
-    const float v = gi[t];
-    bi[t] = f32_to_bf16_rne(v);
-    mx = fmaxf(mx, fabsf(v));
+  // four values per access (K C is a multiple of 128): 16-byte reads, 8-byte bf16 writes
+  static_assert((S::K * kC) % 4 == 0, "whole vectors of four");
+  for (int t = tid; t < S::K * kC / 4; t += 256) {
+    const float4 v = reinterpret_cast<const float4*>(gi)[t];
+    uint2 b;
+    b.x = static_cast<uint32_t>(f32_to_bf16_rne(v.x)) | (static_cast<uint32_t>(f32_to_bf16_rne(v.y)) << 16);
+    b.y = static_cast<uint32_t>(f32_to_bf16_rne(v.z)) | (static_cast<uint32_t>(f32_to_bf16_rne(v.w)) << 16);
+    reinterpret_cast<uint2*>(bi)[t] = b;
+    mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
   }
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((tid & 63) == 0) red[tid >> 6] = mx;
