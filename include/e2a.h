@@ -279,7 +279,9 @@ e2a_status e2a_conv_fwd(const e2a_attn_args* args, void* stream);
  * with the attention fields of this struct; stacking blocks is calling this
  * once per block with that block's weights (h_out of one is h_in of the next).
  * Node-wise products take bf16 operands on the matrix cores for bf16 storage
- * (C a multiple of 32) and fp32 otherwise; sums are fp32.
+ * (C a multiple of 32, at most 128) and fp32 otherwise; sums are fp32.  With
+ * bf16 storage the gated activations are rounded to bf16 (Norm1(h), Norm2(h1)
+ * likewise); u itself stays fp32 up to the gate.
  */
 typedef struct e2a_block_args {
   const float* pos;        /* device f32 [n_atoms, 3]                                 */
@@ -314,8 +316,8 @@ size_t e2a_block_workspace_bytes(int64_t n_atoms, int L, int C, int H, int dtype
 
 /* One block (above).  Asynchronous and deterministic; no memory set or copy
  * commands.  Errors as e2a_attention_fwd, plus E2A_ERR_INVALID_ARG for a NULL
- * h_in, h_out or node-wise weight, and E2A_ERR_UNSUPPORTED for C not a
- * multiple of 4 or n_atoms (2L+1) >= 2^31. */
+ * h_in, h_out or node-wise weight or an h_in, h_out not on a 16-byte boundary,
+ * and E2A_ERR_UNSUPPORTED for C not a multiple of 4 or n_atoms (2L+1) >= 2^31. */
 e2a_status e2a_block_fwd(const e2a_block_args* args, void* stream);
 
 /* ------------------------------------------------------------------------ */

@@ -135,7 +135,7 @@ struct DegGemm {
   const uint16_t* wb;       // bf16 weights, degree l at wb + l * w_deg_stride, [cin][cout]
   const float* wf;          // fp32 weights (VALU path), same layout
   int64_t w_deg_stride;     // elements between degrees' matrices (0: one matrix for all)
-  float* y;                 // fp32 [n][ky][cout]
+  void* y;                  // [n][ky][cout], fp32 (or bf16 with y_bf16 on the matrix-core path)
   const float* res;         // optional fp32 residual, layout of y
   int64_t n;
   int kx, ky;               // components per atom in x and y
@@ -144,9 +144,13 @@ struct DegGemm {
   int l_lo, l_hi;           // degrees computed
   int tile_start[6];        // first tile of degree l_lo + i within a group; [l_hi - l_lo + 1] = tiles per group
   const uint16_t* wb2;      // optional second bf16 product (grid z = 1): the same x times wb2 into y2
-  float* y2;
+  void* y2;
   int tile_rows;            // rows per tile (set by the launcher)
   int64_t group;            // atoms per tile group (set by the launcher)
+  bool y_bf16;              // y stored as bf16 (matrix-core path only)
+  bool gate;                // epilogue: SiLU on degree 0, u * sigmoid(z) on degree l >= 1
+  const float* gate_z;      // gate logits z[a][(l - 1) cout + c], atom stride z_stride (NULL when L = 0)
+  int64_t z_stride;
 };
 
 constexpr int kRows = 64;
@@ -168,13 +172,18 @@ __device__ __forceinline__ void tile_degree(const DegGemm& g, int tile, int& l, 
   row_end = e;
 }
 
-// bf16 matrix-core path: a 128 x 128 output tile per workgroup, four waves of
-// 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16 accumulators).  The tile's rows of
-// x (rounded to bf16) and the weight columns (from the transposed copy wt,
-// k contiguous) are staged in LDS with k contiguous, so both operands are
-// 16-byte LDS reads.
+// bf16 matrix-core path, computed transposed: y^T = W^T x^T for a tile of
+// 128 node rows and 128 output channels per workgroup.  The MFMA's rows are
+// output channels (wave w owns 32 of them; their W^T fragments, k contiguous
+// in the transposed copy wt, sit in registers for the whole tile) and its
+// columns are node rows (x rounded to bf16 and staged in LDS, k contiguous).
+// A lane's accumulators then hold four consecutive channels of one node row
+// per group of four, so the residual loads and the stores of y are 16 bytes
+// (fp32) or 8 bytes (bf16) a lane.  Optional epilogue: the FFN's gate
+// (SiLU on degree 0, sigmoid of the gate logits z on degree l >= 1).
 constexpr int kMRows = 128;
 constexpr int kMCols = 128;
+constexpr int kMaxCin = 128;   // x staging and the weight registers cover cin <= 128
 
 // Eight consecutive values of x as loaded (fp32 or bf16 bits).
 template <typename XT>
@@ -204,21 +213,43 @@ __device__ __forceinline__ void store8_bf16(const XT8<uint16_t>& x, uint16_t* ds
   *reinterpret_cast<uint4*>(dst) = x.a;
 }
 
-template <typename XT>
-__global__ void __launch_bounds__(256) k_deg_gemm_mfma(DegGemm g) {
+// The matrix-core path rounds the gated activations to bf16, so the gate
+// uses the hardware exp2 and reciprocal (each within a few fp32 ulps, far
+// below bf16's 2^-9): sigmoid(z) = 1 / (1 + 2^(-z log2 e)); z -> -inf gives
+// 1 / inf = 0, z -> +inf gives 1.
+__device__ __forceinline__ float sigmoid_fast(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * z));
+}
+__device__ __forceinline__ float silu(float u) { return u * sigmoid_fast(u); }
+__device__ __forceinline__ float gated(float u, float z) { return u * sigmoid_fast(z); }
+
+template <typename XT, typename YT>
+__global__ void __launch_bounds__(256, 3) k_deg_gemm_mfma(DegGemm g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int cin = g.cin, ldk = g.cin + 8, kg = g.cin / 8;
-  uint16_t* As = reinterpret_cast<uint16_t*>(smem);   // [kMRows][ldk]
+  uint16_t* Xs = reinterpret_cast<uint16_t*>(smem);   // [kMRows][ldk]
   int l;
   int64_t row0, row_end;
   tile_degree(g, blockIdx.x, l, row0, row_end);
   const unsigned w = 2 * l + 1;
   const unsigned nrows = static_cast<unsigned>(row_end);   // < 2^31 (checked on the host)
-  const int col0 = blockIdx.y * kMCols;
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, r32 = lane & 31;
+  // the wave's 32 output channels; cout is a multiple of 32, so they are
+  // all valid or all past the end
+  const int cbase = blockIdx.y * kMCols + 32 * wave;
+  const bool wok = cbase < g.cout;
+  // W^T fragments of every k-step: A operand rows = channels cbase + r32
+  const uint16_t* Wt = (blockIdx.z ? g.wb2 : g.wb) + (int64_t)l * g.w_deg_stride;
+  constexpr int kKSteps = kMaxCin / 16;
+  bf16x8 wv[kKSteps];
+#pragma unroll
+  for (int s = 0; s < kKSteps; ++s)
+    wv[s] = (wok && 16 * s < cin) ? *reinterpret_cast<const bf16x8*>(Wt + (size_t)(cbase + r32) * cin + 16 * s + 8 * half)
+                                  : bf16x8{};
   // the tile's rows of x: a lane's 8 k values per step, all loads in flight
   // before the conversions and LDS stores
-  constexpr int kSteps = kMRows * 16 / 256;   // cin <= 128: at most 8 steps of 8 k
+  constexpr int kSteps = kMRows * (kMaxCin / 8) / 256;
   XT8<XT> xv[kSteps];
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
@@ -235,63 +266,62 @@ __global__ void __launch_bounds__(256) k_deg_gemm_mfma(DegGemm g) {
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
     const int t = tid + 256 * q;
-    if (t < kMRows * kg) store8_bf16(xv[q], As + (t / kg) * ldk + (t % kg) * 8);
+    if (t < kMRows * kg) store8_bf16(xv[q], Xs + (t / kg) * ldk + (t % kg) * 8);
   }
-  // wt: [cout][cin] per degree (the transposed weights, k contiguous); the
-  // B fragments come straight from it (L2-resident), 16 bytes per lane
-  const uint16_t* Wt = (blockIdx.z ? g.wb2 : g.wb) + (int64_t)l * g.w_deg_stride;
-  float* Y = blockIdx.z ? g.y2 : g.y;
   __syncthreads();
-  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5;
-  const int wr = 64 * (wave >> 1), wc = 64 * (wave & 1);
-  const uint16_t* bcol[2];
-  bool bok[2];
+  if (!wok) return;
+  // B operand = x^T: column j = node row 32 t + r32, k = 16 s + 8 half ..
+  f32x16 acc[4] = {};
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int col = col0 + wc + 32 * i + (lane & 31);
-    bok[i] = col < g.cout;
-    bcol[i] = Wt + (size_t)(bok[i] ? col : 0) * cin + 8 * half;
-  }
-  f32x16 acc[2][2] = {};
-  for (int k0 = 0; k0 < cin; k0 += 16) {
-    bf16x8 a[2], b[2];
+  for (int s = 0; s < kKSteps; ++s) {
+    if (16 * s >= cin) break;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      a[i] = *reinterpret_cast<const bf16x8*>(As + (wr + 32 * i + (lane & 31)) * ldk + k0 + 8 * half);
-      b[i] = bok[i] ? *reinterpret_cast<const bf16x8*>(bcol[i] + k0) : bf16x8{};
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 xb = *reinterpret_cast<const bf16x8*>(Xs + (32 * t + r32) * ldk + 16 * s + 8 * half);
+      acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[s], xb, acc[t], 0, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j2 = 0; j2 < 2; ++j2) acc[i][j2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j2], acc[i][j2], 0, 0, 0);
   }
-  // output offsets of the lane's 32 rows (two row tiles), then residual
-  // loads in flight together, then the stores
-  size_t off[2][16];
+  // lane: node row 32 t + r32; channels cbase + 8 q + 4 half + (0..3) in
+  // accumulator entries 4 q .. 4 q + 3
+  YT* Y = static_cast<YT*>(blockIdx.z ? g.y2 : g.y);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int t = 0; t < 4; ++t) {
+    const unsigned row = static_cast<unsigned>(row0) + 32 * t + r32;
+    if (row >= nrows) continue;
+    const unsigned a = row / w, comp = l * l + row % w;
+    const size_t o = ((size_t)a * g.ky + comp - g.y_comp0) * g.cout + cbase + 4 * half;
+    const float* zr = (g.gate && l > 0) ? g.gate_z + (size_t)a * g.z_stride + (size_t)(l - 1) * g.cout + cbase + 4 * half
+                                        : nullptr;
+    float4 v[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const unsigned row = static_cast<unsigned>(row0) + wr + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
-      const unsigned a = row / w, comp = l * l + row % w - g.y_comp0;
-      off[i][r] = row < nrows ? ((size_t)a * g.ky + comp) * g.cout : ~size_t(0);
-    }
-#pragma unroll
-  for (int j2 = 0; j2 < 2; ++j2) {
-    const int col = col0 + wc + 32 * j2 + (lane & 31);
-    if (col >= g.cout) continue;
+    for (int q = 0; q < 4; ++q) v[q] = float4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
     if (g.res) {
+      float4 rv[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int q = 0; q < 4; ++q) rv[q] = *reinterpret_cast<const float4*>(g.res + o + 8 * q);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (off[i][r] != ~size_t(0)) acc[i][j2][r] += g.res[off[i][r] + col];
+      for (int q = 0; q < 4; ++q) {
+        v[q].x += rv[q].x;
+        v[q].y += rv[q].y;
+        v[q].z += rv[q].z;
+        v[q].w += rv[q].w;
+      }
+    }
+    if (g.gate) {
+      if (zr) {
+        float4 zv[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) zv[q] = *reinterpret_cast<const float4*>(zr + 8 * q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          v[q] = float4{gated(v[q].x, zv[q].x), gated(v[q].y, zv[q].y), gated(v[q].z, zv[q].z), gated(v[q].w, zv[q].w)};
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = float4{silu(v[q].x), silu(v[q].y), silu(v[q].z), silu(v[q].w)};
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (off[i][r] != ~size_t(0)) Y[off[i][r] + col] = acc[i][j2][r];
+    for (int q = 0; q < 4; ++q) store4(Y + o + 8 * q, v[q]);
   }
 }
 
@@ -372,7 +402,7 @@ __global__ void __launch_bounds__(256) k_deg_gemm_valu(DegGemm g) {
       const int col = col0 + tc + j;
       if (col >= g.cout) continue;
       const size_t o = (size_t)(a * g.ky + comp) * g.cout + col;
-      g.y[o] = (g.res ? g.res[o] : 0.0f) + acc[i][j];
+      static_cast<float*>(g.y)[o] = (g.res ? g.res[o] : 0.0f) + acc[i][j];
     }
   }
 }
@@ -386,7 +416,9 @@ __global__ void k_widen(const T* __restrict__ src, float* __restrict__ dst, int6
 
 }  // namespace
 
-bool block_uses_mfma(int C, int dtype) { return dtype == E2A_DTYPE_BF16 && C % 32 == 0 && C >= 32; }
+bool block_uses_mfma(int C, int dtype) {
+  return dtype == E2A_DTYPE_BF16 && C % 32 == 0 && C >= 32 && C <= kMaxCin;
+}
 
 BlockWs block_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   BlockWs w{};
@@ -445,16 +477,17 @@ e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (tiles > INT32_MAX) return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: %lld tiles", (long long)tiles);
   const dim3 grid(static_cast<unsigned>(tiles), (g.cout + tcols - 1) / tcols, mfma && g.wb2 ? 2 : 1);
   if (mfma) {
+    if (g.cin > kMaxCin || g.cin % 32 != 0 || g.cout % 32 != 0)
+      return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: cin=%d cout=%d on the matrix cores", g.cin, g.cout);
     const size_t smem = sizeof(uint16_t) * (size_t)kMRows * (g.cin + 8);
-    if (x_bf16) {
-      E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_deg_gemm_mfma<uint16_t>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
-      hipLaunchKernelGGL(k_deg_gemm_mfma<uint16_t>, grid, dim3(256), smem, s, g);
-    } else {
-      E2A_HIP_CHECK(hipFuncSetAttribute(reinterpret_cast<const void*>(&k_deg_gemm_mfma<float>),
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem));
-      hipLaunchKernelGGL(k_deg_gemm_mfma<float>, grid, dim3(256), smem, s, g);
-    }
+    if (x_bf16 && g.y_bf16)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, uint16_t>), grid, dim3(256), smem, s, g);
+    else if (x_bf16)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, float>), grid, dim3(256), smem, s, g);
+    else if (g.y_bf16)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t>), grid, dim3(256), smem, s, g);
+    else
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float>), grid, dim3(256), smem, s, g);
   } else {
     const size_t smem = sizeof(float) * (size_t)(kRows + kCols) * g.cin;
     if (x_bf16) {
@@ -605,15 +638,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   // n2 = Norm2(h1)
   st = launch_norm(h1, b->norm2, n2, n, L, C, dtype, s);
   if (st != E2A_OK) return st;
-  // u = n2 W1 (into the attention output's space), z = n2[l = 0] W_gate
-  float* u = attn;
-  g.x = n2;
-  g.wb = w1_t;
-  g.wf = w1_f;
-  g.y = u;
-  g.res = nullptr;
-  st = launch_deg_gemm(g, mfma, bf, s);
-  if (st != E2A_OK) return st;
+  // z = n2[l = 0] W_gate (gate logits of degrees 1..L)
   if (L > 0) {
     DegGemm gz{};
     gz.n = n;
@@ -630,17 +655,46 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     st = launch_deg_gemm(gz, mfma, bf, s);
     if (st != E2A_OK) return st;
   }
-  // act = gate(u, z), in n2's space (Norm2 is no longer needed)
-  {
+  void* act;
+  if (mfma) {
+    // act = gate(n2 W1, z) in the GEMM's epilogue, stored bf16 in the
+    // attention output's space (its rows are read before any is written:
+    // each x row belongs to one tile and cout = C is one column block, but
+    // a separate buffer keeps that independent of the tiling)
+    act = attn;
+    g.x = n2;
+    g.wb = w1_t;
+    g.y = act;
+    g.y_bf16 = true;
+    g.res = nullptr;
+    g.gate = true;
+    g.gate_z = L > 0 ? z : nullptr;
+    g.z_stride = (int64_t)L * C;
+    st = launch_deg_gemm(g, true, true, s);
+    if (st != E2A_OK) return st;
+    g.y_bf16 = false;
+    g.gate = false;
+    g.gate_z = nullptr;
+  } else {
+    // u = n2 W1 (into the attention output's space), then act = gate(u, z)
+    // in n2's space (Norm2 is no longer needed)
+    float* u = attn;
+    g.x = n2;
+    g.wf = w1_f;
+    g.y = u;
+    g.res = nullptr;
+    st = launch_deg_gemm(g, false, bf, s);
+    if (st != E2A_OK) return st;
     const dim3 grid(static_cast<unsigned>(std::min<int64_t>(n, 8192)));
     if (bf)
       hipLaunchKernelGGL(k_gate<uint16_t>, grid, dim3(256), 0, s, u, z, static_cast<uint16_t*>(n2), n, L, C);
     else
       hipLaunchKernelGGL(k_gate<float>, grid, dim3(256), 0, s, u, z, static_cast<float*>(n2), n, L, C);
     E2A_LAUNCH_CHECK();
+    act = n2;
   }
   // out = h1 + act W2
-  g.x = n2;
+  g.x = act;
   g.wb = w2_t;
   g.wf = w2_f;
   g.y = b->h_out;

@@ -457,6 +457,9 @@ e2a_status e2a_block_fwd(const e2a_block_args* b, void* stream) {
     for (int t = 0; t < 7; ++t)
       if (!ptrs[t]) return fail(E2A_ERR_INVALID_ARG, "%s is NULL", names[t]);
     if (b->L > 0 && !b->w_gate) return fail(E2A_ERR_INVALID_ARG, "w_gate is NULL");
+    // the norms read h_in and the last GEMM writes h_out 16 bytes a lane
+    if (misaligned(b->h_in)) return fail(E2A_ERR_INVALID_ARG, "h_in is not 16-byte aligned");
+    if (misaligned(b->h_out)) return fail(E2A_ERR_INVALID_ARG, "h_out is not 16-byte aligned");
   }
   const BlockWs ws = block_layout_full(b->n_atoms, b->L, b->C, b->H, b->dtype);
   if (b->n_atoms > 0 && (!b->workspace || b->workspace_bytes < ws.total))

@@ -64,7 +64,7 @@ def test_tiny_fp32_full_output(B):
     assert np.max(np.abs(lse - want_lse)) <= 1e-5
 
 
-@pytest.mark.parametrize("L,C,H", [(0, 8, 2), (2, 24, 3), (3, 32, 4), (4, 32, 8)])
+@pytest.mark.parametrize("L,C,H", [(0, 8, 2), (2, 24, 3), (3, 32, 4), (4, 32, 8), (1, 160, 5)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_reference_kernel_small_shapes(B, L, C, H, dtype):
     log(f"[attn] reference tiny-geometry L={L} C={C} H={H} {dtype}")

@@ -59,7 +59,10 @@ def gpu_block(B, w, d, h_dev, bwd, variant="auto"):
 @pytest.mark.parametrize("L,C,H,dtype,variant,tol", [
     (1, 16, 1, "f32", "auto", TOL_F32), (0, 8, 2, "f32", "auto", TOL_F32), (3, 16, 2, "f32", "auto", TOL_F32),
     (2, 24, 3, "bf16", "reference", TOL_BF16), (1, 128, 8, "bf16", "mfma", TOL_BF16),
-    (4, 128, 8, "bf16", "mfma", TOL_BF16)])
+    (4, 128, 8, "bf16", "mfma", TOL_BF16),
+    # degree 0 only on the matrix-core GEMMs (the gate is SiLU alone), and
+    # bf16 with C above the matrix-core GEMM's 128 (fp32 node-wise products)
+    (0, 32, 2, "bf16", "auto", TOL_BF16), (1, 160, 5, "bf16", "reference", TOL_BF16)])
 def test_block_tiny_full(B, L, C, H, dtype, variant, tol):
     log(f"[block] tiny L={L} C={C} H={H} {dtype} {variant}")
     w = isolated_atom_variant(make_config("tiny", L=L, C=C, H=H, dtype=dtype))
