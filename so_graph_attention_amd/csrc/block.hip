@@ -151,6 +151,11 @@ struct DegGemm {
   bool gate;                // epilogue: SiLU on degree 0, u * sigmoid(z) on degree l >= 1
   const float* gate_z;      // gate logits z[a][(l - 1) cout + c], atom stride z_stride (NULL when L = 0)
   int64_t z_stride;
+  // x rows normalised per atom and degree before the product (matrix-core
+  // path, fp32 x): x[l,m,c] gamma[l][c] / sqrt(mean_{m,c} x[l]^2 + eps),
+  // gamma bf16; the tiles then hold whole atoms (atom_tiles)
+  const uint16_t* norm_gamma;
+  bool atom_tiles;          // tile rows of degree l: (tile_rows / (2l+1)) (2l+1)
 };
 
 constexpr int kRows = 64;
@@ -165,9 +170,10 @@ __device__ __forceinline__ void tile_degree(const DegGemm& g, int tile, int& l, 
   l = g.l_lo + i;
   const int64_t w = 2 * l + 1;
   const int64_t g0 = grp * g.group * w;
-  row0 = g0 + (int64_t)(in - g.tile_start[i]) * g.tile_rows;
+  const int64_t tr = g.atom_tiles ? g.tile_rows / w * w : g.tile_rows;
+  row0 = g0 + (int64_t)(in - g.tile_start[i]) * tr;
   int64_t e = g0 + g.group * w;
-  if (e > row0 + g.tile_rows) e = row0 + g.tile_rows;
+  if (e > row0 + tr) e = row0 + tr;
   if (e > g.n * w) e = g.n * w;
   row_end = e;
 }
@@ -223,8 +229,55 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 __device__ __forceinline__ float silu(float u) { return u * sigmoid_fast(u); }
 __device__ __forceinline__ float gated(float u, float z) { return u * sigmoid_fast(z); }
 
-template <typename XT, typename YT>
-__global__ void __launch_bounds__(256, 3) k_deg_gemm_mfma(DegGemm g) {
+// Per-atom RMS norm of the staged x rows (fp32 values in registers, before
+// they are rounded to bf16): every row's sum of squares (its kg = cin / 8
+// threads are consecutive lanes of one wave: a shuffle tree), then per atom
+// the sum of its 2l+1 row sums in row order; x <- (x inv) gamma[l][c], the
+// arithmetic of the standalone norm.  The tile holds whole atoms.  The row
+// sums sit past the x tile in LDS.
+__device__ __forceinline__ void norm_rows(const DegGemm& g, XT8<float> (&xv)[kMRows * (kMaxCin / 8) / 256], int l,
+                                          unsigned w, unsigned nr, uint16_t* Xs, int tid) {
+  constexpr int kSteps = kMRows * (kMaxCin / 8) / 256;
+  const int cin = g.cin, kg = cin / 8;
+  float* rs = reinterpret_cast<float*>(Xs + kMRows * (cin + 8));   // [kMRows]
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const XT8<float>& x = xv[q];
+    float ss = x.a.x * x.a.x + x.a.y * x.a.y + x.a.z * x.a.z + x.a.w * x.a.w + x.b.x * x.b.x + x.b.y * x.b.y +
+               x.b.z * x.b.z + x.b.w * x.b.w;
+    for (int o = 1; o < kg; o <<= 1) ss += __shfl_xor(ss, o);
+    const int t = tid + 256 * q;
+    if (t < kMRows * kg && t % kg == 0) rs[t / kg] = ss;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int t = tid + 256 * q;
+    const int r = t / kg, k8 = (t % kg) * 8;
+    // rows past the tile's last whole atom hold zeros and stay zero
+    if (t >= kMRows * kg || r >= static_cast<int>(nr)) continue;
+    const int r0 = r / static_cast<int>(w) * static_cast<int>(w);
+    float ss = 0.0f;
+    for (int i = 0; i < static_cast<int>(w); ++i) ss += rs[r0 + i];
+    const float inv = 1.0f / sqrtf(ss / static_cast<float>(static_cast<int>(w) * cin) + kNormEps);
+    // 8 gains in one 16-byte load (gamma 16-byte aligned, checked on the host)
+    const uint4 gv = *reinterpret_cast<const uint4*>(g.norm_gamma + (size_t)l * cin + k8);
+    auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
+    auto hi = [](uint32_t u) { return __uint_as_float(u & 0xffff0000u); };
+    XT8<float>& x = xv[q];
+    x.a.x = x.a.x * inv * lo(gv.x);
+    x.a.y = x.a.y * inv * hi(gv.x);
+    x.a.z = x.a.z * inv * lo(gv.y);
+    x.a.w = x.a.w * inv * hi(gv.y);
+    x.b.x = x.b.x * inv * lo(gv.z);
+    x.b.y = x.b.y * inv * hi(gv.z);
+    x.b.z = x.b.z * inv * lo(gv.w);
+    x.b.w = x.b.w * inv * hi(gv.w);
+  }
+}
+
+template <typename XT, typename YT, bool NORM>
+__global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int cin = g.cin, ldk = g.cin + 8, kg = g.cin / 8;
   uint16_t* Xs = reinterpret_cast<uint16_t*>(smem);   // [kMRows][ldk]
@@ -263,65 +316,73 @@ __global__ void __launch_bounds__(256, 3) k_deg_gemm_mfma(DegGemm g) {
       xv[q] = XT8<XT>{};
     }
   }
+  if constexpr (NORM) norm_rows(g, xv, l, w, nrows - static_cast<unsigned>(row0), Xs, tid);
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
     const int t = tid + 256 * q;
     if (t < kMRows * kg) store8_bf16(xv[q], Xs + (t / kg) * ldk + (t % kg) * 8);
   }
   __syncthreads();
-  if (!wok) return;
   // B operand = x^T: column j = node row 32 t + r32, k = 16 s + 8 half ..
   f32x16 acc[4] = {};
 #pragma unroll
   for (int s = 0; s < kKSteps; ++s) {
-    if (16 * s >= cin) break;
+    if (!wok || 16 * s >= cin) break;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const bf16x8 xb = *reinterpret_cast<const bf16x8*>(Xs + (32 * t + r32) * ldk + 16 * s + 8 * half);
       acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wv[s], xb, acc[t], 0, 0, 0);
     }
   }
-  // lane: node row 32 t + r32; channels cbase + 8 q + 4 half + (0..3) in
-  // accumulator entries 4 q .. 4 q + 3
+  // Epilogue through LDS, 64 rows at a time: a lane's accumulators (node row
+  // 32 t + r32, channels 8 q + 4 half + 0..3 of the wave's 32) go to an fp32
+  // [row][channel] tile, then each row is read back by 32 consecutive
+  // threads, 4 channels each, so residual and gate loads and the stores cover
+  // whole rows (512 bytes fp32, 256 bytes bf16).
+  float* St = reinterpret_cast<float*>(smem);   // [64][kMCols + 4], over Xs
+  constexpr int lds = kMCols + 4;
   YT* Y = static_cast<YT*>(blockIdx.z ? g.y2 : g.y);
+  const int cw = blockIdx.y * kMCols;
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const unsigned row = static_cast<unsigned>(row0) + 32 * t + r32;
-    if (row >= nrows) continue;
-    const unsigned a = row / w, comp = l * l + row % w;
-    const size_t o = ((size_t)a * g.ky + comp - g.y_comp0) * g.cout + cbase + 4 * half;
-    const float* zr = (g.gate && l > 0) ? g.gate_z + (size_t)a * g.z_stride + (size_t)(l - 1) * g.cout + cbase + 4 * half
-                                        : nullptr;
-    float4 v[4];
+  for (int hh = 0; hh < 2; ++hh) {
+    __syncthreads();   // Xs (or the previous half) no longer read
+    if (wok) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = float4{acc[t][4 * q], acc[t][4 * q + 1], acc[t][4 * q + 2], acc[t][4 * q + 3]};
-    if (g.res) {
-      float4 rv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) rv[q] = *reinterpret_cast<const float4*>(g.res + o + 8 * q);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        v[q].x += rv[q].x;
-        v[q].y += rv[q].y;
-        v[q].z += rv[q].z;
-        v[q].w += rv[q].w;
-      }
-    }
-    if (g.gate) {
-      if (zr) {
-        float4 zv[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) zv[q] = *reinterpret_cast<const float4*>(zr + 8 * q);
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          v[q] = float4{gated(v[q].x, zv[q].x), gated(v[q].y, zv[q].y), gated(v[q].z, zv[q].z), gated(v[q].w, zv[q].w)};
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = float4{silu(v[q].x), silu(v[q].y), silu(v[q].z), silu(v[q].w)};
-      }
+          *reinterpret_cast<float4*>(St + (32 * tt + r32) * lds + 32 * wave + 8 * q + 4 * half) =
+              float4{acc[2 * hh + tt][4 * q], acc[2 * hh + tt][4 * q + 1], acc[2 * hh + tt][4 * q + 2],
+                     acc[2 * hh + tt][4 * q + 3]};
     }
+    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 4; ++q) store4(Y + o + 8 * q, v[q]);
+    for (int j = 0; j < 8; ++j) {
+      const int idx = tid + 256 * j;
+      const int rr = idx >> 5, c4 = (idx & 31) * 4;
+      const unsigned row = static_cast<unsigned>(row0) + 64 * hh + rr;
+      if (row >= nrows || cw + c4 >= g.cout) continue;
+      const unsigned a = row / w, comp = l * l + row % w;
+      const size_t o = ((size_t)a * g.ky + comp - g.y_comp0) * g.cout + cw + c4;
+      float4 v = *reinterpret_cast<const float4*>(St + rr * lds + c4);
+      if (g.res) {
+        const float4 rv = *reinterpret_cast<const float4*>(g.res + o);
+        v.x += rv.x;
+        v.y += rv.y;
+        v.z += rv.z;
+        v.w += rv.w;
+      }
+      if (g.gate) {
+        if (l > 0) {
+          const float4 zv = *reinterpret_cast<const float4*>(g.gate_z + (size_t)a * g.z_stride +
+                                                             (size_t)(l - 1) * g.cout + cw + c4);
+          v = float4{gated(v.x, zv.x), gated(v.y, zv.y), gated(v.z, zv.z), gated(v.w, zv.w)};
+        } else {
+          v = float4{silu(v.x), silu(v.y), silu(v.z), silu(v.w)};
+        }
+      }
+      store4(Y + o, v);
+    }
   }
 }
 
@@ -463,13 +524,15 @@ e2a_status launch_norm(const float* h, const void* gamma, void* out, int64_t n, 
 e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (g.n == 0) return E2A_OK;
   g.tile_rows = mfma ? kMRows : kRows;
+  g.atom_tiles = mfma && g.norm_gamma;
   const int tcols = mfma ? kMCols : kCols;
   g.group = g.n;
   int64_t per = 0;
   for (int l = g.l_lo; l <= g.l_hi; ++l) {
     if (per > INT32_MAX) break;
     g.tile_start[l - g.l_lo] = static_cast<int>(per);
-    per += (g.group * (2 * l + 1) + g.tile_rows - 1) / g.tile_rows;
+    const int64_t tr = g.atom_tiles ? g.tile_rows / (2 * l + 1) * (2 * l + 1) : g.tile_rows;
+    per += (g.group * (2 * l + 1) + tr - 1) / tr;
   }
   if (per > INT32_MAX) return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: %lld tiles", (long long)per);
   g.tile_start[g.l_hi - g.l_lo + 1] = static_cast<int>(per);
@@ -479,15 +542,23 @@ e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (mfma) {
     if (g.cin > kMaxCin || g.cin % 32 != 0 || g.cout % 32 != 0)
       return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: cin=%d cout=%d on the matrix cores", g.cin, g.cout);
-    const size_t smem = sizeof(uint16_t) * (size_t)kMRows * (g.cin + 8);
+    const size_t smem = std::max(sizeof(uint16_t) * (size_t)kMRows * (g.cin + 8) +
+                                     (g.norm_gamma ? sizeof(float) * kMRows : 0),
+                                 sizeof(float) * (size_t)64 * (kMCols + 4));
+    if (g.norm_gamma && (x_bf16 || (g.cin / 8 & (g.cin / 8 - 1)) != 0))
+      return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: the fused norm takes fp32 x and cin / 8 a power of two");
     if (x_bf16 && g.y_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, uint16_t>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, uint16_t, false>), grid, dim3(256), smem, s, g);
     else if (x_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, float>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, float, false>), grid, dim3(256), smem, s, g);
+    else if (g.norm_gamma && g.y_bf16)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, true>), grid, dim3(256), smem, s, g);
+    else if (g.norm_gamma)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, true>), grid, dim3(256), smem, s, g);
     else if (g.y_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, false>), grid, dim3(256), smem, s, g);
     else
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, false>), grid, dim3(256), smem, s, g);
   } else {
     const size_t smem = sizeof(float) * (size_t)(kRows + kCols) * g.cin;
     if (x_bf16) {
@@ -635,14 +706,20 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   g.res = b->h_in;
   st = launch_deg_gemm(g, mfma, false, s);
   if (st != E2A_OK) return st;
-  // n2 = Norm2(h1)
-  st = launch_norm(h1, b->norm2, n2, n, L, C, dtype, s);
-  if (st != E2A_OK) return st;
+  // n2 = Norm2(h1): its own pass on the VALU path; the matrix-core GEMMs
+  // that read it (gate logits, first FFN product) normalise h1's rows as
+  // they stage them instead
+  const bool fuse_norm2 = mfma && (reinterpret_cast<uintptr_t>(b->norm2) & 15) == 0;
+  if (!fuse_norm2) {
+    st = launch_norm(h1, b->norm2, n2, n, L, C, dtype, s);
+    if (st != E2A_OK) return st;
+  }
   // z = n2[l = 0] W_gate (gate logits of degrees 1..L)
   if (L > 0) {
     DegGemm gz{};
     gz.n = n;
-    gz.x = n2;
+    gz.x = fuse_norm2 ? static_cast<const void*>(h1) : n2;
+    gz.norm_gamma = fuse_norm2 ? static_cast<const uint16_t*>(b->norm2) : nullptr;
     gz.kx = K;
     gz.ky = 1;
     gz.cin = C;
@@ -652,7 +729,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     gz.wb = wg_t;
     gz.wf = wg_f;
     gz.y = z;
-    st = launch_deg_gemm(gz, mfma, bf, s);
+    st = launch_deg_gemm(gz, mfma, bf && !fuse_norm2, s);
     if (st != E2A_OK) return st;
   }
   void* act;
@@ -662,7 +739,8 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     // each x row belongs to one tile and cout = C is one column block, but
     // a separate buffer keeps that independent of the tiling)
     act = attn;
-    g.x = n2;
+    g.x = fuse_norm2 ? static_cast<const void*>(h1) : n2;
+    g.norm_gamma = fuse_norm2 ? static_cast<const uint16_t*>(b->norm2) : nullptr;
     g.wb = w1_t;
     g.y = act;
     g.y_bf16 = true;
@@ -670,8 +748,9 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     g.gate = true;
     g.gate_z = L > 0 ? z : nullptr;
     g.z_stride = (int64_t)L * C;
-    st = launch_deg_gemm(g, true, true, s);
+    st = launch_deg_gemm(g, true, !fuse_norm2, s);
     if (st != E2A_OK) return st;
+    g.norm_gamma = nullptr;
     g.y_bf16 = false;
     g.gate = false;
     g.gate_z = nullptr;

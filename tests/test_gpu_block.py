@@ -126,3 +126,25 @@ def test_block_deterministic_and_residual_identity(B):
     z["w_o"] = torch.zeros_like(bw["w_o"])
     z["w_2"] = torch.zeros_like(bw["w_2"])
     assert torch.equal(gpu_block(B, w, d, d["h"], z), d["h"])
+
+
+def test_block_norm2_gamma_off_16_bytes(B):
+    """Norm2's gains at an address off the 16-byte boundary: the separate
+    norm pass runs instead of the norm folded into the products that read
+    Norm2(h1); both agree with the oracle."""
+    w = make_config("tiny", L=2, C=128, H=8, dtype="bf16")
+    rp, col, d, h = setup(w)
+    bwh = make_block_weights(w)
+    bw = bw_device(bwh)
+    g = bw["norm2"].reshape(-1)
+    buf = torch.zeros(g.numel() + 8, dtype=g.dtype, device=g.device)
+    buf[1:1 + g.numel()] = g
+    off = dict(bw)
+    off["norm2"] = buf[1:1 + g.numel()].view(bw["norm2"].shape)
+    assert off["norm2"].data_ptr() % 16 != 0
+    want = O.block(w.pos, rp, col, h, block_weights_f32(bwh), w.L, w.C, w.H, w.cutoff)
+    for weights in (bw, off):
+        got = gpu_block(B, w, d, d["h"], weights).cpu().numpy()
+        err = rel_l2(got, want)
+        log(f"[block] norm2 at {weights['norm2'].data_ptr() % 16} bytes past 16: rel-L2 {err:.3e}")
+        assert err <= TOL_BF16
