@@ -851,10 +851,13 @@ def gated_ffn(n, w1, w_gate, w2, L, C):
     z = n[:, 0, :] @ np.asarray(w_gate, dtype=np.float64)
     act = np.empty_like(u)
     s = u[:, 0, :]
-    act[:, 0, :] = s / (1.0 + np.exp(-s))
-    for l in range(1, L + 1):
-        gate = 1.0 / (1.0 + np.exp(-z[:, (l - 1) * C:l * C]))
-        act[:, l * l:(l + 1) ** 2, :] = u[:, l * l:(l + 1) ** 2, :] * gate[:, None, :]
+    # exp(-x) overflows to inf for x < -709: 1 / (1 + inf) = 0 and s / inf = -0
+    # are then the exact limits, so the overflow is expected, not an error
+    with np.errstate(over="ignore"):
+        act[:, 0, :] = s / (1.0 + np.exp(-s))
+        for l in range(1, L + 1):
+            gate = 1.0 / (1.0 + np.exp(-z[:, (l - 1) * C:l * C]))
+            act[:, l * l:(l + 1) ** 2, :] = u[:, l * l:(l + 1) ** 2, :] * gate[:, None, :]
     return degree_linear(act, w2, L)
 
 
