@@ -985,6 +985,7 @@ struct Gemm {
   int64_t kper;    // k per split, a multiple of 32
   bool overwrite;  // C = alpha AB instead of C += alpha AB
   bool part_acc;   // S > 1: add alpha AB to the partials instead of storing it
+  bool vec_out;    // Cb, S = 1: N and ldc multiples of 8, Cb 16-byte aligned (set by the launcher)
 };
 
 // bf16 x bf16 on the matrix cores: a 128 x 128 output tile per workgroup,
@@ -999,6 +1000,34 @@ struct GemmSmem {
   uint16_t a[2][kTM][kBK + kPad];
   uint16_t b[2][kTM][kBK + kPad];
 };
+
+// bf16 output tile through LDS: the accumulators (register r of tile (i, j):
+// row 64 wm + 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4, column 64 wn + 32 j +
+// lane % 32) go to a [128][136] bf16 tile, then 16 threads store each row's
+// 256 bytes, 16 bytes a lane.  The caller has synchronised the workgroup
+// after its last read of `tile`'s memory; out rows are ldc apart.
+__device__ __forceinline__ void store_tile_bf16(const f32x16 (&acc)[2][2], float alpha, uint16_t* tile,
+                                                uint16_t* out, int64_t ldc, int64_t m0, int64_t n0, int64_t M,
+                                                int64_t N, int tid) {
+  constexpr int ldo = kTM + 8;
+  const int lane = tid & 63, wave = tid >> 6, wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tile[(wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * ldo + wn * 64 + j * 32 + (lane & 31)] =
+            f32_to_bf16_rne(alpha * acc[i][j][r]);
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < kTM * kTM / 8 / 256; ++p) {
+    const int idx = tid + 256 * p;
+    const int rr = idx >> 4, c8 = (idx & 15) * 8;
+    if (m0 + rr < M && n0 + c8 < N)
+      *reinterpret_cast<uint4*>(out + (m0 + rr) * ldc + n0 + c8) = *reinterpret_cast<const uint4*>(tile + rr * ldo + c8);
+  }
+}
 
 // One 128 x 32 slice of an operand X(r, k) = X[r sr + k sk] (rows r0 ..
 // r0+127 of m or n, k0 .. k0+31), fetched into registers first and written
@@ -1167,6 +1196,11 @@ __device__ __forceinline__ void gemm_body(const Gemm& g, GemmSmem& sm) {
     }
     __syncthreads();
     buf ^= 1;
+  }
+  if (g.vec_out) {
+    // the loop ended with a barrier: the slices' LDS is free
+    store_tile_bf16(acc, g.alpha, reinterpret_cast<uint16_t*>(&sm), g.Cb, g.ldc, m0, n0, g.M, g.N, tid);
+    return;
   }
   // register r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
 #pragma unroll
@@ -1347,6 +1381,7 @@ struct GemmCx {
   float* Q_part;
   bool part_acc;
   int64_t kper;
+  bool vec_out;        // KK: N and ldc multiples of 8, P_bf and Q_bf 16-byte aligned (set by the launcher)
 };
 
 constexpr size_t kCxSmemKK = 4 * 2 * (size_t)kTM * (kBK + kPad) * sizeof(uint16_t);
@@ -1455,6 +1490,16 @@ __device__ __forceinline__ void gemm_body_cx(const GemmCx& g, uint16_t* smem) {
     __syncthreads();
     buf ^= 1;
   }
+  if constexpr (!TR) {
+    if (g.vec_out) {
+      // the loop ended with a barrier: the slices' LDS is free; P's tile,
+      // then Q's in the same place
+      store_tile_bf16(accP, g.aP, smem, g.P_bf, g.ldc, m0, n0, g.M, g.N, tid);
+      __syncthreads();
+      store_tile_bf16(accQ, g.aQ, smem, g.Q_bf, g.ldc, m0, n0, g.M, g.N, tid);
+      return;
+    }
+  }
   // register r: row 8 (r / 4) + 4 (lane / 32) + r % 4, column lane % 32
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -1487,7 +1532,10 @@ __global__ void __launch_bounds__(256, 2) k_gemm_cx(GemmCx g) {
 
 // One complex pair over S k ranges (TR: partials; KK: S = 1).
 template <bool TR>
-e2a_status launch_gemm_cx(const GemmCx& g, int S, hipStream_t st) {
+e2a_status launch_gemm_cx(const GemmCx& g0, int S, hipStream_t st) {
+  GemmCx g = g0;
+  g.vec_out = !TR && g.N % 8 == 0 && g.ldc % 8 == 0 && (reinterpret_cast<uintptr_t>(g.P_bf) & 15) == 0 &&
+              (reinterpret_cast<uintptr_t>(g.Q_bf) & 15) == 0;
   const dim3 grid(static_cast<unsigned>((g.N + kTM - 1) / kTM), static_cast<unsigned>((g.M + kTM - 1) / kTM),
                   static_cast<unsigned>(S));
   const size_t smem = TR ? kCxSmemTR : kCxSmemKK;
@@ -1595,8 +1643,11 @@ constexpr int64_t tile_of() {
 
 // Launches the product kernel for g with g.S k-ranges of g.kper (set by the caller).
 template <typename TA, typename TB>
-e2a_status launch_gemm(const Gemm& g, hipStream_t st) {
+e2a_status launch_gemm(const Gemm& g0, hipStream_t st) {
   constexpr int64_t tm = tile_of<TA, TB>();
+  Gemm g = g0;
+  g.vec_out = tm == kTM && g.Cb && g.S == 1 && g.N % 8 == 0 && g.ldc % 8 == 0 &&
+              (reinterpret_cast<uintptr_t>(g.Cb) & 15) == 0;
   const dim3 grid(static_cast<unsigned>((g.N + tm - 1) / tm), static_cast<unsigned>((g.M + tm - 1) / tm),
                   static_cast<unsigned>(g.S));
   if constexpr (tm == kTM) {
