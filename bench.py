@@ -307,9 +307,21 @@ def block_leg(B, torch, dev, w, pos, rp, col, box, attn_ms):
         torch.cuda.synchronize()
         res[name] = ev[0].elapsed_time(ev[1]) / 3
     res["block_nodewise_ms"] = res["block_ms"] - attn_ms
+    if w.dtype == "bf16":
+        # node-wise arrays once each, as the bf16 block moves them: Norm1 (h in
+        # fp32, bf16 out), projection (layer output and h in, h1 out, fp32),
+        # gate logits (h1's degree-0 rows in, z out), first FFN product (h1 and
+        # z in, bf16 activations out), second (activations and h1 in, fp32 out)
+        nkc = w.n_atoms * (w.L + 1) ** 2 * w.C
+        nc = w.n_atoms * w.C
+        alg = nkc * (6 + 12 + 6 + 10) + nc * (4 + 8 * w.L)
+        res["block_nodewise_alg_bytes"] = alg
+        res["block_nodewise_hbm_frac"] = alg / (res["block_nodewise_ms"] * 1e-3) / (PEAK_HBM_GBS * 1e9)
     res["block_finite"] = bool(torch.isfinite(x2).all())
     res["block_kernels"] = ("e2a_block_fwd: per-degree RMS norm, the fused layer, per-degree projection + residual "
-                            "(bf16 MFMA GEMM), norm, gated FFN (bf16 MFMA GEMMs) + residual")
+                            "(bf16 MFMA GEMM), gated FFN (bf16 MFMA GEMMs with the second norm folded into the "
+                            "products that read it and the gate into the first one's epilogue) + residual; "
+                            "block_nodewise_ms is the block's time less the standalone layer call's")
     return res
 
 
