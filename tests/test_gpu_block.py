@@ -148,3 +148,34 @@ def test_block_norm2_gamma_off_16_bytes(B):
         err = rel_l2(got, want)
         log(f"[block] norm2 at {weights['norm2'].data_ptr() % 16} bytes past 16: rel-L2 {err:.3e}")
         assert err <= TOL_BF16
+
+
+def test_block_graph_capture_replays(B):
+    """The block enqueues only kernels (no memset or copy nodes, no host
+    sync), so it records into a HIP graph.  Three replays, with eager work
+    and synchronisation between them, each equal the eager result bitwise."""
+    log("[block] graph capture, drug")
+    w = make_config("drug")
+    rp, col, d, h = setup(w)
+    bw = bw_device(make_block_weights(w))
+    eager = gpu_block(B, w, d, d["h"], bw).cpu().numpy()
+    out = torch.empty_like(d["h"])
+    ws = torch.empty(B.e2a_block_workspace_bytes(w.n_atoms, w.L, w.C, w.H, B.E2A_DTYPE_BF16), dtype=torch.uint8,
+                     device="cuda")
+    kw = dict(L=w.L, C=w.C, H=w.H, cutoff=w.cutoff, box=None if w.box is None else w.box.tolist(), out=out,
+              workspace=ws)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up on the capture stream
+        B.e2a_block_fwd(d["pos"], d["row_ptr"], d["col"], d["h"], bw, **kw)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.e2a_block_fwd(d["pos"], d["row_ptr"], d["col"], d["h"], bw, **kw)
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), eager), f"replay {rep}"
