@@ -15,6 +15,7 @@
 // The pair predicate is the fp32 rule documented in e2a.h, written with
 // explicitly rounded intrinsics so that no multiply-add is ever fused.
 #include <climits>
+#include <cstring>
 
 #include "e2a_internal.hpp"
 
@@ -152,12 +153,18 @@ __global__ void k_bin(const float* __restrict__ pos, int64_t n, Grid g, int32_t*
   atomicAdd(&cell_cnt[c], 1);
 }
 
-__global__ void k_scatter(int64_t n, const int32_t* __restrict__ cell_of, const int32_t* __restrict__ cell_start,
-                          int32_t* __restrict__ cursor, int32_t* __restrict__ cell_atoms) {
+// Atom i to its slot of its cell; the slot also gets i's position and batch
+// id (bits in w), so that the pair tests read a candidate by slot in one
+// 16-byte load, independent of the load of its atom id.
+__global__ void k_scatter(int64_t n, const float* __restrict__ pos, const int32_t* __restrict__ batch,
+                          const int32_t* __restrict__ cell_of, const int32_t* __restrict__ cell_start,
+                          int32_t* __restrict__ cursor, int32_t* __restrict__ cell_atoms, float4* __restrict__ pos_cell) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int c = cell_of[i];
-  cell_atoms[cell_start[c] + atomicAdd(&cursor[c], 1)] = static_cast<int32_t>(i);
+  const int slot = cell_start[c] + atomicAdd(&cursor[c], 1);
+  cell_atoms[slot] = static_cast<int32_t>(i);
+  pos_cell[slot] = float4{pos[3 * i], pos[3 * i + 1], pos[3 * i + 2], __int_as_float(batch ? batch[i] : 0)};
 }
 
 // ---- exclusive scan (int32 in, T out, total at out[n]) ---------------------
@@ -311,12 +318,15 @@ e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, h
 // The <= 27 stencil cells' atom ranges are flattened: lane l handles
 // candidates l, l + 64, ... of the concatenation (cells in stencil order,
 // atoms in cell order), so that every pass keeps all 64 lanes busy.
-// sh: 64 ints of LDS for this wavefront.  f(valid, j) is called once per
-// pass by every lane.
+// sh: 64 ints of LDS for this wavefront.  f(valid, j, q) is called once per
+// pass by every lane, with the candidate's atom id and its cell-order copy of
+// position and batch id (slot 0's when not valid); the next pass's two loads
+// are issued before f runs on the current one.
 template <typename F>
 __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid& g,
                                                const int32_t* __restrict__ cell_start,
-                                               const int32_t* __restrict__ cell_atoms, int lane, int* sh, F&& f) {
+                                               const int32_t* __restrict__ cell_atoms,
+                                               const float4* __restrict__ pos_cell, int lane, int* sh, F&& f) {
   int sx[3], sy[3], sz[3];
   const int nx = stencil(cell_coord(pi[0], 0, g), 0, g, sx);
   const int ny = stencil(cell_coord(pi[1], 1, g), 1, g, sy);
@@ -342,22 +352,28 @@ __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid&
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  for (int base = 0; base < total; base += 64) {
-    const int t = base + lane;
-    bool valid = t < total;
-    int j = 0;
-    if (valid) {
-      // last cell whose first index is <= t (empty cells never win: the next
-      // non-empty cell starts after t)
-      int lo = 0, hi = ncells;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (sh[mid] <= t) lo = mid;
-        else hi = mid;
-      }
-      j = cell_atoms[sh[32 + lo] + (t - sh[lo])];
+  // slot of flattened candidate t: the last cell whose first index is <= t
+  // (empty cells never win: the next non-empty cell starts after t)
+  auto slot_of = [&](int t) {
+    if (t >= total) return 0;
+    int lo = 0, hi = ncells;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (sh[mid] <= t) lo = mid;
+      else hi = mid;
     }
-    f(valid, j);
+    return sh[32 + lo] + (t - sh[lo]);
+  };
+  int s = slot_of(lane);
+  int j = cell_atoms[s];
+  float4 q = pos_cell[s];
+  for (int base = 0; base < total; base += 64) {
+    const int sn = slot_of(base + 64 + lane);
+    const int jn = cell_atoms[sn];
+    const float4 qn = pos_cell[sn];
+    f(base + lane < total, j, q);
+    j = jn;
+    q = qn;
   }
 }
 
@@ -365,7 +381,8 @@ __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid&
 __global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, int64_t n,
                                                const int32_t* __restrict__ batch, Grid g,
                                                const int32_t* __restrict__ cell_start,
-                                               const int32_t* __restrict__ cell_atoms, int32_t* __restrict__ row_cnt) {
+                                               const int32_t* __restrict__ cell_atoms,
+                                               const float4* __restrict__ pos_cell, int32_t* __restrict__ row_cnt) {
   __shared__ int sh[4][64];
   const int w = threadIdx.x >> 6;
   const int64_t i = blockIdx.x * 4 + w;
@@ -374,10 +391,10 @@ __global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, in
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int cnt = 0;
-  for_candidates(pi, g, cell_start, cell_atoms, lane, sh[w], [&](bool valid, int j) {
-    bool ok = valid && (j != i) && (!batch || batch[j] == bi);
+  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], [&](bool valid, int j, const float4& q) {
+    bool ok = valid && (j != i) && (!batch || __float_as_int(q.w) == bi);
     if (ok) {
-      const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+      const float pj[3] = {q.x, q.y, q.z};
       ok = pair_ok(pi, pj, g);
     }
     cnt += __popcll(__ballot(ok));
@@ -422,6 +439,7 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
                                                    const int32_t* __restrict__ batch, Grid g,
                                                    const int32_t* __restrict__ cell_start,
                                                    const int32_t* __restrict__ cell_atoms,
+                                                   const float4* __restrict__ pos_cell,
                                                    const int64_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
   __shared__ int32_t rows[4][kRowFast];
   __shared__ int sh[4][64];
@@ -433,10 +451,10 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int cnt = 0;
-  for_candidates(pi, g, cell_start, cell_atoms, lane, sh[w], [&](bool valid, int j) {
-    bool ok = valid && (j != i) && (!batch || batch[j] == bi);
+  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], [&](bool valid, int j, const float4& q) {
+    bool ok = valid && (j != i) && (!batch || __float_as_int(q.w) == bi);
     if (ok) {
-      const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+      const float pj[3] = {q.x, q.y, q.z};
       ok = pair_ok(pi, pj, g);
     }
     const uint64_t mask = __ballot(ok);
@@ -464,6 +482,7 @@ __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int6
                                              const int32_t* __restrict__ batch, Grid g,
                                              const int32_t* __restrict__ cell_start,
                                              const int32_t* __restrict__ cell_atoms,
+                                             const float4* __restrict__ pos_cell,
                                              const int64_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
   __shared__ int32_t buf[kMaxRow];
   const int64_t i = blockIdx.x;
@@ -486,9 +505,10 @@ __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int6
           int j = 0;
           if (t < t1) {
             j = cell_atoms[t];
-            ok = (j != i) && (!batch || batch[j] == bi);
+            const float4 q = pos_cell[t];
+            ok = (j != i) && (!batch || __float_as_int(q.w) == bi);
             if (ok) {
-              const float pj[3] = {pos[3 * j], pos[3 * j + 1], pos[3 * j + 2]};
+              const float pj[3] = {q.x, q.y, q.z};
               ok = pair_ok(pi, pj, g);
             }
           }
@@ -523,7 +543,7 @@ __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int6
 }
 
 struct WsLayout {
-  size_t cell_of, cell_cnt, cursor, cell_atoms, row_cnt, bsum, small, bbox_part, total;
+  size_t cell_of, cell_cnt, cursor, cell_atoms, pos_cell, row_cnt, bsum, small, bbox_part, total;
   int64_t cap_cells;
 };
 
@@ -537,6 +557,7 @@ WsLayout ws_layout(int64_t n) {
   w.cell_cnt = take(sizeof(int32_t) * (cap + 1));
   w.cursor = take(sizeof(int32_t) * cap);
   w.cell_atoms = take(sizeof(int32_t) * n);
+  w.pos_cell = take(sizeof(float) * 4 * n);
   w.row_cnt = take(sizeof(int32_t) * n);
   w.bsum = take(sizeof(int64_t) * nb);
   w.small = take(256);
@@ -579,6 +600,7 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   int32_t* cell_cnt = reinterpret_cast<int32_t*>(base + L.cell_cnt);
   int32_t* cursor = reinterpret_cast<int32_t*>(base + L.cursor);
   int32_t* cell_atoms = reinterpret_cast<int32_t*>(base + L.cell_atoms);
+  float4* pos_cell = reinterpret_cast<float4*>(base + L.pos_cell);
   int32_t* row_cnt = reinterpret_cast<int32_t*>(base + L.row_cnt);
   int64_t* bsum = reinterpret_cast<int64_t*>(base + L.bsum);
   float* bbox = reinterpret_cast<float*>(base + L.small);
@@ -591,15 +613,31 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
     return E2A_OK;
   }
 
-  // 1. bounding box and coordinate check
+  // 1. bounding box and coordinate check.  Open boundaries read it back now
+  // (it sizes the cell grid); a periodic box reads it back with the edge
+  // count, so the call waits on the device once.  Until then every kernel is
+  // safe on any coordinates: cell indices are clamped into the grid, and a
+  // non-finite coordinate fails the pair test.
   {
     const e2a_status st = launch_bbox(pos, n, bbox_part, bbox, s);
     if (st != E2A_OK) return st;
   }
-  float hb[8];
-  E2A_HIP_CHECK(hipMemcpyAsync(hb, bbox, 7 * sizeof(float), hipMemcpyDeviceToHost, s));
-  E2A_HIP_CHECK(hipStreamSynchronize(s));
-  if (hb[6] != 0.0f) return fail(E2A_ERR_INVALID_ARG, "positions contain a non-finite value");
+  float hb[8] = {};
+  auto check_coords = [&]() -> e2a_status {
+    if (hb[6] != 0.0f) return fail(E2A_ERR_INVALID_ARG, "positions contain a non-finite value");
+    if (box)
+      for (int d = 0; d < 3; ++d)
+        if (hb[d] < 0.0f || hb[3 + d] >= box[d])
+          return fail(E2A_ERR_INVALID_ARG, "periodic coordinate on axis %d outside [0, %g): range [%g, %g]", d,
+                      (double)box[d], (double)hb[d], (double)hb[3 + d]);
+    return E2A_OK;
+  };
+  if (!box) {
+    E2A_HIP_CHECK(hipMemcpyAsync(hb, bbox, 7 * sizeof(float), hipMemcpyDeviceToHost, s));
+    E2A_HIP_CHECK(hipStreamSynchronize(s));
+    const e2a_status st = check_coords();
+    if (st != E2A_OK) return st;
+  }
 
   Grid g{};
   g.periodic = box != nullptr;
@@ -608,9 +646,6 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   int64_t ncell = 1;
   for (int d = 0; d < 3; ++d) {
     if (g.periodic) {
-      if (hb[d] < 0.0f || hb[3 + d] >= box[d])
-        return fail(E2A_ERR_INVALID_ARG, "periodic coordinate on axis %d outside [0, %g): range [%g, %g]", d,
-                    (double)box[d], (double)hb[d], (double)hb[3 + d]);
       g.n[d] = std::max(1, static_cast<int>(floorf(box[d] / side_min)));
       g.origin[d] = 0.0f;
       g.box[d] = box[d];
@@ -651,12 +686,12 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
     if (st != E2A_OK) return st;
   }
   E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
-  k_scatter<<<nblk, tpb, 0, s>>>(n, cell_of, cell_cnt, cursor, cell_atoms);
+  k_scatter<<<nblk, tpb, 0, s>>>(n, pos, batch, cell_of, cell_cnt, cursor, cell_atoms, pos_cell);
   E2A_LAUNCH_CHECK();
 
   // 3-4. count, scan, read back
   const int64_t nwblk = (n + 3) / 4;   // wave-per-atom kernels: 4 atoms per block
-  k_count<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_cnt);
+  k_count<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_cnt);
   E2A_LAUNCH_CHECK();
   {
     e2a_status st = exclusive_scan<int64_t>(row_cnt, n, row_ptr, bsum, s);
@@ -664,9 +699,19 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   }
   k_readback<<<1, 1024, 0, s>>>(row_ptr, n, row_cnt, rb);
   E2A_LAUNCH_CHECK();
-  int64_t hr[2];
-  E2A_HIP_CHECK(hipMemcpyAsync(hr, rb, sizeof(hr), hipMemcpyDeviceToHost, s));
+  // one copy of the small region: the bounding box at its start, the edge
+  // count and longest row 128 bytes in
+  static_assert(7 * sizeof(float) <= 128, "bounding box and read-back slots overlap");
+  unsigned char small[128 + 2 * sizeof(int64_t)];
+  E2A_HIP_CHECK(hipMemcpyAsync(small, bbox, sizeof(small), hipMemcpyDeviceToHost, s));
   E2A_HIP_CHECK(hipStreamSynchronize(s));
+  int64_t hr[2];
+  std::memcpy(hr, small + 128, sizeof(hr));
+  if (box) {
+    std::memcpy(hb, small, 7 * sizeof(float));
+    const e2a_status st = check_coords();
+    if (st != E2A_OK) return st;
+  }
   *n_edges = hr[0];
   if (hr[1] > kMaxRow)
     return fail(E2A_ERR_UNSUPPORTED, "an atom has %lld neighbours; rows longer than %d are not supported",
@@ -676,9 +721,9 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
 
   // 5. fill and sort rows
   if (hr[1] <= kRowFast)
-    k_fill_fast<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
+    k_fill_fast<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
   else
-    k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, row_ptr, col);
+    k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }

@@ -74,6 +74,17 @@ def test_neighbors_edge_cases(B):
     pos = torch.tensor([[1.0, float("nan"), 1.0], [2.0, 1.0, 1.0]], device="cuda")
     with pytest.raises(B.E2AError):
         B.e2a_build_neighbors(pos, 5.0)
+    # a periodic box checks its coordinates with the edge count (one wait on
+    # the device): non-finite, negative and too-large coordinates are refused
+    # there, and the next call is unaffected
+    for bad in ([[1.0, float("nan"), 1.0], [2.0, 1.0, 1.0]], [[1.0, -0.5, 1.0], [2.0, 1.0, 1.0]],
+                [[1.0, 1.0, 1.0], [2.0, 1.0, float("inf")]]):
+        with pytest.raises(B.E2AError) as ei:
+            B.e2a_build_neighbors(torch.tensor(bad, device="cuda"), 5.0, box=[20.0, 20.0, 20.0])
+        assert ei.value.status == B.E2A_ERR_INVALID_ARG
+    rp, col = B.e2a_build_neighbors(torch.tensor([[1.0, 1.0, 1.0], [19.0, 1.0, 1.0]], device="cuda"), 5.0,
+                                    box=[20.0, 20.0, 20.0])
+    assert rp.cpu().tolist() == [0, 1, 2] and col.cpu().tolist() == [1, 0]
 
 
 @pytest.mark.parametrize("side", [10.5, 14.0, 16.0])
