@@ -105,9 +105,11 @@ size_t e2a_neighbors_workspace_bytes(int64_t n_atoms);
  *                required count and col untouched; retry with more space.
  *   workspace    device scratch of e2a_neighbors_workspace_bytes(n_atoms).
  *
- * Blocks the calling host thread until the edge count is known (one device
- * to host copy of 8 bytes, plus one more for open boundaries to read the
- * bounding box).  Rows longer than 4096 neighbours give E2A_ERR_UNSUPPORTED.
+ * Blocks the calling host thread once, until the edge count is known (one
+ * device to host copy of the edge count, the longest row and the bounding
+ * box, whose coordinate checks are made then; the cell grid of open
+ * boundaries is sized on the device).  Rows longer than 4096 neighbours give
+ * E2A_ERR_UNSUPPORTED.
  */
 e2a_status e2a_build_neighbors(const float* pos, int64_t n_atoms, const int32_t* batch,
                                const float* box, float cutoff, int64_t* row_ptr, int32_t* col,

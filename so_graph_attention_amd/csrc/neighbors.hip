@@ -4,11 +4,14 @@
 // English technical summary section 2.2, "Streaming Reduction"; section 1
 // gives |E| ~ kN).  The pages do not say how N(i) is built; this is a
 // deterministic counting-sort cell list:
-//   1. bounding box (and coordinate check), read back once;
-//   2. bin atoms into cells of side >= 1.001 * cutoff (counting sort);
+//   1. bounding box (and coordinate check), on the device; an open system's
+//      cell grid is sized from it there, a periodic one's from the box sides;
+//   2. bin atoms into cells of side >= 1.001 * cutoff (counting sort), with
+//      each atom's position and batch id copied to its cell-order slot;
 //   3. count the neighbours of each atom over its <= 27 stencil cells (one
 //      wavefront per atom, the cells' candidates flattened across lanes);
-//   4. exclusive scan -> row_ptr; read the edge count and longest row back;
+//   4. exclusive scan -> row_ptr; read the edge count, longest row and
+//      bounding box back (the call's one wait on the device) and check them;
 //   5. one wavefront per atom gathers its neighbours with ballot compaction
 //      into LDS and writes the row sorted (rank of each entry for rows of up
 //      to 256, an LDS bitonic sort for longer ones).
@@ -36,6 +39,15 @@ struct Grid {
   float half[3];
   float rc2;
 };
+
+// The grid a kernel runs on: given by value (a periodic box, sized on the
+// host from its sides), or in device memory (open boundaries, sized on the
+// device from the bounding box so that the host need not read it back first).
+struct GridArg {
+  Grid g;
+  const Grid* dev;
+};
+__device__ __forceinline__ Grid load_grid(const GridArg& a) { return a.dev ? *a.dev : a.g; }
 
 __device__ __forceinline__ int cell_coord(float x, int d, const Grid& g) {
   int c = static_cast<int>(floorf((x - g.origin[d]) * g.inv_side[d]));
@@ -141,10 +153,45 @@ __global__ void __launch_bounds__(256) k_bbox_final(const float* __restrict__ pa
   }
 }
 
-__global__ void k_bin(const float* __restrict__ pos, int64_t n, Grid g, int32_t* __restrict__ cell_of,
+// Open boundaries: the cell grid from the bounding box bbox[0..6], cells of
+// side >= 1.001 cutoff over [min, max], the largest axis halved until at
+// most cap cells remain.  Any side of at least the cutoff gives the same
+// neighbour lists (the stencil reaches one cell each way), so the grid only
+// needs to be safe; for non-finite coordinates (reported by the host after
+// the edge-count read-back) it is one cell, and extents are clamped before
+// the integer conversion.  One thread.
+__global__ void k_grid_open(const float* __restrict__ bbox, float cutoff, int64_t cap, Grid* __restrict__ out) {
+  Grid g{};
+  g.periodic = 0;
+  g.rc2 = cutoff * cutoff;
+  const float side_min = cutoff * 1.001f;
+  const bool finite = bbox[6] == 0.0f;
+  for (int d = 0; d < 3; ++d) {
+    const float ext = finite ? bbox[3 + d] - bbox[d] : 0.0f;
+    float e = ext / side_min;
+    if (!(e < 1048576.0f)) e = 1048576.0f;
+    g.n[d] = static_cast<int>(floorf(e)) + 1;
+    g.origin[d] = finite ? bbox[d] : 0.0f;
+  }
+  while ((int64_t)g.n[0] * g.n[1] * g.n[2] > cap) {
+    int d = 0;
+    if (g.n[1] > g.n[d]) d = 1;
+    if (g.n[2] > g.n[d]) d = 2;
+    g.n[d] = g.n[d] / 2 > 1 ? g.n[d] / 2 : 1;
+  }
+  for (int d = 0; d < 3; ++d) {
+    const float ext = finite ? bbox[3 + d] - bbox[d] : 0.0f;
+    const float side = fmaxf(side_min, ext / g.n[d] * 1.0001f);
+    g.inv_side[d] = 1.0f / side;
+  }
+  *out = g;
+}
+
+__global__ void k_bin(const float* __restrict__ pos, int64_t n, GridArg ga, int32_t* __restrict__ cell_of,
                       int32_t* __restrict__ cell_cnt) {
   const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
   if (i >= n) return;
+  const Grid g = load_grid(ga);
   const int cx = cell_coord(pos[3 * i + 0], 0, g);
   const int cy = cell_coord(pos[3 * i + 1], 1, g);
   const int cz = cell_coord(pos[3 * i + 2], 2, g);
@@ -379,15 +426,27 @@ __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid&
 
 // ---- neighbour count: one wavefront per destination atom, 4 per block ------
 __global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, int64_t n,
-                                               const int32_t* __restrict__ batch, Grid g,
+                                               const int32_t* __restrict__ batch, GridArg ga,
                                                const int32_t* __restrict__ cell_start,
                                                const int32_t* __restrict__ cell_atoms,
-                                               const float4* __restrict__ pos_cell, int32_t* __restrict__ row_cnt) {
+                                               const float4* __restrict__ pos_cell, const float* __restrict__ bbox,
+                                               int32_t* __restrict__ row_cnt) {
   __shared__ int sh[4][64];
   const int w = threadIdx.x >> 6;
   const int64_t i = blockIdx.x * 4 + w;
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
+  const Grid g = load_grid(ga);
+  // coordinates the host will refuse (non-finite, or outside a periodic box)
+  // may put every atom into one clamped cell: count nothing instead of
+  // testing all pairs on the way to that error
+  bool bad = bbox[6] != 0.0f;
+  if (g.periodic)
+    for (int d = 0; d < 3; ++d) bad = bad || bbox[d] < 0.0f || bbox[3 + d] >= g.box[d];
+  if (bad) {
+    if (lane == 0) row_cnt[i] = 0;
+    return;
+  }
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int cnt = 0;
@@ -436,7 +495,7 @@ __global__ void __launch_bounds__(1024) k_readback(const int64_t* __restrict__ r
 // entries (the atom ids of a row are distinct), so the row is written sorted
 // straight from registers.
 __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos, int64_t n,
-                                                   const int32_t* __restrict__ batch, Grid g,
+                                                   const int32_t* __restrict__ batch, GridArg ga,
                                                    const int32_t* __restrict__ cell_start,
                                                    const int32_t* __restrict__ cell_atoms,
                                                    const float4* __restrict__ pos_cell,
@@ -447,6 +506,7 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
   const int64_t i = blockIdx.x * 4 + w;
   const int lane = threadIdx.x & 63;
   if (i >= n) return;
+  const Grid g = load_grid(ga);
   int32_t* buf = rows[w];
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
@@ -479,7 +539,7 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
 
 // ---- fill + sort, any row up to kMaxRow: one wavefront (= one block) per atom
 __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int64_t n,
-                                             const int32_t* __restrict__ batch, Grid g,
+                                             const int32_t* __restrict__ batch, GridArg ga,
                                              const int32_t* __restrict__ cell_start,
                                              const int32_t* __restrict__ cell_atoms,
                                              const float4* __restrict__ pos_cell,
@@ -487,6 +547,7 @@ __global__ void __launch_bounds__(64) k_fill(const float* __restrict__ pos, int6
   __shared__ int32_t buf[kMaxRow];
   const int64_t i = blockIdx.x;
   const int lane = threadIdx.x;
+  const Grid g = load_grid(ga);
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int sx[3], sy[3], sz[3];
@@ -613,11 +674,10 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
     return E2A_OK;
   }
 
-  // 1. bounding box and coordinate check.  Open boundaries read it back now
-  // (it sizes the cell grid); a periodic box reads it back with the edge
-  // count, so the call waits on the device once.  Until then every kernel is
-  // safe on any coordinates: cell indices are clamped into the grid, and a
-  // non-finite coordinate fails the pair test.
+  // 1. bounding box and coordinate check, read back with the edge count, so
+  // the call waits on the device once.  Until then every kernel is safe on
+  // any coordinates: cell indices are clamped into the grid, a non-finite
+  // coordinate fails the pair test, and an open grid is sized on the device.
   {
     const e2a_status st = launch_bbox(pos, n, bbox_part, bbox, s);
     if (st != E2A_OK) return st;
@@ -632,43 +692,38 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
                       (double)box[d], (double)hb[d], (double)hb[3 + d]);
     return E2A_OK;
   };
-  if (!box) {
-    E2A_HIP_CHECK(hipMemcpyAsync(hb, bbox, 7 * sizeof(float), hipMemcpyDeviceToHost, s));
-    E2A_HIP_CHECK(hipStreamSynchronize(s));
-    const e2a_status st = check_coords();
-    if (st != E2A_OK) return st;
-  }
-
-  Grid g{};
-  g.periodic = box != nullptr;
-  g.rc2 = cutoff * cutoff;
-  const float side_min = cutoff * 1.001f;
+  GridArg ga{};
   int64_t ncell = 1;
-  for (int d = 0; d < 3; ++d) {
-    if (g.periodic) {
+  if (!box) {
+    // sized on the device; the host scans the cell counts over the whole
+    // workspace capacity (zeros past the grid)
+    Grid* gdev = reinterpret_cast<Grid*>(base + L.small + 32);
+    k_grid_open<<<1, 1, 0, s>>>(bbox, cutoff, L.cap_cells, gdev);
+    E2A_LAUNCH_CHECK();
+    ga.dev = gdev;
+    ncell = L.cap_cells;
+  } else {
+    // periodic: sized on the host from the box sides
+    Grid& g = ga.g;
+    g.periodic = 1;
+    g.rc2 = cutoff * cutoff;
+    const float side_min = cutoff * 1.001f;
+    for (int d = 0; d < 3; ++d) {
       g.n[d] = std::max(1, static_cast<int>(floorf(box[d] / side_min)));
       g.origin[d] = 0.0f;
       g.box[d] = box[d];
       g.half[d] = 0.5f * box[d];
-    } else {
-      g.n[d] = static_cast<int>(floorf((hb[3 + d] - hb[d]) / side_min)) + 1;
-      g.origin[d] = hb[d];
     }
-  }
-  // keep the cell count within the workspace by coarsening the largest axis
-  for (;;) {
-    ncell = (int64_t)g.n[0] * g.n[1] * g.n[2];
-    if (ncell <= L.cap_cells) break;
-    int d = 0;
-    if (g.n[1] > g.n[d]) d = 1;
-    if (g.n[2] > g.n[d]) d = 2;
-    g.n[d] = std::max(1, g.n[d] / 2);
-  }
-  for (int d = 0; d < 3; ++d) {
-    float side;
-    if (g.periodic) side = box[d] / g.n[d];
-    else side = std::max(side_min, (hb[3 + d] - hb[d]) / g.n[d] * 1.0001f);
-    g.inv_side[d] = 1.0f / side;
+    // keep the cell count within the workspace by coarsening the largest axis
+    for (;;) {
+      ncell = (int64_t)g.n[0] * g.n[1] * g.n[2];
+      if (ncell <= L.cap_cells) break;
+      int d = 0;
+      if (g.n[1] > g.n[d]) d = 1;
+      if (g.n[2] > g.n[d]) d = 2;
+      g.n[d] = std::max(1, g.n[d] / 2);
+    }
+    for (int d = 0; d < 3; ++d) g.inv_side[d] = 1.0f / (box[d] / g.n[d]);
   }
 
   const int tpb = 256;
@@ -676,7 +731,7 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   // 2. counting sort into cells
   E2A_HIP_CHECK(hipMemsetAsync(cell_cnt, 0, sizeof(int32_t) * (ncell + 1), s));
   E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
-  k_bin<<<nblk, tpb, 0, s>>>(pos, n, g, cell_of, cell_cnt);
+  k_bin<<<nblk, tpb, 0, s>>>(pos, n, ga, cell_of, cell_cnt);
   E2A_LAUNCH_CHECK();
   // cell_cnt -> exclusive starts in place is not allowed (in/out alias): use cursor area? no:
   // scan into row_cnt scratch would be too small, so scan to cell_cnt via a copy in cursor.
@@ -691,7 +746,7 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
 
   // 3-4. count, scan, read back
   const int64_t nwblk = (n + 3) / 4;   // wave-per-atom kernels: 4 atoms per block
-  k_count<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_cnt);
+  k_count<<<nwblk, 256, 0, s>>>(pos, n, batch, ga, cell_cnt, cell_atoms, pos_cell, bbox, row_cnt);
   E2A_LAUNCH_CHECK();
   {
     e2a_status st = exclusive_scan<int64_t>(row_cnt, n, row_ptr, bsum, s);
@@ -707,8 +762,8 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   E2A_HIP_CHECK(hipStreamSynchronize(s));
   int64_t hr[2];
   std::memcpy(hr, small + 128, sizeof(hr));
-  if (box) {
-    std::memcpy(hb, small, 7 * sizeof(float));
+  std::memcpy(hb, small, 7 * sizeof(float));
+  {
     const e2a_status st = check_coords();
     if (st != E2A_OK) return st;
   }
@@ -721,9 +776,9 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
 
   // 5. fill and sort rows
   if (hr[1] <= kRowFast)
-    k_fill_fast<<<nwblk, 256, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
+    k_fill_fast<<<nwblk, 256, 0, s>>>(pos, n, batch, ga, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
   else
-    k_fill<<<n, 64, 0, s>>>(pos, n, batch, g, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
+    k_fill<<<n, 64, 0, s>>>(pos, n, batch, ga, cell_cnt, cell_atoms, pos_cell, row_ptr, col);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
