@@ -466,6 +466,8 @@ def block_args(**kw):
     (dict(dtype=4), B.E2A_ERR_INVALID_ARG),
     (dict(variant=2), B.E2A_ERR_UNSUPPORTED),            # no MFMA layer for L=1, C=16, fp32
     (dict(workspace_bytes=16), B.E2A_ERR_INVALID_ARG),
+    (dict(h_in=FAKE + 8), B.E2A_ERR_INVALID_ARG),        # read and written 16 bytes a lane
+    (dict(h_out=FAKE + 4), B.E2A_ERR_INVALID_ARG),
 ])
 def test_block_rejects_on_host(kw, status):
     a = block_args(**kw)
