@@ -28,6 +28,7 @@ namespace {
 constexpr int kScanBlock = 1024;   // elements per scan block (256 threads x 4)
 constexpr int kMaxRow = 4096;      // longest row the LDS sort handles
 constexpr int kRowFast = 256;      // rows up to this length take the wave-per-atom fill
+constexpr int kCandTab = 1024;     // candidates per atom whose slots a wave tabulates in LDS
 constexpr int kBboxBlocks = kBboxPartialFloats / 8;   // first-stage blocks of the bounding box
 
 struct Grid {
@@ -160,7 +161,8 @@ __global__ void __launch_bounds__(256) k_bbox_final(const float* __restrict__ pa
 // needs to be safe; for non-finite coordinates (reported by the host after
 // the edge-count read-back) it is one cell, and extents are clamped before
 // the integer conversion.  One thread.
-__global__ void k_grid_open(const float* __restrict__ bbox, float cutoff, int64_t cap, Grid* __restrict__ out) {
+__global__ void k_grid_open(const float* __restrict__ bbox, float cutoff, int64_t cap, Grid* __restrict__ out,
+                            int64_t* __restrict__ ncell) {
   Grid g{};
   g.periodic = 0;
   g.rc2 = cutoff * cutoff;
@@ -185,6 +187,7 @@ __global__ void k_grid_open(const float* __restrict__ bbox, float cutoff, int64_
     g.inv_side[d] = 1.0f / side;
   }
   *out = g;
+  *ncell = (int64_t)g.n[0] * g.n[1] * g.n[2];
 }
 
 __global__ void k_bin(const float* __restrict__ pos, int64_t n, GridArg ga, int32_t* __restrict__ cell_of,
@@ -300,9 +303,12 @@ __device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int o) {
   return static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo));
 }
 
+// n_dev (optional): a length found on the device, at most n, scanned instead.
 template <typename T>
-__global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict__ in, int64_t n, T* __restrict__ out) {
+__global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict__ in, int64_t n, T* __restrict__ out,
+                                                      const int64_t* __restrict__ n_dev) {
   __shared__ int64_t wsum[16];
+  if (n_dev && *n_dev < n) n = *n_dev;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t carry = 0;
   for (int64_t base = 0; base < n; base += 4096) {
@@ -342,15 +348,17 @@ __global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict_
   if (threadIdx.x == 0) out[n] = static_cast<T>(carry);
 }
 
+// n_dev (optional, one-block scans only): the device holds a shorter length.
 template <typename T>
-e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, hipStream_t s) {
+e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, hipStream_t s,
+                          const int64_t* n_dev = nullptr) {
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
   if (nb == 0) {
     E2A_HIP_CHECK(hipMemsetAsync(out, 0, sizeof(T), s));
     return E2A_OK;
   }
   if (n <= kScanSingle) {
-    k_scan_single<T><<<1, 1024, 0, s>>>(in, n, out);
+    k_scan_single<T><<<1, 1024, 0, s>>>(in, n, out, n_dev);
     E2A_LAUNCH_CHECK();
     return E2A_OK;
   }
@@ -365,7 +373,10 @@ e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, h
 // The <= 27 stencil cells' atom ranges are flattened: lane l handles
 // candidates l, l + 64, ... of the concatenation (cells in stencil order,
 // atoms in cell order), so that every pass keeps all 64 lanes busy.
-// sh: 64 ints of LDS for this wavefront.  f(valid, j, q) is called once per
+// sh: 64 ints of LDS for this wavefront, tab: kCandTab ints (the slots of
+// the first kCandTab candidates, written once per atom by the stencil lanes,
+// so that a pass finds its slots in one LDS read; candidates past it search
+// the cell starts).  f(valid, j, q) is called once per
 // pass by every lane, with the candidate's atom id and its cell-order copy of
 // position and batch id (slot 0's when not valid); the next pass's two loads
 // are issued before f runs on the current one.
@@ -373,7 +384,8 @@ template <typename F>
 __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid& g,
                                                const int32_t* __restrict__ cell_start,
                                                const int32_t* __restrict__ cell_atoms,
-                                               const float4* __restrict__ pos_cell, int lane, int* sh, F&& f) {
+                                               const float4* __restrict__ pos_cell, int lane, int* sh, int* tab,
+                                               F&& f) {
   int sx[3], sy[3], sz[3];
   const int nx = stencil(cell_coord(pi[0], 0, g), 0, g, sx);
   const int ny = stencil(cell_coord(pi[1], 1, g), 1, g, sy);
@@ -397,12 +409,15 @@ __device__ __forceinline__ void for_candidates(const float (&pi)[3], const Grid&
     sh[lane] = incl - ccnt;   // first flattened index of the lane's cell
     sh[32 + lane] = cstart;
   }
+  for (int k = 0, t = incl - ccnt; k < ccnt && t < kCandTab; ++k, ++t) tab[t] = cstart + k;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  // slot of flattened candidate t: the last cell whose first index is <= t
-  // (empty cells never win: the next non-empty cell starts after t)
+  // slot of flattened candidate t: from the table, or past it the last cell
+  // whose first index is <= t (empty cells never win: the next non-empty
+  // cell starts after t)
   auto slot_of = [&](int t) {
     if (t >= total) return 0;
+    if (t < kCandTab) return tab[t];
     int lo = 0, hi = ncells;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
@@ -432,6 +447,7 @@ __global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, in
                                                const float4* __restrict__ pos_cell, const float* __restrict__ bbox,
                                                int32_t* __restrict__ row_cnt) {
   __shared__ int sh[4][64];
+  __shared__ int tab[4][kCandTab];
   const int w = threadIdx.x >> 6;
   const int64_t i = blockIdx.x * 4 + w;
   const int lane = threadIdx.x & 63;
@@ -450,7 +466,7 @@ __global__ void __launch_bounds__(256) k_count(const float* __restrict__ pos, in
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int cnt = 0;
-  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], [&](bool valid, int j, const float4& q) {
+  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], tab[w], [&](bool valid, int j, const float4& q) {
     bool ok = valid && (j != i) && (!batch || __float_as_int(q.w) == bi);
     if (ok) {
       const float pj[3] = {q.x, q.y, q.z};
@@ -502,6 +518,7 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
                                                    const int64_t* __restrict__ row_ptr, int32_t* __restrict__ col) {
   __shared__ int32_t rows[4][kRowFast];
   __shared__ int sh[4][64];
+  __shared__ int tab[4][kCandTab];
   const int w = threadIdx.x >> 6;
   const int64_t i = blockIdx.x * 4 + w;
   const int lane = threadIdx.x & 63;
@@ -511,7 +528,7 @@ __global__ void __launch_bounds__(256) k_fill_fast(const float* __restrict__ pos
   const float pi[3] = {pos[3 * i], pos[3 * i + 1], pos[3 * i + 2]};
   const int bi = batch ? batch[i] : 0;
   int cnt = 0;
-  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], [&](bool valid, int j, const float4& q) {
+  for_candidates(pi, g, cell_start, cell_atoms, pos_cell, lane, sh[w], tab[w], [&](bool valid, int j, const float4& q) {
     bool ok = valid && (j != i) && (!batch || __float_as_int(q.w) == bi);
     if (ok) {
       const float pj[3] = {q.x, q.y, q.z};
@@ -694,11 +711,15 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   };
   GridArg ga{};
   int64_t ncell = 1;
+  int64_t* ncell_dev = nullptr;   // open boundaries: the grid's cell count, on the device
   if (!box) {
-    // sized on the device; the host scans the cell counts over the whole
-    // workspace capacity (zeros past the grid)
+    // sized on the device: the host clears and copies the cell counts over
+    // the workspace's cell capacity (zeros past the grid), and a one-block
+    // scan reads the grid's cell count from the device
+    static_assert(32 + sizeof(Grid) <= 104, "grid and cell count overlap in the small region");
     Grid* gdev = reinterpret_cast<Grid*>(base + L.small + 32);
-    k_grid_open<<<1, 1, 0, s>>>(bbox, cutoff, L.cap_cells, gdev);
+    ncell_dev = reinterpret_cast<int64_t*>(base + L.small + 104);
+    k_grid_open<<<1, 1, 0, s>>>(bbox, cutoff, L.cap_cells, gdev, ncell_dev);
     E2A_LAUNCH_CHECK();
     ga.dev = gdev;
     ncell = L.cap_cells;
@@ -737,7 +758,7 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
   // scan into row_cnt scratch would be too small, so scan to cell_cnt via a copy in cursor.
   E2A_HIP_CHECK(hipMemcpyAsync(cursor, cell_cnt, sizeof(int32_t) * ncell, hipMemcpyDeviceToDevice, s));
   {
-    e2a_status st = exclusive_scan<int32_t>(cursor, ncell, cell_cnt, bsum, s);
+    e2a_status st = exclusive_scan<int32_t>(cursor, ncell, cell_cnt, bsum, s, ncell_dev);
     if (st != E2A_OK) return st;
   }
   E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));

@@ -7,6 +7,9 @@
   python -m so_graph_attention_amd.profiling gradients [--config large] [--iters 2] [--forces]
       e2a_attention_bwd_weights on one workload: dL/dh and every weight
       gradient (training), or with --forces dL/dh and dL/dx;
+  python -m so_graph_attention_amd.profiling neighbors [--config large] [--iters 10]
+      the neighbour build (e2a_build_neighbors) on one workload, `iters`
+      calls after one warm-up, each with the edge capacity it needs;
   python -m so_graph_attention_amd.profiling copy [--mib 1024] [--iters 2]
       a plain device-to-device copy of known size, whose FETCH_SIZE /
       WRITE_SIZE readings calibrate the byte counters of the layer's run.
@@ -115,6 +118,24 @@ def run_gradients(config: str, iters: int, forces: bool):
     print(f"gradients ({what}) {config}: {w.n_atoms} atoms, {col.numel()} edges, {iters + 1} calls", flush=True)
 
 
+def run_neighbors(config: str, iters: int):
+    import torch
+
+    import so_graph_attention_amd.e2a as B
+    from workloads import make_config
+
+    dev = torch.device("cuda:0")
+    w = make_config(config)
+    pos = torch.from_numpy(w.pos).to(dev)
+    box = None if w.box is None else w.box.tolist()
+    batch = None if w.batch is None else torch.from_numpy(w.batch.astype(np.int32)).to(dev)
+    rp, col = B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch)
+    for _ in range(iters):
+        B.e2a_build_neighbors(pos, w.cutoff, box=box, batch=batch, capacity=col.numel())
+    torch.cuda.synchronize()
+    print(f"neighbors {config}: {w.n_atoms} atoms, {col.numel()} edges, {iters + 1} builds", flush=True)
+
+
 def run_copy(mib: int, iters: int):
     import torch
 
@@ -141,6 +162,9 @@ def main():
     g.add_argument("--config", default="large")
     g.add_argument("--iters", type=int, default=2)
     g.add_argument("--forces", action="store_true")
+    nb = sub.add_parser("neighbors")
+    nb.add_argument("--config", default="large")
+    nb.add_argument("--iters", type=int, default=10)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=1024)
     c.add_argument("--iters", type=int, default=2)
@@ -149,6 +173,8 @@ def main():
         run_attention(args.config, args.iters, args.variant)
     elif args.what == "block":
         run_block(args.config, args.iters)
+    elif args.what == "neighbors":
+        run_neighbors(args.config, args.iters)
     elif args.what == "gradients":
         run_gradients(args.config, args.iters, args.forces)
     else:
