@@ -261,8 +261,9 @@ __global__ void k_scan_blocks(int64_t* __restrict__ bsum, int64_t nb) {
 }
 
 template <typename T>
-__global__ void k_scan_apply(const int32_t* __restrict__ in, int64_t n, const int64_t* __restrict__ boff,
-                             T* __restrict__ out) {
+// (in and clear may be one array: neither is restrict-qualified)
+__global__ void k_scan_apply(const int32_t* in, int64_t n, const int64_t* __restrict__ boff,
+                             T* __restrict__ out, int32_t* clear) {
   __shared__ int64_t s[256];
   const int64_t base = blockIdx.x * (int64_t)kScanBlock;
   int64_t v[4];
@@ -271,6 +272,7 @@ __global__ void k_scan_apply(const int32_t* __restrict__ in, int64_t n, const in
     const int64_t t = base + threadIdx.x * 4 + k;
     v[k] = t < n ? in[t] : 0;
     loc += v[k];
+    if (clear && t < n) clear[t] = 0;
   }
   s[threadIdx.x] = loc;
   __syncthreads();
@@ -304,9 +306,10 @@ __device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int o) {
 }
 
 // n_dev (optional): a length found on the device, at most n, scanned instead.
+// clear (optional, the input's address): each entry is set to zero once read.
 template <typename T>
-__global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict__ in, int64_t n, T* __restrict__ out,
-                                                      const int64_t* __restrict__ n_dev) {
+__global__ void __launch_bounds__(1024) k_scan_single(const int32_t* in, int64_t n, T* __restrict__ out,
+                                                      const int64_t* __restrict__ n_dev, int32_t* clear) {
   __shared__ int64_t wsum[16];
   if (n_dev && *n_dev < n) n = *n_dev;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -319,6 +322,7 @@ __global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict_
       const int64_t t = base + threadIdx.x * 4 + k;
       v[k] = t < n ? in[t] : 0;
       loc += v[k];
+      if (clear && t < n) clear[t] = 0;
     }
     int64_t inc = loc;   // inclusive sum over the wave's lanes
 #pragma unroll
@@ -349,22 +353,24 @@ __global__ void __launch_bounds__(1024) k_scan_single(const int32_t* __restrict_
 }
 
 // n_dev (optional, one-block scans only): the device holds a shorter length.
+// clear (optional, the input's address): the input is left all zero (the
+// entries scanned are cleared as they are read; the caller owns the rest).
 template <typename T>
 e2a_status exclusive_scan(const int32_t* in, int64_t n, T* out, int64_t* bsum, hipStream_t s,
-                          const int64_t* n_dev = nullptr) {
+                          const int64_t* n_dev = nullptr, int32_t* clear = nullptr) {
   const int64_t nb = (n + kScanBlock - 1) / kScanBlock;
   if (nb == 0) {
     E2A_HIP_CHECK(hipMemsetAsync(out, 0, sizeof(T), s));
     return E2A_OK;
   }
   if (n <= kScanSingle) {
-    k_scan_single<T><<<1, 1024, 0, s>>>(in, n, out, n_dev);
+    k_scan_single<T><<<1, 1024, 0, s>>>(in, n, out, n_dev, clear);
     E2A_LAUNCH_CHECK();
     return E2A_OK;
   }
   k_scan_reduce<<<nb, 256, 0, s>>>(in, n, bsum);
   k_scan_blocks<<<1, 256, 0, s>>>(bsum, nb);
-  k_scan_apply<T><<<nb, 256, 0, s>>>(in, n, bsum, out);
+  k_scan_apply<T><<<nb, 256, 0, s>>>(in, n, bsum, out, clear);
   E2A_LAUNCH_CHECK();
   return E2A_OK;
 }
@@ -749,19 +755,16 @@ e2a_status build_neighbors_impl(const float* pos, int64_t n, const int32_t* batc
 
   const int tpb = 256;
   const int64_t nblk = (n + tpb - 1) / tpb;
-  // 2. counting sort into cells
-  E2A_HIP_CHECK(hipMemsetAsync(cell_cnt, 0, sizeof(int32_t) * (ncell + 1), s));
+  // 2. counting sort into cells: counts in `cursor`, scanned into the cell
+  // starts (cell_cnt), the scan leaving `cursor` zero for the scatter's
+  // per-cell counters
   E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
-  k_bin<<<nblk, tpb, 0, s>>>(pos, n, ga, cell_of, cell_cnt);
+  k_bin<<<nblk, tpb, 0, s>>>(pos, n, ga, cell_of, cursor);
   E2A_LAUNCH_CHECK();
-  // cell_cnt -> exclusive starts in place is not allowed (in/out alias): use cursor area? no:
-  // scan into row_cnt scratch would be too small, so scan to cell_cnt via a copy in cursor.
-  E2A_HIP_CHECK(hipMemcpyAsync(cursor, cell_cnt, sizeof(int32_t) * ncell, hipMemcpyDeviceToDevice, s));
   {
-    e2a_status st = exclusive_scan<int32_t>(cursor, ncell, cell_cnt, bsum, s, ncell_dev);
+    e2a_status st = exclusive_scan<int32_t>(cursor, ncell, cell_cnt, bsum, s, ncell_dev, cursor);
     if (st != E2A_OK) return st;
   }
-  E2A_HIP_CHECK(hipMemsetAsync(cursor, 0, sizeof(int32_t) * ncell, s));
   k_scatter<<<nblk, tpb, 0, s>>>(n, pos, batch, cell_of, cell_cnt, cursor, cell_atoms, pos_cell);
   E2A_LAUNCH_CHECK();
 
