@@ -296,8 +296,10 @@ __global__ void k_scan_apply(const int32_t* in, int64_t n, const int64_t* __rest
 
 // Inputs up to kScanSingle entries: one block of 1024 threads, in tiles of
 // 4096 entries (4 consecutive per thread), each scanned across the block and
-// offset by the total of the tiles before it.  One launch instead of three.
-constexpr int64_t kScanSingle = 65536;
+// offset by the total of the tiles before it.  One launch instead of three;
+// its tiles run one after another, so past about 16k entries the three
+// launches are faster (measured).
+constexpr int64_t kScanSingle = 16384;
 
 __device__ __forceinline__ int64_t shfl_up_i64(int64_t v, int o) {
   const int lo = __shfl_up(static_cast<int>(static_cast<uint64_t>(v)), o);
