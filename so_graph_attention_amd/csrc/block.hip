@@ -94,7 +94,8 @@ __global__ void __launch_bounds__(256) k_degree_norm(const float* __restrict__ h
 }
 
 // act[a][comp][c] = SiLU(u) for l = 0, u * sigmoid(z[a][(l-1) C + c]) for l >= 1;
-// atoms in turn per workgroup, four channels per thread.
+// atoms in turn per workgroup, four channels per thread (the fp32 VALU path;
+// the matrix-core path applies the gate in its first FFN product).
 template <typename OutT>
 __global__ void __launch_bounds__(256) k_gate(const float* __restrict__ u, const float* __restrict__ z,
                                               OutT* __restrict__ act, int64_t n, int L, int C) {
@@ -182,11 +183,12 @@ __device__ __forceinline__ void tile_degree(const DegGemm& g, int tile, int& l, 
 // 128 node rows and 128 output channels per workgroup.  The MFMA's rows are
 // output channels (wave w owns 32 of them; their W^T fragments, k contiguous
 // in the transposed copy wt, sit in registers for the whole tile) and its
-// columns are node rows (x rounded to bf16 and staged in LDS, k contiguous).
-// A lane's accumulators then hold four consecutive channels of one node row
-// per group of four, so the residual loads and the stores of y are 16 bytes
-// (fp32) or 8 bytes (bf16) a lane.  Optional epilogue: the FFN's gate
-// (SiLU on degree 0, sigmoid of the gate logits z on degree l >= 1).
+// columns are node rows (x rounded to bf16 and staged in LDS, k contiguous;
+// optionally normalised per atom first, the RMS norm folded into the
+// product).  The results go through an fp32 LDS tile, 64 rows at a time, and
+// 32 consecutive threads read each row back, so the residual loads and the
+// stores of y cover whole rows.  Optional epilogue: the FFN's gate (SiLU on
+// degree 0, sigmoid of the gate logits z on degree l >= 1).
 constexpr int kMRows = 128;
 constexpr int kMCols = 128;
 constexpr int kMaxCin = 128;   // x staging and the weight registers cover cin <= 128
