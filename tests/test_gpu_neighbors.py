@@ -87,6 +87,19 @@ def test_neighbors_edge_cases(B):
     assert rp.cpu().tolist() == [0, 1, 2] and col.cpu().tolist() == [1, 0]
 
 
+def test_neighbors_open_grid_extreme_extent(B):
+    """Open boundaries size the cell grid on the device: an extent of 1e7
+    cutoffs is clamped before the integer conversion and the grid coarsened
+    to the workspace's cells; the one close pair is still found, bit-exact
+    against the oracle."""
+    pos = np.array([[0.0, 0.0, 0.0], [1.5, 0.5, -0.5], [5.0e7, 0.0, 0.0], [-5.0e7, 3.0e7, 1.0e7],
+                    [2.0e7, -4.0e7, 2.5e7]], dtype=np.float32)
+    rp_o, col_o = O.neighbor_list_bruteforce(pos, 5.0)
+    rp, col = B.e2a_build_neighbors(torch.from_numpy(pos).cuda(), 5.0)
+    assert np.array_equal(rp.cpu().numpy(), rp_o) and np.array_equal(col.cpu().numpy(), col_o)
+    assert rp.cpu().tolist() == [0, 1, 2, 2, 2, 2]
+
+
 @pytest.mark.parametrize("side", [10.5, 14.0, 16.0])
 def test_neighbors_small_periodic_boxes(B, side):
     """Boxes of 2-3 cutoffs give 1 or 2 cells per axis: the stencil must not
