@@ -153,9 +153,16 @@ struct DegGemm {
   const float* gate_z;      // gate logits z[a][(l - 1) cout + c], atom stride z_stride (NULL when L = 0)
   int64_t z_stride;
   // x rows normalised per atom and degree before the product (matrix-core
-  // path, fp32 x): x[l,m,c] gamma[l][c] / sqrt(mean_{m,c} x[l]^2 + eps),
-  // gamma bf16; the tiles then hold whole atoms (atom_tiles)
+  // path, fp32 x): x[l,m,c] inv_in[a][l] gamma[l][c], gamma bf16, inv_in the
+  // per-atom inverse RMS that an earlier product's stats_out wrote
   const uint16_t* norm_gamma;
+  const float* inv_in;
+  // the epilogue writes 1 / sqrt(mean_{m,c} y[l]^2 + eps) of every atom's
+  // degree-l rows of y (the stored values, residual included) to
+  // stats_out[a][l] (matrix-core path, cout <= 128); the tiles then hold
+  // whole atoms
+  float* stats_out;
+  int stats_ld;             // entries per atom in inv_in / stats_out (L + 1)
   bool atom_tiles;          // tile rows of degree l: (tile_rows / (2l+1)) (2l+1)
 };
 
@@ -231,37 +238,20 @@ __device__ __forceinline__ float sigmoid_fast(float z) {
 __device__ __forceinline__ float silu(float u) { return u * sigmoid_fast(u); }
 __device__ __forceinline__ float gated(float u, float z) { return u * sigmoid_fast(z); }
 
-// Per-atom RMS norm of the staged x rows (fp32 values in registers, before
-// they are rounded to bf16): every row's sum of squares (its kg = cin / 8
-// threads are consecutive lanes of one wave: a shuffle tree), then per atom
-// the sum of its 2l+1 row sums in row order; x <- (x inv) gamma[l][c], the
-// arithmetic of the standalone norm.  The tile holds whole atoms.  The row
-// sums sit past the x tile in LDS.
-__device__ __forceinline__ void norm_rows(const DegGemm& g, XT8<float> (&xv)[kMRows * (kMaxCin / 8) / 256], int l,
-                                          unsigned w, unsigned nr, uint16_t* Xs, int tid) {
+// Norm2 of the staged x rows (fp32 values in registers, before they are
+// rounded to bf16): x <- (x inv) gamma[l][c] with the atom's inverse RMS from
+// inv_in, the arithmetic of the standalone norm.
+__device__ __forceinline__ void scale_rows(const DegGemm& g, XT8<float> (&xv)[kMRows * (kMaxCin / 8) / 256], int l,
+                                           unsigned w, unsigned row0, unsigned nrows, int tid) {
   constexpr int kSteps = kMRows * (kMaxCin / 8) / 256;
   const int cin = g.cin, kg = cin / 8;
-  float* rs = reinterpret_cast<float*>(Xs + kMRows * (cin + 8));   // [kMRows]
-#pragma unroll
-  for (int q = 0; q < kSteps; ++q) {
-    const XT8<float>& x = xv[q];
-    float ss = x.a.x * x.a.x + x.a.y * x.a.y + x.a.z * x.a.z + x.a.w * x.a.w + x.b.x * x.b.x + x.b.y * x.b.y +
-               x.b.z * x.b.z + x.b.w * x.b.w;
-    for (int o = 1; o < kg; o <<= 1) ss += __shfl_xor(ss, o);
-    const int t = tid + 256 * q;
-    if (t < kMRows * kg && t % kg == 0) rs[t / kg] = ss;
-  }
-  __syncthreads();
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
     const int t = tid + 256 * q;
     const int r = t / kg, k8 = (t % kg) * 8;
-    // rows past the tile's last whole atom hold zeros and stay zero
-    if (t >= kMRows * kg || r >= static_cast<int>(nr)) continue;
-    const int r0 = r / static_cast<int>(w) * static_cast<int>(w);
-    float ss = 0.0f;
-    for (int i = 0; i < static_cast<int>(w); ++i) ss += rs[r0 + i];
-    const float inv = 1.0f / sqrtf(ss / static_cast<float>(static_cast<int>(w) * cin) + kNormEps);
+    const unsigned row = row0 + static_cast<unsigned>(r);
+    if (t >= kMRows * kg || row >= nrows) continue;
+    const float inv = g.inv_in[(size_t)(row / w) * g.stats_ld + l];
     // 8 gains in one 16-byte load (gamma 16-byte aligned, checked on the host)
     const uint4 gv = *reinterpret_cast<const uint4*>(g.norm_gamma + (size_t)l * cin + k8);
     auto lo = [](uint32_t u) { return __uint_as_float(u << 16); };
@@ -278,7 +268,17 @@ __device__ __forceinline__ void norm_rows(const DegGemm& g, XT8<float> (&xv)[kMR
   }
 }
 
-template <typename XT, typename YT, bool NORM>
+// Byte offset of the epilogue's row sums (mode 2) in dynamic LDS: past both
+// the x tile and the output staging tile.
+__host__ __device__ constexpr size_t rowsum_offset(int cin) {
+  return sizeof(uint16_t) * (size_t)kMRows * (cin + 8) > sizeof(float) * (size_t)64 * (kMCols + 4)
+             ? sizeof(uint16_t) * (size_t)kMRows * (cin + 8)
+             : sizeof(float) * (size_t)64 * (kMCols + 4);
+}
+
+// NM: 0 plain; 1 the x rows scaled by inv_in and the gains (Norm2 folded in);
+// 2 the epilogue writes Norm2's per-atom inverse RMS of y to stats_out.
+template <typename XT, typename YT, int NM>
 __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int cin = g.cin, ldk = g.cin + 8, kg = g.cin / 8;
@@ -298,10 +298,16 @@ __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
   const uint16_t* Wt = (blockIdx.z ? g.wb2 : g.wb) + (int64_t)l * g.w_deg_stride;
   constexpr int kKSteps = kMaxCin / 16;
   bf16x8 wv[kKSteps];
+  auto load_w = [&]() {
 #pragma unroll
-  for (int s = 0; s < kKSteps; ++s)
-    wv[s] = (wok && 16 * s < cin) ? *reinterpret_cast<const bf16x8*>(Wt + (size_t)(cbase + r32) * cin + 16 * s + 8 * half)
-                                  : bf16x8{};
+    for (int s = 0; s < kKSteps; ++s)
+      wv[s] = (wok && 16 * s < cin)
+                  ? *reinterpret_cast<const bf16x8*>(Wt + (size_t)(cbase + r32) * cin + 16 * s + 8 * half)
+                  : bf16x8{};
+  };
+  // with the folded norm the weights load after the rows are staged (their
+  // registers would otherwise be live beside the rows and the gains)
+  if constexpr (NM != 1) load_w();
   // the tile's rows of x: a lane's 8 k values per step, all loads in flight
   // before the conversions and LDS stores
   constexpr int kSteps = kMRows * (kMaxCin / 8) / 256;
@@ -318,12 +324,13 @@ __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
       xv[q] = XT8<XT>{};
     }
   }
-  if constexpr (NORM) norm_rows(g, xv, l, w, nrows - static_cast<unsigned>(row0), Xs, tid);
+  if constexpr (NM == 1) scale_rows(g, xv, l, w, static_cast<unsigned>(row0), nrows, tid);
 #pragma unroll
   for (int q = 0; q < kSteps; ++q) {
     const int t = tid + 256 * q;
     if (t < kMRows * kg) store8_bf16(xv[q], Xs + (t / kg) * ldk + (t % kg) * 8);
   }
+  if constexpr (NM == 1) load_w();
   __syncthreads();
   // B operand = x^T: column j = node row 32 t + r32, k = 16 s + 8 half ..
   f32x16 acc[4] = {};
@@ -342,6 +349,7 @@ __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
   // threads, 4 channels each, so residual and gate loads and the stores cover
   // whole rows (512 bytes fp32, 256 bytes bf16).
   float* St = reinterpret_cast<float*>(smem);   // [64][kMCols + 4], over Xs
+  float* rsum = reinterpret_cast<float*>(smem + rowsum_offset(cin));   // [kMRows] (mode 2)
   constexpr int lds = kMCols + 4;
   YT* Y = static_cast<YT*>(blockIdx.z ? g.y2 : g.y);
   const int cw = blockIdx.y * kMCols;
@@ -363,10 +371,12 @@ __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
       const int idx = tid + 256 * j;
       const int rr = idx >> 5, c4 = (idx & 31) * 4;
       const unsigned row = static_cast<unsigned>(row0) + 64 * hh + rr;
-      if (row >= nrows || cw + c4 >= g.cout) continue;
+      const bool ok = row < nrows && cw + c4 < g.cout;
+      float4 v = {};
+      if (ok) {
       const unsigned a = row / w, comp = l * l + row % w;
       const size_t o = ((size_t)a * g.ky + comp - g.y_comp0) * g.cout + cw + c4;
-      float4 v = *reinterpret_cast<const float4*>(St + rr * lds + c4);
+      v = *reinterpret_cast<const float4*>(St + rr * lds + c4);
       if (g.res) {
         const float4 rv = *reinterpret_cast<const float4*>(g.res + o);
         v.x += rv.x;
@@ -384,6 +394,26 @@ __global__ void __launch_bounds__(256, 4) k_deg_gemm_mfma(DegGemm g) {
         }
       }
       store4(Y + o, v);
+      }
+      if constexpr (NM == 2) {
+        // the row's sum of squares of the stored values: its 32 threads are
+        // consecutive lanes of one wave
+        float sq = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1) sq += __shfl_xor(sq, m);
+        if ((idx & 31) == 0) rsum[64 * hh + rr] = sq;
+      }
+    }
+  }
+  if constexpr (NM == 2) {
+    // per atom of the tile (whole atoms): its 2l+1 row sums in row order
+    __syncthreads();
+    const unsigned nr = nrows - static_cast<unsigned>(row0);
+    for (unsigned k = tid; k * w < nr; k += 256) {
+      float ss = 0.0f;
+      for (unsigned r = 0; r < w; ++r) ss += rsum[k * w + r];
+      const float inv = 1.0f / sqrtf(ss / static_cast<float>(static_cast<int>(w) * g.cout) + kNormEps);
+      g.stats_out[(size_t)((static_cast<unsigned>(row0) + k * w) / w) * g.stats_ld + l] = inv;
     }
   }
 }
@@ -495,6 +525,7 @@ BlockWs block_ws_layout(int64_t n, int L, int C, int H, int dtype) {
   w.h1 = take(sizeof(float) * nkc);
   w.n2 = take(s * nkc);                    // Norm2, later the gated activations
   w.z = take(sizeof(float) * (size_t)n * (L > 0 ? L : 1) * C);
+  w.inv2 = take(sizeof(float) * (size_t)n * (L + 1));   // Norm2's per-atom inverse RMS (matrix-core path)
   const size_t nw = (size_t)(L + 1) * C * C;
   // node-wise weights: transposed bf16 copies (matrix cores) or fp32 copies (VALU)
   w.wf = block_uses_mfma(C, dtype) ? take(sizeof(uint16_t) * (3 * nw + (size_t)C * L * C))
@@ -526,7 +557,7 @@ e2a_status launch_norm(const float* h, const void* gamma, void* out, int64_t n, 
 e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (g.n == 0) return E2A_OK;
   g.tile_rows = mfma ? kMRows : kRows;
-  g.atom_tiles = mfma && g.norm_gamma;
+  g.atom_tiles = mfma && g.stats_out;
   const int tcols = mfma ? kMCols : kCols;
   g.group = g.n;
   int64_t per = 0;
@@ -544,23 +575,24 @@ e2a_status launch_deg_gemm(DegGemm g, bool mfma, bool x_bf16, hipStream_t s) {
   if (mfma) {
     if (g.cin > kMaxCin || g.cin % 32 != 0 || g.cout % 32 != 0)
       return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: cin=%d cout=%d on the matrix cores", g.cin, g.cout);
-    const size_t smem = std::max(sizeof(uint16_t) * (size_t)kMRows * (g.cin + 8) +
-                                     (g.norm_gamma ? sizeof(float) * kMRows : 0),
-                                 sizeof(float) * (size_t)64 * (kMCols + 4));
-    if (g.norm_gamma && (x_bf16 || (g.cin / 8 & (g.cin / 8 - 1)) != 0))
-      return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: the fused norm takes fp32 x and cin / 8 a power of two");
+    const size_t smem = rowsum_offset(g.cin) + (g.stats_out ? sizeof(float) * kMRows : 0);
+    if ((g.norm_gamma && (x_bf16 || !g.inv_in)) || (g.stats_out && (g.cout > kMCols || g.y_bf16 || g.gate)))
+      return fail(E2A_ERR_UNSUPPORTED, "node-wise GEMM: folded norm needs fp32 x and its statistics; statistics "
+                                       "need one column block of fp32 output");
     if (x_bf16 && g.y_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, uint16_t, false>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, uint16_t, 0>), grid, dim3(256), smem, s, g);
     else if (x_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, float, false>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<uint16_t, float, 0>), grid, dim3(256), smem, s, g);
+    else if (g.stats_out)
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, 2>), grid, dim3(256), smem, s, g);
     else if (g.norm_gamma && g.y_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, true>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, 1>), grid, dim3(256), smem, s, g);
     else if (g.norm_gamma)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, true>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, 1>), grid, dim3(256), smem, s, g);
     else if (g.y_bf16)
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, false>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, uint16_t, 0>), grid, dim3(256), smem, s, g);
     else
-      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, false>), grid, dim3(256), smem, s, g);
+      hipLaunchKernelGGL((k_deg_gemm_mfma<float, float, 0>), grid, dim3(256), smem, s, g);
   } else {
     const size_t smem = sizeof(float) * (size_t)(kRows + kCols) * g.cin;
     if (x_bf16) {
@@ -693,6 +725,13 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   a.workspace_bytes = W.attn_ws_bytes;
   st = p.attention(&a, s);
   if (st != E2A_OK) return st;
+  // Norm2 on the matrix cores: the projection's epilogue writes each atom's
+  // inverse RMS of h1 per degree (inv2), and the products that read
+  // Norm2(h1) (gate logits, first FFN product) scale h1's rows by it and the
+  // gains as they stage them; with gains off the 16-byte boundary, or on the
+  // VALU path, Norm2 is a pass of its own
+  const bool fuse_norm2 = mfma && (reinterpret_cast<uintptr_t>(b->norm2) & 15) == 0;
+  float* inv2 = reinterpret_cast<float*>(base + W.inv2);
   // h1 = h + a W_o
   DegGemm g{};
   g.n = n;
@@ -706,12 +745,11 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
   g.wf = wo_f;
   g.y = h1;
   g.res = b->h_in;
+  g.stats_out = fuse_norm2 ? inv2 : nullptr;
+  g.stats_ld = L + 1;
   st = launch_deg_gemm(g, mfma, false, s);
   if (st != E2A_OK) return st;
-  // n2 = Norm2(h1): its own pass on the VALU path; the matrix-core GEMMs
-  // that read it (gate logits, first FFN product) normalise h1's rows as
-  // they stage them instead
-  const bool fuse_norm2 = mfma && (reinterpret_cast<uintptr_t>(b->norm2) & 15) == 0;
+  g.stats_out = nullptr;
   if (!fuse_norm2) {
     st = launch_norm(h1, b->norm2, n2, n, L, C, dtype, s);
     if (st != E2A_OK) return st;
@@ -722,6 +760,8 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     gz.n = n;
     gz.x = fuse_norm2 ? static_cast<const void*>(h1) : n2;
     gz.norm_gamma = fuse_norm2 ? static_cast<const uint16_t*>(b->norm2) : nullptr;
+    gz.inv_in = fuse_norm2 ? inv2 : nullptr;
+    gz.stats_ld = L + 1;
     gz.kx = K;
     gz.ky = 1;
     gz.cin = C;
@@ -743,6 +783,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     act = attn;
     g.x = fuse_norm2 ? static_cast<const void*>(h1) : n2;
     g.norm_gamma = fuse_norm2 ? static_cast<const uint16_t*>(b->norm2) : nullptr;
+    g.inv_in = fuse_norm2 ? inv2 : nullptr;
     g.wb = w1_t;
     g.y = act;
     g.y_bf16 = true;
@@ -753,6 +794,7 @@ e2a_status launch_block(const BlockPlan& p, hipStream_t s) {
     st = launch_deg_gemm(g, true, !fuse_norm2, s);
     if (st != E2A_OK) return st;
     g.norm_gamma = nullptr;
+    g.inv_in = nullptr;
     g.y_bf16 = false;
     g.gate = false;
     g.gate_z = nullptr;

@@ -129,7 +129,8 @@ e2a_status launch_radial_mfma(const BwdPlan& p, float* w_rad, hipStream_t s);
 
 // One block around the layer (block.hip).
 struct BlockWs {
-  size_t n1, attn, h1, n2, z, wf;   // Norm1, layer output / FFN hidden, h1, Norm2 / gated act, gate logits, fp32 weights
+  size_t n1, attn, h1, n2, z, inv2, wf;   // Norm1, layer output / FFN hidden, h1, Norm2 / gated act, gate logits,
+                                         // Norm2's inverse RMS per atom and degree, node-wise weights
   size_t attn_ws, attn_ws_bytes;    // the layer's own workspace
   size_t total;
 };
