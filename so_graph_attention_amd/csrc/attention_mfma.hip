@@ -1197,22 +1197,42 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           s.m_run[d * kH + h] = 0.0f;
         }
         if (d == 0) s.scale[h] = 1.0f;
-      } else if (b1 > b0) {
-        float mx = s.m_run[d * kH + h];
-        for (int e = b0; e < b1; ++e) mx = fmaxf(mx, s.alpha[e * kH + h]);
-        const float sc = expf(s.m_run[d * kH + h] - mx);
-        float sum = 0.0f;
-        for (int e = b0; e < b1; ++e) {
-          const float a = expf(s.alpha[e * kH + h] - mx);
-          s.alpha[e * kH + h] = a;
-          sum += a;
-        }
-        s.l_run[d * kH + h] = s.l_run[d * kH + h] * sc + sum;
-        s.m_run[d * kH + h] = mx;
-        if (d == 0) s.scale[h] = sc;
       }
       if (d == 1)
         for (int e = ne; e < kET; ++e) s.alpha[e * kH + h] = 0.0f;
+    }
+    if constexpr (MD == kFwd) {
+      // forward: wave 0 updates destination A, wave 1 destination B; lane
+      // e = lane % 32 holds edge b0 + e and each 32-lane half one head per
+      // pass; the chunk's max and sum over the edges are butterfly shuffles
+      // within the half (a chunk holds at most 32 edges of a destination)
+      static_assert(kET == 32 && kH % 2 == 0, "one lane per edge slot, two heads per pass");
+      if (tid < 128) {
+        const int d = tid >> 6, e = tid & 31;
+        const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
+        const bool valid = b0 + e < b1;
+        if (b1 > b0) {
+          for (int h = (tid >> 5) & 1; h < kH; h += 2) {
+            const float v = valid ? s.alpha[(b0 + e) * kH + h] : -INFINITY;
+            const float m_old = s.m_run[d * kH + h];
+            float mx = v;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+            mx = fmaxf(mx, m_old);
+            const float a = valid ? expf(v - mx) : 0.0f;
+            if (valid) s.alpha[(b0 + e) * kH + h] = a;
+            float sum = a;
+#pragma unroll
+            for (int o = 16; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+            if (e == 0) {
+              const float sc = expf(m_old - mx);
+              s.l_run[d * kH + h] = s.l_run[d * kH + h] * sc + sum;
+              s.m_run[d * kH + h] = mx;
+              if (d == 0) s.scale[h] = sc;
+            }
+          }
+        }
+      }
     }
     if constexpr (L >= 2) wig_level<L, 2>(s, tid);
     __syncthreads();
