@@ -1162,6 +1162,17 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
           d += kv.x * qv[4 * t] + kv.y * qv[4 * t + 1] + kv.z * qv[4 * t + 2] + kv.w * qv[4 * t + 3];
         }
         sv = d * 0.25f;
+        if constexpr (q_like(MD) || MD == kBwdV || r_like(MD)) {
+          // gradient passes: alpha from the forward's log-normaliser of the
+          // destination of the forward edge (the neighbour, in the value
+          // pass).  The value pass carries the cotangent times gnorm (alpha
+          // scaled by it), so that its rotate-out coefficients sit in fp16's
+          // range whatever the cotangent's magnitude; the normaliser
+          // divides it out
+          const int64_t src = MD != kBwdV ? (e < nA ? ia : ib) : (int64_t)j;
+          sv = expf(sv - p.lse[src * kH + h]);
+          if constexpr (MD == kBwdV) sv *= *p.gnorm;
+        }
       }
       s.alpha[e * kH + h] = sv;
     }
@@ -1172,18 +1183,9 @@ __device__ __forceinline__ void stretch(const MfmaParams& p, const Smem& s, __am
       const int d = tid / kH, h = tid % kH;
       const int b0 = d == 0 ? 0 : nA, b1 = d == 0 ? nA : ne;
       if constexpr (q_like(MD) || MD == kBwdV || r_like(MD)) {
-        // feature gradient: alpha from the forward's log-normaliser of the
-        // destination of the forward edge (the neighbour, in the value pass)
-        for (int e = b0; e < b1; ++e) {
-          const int64_t src = MD != kBwdV ? (d == 0 ? ia : ib) : (int64_t)s.j[e];
-          s.alpha[e * kH + h] = expf(s.alpha[e * kH + h] - p.lse[src * kH + h]);
-        }
-        // the value pass carries the cotangent times gnorm (alpha scaled by
-        // it), so that its rotate-out coefficients sit in fp16's range
-        // whatever the cotangent's magnitude; the normaliser divides it out
+        // gradient passes: the weights were formed with the logits; the
+        // normaliser is the value pass's cotangent scale, or 1
         const float gs = MD == kBwdV ? *p.gnorm : 1.0f;
-        if constexpr (MD == kBwdV)
-          for (int e = b0; e < b1; ++e) s.alpha[e * kH + h] *= gs;
         if (b1 > b0) {
           s.l_run[d * kH + h] = gs;
           s.m_run[d * kH + h] = 0.0f;
